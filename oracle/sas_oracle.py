@@ -1,0 +1,410 @@
+"""Plain fp64 CPU oracle for SAS gated block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is imported by the test suite, by the
+package's smoke check and by the benchmark's CPU-baseline leg; the product path
+(the HIP library and its Python binding) never imports it, and it imports
+nothing from the product path.  It is numpy only, works in float64 and favours
+the most literal reading of the formulas over speed: every step writes out the
+definition on whole matrices (one query head at a time), with no tiling, fusion
+or reordering.
+
+Pages it follows (the text of the web pages about the method):
+  [Blog]   shibing624.github.io, "SAS：别再让稀疏注意力'抄作业'了，让语言模型
+           损失直接教它怎么排序" -- sections 问题动机 (block-sparse attention
+           formula), 方法核心 (the SAS formula, the gate g = softmax(s), the
+           inner-gate gradient).
+  [Review] jaehun.me, "SAS: Simple Attention Sparsification via End-to-End
+           Optimization of Context Ranking" -- "Background" (paper Eq. 1-3),
+           "New Approach" (paper Eq. 4 and Eq. 9), "Why the Four Design
+           Choices Matter" (log g = s - LSE(s); paper Eq. 5), "How It Works:
+           A Concrete Walkthrough" (worked example; paper Alg. 1 and Alg. 2),
+           "Our Perspective" (pooling-based block summaries).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * logits are scaled by `scale` (1/sqrt(D) in every workload); the selector
+    score uses the same scale;
+  * the current block of query t is block c(t) = t // b (causally masked);
+    its history is blocks 0 .. c(t)-1; queries in block 0 have no history;
+  * selection is per (query token, KV head): the fp32 scores of the group's
+    query heads are summed in head-index order, and Top-K keeps exactly
+    min(K, c) blocks, ordered by score descending, ties to the lower block
+    index, -0.0 equal to +0.0, NaN ranked as -inf, rows padded with -1;
+  * the gate softmax always runs over all history blocks (also at sparse
+    scope); unselected history blocks receive -inf logits;
+  * decode: the new token is already in the cache at position len-1; it
+    attends to its own block plus the selected history blocks with no gate;
+  * idx entries outside [0, c) are ignored and a repeated entry counts once.
+
+Parity status: every function below is pinned by tests that do not re-type
+its formula (library attention routines, autograd, finite differences,
+closed forms, the worked example, brute force).  Whole-pipeline results at
+bf16 have no error bound on the pages: that tolerance is a derived reading.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _logsumexp(x, axis=-1):
+    """log(sum(exp(x))) along `axis`; an all -inf slice gives -inf."""
+    x = _as64(x)
+    m = np.max(x, axis=axis, keepdims=True)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore"):
+        out = np.log(np.sum(np.exp(x - m_safe), axis=axis, keepdims=True)) + m_safe
+    return np.squeeze(out, axis=axis)
+
+
+# ----------------------------------------------------------------------------
+# a1 / a2: pooled block keys and selector scores
+# ----------------------------------------------------------------------------
+
+def pool_block_keys(k, block):
+    """Mean-pooled key summary of every complete block.
+
+    K̄[b,g,m,:] = (1/b) * sum_{j in B_m} K[b,g,j,:]   (pooling-based block
+    summaries: [Review] "Our Perspective"; partition into blocks of b tokens:
+    [Review] "Background", paper Eq. 3).
+    k: [B, Hkv, L, D] -> [B, Hkv, L // block, D] float64.
+    """
+    k = _as64(k)
+    B, H, L, D = k.shape
+    C = L // block
+    return k[:, :, : C * block].reshape(B, H, C, block, D).mean(axis=3)
+
+
+def history_blocks(position, block):
+    """Number of complete history blocks c = position // b of a query at `position`."""
+    return np.asarray(position) // block
+
+
+def block_scores(q, kbar, block, scale, positions):
+    """Selector scores s[b,h,t,m] = scale * q[b,h,t] . K̄[b,g(h),m] for m < c(t).
+
+    Entries with m >= c(t) (the current block and the future) are -inf.
+    q: [B, Hq, Nq, D]; kbar: [B, Hkv, C, D]; positions: [B, Nq] integer
+    position of each query.  Query head h reads KV head h // (Hq/Hkv).
+    Returns float64 [B, Hq, Nq, C].  ([Review] "Background", paper Eq. 3:
+    one relevance score per history block.)
+    """
+    q = _as64(q)
+    kbar = _as64(kbar)
+    B, Hq, Nq, D = q.shape
+    Hkv, C = kbar.shape[1], kbar.shape[2]
+    G = Hq // Hkv
+    c = history_blocks(positions, block)  # [B, Nq]
+    valid = np.arange(C)[None, :] < c[:, :, None]  # [B, Nq, C]
+    s = np.full((B, Hq, Nq, C), NEG_INF)
+    for b in range(B):
+        for h in range(Hq):
+            full = scale * (q[b, h] @ kbar[b, h // G].T)
+            s[b, h] = np.where(valid[b], full, NEG_INF)
+    return s
+
+
+def group_sum_scores(scores_f32, heads_per_row):
+    """fp32 sum of the scores of each KV head's query heads, in head-index order.
+
+    scores_f32: float32 [B, Hkv*heads_per_row, Nq, C] -> float32 [B, Hkv, Nq, C],
+    u = ((s_h0 + s_h1) + s_h2) + ... with every addition rounded to fp32.
+    """
+    s = np.asarray(scores_f32, dtype=np.float32)
+    B, H, Nq, C = s.shape
+    s = s.reshape(B, H // heads_per_row, heads_per_row, Nq, C)
+    u = s[:, :, 0].copy()
+    for i in range(1, heads_per_row):
+        u = (u + s[:, :, i]).astype(np.float32)
+    return u
+
+
+# ----------------------------------------------------------------------------
+# a3 / a7: hard Top-K block selection
+# ----------------------------------------------------------------------------
+
+def topk_select(scores_f32, heads_per_row, num_candidates, topk):
+    """Hard Top-K over each row's history blocks ([Review] "Background", paper
+    Eq. 3; inference I = Top-K(s, K): "A Concrete Walkthrough", Step 6).
+
+    scores_f32: float32 [B, Hkv*heads_per_row, Nq, C].
+    num_candidates: int [B, Nq], the row's c (only blocks m < c compete).
+    Returns int32 [B, Hkv, Nq, topk]: the min(topk, c) best blocks by the fp32
+    group-summed score, descending, ties to the lower index; -0.0 counts as
+    +0.0 and NaN as -inf; the remaining slots hold -1.
+    """
+    u = group_sum_scores(scores_f32, heads_per_row)
+    u = np.where(np.isnan(u), np.float32(-np.inf), u)
+    u = np.where(u == 0, np.float32(0.0), u)  # -0.0 -> +0.0
+    B, Hkv, Nq, C = u.shape
+    c = np.asarray(num_candidates).reshape(B, 1, Nq, 1)
+    m = np.broadcast_to(np.arange(C), u.shape)
+    # Blocks that do not compete sort after every candidate: lexsort orders
+    # by the last key first (not-a-candidate flag), then -score, then index.
+    not_candidate = (m >= c).astype(np.int8)
+    order = np.lexsort((m, -u.astype(np.float64), not_candidate), axis=-1)
+    out = np.full((B, Hkv, Nq, topk), -1, dtype=np.int32)
+    take = min(topk, C)
+    out[..., :take] = order[..., :take]
+    slot = np.arange(topk).reshape(1, 1, 1, topk)
+    out = np.where(slot < np.minimum(c, topk), out, -1)
+    return out.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# a4 / a5: SAS gated attention, forward and backward
+# ----------------------------------------------------------------------------
+
+def _selection_mask(idx_row_sets, c, C):
+    """Boolean [rows, C]: block m is selected for the row (m < c only)."""
+    rows = len(c)
+    sel = np.zeros((rows, C), dtype=bool)
+    for r in range(rows):
+        for m in idx_row_sets[r]:
+            m = int(m)
+            if 0 <= m < c[r]:
+                sel[r, m] = True
+    return sel
+
+
+def _row_terms(s_rows, idx_rows, rows, block, N, C):
+    """Per-row gate terms shared by forward and backward.
+
+    For each query t in `rows`: c(t), LSE_s(t) over its history blocks,
+    beta[t,m] = s[t,m] - LSE_s(t) = log g_m  ([Review] "Why the Four Design
+    Choices Matter": log g_m = s_m - LSE(s); gate g = softmax(s) over history
+    blocks: [Blog] 方法核心, [Review] "New Approach", paper Eq. 4), the
+    selection mask, and the additive bias over all N keys:
+        0          own block, key j <= t   (current block gate is 1, log 1 = 0)
+        beta[t,m]  key j in a selected history block m
+        -inf       any other key (unselected history, the future)
+    """
+    rows = np.asarray(rows)
+    c = rows // block
+    hist = np.arange(C)[None, :] < c[:, None]  # [R, C]
+    s_hist = np.where(hist, _as64(s_rows), NEG_INF)
+    lse_s = _logsumexp(s_hist, axis=-1)  # -inf when c == 0
+    with np.errstate(invalid="ignore"):
+        beta = np.where(hist, s_hist - lse_s[:, None], NEG_INF)
+    if idx_rows is None:  # full scope: every history block is gated
+        sel = hist.copy()
+    else:
+        sel = _selection_mask(idx_rows, c, C)
+    key = np.arange(N)
+    key_block = key // block
+    own = (key_block[None, :] == c[:, None]) & (key[None, :] <= rows[:, None])
+    kb = np.minimum(key_block, C - 1)
+    hist_key = (key_block[None, :] < c[:, None]) & np.take_along_axis(
+        sel, np.broadcast_to(kb, (len(rows), N)), axis=1)
+    beta_key = np.take_along_axis(beta, np.broadcast_to(kb, (len(rows), N)), axis=1)
+    bias = np.where(own, 0.0, np.where(hist_key, beta_key, NEG_INF))
+    return c, lse_s, beta, sel, bias
+
+
+def _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows):
+    N = k.shape[2]
+    C = s.shape[3]
+    g = h // G
+    idx_rows = None if idx is None else [idx[b, g, t] for t in rows]
+    c, lse_s, beta, sel, bias = _row_terms(s[b, h, rows], idx_rows, rows, block, N, C)
+    z = scale * (_as64(q[b, h, rows]) @ _as64(k[b, g]).T) + bias
+    lse = _logsumexp(z, axis=-1)
+    p = np.exp(z - lse[:, None])
+    return c, lse_s, beta, sel, p, lse
+
+
+def gated_attention_forward(q, k, v, s, idx, block, scale, rows=None):
+    """SAS forward o = softmax(q K_S^T * scale + log g_S) V_S
+    ([Blog] 方法核心 and [Review] "New Approach", paper Eq. 9).
+
+    q: [B,Hq,N,D]; k, v: [B,Hkv,N,D]; s: [B,Hq,N,C] selector scores;
+    idx: None (full scope: all history blocks gated) or int [B,Hkv,N,K]
+    (sparse scope: only the selected history blocks take part).
+    rows: optional list of query positions to evaluate (default: all).
+    Returns (o [B,Hq,R,D], lse [B,Hq,R], lse_s [B,Hq,R]) in float64, where lse
+    is the log-sum-exp of the biased logits and lse_s that of the row's
+    history scores (-inf for rows without history).
+    """
+    B, Hq, N, D = q.shape
+    G = Hq // k.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    R = len(rows)
+    o = np.zeros((B, Hq, R, D))
+    lse = np.zeros((B, Hq, R))
+    lse_s = np.zeros((B, Hq, R))
+    for b in range(B):
+        for h in range(Hq):
+            _, ls, _, _, p, l = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            o[b, h] = p @ _as64(v[b, h // G])
+            lse[b, h] = l
+            lse_s[b, h] = ls
+    return o, lse, lse_s
+
+
+def gated_attention_backward(q, k, v, do, s, idx, block, scale):
+    """Gradients of L = sum(dO * o) for the SAS forward, with s held as an input.
+
+    Returns (dq, dk, dv, ds) in float64.  dq, dk, dv are the partial
+    derivatives of the attention at fixed s (dk, dv summed over the query
+    heads that share a KV head).  ds is the selector-score gradient through
+    the log-softmax gate: with dbeta[t,m] = sum_{j in B_m} dz[t,j] for
+    selected m (0 otherwise) and g = softmax(s) over the history,
+        ds[t,m] = dbeta[t,m] - g[t,m] * sum_{m' in H(t)} dbeta[t,m'],
+    zero outside the history.  dbeta is g_m times the inner-gate gradient of
+    [Blog] 方法核心 / [Review] "Why the Four Design Choices Matter" (paper
+    Eq. 5); the second term is the chain rule through log g = s - LSE(s).
+    The recomputed forward is this oracle's own (exact o and softmax).
+    """
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    C = s.shape[3]
+    rows = np.arange(N)
+    dq = np.zeros((B, Hq, N, D))
+    dk = np.zeros((B, Hkv, N, D))
+    dv = np.zeros((B, Hkv, N, D))
+    ds = np.zeros((B, Hq, N, C))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            qh, kh, vh, doh = _as64(q[b, h]), _as64(k[b, g]), _as64(v[b, g]), _as64(do[b, h])
+            o = p @ vh
+            delta = np.sum(doh * o, axis=-1)
+            dp = doh @ vh.T
+            dz = p * (dp - delta[:, None])
+            dq[b, h] = scale * (dz @ kh)
+            dk[b, g] += scale * (dz.T @ qh)
+            dv[b, g] += p.T @ doh
+            # dbeta: sum of dz over the keys of each selected history block.
+            dbeta = np.zeros((N, C))
+            for m in range(C):
+                dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
+            dbeta = np.where(sel, dbeta, 0.0)
+            hist = np.arange(C)[None, :] < c[:, None]
+            gate = np.where(hist, np.exp(np.where(hist, beta, 0.0)), 0.0)
+            total = dbeta.sum(axis=1, keepdims=True)
+            ds[b, h] = np.where(hist, dbeta - gate * total, 0.0)
+    return dq, dk, dv, ds
+
+
+def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows):
+    """dq and ds of selected query rows (row-local parts of the backward).
+
+    Same definitions as `gated_attention_backward`, evaluated only for the
+    query positions in `rows` of head h in batch b.  Returns (dq [R,D], ds [R,C]).
+    """
+    Hq = q.shape[1]
+    G = Hq // k.shape[1]
+    C = s.shape[3]
+    g = h // G
+    rows = np.asarray(rows)
+    c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+    vh, kh, doh = _as64(v[b, g]), _as64(k[b, g]), _as64(do[b, h, rows])
+    o = p @ vh
+    delta = np.sum(doh * o, axis=-1)
+    dz = p * (doh @ vh.T - delta[:, None])
+    dq = scale * (dz @ kh)
+    dbeta = np.zeros((len(rows), C))
+    for m in range(C):
+        dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
+    dbeta = np.where(sel, dbeta, 0.0)
+    hist = np.arange(C)[None, :] < c[:, None]
+    gate = np.where(hist, np.exp(np.where(hist, beta, 0.0)), 0.0)
+    ds = np.where(hist, dbeta - gate * dbeta.sum(axis=1, keepdims=True), 0.0)
+    return dq, ds
+
+
+def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024):
+    """dk and dv of selected keys of KV head g in batch b.
+
+    dk[j] = scale * sum_{h in group(g)} sum_t dz[h,t,j] q[h,t];
+    dv[j] = sum_{h in group(g)} sum_t p[h,t,j] dO[h,t]; the sums run over every
+    query row (rows that do not attend key j contribute p = dz = 0).  Rows are
+    visited in chunks only to bound memory; each row is computed exactly as in
+    `gated_attention_backward`.  Returns (dk [J,D], dv [J,D]).
+    """
+    B, Hq, N, D = q.shape
+    G = Hq // k.shape[1]
+    keys = np.asarray(keys)
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    kmin = int(keys.min())
+    for h in range(g * G, (g + 1) * G):
+        for r0 in range(kmin, N, row_chunk):
+            rows = np.arange(r0, min(N, r0 + row_chunk))
+            _, _, _, _, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            vh = _as64(v[b, g])
+            doh = _as64(do[b, h, rows])
+            o = p @ vh
+            delta = np.sum(doh * o, axis=-1)
+            pk = p[:, keys]
+            dz = pk * (doh @ vh[keys].T - delta[:, None])
+            dk += scale * (dz.T @ _as64(q[b, h, rows]))
+            dv += pk.T @ doh
+    return dk, dv
+
+
+# ----------------------------------------------------------------------------
+# a8: sparse decode attention (inference, no gate)
+# ----------------------------------------------------------------------------
+
+def sparse_decode(q, k_cache, v_cache, cache_len, idx, block, scale):
+    """One decode step per sequence: o = softmax(scale * q K_S^T) V_S over
+    S = current block ∪ selected history blocks, with no gate
+    ([Blog] 问题动机 block-sparse attention formula; [Review] "Background",
+    paper Eq. 2, and "A Concrete Walkthrough", Step 6 / paper Alg. 2).
+
+    q: [B, Hq, D]; caches: [B, Hkv, L_max, D]; cache_len: [B] (the new token
+    sits at position len-1); idx: int [B, Hkv, K] (entries outside [0, c)
+    ignored, repeats counted once) or None for dense decode over every
+    cached position.  Returns (o [B,Hq,D], lse [B,Hq]) in float64.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        pos = int(cache_len[b]) - 1
+        c = pos // block
+        if idx is None:
+            keys_by_g = [np.arange(pos + 1)] * Hkv
+        else:
+            keys_by_g = []
+            for g in range(Hkv):
+                blocks = sorted({int(m) for m in idx[b, g] if 0 <= int(m) < c})
+                parts = [np.arange(m * block, (m + 1) * block) for m in blocks]
+                parts.append(np.arange(c * block, pos + 1))
+                keys_by_g.append(np.concatenate(parts))
+        for h in range(Hq):
+            g = h // G
+            keys = keys_by_g[g]
+            kk = _as64(k_cache[b, g, keys])
+            vv = _as64(v_cache[b, g, keys])
+            z = scale * (kk @ _as64(q[b, h]))
+            l = _logsumexp(z)
+            o[b, h] = np.exp(z - l) @ vv
+            lse[b, h] = l
+    return o, lse
+
+
+def decode_scores(q, kbar, cache_len, block, scale, group_sum):
+    """Decode-mode selector scores for one new token per sequence.
+
+    q: [B, Hq, D]; kbar: [B, Hkv, C, D]; the query sits at len-1, so blocks
+    m < (len-1)//b compete.  group_sum=False: float64 [B, Hq, C];
+    group_sum=True: float32 [B, Hkv, C], the fp32 sum (head-index order) of
+    each head's score rounded to fp32.  Non-candidates hold -inf.
+    """
+    B, Hq, D = q.shape
+    pos = (np.asarray(cache_len) - 1).reshape(B, 1)
+    s = block_scores(np.asarray(q)[:, :, None, :], kbar, block, scale, pos)[:, :, 0, :]
+    if not group_sum:
+        return s
+    G = Hq // kbar.shape[1]
+    return group_sum_scores(s.astype(np.float32)[:, :, None, :], G)[:, :, 0, :]
