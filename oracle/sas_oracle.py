@@ -362,15 +362,22 @@ def sparse_decode(q, k_cache, v_cache, cache_len, idx, block, scale):
     q: [B, Hq, D]; caches: [B, Hkv, L_max, D]; cache_len: [B] (the new token
     sits at position len-1); idx: int [B, Hkv, K] (entries outside [0, c)
     ignored, repeats counted once) or None for dense decode over every
-    cached position.  Returns (o [B,Hq,D], lse [B,Hq]) in float64.
+    cached position.  A length <= 0 marks an idle sequence (o = 0, lse = -inf)
+    and a length above L_max counts as L_max (readings: the pages describe
+    only live sequences).  Returns (o [B,Hq,D], lse [B,Hq]) in float64.
     """
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     G = Hq // Hkv
     o = np.zeros((B, Hq, D))
     lse = np.zeros((B, Hq))
+    L = k_cache.shape[2]
     for b in range(B):
-        pos = int(cache_len[b]) - 1
+        n = min(int(cache_len[b]), L)  # lengths above the capacity count as the capacity
+        if n <= 0:  # idle sequence: no query; output 0 and lse -inf
+            lse[b] = -np.inf
+            continue
+        pos = n - 1
         c = pos // block
         if idx is None:
             keys_by_g = [np.arange(pos + 1)] * Hkv
@@ -397,12 +404,13 @@ def decode_scores(q, kbar, cache_len, block, scale, group_sum):
     """Decode-mode selector scores for one new token per sequence.
 
     q: [B, Hq, D]; kbar: [B, Hkv, C, D]; the query sits at len-1, so blocks
-    m < (len-1)//b compete.  group_sum=False: float64 [B, Hq, C];
+    m < (len-1)//b compete (none for an idle sequence, len <= 0).  group_sum=False: float64 [B, Hq, C];
     group_sum=True: float32 [B, Hkv, C], the fp32 sum (head-index order) of
     each head's score rounded to fp32.  Non-candidates hold -inf.
     """
     B, Hq, D = q.shape
-    pos = (np.asarray(cache_len) - 1).reshape(B, 1)
+    lens = np.minimum(np.asarray(cache_len), kbar.shape[2] * block + block - 1)
+    pos = np.maximum(lens - 1, 0).reshape(B, 1)
     s = block_scores(np.asarray(q)[:, :, None, :], kbar, block, scale, pos)[:, :, 0, :]
     if not group_sum:
         return s

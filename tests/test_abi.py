@@ -1,0 +1,109 @@
+"""C ABI contract checks that need no GPU: the library loads, exports every
+function include/sas.h declares, and rejects invalid arguments on the host
+(before any HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+
+sas = pytest.importorskip("trainable_block_sparse_sas_amd.binding")
+L = sas._lib
+N = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
+                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_workspace_bytes",
+                          "sas_last_error", "sas_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in sas.EXPORTED
+
+
+def test_version_and_workspace_sizes():
+    assert sas.sas_abi_version() == 100
+    assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
+    assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
+    assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
+    assert sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 3, 2, 64, 128, 64, -1, 1) == ctypes.c_size_t(-1).value
+    assert sas.sas_workspace_bytes(99, 1, 4, 2, 64, 128, 64, -1, 1) == ctypes.c_size_t(-1).value
+
+
+def fwd(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, topk=0, dtype=1, ptr=1, idx=None, ws=None, wsb=0):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return L.sas_gated_attn_fwd(p, p, p, p, idx, p, p, p, B, Hq, Hkv, N_, D, block, topk, 0.1, dtype,
+                                ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Hq=3, Hkv=2), sas.SAS_EINVAL, "multiple"),
+    (dict(Hkv=0), sas.SAS_EINVAL, "Hkv"),
+    (dict(B=-1), sas.SAS_EINVAL, "non-negative"),
+    (dict(block=0), sas.SAS_EINVAL, "block"),
+    (dict(dtype=7), sas.SAS_EINVAL, "dtype"),
+    (dict(D=96), sas.SAS_EUNSUPPORTED, "head dim"),
+    (dict(ptr=0), sas.SAS_EINVAL, "non-NULL"),
+    (dict(idx=ctypes.c_void_p(8), topk=-1), sas.SAS_EINVAL, "topk"),
+    (dict(idx=ctypes.c_void_p(8), topk=300), sas.SAS_EUNSUPPORTED, "topk"),
+])
+def test_fwd_rejects(kw, code, msg):
+    assert fwd(**kw) == code
+    assert msg in sas.sas_last_error()
+
+
+def test_empty_calls_succeed_without_gpu():
+    assert fwd(N_=0) == 0
+    assert fwd(B=0) == 0
+    assert L.sas_topk_select(N, N, N, 1, 2, 4, 16, 8, 64, 0, N, 0, N) == 0
+
+
+def test_other_entry_points_reject():
+    v = ctypes.c_void_p(8)
+    # score: training mode needs Nq == L
+    assert L.sas_score_blocks(v, v, v, v, N, 1, 4, 2, 100, 128, 128, 64, 0.1, 0, 1, N) == sas.SAS_EINVAL
+    # score: decode mode needs Nq == 1 and at most 16 heads per KV head
+    assert L.sas_score_blocks(v, N, v, v, v, 1, 4, 2, 2, 128, 128, 64, 0.1, 1, 1, N) == sas.SAS_EINVAL
+    assert L.sas_score_blocks(v, N, v, v, v, 1, 34, 2, 1, 128, 128, 64, 0.1, 1, 1, N) == sas.SAS_EUNSUPPORTED
+    # topk: heads_per_row, sizes, limits
+    assert L.sas_topk_select(v, v, N, 1, 2, 0, 16, 8, 64, 4, N, 0, N) == sas.SAS_EINVAL
+    assert L.sas_topk_select(v, v, N, 1, 2, 4, 16, 8, 64, -2, N, 0, N) == sas.SAS_EINVAL
+    assert L.sas_topk_select(v, v, N, 1, 2, 4, 16, 20000, 64, 4, N, 0, N) == sas.SAS_EUNSUPPORTED
+    assert L.sas_topk_select(v, v, N, 1, 2, 4, 16, 8, 64, 257, N, 0, N) == sas.SAS_EUNSUPPORTED
+    assert L.sas_topk_select(v, v, v, 1, 2, 1, 3, 8, 64, 4, N, 0, N) == sas.SAS_EINVAL
+    assert L.sas_topk_select(N, v, N, 1, 2, 1, 3, 8, 64, 4, N, 0, N) == sas.SAS_EINVAL
+    # bwd: workspace required
+    args = [v] * 13 + [1, 4, 2, 128, 128, 64, 0, 0.1, 1]
+    assert L.sas_gated_attn_bwd(*args, N, 0, N) == sas.SAS_EWORKSPACE
+    assert "workspace" in sas.sas_last_error()
+    # decode: workspace, cache_len and head-group limits
+    dargs = [v, v, v, v, N, v, N, 2, 8, 2, 1024, 128, 64, 4, 0.1, 1]
+    assert L.sas_sparse_decode(*dargs, N, 0, N) == sas.SAS_EWORKSPACE
+    dargs2 = [v, v, v, N, N, v, N, 2, 8, 2, 1024, 128, 64, 4, 0.1, 1]
+    assert L.sas_sparse_decode(*dargs2, v, 1 << 30, N) == sas.SAS_EINVAL
+    dargs3 = [v, v, v, v, N, v, N, 2, 40, 2, 1024, 128, 64, 4, 0.1, 1]
+    assert L.sas_sparse_decode(*dargs3, v, 1 << 30, N) == sas.SAS_EUNSUPPORTED
+
+
+def test_errors_are_thread_local():
+    import threading
+    assert fwd(Hq=3, Hkv=2) == sas.SAS_EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = sas.sas_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "multiple" in sas.sas_last_error()

@@ -1,0 +1,258 @@
+"""GPU parity of every libsas entry point against the CPU oracle (small shapes).
+
+Inputs come from the seeded generators; selector scores and Top-K indices fed
+to the attention calls come from the oracle, so each entry point is compared
+on identical inputs.  Tolerances: see tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sas_oracle as orc
+from tests.gpu_util import max_abs, normwise, to64, tolerances
+from trainable_block_sparse_sas_amd.inputs import Workload, decode_inputs, score_matrix, training_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from trainable_block_sparse_sas_amd import binding as sas
+    from trainable_block_sparse_sas_amd.pipeline import DecodeStep, TrainStep
+
+DEV = "cuda"
+
+
+def _dt(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+def _oracle_selector(q, k, block, scale, topk, G):
+    """Oracle pooled keys, fp32 scores and (sparse scope) indices for training rows."""
+    q64, k64 = to64(q), to64(k)
+    kbar = orc.pool_block_keys(k64, block)
+    kbar_r = to64(torch.tensor(kbar).to(q.dtype))  # pooled keys are stored in the input dtype
+    N = q.shape[2]
+    pos = np.broadcast_to(np.arange(N), (q.shape[0], N))
+    s32 = orc.block_scores(q64, kbar_r, block, scale, pos).astype(np.float32)
+    idx = None
+    if topk is not None:
+        idx = orc.topk_select(s32, G, pos // block, topk)
+    return kbar, kbar_r, s32, idx
+
+
+TRAIN_CASES = [
+    # name, dtype, B, Hq, Hkv, D, N, block, topk
+    ("tiny-f32-full", "f32", 1, 2, 1, 64, 512, 64, None),
+    ("f32-ragged-sparse", "f32", 2, 4, 2, 64, 300, 64, 2),
+    ("f32-block16-sparse", "f32", 1, 2, 1, 128, 130, 16, 3),
+    ("bf16-full", "bf16", 1, 8, 2, 128, 384, 64, None),
+    ("bf16-ragged-sparse", "bf16", 1, 8, 2, 128, 450, 64, 3),
+    ("bf16-g1-d64-sparse", "bf16", 2, 4, 4, 64, 256, 64, 1),
+    ("bf16-block32-sparse", "bf16", 1, 4, 1, 128, 200, 32, 2),
+    ("bf16-topk0", "bf16", 1, 4, 2, 128, 256, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
+def test_training_parity(case):
+    name, dts, B, Hq, Hkv, D, N, block, topk = case
+    dt = _dt(dts)
+    w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=7)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    scale = w.scale
+    G = Hq // Hkv
+    tol = tolerances(dt)
+    kbar, kbar_r, s32, idx = _oracle_selector(q, k, block, scale, topk, G)
+    step = TrainStep(B, Hq, Hkv, N, D, block, topk, dt)
+
+    # Selector: pooled keys and scores.
+    step.select(q, k)
+    torch.cuda.synchronize()
+    gk = to64(step.kbar)
+    if dt == torch.float32:
+        normwise(gk, kbar, 1e-6, "kbar")
+    else:  # fp32 mean rounded to bf16: at most one bf16 step from the rounded exact mean
+        assert np.all(np.abs(gk - kbar_r) <= np.abs(kbar_r) * 2.0 ** -7 + 1e-30), "kbar"
+    sc_in = torch.tensor(kbar_r).to(dt).to(DEV)
+    sas.sas_score_blocks(q, None, sc_in, step.scores, None, block, scale)
+    torch.cuda.synchronize()
+    normwise(to64(step.scores), s32.astype(np.float64), 1e-5, "scores")
+
+    # Top-K on the oracle's fp32 scores: bit-exact.
+    scores = torch.tensor(s32).to(DEV)
+    idx_t = None
+    if topk is not None:
+        sas.sas_topk_select(scores, step.idx, None, G, block)
+        torch.cuda.synchronize()
+        assert np.array_equal(step.idx.cpu().numpy(), idx), "topk"
+        idx_t = torch.tensor(idx).to(DEV)
+
+    # Forward.
+    step.forward(q, k, v, scores, idx_t)
+    torch.cuda.synchronize()
+    s64 = s32.astype(np.float64)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale)
+    if tol["o_abs"] is not None:
+        max_abs(to64(step.o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(step.o), o_ref, tol["o_rel"], "o")
+    normwise(to64(step.lse), lse_ref, tol["lse"], "lse")
+    normwise(to64(step.lse_s), lses_ref, tol["lse"], "lse_s")
+
+    # Backward.
+    step.backward(q, k, v, do, scores, idx_t)
+    torch.cuda.synchronize()
+    dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, scale)
+    normwise(to64(step.dq), dq, tol["grad"], "dq")
+    normwise(to64(step.dk), dk, tol["grad"], "dk")
+    normwise(to64(step.dv), dv, tol["grad"], "dv")
+    normwise(to64(step.ds), ds, tol["ds"], "ds")
+
+
+TOPK_CASES = [
+    # C, hpr, training(1)-or-None(decode), topk
+    (40, 4, 1, 5),
+    (300, 1, 1, 32),
+    (900, 2, 1, 64),
+    (1500, 1, 1, 32),
+    (2047, 1, None, 16),
+    (8191, 1, None, 32),
+    (5000, 1, None, 256),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[f"C{c[0]}-h{c[1]}-k{c[3]}" for c in TOPK_CASES])
+def test_topk_bit_exact(case):
+    C, hpr, Nq, topk = case
+    Hkv, block = 2, 4
+    if Nq is None:  # decode rows of several lengths, including an idle one
+        B = 5
+        s = score_matrix((B, Hkv * hpr, C), seed=C)
+        s = torch.where(torch.rand(s.shape, generator=torch.Generator().manual_seed(1)) < 0.2,
+                        torch.round(s * 4) / 4, s)
+        lens = torch.tensor([C * block + 1, 1 + block * 7, 0, C * block // 2, block * (C + 3)],
+                            dtype=torch.int32)
+        c = np.minimum(np.maximum(lens.numpy() - 1, 0) // block, C)
+        c[lens.numpy() <= 0] = 0
+        ref = orc.topk_select(s.numpy()[:, :, None, :], hpr, c[:, None], topk)[:, :, 0, :]
+        idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=DEV)
+        sas.sas_topk_select(s.to(DEV), idx, lens.to(DEV), hpr, block)
+    else:
+        B = 1
+        N = C + 8  # block 1: row t has min(t, C) candidates
+        s = score_matrix((B, Hkv * hpr, N, C), seed=C + 1)
+        s = torch.round(s * 8) / 8  # many exact ties
+        s[0, 0, :, :3] = torch.tensor([float("nan"), -0.0, 0.0])
+        s[0, 0, :, 3:5] = torch.tensor([float("inf"), float("-inf")])
+        pos = np.arange(N)[None, :]
+        ref = orc.topk_select(s.numpy(), hpr, np.minimum(pos, C), topk)
+        idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=DEV)
+        sas.sas_topk_select(s.to(DEV), idx, None, hpr, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+DECODE_CASES = [
+    # name, dtype, Hq, Hkv, D, L, block, topk
+    ("bf16-g4", "bf16", 8, 2, 128, 2048, 64, 4),
+    ("bf16-g5", "bf16", 10, 2, 128, 1536, 64, 3),
+    ("bf16-dense", "bf16", 8, 2, 128, 2048, 64, None),
+    ("f32-d64", "f32", 4, 1, 64, 1024, 64, 2),
+    ("bf16-block32", "bf16", 4, 2, 128, 1000, 32, 5),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_parity(case):
+    name, dts, Hq, Hkv, D, L, block, topk = case
+    dt = _dt(dts)
+    B = 4
+    w = Workload(name, "decode", dts, B, Hq, Hkv, D, L, block, topk, index=9)
+    q, kc, vc, _ = decode_inputs(w, device="cpu")
+    lens = torch.tensor([L, L - 37, 40, 0], dtype=torch.int32)
+    q, kc, vc, lens_d = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    scale = w.scale
+    G = Hq // Hkv
+    tol = tolerances(dt)
+    step = DecodeStep(B, Hq, Hkv, L, D, block, topk if topk is not None else 1, dt)
+    # Pooled keys.
+    step.pool(kc)
+    torch.cuda.synchronize()
+    kbar = orc.pool_block_keys(to64(kc), block)
+    kbar_r = to64(torch.tensor(kbar).to(dt))
+    if dt == torch.float32:
+        normwise(to64(step.kbar), kbar, 1e-6, "kbar")
+    else:
+        assert np.all(np.abs(to64(step.kbar) - kbar_r) <= np.abs(kbar_r) * 2.0 ** -7 + 1e-30)
+    # Group-summed decode scores from the oracle's pooled keys.
+    kb = torch.tensor(kbar_r).to(dt).to(DEV)
+    sas.sas_score_blocks(q, None, kb, step.u, lens_d, block, scale, group_sum=True, L=L)
+    torch.cuda.synchronize()
+    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, True)
+    normwise(to64(step.u), u_ref.astype(np.float64), 1e-5, "u")
+    # Per-head decode scores.
+    s_h = torch.empty((B, Hq, L // block), dtype=torch.float32, device=DEV)
+    sas.sas_score_blocks(q, None, kb, s_h, lens_d, block, scale, group_sum=False, L=L)
+    torch.cuda.synchronize()
+    s_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, False)
+    normwise(to64(s_h), s_ref, 1e-5, "s")
+    # Top-K on the oracle's group sums: bit-exact.
+    c = np.maximum(lens.numpy() - 1, 0) // block
+    idx_ref = None
+    if topk is not None:
+        idx_ref = orc.topk_select(u_ref[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+        sas.sas_topk_select(torch.tensor(u_ref).to(DEV), step.idx, lens_d, 1, block)
+        torch.cuda.synchronize()
+        assert np.array_equal(step.idx.cpu().numpy(), idx_ref)
+    # Attention over the selected blocks (or all blocks).
+    idx_in = None if topk is None else torch.tensor(idx_ref).to(DEV)
+    step.ws = sas.workspace(sas.SAS_OP_DECODE, B, Hq, Hkv, L, D, block, -1 if topk is None else topk,
+                            sas.SAS_BF16 if dt == torch.bfloat16 else sas.SAS_F32)
+    sas.sas_sparse_decode(q, kc, vc, lens_d, idx_in, step.o, step.lse, block, scale, step.ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.sparse_decode(to64(q), to64(kc), to64(vc), lens.numpy(), idx_ref, block, scale)
+    active = lens.numpy() > 0
+    if tol["o_abs"] is not None:
+        max_abs(to64(step.o)[active], o_ref[active], tol["o_abs"], "o")
+    else:
+        normwise(to64(step.o)[active], o_ref[active], tol["o_rel"], "o")
+    normwise(to64(step.lse)[active], lse_ref[active], 1e-4, "lse")
+    # Idle sequence: zeros and -inf.
+    assert torch.all(step.o[~torch.tensor(active)] == 0)
+    assert torch.all(step.lse[~torch.tensor(active)] == float("-inf"))
+
+
+def test_empty_sizes_are_noops():
+    dt = torch.bfloat16
+    z = torch.empty((1, 4, 0, 128), dtype=dt, device=DEV)
+    zk = torch.empty((1, 2, 0, 128), dtype=dt, device=DEV)
+    sc = torch.empty((1, 4, 0, 0), dtype=torch.float32, device=DEV)
+    l = torch.empty((1, 4, 0), dtype=torch.float32, device=DEV)
+    sas.sas_gated_attn_fwd(z, zk, zk, sc, None, z, l, l, 64, 0.1)
+    sas.sas_gated_attn_bwd(z, zk, zk, z, z, sc, None, l, l, z, zk, zk, sc, 64, 0.1)
+    torch.cuda.synchronize()
+
+
+def test_repeated_and_invalid_idx_entries():
+    """Repeated entries count once and entries outside [0, c) are ignored."""
+    dt = torch.bfloat16
+    B, Hq, Hkv, D, N, block = 1, 4, 2, 128, 320, 64
+    w = Workload("dup", "train", "bf16", B, Hq, Hkv, D, N, block, 4, index=11)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    _, _, s32, _ = _oracle_selector(q, k, block, w.scale, None, 2)
+    r = np.random.default_rng(3)
+    idx = r.integers(-2, 6, size=(B, Hkv, N, 4)).astype(np.int32)
+    idx[..., 1] = idx[..., 0]
+    step = TrainStep(B, Hq, Hkv, N, D, block, 4, dt)
+    scores = torch.tensor(s32).to(DEV)
+    it = torch.tensor(idx).to(DEV)
+    step.forward(q, k, v, scores, it)
+    step.backward(q, k, v, do, scores, it)
+    torch.cuda.synchronize()
+    s64 = s32.astype(np.float64)
+    o_ref, _, _ = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, w.scale)
+    max_abs(to64(step.o), o_ref, 2e-2, "o")
+    dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, w.scale)
+    normwise(to64(step.dq), dq, 2e-2, "dq")
+    normwise(to64(step.dk), dk, 2e-2, "dk")
+    normwise(to64(step.dv), dv, 2e-2, "dv")
+    normwise(to64(step.ds), ds, 2e-2, "ds")

@@ -475,3 +475,17 @@ def test_row_and_key_gradient_helpers_match_full_backward():
         o2, lse2, lse_s2 = orc.gated_attention_forward(q, k, v, s, sc, block, 0.4, rows=rows)
         np.testing.assert_allclose(o2, o[:, :, rows], atol=1e-13)
         np.testing.assert_allclose(lse2, lse[:, :, rows], atol=1e-13)
+
+
+def test_decode_idle_and_overlong_sequences():
+    """Idle sequences give zero output and lse -inf; lengths beyond the cache clamp."""
+    q, kc, vc = _decode_problem(5, L=64)
+    idx = np.array([[[0, 1], [1, 0]], [[0, 2], [3, 1]]], dtype=np.int32)
+    o, lse = orc.sparse_decode(q, kc, vc, np.array([0, 500]), idx, 16, 0.3)
+    assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf)
+    o2, lse2 = orc.sparse_decode(q, kc, vc, np.array([0, 64]), idx, 16, 0.3)
+    np.testing.assert_array_equal(o[1], o2[1])
+    od, _ = orc.sparse_decode(q, kc, vc, np.array([-3, 64]), None, 16, 0.3)
+    assert np.all(od[0] == 0)
+    u = orc.decode_scores(q, orc.pool_block_keys(kc, 16), np.array([0, 64]), 16, 0.3, True)
+    assert np.all(u[0] == -np.inf)
