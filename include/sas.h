@@ -1,0 +1,218 @@
+/*
+ * sas.h -- C ABI of libsas, SAS (Simple Attention Sparsification) gated
+ * block-sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method, as the pages describe it:
+ *   - block-sparse attention: the context is cut into blocks of b tokens, a
+ *     selector scores each block, and a query attends only to the Top-K
+ *     blocks (shibing624 blog post, section 问题动机 "motivation", block-sparse
+ *     attention formula; jaehun.me review "SAS: Simple Attention
+ *     Sparsification via End-to-End Optimization of Context Ranking",
+ *     section "Background", paper Eq. 2 and Eq. 3);
+ *   - SAS training attention: o = softmax(q K_S^T + log g_S) V_S with
+ *     g = softmax(s) over the query's history blocks and gate 1 (bias 0) on the
+ *     query's own block (blog section 方法核心 "method core"; review section
+ *     "New Approach", paper Eq. 4 and Eq. 9; log g = s - LSE(s) in review
+ *     section "Why the Four Design Choices Matter");
+ *   - inference: hard Top-K on the scores, no gate (review section "How It
+ *     Works: A Concrete Walkthrough", Step 6, paper Alg. 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *   Tensors are device memory owned by the caller, dense and row-major:
+ *     q, o, dq, dO       [B, Hq,  N, D]    (decode: [B, Hq, D])
+ *     k, v, dk, dv       [B, Hkv, N, D]    (decode caches: [B, Hkv, L_max, D])
+ *     kbar               [B, Hkv, C, D]    pooled block keys, C = N / block
+ *                                          (integer division; decode C = L_max / block)
+ *     scores, ds         [B, Hq,  N, C]    fp32 (decode: [B, Hq, C])
+ *     group-summed scores[B, Hkv, N, C]    fp32 (decode: [B, Hkv, C])
+ *     idx                [B, Hkv, N, topk] int32 (decode: [B, Hkv, topk])
+ *     lse, lse_s         [B, Hq,  N]       fp32 (decode lse: [B, Hq])
+ *   `dtype` (sas_dtype) is the element type of q, k, v, o, dO, dq, dk, dv
+ *   and kbar.  Query head h reads KV head h / (Hq / Hkv) (grouped-query
+ *   attention).  `scale` multiplies q.k in the logits and in the selector
+ *   score (1/sqrt(D) in the usual setting).
+ *
+ *   Positions.  Training calls (cache_len == NULL) place query t at position
+ *   t.  Decode calls place the single new token of sequence b at position
+ *   cache_len[b] - 1 (its K and V are already in the cache); lengths above
+ *   L_max count as L_max and a length <= 0 marks an idle sequence.
+ *   The current block of a query at position p is c = p / block; its history
+ *   is blocks 0 .. c-1 (complete blocks only).  The current block is always
+ *   attended, causally, with bias 0.
+ *
+ *   idx: hard Top-K output, per (query token, KV head).  Entries outside
+ *   [0, c) are ignored and a repeated entry counts once.  idx == NULL in the
+ *   attention calls means full scope (every history block).
+ *
+ *   Every call validates all arguments on the host before touching the GPU;
+ *   on failure it returns a negative sas_status, launches nothing, and
+ *   sas_last_error() describes the problem.  Work is enqueued asynchronously
+ *   on `stream` (a hipStream_t; NULL is the null stream): inputs must stay
+ *   valid and outputs untouched until the stream reaches that point.  The
+ *   library allocates no memory; calls that need scratch take a caller
+ *   workspace of at least sas_workspace_bytes() bytes.  No call keeps a
+ *   pointer after it returns.  Calls are thread-safe (the error string is
+ *   thread-local).  Sizes of zero (B, Hq, N or L_max) are valid and do nothing.
+ */
+#ifndef SAS_H_
+#define SAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAS_OK = 0,
+  SAS_EINVAL = -1,        /* an argument is invalid (shape, pointer, value) */
+  SAS_EUNSUPPORTED = -2,  /* valid, but outside what the library implements */
+  SAS_EHIP = -3,          /* the HIP runtime reported an error at launch */
+  SAS_EWORKSPACE = -4     /* workspace missing or smaller than required */
+} sas_status;
+
+typedef enum { SAS_F32 = 0, SAS_BF16 = 1 } sas_dtype;
+
+typedef enum {
+  SAS_OP_SCORE = 1,
+  SAS_OP_TOPK = 2,
+  SAS_OP_FWD = 3,
+  SAS_OP_BWD = 4,
+  SAS_OP_DECODE = 5
+} sas_op;
+
+/*
+ * sas_score_blocks -- block mean-pooling and selector scores.
+ *   K̄[b,g,m,:] = mean of k over the `block` tokens of block m  (pooling-based
+ *   block summaries: review section "Our Perspective", Limitations), and
+ *   s[b,h,t,m] = scale * q[b,h,t] . K̄[b,h/G,m] for every history block
+ *   m < c(t); all other columns are written as -inf (review "Background",
+ *   paper Eq. 3: one relevance score per block).
+ * k:          if non-NULL, kbar is first computed from k ([B,Hkv,L,D]) for
+ *             all C = L/block complete blocks and written; if NULL, kbar is an
+ *             input (decode: pooled keys kept beside the cache).
+ * kbar:       [B,Hkv,C,D] in `dtype` (the mean is taken in fp32, then rounded).
+ * scores:     fp32 output; [B,Hq,Nq,C], or with group_sum != 0 the per-KV-head
+ *             sum [B,Hkv,Nq,C] (query heads added in index order, fp32).
+ * cache_len:  NULL for training (Nq must equal L; query t at position t);
+ *             device int32 [B] for decode (Nq must be 1).
+ * Errors: SAS_EINVAL for null required pointers, Hq % Hkv != 0, block < 1,
+ *         Nq/L mismatch; SAS_EUNSUPPORTED for D outside {64, 128} or, in decode
+ *         mode, more than 16 query heads per KV head.
+ */
+int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
+                     const int32_t* cache_len, int B, int Hq, int Hkv, int Nq,
+                     int L, int D, int block, float scale, int group_sum,
+                     int dtype, void* stream);
+
+/*
+ * sas_topk_select -- hard Top-K over each row's history blocks (review
+ *   "Background", paper Eq. 3; training selection per query token and KV
+ *   head; review "A Concrete Walkthrough" Step 3 and Step 6).
+ * scores:        fp32 [B, Hkv*heads_per_row, Nq, C]; the heads_per_row rows
+ *                of one KV head are summed in fp32 in index order
+ *                (heads_per_row = 1: already summed).
+ * idx:           int32 [B, Hkv, Nq, topk] output: the min(topk, c) best
+ *                history blocks, score descending, ties to the lower block
+ *                index (-0.0 equals +0.0, NaN ranks as -inf), remaining slots
+ *                -1.  Bit-exact and deterministic.
+ * cache_len:     NULL: row t has c = t / block candidates (training, Nq rows);
+ *                device int32 [B]: decode, Nq must be 1, c = (len-1)/block.
+ *                Candidates never exceed C.
+ * workspace:     needed only for decode rows (see sas_workspace_bytes).
+ * Errors: SAS_EINVAL (pointers, sizes, topk < 0, heads_per_row < 1);
+ *         SAS_EUNSUPPORTED for topk > 256 or C > 16384; SAS_EWORKSPACE.
+ */
+int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len,
+                    int B, int Hkv, int heads_per_row, int Nq, int C, int block,
+                    int topk, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * sas_gated_attn_fwd -- SAS gated attention forward (blog 方法核心; review
+ *   "New Approach", paper Eq. 9; tiled FlashAttention-style evaluation with
+ *   an online softmax: review "A Concrete Walkthrough", kernel paragraph).
+ *   z[t,j] = scale * q_t . k_j + bias, bias = 0 on the own block (j <= t),
+ *   log g[t,m] = s[t,m] - LSE_s(t) on a gated history block m, -inf
+ *   elsewhere; o = softmax(z) v.
+ * scores:  fp32 [B,Hq,N,C] selector scores (columns m >= c(t) are not read).
+ * idx:     NULL for full scope, else int32 [B,Hkv,N,topk] (sparse scope).
+ * o:       [B,Hq,N,D] output in dtype.
+ * lse:     fp32 [B,Hq,N] output, log-sum-exp of z per row.
+ * lse_s:   fp32 [B,Hq,N] output, log-sum-exp of the row's history scores
+ *          (-inf for rows without history).
+ * N must be >= 0; a last block shorter than `block` is allowed.
+ * Errors: SAS_EINVAL, SAS_EUNSUPPORTED (D outside {64, 128}; sparse scope
+ *         with C > 16384 or topk > 256), SAS_EWORKSPACE.
+ */
+int sas_gated_attn_fwd(const void* q, const void* k, const void* v,
+                       const float* scores, const int32_t* idx, void* o,
+                       float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
+                       int D, int block, int topk, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sas_gated_attn_bwd -- gradients of the forward for an upstream dO
+ *   (blog 方法核心, inner-gate gradient; review "Why the Four Design Choices
+ *   Matter", paper Eq. 5; gradient path o -> g -> s of review "A Concrete
+ *   Walkthrough", Step 5).
+ *   With P = softmax(z), Delta = rowsum(dO * o), dZ = P * (dO V^T - Delta):
+ *     dq = scale dZ K,  dk = scale dZ^T Q,  dv = P^T dO  (dk, dv summed over the
+ *     query heads sharing a KV head); dq, dk, dv are taken at fixed s.
+ *     dbeta[t,m] = sum of dZ over the keys of gated history block m,
+ *     ds[t,m] = dbeta[t,m] - g[t,m] * sum_m' dbeta[t,m']   (m < c(t)), else 0.
+ * o, lse, lse_s: the forward's outputs for the same inputs.
+ * ds:      fp32 [B,Hq,N,C] output (dense: also unselected history blocks).
+ * dq, dk, dv: outputs in dtype.
+ * Errors: as for the forward.
+ */
+int sas_gated_attn_bwd(const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* scores,
+                       const int32_t* idx, const float* lse, const float* lse_s,
+                       void* dq, void* dk, void* dv, float* ds, int B, int Hq,
+                       int Hkv, int N, int D, int block, int topk, float scale,
+                       int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * sas_sparse_decode -- one decode step: each sequence's new token attends to
+ *   its current block plus the selected history blocks, with no gate
+ *   (review "A Concrete Walkthrough", Step 6, paper Alg. 2; block-sparse
+ *   attention of blog 问题动机 and review "Background", paper Eq. 2).
+ * q:          [B,Hq,D]; k_cache, v_cache [B,Hkv,L_max,D]; cache_len int32 [B]
+ *             on the device.
+ * idx:        int32 [B,Hkv,topk] selected history blocks, or NULL for dense
+ *             decode over every cached position.
+ * o:          [B,Hq,D] output in dtype (zeros for idle sequences).
+ * lse:        optional fp32 [B,Hq] output (-inf for idle sequences).
+ * Errors: SAS_EINVAL, SAS_EUNSUPPORTED (D outside {64, 128}, more than 16
+ *         query heads per KV head, topk > 256), SAS_EWORKSPACE.
+ */
+int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_len, const int32_t* idx, void* o,
+                      float* lse, int B, int Hq, int Hkv, int L_max, int D,
+                      int block, int topk, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sas_workspace_bytes -- device workspace a call with these sizes needs
+ *   (0 if none).  `n_or_lmax` is N for training calls and L_max for decode;
+ *   `topk` < 0 means full scope / dense decode.  Returns (size_t)-1 for
+ *   invalid sizes.
+ */
+size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n_or_lmax, int D,
+                           int block, int topk, int dtype);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* sas_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int sas_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H_ */

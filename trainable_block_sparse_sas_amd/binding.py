@@ -1,0 +1,180 @@
+"""ctypes binding of libsas (C ABI in include/sas.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, reads their shapes, passes raw device pointers and the current
+HIP stream to the library call of the same name, and raises SasError on a
+non-zero status.  No computation happens here and there is no fallback: if
+libsas.so is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SAS_LIB", os.path.join(_HERE, "libsas.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libsas.so not found at {LIB_PATH}; build it with "
+                      f"`python -m trainable_block_sparse_sas_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+SAS_OK, SAS_EINVAL, SAS_EUNSUPPORTED, SAS_EHIP, SAS_EWORKSPACE = 0, -1, -2, -3, -4
+SAS_F32, SAS_BF16 = 0, 1
+SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE = 1, 2, 3, 4, 5
+
+EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
+            "sas_sparse_decode", "sas_workspace_bytes", "sas_last_error", "sas_abi_version")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.sas_score_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+_lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_workspace_bytes.argtypes = [_i] * 9
+_lib.sas_workspace_bytes.restype = _sz
+_lib.sas_last_error.restype = ctypes.c_char_p
+_lib.sas_abi_version.restype = _i
+for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
+              "sas_sparse_decode"):
+    getattr(_lib, _name).restype = _i
+
+
+class SasError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libsas tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_EMPTY_IDX = {}
+
+
+def _idx_ptr(idx: Optional[torch.Tensor]):
+    """idx pointer: NULL only for full scope.  A zero-width index tensor (topk 0)
+    has no storage, so a one-element placeholder on its device stands in."""
+    if idx is None:
+        return None
+    if idx.numel() == 0:
+        dev = idx.device
+        if dev not in _EMPTY_IDX:
+            _EMPTY_IDX[dev] = torch.full((1,), -1, dtype=torch.int32, device=dev)
+        return ctypes.c_void_p(_EMPTY_IDX[dev].data_ptr())
+    return _p(idx)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SAS_F32
+    if t.dtype == torch.bfloat16:
+        return SAS_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(code: int):
+    if code != SAS_OK:
+        raise SasError(code, _lib.sas_last_error().decode())
+
+
+def sas_abi_version() -> int:
+    return _lib.sas_abi_version()
+
+
+def sas_last_error() -> str:
+    return _lib.sas_last_error().decode()
+
+
+def sas_workspace_bytes(op: int, B: int, Hq: int, Hkv: int, n_or_lmax: int, D: int, block: int,
+                        topk: int, dtype: int) -> int:
+    return int(_lib.sas_workspace_bytes(op, B, Hq, Hkv, n_or_lmax, D, block, topk, dtype))
+
+
+def workspace(op, B, Hq, Hkv, n_or_lmax, D, block, topk, dtype, device="cuda"):
+    """A byte tensor of the size sas_workspace_bytes asks for (None if 0)."""
+    n = sas_workspace_bytes(op, B, Hq, Hkv, n_or_lmax, D, block, topk, dtype)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sas_score_blocks(q, k, kbar, scores, cache_len, block, scale, group_sum=False, L=None,
+                     stream=None):
+    """Training: q [B,Hq,N,D], k [B,Hkv,N,D] or None, kbar [B,Hkv,C,D], scores fp32.
+    Decode (cache_len given): q [B,Hq,D], k the cache or None, L = cache capacity."""
+    B, Hq, D = q.shape[0], q.shape[1], q.shape[-1]
+    Hkv = kbar.shape[1]
+    if cache_len is None:
+        Nq = q.shape[2]
+        L = Nq
+    else:
+        Nq = 1
+        if L is None:
+            L = k.shape[2] if k is not None else kbar.shape[2] * block
+    _check(_lib.sas_score_blocks(_p(q), _p(k), _p(kbar), _p(scores), _p(cache_len), B, Hq, Hkv,
+                                 Nq, L, D, block, scale, int(bool(group_sum)), _dt(q),
+                                 _stream(stream)))
+
+
+def sas_topk_select(scores, idx, cache_len, heads_per_row, block, workspace=None, stream=None):
+    """scores fp32 [B, Hkv*hpr, Nq, C] (decode: [B, Hkv*hpr, C]); idx int32 [B,Hkv,Nq,K] / [B,Hkv,K]."""
+    if cache_len is None:
+        B, H, Nq, C = scores.shape
+    else:
+        B, H, C = scores.shape
+        Nq = 1
+    Hkv = H // heads_per_row
+    topk = idx.shape[-1]
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_topk_select(_p(scores), _p(idx), _p(cache_len), B, Hkv, heads_per_row, Nq, C,
+                                block, topk, _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_fwd(q, k, v, scores, idx, o, lse, lse_s, block, scale, workspace=None,
+                       stream=None):
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_gated_attn_fwd(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(o), _p(lse),
+                                   _p(lse_s), B, Hq, Hkv, N, D, block, topk, scale, _dt(q),
+                                   _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, block, scale,
+                       workspace=None, stream=None):
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_gated_attn_bwd(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(scores), _idx_ptr(idx),
+                                   _p(lse), _p(lse_s), _p(dq), _p(dk), _p(dv), _p(ds), B, Hq, Hkv,
+                                   N, D, block, topk, scale, _dt(q), _p(workspace), wsb,
+                                   _stream(stream)))
+
+
+def sas_sparse_decode(q, k_cache, v_cache, cache_len, idx, o, lse, block, scale, workspace=None,
+                      stream=None):
+    B, Hq, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_sparse_decode(_p(q), _p(k_cache), _p(v_cache), _p(cache_len), _idx_ptr(idx), _p(o),
+                                  _p(lse), B, Hq, Hkv, L, D, block, topk, scale, _dt(q),
+                                  _p(workspace), wsb, _stream(stream)))

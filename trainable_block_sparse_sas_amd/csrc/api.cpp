@@ -1,0 +1,221 @@
+// C ABI of libsas: argument validation on the host, then dispatch to the
+// kernel launchers.  Nothing here touches the GPU before every check passed.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sas.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SAS_EHIP, "%s: HIP error %d (%s)", what, int(e), hipGetErrorString(e));
+  g_error.clear();
+  return SAS_OK;
+}
+
+constexpr int kMaxTopk = 256;
+constexpr int kMaxBlocks = 16384;
+constexpr int kMaxGroupDecode = 16;
+
+int check_common(int B, int Hq, int Hkv, int n, int D, int block, int dtype, const char* what) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || n < 0)
+    return fail(SAS_EINVAL, "%s: sizes must be non-negative and Hkv >= 1 (B=%d Hq=%d Hkv=%d N=%d)",
+                what, B, Hq, Hkv, n);
+  if (Hq % Hkv != 0) return fail(SAS_EINVAL, "%s: Hq (%d) must be a multiple of Hkv (%d)", what, Hq, Hkv);
+  if (block < 1) return fail(SAS_EINVAL, "%s: block must be >= 1 (got %d)", what, block);
+  if (dtype != SAS_F32 && dtype != SAS_BF16) return fail(SAS_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (D != 64 && D != 128) return fail(SAS_EUNSUPPORTED, "%s: head dim %d not supported (64 or 128)", what, D);
+  return SAS_OK;
+}
+
+bool empty(int B, int Hq, int n) { return B == 0 || Hq == 0 || n == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sas_last_error(void) { return g_error.c_str(); }
+
+int sas_abi_version(void) { return 100; }
+
+size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
+                           int dtype) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || n < 0 || block < 1 || (Hq % Hkv) != 0) return size_t(-1);
+  sas::Dims d{B, Hq, Hkv, n, D, block, n / block};
+  const bool bf16 = dtype == SAS_BF16;
+  switch (op) {
+    case SAS_OP_SCORE:
+    case SAS_OP_TOPK:
+      return 0;
+    case SAS_OP_FWD:
+      return sas::fwd_workspace(d, topk, bf16);
+    case SAS_OP_BWD:
+      return sas::bwd_workspace(d, topk, bf16);
+    case SAS_OP_DECODE:
+      return sas::decode_workspace(B, Hq, Hkv, n, D, block, topk);
+    default:
+      return size_t(-1);
+  }
+}
+
+int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
+                     const int32_t* cache_len, int B, int Hq, int Hkv, int Nq, int L, int D,
+                     int block, float scale, int group_sum, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, L, D, block, dtype, "sas_score_blocks");
+  if (st) return st;
+  if (Nq < 0) return fail(SAS_EINVAL, "sas_score_blocks: Nq must be >= 0");
+  const int C = L / block;
+  if (cache_len) {
+    if (Nq != 1 && !(B == 0 || Hq == 0)) return fail(SAS_EINVAL, "sas_score_blocks: decode mode needs Nq == 1 (got %d)", Nq);
+    if (Hq / Hkv > kMaxGroupDecode)
+      return fail(SAS_EUNSUPPORTED, "sas_score_blocks: at most %d query heads per KV head in decode mode", kMaxGroupDecode);
+  } else if (Nq != L) {
+    return fail(SAS_EINVAL, "sas_score_blocks: training mode needs Nq == L (got Nq=%d L=%d)", Nq, L);
+  }
+  if (empty(B, Hq, Nq) && !(k && B > 0 && C > 0)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !kbar || !scores) return fail(SAS_EINVAL, "sas_score_blocks: q, kbar and scores must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SAS_BF16;
+  if (k) {
+    hipError_t e = sas::launch_pool(k, kbar, B, Hkv, L, D, block, C, bf16, s);
+    if (e != hipSuccess) return hip_status(e, "sas_score_blocks (pool)");
+  }
+  if (empty(B, Hq, Nq)) return hip_status(hipSuccess, "");
+  hipError_t e;
+  if (cache_len) {
+    e = sas::launch_score_decode(q, kbar, scores, cache_len, B, Hq, Hkv, L, D, block, C, scale,
+                                 group_sum != 0, bf16, s);
+  } else {
+    sas::Dims d{B, Hq, Hkv, L, D, block, C};
+    e = sas::launch_score_train(q, kbar, scores, d, scale, group_sum != 0, bf16, s);
+  }
+  return hip_status(e, "sas_score_blocks");
+}
+
+int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
+                    int heads_per_row, int Nq, int C, int block, int topk, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || Hkv < 1 || Nq < 0 || C < 0)
+    return fail(SAS_EINVAL, "sas_topk_select: invalid sizes (B=%d Hkv=%d Nq=%d C=%d)", B, Hkv, Nq, C);
+  if (heads_per_row < 1) return fail(SAS_EINVAL, "sas_topk_select: heads_per_row must be >= 1");
+  if (block < 1) return fail(SAS_EINVAL, "sas_topk_select: block must be >= 1");
+  if (topk < 0) return fail(SAS_EINVAL, "sas_topk_select: topk must be >= 0");
+  if (topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "sas_topk_select: topk %d > %d", topk, kMaxTopk);
+  if (C > kMaxBlocks) return fail(SAS_EUNSUPPORTED, "sas_topk_select: C %d > %d", C, kMaxBlocks);
+  if (cache_len && Nq != 1 && B > 0) return fail(SAS_EINVAL, "sas_topk_select: decode rows need Nq == 1");
+  if (B == 0 || Nq == 0 || topk == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!scores || !idx) return fail(SAS_EINVAL, "sas_topk_select: scores and idx must be non-NULL");
+  hipError_t e = sas::launch_topk(scores, idx, cache_len, B, Hkv, heads_per_row, Nq, C, block, topk,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_topk_select");
+}
+
+static int check_attn(const char* what, int B, int Hq, int Hkv, int N, int D, int block,
+                      const int32_t* idx, int topk, int dtype) {
+  int st = check_common(B, Hq, Hkv, N, D, block, dtype, what);
+  if (st) return st;
+  if (idx) {
+    if (topk < 0) return fail(SAS_EINVAL, "%s: topk must be >= 0 with idx", what);
+    if (topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "%s: topk %d > %d", what, topk, kMaxTopk);
+    if (N / block > kMaxBlocks) return fail(SAS_EUNSUPPORTED, "%s: sparse scope with more than %d blocks", what, kMaxBlocks);
+  }
+  return SAS_OK;
+}
+
+int sas_gated_attn_fwd(const void* q, const void* k, const void* v, const float* scores,
+                       const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq,
+                       int Hkv, int N, int D, int block, int topk, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn("sas_gated_attn_fwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (st) return st;
+  if (empty(B, Hq, N)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k || !v || !scores || !o || !lse || !lse_s)
+    return fail(SAS_EINVAL, "sas_gated_attn_fwd: q, k, v, scores, o, lse, lse_s must be non-NULL");
+  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
+  const bool bf16 = dtype == SAS_BF16;
+  const size_t need = sas::fwd_workspace(d, idx ? topk : -1, bf16);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SAS_EWORKSPACE, "sas_gated_attn_fwd: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  hipError_t e = sas::launch_fwd(q, k, v, scores, idx, o, lse, lse_s, d, idx ? topk : 0, scale,
+                                 bf16, workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_gated_attn_fwd");
+}
+
+int sas_gated_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* scores, const int32_t* idx,
+                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
+                       float* ds, int B, int Hq, int Hkv, int N, int D, int block, int topk,
+                       float scale, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_attn("sas_gated_attn_bwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (st) return st;
+  if (empty(B, Hq, N)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k || !v || !o || !dout || !scores || !lse || !lse_s || !dq || !dk || !dv || !ds)
+    return fail(SAS_EINVAL, "sas_gated_attn_bwd: every tensor pointer except idx must be non-NULL");
+  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
+  const bool bf16 = dtype == SAS_BF16;
+  const size_t need = sas::bwd_workspace(d, idx ? topk : -1, bf16);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SAS_EWORKSPACE, "sas_gated_attn_bwd: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  hipError_t e = sas::launch_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d,
+                                 idx ? topk : 0, scale, bf16, workspace,
+                                 static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_gated_attn_bwd");
+}
+
+int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_len, const int32_t* idx, void* o, float* lse, int B,
+                      int Hq, int Hkv, int L_max, int D, int block, int topk, float scale,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, "sas_sparse_decode");
+  if (st) return st;
+  if (Hkv > 0 && Hq / Hkv > kMaxGroupDecode)
+    return fail(SAS_EUNSUPPORTED, "sas_sparse_decode: at most %d query heads per KV head", kMaxGroupDecode);
+  if (idx && topk < 0) return fail(SAS_EINVAL, "sas_sparse_decode: topk must be >= 0 with idx");
+  if (idx && topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "sas_sparse_decode: topk %d > %d", topk, kMaxTopk);
+  if (B == 0 || Hq == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k_cache || !v_cache || !cache_len || !o)
+    return fail(SAS_EINVAL, "sas_sparse_decode: q, caches, cache_len and o must be non-NULL");
+  const size_t need = sas::decode_workspace(B, Hq, Hkv, L_max, D, block, idx ? topk : -1);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAS_EWORKSPACE, "sas_sparse_decode: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  hipError_t e = sas::launch_decode(q, k_cache, v_cache, cache_len, idx, o, lse, B, Hq, Hkv, L_max,
+                                    D, block, idx ? topk : -1, scale, dtype == SAS_BF16, workspace,
+                                    static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_sparse_decode");
+}
+
+}  // extern "C"

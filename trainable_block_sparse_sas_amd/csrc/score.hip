@@ -1,0 +1,226 @@
+// Selector stage: block mean-pooling of keys and block scores.
+//
+// Pooled block summaries (jaehun.me review, "Our Perspective", Limitations)
+// K̄_m = mean of the keys of block m; the selector score of history block m for
+// a query is s_m = scale * q . K̄_m (one score per block: review "Background",
+// paper Eq. 3).  Columns that are not history blocks of the query hold -inf.
+#include "common.h"
+#include "internal.h"
+
+namespace sas {
+namespace {
+
+// One workgroup per (block m, KV head g, batch b); thread d sums the b tokens of
+// column d in fp32 and writes the mean in the storage type.
+template <typename T>
+__global__ void pool_kernel(const T* __restrict__ k, T* __restrict__ kbar, int Hkv, int L, int D,
+                            int block, int C) {
+  const int m = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const T* src = k + ((size_t(b) * Hkv + g) * L + size_t(m) * block) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < block; ++j) acc += to_f32(src[size_t(j) * D + d]);
+    kbar[((size_t(b) * Hkv + g) * C + m) * D + d] = from_f32<T>(acc / float(block));
+  }
+}
+
+// Training scores: a workgroup owns 64 query rows of one KV head and loops over
+// that head's G query heads and over 64-wide tiles of blocks.  Tiles are staged
+// in LDS as fp32; each thread produces 4 rows x 4 blocks per tile.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ q,
+                                                          const T* __restrict__ kbar,
+                                                          float* __restrict__ out, int Hq, int Hkv,
+                                                          int N, int C, int block, float scale,
+                                                          int group_sum) {
+  constexpr int TR = 64, TM = 64, PAD = 1;
+  __shared__ float qs[TR][D + PAD];
+  __shared__ float ks[TM][D + PAD];
+  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int r0 = (tid / 16) * 4;  // 16 x 16 thread grid, 4 x 4 outputs each
+  const int c0 = (tid % 16) * 4;
+  const int t0 = tile * TR;
+  for (int mt = 0; mt < C; mt += TM) {
+    float usum[4][4];
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+      __syncthreads();
+      for (int i = tid; i < TR * D; i += 256) {
+        int r = i / D, d = i % D;
+        int t = t0 + r;
+        qs[r][d] = t < N ? to_f32(q[((size_t(b) * Hq + h) * N + t) * D + d]) : 0.f;
+      }
+      if (h == g * G) {
+        for (int i = tid; i < TM * D; i += 256) {
+          int r = i / D, d = i % D;
+          int m = mt + r;
+          ks[r][d] = m < C ? to_f32(kbar[((size_t(b) * Hkv + g) * C + m) * D + d]) : 0.f;
+        }
+      }
+      __syncthreads();
+      float acc[4][4] = {};
+      for (int d = 0; d < D; ++d) {
+        float a[4], w[4];
+        for (int i = 0; i < 4; ++i) a[i] = qs[r0 + i][d];
+        for (int j = 0; j < 4; ++j) w[j] = ks[c0 + j][d];
+        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+      }
+      for (int i = 0; i < 4; ++i) {
+        int t = t0 + r0 + i;
+        if (t >= N) continue;
+        int c = t / block;
+        for (int j = 0; j < 4; ++j) {
+          int m = mt + c0 + j;
+          if (m >= C) continue;
+          float sv = m < c ? acc[i][j] * scale : kNegInf;
+          if (group_sum) {
+            usum[i][j] = (h == g * G) ? sv : usum[i][j] + sv;
+          } else {
+            out[((size_t(b) * Hq + h) * N + t) * C + m] = sv;
+          }
+        }
+      }
+    }
+    if (group_sum) {
+      for (int i = 0; i < 4; ++i) {
+        int t = t0 + r0 + i;
+        if (t >= N) continue;
+        for (int j = 0; j < 4; ++j) {
+          int m = mt + c0 + j;
+          if (m < C) out[((size_t(b) * Hkv + g) * N + t) * C + m] = usum[i][j];
+        }
+      }
+    }
+  }
+}
+
+// Decode scores: one query token per sequence scans the pooled keys of its KV
+// head.  A K̄ row (D values) is read by LPR lanes with 16-byte loads, so a wave
+// covers 64/LPR rows per load; partial dots are reduced across those lanes.
+// The G query heads of the group are handled together; with group_sum the fp32
+// scores are added in head-index order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ kbar, float* __restrict__ out,
+    const int32_t* __restrict__ cache_len, int Hq, int Hkv, int L, int C, int block, float scale,
+    int group_sum) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LPR = D / VEC;        // lanes per K̄ row
+  constexpr int RPW = 64 / LPR;       // rows per wave per load
+  constexpr int MAXG = 16;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR, rsub = lane / LPR;
+  int len = cache_len[b];
+  len = len > L ? L : len;
+  const int c = len > 0 ? (len - 1) / block : 0;
+  const int c_eff = c < C ? c : C;
+  float qv[MAXG][VEC];
+  for (int h = 0; h < G; ++h)
+    for (int i = 0; i < VEC; ++i)
+      qv[h][i] = to_f32(q[(size_t(b) * Hq + g * G + h) * D + sub * VEC + i]);
+  const int rows_per_wg = RPW * 4 * 4;  // 4 waves, 4 loads per wave
+  const int m_base = blockIdx.x * rows_per_wg;
+  for (int it = 0; it < 4; ++it) {
+    const int m = m_base + (it * 4 + wave) * RPW + rsub;
+    float dots[MAXG];
+    const bool in = m < C;
+    T kv[VEC];
+    if (in && m < c_eff) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(
+          kbar + ((size_t(b) * Hkv + g) * C + m) * D + sub * VEC);
+      const T* p = reinterpret_cast<const T*>(&raw);
+      for (int i = 0; i < VEC; ++i) kv[i] = p[i];
+    } else {
+      for (int i = 0; i < VEC; ++i) kv[i] = T(0);
+    }
+    for (int h = 0; h < G; ++h) {
+      float a = 0.f;
+      for (int i = 0; i < VEC; ++i) a = fmaf(qv[h][i], to_f32(kv[i]), a);
+      for (int off = LPR / 2; off >= 1; off >>= 1) a += shfl_xor(a, off);
+      dots[h] = a;
+    }
+    if (in && sub == 0) {
+      if (group_sum) {
+        float u = kNegInf;
+        if (m < c_eff) {
+          u = dots[0] * scale;
+          for (int h = 1; h < G; ++h) u = u + dots[h] * scale;
+        }
+        out[(size_t(b) * Hkv + g) * C + m] = u;
+      } else {
+        for (int h = 0; h < G; ++h)
+          out[(size_t(b) * Hq + g * G + h) * C + m] = m < c_eff ? dots[h] * scale : kNegInf;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, int block, int C,
+                       bool bf16, hipStream_t s) {
+  if (C == 0 || B == 0) return hipSuccess;
+  dim3 grid(C, Hkv, B);
+  if (bf16)
+    hipLaunchKernelGGL(pool_kernel<bf16_t>, grid, dim3(D), 0, s, (const bf16_t*)k, (bf16_t*)kbar,
+                       Hkv, L, D, block, C);
+  else
+    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(D), 0, s, (const float*)k, (float*)kbar, Hkv,
+                       L, D, block, C);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void score_train_t(const void* q, const void* kbar, float* scores, const Dims& d,
+                          float scale, bool group_sum, hipStream_t s) {
+  dim3 grid((d.N + 63) / 64, d.Hkv, d.B);
+  hipLaunchKernelGGL((score_train_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
+                     (const T*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale,
+                     group_sum ? 1 : 0);
+}
+
+hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
+                              float scale, bool group_sum, bool bf16, hipStream_t s) {
+  if (d.N == 0 || d.B == 0 || d.C == 0) return hipSuccess;
+  if (bf16) {
+    if (d.D == 64) score_train_t<bf16_t, 64>(q, kbar, scores, d, scale, group_sum, s);
+    else score_train_t<bf16_t, 128>(q, kbar, scores, d, scale, group_sum, s);
+  } else {
+    if (d.D == 64) score_train_t<float, 64>(q, kbar, scores, d, scale, group_sum, s);
+    else score_train_t<float, 128>(q, kbar, scores, d, scale, group_sum, s);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void score_decode_t(const void* q, const void* kbar, float* scores, const int32_t* cl,
+                           int B, int Hq, int Hkv, int L, int block, int C, float scale,
+                           bool group_sum, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int RPW = 64 / (D / VEC);
+  const int rows_per_wg = RPW * 16;
+  dim3 grid((C + rows_per_wg - 1) / rows_per_wg, Hkv, B);
+  hipLaunchKernelGGL((score_decode_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
+                     (const T*)kbar, scores, cl, Hq, Hkv, L, C, block, scale, group_sum ? 1 : 0);
+}
+
+hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
+                               const int32_t* cache_len, int B, int Hq, int Hkv, int L, int D,
+                               int block, int C, float scale, bool group_sum, bool bf16,
+                               hipStream_t s) {
+  if (B == 0 || C == 0) return hipSuccess;
+  if (bf16) {
+    if (D == 64) score_decode_t<bf16_t, 64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+    else score_decode_t<bf16_t, 128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+  } else {
+    if (D == 64) score_decode_t<float, 64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+    else score_decode_t<float, 128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sas
