@@ -319,14 +319,15 @@ def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows):
     return dq, ds
 
 
-def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024):
+def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024, rows=None):
     """dk and dv of selected keys of KV head g in batch b.
 
     dk[j] = scale * sum_{h in group(g)} sum_t dz[h,t,j] q[h,t];
     dv[j] = sum_{h in group(g)} sum_t p[h,t,j] dO[h,t]; the sums run over every
-    query row (rows that do not attend key j contribute p = dz = 0).  Rows are
-    visited in chunks only to bound memory; each row is computed exactly as in
-    `gated_attention_backward`.  Returns (dk [J,D], dv [J,D]).
+    query row (rows that do not attend key j contribute p = dz = 0), or over
+    `rows` when given, which must then hold every row that attends the keys.
+    Rows are visited in chunks only to bound memory; each row is computed
+    exactly as in `gated_attention_backward`.  Returns (dk [J,D], dv [J,D]).
     """
     B, Hq, N, D = q.shape
     G = Hq // k.shape[1]
@@ -334,9 +335,10 @@ def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024)
     dk = np.zeros((len(keys), D))
     dv = np.zeros((len(keys), D))
     kmin = int(keys.min())
+    all_rows = np.arange(kmin, N) if rows is None else np.asarray(rows)
     for h in range(g * G, (g + 1) * G):
-        for r0 in range(kmin, N, row_chunk):
-            rows = np.arange(r0, min(N, r0 + row_chunk))
+        for r0 in range(0, len(all_rows), row_chunk):
+            rows = all_rows[r0:r0 + row_chunk]
             _, _, _, _, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
             vh = _as64(v[b, g])
             doh = _as64(do[b, h, rows])

@@ -1,0 +1,176 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration bench.py times.
+
+The oracle computes sampled outputs one by one (rows for o, lse, lse_s, dq, ds;
+keys for dk, dv), plus whole-tensor checks where it is cheap (pooled keys,
+Top-K, decode).  Selector scores and Top-K indices fed to the attention calls
+are the oracle's, so every entry point sees identical inputs; the all-GPU
+chain is checked separately, where only near-tie flips of the Top-K may differ.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sas_oracle as orc
+from tests.gpu_util import kbar_close, max_abs, normwise, to64
+from trainable_block_sparse_sas_amd.inputs import WORKLOADS, decode_inputs, training_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+if torch.cuda.is_available():
+    from trainable_block_sparse_sas_amd import binding as sas
+    from trainable_block_sparse_sas_amd.pipeline import DecodeStep, TrainStep
+
+DEV = "cuda"
+
+
+def _oracle_scores_f32(q64, kbar_r, block, scale):
+    """Oracle scores for every row, one head at a time, stored as fp32."""
+    B, Hq, N, D = q64.shape
+    C = kbar_r.shape[2]
+    out = np.empty((B, Hq, N, C), dtype=np.float32)
+    pos = np.broadcast_to(np.arange(N), (1, N))
+    G = Hq // kbar_r.shape[1]
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h] = orc.block_scores(q64[b:b + 1, h:h + 1], kbar_r[b:b + 1, h // G:h // G + 1], block, scale,
+                                         pos)[0, 0].astype(np.float32)
+    return out
+
+
+def _sample_rows(N, block, n=24, seed=0):
+    r = np.random.default_rng(seed)
+    fixed = [0, 1, block - 1, block, block + 5, N // 2, N - block - 1, N - 2, N - 1]
+    return np.unique(np.concatenate([fixed, r.integers(0, N, size=n)]))
+
+
+@pytest.mark.parametrize("wi", [1, 2], ids=["train-8k-full", "train-32k-sparse"])
+def test_training_fullsize(wi):
+    w = WORKLOADS[wi]
+    dt = w.torch_dtype
+    q, k, v, do = training_inputs(w, device=DEV)
+    q64, k64 = to64(q), to64(k)
+    G = w.Hq // w.Hkv
+    # Pooled keys: GPU vs oracle (at most one bf16 step apart).
+    step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, dt)
+    step.select(q, k)
+    torch.cuda.synchronize()
+    kbar = orc.pool_block_keys(k64, w.block)
+    kbar_r = to64(torch.tensor(kbar).to(dt))
+    kbar_close(to64(step.kbar), kbar_r)
+    gpu_chain_idx = None if w.topk is None else step.idx.cpu().numpy()
+    s32 = _oracle_scores_f32(q64, kbar_r, w.block, w.scale)
+    rows = _sample_rows(w.N, w.block)
+    # GPU scores from the oracle's pooled keys, sampled rows.
+    sas.sas_score_blocks(q, None, torch.tensor(kbar_r).to(dt).to(DEV), step.scores, None, w.block, w.scale)
+    torch.cuda.synchronize()
+    normwise(to64(step.scores[:, :, rows]), s32[:, :, rows].astype(np.float64), 1e-5, "scores")
+    scores = torch.tensor(s32).to(DEV)
+    idx = None
+    g_chk = w.Hkv - 1
+    if w.topk is not None:
+        sas.sas_topk_select(scores, step.idx, None, G, w.block)
+        torch.cuda.synchronize()
+        gidx = step.idx.cpu().numpy()
+        pos = np.arange(w.N)[None, :] // w.block
+        ref_g = orc.topk_select(s32[:, g_chk * G:(g_chk + 1) * G], G, pos, w.topk)
+        assert np.array_equal(gidx[:, g_chk:g_chk + 1], ref_g), "topk (one KV head, every row)"
+        ref_rows = orc.topk_select(s32[:, :, rows], G, pos[:, rows], w.topk)
+        assert np.array_equal(gidx[:, :, rows], ref_rows), "topk (sampled rows, every KV head)"
+        idx = gidx
+        # The all-GPU chain (GPU pooled keys and scores): rows may differ only at near-ties.
+        diff = np.any(gpu_chain_idx != gidx, axis=-1)
+        assert diff.mean() < 1e-3, f"chain Top-K differs on {diff.mean():.2%} of rows"
+    idx_t = None if idx is None else torch.tensor(idx).to(DEV)
+    step.forward(q, k, v, scores, idx_t)
+    step.backward(q, k, v, do, scores, idx_t)
+    torch.cuda.synchronize()
+    v64, do64, s64 = to64(v), to64(do), s32.astype(np.float64)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(q64, k64, v64, s64, idx, w.block, w.scale, rows=rows)
+    max_abs(to64(step.o[:, :, rows]), o_ref, 2e-2, "o")
+    normwise(to64(step.lse[:, :, rows]), lse_ref, 1e-4, "lse")
+    normwise(to64(step.lse_s[:, :, rows]), lses_ref, 1e-4, "lse_s")
+    for h in (0, w.Hq // 2 + 1, w.Hq - 1):
+        dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, h, rows)
+        normwise(to64(step.dq[0, h, rows]), dq_r, 2e-2, f"dq h{h}")
+        normwise(to64(step.ds[0, h, rows]), ds_r, 2e-2, f"ds h{h}")
+    if idx is None:
+        keys = np.array([0, 1, w.block - 1, w.block, w.N // 2 + 3, w.N - w.block, w.N - 1])
+        attend = None
+    else:
+        # late blocks (few selecting rows keep the oracle quick) plus the last block
+        C = w.C
+        keys = np.array([(C - 90) * w.block + 3, (C - 7) * w.block, (C - 2) * w.block + 63, w.N - 1])
+        kb = np.unique(keys // w.block)
+        tsel = np.any(np.isin(idx[0, g_chk], kb), axis=-1)  # tokens selecting one of the blocks
+        own = np.isin(np.arange(w.N) // w.block, kb)
+        attend = np.nonzero(tsel | own)[0]
+    dk_r, dv_r = orc.key_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, g_chk, keys,
+                                   rows=attend)
+    normwise(to64(step.dk[0, g_chk, keys]), dk_r, 2e-2, "dk")
+    normwise(to64(step.dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
+
+
+@pytest.mark.parametrize("wi", [3, 4], ids=["decode-128k-b8", "decode-512k-b1"])
+def test_decode_fullsize(wi):
+    w = WORKLOADS[wi]
+    dt = w.torch_dtype
+    q, kc, vc, lens = decode_inputs(w, device=DEV)
+    G = w.Hq // w.Hkv
+    step = DecodeStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, dt)
+    step.pool(kc)
+    step.select(q, lens)  # the all-GPU chain
+    step.attend(q, kc, vc, lens)
+    torch.cuda.synchronize()
+    chain_idx = step.idx.cpu().numpy()
+    chain_o = to64(step.o)
+    q64 = to64(q)
+    lens_np = lens.cpu().numpy()
+    # Oracle pooled keys, one (sequence, KV head) at a time.
+    kbar = np.empty((w.B, w.Hkv, w.C, w.D))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            kbar[b, g] = orc.pool_block_keys(to64(kc[b:b + 1, g:g + 1]), w.block)[0, 0]
+    kbar_r = to64(torch.tensor(kbar).to(dt))
+    kbar_close(to64(step.kbar), kbar_r)
+    u_ref = orc.decode_scores(q64, kbar_r, lens_np, w.block, w.scale, True)
+    sas.sas_score_blocks(q, None, torch.tensor(kbar_r).to(dt).to(DEV), step.u, lens, w.block, w.scale,
+                         group_sum=True, L=w.N)
+    torch.cuda.synchronize()
+    normwise(to64(step.u), u_ref.astype(np.float64), 1e-5, "u")
+    c = (lens_np - 1) // w.block
+    idx_ref = orc.topk_select(u_ref[:, :, None, :], 1, c[:, None], w.topk)[:, :, 0, :]
+    sas.sas_topk_select(torch.tensor(u_ref).to(DEV), step.idx, lens, 1, w.block)
+    torch.cuda.synchronize()
+    assert np.array_equal(step.idx.cpu().numpy(), idx_ref), "topk"
+    # Selection is non-trivial: the shifted blocks dominate the top of the ranking.
+    assert len(np.unique(idx_ref)) > w.topk
+    step.attend(q, kc, vc, lens, torch.tensor(idx_ref).to(DEV))
+    torch.cuda.synchronize()
+    kc64, vc64 = None, None
+    o_ref = np.empty((w.B, w.Hq, w.D))
+    lse_ref = np.empty((w.B, w.Hq))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            sl = slice(g * G, (g + 1) * G)
+            ob, lb = orc.sparse_decode(q64[b:b + 1, sl], to64(kc[b:b + 1, g:g + 1]), to64(vc[b:b + 1, g:g + 1]),
+                                       lens_np[b:b + 1], idx_ref[b:b + 1, g:g + 1], w.block, w.scale)
+            o_ref[b, sl], lse_ref[b, sl] = ob[0], lb[0]
+    max_abs(to64(step.o), o_ref, 2e-2, "o")
+    normwise(to64(step.lse), lse_ref, 1e-4, "lse")
+    # All-GPU chain: same selection except at near-ties, and then the same output.
+    same = np.all(chain_idx == idx_ref, axis=-1)
+    assert same.mean() > 0.95
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            if same[b, g]:
+                sl = slice(g * G, (g + 1) * G)
+                max_abs(chain_o[b, sl], o_ref[b, sl], 2e-2, "chain o")
+    if wi == 4:  # dense decode on the same inputs: every cached position
+        dstep = DecodeStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, None, dt)
+        dstep.attend(q, kc, vc, lens)
+        torch.cuda.synchronize()
+        for g in range(w.Hkv):
+            sl = slice(g * G, (g + 1) * G)
+            ob, _ = orc.sparse_decode(q64[:, sl], to64(kc[:, g:g + 1]), to64(vc[:, g:g + 1]), lens_np, None,
+                                      w.block, w.scale)
+            max_abs(to64(dstep.o[:, sl]), ob, 2e-2, "dense o")

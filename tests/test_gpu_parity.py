@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import sas_oracle as orc
-from tests.gpu_util import max_abs, normwise, to64, tolerances
+from tests.gpu_util import kbar_close, max_abs, normwise, to64, tolerances
 from trainable_block_sparse_sas_amd.inputs import Workload, decode_inputs, score_matrix, training_inputs
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +71,7 @@ def test_training_parity(case):
     if dt == torch.float32:
         normwise(gk, kbar, 1e-6, "kbar")
     else:  # fp32 mean rounded to bf16: at most one bf16 step from the rounded exact mean
-        assert np.all(np.abs(gk - kbar_r) <= np.abs(kbar_r) * 2.0 ** -7 + 1e-30), "kbar"
+        kbar_close(gk, kbar_r)
     sc_in = torch.tensor(kbar_r).to(dt).to(DEV)
     sas.sas_score_blocks(q, None, sc_in, step.scores, None, block, scale)
     torch.cuda.synchronize()
@@ -182,7 +182,7 @@ def test_decode_parity(case):
     if dt == torch.float32:
         normwise(to64(step.kbar), kbar, 1e-6, "kbar")
     else:
-        assert np.all(np.abs(to64(step.kbar) - kbar_r) <= np.abs(kbar_r) * 2.0 ** -7 + 1e-30)
+        kbar_close(to64(step.kbar), kbar_r)
     # Group-summed decode scores from the oracle's pooled keys.
     kb = torch.tensor(kbar_r).to(dt).to(DEV)
     sas.sas_score_blocks(q, None, kb, step.u, lens_d, block, scale, group_sum=True, L=L)

@@ -327,12 +327,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // -------------------------------------------------------------------- dQ ----
-template <int D, int G, int NSUB, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+template <int D, int G, int NSUB, int WAVES, bool SPARSE>
+__global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;
   constexpr int MD = D / 16;
   constexpr int TOK_SUB = 16 / G;
-  constexpr int ROWS_WG = 64 * NSUB;
+  constexpr int ROWS_WG = 16 * NSUB * WAVES;
   constexpr int TOK_WG = ROWS_WG / G;
   constexpr int CH = D / 8;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][D + PAD];
@@ -364,9 +365,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   int32_t* umask = dyn;
   int32_t* sorted = dyn + MW;
   int32_t* raw = sorted + TOK_WG * a.topk;
+  float* beta = reinterpret_cast<float*>(raw + TOK_WG * a.topk);  // [ROWS_WG][topk] (sparse)
   if (SPARSE) {
-    for (int i = tid; i < MW; i += 256) umask[i] = 0;
-    for (int i = tid; i < TOK_WG * a.topk; i += 256) {
+    for (int i = tid; i < MW; i += NT) umask[i] = 0;
+    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
       const int tok = i / a.topk, e = i % a.topk;
       const int t = t_wg0 + tok;
       int mm = -1;
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       raw[i] = mm < 0 ? 0x7fffffff : mm;
     }
     __syncthreads();
-    for (int i = tid; i < TOK_WG * a.topk; i += 256) {
+    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
       const int tok = i / a.topk, e = i % a.topk;
       const int32_t* rr = raw + tok * a.topk;
       const int mm = rr[e];
@@ -389,9 +391,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       sorted[tok * a.topk + rank] = mm;
       if (mm != 0x7fffffff) atomicOr(&umask[mm >> 5], 1 << (mm & 31));
     }
-    if (tid < 4 * NSUB) {
+    if (tid < WAVES * NSUB) {
       const int t0 = t_wg0 + tid * TOK_SUB;
       if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
+    }
+    __syncthreads();
+    // Gate bias (base 2) of every (row, selected block), read from LDS in the loop.
+    for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
+      const int r = i / a.topk, e = i % a.topk;
+      const int sg = r >> 4, rl = r & 15;
+      const int t = t_wg0 + sg * TOK_SUB + rl / G;
+      const int tok = t - t_wg0;
+      const int mm2 = sorted[tok * a.topk + e];
+      float bv = kNegInf;
+      if (t < N && mm2 != 0x7fffffff) {
+        const size_t gr = (size_t(b) * a.Hq + g * G + rl % G) * N + t;
+        bv = (a.scores[gr * C + mm2] - a.lse_s[gr]) * kLog2e;
+      }
+      beta[i] = bv;
     }
   }
   __shared__ int wg_last;
@@ -440,12 +457,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  constexpr int LOADS = (KT * CH + 255) / 256;
+  constexpr int LOADS = (KT * CH + NT - 1) / NT;
   uint4 kreg[LOADS], vreg[LOADS];
   auto load_tile = [&](int mm) {
     const int jb = mm * KT;
     for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + 256 * i;
+      const int chunk = tid + NT * i;
       const int key = chunk / CH, c8 = chunk % CH;
       const int j = jb + key;
       const bool ok = chunk < KT * CH && j < N;
@@ -455,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   auto store_tile = [&]() {
     for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + 256 * i;
+      const int chunk = tid + NT * i;
       if (chunk >= KT * CH) continue;
       const int key = chunk / CH, c8 = chunk % CH;
       *reinterpret_cast<uint4*>(&Ks[key][c8 * 8]) = kreg[i];
@@ -470,11 +487,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   int mm = next_tile(-1);
   if (mm >= 0) load_tile(mm);
+  float s_cur[NSUB];
+  for (int s = 0; s < NSUB; ++s) {
+    s_cur[s] = 0.f;
+    if (!SPARSE && mm >= 0 && mm < c_sub[s] && row_t[s] < N)
+      s_cur[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + mm];
+  }
   while (mm >= 0) {
     __syncthreads();  // previous tile's LDS reads are done
     store_tile();
     __syncthreads();
     const int m_next = next_tile(mm);
+    float s_nxt[NSUB];
+    for (int s = 0; s < NSUB; ++s) {
+      s_nxt[s] = 0.f;
+      if (!SPARSE && m_next >= 0 && m_next < c_sub[s] && row_t[s] < N)
+        s_nxt[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m_next];
+    }
     if (m_next >= 0) load_tile(m_next);
 
     bool need[NSUB];
@@ -484,12 +513,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const bool own = (mm == c_sub[s]);
       const bool hist = (mm < c_sub[s]);
       bool sel = false;
+      float bsel = kNegInf;
       if (hist && row_t[s] < N) {
         if (SPARSE) {
           const int tok = row_t[s] - t_wg0;
           const int32_t* srt = sorted + tok * a.topk;
           int cu = cursor[s];
           sel = (cu < a.topk && srt[cu] == mm);
+          if (sel) bsel = beta[((wave * NSUB + s) * 16 + lr) * a.topk + cu];
           while (cu < a.topk && srt[cu] == mm) ++cu;
           cursor[s] = cu;
         } else {
@@ -500,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       gated[s] = sel;
       float bb = kNegInf;
       if (own) bb = 0.f;
-      else if (sel) bb = (a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + mm] - lses[s]) * kLog2e;
+      else if (sel) bb = SPARSE ? bsel : (s_cur[s] - lses[s]) * kLog2e;
       bias2[s] = bb;
     }
     // S^T = K Q^T and dP^T = V dO^T.
@@ -557,6 +588,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int s = 0; s < NSUB; ++s)
           if (need[s]) dqa[s][md] = mfma16(ka, dsf[s][kk], dqa[s][md]);
       }
+    for (int s = 0; s < NSUB; ++s) s_cur[s] = s_nxt[s];
     mm = m_next;
   }
 
@@ -610,8 +642,8 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (sparse) {
-    const int tok_wg = 64 * 2 / G;
-    if (size_t(tok_wg) * topk > 4096) return false;
+    // LDS of the dQ kernel's sparse prologue (128 rows x topk bias table).
+    if (size_t(128) * topk > 8192) return false;
     if (((d.C + 32) >> 5) > 1024) return false;
   }
   return true;
@@ -630,7 +662,8 @@ size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 template <int D, int G, bool SPARSE>
 static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
   constexpr int NSUB = 1;  // rows per wave in the dQ kernel: 16 (register budget)
-  constexpr int TOK_WG = 64 * NSUB / G;
+  constexpr int WAVES = SPARSE ? 8 : 4;
+  constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   const size_t rows = size_t(B) * a.Hq * a.N;
   hipLaunchKernelGGL((bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
                      dim3(256), 0, s, a.o, a.dout, a.delta, rows);
@@ -643,8 +676,8 @@ static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
   a.n_tiles = (a.N + KT - 1) / KT;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
-  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + 2 * size_t(TOK_WG) * a.topk) * 4 : 0;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G, NSUB, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), dyn, s, a);
+  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + (2 + G) * size_t(TOK_WG) * a.topk) * 4 : 0;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), dyn, s, a);
   return hipGetLastError();
 }
 

@@ -42,12 +42,13 @@ struct FwdArgs {
   float scale;
 };
 
-template <int D, int G, int NSUB, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
+template <int D, int G, int NSUB, int WAVES, bool SPARSE>
+__global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
+  constexpr int NT = 64 * WAVES;  // threads
   constexpr int KS = D / 32;    // k-steps of S = K Q^T
   constexpr int MD = D / 16;    // output tiles of O^T
   constexpr int TOK_SUB = 16 / G;
-  constexpr int ROWS_WG = 64 * NSUB;
+  constexpr int ROWS_WG = 16 * NSUB * WAVES;
   constexpr int TOK_WG = ROWS_WG / G;
   constexpr int CH = D / 8;     // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT][D + KPAD];
@@ -103,10 +104,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int MW = (C + 32) >> 5;  // bits 0..C (the own block may be block C)
   int32_t* umask = dyn;
   int32_t* sorted = dyn + MW;                 // [TOK_WG][topk]
-  int32_t* raw = sorted + TOK_WG * a.topk;    // [TOK_WG][topk]
+  int32_t* raw = sorted + TOK_WG * a.topk;
+  float* beta = reinterpret_cast<float*>(raw + TOK_WG * a.topk);  // [ROWS_WG][topk] (sparse)    // [TOK_WG][topk]
   if (SPARSE) {
-    for (int i = tid; i < MW; i += 256) umask[i] = 0;
-    for (int i = tid; i < TOK_WG * a.topk; i += 256) {
+    for (int i = tid; i < MW; i += NT) umask[i] = 0;
+    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
       const int tok = i / a.topk, e = i % a.topk;
       const int t = t_wg0 + tok;
       int m = -1;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       raw[i] = m < 0 ? 0x7fffffff : m;
     }
     __syncthreads();
-    for (int i = tid; i < TOK_WG * a.topk; i += 256) {
+    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
       const int tok = i / a.topk, e = i % a.topk;
       const int32_t* rr = raw + tok * a.topk;
       const int m = rr[e];
@@ -129,12 +131,28 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       sorted[tok * a.topk + rank] = m;
       if (m != 0x7fffffff) atomicOr(&umask[m >> 5], 1 << (m & 31));
     }
-    if (tid < 4 * NSUB) {
+    if (tid < WAVES * NSUB) {
       const int t0 = t_wg0 + tid * TOK_SUB;
       if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
     }
   }
   __syncthreads();
+  if (SPARSE) {
+    // Gate bias (base 2) of every (row, selected block): the main loop reads it
+    // from LDS instead of gathering the score per tile.
+    for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
+      const int r = i / a.topk, e = i % a.topk;
+      const int sg = r >> 4, rl = r & 15;
+      const int t = t_wg0 + sg * TOK_SUB + rl / G;
+      const int tok = t - t_wg0;
+      const int mm = sorted[tok * a.topk + e];
+      float bv = kNegInf;
+      if (t < N && mm != 0x7fffffff)
+        bv = (a.scores[((size_t(b) * a.Hq + g * G + rl % G) * N + t) * C + mm] - lses_sh[r]) * kLog2e;
+      beta[i] = bv;
+    }
+    __syncthreads();
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T), one row per lane ----------------
   uint4 qf[NSUB][KS];
@@ -175,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  constexpr int KLOADS = (KT * CH + 255) / 256;
+  constexpr int KLOADS = (KT * CH + NT - 1) / NT;
   constexpr int VGROUPS = 16 * CH;  // 4-key groups x 16-byte column chunks
   uint4 kreg[KLOADS];
   uint4 vreg[4];
@@ -183,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   auto load_tile = [&](int m) {
     const int j0 = m * KT;
     for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + 256 * i;
+      const int chunk = tid + NT * i;
       const int key = chunk / CH, c8 = chunk % CH;
       const int j = j0 + key;
       kreg[i] = (chunk < KT * CH && j < N) ? *reinterpret_cast<const uint4*>(kh + size_t(j) * D + c8 * 8)
@@ -199,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
   };
   auto store_tile = [&](int buf) {
     for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + 256 * i;
+      const int chunk = tid + NT * i;
       if (chunk < KT * CH) {
         const int key = chunk / CH, c8 = chunk % CH;
         *reinterpret_cast<uint4*>(&Ks[buf][key][c8 * 8]) = kreg[i];
@@ -241,8 +259,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     store_tile(0);
   }
   __syncthreads();
+  float s_cur[NSUB];
+  for (int s = 0; s < NSUB; ++s) {
+    s_cur[s] = 0.f;
+    if (!SPARSE && m >= 0 && m < c_sub[s] && row_t[s] < N)
+      s_cur[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m];
+  }
   while (m >= 0) {
     const int m_next = next_tile(m);
+    float s_nxt[NSUB];
+    for (int s = 0; s < NSUB; ++s) {
+      s_nxt[s] = 0.f;
+      if (!SPARSE && m_next >= 0 && m_next < c_sub[s] && row_t[s] < N)
+        s_nxt[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m_next];
+    }
     if (m_next >= 0) load_tile(m_next);
 
     // Which subtiles take part, and each lane's bias for its row.
@@ -252,12 +282,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       const bool own = (m == c_sub[s]);
       const bool hist = (m < c_sub[s]);
       bool sel = false;
+      float bsel = kNegInf;
       if (hist && row_t[s] < N) {
         if (SPARSE) {
           const int tok = row_t[s] - t_wg0;
           const int32_t* srt = sorted + tok * a.topk;
           int cu = cursor[s];
           sel = (cu < a.topk && srt[cu] == m);
+          if (sel) bsel = beta[((wave * NSUB + s) * 16 + lr) * a.topk + cu];
           while (cu < a.topk && srt[cu] == m) ++cu;
           cursor[s] = cu;
         } else {
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
       need[s] = any;
       float bb = kNegInf;
       if (own) bb = 0.f;
-      else if (sel) bb = (a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m] - lses[s]) * kLog2e;
+      else if (sel) bb = SPARSE ? bsel : (s_cur[s] - lses[s]) * kLog2e;
       bias2[s] = bb;
     }
 
@@ -329,6 +361,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
     if (m_next >= 0) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    for (int s = 0; s < NSUB; ++s) s_cur[s] = s_nxt[s];
     m = m_next;
   }
 
@@ -352,13 +385,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs a) {
 
 template <int D, int G, bool SPARSE>
 hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
+  // Sparse scope: wider workgroups (more tokens share each K/V tile load).
   constexpr int NSUB = 2;
-  constexpr int TOK_WG = 64 * NSUB / G;
+  constexpr int WAVES = SPARSE ? 8 : 4;
+  constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   FwdArgs a = a0;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
-  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + 2 * size_t(TOK_WG) * a.topk) * 4 : 0;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256),
+  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + (2 + G) * size_t(TOK_WG) * a.topk) * 4 : 0;
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES),
                      dyn, stream, a);
   return hipGetLastError();
 }
@@ -372,8 +407,9 @@ bool fwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (sparse) {
-    const int tok_wg = 128 / G;
-    if (size_t(tok_wg) * topk > 4096) return false;
+    // LDS of the sparse prologue: sorted/raw lists (tokens x topk) and the gate
+    // bias table (256 rows x topk).
+    if (size_t(256) * topk > 8192) return false;
     if (((d.C + 32) >> 5) > 1024) return false;
   }
   return true;

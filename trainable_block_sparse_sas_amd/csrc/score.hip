@@ -6,6 +6,7 @@
 // paper Eq. 3).  Columns that are not history blocks of the query hold -inf.
 #include "common.h"
 #include "internal.h"
+#include "mfma.h"
 
 namespace sas {
 namespace {
@@ -92,6 +93,69 @@ __global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ 
           if (m < C) out[((size_t(b) * Hkv + g) * N + t) * C + m] = usum[i][j];
         }
       }
+    }
+  }
+}
+
+// Training scores on the matrix cores (bf16 q and pooled keys, fp32 out):
+// S = Q K̄^T on v_mfma_f32_16x16x32_bf16.  A workgroup owns 64 query rows of
+// one head (16 per wave; the rows of a wave share one block when block % 16 == 0)
+// and walks the blocks in chunks of 64 staged in LDS.  Chunks at or beyond a
+// wave's own block are not computed, only filled with -inf.
+template <int D>
+__global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __restrict__ q,
+                                                               const bf16_t* __restrict__ kbar,
+                                                               float* __restrict__ out, int Hq,
+                                                               int Hkv, int N, int C, int block,
+                                                               float scale) {
+  constexpr int KS = D / 32, CH = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[64][D + 8];
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int t0 = tile * 64 + wave * 16;
+  const int c = t0 < N ? t0 / block : 0;  // shared by the wave's 16 rows
+  int c_max = min(N - 1, tile * 64 + 63) / block;
+  const bf16_t* kb = kbar + (size_t(b) * Hkv + g) * size_t(C) * D;
+  uint4 qa[KS];
+  {
+    const int t = t0 + lr;
+    const bf16_t* qr = q + ((size_t(b) * Hq + h) * N + (t < N ? t : 0)) * D;
+    for (int k2 = 0; k2 < KS; ++k2)
+      qa[k2] = t < N ? *reinterpret_cast<const uint4*>(qr + k2 * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
+  }
+  float* orow[4];
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * lq + i;
+    orow[i] = t < N ? out + ((size_t(b) * Hq + h) * N + t) * C : nullptr;
+  }
+  for (int m0 = 0; m0 < C; m0 += 64) {
+    const bool load = m0 < c_max;  // uniform: some wave of the group computes here
+    if (load) {
+      __syncthreads();
+      for (int i = tid; i < 64 * CH; i += 256) {
+        const int r = i / CH, c8 = i % CH;
+        const int m = m0 + r;
+        *reinterpret_cast<uint4*>(&ks[r][c8 * 8]) =
+            m < C ? *reinterpret_cast<const uint4*>(kb + size_t(m) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+    }
+    for (int nt = 0; nt < 4; ++nt) {
+      const int mb = m0 + 16 * nt;
+      if (mb >= C) break;
+      const int m = mb + lr;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (mb < c) {
+        for (int k2 = 0; k2 < KS; ++k2) {
+          const uint4 bf = *reinterpret_cast<const uint4*>(&ks[16 * nt + lr][k2 * 32 + lq * 8]);
+          acc = mfma16(qa[k2], bf, acc);
+        }
+      }
+      if (m < C)
+        for (int i = 0; i < 4; ++i)
+          if (orow[i]) orow[i][m] = m < c ? acc[i] * scale : kNegInf;
     }
   }
 }
@@ -186,6 +250,16 @@ static void score_train_t(const void* q, const void* kbar, float* scores, const 
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
                               float scale, bool group_sum, bool bf16, hipStream_t s) {
   if (d.N == 0 || d.B == 0 || d.C == 0) return hipSuccess;
+  if (bf16 && !group_sum && d.block % 16 == 0) {
+    dim3 grid((d.N + 63) / 64, d.Hq, d.B);
+    if (d.D == 64)
+      hipLaunchKernelGGL(score_train_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                         (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+    else
+      hipLaunchKernelGGL(score_train_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                         (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+    return hipGetLastError();
+  }
   if (bf16) {
     if (d.D == 64) score_train_t<bf16_t, 64>(q, kbar, scores, d, scale, group_sum, s);
     else score_train_t<bf16_t, 128>(q, kbar, scores, d, scale, group_sum, s);
