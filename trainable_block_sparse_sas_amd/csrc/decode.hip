@@ -5,18 +5,19 @@
 // every history block is attended (dense decode).
 //
 // Work is split per attended block: a workgroup streams EPW blocks of one
-// (sequence, KV head), keeps an online softmax for the G query heads of the
-// group and writes a partial (max, sum, acc[D]) per head.  A second kernel
-// merges the partials by their log-sum-exp.  K rows are read with 16-byte
-// lane loads (four lanes per key, D/4 columns each); V is read row by row,
-// one 4-byte column pair per lane, so every wave load covers whole rows.
+// (sequence, KV head) in 64-key chunks, keeps an online softmax for the G query
+// heads of the group and writes a partial (max, sum, acc[D]) per head; a second
+// kernel merges the partials by their log-sum-exp.  Every lane loads 16-byte
+// pieces: K as four lanes per key (D/4 columns each), V as D/8 lanes per row,
+// so a wave load covers whole rows.  The next chunk's K and V are in flight
+// while the current one is computed; one barrier per chunk (scores in
+// double-buffered LDS; every wave redoes the per-head softmax statistics).
 #include "common.h"
 #include "internal.h"
 
 namespace sas {
 namespace {
 
-constexpr int kMaxG = 16;
 constexpr int kKeys = 64;  // keys per LDS step
 
 struct DecodeArgs {
@@ -46,16 +47,18 @@ __device__ __forceinline__ int entry_block(const DecodeArgs& a, int b, int g, in
   return m;
 }
 
-template <typename T, int D>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int DQ = D / 4;   // K columns per lane (4 lanes per key)
-  constexpr int DV = D / 64;  // V columns per lane (one wave per row)
-  __shared__ float qsh[kMaxG][D];
-  __shared__ float sc[kMaxG][kKeys];
-  __shared__ float red[4][kMaxG][D];
-  __shared__ float run_m[kMaxG], run_l[kMaxG], alpha_sh[kMaxG];
+  constexpr int DQ = D / 4;                 // K columns per lane (4 lanes per key)
+  constexpr int VE = 16 / int(sizeof(T));   // V columns per 16-byte load
+  constexpr int LPV = D / VE;               // lanes per V row
+  constexpr int VSLOT = 64 / LPV;           // V rows per wave load
+  constexpr int VKEYS = kKeys / 4 / VSLOT;  // V rows per lane per block
+  constexpr int KLD = DQ / VE;              // 16-byte K loads per lane
+  __shared__ __attribute__((aligned(16))) float qsh[G][D];
+  __shared__ float sc[2][G][kKeys];
+  __shared__ float red[4][G][D];
   const int part_i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int len = a.cache_len[b];
   len = len > a.L ? a.L : len;
@@ -63,87 +66,137 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   const int c = len > 0 ? pos / a.block : 0;
   const T* qb = reinterpret_cast<const T*>(a.q) + (size_t(b) * a.Hq + g * G) * D;
   for (int i = tid; i < G * D; i += 256) qsh[i / D][i % D] = to_f32(qb[i]);
-  if (tid < kMaxG) {
-    run_m[tid] = kNegInf;
-    run_l[tid] = 0.f;
-  }
   const T* kbase = reinterpret_cast<const T*>(a.kc) + (size_t(b) * a.Hkv + g) * size_t(a.L) * D;
   const T* vbase = reinterpret_cast<const T*>(a.vc) + (size_t(b) * a.Hkv + g) * size_t(a.L) * D;
-  float acc[kMaxG][DV];
-  for (int h = 0; h < kMaxG; ++h)
-    for (int i = 0; i < DV; ++i) acc[h][i] = 0.f;
-  __syncthreads();
+  const int key = tid >> 2, quarter = tid & 3;     // K phase
+  const int vch = lane % LPV, vslot = lane / LPV;  // V phase
 
-  const int key = tid >> 2, quarter = tid & 3;
-  for (int ei = 0; ei < a.EPW; ++ei) {
-    const int e = part_i * a.EPW + ei;
-    const int m = len > 0 ? entry_block(a, b, g, e, c) : -1;
-    if (m < 0) continue;  // uniform across the workgroup
-    const int j_begin = m * a.block;
-    const int j_end = (m == c) ? pos + 1 : j_begin + a.block;
-    for (int j0 = j_begin; j0 < j_end; j0 += kKeys) {
-      // Scores: lanes 4*key .. 4*key+3 hold one key's D columns in quarters.
-      const int j = j0 + key;
-      float kv[DQ];
-      if (j < j_end) {
-        const T* kr = kbase + size_t(j) * D + quarter * DQ;
-        for (int i = 0; i < DQ; i += 16 / int(sizeof(T))) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(kr + i);
-          const T* pv = reinterpret_cast<const T*>(&raw);
-          for (int u = 0; u < int(16 / sizeof(T)); ++u) kv[i + u] = to_f32(pv[u]);
-        }
-      } else {
-        for (int i = 0; i < DQ; ++i) kv[i] = 0.f;
-      }
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-        for (int i = 0; i < DQ; ++i) s = fmaf(qsh[h][quarter * DQ + i], kv[i], s);
-        s += shfl_xor(s, 1);
-        s += shfl_xor(s, 2);
-        if (quarter == 0) sc[h][key] = (j < j_end) ? s * a.scale : kNegInf;
-      }
-      __syncthreads();
-      // Online softmax step: wave w handles heads w, w+4, ...; lane = key.
-      for (int h = wave; h < G; h += 4) {
-        const float x = sc[h][lane];
-        float mx = x;
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-        const float pm = run_m[h];
-        const float nm = fmaxf(pm, mx);  // finite: every step holds >= 1 key
-        const float p = exp_hw(x - nm);
-        float ps = p;
-        for (int off = 32; off >= 1; off >>= 1) ps += shfl_xor(ps, off);
-        sc[h][lane] = p;
-        if (lane == 0) {
-          const float al = exp_hw(pm - nm);
-          alpha_sh[h] = al;
-          run_m[h] = nm;
-          run_l[h] = run_l[h] * al + ps;
-        }
-      }
-      __syncthreads();
-      // Values: wave w covers keys w, w+4, ...; each lane DV adjacent columns.
-      for (int h = 0; h < G; ++h) {
-        const float al = alpha_sh[h];
-        for (int i = 0; i < DV; ++i) acc[h][i] *= al;
-      }
-      for (int kk = wave; kk < kKeys; kk += 4) {
-        const int jv = j0 + kk;
-        if (jv >= j_end) break;
-        const T* vr = vbase + size_t(jv) * D + lane * DV;
-        float vv[DV];
-        for (int i = 0; i < DV; ++i) vv[i] = to_f32(vr[i]);
-        for (int h = 0; h < G; ++h) {
-          const float p = sc[h][kk];
-          for (int i = 0; i < DV; ++i) acc[h][i] = fmaf(p, vv[i], acc[h][i]);
-        }
-      }
-      __syncthreads();
-    }
+  float m_run[G], l_run[G], acc[G][VE];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[h][i] = 0.f;
   }
-  // Reduce the four waves' accumulators and write the partial.
+
+  // The (block, key range) of each of this workgroup's steps; steps of one
+  // block beyond 64 keys (block > 64) follow in order.
+  auto step_range = [&](int e, int& j0, int& j_end) -> bool {
+    const int m = len > 0 ? entry_block(a, b, g, e, c) : -1;
+    if (m < 0) return false;
+    j0 = m * a.block;
+    j_end = (m == c) ? pos + 1 : j0 + a.block;
+    return true;
+  };
+  uint4 kr[KLD], vr[VKEYS];
+  auto load = [&](int j0, int j_end, uint4* kd, uint4* vd) {
+    const int j = j0 + key;
+    for (int i = 0; i < KLD; ++i)
+      kd[i] = j < j_end ? *reinterpret_cast<const uint4*>(kbase + size_t(j) * D + quarter * DQ + i * VE)
+                        : make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < VKEYS; ++r) {
+      const int jv = j0 + wave * (kKeys / 4) + r * VSLOT + vslot;
+      vd[r] = jv < j_end ? *reinterpret_cast<const uint4*>(vbase + size_t(jv) * D + vch * VE)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // Walk the (entry, 64-key chunk) steps with the next step's loads in flight.
+  int e = part_i * a.EPW, e_end = e + a.EPW;
+  int j0 = 0, j_end = 0;
+  bool have = false;
+  while (e < e_end && !(have = step_range(e, j0, j_end))) ++e;
+  if (have) load(j0, j_end, kr, vr);
+  __syncthreads();  // qsh ready
+  int buf = 0;
+  while (have) {
+    // next step
+    int ne = e, nj0 = j0 + kKeys, nj_end = j_end;
+    bool nhave = nj0 < j_end;
+    if (!nhave) {
+      ++ne;
+      while (ne < e_end && !(nhave = step_range(ne, nj0, nj_end))) ++ne;
+    }
+    uint4 kn[KLD], vn[VKEYS];
+    if (nhave) load(nj0, nj_end, kn, vn);
+    // scores of this chunk's 64 keys
+    const int j = j0 + key;
+    {
+      float kf[DQ];
+      for (int i = 0; i < KLD; ++i) {
+        const T* pv = reinterpret_cast<const T*>(&kr[i]);
+        for (int u = 0; u < VE; ++u) kf[i * VE + u] = to_f32(pv[u]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sdot = 0.f;
+        const float4* qv = reinterpret_cast<const float4*>(&qsh[h][quarter * DQ]);
+        for (int i = 0; i < DQ / 4; ++i) {
+          const float4 qq = qv[i];
+          sdot = fmaf(qq.x, kf[4 * i], sdot);
+          sdot = fmaf(qq.y, kf[4 * i + 1], sdot);
+          sdot = fmaf(qq.z, kf[4 * i + 2], sdot);
+          sdot = fmaf(qq.w, kf[4 * i + 3], sdot);
+        }
+        sdot += shfl_xor(sdot, 1);
+        sdot += shfl_xor(sdot, 2);
+        if (quarter == 0) sc[buf][h][key] = j < j_end ? sdot * a.scale : kNegInf;
+      }
+    }
+    __syncthreads();
+    // online softmax, every wave for every head (lane = key)
+    float p[G], alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float x = sc[buf][h][lane];
+      float mx = x;
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+      const float nm = fmaxf(m_run[h], mx);  // finite: every chunk holds a key
+      p[h] = exp2_hw((x - nm) * kLog2e);
+      float ps = p[h];
+      for (int off = 32; off >= 1; off >>= 1) ps += shfl_xor(ps, off);
+      alpha[h] = exp2_hw((m_run[h] - nm) * kLog2e);
+      l_run[h] = l_run[h] * alpha[h] + ps;
+      m_run[h] = nm;
+    }
+    // values: this lane's VKEYS rows, VE columns each
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[h][i] *= alpha[h];
+    for (int r = 0; r < VKEYS; ++r) {
+      const int kk = wave * (kKeys / 4) + r * VSLOT + vslot;
+      const T* pv = reinterpret_cast<const T*>(&vr[r]);
+      float vf[VE];
+      for (int u = 0; u < VE; ++u) vf[u] = to_f32(pv[u]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ph = __shfl(p[h], kk, 64);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) acc[h][i] = fmaf(ph, vf[i], acc[h][i]);
+      }
+    }
+    // advance
+    have = nhave;
+    e = ne;
+    j0 = nj0;
+    j_end = nj_end;
+    for (int i = 0; i < KLD; ++i) kr[i] = kn[i];
+    for (int r = 0; r < VKEYS; ++r) vr[r] = vn[r];
+    buf ^= 1;
+  }
+  // Sum the V slots of each wave, then the four waves, and write the partial.
+#pragma unroll
   for (int h = 0; h < G; ++h)
-    for (int i = 0; i < DV; ++i) red[wave][h][lane * DV + i] = acc[h][i];
+#pragma unroll
+    for (int i = 0; i < VE; ++i)
+      for (int off = LPV; off < 64; off <<= 1) acc[h][i] += shfl_xor(acc[h][i], off);
+  if (vslot == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < VE; ++i) red[wave][h][vch * VE + i] = acc[h][i];
   __syncthreads();
   float* out = a.part + ((size_t(b) * a.Hkv + g) * a.P + part_i) * G * (D + 2);
   for (int i = tid; i < G * D; i += 256) {
@@ -151,8 +204,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     out[h * (D + 2) + 2 + d] = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
   }
   if (tid < G) {
-    out[tid * (D + 2) + 0] = run_m[tid];
-    out[tid * (D + 2) + 1] = run_l[tid];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (h == tid) {
+        out[h * (D + 2) + 0] = m_run[h];
+        out[h * (D + 2) + 1] = l_run[h];
+      }
   }
 }
 
@@ -202,7 +259,15 @@ template <typename T, int D>
 hipError_t decode_t(const DecodeArgs& a0, int B, T* o, float* lse, hipStream_t s) {
   DecodeArgs a = a0;
   dim3 grid(a.P, a.Hkv, B);
-  hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(256), 0, s, a);
+  switch (a.Hq / a.Hkv) {
+#define SAS_DEC_G(GG) \
+  case GG: hipLaunchKernelGGL((decode_partial_kernel<T, D, GG>), grid, dim3(256), 0, s, a); break;
+    SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4) SAS_DEC_G(5) SAS_DEC_G(6) SAS_DEC_G(7)
+    SAS_DEC_G(8) SAS_DEC_G(9) SAS_DEC_G(10) SAS_DEC_G(11) SAS_DEC_G(12) SAS_DEC_G(13) SAS_DEC_G(14)
+    SAS_DEC_G(15) SAS_DEC_G(16)
+#undef SAS_DEC_G
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.Hq, B), dim3(D), 0, s, a.part, o, lse,
                      a.Hq, a.Hkv, a.P);
   return hipGetLastError();

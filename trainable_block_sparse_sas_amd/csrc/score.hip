@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __r
 // covers 64/LPR rows per load; partial dots are reduced across those lanes.
 // The G query heads of the group are handled together; with group_sum the fp32
 // scores are added in head-index order.
-template <typename T, int D>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, float* __restrict__ out,
     const int32_t* __restrict__ cache_len, int Hq, int Hkv, int L, int C, int block, float scale,
@@ -173,9 +173,8 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   constexpr int VEC = 16 / sizeof(T);
   constexpr int LPR = D / VEC;        // lanes per K̄ row
   constexpr int RPW = 64 / LPR;       // rows per wave per load
-  constexpr int MAXG = 16;
+  constexpr int MAXG = G;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPR, rsub = lane / LPR;
   int len = cache_len[b];
@@ -183,7 +182,9 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int c = len > 0 ? (len - 1) / block : 0;
   const int c_eff = c < C ? c : C;
   float qv[MAXG][VEC];
+#pragma unroll
   for (int h = 0; h < G; ++h)
+#pragma unroll
     for (int i = 0; i < VEC; ++i)
       qv[h][i] = to_f32(q[(size_t(b) * Hq + g * G + h) * D + sub * VEC + i]);
   const int rows_per_wg = RPW * 4 * 4;  // 4 waves, 4 loads per wave
@@ -201,8 +202,10 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     } else {
       for (int i = 0; i < VEC; ++i) kv[i] = T(0);
     }
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       float a = 0.f;
+#pragma unroll
       for (int i = 0; i < VEC; ++i) a = fmaf(qv[h][i], to_f32(kv[i]), a);
       for (int off = LPR / 2; off >= 1; off >>= 1) a += shfl_xor(a, off);
       dots[h] = a;
@@ -212,10 +215,12 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
         float u = kNegInf;
         if (m < c_eff) {
           u = dots[0] * scale;
+#pragma unroll
           for (int h = 1; h < G; ++h) u = u + dots[h] * scale;
         }
         out[(size_t(b) * Hkv + g) * C + m] = u;
       } else {
+#pragma unroll
         for (int h = 0; h < G; ++h)
           out[(size_t(b) * Hq + g * G + h) * C + m] = m < c_eff ? dots[h] * scale : kNegInf;
       }
@@ -278,8 +283,18 @@ static void score_decode_t(const void* q, const void* kbar, float* scores, const
   constexpr int RPW = 64 / (D / VEC);
   const int rows_per_wg = RPW * 16;
   dim3 grid((C + rows_per_wg - 1) / rows_per_wg, Hkv, B);
-  hipLaunchKernelGGL((score_decode_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
-                     (const T*)kbar, scores, cl, Hq, Hkv, L, C, block, scale, group_sum ? 1 : 0);
+  switch (Hq / Hkv) {
+#define SAS_SCD_G(GG)                                                                        \
+  case GG:                                                                                  \
+    hipLaunchKernelGGL((score_decode_kernel<T, D, GG>), grid, dim3(256), 0, s, (const T*)q, \
+                       (const T*)kbar, scores, cl, Hq, Hkv, L, C, block, scale, group_sum ? 1 : 0); \
+    break;
+    SAS_SCD_G(1) SAS_SCD_G(2) SAS_SCD_G(3) SAS_SCD_G(4) SAS_SCD_G(5) SAS_SCD_G(6) SAS_SCD_G(7)
+    SAS_SCD_G(8) SAS_SCD_G(9) SAS_SCD_G(10) SAS_SCD_G(11) SAS_SCD_G(12) SAS_SCD_G(13)
+    SAS_SCD_G(14) SAS_SCD_G(15) SAS_SCD_G(16)
+#undef SAS_SCD_G
+    default: break;
+  }
 }
 
 hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,

@@ -182,6 +182,195 @@ __global__ __launch_bounds__(256 * (WPR > 4 ? 4 : 1)) void topk_kernel(
   }
 }
 
+// ---- long rows (decode: thousands of candidates per row) ----------------------
+// Composite key (hi, lo) = (order-preserving score key, ~block index): all
+// distinct, and larger means "score higher, or equal score and lower index".
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Marks in `take` the K largest composite keys among the wave's valid
+// candidates (PER per lane; fewer valid than K: all of them).  MSB-first radix
+// select over 8-bit digits of hi then lo with a histogram private to the wave
+// (256 LDS counters); stops as soon as the tied candidates are exactly the
+// number still needed.
+template <int PER>
+__device__ void wave_select(const uint32_t (&hi)[PER], const uint32_t (&lo)[PER],
+                            const bool (&valid)[PER], int K, uint32_t* hist, bool (&take)[PER]) {
+  const int lane = threadIdx.x & 63;
+  bool tied[PER];
+  int nvalid = 0;
+  for (int i = 0; i < PER; ++i) {
+    take[i] = false;
+    tied[i] = valid[i];
+    nvalid += __popcll(__ballot(valid[i]));
+  }
+  int need = K < nvalid ? K : nvalid;
+  if (need == nvalid) {  // everything valid is taken
+    for (int i = 0; i < PER; ++i) take[i] = valid[i];
+    return;
+  }
+  for (int pass = 0; pass < 8 && need > 0; ++pass) {
+    const int shift = 24 - 8 * (pass & 3);
+    for (int j = lane; j < 256; j += 64) hist[j] = 0;
+    wave_sync();
+    uint32_t dig[PER];
+    for (int i = 0; i < PER; ++i) {
+      dig[i] = (((pass < 4) ? hi[i] : lo[i]) >> shift) & 255u;
+      if (tied[i]) atomicAdd(&hist[dig[i]], 1u);
+    }
+    wave_sync();
+    uint32_t h4[4];
+    for (int j = 0; j < 4; ++j) h4[j] = hist[4 * lane + j];
+    const uint32_t local = h4[0] + h4[1] + h4[2] + h4[3];
+    uint32_t suffix = local;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suffix, off, 64);
+      if (lane + off < 64) suffix += o;
+    }
+    const unsigned long long ball = __ballot(suffix >= uint32_t(need));
+    const int L = 63 - __builtin_clzll(ball);
+    uint32_t digit = 0, above = 0, cnt = 0;
+    if (lane == L) {
+      above = suffix - local;
+      for (int j = 3; j >= 0; --j) {
+        if (above + h4[j] >= uint32_t(need)) {
+          digit = 4 * L + j;
+          cnt = h4[j];
+          break;
+        }
+        above += h4[j];
+      }
+    }
+    digit = __shfl(digit, L, 64);
+    above = __shfl(above, L, 64);
+    cnt = __shfl(cnt, L, 64);
+    wave_sync();
+    for (int i = 0; i < PER; ++i) {
+      if (!tied[i]) continue;
+      if (dig[i] > digit) {
+        take[i] = true;
+        tied[i] = false;
+      } else if (dig[i] < digit) {
+        tied[i] = false;
+      }
+    }
+    need -= int(above);
+    if (int(cnt) == need) {
+      for (int i = 0; i < PER; ++i)
+        if (tied[i]) take[i] = true;
+      need = 0;
+    }
+  }
+}
+
+// One row per workgroup of 16 waves.  Stage 1: wave w selects the top K of its
+// candidates m = (i*16 + w)*64 + lane.  Stage 2: wave 0 selects the top K of
+// the 16 survivor lists.  The K winners are then ranked by counting.
+template <int PER, int PER2>
+__global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict__ scores,
+                                                         int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ cache_len,
+                                                         int Hkv, int hpr, int Nq, int C, int block,
+                                                         int topk) {
+  __shared__ uint32_t hist[16][256];
+  __shared__ uint32_t cand_hi[16][kMaxTopk];
+  __shared__ uint32_t cand_lo[16][kMaxTopk];
+  __shared__ int cand_n[16];
+  __shared__ uint32_t fin_hi[kMaxTopk], fin_lo[kMaxTopk];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long row = blockIdx.x;
+  const long t = row % Nq, bg = row / Nq;
+  const int b = int(bg / Hkv), g = int(bg % Hkv);
+  int c;
+  if (cache_len) {
+    const int len = cache_len[b];
+    c = len > 0 ? (len - 1) / block : 0;
+  } else {
+    c = int(t / block);
+  }
+  c = c < C ? c : C;
+  const int K = topk < c ? topk : c;
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+
+  uint32_t hi[PER], lo[PER];
+  bool valid[PER], take[PER];
+  for (int i = 0; i < PER; ++i) {
+    const int m = (i * 16 + w) * 64 + lane;
+    valid[i] = m < c;
+    hi[i] = 0;
+    lo[i] = ~uint32_t(m);
+    if (valid[i]) {
+      const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C + m;
+      float u = base[0];
+      for (int h = 1; h < hpr; ++h) u = u + base[size_t(h) * Nq * C];
+      hi[i] = score_key(u);
+    }
+  }
+  if (K > 0) wave_select<PER>(hi, lo, valid, K, hist[w], take);
+  else
+    for (int i = 0; i < PER; ++i) take[i] = false;
+  int n = 0;
+  for (int i = 0; i < PER; ++i) {
+    const unsigned long long bt = __ballot(take[i]);
+    if (take[i]) {
+      const int pos = n + __popcll(bt & lt);
+      cand_hi[w][pos] = hi[i];
+      cand_lo[w][pos] = lo[i];
+    }
+    n += __popcll(bt);
+  }
+  if (lane == 0) cand_n[w] = n;
+  __syncthreads();
+  if (w == 0 && K > 0) {
+    int off[16];
+    int tot = 0;
+    for (int v = 0; v < 16; ++v) {
+      off[v] = tot;
+      tot += cand_n[v];
+    }
+    uint32_t h2[PER2], l2[PER2];
+    bool v2[PER2], t2[PER2];
+    for (int i = 0; i < PER2; ++i) {
+      const int e = i * 64 + lane;
+      v2[i] = e < tot;
+      h2[i] = 0;
+      l2[i] = 0;
+      if (v2[i]) {
+        int src = 0;
+        while (src < 15 && e >= off[src + 1]) ++src;
+        h2[i] = cand_hi[src][e - off[src]];
+        l2[i] = cand_lo[src][e - off[src]];
+      }
+    }
+    wave_select<PER2>(h2, l2, v2, K, hist[0], t2);
+    int nn = 0;
+    for (int i = 0; i < PER2; ++i) {
+      const unsigned long long bt = __ballot(t2[i]);
+      if (t2[i]) {
+        const int pos = nn + __popcll(bt & lt);
+        fin_hi[pos] = h2[i];
+        fin_lo[pos] = l2[i];
+      }
+      nn += __popcll(bt);
+    }
+  }
+  __syncthreads();
+  int32_t* out = idx + size_t(row) * topk;
+  for (int e = threadIdx.x; e < topk; e += 1024) {
+    if (e >= K) {
+      out[e] = -1;
+      continue;
+    }
+    const uint32_t he = fin_hi[e], le = fin_lo[e];
+    int slot = 0;
+    for (int f = 0; f < K; ++f) slot += (fin_hi[f] > he) || (fin_hi[f] == he && fin_lo[f] > le);
+    out[slot] = int(~le);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
@@ -194,9 +383,12 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
   } else if (C <= 1024) {
     hipLaunchKernelGGL((topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
+  } else if (topk <= 32) {
+    hipLaunchKernelGGL((topk_long_kernel<16, 8>), dim3(rows), dim3(1024), 0, s, scores, idx,
+                       cache_len, Hkv, hpr, Nq, C, block, topk);
   } else {
-    hipLaunchKernelGGL((topk_kernel<16, 16>), dim3(rows), dim3(1024), 0, s, scores, idx,
-                       cache_len, Hkv, hpr, Nq, C, block, topk, rows);
+    hipLaunchKernelGGL((topk_long_kernel<16, 64>), dim3(rows), dim3(1024), 0, s, scores, idx,
+                       cache_len, Hkv, hpr, Nq, C, block, topk);
   }
   return hipGetLastError();
 }
