@@ -15,9 +15,10 @@ hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const vo
                            float* delta, hipStream_t s);
 
 bool fwd_mfma_supported(const Dims& d, int topk, bool sparse);
+size_t fwd_mfma_workspace(const Dims& d);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, hipStream_t s);
+                           int topk, float scale, void* ws, hipStream_t s);
 
 bool bwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse);
@@ -28,9 +29,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            hipStream_t s);
 
 size_t fwd_workspace(const Dims& d, int topk, bool bf16) {
-  (void)d;
-  (void)topk;
-  (void)bf16;
+  const bool sparse = topk >= 0;
+  if (bf16 && fwd_mfma_supported(d, sparse ? topk : 0, sparse)) return fwd_mfma_workspace(d);
   return 0;
 }
 
@@ -44,9 +44,8 @@ size_t bwd_workspace(const Dims& d, int topk, bool bf16) {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, void* ws, hipStream_t s) {
-  (void)ws;
   if (bf16 && fwd_mfma_supported(d, topk, idx != nullptr))
-    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, s);
+    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, ws, s);
   return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, s);
 }
 

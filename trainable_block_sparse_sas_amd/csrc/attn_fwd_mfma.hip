@@ -7,54 +7,134 @@
 // online softmax as in the review's kernel paragraph ("A Concrete Walkthrough").
 //
 // Layout.  A workgroup owns TOK_WG consecutive query tokens of one KV head and
-// all G query heads of that head, i.e. 64*NSUB rows, split into 4 waves x NSUB
-// subtiles of 16 rows (16/G tokens x G heads).  Everything is transposed so that
+// all G query heads of that head, 16*NSUB*WAVES rows, split into WAVES waves x
+// NSUB subtiles of 16 rows (16/G tokens x G heads).  Everything is transposed so
 // a lane owns one query row: S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_16x16x32_bf16, so the softmax statistics and the output rescale
-// stay lane-local (the four lanes of a row only meet for the row max).  Key
-// tiles are one block (64 keys): K row-major and V transposed (keys permuted to
-// match the MFMA B layout of P) in double-buffered LDS.  The gate bias is
-// constant over a block, so it enters once per (row, tile).
+// stay lane-local (the four lanes of a row only meet for the row max).  A key
+// tile is one block (64 keys).  The gate bias is constant over a block, so it
+// enters once per (row, tile).
 //
-// Sparse scope: each token's selected blocks are sorted in LDS; the workgroup
-// visits the union of its rows' blocks in ascending order and a subtile skips a
-// tile no row of it selected.  Full scope visits every block up to the own one.
+// Tile pipeline.  Tiles stream through an NST-stage ring in LDS filled by
+// direct global->LDS loads (global_load_lds_dwordx4), so NST-1 tiles are in
+// flight without holding registers.  K is copied from the caller's tensor into
+// an XOR-swizzled layout (conflict-free 16-byte MFMA operand reads); V comes
+// from a per-block transposed copy in the workspace, written by vt_kernel with
+// the keys permuted to the MFMA k order of P^T and the same kind of swizzle.
+// Full scope also streams the rows' selector scores of the tile.
+//
+// Sparse scope: each token's selected blocks are sorted in LDS and the gate
+// biases of every (row, selected block) are tabulated up front; the workgroup
+// visits the union of its rows' blocks in ascending order and a subtile skips
+// a tile none of its rows selected.  Full scope visits every block up to the
+// own one.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
+
+#include <type_traits>
 
 namespace sas {
 namespace {
 
 constexpr int KT = 64;  // keys per tile = block size of this kernel
-constexpr int KPAD = 8;
+constexpr int kMaskWords = 1024;  // sparse scope: C + 1 <= 32768 blocks
+constexpr int kListMax = 4096;    // sparse scope: tokens per workgroup x topk
+constexpr int kBiasMax = 8192;    // sparse scope: rows per workgroup x topk
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct FwdArgs {
   const bf16_t* q;
   const bf16_t* k;
   const bf16_t* v;
+  const bf16_t* vt;  // workspace: transposed, permuted, swizzled V blocks
   const float* scores;
   const int32_t* idx;
   bf16_t* o;
   float* lse;
   float* lse_s;
-  int Hq, Hkv, N, C, topk, n_tiles, n_pairs;
+  int Hq, Hkv, N, C, topk, n_tiles, n_pairs, NB;
   float scale;
 };
 
-template <int D, int G, int NSUB, int WAVES, bool SPARSE>
+// Key position p (0..63) inside a 64-key tile of V^T -> key index.  Within each
+// group of 32, position 8q + j holds key 4q + j (j < 4) or 16 + 4q + j - 4: the
+// k order in which a lane's P^T values leave the S^T accumulators.
+__device__ __forceinline__ int vt_key_of_pos(int p) {
+  const int hh = p >> 5, q = (p >> 3) & 3, j = p & 7;
+  return 32 * hh + (j < 4 ? 4 * q + j : 16 + 4 * q + j - 4);
+}
+// 16-byte chunk swizzles (conflict-free reads of 16 rows at one chunk column).
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
+
+// Per block of V: V^T [D][64] with keys in vt_key_of_pos order; row d's 16-byte
+// chunk cc stored at chunk cc ^ vt_swz(d).  Keys beyond N are zero.
+template <int D>
+__global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, bf16_t* __restrict__ vt,
+                                                 int Hkv, int N, int NB) {
+  __shared__ uint16_t vs[KT][D + 2];
+  const int m = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const bf16_t* src = v + ((size_t(b) * Hkv + g) * N + size_t(m) * KT) * D;
+  for (int i = threadIdx.x; i < KT * D; i += 256) {
+    const int key = i / D, d = i % D;
+    vs[key][d] = (m * KT + key < N) ? src[size_t(key) * D + d] : 0;
+  }
+  __syncthreads();
+  bf16_t* dst = vt + ((size_t(b) * Hkv + g) * NB + m) * size_t(KT) * D;
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int d = i >> 3, pc = i & 7;
+    const int cc = pc ^ vt_swz(d);
+    uint32_t w[4];
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const int p0 = cc * 8 + 2 * j2;
+      w[j2] = uint32_t(vs[vt_key_of_pos(p0)][d]) | (uint32_t(vs[vt_key_of_pos(p0 + 1)][d]) << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + size_t(d) * KT + pc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | 0xF00 | (((n >> 4) & 3) << 14));
+}
+
+template <int D, int G, int NSUB, int WAVES, int NST, bool SPARSE>
 __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
-  constexpr int NT = 64 * WAVES;  // threads
+  constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;    // k-steps of S = K Q^T
   constexpr int MD = D / 16;    // output tiles of O^T
   constexpr int TOK_SUB = 16 / G;
   constexpr int ROWS_WG = 16 * NSUB * WAVES;
   constexpr int TOK_WG = ROWS_WG / G;
-  constexpr int CH = D / 8;     // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT][D + KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D][KT + KPAD];
+  constexpr int CH = D / 8;               // 16-byte chunks per K row
+  constexpr int NKL = KT * D * 2 / 1024;  // 1 KB wave loads per K (and per V) tile
+  constexpr int LPW = NKL / WAVES;        // per wave, per operand
+  constexpr int L = 2 * LPW + (SPARSE ? 0 : 1);  // DMA instructions per wave per tile
+  static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
+  static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
+  static_assert(kBiasMax >= kListMax, "raw index scratch reuses the bias table");
+  // One array per ring stage: the compiler can then tell a stage being read
+  // from the stages the in-flight loads write, and adds no waits of its own.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8],
+      K3[NST > 3 ? KT * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT], V1[D * KT], V2[NST > 2 ? D * KT : 8],
+      V3[NST > 3 ? D * KT : 8];
+  __shared__ __attribute__((aligned(16))) float S0[WAVES * 64], S1[WAVES * 64], S2[WAVES * 64],
+      S3[WAVES * 64];
   __shared__ float lses_sh[ROWS_WG];
-  extern __shared__ int32_t dyn[];  // sparse: union mask | sorted idx | raw idx
+  __shared__ int wg_last;
+  // Sparse-scope tables, static so that reads in the loop do not alias the
+  // in-flight tile loads: union of selected blocks (bit mask), each token's
+  // selections sorted, and the gate bias of every (row, selection).
+  __shared__ int32_t umask[SPARSE ? kMaskWords : 1];
+  __shared__ int32_t sorted[SPARSE ? kListMax : 1];
+  __shared__ float beta[SPARSE ? kBiasMax : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -64,7 +144,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int N = a.N, C = a.C;
   const int t_wg0 = tile * TOK_WG;
 
-  // Rows of this lane, one per subtile.
   int row_t[NSUB], row_h[NSUB], c_sub[NSUB];
   bool sub_live[NSUB];
   for (int s = 0; s < NSUB; ++s) {
@@ -100,12 +179,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     if (lane == 0) lses_sh[wave * 16 * NSUB + rr] = res;
   }
 
-  // ---- sparse scope: per-token sorted selections and the union of blocks ----
+  // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
   const int MW = (C + 32) >> 5;  // bits 0..C (the own block may be block C)
-  int32_t* umask = dyn;
-  int32_t* sorted = dyn + MW;                 // [TOK_WG][topk]
-  int32_t* raw = sorted + TOK_WG * a.topk;
-  float* beta = reinterpret_cast<float*>(raw + TOK_WG * a.topk);  // [ROWS_WG][topk] (sparse)    // [TOK_WG][topk]
+  int32_t* raw = reinterpret_cast<int32_t*>(beta);  // [TOK_WG][topk], until the bias table is built
   if (SPARSE) {
     for (int i = tid; i < MW; i += NT) umask[i] = 0;
     for (int i = tid; i < TOK_WG * a.topk; i += NT) {
@@ -135,48 +211,40 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
       const int t0 = t_wg0 + tid * TOK_SUB;
       if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
     }
-  }
-  __syncthreads();
-  if (SPARSE) {
-    // Gate bias (base 2) of every (row, selected block): the main loop reads it
-    // from LDS instead of gathering the score per tile.
+    __syncthreads();
     for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
       const int r = i / a.topk, e = i % a.topk;
       const int sg = r >> 4, rl = r & 15;
       const int t = t_wg0 + sg * TOK_SUB + rl / G;
-      const int tok = t - t_wg0;
-      const int mm = sorted[tok * a.topk + e];
+      const int mm = sorted[(t - t_wg0) * a.topk + e];
       float bv = kNegInf;
       if (t < N && mm != 0x7fffffff)
         bv = (a.scores[((size_t(b) * a.Hq + g * G + rl % G) * N + t) * C + mm] - lses_sh[r]) * kLog2e;
       beta[i] = bv;
     }
-    __syncthreads();
   }
+  if (tid == 0) wg_last = -1;
+  __syncthreads();
+  {
+    int lt = -1;
+    for (int s = 0; s < NSUB; ++s) lt = max(lt, sub_live[s] ? c_sub[s] : -1);
+    if (lane == 0) atomicMax(&wg_last, lt);
+  }
+  __syncthreads();
+  const int last_tile = wg_last;
 
   // ---- Q fragments (B operand of S^T = K Q^T), one row per lane ----------------
   uint4 qf[NSUB][KS];
   float lses[NSUB];
+  int cursor[NSUB];
   for (int s = 0; s < NSUB; ++s) {
     const bool ok = row_t[s] < N;
     const bf16_t* qr = a.q + ((size_t(b) * a.Hq + row_h[s]) * N + (ok ? row_t[s] : 0)) * D;
     for (int ks = 0; ks < KS; ++ks)
       qf[s][ks] = ok ? *reinterpret_cast<const uint4*>(qr + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
     lses[s] = lses_sh[wave * 16 * NSUB + s * 16 + lr];
+    cursor[s] = 0;
   }
-  int cursor[NSUB];
-  for (int s = 0; s < NSUB; ++s) cursor[s] = 0;
-
-  // Tiles of the workgroup: full scope 0 .. max own block; sparse: set bits.
-  int last_tile = -1;
-  for (int s = 0; s < NSUB; ++s) last_tile = max(last_tile, sub_live[s] ? c_sub[s] : -1);
-  // every wave needs the workgroup maximum, through LDS
-  __shared__ int wg_last;
-  if (tid == 0) wg_last = -1;
-  __syncthreads();
-  if (lane == 0) atomicMax(&wg_last, last_tile);
-  __syncthreads();
-  last_tile = wg_last;
 
   auto next_tile = [&](int m) -> int {
     if (!SPARSE) return (m + 1 <= last_tile) ? m + 1 : -1;
@@ -191,55 +259,61 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     return -1;
   };
 
+  // ---- direct global -> LDS tile loads ------------------------------------------
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  constexpr int KLOADS = (KT * CH + NT - 1) / NT;
-  constexpr int VGROUPS = 16 * CH;  // 4-key groups x 16-byte column chunks
-  uint4 kreg[KLOADS];
-  uint4 vreg[4];
-
-  auto load_tile = [&](int m) {
-    const int j0 = m * KT;
-    for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + NT * i;
-      const int key = chunk / CH, c8 = chunk % CH;
-      const int j = j0 + key;
-      kreg[i] = (chunk < KT * CH && j < N) ? *reinterpret_cast<const uint4*>(kh + size_t(j) * D + c8 * 8)
-                                             : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VGROUPS) {
-      const int kg = tid / CH, c8 = tid % CH;
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kg + r;
-        vreg[r] = j < N ? *reinterpret_cast<const uint4*>(vh + size_t(j) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-      }
-    }
+  const bf16_t* vth = a.vt + (size_t(b) * a.Hkv + g) * size_t(a.NB) * KT * D;
+  // this lane's score row (full scope): the wave's rows 16s + lr, repeated
+  const int srow_i = lane % (16 * NSUB);
+  const int s_s = srow_i >> 4, s_lr = srow_i & 15;
+  const int s_t = min(t_wg0 + (wave * NSUB + s_s) * TOK_SUB + s_lr / G, N - 1);
+  const float* s_base = a.scores + ((size_t(b) * a.Hq + g * G + s_lr % G) * N + s_t) * C;
+  auto kst = [&](auto tag) -> uint16_t* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return K0;
+    else if constexpr (P == 1) return K1;
+    else if constexpr (P == 2) return K2;
+    else return K3;
   };
-  auto store_tile = [&](int buf) {
-    for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + NT * i;
-      if (chunk < KT * CH) {
-        const int key = chunk / CH, c8 = chunk % CH;
-        *reinterpret_cast<uint4*>(&Ks[buf][key][c8 * 8]) = kreg[i];
-      }
+  auto vst = [&](auto tag) -> uint16_t* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return V0;
+    else if constexpr (P == 1) return V1;
+    else if constexpr (P == 2) return V2;
+    else return V3;
+  };
+  auto sst = [&](auto tag) -> float* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return S0;
+    else if constexpr (P == 1) return S1;
+    else if constexpr (P == 2) return S2;
+    else return S3;
+  };
+  auto issue = [&](int m, auto tag) {
+    uint16_t* kd = kst(tag);
+    uint16_t* vd = vst(tag);
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;  // 1 KB piece of the tile
+      const int sl = 64 * j + lane;  // 16-byte slot
+      const int r = sl / CH, pc = sl % CH;
+      const int key = min(m * KT + r, N - 1);
+      const int c = pc ^ k_swz<D>(r);
+      __builtin_amdgcn_global_load_lds(kh + size_t(key) * D + c * 8, (lds_ptr_t)(kd + j * 512), 16, 0, 0);
     }
-    if (tid < VGROUPS) {
-      const int kg = tid / CH, c8 = tid % CH;
-      const int kap = (4 * kg) & 31;  // key within its 32-key group: 16*hi + 4*q
-      const int phys = ((4 * kg) & ~31) + 8 * ((kap >> 2) & 3) + 4 * (kap >> 4);
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-      for (int d2 = 0; d2 < 4; ++d2) {
-        // columns 2*d2 and 2*d2+1 of the chunk, four keys each
-        const uint32_t lo0 = (w0[d2] & 0xffffu) | (w1[d2] << 16);
-        const uint32_t lo1 = (w2[d2] & 0xffffu) | (w3[d2] << 16);
-        const uint32_t hi0 = (w0[d2] >> 16) | (w1[d2] & 0xffff0000u);
-        const uint32_t hi1 = (w2[d2] >> 16) | (w3[d2] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(&Vt[buf][c8 * 8 + 2 * d2][phys]) = make_uint2(lo0, lo1);
-        *reinterpret_cast<uint2*>(&Vt[buf][c8 * 8 + 2 * d2 + 1][phys]) = make_uint2(hi0, hi1);
-      }
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      __builtin_amdgcn_global_load_lds(vth + size_t(m) * KT * D + (64 * j + lane) * 8,
+                                       (lds_ptr_t)(vd + j * 512), 16, 0, 0);
+    }
+    if (!SPARSE)
+      __builtin_amdgcn_global_load_lds(s_base + min(m, C - 1), (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
+  };
+  auto wait_tile = [&](int after) {
+    // wait until at most `after` later tiles' loads are still outstanding
+    switch (after) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<L>(); break;
+      case 2: wait_vm<2 * L>(); break;
+      default: wait_vm<3 * L>(); break;
     }
   };
 
@@ -252,29 +326,26 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   }
   const float c1 = a.scale * kLog2e;
 
-  int m = next_tile(-1);
-  int buf = 0;
-  if (m >= 0) {
-    load_tile(m);
-    store_tile(0);
-  }
-  __syncthreads();
-  float s_cur[NSUB];
-  for (int s = 0; s < NSUB; ++s) {
-    s_cur[s] = 0.f;
-    if (!SPARSE && m >= 0 && m < c_sub[s] && row_t[s] < N)
-      s_cur[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m];
-  }
-  while (m >= 0) {
-    const int m_next = next_tile(m);
-    float s_nxt[NSUB];
-    for (int s = 0; s < NSUB; ++s) {
-      s_nxt[s] = 0.f;
-      if (!SPARSE && m_next >= 0 && m_next < c_sub[s] && row_t[s] < N)
-        s_nxt[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m_next];
-    }
-    if (m_next >= 0) load_tile(m_next);
+  int tq[NST];
+  tq[0] = next_tile(-1);
+  for (int i = 1; i < NST; ++i) tq[i] = tq[i - 1] >= 0 ? next_tile(tq[i - 1]) : -1;
+  if (tq[0] >= 0) issue(tq[0], std::integral_constant<int, 0>{});
+  if (NST > 2 && tq[1] >= 0) issue(tq[1], std::integral_constant<int, 1>{});
+  if (NST > 3 && tq[2] >= 0) issue(tq[2], std::integral_constant<int, 2>{});
 
+  // One pipeline step on ring stage P; returns false once the tiles are done.
+  auto step = [&](auto tag) -> bool {
+    constexpr int P = decltype(tag)::value;
+    if (tq[0] < 0) return false;
+    const int m = tq[0];
+    int after = 0;
+    for (int i = 1; i < NST - 1; ++i) after += tq[i] >= 0;
+    wait_tile(after);
+    __syncthreads();
+    if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{});
+    const uint16_t* Ks = kst(tag);
+    const uint16_t* Vs = vst(tag);
+    const float* Ss = sst(tag);
     // Which subtiles take part, and each lane's bias for its row.
     bool need[NSUB];
     float bias2[NSUB];
@@ -294,23 +365,29 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
           cursor[s] = cu;
         } else {
           sel = true;
+          bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
         }
       }
-      const bool any = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
-      need[s] = any;
-      float bb = kNegInf;
-      if (own) bb = 0.f;
-      else if (sel) bb = SPARSE ? bsel : (s_cur[s] - lses[s]) * kLog2e;
-      bias2[s] = bb;
+      need[s] = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
+      bias2[s] = own ? 0.f : (sel ? bsel : kNegInf);
     }
 
+    bool any_need = false;
+    for (int s = 0; s < NSUB; ++s) any_need |= need[s];
+    if (!any_need) {  // wave-uniform: nothing of this tile for this wave
+      for (int i = 0; i < NST - 1; ++i) tq[i] = tq[i + 1];
+      tq[NST - 1] = tq[NST - 2] >= 0 ? next_tile(tq[NST - 2]) : -1;
+      return true;
+    }
     // S^T = K Q^T for every needed subtile.
     f32x4 sacc[NSUB][4];
     for (int s = 0; s < NSUB; ++s)
       for (int mt = 0; mt < 4; ++mt) sacc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int ks = 0; ks < KS; ++ks) {
       for (int mt = 0; mt < 4; ++mt) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(&Ks[buf][16 * mt + lr][ks * 32 + lq * 8]);
+        const int key = 16 * mt + lr;
+        const uint4 kf =
+            *reinterpret_cast<const uint4*>(Ks + key * D + (((ks * 4 + lq) ^ k_swz<D>(key)) * 8));
         for (int s = 0; s < NSUB; ++s)
           if (need[s]) sacc[s][mt] = mfma16(kf, qf[s][ks], sacc[s][mt]);
       }
@@ -352,17 +429,24 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     }
     // O^T += V^T P^T.
     for (int md = 0; md < MD; ++md) {
+      const int d = 16 * md + lr;
       for (int kk = 0; kk < 2; ++kk) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(&Vt[buf][16 * md + lr][kk * 32 + lq * 8]);
+        const uint4 vf = *reinterpret_cast<const uint4*>(Vs + d * KT + (((kk * 4 + lq) ^ vt_swz(d)) * 8));
         for (int s = 0; s < NSUB; ++s)
           if (need[s]) oacc[s][md] = mfma16(vf, pf[s][kk], oacc[s][md]);
       }
     }
-    if (m_next >= 0) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    for (int s = 0; s < NSUB; ++s) s_cur[s] = s_nxt[s];
-    m = m_next;
+    for (int i = 0; i < NST - 1; ++i) tq[i] = tq[i + 1];
+    tq[NST - 1] = tq[NST - 2] >= 0 ? next_tile(tq[NST - 2]) : -1;
+    return true;
+  };
+  while (true) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if constexpr (NST > 2)
+      if (!step(std::integral_constant<int, 2>{})) break;
+    if constexpr (NST > 3)
+      if (!step(std::integral_constant<int, 3>{})) break;
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -387,43 +471,52 @@ template <int D, int G, bool SPARSE>
 hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
   // Sparse scope: wider workgroups (more tokens share each K/V tile load).
   constexpr int NSUB = 2;
-  constexpr int WAVES = SPARSE ? 8 : 4;
+  constexpr int WAVES = 8;
+  constexpr int NST = 3;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   FwdArgs a = a0;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
-  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + (2 + G) * size_t(TOK_WG) * a.topk) * 4 : 0;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES),
-                     dyn, stream, a);
+  hipLaunchKernelGGL((vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
+                     const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, WAVES, NST, SPARSE>),
+                     dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Shapes the matrix-core forward covers: bf16, block 64, D 64/128, G in
-// {1,2,4,8}; sparse scope needs the per-workgroup index lists to fit in LDS.
+// {1,2,4,8}, at least one complete block; sparse scope needs the per-workgroup
+// index lists and bias table to fit in LDS.
 bool fwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   if (d.block != KT || (d.D != 64 && d.D != 128)) return false;
+  if (d.C < 1) return false;
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (sparse) {
-    // LDS of the sparse prologue: sorted/raw lists (tokens x topk) and the gate
-    // bias table (256 rows x topk).
-    if (size_t(256) * topk > 8192) return false;
-    if (((d.C + 32) >> 5) > 1024) return false;
+    // sorted lists (tokens x topk) and the gate bias table (256 rows x topk)
+    if (size_t(256) * topk > kBiasMax || size_t(256 / G) * topk > kListMax) return false;
+    if (((d.C + 32) >> 5) > kMaskWords) return false;
   }
   return true;
 }
 
+size_t fwd_mfma_workspace(const Dims& d) {
+  const int NB = (d.N + KT - 1) / KT;
+  return align_up(size_t(d.B) * d.Hkv * NB * KT * d.D * sizeof(bf16_t));
+}
+
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, hipStream_t s) {
-  FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, scores, idx, (bf16_t*)o, lse, lse_s,
-            d.Hq, d.Hkv, d.N, d.C, idx ? topk : 0, 0, 0, scale};
+                           int topk, float scale, void* ws, hipStream_t s) {
+  FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores, idx,
+            (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, idx ? topk : 0, 0, 0,
+            (d.N + KT - 1) / KT, scale};
   const int G = d.G();
   const bool sp = idx != nullptr;
-#define SAS_FWD_CASE(DD, GG)                                             \
-  if (d.D == DD && G == GG) {                                            \
+#define SAS_FWD_CASE(DD, GG)                                                                  \
+  if (d.D == DD && G == GG) {                                                                 \
     return sp ? fwd_mfma_t<DD, GG, true>(a, d.B, s) : fwd_mfma_t<DD, GG, false>(a, d.B, s); \
   }
   SAS_FWD_CASE(128, 4)
