@@ -104,6 +104,37 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | 0xF00 | (((n >> 4) & 3) << 14));
 }
 
+// LSE_s of every query row over its history scores (the gate normaliser):
+// one wave per row, a single pass of running (max, sum) per lane, then a
+// butterfly merge.  Rows without history get -inf.
+__global__ __launch_bounds__(256) void lse_rows_kernel(const float* __restrict__ scores,
+                                                       float* __restrict__ lse_s, int N, int C,
+                                                       int block, size_t rows) {
+  const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int t = int(row % size_t(N));
+  const int c = min(t / block, C);
+  const float* srow = scores + row * size_t(C);
+  float mx = kNegInf, sm = 0.f;
+  for (int m = lane; m < c; m += 64) {
+    const float x = srow[m];
+    if (x > mx) {
+      sm = sm * exp2_hw((mx - x) * kLog2e) + 1.f;
+      mx = x;
+    } else if (mx != kNegInf) {
+      sm += exp2_hw((x - mx) * kLog2e);
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float mo = shfl_xor(mx, off), so = shfl_xor(sm, off);
+    const float mn = fmaxf(mx, mo);
+    if (mn != kNegInf) sm = sm * exp2_hw((mx - mn) * kLog2e) + so * exp2_hw((mo - mn) * kLog2e);
+    mx = mn;
+  }
+  if (lane == 0) lse_s[row] = c > 0 ? mx + log_hw(sm) : kNegInf;
+}
+
 template <int D, int G, int NSUB, int WAVES, int NST, bool SPARSE>
 __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int NT = 64 * WAVES;
@@ -119,6 +150,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
   static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
   static_assert(kBiasMax >= kListMax, "raw index scratch reuses the bias table");
+  static_assert(NSUB == 1 || NSUB == 2, "one or two subtiles per wave");
   // One array per ring stage: the compiler can then tell a stage being read
   // from the stages the in-flight loads write, and adds no waits of its own.
   __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8],
@@ -155,29 +187,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     sub_live[s] = t0 < N;
   }
 
-  // ---- LSE of each row's history scores (gate normaliser) -------------------
-  for (int rr = 0; rr < 16 * NSUB; ++rr) {
-    const int s = rr >> 4, r = rr & 15;
-    const int sg = wave * NSUB + s;
+  // ---- gate normaliser LSE_s of each row (written by lse_rows_kernel) ---------
+  for (int i = tid; i < ROWS_WG; i += NT) {
+    const int sg = i >> 4, r = i & 15;
     const int t = t_wg0 + sg * TOK_SUB + r / G;
-    const int h = g * G + r % G;
-    float res = kNegInf;
-    if (t < N) {
-      const int c = t / KT;
-      const float* srow = a.scores + ((size_t(b) * a.Hq + h) * N + t) * C;
-      float mx = kNegInf;
-      for (int m = lane; m < c; m += 64) mx = fmaxf(mx, srow[m]);
-      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-      float sm = 0.f;
-      if (c > 0) {
-        for (int m = lane; m < c; m += 64) sm += exp2_hw((srow[m] - mx) * kLog2e);
-        for (int off = 32; off >= 1; off >>= 1) sm += shfl_xor(sm, off);
-        res = mx + log_hw(sm);
-      }
-      if (lane == 0) a.lse_s[(size_t(b) * a.Hq + h) * N + t] = res;
-    }
-    if (lane == 0) lses_sh[wave * 16 * NSUB + rr] = res;
+    lses_sh[i] = t < N ? a.lse_s[(size_t(b) * a.Hq + g * G + r % G) * N + t] : kNegInf;
   }
+  __syncthreads();
 
   // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
   const int MW = (C + 32) >> 5;  // bits 0..C (the own block may be block C)
@@ -288,16 +304,36 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     else if constexpr (P == 2) return S2;
     else return S3;
   };
+  // This lane's 16-byte piece i of a K tile, as an element offset in the tile:
+  // tile row r, stored chunk pc, source chunk pc ^ k_swz(r).
+  uint32_t k_goff[LPW];
+  for (int i = 0; i < LPW; ++i) {
+    const int sl = 64 * (wave * LPW + i) + lane;
+    const int r = sl / CH, pc = sl % CH;
+    k_goff[i] = uint32_t(r * D + (pc ^ k_swz<D>(r)) * 8);
+  }
   auto issue = [&](int m, auto tag) {
     uint16_t* kd = kst(tag);
     uint16_t* vd = vst(tag);
-    for (int i = 0; i < LPW; ++i) {
-      const int j = wave * LPW + i;  // 1 KB piece of the tile
-      const int sl = 64 * j + lane;  // 16-byte slot
-      const int r = sl / CH, pc = sl % CH;
-      const int key = min(m * KT + r, N - 1);
-      const int c = pc ^ k_swz<D>(r);
-      __builtin_amdgcn_global_load_lds(kh + size_t(key) * D + c * 8, (lds_ptr_t)(kd + j * 512), 16, 0, 0);
+    if (m * KT + KT <= N) {
+      // whole tile: uniform tile base plus this lane's offset inside the tile
+      const bf16_t* kt = kh + size_t(m) * KT * D;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        uint32_t off = k_goff[i];
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(kt + off, (lds_ptr_t)(kd + (wave * LPW + i) * 512), 16, 0, 0);
+      }
+    } else {
+      // tail tile: keys past N repeat key N-1 (their logits are masked)
+      for (int i = 0; i < LPW; ++i) {
+        const int j = wave * LPW + i;  // 1 KB piece of the tile
+        const int sl = 64 * j + lane;  // 16-byte slot
+        const int r = sl / CH, pc = sl % CH;
+        const int key = min(m * KT + r, N - 1);
+        const int c = pc ^ k_swz<D>(r);
+        __builtin_amdgcn_global_load_lds(kh + size_t(key) * D + c * 8, (lds_ptr_t)(kd + j * 512), 16, 0, 0);
+      }
     }
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
@@ -325,6 +361,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     lpart[s] = 0.f;
   }
   const float c1 = a.scale * kLog2e;
+  // MFMA operand reads.  K row key = 16 mt + lr holds chunk (4 ks + lq) at
+  // chunk (4 ks + lq) ^ sw with sw = k_swz(key) (a function of lr alone); the
+  // XOR splits into a lane part (low two bits) and (ks ^ (sw >> 2)) * 4.
+  // V^T row d = 16 md + lr likewise with sw = vt_swz(lr).
+  const int ksw = k_swz<D>(lr), vsw = vt_swz(lr);
+  const uint32_t k_base = lr * D + ((lq ^ (ksw & 3)) * 8), k_xor = (ksw >> 2) * 32;
+  const uint32_t v_base = lr * KT + ((lq ^ (vsw & 3)) * 8), v_xor = (vsw >> 2) * 32;
 
   int tq[NST];
   tq[0] = next_tile(-1);
@@ -334,9 +377,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   if (NST > 3 && tq[2] >= 0) issue(tq[2], std::integral_constant<int, 2>{});
 
   // One pipeline step on ring stage P; returns false once the tiles are done.
-  auto step = [&](auto tag) -> bool {
+  // One pipeline step on ring stage P for tile tq[0] >= 0.  MK: the tile may be
+  // a subtile's own block (keys above the row are masked).
+  auto step = [&](auto tag, auto mkt) {
     constexpr int P = decltype(tag)::value;
-    if (tq[0] < 0) return false;
+    constexpr bool MK = decltype(mkt)::value;
     const int m = tq[0];
     int after = 0;
     for (int i = 1; i < NST - 1; ++i) after += tq[i] >= 0;
@@ -346,8 +391,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     const uint16_t* Ks = kst(tag);
     const uint16_t* Vs = vst(tag);
     const float* Ss = sst(tag);
-    // Which subtiles take part, and each lane's bias for its row.
-    bool need[NSUB];
+    // Which subtiles take part (a wave-uniform bit mask), and each lane's bias
+    // for its row (base 2; -inf where the row does not attend the tile).
+    int nmask = 0;
     float bias2[NSUB];
     for (int s = 0; s < NSUB; ++s) {
       const bool own = (m == c_sub[s]);
@@ -368,92 +414,136 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
           bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
         }
       }
-      need[s] = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
+      const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
+      nmask |= int(nd) << s;
       bias2[s] = own ? 0.f : (sel ? bsel : kNegInf);
     }
+    nmask = __builtin_amdgcn_readfirstlane(nmask);
 
-    bool any_need = false;
-    for (int s = 0; s < NSUB; ++s) any_need |= need[s];
-    if (!any_need) {  // wave-uniform: nothing of this tile for this wave
-      for (int i = 0; i < NST - 1; ++i) tq[i] = tq[i + 1];
-      tq[NST - 1] = tq[NST - 2] >= 0 ? next_tile(tq[NST - 2]) : -1;
-      return true;
-    }
-    // S^T = K Q^T for every needed subtile.
-    f32x4 sacc[NSUB][4];
-    for (int s = 0; s < NSUB; ++s)
-      for (int mt = 0; mt < 4; ++mt) sacc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < KS; ++ks) {
-      for (int mt = 0; mt < 4; ++mt) {
-        const int key = 16 * mt + lr;
-        const uint4 kf =
-            *reinterpret_cast<const uint4*>(Ks + key * D + (((ks * 4 + lq) ^ k_swz<D>(key)) * 8));
-        for (int s = 0; s < NSUB; ++s)
-          if (need[s]) sacc[s][mt] = mfma16(kf, qf[s][ks], sacc[s][mt]);
-      }
-    }
-    // Online softmax (base 2) and P^T fragments.
-    uint4 pf[NSUB][2];
-    for (int s = 0; s < NSUB; ++s) {
-      if (!need[s]) continue;
-      const bool own = (m == c_sub[s]);
-      float z[4][4];
-      float mx = kNegInf;
-      for (int mt = 0; mt < 4; ++mt)
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[s][mt][i] * c1 + bias2[s];
-          if (own && (m * KT + 16 * mt + 4 * lq + i > row_t[s])) v = kNegInf;
-          z[mt][i] = v;
-          mx = fmaxf(mx, v);
+    // Straight-line compute of the subtiles in SM.
+    auto compute = [&](auto smt) {
+      constexpr int SM = decltype(smt)::value;
+      f32x4 sacc[NSUB][4];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sacc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // S^T = K Q^T
+      // Operand offsets: a lane base plus an XOR term per k step (one v_xad at
+      // the use); opaque, so no register is kept per (stage, step).
+      uint32_t kb = k_base, kx = k_xor, vb = v_base, vx = v_xor;
+      asm volatile("" : "+v"(kb), "+v"(kx), "+v"(vb), "+v"(vx));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(Ks + mt * 16 * D + (((ks * 32) ^ kx) + kb));
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s)
+            if ((SM >> s) & 1) sacc[s][mt] = mfma16(kf, qf[s][ks], sacc[s][mt]);
         }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[s], mx);
-      const float muse = (mnew == kNegInf) ? 0.f : mnew;
-      const float alpha = exp2_hw(mrow[s] - muse);
-      mrow[s] = mnew;
-      float ps = 0.f;
-      for (int mt = 0; mt < 4; ++mt)
-        for (int i = 0; i < 4; ++i) {
-          z[mt][i] = exp2_hw(z[mt][i] - muse);
-          ps += z[mt][i];
+      }
+      // Online softmax (base 2).  The bias is constant over the tile, so the
+      // row max is scale * max(S) + bias.  The running max moves only when it
+      // grows by more than 2^8, which bounds every P by 256 and skips most
+      // rescales of the output accumulators.
+      uint4 pf[NSUB][2];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        if (!((SM >> s) & 1)) continue;
+        if (MK) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (m * KT + 16 * mt + 4 * lq + i > row_t[s]) sacc[s][mt][i] = kNegInf;
         }
-      lpart[s] = lpart[s] * alpha + ps;
-      for (int md = 0; md < MD; ++md) oacc[s][md] *= alpha;
-      for (int kk = 0; kk < 2; ++kk) {
-        pf[s][kk].x = pack_bf16(z[2 * kk][0], z[2 * kk][1]);
-        pf[s][kk].y = pack_bf16(z[2 * kk][2], z[2 * kk][3]);
-        pf[s][kk].z = pack_bf16(z[2 * kk + 1][0], z[2 * kk + 1][1]);
-        pf[s][kk].w = pack_bf16(z[2 * kk + 1][2], z[2 * kk + 1][3]);
+        float mr = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          mr = fmaxf(fmaxf(mr, fmaxf(sacc[s][mt][0], sacc[s][mt][1])), fmaxf(sacc[s][mt][2], sacc[s][mt][3]));
+        mr = max_xrows(mr);
+        const float mx = mr * c1 + bias2[s];
+        const bool upd = mx > mrow[s] + 8.f;
+        if (__any(upd)) {
+          const float alpha = upd ? exp2_hw(mrow[s] - mx) : 1.f;
+          mrow[s] = upd ? mx : mrow[s];
+          lpart[s] *= alpha;
+#pragma unroll
+          for (int md = 0; md < MD; ++md) oacc[s][md] *= alpha;
+        }
+        const float off = bias2[s] - (mrow[s] == kNegInf ? 0.f : mrow[s]);
+        float ps = 0.f;
+        float z[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[mt][i] = exp2_hw(fmaf(sacc[s][mt][i], c1, off));
+            ps += z[mt][i];
+          }
+        lpart[s] += ps;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pf[s][kk].x = pack_bf16(z[2 * kk][0], z[2 * kk][1]);
+          pf[s][kk].y = pack_bf16(z[2 * kk][2], z[2 * kk][3]);
+          pf[s][kk].z = pack_bf16(z[2 * kk + 1][0], z[2 * kk + 1][1]);
+          pf[s][kk].w = pack_bf16(z[2 * kk + 1][2], z[2 * kk + 1][3]);
+        }
       }
-    }
-    // O^T += V^T P^T.
-    for (int md = 0; md < MD; ++md) {
-      const int d = 16 * md + lr;
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(Vs + d * KT + (((kk * 4 + lq) ^ vt_swz(d)) * 8));
-        for (int s = 0; s < NSUB; ++s)
-          if (need[s]) oacc[s][md] = mfma16(vf, pf[s][kk], oacc[s][md]);
+      // Keep the V^T operand reads below the softmax (register pressure).
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint4 vf = *reinterpret_cast<const uint4*>(Vs + md * 16 * KT + (((kk * 32) ^ vx) + vb));
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s)
+            if ((SM >> s) & 1) oacc[s][md] = mfma16(vf, pf[s][kk], oacc[s][md]);
+        }
       }
+    };
+    if (nmask) {
+      // every subtile of the wave (a subtile without the tile has bias -inf
+      // on all rows and adds nothing)
+      compute(std::integral_constant<int, (1 << NSUB) - 1>{});
     }
     for (int i = 0; i < NST - 1; ++i) tq[i] = tq[i + 1];
     tq[NST - 1] = tq[NST - 2] >= 0 ? next_tile(tq[NST - 2]) : -1;
-    return true;
   };
+  // History tiles of every subtile (no masking), then the workgroup's own
+  // blocks (masked), continuing the ring where the first loop stopped.
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  const int c_first = t_wg0 / KT;
+  int ph = 0;
   while (true) {
-    if (!step(std::integral_constant<int, 0>{})) break;
-    if (!step(std::integral_constant<int, 1>{})) break;
-    if constexpr (NST > 2)
-      if (!step(std::integral_constant<int, 2>{})) break;
-    if constexpr (NST > 3)
-      if (!step(std::integral_constant<int, 3>{})) break;
+    if (tq[0] < 0 || tq[0] >= c_first) { ph = 0; break; }
+    step(std::integral_constant<int, 0>{}, Unmasked{});
+    if (tq[0] < 0 || tq[0] >= c_first) { ph = 1; break; }
+    step(std::integral_constant<int, 1>{}, Unmasked{});
+    if constexpr (NST > 2) {
+      if (tq[0] < 0 || tq[0] >= c_first) { ph = 2; break; }
+      step(std::integral_constant<int, 2>{}, Unmasked{});
+    }
+    if constexpr (NST > 3) {
+      if (tq[0] < 0 || tq[0] >= c_first) { ph = 3; break; }
+      step(std::integral_constant<int, 3>{}, Unmasked{});
+    }
+  }
+  while (tq[0] >= 0) {
+    if (ph == 0) step(std::integral_constant<int, 0>{}, Masked{});
+    else if (ph == 1) step(std::integral_constant<int, 1>{}, Masked{});
+    else if (NST > 2 && ph == 2) step(std::integral_constant<int, (NST > 2 ? 2 : 0)>{}, Masked{});
+    else if (NST > 3) step(std::integral_constant<int, (NST > 3 ? 3 : 0)>{}, Masked{});
+    ph = ph + 1 == NST ? 0 : ph + 1;
   }
 
   // ---- epilogue ---------------------------------------------------------------
   for (int s = 0; s < NSUB; ++s) {
-    float l = lpart[s];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    const float l = sum_xrows(lpart[s]);
     if (row_t[s] >= N) continue;
     const size_t row = (size_t(b) * a.Hq + row_h[s]) * N + row_t[s];
     const float inv = 1.f / l;
@@ -477,6 +567,9 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
   FwdArgs a = a0;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
+  const size_t rows = size_t(B) * a.Hq * a.N;
+  hipLaunchKernelGGL(lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
+                     a.lse_s, a.N, a.C, KT, rows);
   hipLaunchKernelGGL((vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
                      const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, WAVES, NST, SPARSE>),

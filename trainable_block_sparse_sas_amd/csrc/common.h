@@ -40,6 +40,21 @@ __device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one 16-lane column of an
+// MFMA accumulator tile) with the gfx950 row swaps instead of LDS permutes.
+__device__ __forceinline__ float max_xrows(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_xrows(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Order-preserving map of an fp32 value to uint32 (larger float -> larger key).
 // -0.0 is folded onto +0.0 and NaN onto -inf first.
 __device__ __forceinline__ uint32_t score_key(float f) {
