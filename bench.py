@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="training workload only (no decode, no full scope)")
     ap.add_argument("--workload", default="train-32k-sparse")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device copy first (counter calibration)")
     return ap.parse_args()
 
 
@@ -112,15 +114,22 @@ def bench_train(torch, w, steps, warmup, scope_topk="cfg"):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ms_step = s0.elapsed_time(s1) / steps
-    # Per-stage split in separate, event-bracketed steps.
-    for _ in range(max(2, steps // 2)):
+    # Per-stage split in separate, event-bracketed steps; the library brackets
+    # each of its kernels with HIP events on the same stream meanwhile.
+    from trainable_block_sparse_sas_amd import binding as sas
+    sas.sas_profile_read()
+    sas.sas_profile_enable(True)
+    n_split = max(2, steps // 2)
+    for _ in range(n_split):
         one(True)
     torch.cuda.synchronize()
+    sas.sas_profile_enable(False)
+    kernels = {name: (ms / cnt, cnt // n_split) for name, (ms, cnt) in sas.sas_profile_read().items()}
     pairs = attended_pairs(w.N, w.block, topk, w.Hq, w.B)
     fl_fwd = 4 * w.D * pairs
     fl_bwd = 10 * w.D * pairs
     return dict(ms_step=ms_step, wall_ms_step=wall, pairs=pairs, flops_fwd=fl_fwd, flops_bwd=fl_bwd,
-                ms_select=tm.ms("select"), ms_fwd=tm.ms("fwd"), ms_bwd=tm.ms("bwd"))
+                ms_select=tm.ms("select"), ms_fwd=tm.ms("fwd"), ms_bwd=tm.ms("bwd"), kernels=kernels)
 
 
 def bench_decode(torch, w, steps, warmup, dense=False):
@@ -171,6 +180,71 @@ def bench_decode(torch, w, steps, warmup, dense=False):
                 attend_gbs=kv_bytes / (tm.ms("attend") * 1e-3) / 1e9)
 
 
+# Algorithmic work of the matrix-core kernels per attended (query row, key)
+# pair: the forward's S = QK^T and PV (4D flops); the dQ kernel's S and dP
+# recompute plus dS K (6D); the dK/dV kernel's S and dP recompute plus P^T dO
+# and dS^T Q (8D).
+KERNEL_FLOPS_PER_PAIR = {"fwd_mfma": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+KERNEL_SOURCES = {"fwd_mfma": "attn_fwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
+                  "bwd_dkdv": "attn_bwd_mfma.hip"}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    csrc = os.path.join(ROOT, "trainable_block_sparse_sas_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h", "mfma.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    and workload, if the kernel's sources are unchanged since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline(kernels, pairs, D, workload):
+    """Roofline entry for the kernel with the largest share of the step."""
+    name = max((k for k in kernels if k in KERNEL_FLOPS_PER_PAIR),
+               key=lambda k: kernels[k][0] * kernels[k][1])
+    ms = kernels[name][0]
+    flops = KERNEL_FLOPS_PER_PAIR[name] * D * pairs
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": name, "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+            "traffic": measured_traffic(name, workload),
+            "flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
+            "timing": "HIP events around each launch on its stream (library kernel timing)"}
+
+
+def copy_probe(torch):
+    """One plain streaming kernel over 1 GiB (bitwise not of 2^28 int32: 1 GiB
+    read, 1 GiB written); its counter readings calibrate FETCH_SIZE and
+    WRITE_SIZE."""
+    src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(w):
     """The oracle, as it stands, on a bounded prefix sample of the workload."""
     import numpy as np
@@ -179,7 +253,7 @@ def cpu_baseline(w):
     from oracle import sas_oracle as orc
     from trainable_block_sparse_sas_amd.inputs import training_inputs
 
-    n_s = 4096
+    n_s = 16384
     ws = w.with_(N=n_s, Hq=w.Hq // w.Hkv, Hkv=1, B=1)
     q, k, v, do = training_inputs(ws, device="cpu", seed=1000 + w.index)
     f = lambda t: t.to(torch.float64).numpy()
@@ -218,9 +292,10 @@ def main():
     wmap = {w.name: w for w in WORKLOADS}
     w = wmap[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
     tr = bench_train(torch, w, args.steps, args.warmup)
     tflops = (tr["flops_fwd"] + tr["flops_bwd"]) / (tr["ms_step"] * 1e-3) / 1e12
-    bwd_tf = tr["flops_bwd"] / (tr["ms_bwd"] * 1e-3) / 1e12
     out = {
         "metric": "gated attn fwd+bwd TFLOP/s @32K (sparse scope, Top-K 32)",
         "value": round(tflops, 3),
@@ -240,9 +315,8 @@ def main():
         "stages_ms": {"select": round(tr["ms_select"], 4), "fwd": round(tr["ms_fwd"], 4),
                       "bwd": round(tr["ms_bwd"], 4)},
         "attended_pairs": tr["pairs"],
-        "roofline": {"bound": "mfma", "kernel": "gated bwd", "achieved": round(bwd_tf, 3),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 5),
-                     "traffic": None},
+        "kernels_ms": {k: round(v[0], 4) for k, v in sorted(tr["kernels"].items(), key=lambda kv: -kv[1][0])},
+        "roofline": roofline(tr["kernels"], tr["pairs"], w.D, w.name),
     }
     if not args.quick:
         full = bench_train(torch, w, max(2, args.steps // 2), 1, scope_topk=None)

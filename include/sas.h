@@ -31,7 +31,7 @@
  *   `dtype` (sas_dtype) is the element type of q, k, v, o, dO, dq, dk, dv
  *   and kbar.  Query head h reads KV head h / (Hq / Hkv) (grouped-query
  *   attention).  `scale` multiplies q.k in the logits and in the selector
- *   score (1/sqrt(D) in the usual setting).
+ *   score (1/sqrt(D) in the usual setting); it must be positive and finite.
  *
  *   Positions.  Training calls (cache_len == NULL) place query t at position
  *   t.  Decode calls place the single new token of sequence b at position
@@ -204,6 +204,22 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
  */
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n_or_lmax, int D,
                            int block, int topk, int dtype);
+
+/*
+ * Kernel timing (diagnostics; not part of the method).
+ * sas_profile_enable(1) makes every later kernel launch record a HIP event on
+ *   its stream just before and just after the kernel; (0) stops recording.
+ *   Events are host-side objects: no device memory is allocated.
+ * sas_profile_read waits for every recorded launch, sums the durations per
+ *   kernel name, writes up to max_entries of them (name as a NUL-terminated
+ *   string in a slot of name_bytes bytes of `names`, total milliseconds in
+ *   ms[i], launches in counts[i]), clears the record and returns the number of
+ *   distinct kernels (which may exceed max_entries).  SAS_EINVAL for bad
+ *   arguments, SAS_EHIP if an event could not be read.
+ */
+int sas_profile_enable(int on);
+int sas_profile_read(int max_entries, char* names, int name_bytes, double* ms,
+                     int* counts);
 
 /* Message for the last non-OK status returned on this thread. */
 const char* sas_last_error(void);

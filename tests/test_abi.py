@@ -25,14 +25,15 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
                           "sas_gated_attn_bwd", "sas_sparse_decode", "sas_workspace_bytes",
-                          "sas_last_error", "sas_abi_version"}
+                          "sas_last_error", "sas_abi_version", "sas_profile_enable",
+                          "sas_profile_read"}
     for n in names:
         assert hasattr(L, n), n
         assert n in sas.EXPORTED
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 100
+    assert sas.sas_abi_version() == 101
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
@@ -40,9 +41,10 @@ def test_version_and_workspace_sizes():
     assert sas.sas_workspace_bytes(99, 1, 4, 2, 64, 128, 64, -1, 1) == ctypes.c_size_t(-1).value
 
 
-def fwd(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, topk=0, dtype=1, ptr=1, idx=None, ws=None, wsb=0):
+def fwd(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, topk=0, dtype=1, ptr=1, idx=None, ws=None, wsb=0,
+        scale=0.1):
     p = ctypes.c_void_p(ptr) if ptr else None
-    return L.sas_gated_attn_fwd(p, p, p, p, idx, p, p, p, B, Hq, Hkv, N_, D, block, topk, 0.1, dtype,
+    return L.sas_gated_attn_fwd(p, p, p, p, idx, p, p, p, B, Hq, Hkv, N_, D, block, topk, scale, dtype,
                                 ws, wsb, None)
 
 
@@ -56,6 +58,10 @@ def fwd(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, topk=0, dtype=1, ptr=1, idx=N
     (dict(ptr=0), sas.SAS_EINVAL, "non-NULL"),
     (dict(idx=ctypes.c_void_p(8), topk=-1), sas.SAS_EINVAL, "topk"),
     (dict(idx=ctypes.c_void_p(8), topk=300), sas.SAS_EUNSUPPORTED, "topk"),
+    (dict(scale=0.0), sas.SAS_EINVAL, "scale"),
+    (dict(scale=-0.5), sas.SAS_EINVAL, "scale"),
+    (dict(scale=float("nan")), sas.SAS_EINVAL, "scale"),
+    (dict(scale=float("inf")), sas.SAS_EINVAL, "scale"),
 ])
 def test_fwd_rejects(kw, code, msg):
     assert fwd(**kw) == code
@@ -93,6 +99,28 @@ def test_other_entry_points_reject():
     assert L.sas_sparse_decode(*dargs2, v, 1 << 30, N) == sas.SAS_EINVAL
     dargs3 = [v, v, v, v, N, v, N, 2, 40, 2, 1024, 128, 64, 4, 0.1, 1]
     assert L.sas_sparse_decode(*dargs3, v, 1 << 30, N) == sas.SAS_EUNSUPPORTED
+
+
+def test_scale_checked_by_every_scaled_call():
+    v = ctypes.c_void_p(8)
+    assert L.sas_score_blocks(v, v, v, v, N, 1, 4, 2, 128, 128, 128, 64, -1.0, 0, 1, N) == sas.SAS_EINVAL
+    args = [v] * 13 + [1, 4, 2, 128, 128, 64, 0, 0.0, 1]
+    assert L.sas_gated_attn_bwd(*args, v, 1 << 30, N) == sas.SAS_EINVAL
+    dargs = [v, v, v, v, N, v, N, 2, 8, 2, 1024, 128, 64, 4, float("nan"), 1]
+    assert L.sas_sparse_decode(*dargs, v, 1 << 30, N) == sas.SAS_EINVAL
+    assert "scale" in sas.sas_last_error()
+
+
+def test_profile_api_without_launches():
+    sas.sas_profile_enable(True)
+    sas.sas_profile_enable(False)
+    assert sas.sas_profile_read() == {}
+    names = ctypes.create_string_buffer(8)
+    ms = (ctypes.c_double * 1)()
+    cnt = (ctypes.c_int * 1)()
+    assert L.sas_profile_read(-1, names, 8, ms, cnt) == sas.SAS_EINVAL
+    assert L.sas_profile_read(1, names, 0, ms, cnt) == sas.SAS_EINVAL
+    assert L.sas_profile_read(1, None, 8, ms, cnt) == sas.SAS_EINVAL
 
 
 def test_errors_are_thread_local():

@@ -27,7 +27,8 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE = 1, 2, 3, 4, 5
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-            "sas_sparse_decode", "sas_workspace_bytes", "sas_last_error", "sas_abi_version")
+            "sas_sparse_decode", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.sas_score_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
@@ -39,6 +40,11 @@ _lib.sas_workspace_bytes.argtypes = [_i] * 9
 _lib.sas_workspace_bytes.restype = _sz
 _lib.sas_last_error.restype = ctypes.c_char_p
 _lib.sas_abi_version.restype = _i
+_lib.sas_profile_enable.argtypes = [_i]
+_lib.sas_profile_enable.restype = _i
+_lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(_i)]
+_lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
               "sas_sparse_decode"):
     getattr(_lib, _name).restype = _i
@@ -95,6 +101,25 @@ def _check(code: int):
 
 def sas_abi_version() -> int:
     return _lib.sas_abi_version()
+
+
+def sas_profile_enable(on: bool = True) -> None:
+    _check(_lib.sas_profile_enable(int(bool(on))))
+
+
+def sas_profile_read(max_entries: int = 64) -> dict:
+    """{kernel name: (total ms, launches)} since the last read (waits for them)."""
+    nb = 48
+    names = ctypes.create_string_buffer(max_entries * nb)
+    ms = (ctypes.c_double * max_entries)()
+    counts = (_i * max_entries)()
+    n = _lib.sas_profile_read(max_entries, names, nb, ms, counts)
+    if n < 0:
+        raise SasError(n, "sas_profile_read failed")
+    out = {}
+    for i in range(min(n, max_entries)):
+        out[names.raw[i * nb:(i + 1) * nb].split(b"\0", 1)[0].decode()] = (ms[i], counts[i])
+    return out
 
 
 def sas_last_error() -> str:

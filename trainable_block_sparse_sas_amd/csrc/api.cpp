@@ -46,13 +46,22 @@ int check_common(int B, int Hq, int Hkv, int n, int D, int block, int dtype, con
 
 bool empty(int B, int Hq, int n) { return B == 0 || Hq == 0 || n == 0; }
 
+// The logit scale must be a positive finite number (the kernels take the row
+// maximum of the raw scores, which is the maximum of the scaled ones only for
+// a positive scale).
+int check_scale(float scale, const char* what) {
+  if (!(scale > 0.f) || !(scale < __builtin_huge_valf()))
+    return fail(SAS_EINVAL, "%s: scale must be positive and finite (got %g)", what, double(scale));
+  return SAS_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 100; }
+int sas_abi_version(void) { return 101; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
@@ -78,6 +87,7 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
                      const int32_t* cache_len, int B, int Hq, int Hkv, int Nq, int L, int D,
                      int block, float scale, int group_sum, int dtype, void* stream) {
   int st = check_common(B, Hq, Hkv, L, D, block, dtype, "sas_score_blocks");
+  if (!st) st = check_scale(scale, "sas_score_blocks");
   if (st) return st;
   if (Nq < 0) return fail(SAS_EINVAL, "sas_score_blocks: Nq must be >= 0");
   const int C = L / block;
@@ -151,6 +161,7 @@ int sas_gated_attn_fwd(const void* q, const void* k, const void* v, const float*
                        int Hkv, int N, int D, int block, int topk, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_attn("sas_gated_attn_fwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (!st) st = check_scale(scale, "sas_gated_attn_fwd");
   if (st) return st;
   if (empty(B, Hq, N)) {
     g_error.clear();
@@ -175,6 +186,7 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        float scale, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
   int st = check_attn("sas_gated_attn_bwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (!st) st = check_scale(scale, "sas_gated_attn_bwd");
   if (st) return st;
   if (empty(B, Hq, N)) {
     g_error.clear();
@@ -198,6 +210,7 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       int Hq, int Hkv, int L_max, int D, int block, int topk, float scale,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, "sas_sparse_decode");
+  if (!st) st = check_scale(scale, "sas_sparse_decode");
   if (st) return st;
   if (Hkv > 0 && Hq / Hkv > kMaxGroupDecode)
     return fail(SAS_EUNSUPPORTED, "sas_sparse_decode: at most %d query heads per KV head", kMaxGroupDecode);

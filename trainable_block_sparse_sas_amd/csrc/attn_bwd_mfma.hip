@@ -665,19 +665,19 @@ static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
   constexpr int WAVES = SPARSE ? 8 : 4;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   const size_t rows = size_t(B) * a.Hq * a.N;
-  hipLaunchKernelGGL((bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
+  SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
                      dim3(256), 0, s, a.o, a.dout, a.delta, rows);
   if (SPARSE) {
     const size_t tokens = size_t(B) * a.Hkv * a.N;
-    hipLaunchKernelGGL(selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits, a.N,
+    SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits, a.N,
                        a.topk, a.MWB, tokens);
   }
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
+  SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + (2 + G) * size_t(TOK_WG) * a.topk) * 4 : 0;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), dyn, s, a);
+  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), dyn, s, a);
   return hipGetLastError();
 }
 

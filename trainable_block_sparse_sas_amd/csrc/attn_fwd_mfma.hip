@@ -568,11 +568,11 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
   const size_t rows = size_t(B) * a.Hq * a.N;
-  hipLaunchKernelGGL(lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
+  SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
                      a.lse_s, a.N, a.C, KT, rows);
-  hipLaunchKernelGGL((vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
+  SAS_LAUNCH("vt", (vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
                      const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, G, NSUB, WAVES, NST, SPARSE>),
+  SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST, SPARSE>),
                      dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }

@@ -379,7 +379,7 @@ hipError_t fwd_simt(const void* q, const void* k, const void* v, const float* sc
                     float scale, hipStream_t s) {
   const size_t mask_bytes = idx ? size_t(64) * ((d.C + 31) / 32) * 4 : 0;
   dim3 grid((d.N + 63) / 64, d.Hq, d.B);
-  hipLaunchKernelGGL((fwd_simt_kernel<T, D>), grid, dim3(256), mask_bytes, s, (const T*)q,
+  SAS_LAUNCH("fwd_simt", (fwd_simt_kernel<T, D>), grid, dim3(256), mask_bytes, s, (const T*)q,
                      (const T*)k, (const T*)v, scores, idx, (T*)o, lse, lse_s, d.Hq, d.Hkv, d.N,
                      d.C, d.block, topk, scale);
   return hipGetLastError();
@@ -391,14 +391,14 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
                     void* dq, void* dk, void* dv, float* ds, const Dims& d, int topk, float scale,
                     float* delta, hipStream_t s) {
   const size_t rows = size_t(d.B) * d.Hq * d.N;
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((rows + 63) / 64), dim3(256), 0, s,
+  SAS_LAUNCH("bwd_delta", (bwd_delta_kernel<T, D>), dim3((rows + 63) / 64), dim3(256), 0, s,
                      (const T*)o, (const T*)dout, delta, rows);
   const size_t mask_bytes = idx ? size_t(64) * ((d.C + 31) / 32) * 4 : 0;
-  hipLaunchKernelGGL((bwd_dq_simt_kernel<T, D>), dim3((d.N + 63) / 64, d.Hq, d.B), dim3(256),
+  SAS_LAUNCH("bwd_dq_simt", (bwd_dq_simt_kernel<T, D>), dim3((d.N + 63) / 64, d.Hq, d.B), dim3(256),
                      mask_bytes, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, scores,
                      idx, lse, lse_s, delta, (T*)dq, ds, d.Hq, d.Hkv, d.N, d.C, d.block, topk,
                      scale);
-  hipLaunchKernelGGL((bwd_dkdv_simt_kernel<T, D>), dim3((d.N + KT - 1) / KT, d.Hkv, d.B),
+  SAS_LAUNCH("bwd_dkdv_simt", (bwd_dkdv_simt_kernel<T, D>), dim3((d.N + KT - 1) / KT, d.Hkv, d.B),
                      dim3(128), 0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout,
                      scores, idx, lse, lse_s, delta, (T*)dk, (T*)dv, d.Hq, d.Hkv, d.N, d.C,
                      d.block, topk, scale);

@@ -261,14 +261,14 @@ hipError_t decode_t(const DecodeArgs& a0, int B, T* o, float* lse, hipStream_t s
   dim3 grid(a.P, a.Hkv, B);
   switch (a.Hq / a.Hkv) {
 #define SAS_DEC_G(GG) \
-  case GG: hipLaunchKernelGGL((decode_partial_kernel<T, D, GG>), grid, dim3(256), 0, s, a); break;
+  case GG: SAS_LAUNCH("decode_partial", (decode_partial_kernel<T, D, GG>), grid, dim3(256), 0, s, a); break;
     SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4) SAS_DEC_G(5) SAS_DEC_G(6) SAS_DEC_G(7)
     SAS_DEC_G(8) SAS_DEC_G(9) SAS_DEC_G(10) SAS_DEC_G(11) SAS_DEC_G(12) SAS_DEC_G(13) SAS_DEC_G(14)
     SAS_DEC_G(15) SAS_DEC_G(16)
 #undef SAS_DEC_G
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.Hq, B), dim3(D), 0, s, a.part, o, lse,
+  SAS_LAUNCH("decode_merge", (decode_merge_kernel<T, D>), dim3(a.Hq, B), dim3(D), 0, s, a.part, o, lse,
                      a.Hq, a.Hkv, a.P);
   return hipGetLastError();
 }

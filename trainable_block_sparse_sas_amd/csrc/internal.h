@@ -9,6 +9,25 @@
 
 namespace sas {
 
+// Kernel timing for diagnostics (sas_profile_enable): while on, every launch
+// is bracketed by a pair of HIP events recorded on its stream.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr;
+};
+
+#define SAS_LAUNCH(NAME, K, GRID, BLOCK, SHMEM, STREAM, ...)      \
+  do {                                                              \
+    ::sas::ProfScope sas_prof_scope_(NAME, STREAM);                 \
+    hipLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); \
+  } while (0)
+
 struct Dims {
   int B, Hq, Hkv, N, D, block, C;
   int G() const { return Hq / Hkv; }

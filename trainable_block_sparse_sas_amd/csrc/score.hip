@@ -235,10 +235,10 @@ hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, 
   if (C == 0 || B == 0) return hipSuccess;
   dim3 grid(C, Hkv, B);
   if (bf16)
-    hipLaunchKernelGGL(pool_kernel<bf16_t>, grid, dim3(D), 0, s, (const bf16_t*)k, (bf16_t*)kbar,
+    SAS_LAUNCH("pool", pool_kernel<bf16_t>, grid, dim3(D), 0, s, (const bf16_t*)k, (bf16_t*)kbar,
                        Hkv, L, D, block, C);
   else
-    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(D), 0, s, (const float*)k, (float*)kbar, Hkv,
+    SAS_LAUNCH("pool", pool_kernel<float>, grid, dim3(D), 0, s, (const float*)k, (float*)kbar, Hkv,
                        L, D, block, C);
   return hipGetLastError();
 }
@@ -247,7 +247,7 @@ template <typename T, int D>
 static void score_train_t(const void* q, const void* kbar, float* scores, const Dims& d,
                           float scale, bool group_sum, hipStream_t s) {
   dim3 grid((d.N + 63) / 64, d.Hkv, d.B);
-  hipLaunchKernelGGL((score_train_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
+  SAS_LAUNCH("score_train", (score_train_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
                      (const T*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale,
                      group_sum ? 1 : 0);
 }
@@ -258,10 +258,10 @@ hipError_t launch_score_train(const void* q, const void* kbar, float* scores, co
   if (bf16 && !group_sum && d.block % 16 == 0) {
     dim3 grid((d.N + 63) / 64, d.Hq, d.B);
     if (d.D == 64)
-      hipLaunchKernelGGL(score_train_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
+      SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
                          (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
     else
-      hipLaunchKernelGGL(score_train_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
+      SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
                          (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
     return hipGetLastError();
   }
@@ -286,7 +286,7 @@ static void score_decode_t(const void* q, const void* kbar, float* scores, const
   switch (Hq / Hkv) {
 #define SAS_SCD_G(GG)                                                                        \
   case GG:                                                                                  \
-    hipLaunchKernelGGL((score_decode_kernel<T, D, GG>), grid, dim3(256), 0, s, (const T*)q, \
+    SAS_LAUNCH("score_decode", (score_decode_kernel<T, D, GG>), grid, dim3(256), 0, s, (const T*)q, \
                        (const T*)kbar, scores, cl, Hq, Hkv, L, C, block, scale, group_sum ? 1 : 0); \
     break;
     SAS_SCD_G(1) SAS_SCD_G(2) SAS_SCD_G(3) SAS_SCD_G(4) SAS_SCD_G(5) SAS_SCD_G(6) SAS_SCD_G(7)

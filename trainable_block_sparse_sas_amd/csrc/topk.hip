@@ -378,16 +378,16 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
   const long rows = long(B) * Hkv * Nq;
   if (rows == 0 || topk == 0) return hipSuccess;
   if (C <= 256) {
-    hipLaunchKernelGGL((topk_kernel<1, 4>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
+    SAS_LAUNCH("topk", (topk_kernel<1, 4>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
   } else if (C <= 1024) {
-    hipLaunchKernelGGL((topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
+    SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
   } else if (topk <= 32) {
-    hipLaunchKernelGGL((topk_long_kernel<16, 8>), dim3(rows), dim3(1024), 0, s, scores, idx,
+    SAS_LAUNCH("topk_long", (topk_long_kernel<16, 8>), dim3(rows), dim3(1024), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk);
   } else {
-    hipLaunchKernelGGL((topk_long_kernel<16, 64>), dim3(rows), dim3(1024), 0, s, scores, idx,
+    SAS_LAUNCH("topk_long", (topk_long_kernel<16, 64>), dim3(rows), dim3(1024), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk);
   }
   return hipGetLastError();

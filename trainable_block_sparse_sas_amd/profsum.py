@@ -1,0 +1,138 @@
+"""Summaries of rocprofv3 result databases for the text files under profiles/.
+
+  python -m trainable_block_sparse_sas_amd.profsum stats DB --cmd "..."
+      kernel-trace table: launches, average and total duration per kernel.
+  python -m trainable_block_sparse_sas_amd.profsum traffic --fetch DB --write DB
+         --kernel bwd_dq --workload train-32k-sparse --cmd-fetch "..." --cmd-write "..."
+      HBM bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE
+      run, each scaled by what the same counter reads for a plain copy kernel
+      that reads and writes 1 GiB (bench.py --copy-probe).
+
+Reads only the SQLite views rocprofv3 writes (kernels, pmc_events).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import os
+import re
+import sqlite3
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+KERNEL_SOURCES = {"fwd_mfma": "attn_fwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
+                  "bwd_dkdv": "attn_bwd_mfma.hip"}
+
+
+def short_name(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", n).strip()
+
+
+def kernel_rows(db):
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    ni = cols.index("name") if "name" in cols else cols.index("kernel_name")
+    si, ei = cols.index("start"), cols.index("end")
+    for r in con.execute("select * from kernels"):
+        yield short_name(r[ni]), (r[ei] - r[si]) / 1e3  # us
+
+
+def stats(db, cmd):
+    agg = {}
+    for n, us in kernel_rows(db):
+        a = agg.setdefault(n, [0, 0.0])
+        a[0] += 1
+        a[1] += us
+    tot = sum(v[1] for v in agg.values())
+    out = ["# Kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
+           "| kernel | launches | avg us | total ms | share |", "|---|---:|---:|---:|---:|"]
+    for n, (c, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+        if t / tot < 1e-4:
+            continue
+        out.append(f"| `{n[:100]}` | {c} | {t / c:.1f} | {t / 1e3:.3f} | {100 * t / tot:.1f}% |")
+    return "\n".join(out) + "\n"
+
+
+def counter_per_dispatch(db, counter):
+    """{kernel short name: mean counter value per dispatch}."""
+    con = sqlite3.connect(db)
+    per = {}
+    for name, disp, cn, cv in con.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if cn != counter:
+            continue
+        d = per.setdefault(short_name(name), {})
+        d[disp] = d.get(disp, 0.0) + cv
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def source_hash(kernel):
+    csrc = os.path.join(HERE, "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h", "mfma.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pick(vals, key):
+    hits = [k for k in vals if key in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {key!r}, found {hits}")
+    return hits[0], vals[hits[0]]
+
+
+def traffic(fetch_db, write_db, kernel, workload, cmd_fetch, cmd_write):
+    f = counter_per_dispatch(fetch_db, "FETCH_SIZE")
+    w = counter_per_dispatch(write_db, "WRITE_SIZE")
+    kname, kf = _pick(f, kernel + "_kernel<")
+    _, kw = _pick(w, kernel + "_kernel<")
+    cname, cf = _pick(f, "bitwise_not")
+    _, cw = _pick(w, "bitwise_not")
+    sf = COPY_BYTES / (cf * 1024.0)
+    sw = COPY_BYTES / (cw * 1024.0)
+    total = int(kf * 1024.0 * sf + kw * 1024.0 * sw)
+    lines = [
+        f"# HBM traffic of `{kernel}` on {workload}", "",
+        "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one counter per run), each",
+        "scaled by the same counter's reading for a plain copy kernel that reads and writes",
+        "1 GiB (torch bitwise_not over 2^28 int32, run first by bench.py --copy-probe).", "",
+        "Commands:", "", "```", cmd_fetch, cmd_write, "```", "",
+        f"- kernel: `{kname}`",
+        f"- fetch_kib_per_dispatch: {kf:.1f}",
+        f"- write_kib_per_dispatch: {kw:.1f}",
+        f"- copy_kernel: `{cname[:80]}`",
+        f"- copy_fetch_kib: {cf:.1f}",
+        f"- copy_write_kib: {cw:.1f}",
+        f"- fetch_scale: {sf:.4f}",
+        f"- write_scale: {sw:.4f}",
+        f"- hbm_bytes_per_launch: {total}",
+        f"- source_sha256_16: `{source_hash(kernel)}`",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("db")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--cmd-fetch", required=True)
+    b.add_argument("--cmd-write", required=True)
+    args = ap.parse_args()
+    if args.what == "stats":
+        print(stats(args.db, args.cmd), end="")
+    else:
+        print(traffic(args.fetch, args.write, args.kernel, args.workload, args.cmd_fetch,
+                      args.cmd_write), end="")
+
+
+if __name__ == "__main__":
+    main()
