@@ -24,6 +24,9 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
+#include "tiles.h"
+
+#include <type_traits>
 
 namespace sas {
 namespace {
@@ -47,7 +50,8 @@ struct BwdArgs {
   float* ds;
   float* delta;      // workspace [B, Hq, N]
   uint32_t* selbits; // workspace [B, Hkv, N, MWB] (sparse)
-  int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs;
+  const bf16_t* kt;  // workspace: K^T per block (tiles.h layout)
+  int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
 };
 
@@ -327,8 +331,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // -------------------------------------------------------------------- dQ ----
-template <int D, int G, int NSUB, int WAVES, bool SPARSE>
-__global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
+// Query-major, the forward's structure: a workgroup owns TOK_WG tokens
+// of one KV head (all G query heads: 16 * NSUB * WAVES rows, a lane per row)
+// and streams the tiles its rows attend through an NST-stage LDS ring filled by
+// direct global -> LDS loads: K and V row-major (A operands of S^T = K Q^T and
+// dP^T = V dO^T) and K^T from the workspace (A operand of dQ^T = K^T dS^T).
+// Per tile and row: P = exp2(S scale log2e + bias - lse log2e),
+// dZ = P (dP - Delta), dbeta = sum of dZ over the tile (gated history tiles
+// only, written to ds as scratch), dZ packed to bf16 for the dQ product.  Own
+// blocks run in a second, masked loop.  The epilogue writes dq and turns the
+// row's dbeta into ds = dbeta - g sum(dbeta) (dense over the history).
+constexpr int kDqMaskWords = 1024;  // sparse scope: C + 1 <= 32768 blocks
+constexpr int kDqListMax = 4096;    // sparse scope: tokens per workgroup x topk
+constexpr int kDqBiasMax = 8192;    // sparse scope: rows per workgroup x topk
+
+template <int D, int G, int NSUB, int WAVES, int NST, bool SPARSE>
+__global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+  using namespace tiles;
   constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;
   constexpr int MD = D / 16;
@@ -336,10 +355,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int ROWS_WG = 16 * NSUB * WAVES;
   constexpr int TOK_WG = ROWS_WG / G;
   constexpr int CH = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][D + PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT][D + PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D][KT + PAD];
-  extern __shared__ int32_t dyn[];  // sparse: union mask | sorted idx | raw idx
+  constexpr int NKL = KT * D * 2 / 1024;  // 1 KB wave loads per operand tile
+  constexpr int LPW = NKL / WAVES;
+  constexpr int L = 3 * LPW + (SPARSE ? 0 : 1);  // loads per wave per tile
+  static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
+  static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
+  static_assert(NST == 2 || NST == 3, "two or three ring stages");
+  static_assert(kDqBiasMax >= kDqListMax, "raw index scratch reuses the bias table");
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D], V1[KT * D], V2[NST > 2 ? KT * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t T0[D * KT], T1[D * KT], T2[NST > 2 ? D * KT : 8];
+  __shared__ __attribute__((aligned(16))) float S0[SPARSE ? 1 : WAVES * 64], S1[SPARSE ? 1 : WAVES * 64],
+      S2[SPARSE || NST < 3 ? 1 : WAVES * 64];
+  __shared__ int32_t umask[SPARSE ? kDqMaskWords : 1];
+  __shared__ int32_t sorted[SPARSE ? kDqListMax : 1];
+  __shared__ float beta[SPARSE ? kDqBiasMax : 1];
+  __shared__ float tot_sh[ROWS_WG];
+  __shared__ int wg_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -361,11 +393,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
     sub_live[s] = t0 < N;
   }
 
+  // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
   const int MW = (C + 32) >> 5;
-  int32_t* umask = dyn;
-  int32_t* sorted = dyn + MW;
-  int32_t* raw = sorted + TOK_WG * a.topk;
-  float* beta = reinterpret_cast<float*>(raw + TOK_WG * a.topk);  // [ROWS_WG][topk] (sparse)
+  int32_t* raw = reinterpret_cast<int32_t*>(beta);  // [TOK_WG][topk] until the bias table is built
   if (SPARSE) {
     for (int i = tid; i < MW; i += NT) umask[i] = 0;
     for (int i = tid; i < TOK_WG * a.topk; i += NT) {
@@ -396,13 +426,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
       if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
     }
     __syncthreads();
-    // Gate bias (base 2) of every (row, selected block), read from LDS in the loop.
     for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
       const int r = i / a.topk, e = i % a.topk;
       const int sg = r >> 4, rl = r & 15;
       const int t = t_wg0 + sg * TOK_SUB + rl / G;
-      const int tok = t - t_wg0;
-      const int mm2 = sorted[tok * a.topk + e];
+      const int mm2 = sorted[(t - t_wg0) * a.topk + e];
       float bv = kNegInf;
       if (t < N && mm2 != 0x7fffffff) {
         const size_t gr = (size_t(b) * a.Hq + g * G + rl % G) * N + t;
@@ -411,7 +439,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
       beta[i] = bv;
     }
   }
-  __shared__ int wg_last;
   if (tid == 0) wg_last = -1;
   __syncthreads();
   {
@@ -422,7 +449,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
   __syncthreads();
   const int last_tile = wg_last;
 
-  // Row state: Q and dO fragments (B operands), lse (base 2), Delta, lse_s.
+  // ---- row state: Q and dO fragments (B operands), lse, Delta, lse_s ----------
   uint4 qf[NSUB][KS], of[NSUB][KS];
   float lse2[NSUB], del[NSUB], lses[NSUB], dbt[NSUB];
   f32x4 dqa[NSUB][MD];
@@ -455,63 +482,118 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
     return -1;
   };
 
+  // ---- direct global -> LDS tile loads ------------------------------------------
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  constexpr int LOADS = (KT * CH + NT - 1) / NT;
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int mm) {
-    const int jb = mm * KT;
-    for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + NT * i;
-      const int key = chunk / CH, c8 = chunk % CH;
-      const int j = jb + key;
-      const bool ok = chunk < KT * CH && j < N;
-      kreg[i] = ok ? *reinterpret_cast<const uint4*>(kh + size_t(j) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-      vreg[i] = ok ? *reinterpret_cast<const uint4*>(vh + size_t(j) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-    }
+  const bf16_t* th = a.kt + (size_t(b) * a.Hkv + g) * size_t(a.NB) * KT * D;
+  const int srow_i = lane % (16 * NSUB);
+  const int s_s = srow_i >> 4, s_lr = srow_i & 15;
+  const int s_t = min(t_wg0 + (wave * NSUB + s_s) * TOK_SUB + s_lr / G, N - 1);
+  const float* s_base = a.scores + ((size_t(b) * a.Hq + g * G + s_lr % G) * N + s_t) * C;
+  auto kst = [&](auto tag) -> uint16_t* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return K0;
+    else if constexpr (P == 1) return K1;
+    else return K2;
   };
-  auto store_tile = [&]() {
-    for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + NT * i;
-      if (chunk >= KT * CH) continue;
-      const int key = chunk / CH, c8 = chunk % CH;
-      *reinterpret_cast<uint4*>(&Ks[key][c8 * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&Vs[key][c8 * 8]) = vreg[i];
-      // K^T with keys permuted to the MFMA k order of dS^T.
-      const int kap = key & 31;
-      const int phys = (key & ~31) + 8 * ((kap >> 2) & 3) + 4 * (kap >> 4) + (kap & 3);
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&kreg[i]);
-      for (int d = 0; d < 8; ++d) Kt[c8 * 8 + d][phys] = hv[d];
-    }
+  auto vst = [&](auto tag) -> uint16_t* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return V0;
+    else if constexpr (P == 1) return V1;
+    else return V2;
   };
-
-  int mm = next_tile(-1);
-  if (mm >= 0) load_tile(mm);
-  float s_cur[NSUB];
-  for (int s = 0; s < NSUB; ++s) {
-    s_cur[s] = 0.f;
-    if (!SPARSE && mm >= 0 && mm < c_sub[s] && row_t[s] < N)
-      s_cur[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + mm];
+  auto tst = [&](auto tag) -> uint16_t* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return T0;
+    else if constexpr (P == 1) return T1;
+    else return T2;
+  };
+  auto sst = [&](auto tag) -> float* {
+    constexpr int P = decltype(tag)::value;
+    if constexpr (P == 0) return S0;
+    else if constexpr (P == 1) return S1;
+    else return S2;
+  };
+  // This lane's 16-byte piece i of a row-major K/V tile, as an element offset.
+  uint32_t k_goff[LPW];
+  for (int i = 0; i < LPW; ++i) {
+    const int sl = 64 * (wave * LPW + i) + lane;
+    const int r = sl / CH, pc = sl % CH;
+    k_goff[i] = uint32_t(r * D + (pc ^ k_swz<D>(r)) * 8);
   }
-  while (mm >= 0) {
-    __syncthreads();  // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    const int m_next = next_tile(mm);
-    float s_nxt[NSUB];
-    for (int s = 0; s < NSUB; ++s) {
-      s_nxt[s] = 0.f;
-      if (!SPARSE && m_next >= 0 && m_next < c_sub[s] && row_t[s] < N)
-        s_nxt[s] = a.scores[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m_next];
+  auto issue = [&](int m, auto tag) {
+    uint16_t* kd = kst(tag);
+    uint16_t* vd = vst(tag);
+    uint16_t* td = tst(tag);
+    if (m * KT + KT <= N) {
+      const bf16_t* kt = kh + size_t(m) * KT * D;
+      const bf16_t* vt = vh + size_t(m) * KT * D;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        uint32_t off = k_goff[i];
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(kt + off, (lds_ptr_t)(kd + (wave * LPW + i) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off, (lds_ptr_t)(vd + (wave * LPW + i) * 512), 16, 0, 0);
+      }
+    } else {
+      // tail tile: keys past N repeat key N-1 (their logits are masked)
+      for (int i = 0; i < LPW; ++i) {
+        const int j = wave * LPW + i;
+        const int sl = 64 * j + lane;
+        const int r = sl / CH, pc = sl % CH;
+        const size_t key = size_t(min(m * KT + r, N - 1));
+        const int c = pc ^ k_swz<D>(r);
+        __builtin_amdgcn_global_load_lds(kh + key * D + c * 8, (lds_ptr_t)(kd + j * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vh + key * D + c * 8, (lds_ptr_t)(vd + j * 512), 16, 0, 0);
+      }
     }
-    if (m_next >= 0) load_tile(m_next);
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      __builtin_amdgcn_global_load_lds(th + size_t(m) * KT * D + (64 * j + lane) * 8,
+                                       (lds_ptr_t)(td + j * 512), 16, 0, 0);
+    }
+    if (!SPARSE)
+      __builtin_amdgcn_global_load_lds(s_base + min(m, C - 1), (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
+  };
+  auto wait_tile = [&](int after) {
+    switch (after) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<L>(); break;
+      default: wait_vm<(NST > 2 ? 2 * L : L)>(); break;
+    }
+  };
+  // MFMA operand reads (the forward's addressing): K and V rows key = 16 mt + lr,
+  // chunk (4 ks + lq) ^ k_swz(lr); K^T rows d = 16 md + lr, chunk
+  // (4 kk + lq) ^ vt_swz(lr).
+  const int ksw = k_swz<D>(lr), tsw = vt_swz(lr);
+  const uint32_t k_base = lr * D + ((lq ^ (ksw & 3)) * 8), k_xor = (ksw >> 2) * 32;
+  const uint32_t t_base = lr * KT + ((lq ^ (tsw & 3)) * 8), t_xor = (tsw >> 2) * 32;
 
-    bool need[NSUB];
+  int tq[NST];
+  tq[0] = next_tile(-1);
+  for (int i = 1; i < NST; ++i) tq[i] = tq[i - 1] >= 0 ? next_tile(tq[i - 1]) : -1;
+  if (tq[0] >= 0) issue(tq[0], std::integral_constant<int, 0>{});
+  if (NST > 2 && tq[1] >= 0) issue(tq[1], std::integral_constant<int, 1>{});
+
+  auto step = [&](auto tag, auto mkt) {
+    constexpr int P = decltype(tag)::value;
+    constexpr bool MK = decltype(mkt)::value;
+    const int m = tq[0];
+    int after = 0;
+    for (int i = 1; i < NST - 1; ++i) after += tq[i] >= 0;
+    wait_tile(after);
+    __syncthreads();
+    if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{});
+    const uint16_t* Ks = kst(tag);
+    const uint16_t* Vs = vst(tag);
+    const uint16_t* Ts = tst(tag);
+    const float* Ss = sst(tag);
+    int nmask = 0;
     float bias2[NSUB];
     bool gated[NSUB];
     for (int s = 0; s < NSUB; ++s) {
-      const bool own = (mm == c_sub[s]);
-      const bool hist = (mm < c_sub[s]);
+      const bool own = (m == c_sub[s]);
+      const bool hist = (m < c_sub[s]);
       bool sel = false;
       float bsel = kNegInf;
       if (hist && row_t[s] < N) {
@@ -519,80 +601,116 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
           const int tok = row_t[s] - t_wg0;
           const int32_t* srt = sorted + tok * a.topk;
           int cu = cursor[s];
-          sel = (cu < a.topk && srt[cu] == mm);
+          sel = (cu < a.topk && srt[cu] == m);
           if (sel) bsel = beta[((wave * NSUB + s) * 16 + lr) * a.topk + cu];
-          while (cu < a.topk && srt[cu] == mm) ++cu;
+          while (cu < a.topk && srt[cu] == m) ++cu;
           cursor[s] = cu;
         } else {
           sel = true;
+          bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
         }
       }
-      need[s] = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
+      const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
+      nmask |= int(nd) << s;
       gated[s] = sel;
-      float bb = kNegInf;
-      if (own) bb = 0.f;
-      else if (sel) bb = SPARSE ? bsel : (s_cur[s] - lses[s]) * kLog2e;
-      bias2[s] = bb;
+      // bias minus the row's lse (base 2); -inf where the row skips the tile
+      const bool valid = row_t[s] < N && (own || sel);
+      bias2[s] = valid ? (own ? 0.f : bsel) - lse2[s] : kNegInf;
     }
-    // S^T = K Q^T and dP^T = V dO^T.
-    f32x4 sacc[NSUB][4], pacc[NSUB][4];
-    for (int s = 0; s < NSUB; ++s)
+    nmask = __builtin_amdgcn_readfirstlane(nmask);
+    if (nmask) {
+      uint32_t kb = k_base, kx = k_xor, tb = t_base, tx = t_xor;
+      asm volatile("" : "+v"(kb), "+v"(kx), "+v"(tb), "+v"(tx));
+      // One 16-key slice (mt) at a time: S^T = K Q^T and dP^T = V dO^T over the
+      // k steps, then dZ = P (dP - Delta) for those keys, packed into dZ^T
+      // fragments (keys 16 mt .. 16 mt + 15 are half of the k range of kk = mt/2).
+      uint4 dsf[NSUB][2];
+      float dsum[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) dsum[s] = 0.f;
+#pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        sacc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    for (int ks = 0; ks < KS; ++ks)
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint4 kfr = *reinterpret_cast<const uint4*>(&Ks[16 * mt + lr][ks * 32 + lq * 8]);
-        const uint4 vfr = *reinterpret_cast<const uint4*>(&Vs[16 * mt + lr][ks * 32 + lq * 8]);
-        for (int s = 0; s < NSUB; ++s)
-          if (need[s]) {
-            sacc[s][mt] = mfma16(kfr, qf[s][ks], sacc[s][mt]);
-            pacc[s][mt] = mfma16(vfr, of[s][ks], pacc[s][mt]);
-          }
-      }
-    uint4 dsf[NSUB][2];
-    for (int s = 0; s < NSUB; ++s) {
-      if (!need[s]) continue;
-      const bool own = (mm == c_sub[s]);
-      float dz[4][4];
-      float dsum = 0.f;
-      for (int mt = 0; mt < 4; ++mt)
-        for (int i = 0; i < 4; ++i) {
-          const int j = mm * KT + 16 * mt + 4 * lq + i;
-          float pv = 0.f;
-          if (bias2[s] != kNegInf && !(own && j > row_t[s]) && row_t[s] < N)
-            pv = exp2_hw(sacc[s][mt][i] * c1 + bias2[s] - lse2[s]);
-          const float d = pv * (pacc[s][mt][i] - del[s]);
-          dz[mt][i] = d;
-          dsum += d;
+        f32x4 sa[NSUB], pa[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          sa[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pa[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      if (!own && gated[s]) {
-        // dbeta for (row, mm): sum over the block's 64 keys.
-        dsum += shfl_xor(dsum, 16);
-        dsum += shfl_xor(dsum, 32);
-        dbt[s] += dsum;
-        if (lq == 0) a.ds[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + mm] = dsum;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t off = mt * 16 * D + (((ks * 32) ^ kx) + kb);
+          const uint4 kf = *reinterpret_cast<const uint4*>(Ks + off);
+          const uint4 vf = *reinterpret_cast<const uint4*>(Vs + off);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            sa[s] = mfma16(kf, qf[s][ks], sa[s]);
+            pa[s] = mfma16(vf, of[s][ks], pa[s]);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          float dz[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = fmaf(sa[s][i], c1, bias2[s]);
+            if (MK && m * KT + 16 * mt + 4 * lq + i > row_t[s]) x = kNegInf;
+            dz[i] = exp2_hw(x) * (pa[s][i] - del[s]);
+            dsum[s] += dz[i];
+          }
+          if (mt & 1) {
+            dsf[s][mt >> 1].z = pack_bf16(dz[0], dz[1]);
+            dsf[s][mt >> 1].w = pack_bf16(dz[2], dz[3]);
+          } else {
+            dsf[s][mt >> 1].x = pack_bf16(dz[0], dz[1]);
+            dsf[s][mt >> 1].y = pack_bf16(dz[2], dz[3]);
+          }
+        }
       }
-      for (int kk = 0; kk < 2; ++kk) {
-        dsf[s][kk].x = pack_bf16(dz[2 * kk][0], dz[2 * kk][1]);
-        dsf[s][kk].y = pack_bf16(dz[2 * kk][2], dz[2 * kk][3]);
-        dsf[s][kk].z = pack_bf16(dz[2 * kk + 1][0], dz[2 * kk + 1][1]);
-        dsf[s][kk].w = pack_bf16(dz[2 * kk + 1][2], dz[2 * kk + 1][3]);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const float tsum = sum_xrows(dsum[s]);
+        if (gated[s]) {
+          dbt[s] += tsum;
+          if (lq == 0) a.ds[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m] = tsum;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(Ts + md * 16 * KT + (((kk * 32) ^ tx) + tb));
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) dqa[s][md] = mfma16(ka, dsf[s][kk], dqa[s][md]);
+        }
       }
     }
-    // dQ^T += K^T dS^T.
-    for (int md = 0; md < MD; ++md)
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&Kt[16 * md + lr][kk * 32 + lq * 8]);
-        for (int s = 0; s < NSUB; ++s)
-          if (need[s]) dqa[s][md] = mfma16(ka, dsf[s][kk], dqa[s][md]);
-      }
-    for (int s = 0; s < NSUB; ++s) s_cur[s] = s_nxt[s];
-    mm = m_next;
+    for (int i = 0; i < NST - 1; ++i) tq[i] = tq[i + 1];
+    tq[NST - 1] = tq[NST - 2] >= 0 ? next_tile(tq[NST - 2]) : -1;
+  };
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  const int c_first = t_wg0 / KT;
+  int ph = 0;
+  while (true) {
+    if (tq[0] < 0 || tq[0] >= c_first) { ph = 0; break; }
+    step(std::integral_constant<int, 0>{}, Unmasked{});
+    if (tq[0] < 0 || tq[0] >= c_first) { ph = 1; break; }
+    step(std::integral_constant<int, 1>{}, Unmasked{});
+    if constexpr (NST > 2) {
+      if (tq[0] < 0 || tq[0] >= c_first) { ph = 2; break; }
+      step(std::integral_constant<int, (NST > 2 ? 2 : 0)>{}, Unmasked{});
+    }
+  }
+  while (tq[0] >= 0) {
+    if (ph == 0) step(std::integral_constant<int, 0>{}, Masked{});
+    else if (ph == 1) step(std::integral_constant<int, 1>{}, Masked{});
+    else step(std::integral_constant<int, (NST > 2 ? 2 : 0)>{}, Masked{});
+    ph = ph + 1 == NST ? 0 : ph + 1;
   }
 
-  // dQ (scaled): lane holds row, columns 16md + 4lq + i.
+  // ---- epilogue: dQ (scaled), then ds = dbeta - g sum(dbeta) -----------------
   for (int s = 0; s < NSUB; ++s) {
     if (row_t[s] >= N) continue;
     const size_t gr = (size_t(b) * a.Hq + row_h[s]) * N + row_t[s];
@@ -603,8 +721,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
       *reinterpret_cast<uint2*>(a.dq + gr * D + 16 * md + 4 * lq) = w;
     }
   }
-  // ds epilogue: ds = dbeta - g * sum(dbeta) over the history, dense; 0 beyond.
-  __shared__ float tot_sh[ROWS_WG];
   for (int s = 0; s < NSUB; ++s)
     if (lq == 0) tot_sh[wave * 16 * NSUB + s * 16 + lr] = dbt[s];
   __threadfence();
@@ -621,7 +737,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
     const float ls = a.lse_s[gr];
     const float* srow = a.scores + gr * C;
     float* drow = a.ds + gr * C;
-    // selection of this token (sparse): bitmask built by the prep kernel
     const uint32_t* bits = SPARSE ? a.selbits + ((size_t(b) * a.Hkv + g) * N + t) * a.MWB : nullptr;
     for (int m2 = lane; m2 < C; m2 += 64) {
       float out = 0.f;
@@ -639,18 +754,25 @@ __global__ __launch_bounds__(64 * WAVES, 2) void bwd_dq_kernel(BwdArgs a) {
 
 bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   if (d.block != KT || (d.D != 64 && d.D != 128)) return false;
+  if (d.C < 1) return false;
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (sparse) {
-    // LDS of the dQ kernel's sparse prologue (128 rows x topk bias table).
-    if (size_t(128) * topk > 8192) return false;
-    if (((d.C + 32) >> 5) > 1024) return false;
+    // the dQ kernel's per-workgroup tables (256 rows, 256 / G tokens)
+    if (size_t(256) * topk > kDqBiasMax || size_t(256 / G) * topk > kDqListMax) return false;
+    if (((d.C + 32) >> 5) > kDqMaskWords) return false;
   }
   return true;
 }
 
+// Workspace: Delta per row | K^T blocks | (sparse) per-token selection bitmask.
+static size_t kt_bytes(const Dims& d) {
+  const int NB = (d.N + KT - 1) / KT;
+  return align_up(size_t(d.B) * d.Hkv * NB * KT * d.D * sizeof(bf16_t));
+}
+
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
-  size_t bytes = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));
+  size_t bytes = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float)) + kt_bytes(d);
   if (sparse) {
     const int MWB = (d.C + 31) / 32;
     bytes += align_up(size_t(d.B) * d.Hkv * d.N * (MWB > 0 ? MWB : 1) * sizeof(uint32_t));
@@ -661,23 +783,26 @@ size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 template <int D, int G, bool SPARSE>
 static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
-  constexpr int NSUB = 1;  // rows per wave in the dQ kernel: 16 (register budget)
-  constexpr int WAVES = SPARSE ? 8 : 4;
+  constexpr int NSUB = 2;
+  constexpr int WAVES = 8;
+  constexpr int NST = 2;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   const size_t rows = size_t(B) * a.Hq * a.N;
   SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
-                     dim3(256), 0, s, a.o, a.dout, a.delta, rows);
+             dim3(256), 0, s, a.o, a.dout, a.delta, rows);
   if (SPARSE) {
     const size_t tokens = size_t(B) * a.Hkv * a.N;
     SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits, a.N,
-                       a.topk, a.MWB, tokens);
+               a.topk, a.MWB, tokens);
   }
+  SAS_LAUNCH("kt", (tiles::vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, s, a.k,
+             const_cast<bf16_t*>(a.kt), a.Hkv, a.N, a.NB);
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
   SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
-  const size_t dyn = SPARSE ? (size_t((a.C + 32) >> 5) + (2 + G) * size_t(TOK_WG) * a.topk) * 4 : 0;
-  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), dyn, s, a);
+  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, SPARSE>), dim3(a.n_tiles * a.n_pairs),
+             dim3(64 * WAVES), 0, s, a);
   return hipGetLastError();
 }
 
@@ -689,10 +814,13 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(w);
-  uint32_t* selbits = reinterpret_cast<uint32_t*>(w + align_up(size_t(d.B) * d.Hq * d.N * sizeof(float)));
+  const size_t off_kt = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));
+  bf16_t* kt = reinterpret_cast<bf16_t*>(w + off_kt);
+  uint32_t* selbits = reinterpret_cast<uint32_t*>(w + off_kt + kt_bytes(d));
   BwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
             scores, idx, lse, lse_s, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, ds, delta,
-            sp ? selbits : nullptr, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0, scale};
+            sp ? selbits : nullptr, kt, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
+            (d.N + KT - 1) / KT, scale};
   if (a.MWB < 1) a.MWB = 1;
   const int G = d.G();
 #define SAS_BWD_CASE(DD, GG)                                                              \

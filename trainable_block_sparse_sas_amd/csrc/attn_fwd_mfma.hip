@@ -31,18 +31,18 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
+#include "tiles.h"
 
 #include <type_traits>
 
 namespace sas {
 namespace {
 
-constexpr int KT = 64;  // keys per tile = block size of this kernel
+using namespace tiles;
+
 constexpr int kMaskWords = 1024;  // sparse scope: C + 1 <= 32768 blocks
 constexpr int kListMax = 4096;    // sparse scope: tokens per workgroup x topk
 constexpr int kBiasMax = 8192;    // sparse scope: rows per workgroup x topk
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct FwdArgs {
   const bf16_t* q;
@@ -57,52 +57,6 @@ struct FwdArgs {
   int Hq, Hkv, N, C, topk, n_tiles, n_pairs, NB;
   float scale;
 };
-
-// Key position p (0..63) inside a 64-key tile of V^T -> key index.  Within each
-// group of 32, position 8q + j holds key 4q + j (j < 4) or 16 + 4q + j - 4: the
-// k order in which a lane's P^T values leave the S^T accumulators.
-__device__ __forceinline__ int vt_key_of_pos(int p) {
-  const int hh = p >> 5, q = (p >> 3) & 3, j = p & 7;
-  return 32 * hh + (j < 4 ? 4 * q + j : 16 + 4 * q + j - 4);
-}
-// 16-byte chunk swizzles (conflict-free reads of 16 rows at one chunk column).
-template <int D>
-__device__ __forceinline__ int k_swz(int key) {
-  return D == 128 ? (key & 15) : ((key >> 1) & 7);
-}
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
-
-// Per block of V: V^T [D][64] with keys in vt_key_of_pos order; row d's 16-byte
-// chunk cc stored at chunk cc ^ vt_swz(d).  Keys beyond N are zero.
-template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, bf16_t* __restrict__ vt,
-                                                 int Hkv, int N, int NB) {
-  __shared__ uint16_t vs[KT][D + 2];
-  const int m = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const bf16_t* src = v + ((size_t(b) * Hkv + g) * N + size_t(m) * KT) * D;
-  for (int i = threadIdx.x; i < KT * D; i += 256) {
-    const int key = i / D, d = i % D;
-    vs[key][d] = (m * KT + key < N) ? src[size_t(key) * D + d] : 0;
-  }
-  __syncthreads();
-  bf16_t* dst = vt + ((size_t(b) * Hkv + g) * NB + m) * size_t(KT) * D;
-  for (int i = threadIdx.x; i < D * 8; i += 256) {
-    const int d = i >> 3, pc = i & 7;
-    const int cc = pc ^ vt_swz(d);
-    uint32_t w[4];
-    for (int j2 = 0; j2 < 4; ++j2) {
-      const int p0 = cc * 8 + 2 * j2;
-      w[j2] = uint32_t(vs[vt_key_of_pos(p0)][d]) | (uint32_t(vs[vt_key_of_pos(p0 + 1)][d]) << 16);
-    }
-    *reinterpret_cast<uint4*>(dst + size_t(d) * KT + pc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | 0xF00 | (((n >> 4) & 3) << 14));
-}
 
 // LSE_s of every query row over its history scores (the gate normaliser):
 // one wave per row, a single pass of running (max, sum) per lane, then a
