@@ -371,6 +371,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   __shared__ int32_t sorted[SPARSE ? kDqListMax : 1];
   __shared__ float beta[SPARSE ? kDqBiasMax : 1];
   __shared__ float tot_sh[ROWS_WG];
+  // per row: lse (base 2), Delta, LSE_s -- read per step rather than held in
+  // registers across the tile loop
+  __shared__ float rstat[ROWS_WG][4];
   __shared__ int wg_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -382,63 +385,22 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   const int t_wg0 = tile * TOK_WG;
   const float c1 = a.scale * kLog2e;
 
-  int row_t[NSUB], row_h[NSUB], c_sub[NSUB];
+  // Row of subtile s for lane row index r (0..15): token and query head.
+  auto tok_of = [&](int s, int r) { return t_wg0 + (wave * NSUB + s) * TOK_SUB + r / G; };
+  auto head_of = [&](int r) { return g * G + r % G; };
+  int c_sub[NSUB];
   bool sub_live[NSUB];
   for (int s = 0; s < NSUB; ++s) {
-    const int sg = wave * NSUB + s;
-    const int t0 = t_wg0 + sg * TOK_SUB;
-    row_t[s] = t0 + lr / G;
-    row_h[s] = g * G + lr % G;
+    const int t0 = t_wg0 + (wave * NSUB + s) * TOK_SUB;
     c_sub[s] = t0 / KT;
     sub_live[s] = t0 < N;
   }
 
   // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
   const int MW = (C + 32) >> 5;
-  int32_t* raw = reinterpret_cast<int32_t*>(beta);  // [TOK_WG][topk] until the bias table is built
-  if (SPARSE) {
-    for (int i = tid; i < MW; i += NT) umask[i] = 0;
-    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
-      const int tok = i / a.topk, e = i % a.topk;
-      const int t = t_wg0 + tok;
-      int mm = -1;
-      if (t < N) {
-        mm = a.idx[((size_t(b) * a.Hkv + g) * N + t) * a.topk + e];
-        if (mm < 0 || mm >= t / KT) mm = -1;
-      }
-      raw[i] = mm < 0 ? 0x7fffffff : mm;
-    }
-    __syncthreads();
-    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
-      const int tok = i / a.topk, e = i % a.topk;
-      const int32_t* rr = raw + tok * a.topk;
-      const int mm = rr[e];
-      int rank = 0;
-      for (int e2 = 0; e2 < a.topk; ++e2) {
-        const int m2 = rr[e2];
-        rank += (m2 < mm) || (m2 == mm && e2 < e);
-      }
-      sorted[tok * a.topk + rank] = mm;
-      if (mm != 0x7fffffff) atomicOr(&umask[mm >> 5], 1 << (mm & 31));
-    }
-    if (tid < WAVES * NSUB) {
-      const int t0 = t_wg0 + tid * TOK_SUB;
-      if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
-    }
-    __syncthreads();
-    for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
-      const int r = i / a.topk, e = i % a.topk;
-      const int sg = r >> 4, rl = r & 15;
-      const int t = t_wg0 + sg * TOK_SUB + rl / G;
-      const int mm2 = sorted[(t - t_wg0) * a.topk + e];
-      float bv = kNegInf;
-      if (t < N && mm2 != 0x7fffffff) {
-        const size_t gr = (size_t(b) * a.Hq + g * G + rl % G) * N + t;
-        bv = (a.scores[gr * C + mm2] - a.lse_s[gr]) * kLog2e;
-      }
-      beta[i] = bv;
-    }
-  }
+  if (SPARSE)
+    sparse_tables<G, NSUB, WAVES>(a.idx, a.scores, a.lse_s, a.Hq, a.Hkv, N, C, a.topk, b, g, t_wg0, umask,
+                                  sorted, beta);
   if (tid == 0) wg_last = -1;
   __syncthreads();
   {
@@ -451,19 +413,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
 
   // ---- row state: Q and dO fragments (B operands), lse, Delta, lse_s ----------
   uint4 qf[NSUB][KS], of[NSUB][KS];
-  float lse2[NSUB], del[NSUB], lses[NSUB], dbt[NSUB];
+  float dbt[NSUB];
   f32x4 dqa[NSUB][MD];
   int cursor[NSUB];
   for (int s = 0; s < NSUB; ++s) {
-    const bool ok = row_t[s] < N;
-    const size_t gr = (size_t(b) * a.Hq + row_h[s]) * N + (ok ? row_t[s] : 0);
+    const int rt = tok_of(s, lr);
+    const bool ok = rt < N;
+    const size_t gr = (size_t(b) * a.Hq + head_of(lr)) * N + (ok ? rt : 0);
     for (int ks = 0; ks < KS; ++ks) {
       qf[s][ks] = ok ? *reinterpret_cast<const uint4*>(a.q + gr * D + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
       of[s][ks] = ok ? *reinterpret_cast<const uint4*>(a.dout + gr * D + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
     }
-    lse2[s] = ok ? a.lse[gr] * kLog2e : 0.f;
-    del[s] = ok ? a.delta[gr] : 0.f;
-    lses[s] = ok ? a.lse_s[gr] : 0.f;
+    if (lq == 0) {
+      float* rs = rstat[(wave * NSUB + s) * 16 + lr];
+      rs[0] = ok ? a.lse[gr] * kLog2e : 0.f;
+      rs[1] = ok ? a.delta[gr] : 0.f;
+      rs[2] = ok ? a.lse_s[gr] : 0.f;
+    }
     dbt[s] = 0.f;
     cursor[s] = 0;
     for (int md = 0; md < MD; ++md) dqa[s][md] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -486,10 +452,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* th = a.kt + (size_t(b) * a.Hkv + g) * size_t(a.NB) * KT * D;
-  const int srow_i = lane % (16 * NSUB);
-  const int s_s = srow_i >> 4, s_lr = srow_i & 15;
-  const int s_t = min(t_wg0 + (wave * NSUB + s_s) * TOK_SUB + s_lr / G, N - 1);
-  const float* s_base = a.scores + ((size_t(b) * a.Hq + g * G + s_lr % G) * N + s_t) * C;
   auto kst = [&](auto tag) -> uint16_t* {
     constexpr int P = decltype(tag)::value;
     if constexpr (P == 0) return K0;
@@ -514,14 +476,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     else if constexpr (P == 1) return S1;
     else return S2;
   };
-  // This lane's 16-byte piece i of a row-major K/V tile, as an element offset.
-  uint32_t k_goff[LPW];
-  for (int i = 0; i < LPW; ++i) {
-    const int sl = 64 * (wave * LPW + i) + lane;
-    const int r = sl / CH, pc = sl % CH;
-    k_goff[i] = uint32_t(r * D + (pc ^ k_swz<D>(r)) * 8);
-  }
-  auto issue = [&](int m, auto tag) {
+  // ln: this lane's index, recomputed per step (see step).
+  auto issue = [&](int m, auto tag, int ln) {
     uint16_t* kd = kst(tag);
     uint16_t* vd = vst(tag);
     uint16_t* td = tst(tag);
@@ -530,8 +486,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       const bf16_t* vt = vh + size_t(m) * KT * D;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        uint32_t off = k_goff[i];
-        asm volatile("" : "+v"(off));
+        // 16-byte piece: tile row r, stored chunk pc, source chunk pc ^ k_swz(r)
+        const int sl = 64 * (wave * LPW + i) + ln;
+        const int r = sl / CH, pc = sl % CH;
+        const uint32_t off = uint32_t(r * D + (pc ^ k_swz<D>(r)) * 8);
         __builtin_amdgcn_global_load_lds(kt + off, (lds_ptr_t)(kd + (wave * LPW + i) * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vt + off, (lds_ptr_t)(vd + (wave * LPW + i) * 512), 16, 0, 0);
       }
@@ -539,7 +497,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       // tail tile: keys past N repeat key N-1 (their logits are masked)
       for (int i = 0; i < LPW; ++i) {
         const int j = wave * LPW + i;
-        const int sl = 64 * j + lane;
+        const int sl = 64 * j + ln;
         const int r = sl / CH, pc = sl % CH;
         const size_t key = size_t(min(m * KT + r, N - 1));
         const int c = pc ^ k_swz<D>(r);
@@ -549,11 +507,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     }
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
-      __builtin_amdgcn_global_load_lds(th + size_t(m) * KT * D + (64 * j + lane) * 8,
+      __builtin_amdgcn_global_load_lds(th + size_t(m) * KT * D + (64 * j + ln) * 8,
                                        (lds_ptr_t)(td + j * 512), 16, 0, 0);
     }
-    if (!SPARSE)
-      __builtin_amdgcn_global_load_lds(s_base + min(m, C - 1), (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
+    if (!SPARSE) {
+      // score of row (ln % (16 NSUB)) of this wave, block m
+      const int sr = ln % (16 * NSUB);
+      const int st = min(tok_of(sr >> 4, sr & 15), N - 1);
+      const float* sp = a.scores + ((size_t(b) * a.Hq + head_of(sr & 15)) * N + st) * C + min(m, C - 1);
+      __builtin_amdgcn_global_load_lds(sp, (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
+    }
   };
   auto wait_tile = [&](int after) {
     switch (after) {
@@ -562,28 +525,27 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       default: wait_vm<(NST > 2 ? 2 * L : L)>(); break;
     }
   };
-  // MFMA operand reads (the forward's addressing): K and V rows key = 16 mt + lr,
-  // chunk (4 ks + lq) ^ k_swz(lr); K^T rows d = 16 md + lr, chunk
-  // (4 kk + lq) ^ vt_swz(lr).
-  const int ksw = k_swz<D>(lr), tsw = vt_swz(lr);
-  const uint32_t k_base = lr * D + ((lq ^ (ksw & 3)) * 8), k_xor = (ksw >> 2) * 32;
-  const uint32_t t_base = lr * KT + ((lq ^ (tsw & 3)) * 8), t_xor = (tsw >> 2) * 32;
 
   int tq[NST];
   tq[0] = next_tile(-1);
   for (int i = 1; i < NST; ++i) tq[i] = tq[i - 1] >= 0 ? next_tile(tq[i - 1]) : -1;
-  if (tq[0] >= 0) issue(tq[0], std::integral_constant<int, 0>{});
-  if (NST > 2 && tq[1] >= 0) issue(tq[1], std::integral_constant<int, 1>{});
+  if (tq[0] >= 0) issue(tq[0], std::integral_constant<int, 0>{}, lane);
+  if (NST > 2 && tq[1] >= 0) issue(tq[1], std::integral_constant<int, 1>{}, lane);
 
   auto step = [&](auto tag, auto mkt) {
     constexpr int P = decltype(tag)::value;
     constexpr bool MK = decltype(mkt)::value;
     const int m = tq[0];
+    // Every lane-dependent offset below derives from an opaque copy of the lane
+    // index, so none of them is kept live (or spilled) across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 15, lq = ln >> 4;
     int after = 0;
     for (int i = 1; i < NST - 1; ++i) after += tq[i] >= 0;
     wait_tile(after);
-    __syncthreads();
-    if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{});
+    ring_barrier();
+    if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{}, ln);
     const uint16_t* Ks = kst(tag);
     const uint16_t* Vs = vst(tag);
     const uint16_t* Ts = tst(tag);
@@ -591,7 +553,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     int nmask = 0;
     float bias2[NSUB];
     bool gated[NSUB];
+    int row_t[NSUB];
+    float lse2[NSUB], del[NSUB];
     for (int s = 0; s < NSUB; ++s) {
+      row_t[s] = tok_of(s, lr);
+      const float4 rs = *reinterpret_cast<const float4*>(rstat[(wave * NSUB + s) * 16 + lr]);
+      lse2[s] = rs.x;
+      del[s] = rs.y;
+      const float lses = rs.z;
       const bool own = (m == c_sub[s]);
       const bool hist = (m < c_sub[s]);
       bool sel = false;
@@ -607,7 +576,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
           cursor[s] = cu;
         } else {
           sel = true;
-          bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
+          bsel = (Ss[wave * 64 + 16 * s + lr] - lses) * kLog2e;
         }
       }
       const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
@@ -619,8 +588,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     }
     nmask = __builtin_amdgcn_readfirstlane(nmask);
     if (nmask) {
-      uint32_t kb = k_base, kx = k_xor, tb = t_base, tx = t_xor;
-      asm volatile("" : "+v"(kb), "+v"(kx), "+v"(tb), "+v"(tx));
+      // MFMA operand reads (the forward's addressing): K and V rows key =
+      // 16 mt + lr, chunk (4 ks + lq) ^ k_swz(lr); K^T rows d = 16 md + lr,
+      // chunk (4 kk + lq) ^ vt_swz(lr).
+      const int ksw = k_swz<D>(lr), tsw = vt_swz(lr);
+      const uint32_t kb = lr * D + ((lq ^ (ksw & 3)) * 8), kx = (ksw >> 2) * 32;
+      const uint32_t tb = lr * KT + ((lq ^ (tsw & 3)) * 8), tx = (tsw >> 2) * 32;
       // One 16-key slice (mt) at a time: S^T = K Q^T and dP^T = V dO^T over the
       // k steps, then dZ = P (dP - Delta) for those keys, packed into dZ^T
       // fragments (keys 16 mt .. 16 mt + 15 are half of the k range of kk = mt/2).
@@ -671,7 +644,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
         const float tsum = sum_xrows(dsum[s]);
         if (gated[s]) {
           dbt[s] += tsum;
-          if (lq == 0) a.ds[((size_t(b) * a.Hq + row_h[s]) * N + row_t[s]) * C + m] = tsum;
+          if (lq == 0) a.ds[((size_t(b) * a.Hq + head_of(lr)) * N + row_t[s]) * C + m] = tsum;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -712,8 +685,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
 
   // ---- epilogue: dQ (scaled), then ds = dbeta - g sum(dbeta) -----------------
   for (int s = 0; s < NSUB; ++s) {
-    if (row_t[s] >= N) continue;
-    const size_t gr = (size_t(b) * a.Hq + row_h[s]) * N + row_t[s];
+    const int rt = tok_of(s, lr);
+    if (rt >= N) continue;
+    const size_t gr = (size_t(b) * a.Hq + head_of(lr)) * N + rt;
     for (int md = 0; md < MD; ++md) {
       uint2 w;
       w.x = pack_bf16(dqa[s][md][0] * a.scale, dqa[s][md][1] * a.scale);

@@ -107,12 +107,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   static_assert(NSUB == 1 || NSUB == 2, "one or two subtiles per wave");
   // One array per ring stage: the compiler can then tell a stage being read
   // from the stages the in-flight loads write, and adds no waits of its own.
-  __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8],
-      K3[NST > 3 ? KT * D : 8];
+  // Full scope: each K stage also holds the rows' selector scores of its tile
+  // (WAVES * 64 fp32 after the keys), so a stage is two load targets, not three.
+  constexpr int KX = KT * D + (SPARSE ? 0 : WAVES * 64 * 2);
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KX], K1[KX], K2[NST > 2 ? KX : 8],
+      K3[NST > 3 ? KX : 8];
   __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT], V1[D * KT], V2[NST > 2 ? D * KT : 8],
       V3[NST > 3 ? D * KT : 8];
-  __shared__ __attribute__((aligned(16))) float S0[WAVES * 64], S1[WAVES * 64], S2[WAVES * 64],
-      S3[WAVES * 64];
   __shared__ float lses_sh[ROWS_WG];
   __shared__ int wg_last;
   // Sparse-scope tables, static so that reads in the loop do not alias the
@@ -151,48 +152,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
 
   // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
   const int MW = (C + 32) >> 5;  // bits 0..C (the own block may be block C)
-  int32_t* raw = reinterpret_cast<int32_t*>(beta);  // [TOK_WG][topk], until the bias table is built
-  if (SPARSE) {
-    for (int i = tid; i < MW; i += NT) umask[i] = 0;
-    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
-      const int tok = i / a.topk, e = i % a.topk;
-      const int t = t_wg0 + tok;
-      int m = -1;
-      if (t < N) {
-        m = a.idx[((size_t(b) * a.Hkv + g) * N + t) * a.topk + e];
-        if (m < 0 || m >= t / KT) m = -1;
-      }
-      raw[i] = m < 0 ? 0x7fffffff : m;
-    }
-    __syncthreads();
-    for (int i = tid; i < TOK_WG * a.topk; i += NT) {
-      const int tok = i / a.topk, e = i % a.topk;
-      const int32_t* rr = raw + tok * a.topk;
-      const int m = rr[e];
-      int rank = 0;
-      for (int e2 = 0; e2 < a.topk; ++e2) {
-        const int m2 = rr[e2];
-        rank += (m2 < m) || (m2 == m && e2 < e);
-      }
-      sorted[tok * a.topk + rank] = m;
-      if (m != 0x7fffffff) atomicOr(&umask[m >> 5], 1 << (m & 31));
-    }
-    if (tid < WAVES * NSUB) {
-      const int t0 = t_wg0 + tid * TOK_SUB;
-      if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
-    }
-    __syncthreads();
-    for (int i = tid; i < ROWS_WG * a.topk; i += NT) {
-      const int r = i / a.topk, e = i % a.topk;
-      const int sg = r >> 4, rl = r & 15;
-      const int t = t_wg0 + sg * TOK_SUB + rl / G;
-      const int mm = sorted[(t - t_wg0) * a.topk + e];
-      float bv = kNegInf;
-      if (t < N && mm != 0x7fffffff)
-        bv = (a.scores[((size_t(b) * a.Hq + g * G + rl % G) * N + t) * C + mm] - lses_sh[r]) * kLog2e;
-      beta[i] = bv;
-    }
-  }
+  if (SPARSE)
+    sparse_tables<G, NSUB, WAVES>(a.idx, a.scores, a.lse_s, a.Hq, a.Hkv, N, C, a.topk, b, g, t_wg0, umask,
+                                  sorted, beta);
   if (tid == 0) wg_last = -1;
   __syncthreads();
   {
@@ -251,13 +213,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     else if constexpr (P == 2) return V2;
     else return V3;
   };
-  auto sst = [&](auto tag) -> float* {
-    constexpr int P = decltype(tag)::value;
-    if constexpr (P == 0) return S0;
-    else if constexpr (P == 1) return S1;
-    else if constexpr (P == 2) return S2;
-    else return S3;
-  };
+  auto sst = [&](auto tag) -> float* { return reinterpret_cast<float*>(kst(tag) + KT * D); };
   // This lane's 16-byte piece i of a K tile, as an element offset in the tile:
   // tile row r, stored chunk pc, source chunk pc ^ k_swz(r).
   uint32_t k_goff[LPW];
@@ -340,7 +296,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     int after = 0;
     for (int i = 1; i < NST - 1; ++i) after += tq[i] >= 0;
     wait_tile(after);
-    __syncthreads();
+    ring_barrier();
     if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{});
     const uint16_t* Ks = kst(tag);
     const uint16_t* Vs = vst(tag);
@@ -516,7 +472,7 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
   // Sparse scope: wider workgroups (more tokens share each K/V tile load).
   constexpr int NSUB = 2;
   constexpr int WAVES = 8;
-  constexpr int NST = 3;
+  constexpr int NST = 2;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   FwdArgs a = a0;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
