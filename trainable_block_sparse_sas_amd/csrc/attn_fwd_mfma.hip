@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
         }
       }
       // Keep the V^T operand reads below the softmax (register pressure).
-      __builtin_amdgcn_sched_barrier(0);
+      
       // O^T += V^T P^T
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
@@ -415,7 +415,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
         }
       }
     };
-    if (nmask) {
+    if (SPARSE && NSUB == 2) {
+      // each subtile only when one of its rows selected the tile (its K and V
+      // fragments are then read once per subtile)
+      if (nmask & 1) compute(std::integral_constant<int, 1>{});
+      if (nmask & 2) compute(std::integral_constant<int, 2>{});
+    } else if (nmask) {
       // every subtile of the wave (a subtile without the tile has bias -inf
       // on all rows and adds nothing)
       compute(std::integral_constant<int, (1 << NSUB) - 1>{});
