@@ -100,41 +100,65 @@ __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict_
 }
 
 // --------------------------------------------------------------- dK / dV ----
+// KV-major: a workgroup owns one 64-key block m of one KV head, 16 keys per
+// wave (lane = key; K and V are B operands held in registers), and streams the
+// query rows that attend the block, RS = 64 rows (RS/G tokens x G heads) per
+// step, through a two-stage LDS ring filled by direct global -> LDS loads: Q
+// and dO rows (row-major, 16-byte chunks XOR-swizzled by row) and, per row,
+// lse, Delta, the block's selector score and LSE_s.  The own block's tokens
+// come first (causal mask, bias 0), then every later token (full scope) or the
+// later tokens whose selection holds m (sparse scope, compacted on the fly).
+//   S = Q K^T, dP = dO V^T      A: Q / dO row fragments
+//   dV += P^T dO, dK += dS^T Q  A: P^T / dS^T from registers (the permuted row
+//                               order of the S accumulators); B: dO / Q read
+//                               transposed from the row-major tile
 template <int D, int G, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  using namespace tiles;
+  constexpr int WAVES = 4;
+  constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;
   constexpr int ND = D / 16;
-  constexpr int CH = D / 8;
-  constexpr int RS = 32;       // rows per step
-  constexpr int TPS = RS / G;  // tokens per step
-  constexpr int QCAP = 256 + TPS;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][RS][D + PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][RS][D + PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D][RS + PAD];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D][RS + PAD];
-  __shared__ float r_lse[2][RS], r_del[2][RS], r_bias[2][RS];
-  __shared__ int r_tok[2][RS];
-  __shared__ int queue[QCAP];
-  __shared__ int q_count, q_wave[4];
+  constexpr int CH = D / 8;         // 16-byte chunks per row
+  constexpr int RS = 64;            // rows per step
+  constexpr int TPS = RS / G;       // tokens per step
+  constexpr int NPIECE = RS * D * 2 / 1024;  // 1 KB loads per operand per step
+  constexpr int PPW = NPIECE / WAVES;
+  constexpr int L = 2 * PPW + 1;    // loads per wave per step
+  // Stage layout (16-bit units): Q [RS][D] | dO [RS][D] | fp32 [4][RS]
+  // (lse, Delta, score of block m, LSE_s): one load target per stage.
+  constexpr int ST_DO = RS * D, ST_F = 2 * RS * D;
+  constexpr int STAGE = 2 * RS * D + 4 * RS * 2;
+  constexpr int QCAP = 512;
+  static_assert(NPIECE % WAVES == 0 && WAVES == 4, "stat loads: one per wave");
+  static_assert(QCAP >= NT + TPS, "queue holds one scan chunk plus a step");
+  __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
+  __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];  // token of each row, -1: none
+  __shared__ int queue[SPARSE ? QCAP : 1];
+  __shared__ int q_wave[WAVES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tile, pair;
   xcd_order(blockIdx.x, a.n_tiles, a.n_pairs, &tile, &pair);
   const int m = a.n_tiles - 1 - tile;  // lowest blocks (most rows) first
   const int b = pair / a.Hkv, g = pair % a.Hkv;
   const int N = a.N, C = a.C;
   const int j0 = m * KT;
-  const int my_key = j0 + wave * 16 + lr;  // this lane's key (B operand rows)
   const float c1 = a.scale * kLog2e;
+  const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;  // row index of head g*G, token 0
 
-  // Stationary K and V fragments: lane holds key my_key, columns 32ks + 8lq.
+  // Stationary K and V fragments (B operands): lane holds key my_key, columns
+  // 32 ks + 8 (lane / 16).
   uint4 kf[KS], vf[KS];
   {
+    const int my_key = j0 + wave * 16 + (lane & 15);
     const size_t kr = (size_t(b) * a.Hkv + g) * N + (my_key < N ? my_key : 0);
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.k + kr * D + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
-      vf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.v + kr * D + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
+      kf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.k + kr * D + ks * 32 + (lane >> 4) * 8)
+                          : make_uint4(0, 0, 0, 0);
+      vf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.v + kr * D + ks * 32 + (lane >> 4) * 8)
+                          : make_uint4(0, 0, 0, 0);
     }
   }
   f32x4 dk[ND], dv[ND];
@@ -143,182 +167,227 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     dv[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Row loader: rows of one step -> registers, then LDS (row-major + transposed).
-  uint4 rq[4];
-  float rs_lse = 0.f, rs_del = 0.f, rs_bias = kNegInf;
-  int rs_tok = -1;
-  auto load_rows = [&](const int* toks, int ntok) {
-    // threads 0..127: Q rows; 128..255: dO rows; 4 rows x one 16-byte chunk each
-    const int half = tid >> 7, u = tid & 127;
-    const int rg = u / CH, c8 = u % CH;
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * rg + r;
-      rq[r] = make_uint4(0, 0, 0, 0);
-      if (rg < RS / 4) {
-        const int ti = row / G;
-        if (ti < ntok) {
-          const int t = toks[ti];
-          const size_t gr = (size_t(b) * a.Hq + g * G + row % G) * N + t;
-          const bf16_t* src = half ? a.dout : a.q;
-          rq[r] = *reinterpret_cast<const uint4*>(src + gr * D + c8 * 8);
-        }
-      }
-    }
-    if (tid < RS) {
-      const int ti = tid / G;
-      rs_tok = -1;
-      rs_bias = kNegInf;
-      rs_lse = 0.f;
-      rs_del = 0.f;
-      if (ti < ntok) {
-        const int t = toks[ti];
-        const size_t gr = (size_t(b) * a.Hq + g * G + tid % G) * N + t;
-        rs_tok = t;
-        rs_lse = a.lse[gr] * kLog2e;
-        rs_del = a.delta[gr];
-        rs_bias = (t / KT == m) ? 0.f : (a.scores[gr * C + m] - a.lse_s[gr]) * kLog2e;
-      }
-    }
-  };
-  auto store_rows = [&](int buf) {
-    const int half = tid >> 7, u = tid & 127;
-    const int rg = u / CH, c8 = u % CH;
-    if (rg < RS / 4) {
-      uint16_t(*rm)[D + PAD] = half ? dOs[buf] : Qs[buf];
-      uint16_t(*tr)[RS + PAD] = half ? dOt[buf] : Qt[buf];
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&rm[4 * rg + r][c8 * 8]) = rq[r];
-      const int kap = (4 * rg) & 31;
-      const int phys = ((4 * rg) & ~31) + 8 * ((kap >> 2) & 3) + 4 * (kap >> 4);
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rq[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rq[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rq[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rq[3]);
-      for (int d2 = 0; d2 < 4; ++d2) {
-        const uint32_t lo0 = (w0[d2] & 0xffffu) | (w1[d2] << 16);
-        const uint32_t lo1 = (w2[d2] & 0xffffu) | (w3[d2] << 16);
-        const uint32_t hi0 = (w0[d2] >> 16) | (w1[d2] & 0xffff0000u);
-        const uint32_t hi1 = (w2[d2] >> 16) | (w3[d2] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(&tr[c8 * 8 + 2 * d2][phys]) = make_uint2(lo0, lo1);
-        *reinterpret_cast<uint2*>(&tr[c8 * 8 + 2 * d2 + 1][phys]) = make_uint2(hi0, hi1);
-      }
-    }
-    if (tid < RS) {
-      r_lse[buf][tid] = rs_lse;
-      r_del[buf][tid] = rs_del;
-      r_bias[buf][tid] = rs_bias;
-      r_tok[buf][tid] = rs_tok;
-    }
-  };
-  auto compute_step = [&](int buf) {
-    f32x4 sacc[2], dpacc[2];
-    for (int s = 0; s < 2; ++s) {
-      sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dpacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int ks = 0; ks < KS; ++ks) {
-      for (int s = 0; s < 2; ++s) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(&Qs[buf][16 * s + lr][ks * 32 + lq * 8]);
-        const uint4 da = *reinterpret_cast<const uint4*>(&dOs[buf][16 * s + lr][ks * 32 + lq * 8]);
-        sacc[s] = mfma16(qa, kf[ks], sacc[s]);
-        dpacc[s] = mfma16(da, vf[ks], dpacc[s]);
-      }
-    }
-    // C layout: lane holds key my_key (column lr), rows 16s + 4lq + i.
-    float p[2][4], dsv[2][4];
-    for (int s = 0; s < 2; ++s)
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * s + 4 * lq + i;
-        const int t = r_tok[buf][row];
-        float pv = 0.f;
-        if (t >= 0 && my_key <= t && my_key < N) {
-          pv = exp2_hw(sacc[s][i] * c1 + r_bias[buf][row] - r_lse[buf][row]);
-        }
-        p[s][i] = pv;
-        dsv[s][i] = pv * (dpacc[s][i] - r_del[buf][row]);
-      }
-    uint4 pa, da;
-    pa.x = pack_bf16(p[0][0], p[0][1]);
-    pa.y = pack_bf16(p[0][2], p[0][3]);
-    pa.z = pack_bf16(p[1][0], p[1][1]);
-    pa.w = pack_bf16(p[1][2], p[1][3]);
-    da.x = pack_bf16(dsv[0][0], dsv[0][1]);
-    da.y = pack_bf16(dsv[0][2], dsv[0][3]);
-    da.z = pack_bf16(dsv[1][0], dsv[1][1]);
-    da.w = pack_bf16(dsv[1][2], dsv[1][3]);
-    for (int nd = 0; nd < ND; ++nd) {
-      const uint4 ob = *reinterpret_cast<const uint4*>(&dOt[buf][16 * nd + lr][lq * 8]);
-      const uint4 qb = *reinterpret_cast<const uint4*>(&Qt[buf][16 * nd + lr][lq * 8]);
-      dv[nd] = mfma16(pa, ob, dv[nd]);
-      dk[nd] = mfma16(da, qb, dk[nd]);
-    }
-  };
-
-  // Steps: a list of token groups of TPS tokens.  The own block's tokens first,
-  // then (full scope) every later token or (sparse) the later tokens that
-  // selected block m, compacted through the queue.
-  int buf = 0;
-  bool have = false;  // a step is staged in LDS buffer `buf`
-  auto run_tokens = [&](const int* toks, int ntok) {
-    // Enqueue one step: prefetch to registers; compute the staged step; store.
-    load_rows(toks, ntok);
-    if (have) compute_step(buf);
-    store_rows(have ? buf ^ 1 : buf);
-    __syncthreads();
-    if (have) buf ^= 1;
-    have = true;
-  };
-
-  __shared__ int own_toks[KT];
+  // ---- token stream: own block, then history (uniform state in every thread)
   const int own_n = min(KT, N - j0);
-  if (tid < KT) own_toks[tid] = j0 + tid;
-  __syncthreads();
-  for (int s0 = 0; s0 < own_n; s0 += TPS) run_tokens(own_toks + s0, min(TPS, own_n - s0));
-
-  if (!SPARSE) {
-    __shared__ int seq_toks[TPS];
-    for (int t0 = j0 + KT; t0 < N; t0 += TPS) {
-      if (tid < TPS) seq_toks[tid] = t0 + tid;
-      __syncthreads();
-      run_tokens(seq_toks, min(TPS, N - t0));
-    }
-  } else {
-    if (tid == 0) q_count = 0;
-    __syncthreads();
-    const uint32_t* bits = a.selbits + (size_t(b) * a.Hkv + g) * size_t(N) * a.MWB;
-    const int word = m >> 5;
-    const uint32_t bit = 1u << (m & 31);
-    for (int t0 = j0 + KT; t0 < N; t0 += 256) {
-      const int t = t0 + tid;
-      const bool sel = t < N && (bits[size_t(t) * a.MWB + word] & bit);
+  int own_pos = 0;                 // next own token offset
+  int seq = j0 + KT;               // full scope: next history token
+  int qh = 0, qt = 0, scan = j0 + KT;  // sparse: queue head / tail, next token to scan
+  const uint32_t* bits = SPARSE ? a.selbits + (size_t(b) * a.Hkv + g) * size_t(N) * a.MWB : nullptr;
+  // Sparse: top up the queue to a step's worth of tokens (or the end).
+  auto refill = [&]() {
+    while (qt - qh < TPS && scan < N) {
+      const int t = scan + tid;
+      const bool sel = t < N && ((bits[size_t(t) * a.MWB + (m >> 5)] >> (m & 31)) & 1u);
       const unsigned long long bal = __ballot(sel);
       if (lane == 0) q_wave[wave] = __popcll(bal);
       __syncthreads();
-      int base = q_count;
-      for (int w = 0; w < wave; ++w) base += q_wave[w];
-      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-      if (sel) queue[base + __popcll(bal & lt)] = t;
-      __syncthreads();
-      int total = q_count + q_wave[0] + q_wave[1] + q_wave[2] + q_wave[3];
-      int done = 0;
-      while (total - done >= TPS) {
-        run_tokens(queue + done, TPS);
-        done += TPS;
+      int base = qt, total = 0;
+      for (int w = 0; w < WAVES; ++w) {
+        const int c = q_wave[w];
+        base += w < wave ? c : 0;
+        total += c;
       }
-      // keep the remainder at the front of the queue
-      const int rem = total - done;
-      int keep = 0;
-      if (tid < rem) keep = queue[done + tid];
+      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+      if (sel) queue[(base + __popcll(bal & lt)) % QCAP] = t;
       __syncthreads();
-      if (tid < rem) queue[tid] = keep;
-      if (tid == 0) q_count = rem;
-      __syncthreads();
+      qt += total;
+      scan += NT;
     }
-    if (q_count > 0) run_tokens(queue, q_count);
-  }
-  if (have) compute_step(buf);
+  };
+  // Tokens of the next step: returns the first token (own / full scope) or the
+  // queue head (sparse history), and the count; -1 count: no more rows.
+  // phase: 0 own block, 1 history.
+  auto take = [&](int& phase, int& first, int& cnt) {
+    if (own_pos < own_n) {
+      phase = 0;
+      first = j0 + own_pos;
+      cnt = min(TPS, own_n - own_pos);
+      own_pos += cnt;
+      return;
+    }
+    phase = 1;
+    if (!SPARSE) {
+      first = seq;
+      cnt = seq < N ? min(TPS, N - seq) : -1;
+      seq += TPS;
+      return;
+    }
+    first = qh;
+    cnt = qt > qh ? min(TPS, qt - qh) : -1;
+    qh += cnt > 0 ? cnt : 0;
+  };
+  auto token_of = [&](int phase, int first, int cnt, int i) -> int {  // i-th token of a step
+    if (i >= cnt) return -1;
+    if (SPARSE && phase == 1) return queue[(first + i) % QCAP];
+    return first + i;
+  };
 
-  // Write dK (scaled) and dV: lane holds column 16nd + lr, keys 4lq + i of the
-  // wave's 16 keys.
+  auto rst = [&](auto tag) -> uint16_t* {
+    if constexpr (decltype(tag)::value == 0) return R0;
+    else return R1;
+  };
+  // Loads of one step into stage `tag` (ln: opaque lane index).
+  auto issue = [&](auto tag, int phase, int first, int cnt, int ln) {
+    constexpr int P = decltype(tag)::value;
+    uint16_t* st = rst(tag);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int j = wave * PPW + i;          // 1 KB piece of the Q (dO) tile
+      const int sl = 64 * j + ln;            // 16-byte slot: row r, stored chunk pc
+      const int r = sl / CH, pc = sl % CH;
+      const int t = token_of(phase, first, cnt, r / G);
+      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
+      const int c = pc ^ k_swz<D>(r);
+      __builtin_amdgcn_global_load_lds(a.q + gr * D + c * 8, (lds_ptr_t)(st + j * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.dout + gr * D + c * 8, (lds_ptr_t)(st + ST_DO + j * 512), 16, 0,
+                                       0);
+    }
+    {
+      const int r = ln;  // stat `wave` of row r
+      const int t = token_of(phase, first, cnt, r / G);
+      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
+      // (own-block rows use no score; they read lse there, which always exists)
+      const float* src = wave == 0 ? a.lse + gr
+                       : wave == 1 ? a.delta + gr
+                       : wave == 2 ? (phase == 1 ? a.scores + gr * C + m : a.lse + gr)
+                                   : a.lse_s + gr;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + ST_F + wave * RS * 2), 4, 0, 0);
+      if (wave == 0) tok_sh[P][r] = t;
+    }
+  };
+
+  // One step on stage `tag`; MK: own-block rows (causal, bias 0) else gated history rows.
+  auto compute = [&](auto tag, auto mkt, int ln) {
+    constexpr int P = decltype(tag)::value;
+    constexpr bool MK = decltype(mkt)::value;
+    const uint16_t* Qs = rst(tag);
+    const uint16_t* dOs = Qs + ST_DO;
+    const float* F = reinterpret_cast<const float*>(Qs + ST_F);
+    const int lr = ln & 15, lq = ln >> 4;
+    const int key = j0 + wave * 16 + lr;
+    // S and dP for the 64 rows: 4 row subtiles of 16 (A row 16 rs + lr,
+    // k = d chunk 4 ks + lq stored at chunk (4 ks + lq) ^ k_swz(row), which
+    // depends on lr alone).
+    const int qsw = k_swz<D>(lr);
+    f32x4 sacc[4], pacc[4];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      sacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rs = 0; rs < 4; ++rs) {
+        const int off = (16 * rs + lr) * D + (((4 * ks + lq) ^ qsw) * 8);
+        const uint4 qa = *reinterpret_cast<const uint4*>(Qs + off);
+        const uint4 oa = *reinterpret_cast<const uint4*>(dOs + off);
+        sacc[rs] = mfma16(qa, kf[ks], sacc[rs]);
+        pacc[rs] = mfma16(oa, vf[ks], pacc[rs]);
+      }
+    // P and dS: lane holds key `key`, rows 16 rs + 4 lq + i.
+    uint4 pa[2], dsa[2];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      const int r0 = 16 * rs + 4 * lq;
+      const float4 lse = *reinterpret_cast<const float4*>(F + r0);
+      const float4 del = *reinterpret_cast<const float4*>(F + RS + r0);
+      const float4 sc = *reinterpret_cast<const float4*>(F + 2 * RS + r0);
+      const float4 lss = *reinterpret_cast<const float4*>(F + 3 * RS + r0);
+      const int4 tk = *reinterpret_cast<const int4*>(&tok_sh[P][r0]);
+      const float lv[4] = {lse.x, lse.y, lse.z, lse.w}, dl[4] = {del.x, del.y, del.z, del.w};
+      const float sv[4] = {sc.x, sc.y, sc.z, sc.w}, ls[4] = {lss.x, lss.y, lss.z, lss.w};
+      const int tv[4] = {tk.x, tk.y, tk.z, tk.w};
+      float p[4], d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // base-2 logit offset: bias - lse
+        const float off = MK ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
+        float x = fmaf(sacc[rs][i], c1, off);
+        const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
+        x = ok ? x : kNegInf;
+        p[i] = exp2_hw(x);
+        d[i] = p[i] * (pacc[rs][i] - dl[i]);
+      }
+      const int kk = rs >> 1;
+      if (rs & 1) {
+        pa[kk].z = pack_bf16(p[0], p[1]);
+        pa[kk].w = pack_bf16(p[2], p[3]);
+        dsa[kk].z = pack_bf16(d[0], d[1]);
+        dsa[kk].w = pack_bf16(d[2], d[3]);
+      } else {
+        pa[kk].x = pack_bf16(p[0], p[1]);
+        pa[kk].y = pack_bf16(p[2], p[3]);
+        dsa[kk].x = pack_bf16(d[0], d[1]);
+        dsa[kk].y = pack_bf16(d[2], d[3]);
+      }
+    }
+    // dV += P^T dO, dK += dS^T Q.  B operand (32 rows x 16 columns) read
+    // transposed: lane s of group lq points at row 32 kk + 4 lq + s / 4 (and
+    // + 16), column 16 nd + 4 (s % 4).
+    const int trow = 4 * lq + (lr >> 2);
+    const int tcol = 4 * (lr & 3);
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ra = 32 * kk + trow, rb = ra + 16;
+        const int col = 16 * nd + tcol;
+        const int oa = ra * D + (((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7);
+        const int ob = rb * D + (((col >> 3) ^ k_swz<D>(rb)) << 3) + (col & 7);
+        const uint2 o0 = lds_read_tr16(dOs + oa), o1 = lds_read_tr16(dOs + ob);
+        const uint2 q0 = lds_read_tr16(Qs + oa), q1 = lds_read_tr16(Qs + ob);
+        dv[nd] = mfma16(pa[kk], make_uint4(o0.x, o0.y, o1.x, o1.y), dv[nd]);
+        dk[nd] = mfma16(dsa[kk], make_uint4(q0.x, q0.y, q1.x, q1.y), dk[nd]);
+      }
+    }
+  };
+
+  // ---- the ring: step k computes stage k % 2 and loads step k + 1 into the other
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Own = std::integral_constant<bool, true>;
+  using Hist = std::integral_constant<bool, false>;
+  int cur_phase, cur_first, cur_cnt;
+  take(cur_phase, cur_first, cur_cnt);
+  if (SPARSE && own_pos >= own_n) refill();
+  if (cur_cnt > 0) issue(S0{}, cur_phase, cur_first, cur_cnt, lane);
+  // One step on stage `tag`: wait for its rows, load the next step's rows
+  // into the other stage, compute.  MK: own-block rows (the first steps).
+  auto step = [&](auto tag, auto mkt) {
+    using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    wait_vm<0>();
+    ring_barrier();
+    int nph, nfirst, ncnt;
+    take(nph, nfirst, ncnt);
+    if (ncnt > 0) issue(Pn{}, nph, nfirst, ncnt, ln);
+    compute(tag, mkt, ln);
+    // Sparse: top up the token queue once the own block's steps are issued.
+    if (SPARSE && own_pos >= own_n) refill();
+    cur_phase = nph;
+    cur_first = nfirst;
+    cur_cnt = ncnt;
+  };
+  // Own-block steps (one variant per loop: no accumulator merges), then the
+  // history, continuing on the stage where the first loop stopped.
+  int ph = 0;
+  while (cur_cnt > 0 && cur_phase == 0) {
+    step(S0{}, Own{});
+    if (cur_cnt <= 0 || cur_phase != 0) { ph = 1; break; }
+    step(S1{}, Own{});
+  }
+  while (cur_cnt > 0) {
+    if (ph == 0) step(S0{}, Hist{});
+    else step(S1{}, Hist{});
+    ph ^= 1;
+  }
+  (void)L;
+
+  // Write dK (scaled) and dV: lane holds column 16 nd + lr of keys 4 lq + i of
+  // the wave's 16.
+  const int lr = lane & 15, lq = lane >> 4;
   for (int i = 0; i < 4; ++i) {
     const int key = j0 + wave * 16 + 4 * lq + i;
     if (key >= N) continue;

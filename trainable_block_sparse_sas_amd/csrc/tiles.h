@@ -153,6 +153,18 @@ __device__ void sparse_tables(const int32_t* __restrict__ idx, const float* __re
   }
 }
 
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + c receives
+// element c of the 4 x 16-bit values addressed by lanes a, a + 4, a + 8 and
+// a + 12 of its group (checked on gfx950 with a standalone probe).  Pointing
+// lane s of a group at (row_i, col0 + 4 (s % 4)) with i = s / 4 hands lane
+// 4a + c the column col0 + 4a + c of rows row_0 .. row_3: four k values of an
+// MFMA operand whose k runs over rows, read from a row-major tile.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Workgroup barrier of a load ring.  __syncthreads() carries a release fence,
 // which waits for every outstanding global->LDS load (vmcnt(0)), including the
 // tiles meant to stay in flight across the barrier.  Here each wave first waits
