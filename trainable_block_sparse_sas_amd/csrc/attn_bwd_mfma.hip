@@ -50,7 +50,6 @@ struct BwdArgs {
   float* ds;
   float* delta;      // workspace [B, Hq, N]
   uint32_t* selbits; // workspace [B, Hkv, N, MWB] (sparse)
-  const bf16_t* kt;  // workspace: K^T per block (tiles.h layout)
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
 };
@@ -403,8 +402,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 // Query-major, the forward's structure: a workgroup owns TOK_WG tokens
 // of one KV head (all G query heads: 16 * NSUB * WAVES rows, a lane per row)
 // and streams the tiles its rows attend through an NST-stage LDS ring filled by
-// direct global -> LDS loads: K and V row-major (A operands of S^T = K Q^T and
-// dP^T = V dO^T) and K^T from the workspace (A operand of dQ^T = K^T dS^T).
+// direct global -> LDS loads of K and V, row-major: A operands of S^T = K Q^T
+// and dP^T = V dO^T, and (read transposed) of dQ^T = K^T dS^T.
 // Per tile and row: P = exp2(S scale log2e + bias - lse log2e),
 // dZ = P (dP - Delta), dbeta = sum of dZ over the tile (gated history tiles
 // only, written to ds as scratch), dZ packed to bf16 for the dQ product.  Own
@@ -426,14 +425,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   constexpr int CH = D / 8;
   constexpr int NKL = KT * D * 2 / 1024;  // 1 KB wave loads per operand tile
   constexpr int LPW = NKL / WAVES;
-  constexpr int L = 3 * LPW + (SPARSE ? 0 : 1);  // loads per wave per tile
+  constexpr int L = 2 * LPW + (SPARSE ? 0 : 1);  // loads per wave per tile
   static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
   static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
   static_assert(NST == 2 || NST == 3, "two or three ring stages");
   static_assert(kDqBiasMax >= kDqListMax, "raw index scratch reuses the bias table");
   __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8];
   __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D], V1[KT * D], V2[NST > 2 ? KT * D : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t T0[D * KT], T1[D * KT], T2[NST > 2 ? D * KT : 8];
   __shared__ __attribute__((aligned(16))) float S0[SPARSE ? 1 : WAVES * 64], S1[SPARSE ? 1 : WAVES * 64],
       S2[SPARSE || NST < 3 ? 1 : WAVES * 64];
   __shared__ int32_t umask[SPARSE ? kDqMaskWords : 1];
@@ -520,7 +518,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   // ---- direct global -> LDS tile loads ------------------------------------------
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-  const bf16_t* th = a.kt + (size_t(b) * a.Hkv + g) * size_t(a.NB) * KT * D;
   auto kst = [&](auto tag) -> uint16_t* {
     constexpr int P = decltype(tag)::value;
     if constexpr (P == 0) return K0;
@@ -533,12 +530,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     else if constexpr (P == 1) return V1;
     else return V2;
   };
-  auto tst = [&](auto tag) -> uint16_t* {
-    constexpr int P = decltype(tag)::value;
-    if constexpr (P == 0) return T0;
-    else if constexpr (P == 1) return T1;
-    else return T2;
-  };
   auto sst = [&](auto tag) -> float* {
     constexpr int P = decltype(tag)::value;
     if constexpr (P == 0) return S0;
@@ -549,7 +540,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   auto issue = [&](int m, auto tag, int ln) {
     uint16_t* kd = kst(tag);
     uint16_t* vd = vst(tag);
-    uint16_t* td = tst(tag);
     if (m * KT + KT <= N) {
       const bf16_t* kt = kh + size_t(m) * KT * D;
       const bf16_t* vt = vh + size_t(m) * KT * D;
@@ -573,11 +563,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
         __builtin_amdgcn_global_load_lds(kh + key * D + c * 8, (lds_ptr_t)(kd + j * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vh + key * D + c * 8, (lds_ptr_t)(vd + j * 512), 16, 0, 0);
       }
-    }
-    for (int i = 0; i < LPW; ++i) {
-      const int j = wave * LPW + i;
-      __builtin_amdgcn_global_load_lds(th + size_t(m) * KT * D + (64 * j + ln) * 8,
-                                       (lds_ptr_t)(td + j * 512), 16, 0, 0);
     }
     if (!SPARSE) {
       // score of row (ln % (16 NSUB)) of this wave, block m
@@ -617,7 +602,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     if (tq[NST - 1] >= 0) issue(tq[NST - 1], std::integral_constant<int, (P + NST - 1) % NST>{}, ln);
     const uint16_t* Ks = kst(tag);
     const uint16_t* Vs = vst(tag);
-    const uint16_t* Ts = tst(tag);
     const float* Ss = sst(tag);
     int nmask = 0;
     float bias2[NSUB];
@@ -660,9 +644,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       // MFMA operand reads (the forward's addressing): K and V rows key =
       // 16 mt + lr, chunk (4 ks + lq) ^ k_swz(lr); K^T rows d = 16 md + lr,
       // chunk (4 kk + lq) ^ vt_swz(lr).
-      const int ksw = k_swz<D>(lr), tsw = vt_swz(lr);
+      const int ksw = k_swz<D>(lr);
       const uint32_t kb = lr * D + ((lq ^ (ksw & 3)) * 8), kx = (ksw >> 2) * 32;
-      const uint32_t tb = lr * KT + ((lq ^ (tsw & 3)) * 8), tx = (tsw >> 2) * 32;
       // One 16-key slice (mt) at a time: S^T = K Q^T and dP^T = V dO^T over the
       // k steps, then dZ = P (dP - Delta) for those keys, packed into dZ^T
       // fragments (keys 16 mt .. 16 mt + 15 are half of the k range of kk = mt/2).
@@ -722,7 +705,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       for (int md = 0; md < MD; ++md) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(Ts + md * 16 * KT + (((kk * 32) ^ tx) + tb));
+          // K^T fragment (A: d rows, keys along k in the dS^T order), read
+          // transposed from the row-major K tile: lane s of group lq points at
+          // key 32 kk + 4 lq + s / 4 (and + 16), column 16 md + 4 (s % 4).
+          const int ra = 32 * kk + 4 * lq + (lr >> 2), rb = ra + 16;
+          const int col = 16 * md + 4 * (lr & 3);
+          const uint2 k0 = lds_read_tr16(Ks + ra * D + ((((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7)));
+          const uint2 k1 = lds_read_tr16(Ks + rb * D + ((((col >> 3) ^ k_swz<D>(rb)) << 3) + (col & 7)));
+          const uint4 ka = make_uint4(k0.x, k0.y, k1.x, k1.y);
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) dqa[s][md] = mfma16(ka, dsf[s][kk], dqa[s][md]);
         }
@@ -808,14 +798,10 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   return true;
 }
 
-// Workspace: Delta per row | K^T blocks | (sparse) per-token selection bitmask.
-static size_t kt_bytes(const Dims& d) {
-  const int NB = (d.N + KT - 1) / KT;
-  return align_up(size_t(d.B) * d.Hkv * NB * KT * d.D * sizeof(bf16_t));
-}
+// Workspace: Delta per row | (sparse) per-token selection bitmask.
 
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
-  size_t bytes = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float)) + kt_bytes(d);
+  size_t bytes = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));
   if (sparse) {
     const int MWB = (d.C + 31) / 32;
     bytes += align_up(size_t(d.B) * d.Hkv * d.N * (MWB > 0 ? MWB : 1) * sizeof(uint32_t));
@@ -838,8 +824,6 @@ static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
     SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits, a.N,
                a.topk, a.MWB, tokens);
   }
-  SAS_LAUNCH("kt", (tiles::vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, s, a.k,
-             const_cast<bf16_t*>(a.kt), a.Hkv, a.N, a.NB);
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
   SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
@@ -857,12 +841,10 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(w);
-  const size_t off_kt = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));
-  bf16_t* kt = reinterpret_cast<bf16_t*>(w + off_kt);
-  uint32_t* selbits = reinterpret_cast<uint32_t*>(w + off_kt + kt_bytes(d));
+  uint32_t* selbits = reinterpret_cast<uint32_t*>(w + align_up(size_t(d.B) * d.Hq * d.N * sizeof(float)));
   BwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
             scores, idx, lse, lse_s, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, ds, delta,
-            sp ? selbits : nullptr, kt, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
+            sp ? selbits : nullptr, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
             (d.N + KT - 1) / KT, scale};
   if (a.MWB < 1) a.MWB = 1;
   const int G = d.G();
