@@ -50,6 +50,8 @@ struct BwdArgs {
   float* ds;
   float* delta;      // workspace [B, Hq, N]
   uint32_t* selbits; // workspace [B, Hkv, N, MWB] (sparse)
+  uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
+  bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: partial dQ per selected block (sparse)
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
 };
@@ -77,9 +79,12 @@ __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __res
   if (row < rows && sub == 0) delta[row] = acc;
 }
 
-// One wave per token: bitmask of the token's valid selected blocks.
+// One wave per token: bitmask of the token's valid selected blocks, and (pre
+// != NULL) the number of set bits before each word, pre[tok][w] for w = 0 ..
+// MWB (the last entry is the token's number of selected blocks).
 __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
-                                                      uint32_t* __restrict__ bits, int N, int topk,
+                                                      uint32_t* __restrict__ bits,
+                                                      uint16_t* __restrict__ pre, int N, int topk,
                                                       int MWB, size_t tokens) {
   const size_t tok = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -87,6 +92,7 @@ __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict_
   const int t = int(tok % N);
   const int c = t / KT;
   const int32_t* ir = idx + tok * topk;
+  int carry = 0;
   for (int w0 = 0; w0 < MWB; w0 += 64) {
     const int w = w0 + lane;
     uint32_t word = 0;
@@ -95,7 +101,18 @@ __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict_
       if (m >= 0 && m < c && (m >> 5) == w) word |= 1u << (m & 31);
     }
     if (w < MWB) bits[tok * MWB + w] = word;
+    if (pre) {
+      const int cnt = __popc(word);
+      int incl = cnt;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (w < MWB) pre[tok * (MWB + 1) + w] = uint16_t(carry + incl - cnt);
+      carry += __shfl(incl, 63, 64);
+    }
   }
+  if (pre && lane == 0) pre[tok * (MWB + 1) + MWB] = uint16_t(carry);
 }
 
 // --------------------------------------------------------------- dK / dV ----
@@ -395,6 +412,410 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       a.dk[kr + 16 * nd + lr] = f32_to_bf16(dk[nd][i] * a.scale);
       a.dv[kr + 16 * nd + lr] = f32_to_bf16(dv[nd][i]);
     }
+  }
+}
+
+// ------------------------------------------------------- dQ, sparse scope ----
+// KV-major, the dK/dV kernel's row stream: a workgroup owns block m of one KV
+// head and takes RS = 128 rows per step (waves 0-3 rows 0-63, waves 4-7 rows
+// 64-127, each wave 16 of the block's keys).  Per step it recomputes P and dS
+// for its rows, sums dS over the block's 64 keys into dbeta (gated rows; the
+// value goes to ds[row, m], finished by ds_sparse_kernel), stages dS^T over
+// the step's Q and dO area of LDS, and writes the block's share of dQ, dS K over the 64
+// keys, to the row's slot of the partial buffer: slot = rank of m among the
+// token's selected blocks, or topk for the own block (dq_reduce_kernel adds the
+// slots).  Every (row, key) pair is computed once, with no tile of unselected
+// blocks.
+template <int D, int G>
+__global__ __launch_bounds__(512) void bwd_dq_kv_kernel(BwdArgs a) {
+  using namespace tiles;
+  constexpr int WAVES = 8;
+  constexpr int NT = 64 * WAVES;
+  constexpr int KS = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int CH = D / 8;
+  constexpr int RS = 128;           // rows per step
+  constexpr int TPS = RS / G;       // tokens per step
+  constexpr int NPIECE = RS * D * 2 / 1024;
+  constexpr int PPW = NPIECE / WAVES;
+  constexpr int NSTAT = 6;          // lse, Delta, score, LSE_s, prefix count, selection word
+  // Stage layout (16-bit units): Q [RS][D] | dO [RS][D] | fp32 [NSTAT][RS].
+  constexpr int ST_DO = RS * D, ST_F = 2 * RS * D;
+  constexpr int STAGE = 2 * RS * D + NSTAT * RS * 2;
+  constexpr int DSP = RS + 8;       // dS^T [key][row] stride (padded)
+  constexpr int QCAP = 1024;
+  static_assert(KT * DSP <= 2 * RS * D, "dS^T fits in the step's Q and dO area");
+  static_assert(NPIECE % WAVES == 0, "tile loads must split evenly over the waves");
+  static_assert(QCAP >= NT + TPS, "queue holds one scan chunk plus a step");
+  __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];  // the block's keys, row-major
+  __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];
+  __shared__ __attribute__((aligned(16))) float red[4][RS];
+  __shared__ int queue[QCAP];
+  __shared__ int q_wave[WAVES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave >> 2, kw = wave & 3;  // row group (64 rows), key group (16 keys)
+  int tile, pair;
+  xcd_order(blockIdx.x, a.n_tiles, a.n_pairs, &tile, &pair);
+  const int m = a.n_tiles - 1 - tile;
+  const int b = pair / a.Hkv, g = pair % a.Hkv;
+  const int N = a.N, C = a.C;
+  const int j0 = m * KT;
+  const float c1 = a.scale * kLog2e;
+  const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
+  const size_t tok0 = (size_t(b) * a.Hkv + g) * N;   // token index base (selection tables)
+  const int MWB = a.MWB;
+
+  // The block's keys into LDS (A operand of dQ^T = K^T dS^T, read transposed),
+  // and this wave's 16 keys as B operands of S and dP.
+  {
+    // 16 pieces of 1 KB (4 rows each for D = 128) over the waves; swizzled
+    // like the Q tile: row r's chunk pc holds chunk pc ^ k_swz(r).
+    const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+    constexpr int KPIECE = KT * D * 2 / 1024;
+    for (int j = wave; j < KPIECE; j += WAVES) {
+      const int sl = 64 * j + lane;
+      const int r = sl / CH, pc = sl % CH;
+      const int key = min(j0 + r, N - 1);
+      dma16_to_lds(kh + size_t(key) * D + ((pc ^ k_swz<D>(r)) * 8), Ksh + j * 512);
+    }
+  }
+  uint4 kf[KS], vf[KS];
+  {
+    const int my_key = j0 + kw * 16 + (lane & 15);
+    const size_t kr = (size_t(b) * a.Hkv + g) * N + (my_key < N ? my_key : 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.k + kr * D + ks * 32 + (lane >> 4) * 8)
+                          : make_uint4(0, 0, 0, 0);
+      vf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.v + kr * D + ks * 32 + (lane >> 4) * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // ---- token stream (the dK/dV kernel's): own block, then selecting tokens
+  const int own_n = min(KT, N - j0);
+  int own_pos = 0;
+  int qh = 0, qt = 0, scan = j0 + KT;
+  const uint32_t* bits = a.selbits + tok0 * size_t(MWB);
+  auto refill = [&]() {
+    while (qt - qh < TPS && scan < N) {
+      const int t = scan + tid;
+      const bool sel = t < N && ((bits[size_t(t) * MWB + (m >> 5)] >> (m & 31)) & 1u);
+      const unsigned long long bal = __ballot(sel);
+      if (lane == 0) q_wave[wave] = __popcll(bal);
+      __syncthreads();
+      int base = qt, total = 0;
+      for (int w = 0; w < WAVES; ++w) {
+        const int c = q_wave[w];
+        base += w < wave ? c : 0;
+        total += c;
+      }
+      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+      if (sel) queue[(base + __popcll(bal & lt)) % QCAP] = t;
+      __syncthreads();
+      qt += total;
+      scan += NT;
+    }
+  };
+  auto take = [&](int& phase, int& first, int& cnt) {
+    if (own_pos < own_n) {
+      phase = 0;
+      first = j0 + own_pos;
+      cnt = min(TPS, own_n - own_pos);
+      own_pos += cnt;
+      return;
+    }
+    phase = 1;
+    first = qh;
+    cnt = qt > qh ? min(TPS, qt - qh) : -1;
+    qh += cnt > 0 ? cnt : 0;
+  };
+  auto token_of = [&](int phase, int first, int cnt, int i) -> int {
+    if (i >= cnt) return -1;
+    if (phase == 1) return queue[(first + i) % QCAP];
+    return first + i;
+  };
+  auto rst = [&](auto tag) -> uint16_t* {
+    if constexpr (decltype(tag)::value == 0) return R0;
+    else return R1;
+  };
+  auto issue = [&](auto tag, int phase, int first, int cnt, int ln) {
+    constexpr int P = decltype(tag)::value;
+    uint16_t* st = rst(tag);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int j = wave * PPW + i;
+      const int sl = 64 * j + ln;
+      const int r = sl / CH, pc = sl % CH;
+      const int t = token_of(phase, first, cnt, r / G);
+      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
+      const int c = pc ^ k_swz<D>(r);
+      __builtin_amdgcn_global_load_lds(a.q + gr * D + c * 8, (lds_ptr_t)(st + j * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.dout + gr * D + c * 8, (lds_ptr_t)(st + ST_DO + j * 512), 16, 0,
+                                       0);
+    }
+    // per-row statistics: 2 x NSTAT loads of 64 rows over the waves
+    for (int k = wave; k < 2 * NSTAT; k += WAVES) {
+      const int stat = k >> 1, r = 64 * (k & 1) + ln;
+      const int t = token_of(phase, first, cnt, r / G);
+      const int tt = t >= 0 ? t : 0;
+      const size_t gr = hrow0 + size_t(r % G) * N + tt;
+      const void* src;
+      switch (stat) {
+        case 0: src = a.lse + gr; break;
+        case 1: src = a.delta + gr; break;
+        case 2: src = phase == 1 ? a.scores + gr * C + m : a.lse + gr; break;
+        case 3: src = a.lse_s + gr; break;
+        // prefix count: a 32-bit load of the aligned pair holding the 16-bit entry
+        case 4:
+          src = phase == 1 ? (const void*)(a.selpre + (((tok0 + tt) * (MWB + 1) + (m >> 5)) & ~size_t(1)))
+                           : (const void*)(a.lse + gr);
+          break;
+        default: src = phase == 1 ? (const void*)(bits + size_t(tt) * MWB + (m >> 5)) : (const void*)(a.lse + gr);
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + ST_F + (stat * RS + 64 * (k & 1)) * 2), 4, 0, 0);
+    }
+    if (tid < RS) tok_sh[P][tid] = token_of(phase, first, cnt, tid / G);
+  };
+
+  // Reduce-scatter of 16 values over the 16 lanes of a row of lanes: afterwards
+  // lane lr holds the sum of value lr.
+  auto reduce16 = [&](float (&v)[16], int lr) -> float {
+#pragma unroll
+    for (int M = 8, n = 16; M >= 1; M >>= 1, n >>= 1) {
+      const bool hi = (lr & M) != 0;
+#pragma unroll
+      for (int j = 0; j < n / 2; ++j) {
+        const float send = hi ? v[j] : v[j + n / 2];
+        const float keep = hi ? v[j + n / 2] : v[j];
+        v[j] = keep + __shfl_xor(send, M, 64);
+      }
+    }
+    return v[0];
+  };
+
+  auto compute = [&](auto tag, auto mkt, int ln) {
+    constexpr int P = decltype(tag)::value;
+    constexpr bool MK = decltype(mkt)::value;
+    uint16_t* st = rst(tag);
+    const uint16_t* Qs = st;
+    const uint16_t* dOs = st + ST_DO;
+    const float* F = reinterpret_cast<const float*>(st + ST_F);
+    const int lr = ln & 15, lq = ln >> 4;
+    const int key = j0 + kw * 16 + lr;
+    const int qsw = k_swz<D>(lr);
+    // S and dP for this wave's 64 rows (64 rg + 16 rs + lr) and 16 keys.
+    f32x4 sacc[4], pacc[4];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      sacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rs = 0; rs < 4; ++rs) {
+        const int off = (64 * rg + 16 * rs + lr) * D + (((4 * ks + lq) ^ qsw) * 8);
+        const uint4 qa = *reinterpret_cast<const uint4*>(Qs + off);
+        const uint4 oa = *reinterpret_cast<const uint4*>(dOs + off);
+        sacc[rs] = mfma16(qa, kf[ks], sacc[rs]);
+        pacc[rs] = mfma16(oa, vf[ks], pacc[rs]);
+      }
+    // dS (lane: key, rows 64 rg + 16 rs + 4 lq + i)
+    float dsv[16];
+    uint2 dpk[4];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      const int r0 = 64 * rg + 16 * rs + 4 * lq;
+      const float4 lse = *reinterpret_cast<const float4*>(F + r0);
+      const float4 del = *reinterpret_cast<const float4*>(F + RS + r0);
+      const float4 sc = *reinterpret_cast<const float4*>(F + 2 * RS + r0);
+      const float4 lss = *reinterpret_cast<const float4*>(F + 3 * RS + r0);
+      const int4 tk = *reinterpret_cast<const int4*>(&tok_sh[P][r0]);
+      const float lv[4] = {lse.x, lse.y, lse.z, lse.w}, dl[4] = {del.x, del.y, del.z, del.w};
+      const float sv[4] = {sc.x, sc.y, sc.z, sc.w}, ls[4] = {lss.x, lss.y, lss.z, lss.w};
+      const int tv[4] = {tk.x, tk.y, tk.z, tk.w};
+      float d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float off = MK ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
+        float x = fmaf(sacc[rs][i], c1, off);
+        const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
+        x = ok ? x : kNegInf;
+        d[i] = exp2_hw(x) * (pacc[rs][i] - dl[i]);
+        dsv[4 * rs + i] = d[i];
+      }
+      dpk[rs] = make_uint2(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]));
+    }
+    // dbeta: sum of dS over this wave's 16 keys, one row per lane; the four key
+    // groups meet in LDS.
+    if (!MK) {
+      const float part = reduce16(dsv, lr);
+      red[kw][64 * rg + 16 * (lr >> 2) + 4 * lq + (lr & 3)] = part;
+    }
+    ring_barrier();  // every wave is done with Q and dO of this stage
+    // dS^T [key][row] over the Q (and dO) area
+    uint16_t* dst = st;
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs)
+      *reinterpret_cast<uint2*>(dst + (kw * 16 + lr) * DSP + 64 * rg + 16 * rs + 4 * lq) = dpk[rs];
+    if (!MK && tid < RS) {
+      const int t = tok_sh[P][tid];
+      if (t >= 0) {
+        const float db = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+        a.ds[(hrow0 + size_t(tid % G) * N + t) * C + m] = db;
+      }
+    }
+    ring_barrier();  // dS^T complete
+    // dQ^T (d x rows) for rows 16 wave .. 16 wave + 15: A = K^T (keys along k),
+    // B = dS^T, both read transposed: lane s of group lq points at key
+    // 32 kk + 8 lq + s / 4 (and + 4), column 4 (s % 4) of its 16-wide tile.
+    f32x4 dqa[ND];
+#pragma unroll
+    for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ka = 32 * kk + 8 * lq + (lr >> 2), kb = ka + 4;
+      const uint2 s0 = lds_read_tr16(dst + ka * DSP + 16 * wave + 4 * (lr & 3));
+      const uint2 s1 = lds_read_tr16(dst + kb * DSP + 16 * wave + 4 * (lr & 3));
+      const uint4 dsb = make_uint4(s0.x, s0.y, s1.x, s1.y);
+#pragma unroll
+      for (int md = 0; md < ND; ++md) {
+        const int col = 16 * md + 4 * (lr & 3);
+        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ k_swz<D>(ka)) << 3) + (col & 7)));
+        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ k_swz<D>(kb)) << 3) + (col & 7)));
+        dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb, dqa[md]);
+      }
+    }
+    // partial dQ of row 16 wave + lr: lane holds d = 16 md + 4 lq + i
+    {
+      const int r = 16 * wave + lr;
+      const int t = tok_sh[P][r];
+      if (t >= 0) {
+        int slot = a.topk;
+        if (!MK) {
+          const uint32_t pw = reinterpret_cast<const uint32_t*>(F + 4 * RS)[r];
+          const size_t pidx = (tok0 + t) * (MWB + 1) + (m >> 5);
+          const int pre = int((pidx & 1) ? (pw >> 16) : (pw & 0xffffu));
+          const uint32_t word = reinterpret_cast<const uint32_t*>(F + 5 * RS)[r];
+          slot = pre + __popc(word & ((1u << (m & 31)) - 1u));
+        }
+        bf16_t* dp = a.dqp + ((hrow0 + size_t(r % G) * N + t) * (a.topk + 1) + slot) * D;
+#pragma unroll
+        for (int md = 0; md < ND; ++md) {
+          uint2 w;
+          w.x = pack_bf16(dqa[md][0], dqa[md][1]);
+          w.y = pack_bf16(dqa[md][2], dqa[md][3]);
+          *reinterpret_cast<uint2*>(dp + 16 * md + 4 * lq) = w;
+        }
+      }
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Own = std::integral_constant<bool, true>;
+  using Hist = std::integral_constant<bool, false>;
+  int cur_phase, cur_first, cur_cnt;
+  take(cur_phase, cur_first, cur_cnt);
+  if (own_pos >= own_n) refill();
+  if (cur_cnt > 0) issue(S0{}, cur_phase, cur_first, cur_cnt, lane);
+  auto step = [&](auto tag, auto mkt) {
+    using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    wait_vm<0>();
+    ring_barrier();
+    int nph, nfirst, ncnt;
+    take(nph, nfirst, ncnt);
+    if (ncnt > 0) issue(Pn{}, nph, nfirst, ncnt, ln);
+    compute(tag, mkt, ln);
+    if (own_pos >= own_n) refill();
+    cur_phase = nph;
+    cur_first = nfirst;
+    cur_cnt = ncnt;
+  };
+  int ph = 0;
+  while (cur_cnt > 0 && cur_phase == 0) {
+    step(S0{}, Own{});
+    if (cur_cnt <= 0 || cur_phase != 0) { ph = 1; break; }
+    step(S1{}, Own{});
+  }
+  while (cur_cnt > 0) {
+    if (ph == 0) step(S0{}, Hist{});
+    else step(S1{}, Hist{});
+    ph ^= 1;
+  }
+}
+
+// dq = scale * (sum of a row's partial slots): its selected blocks' slots
+// 0 .. nsel-1 and the own block's slot topk.  One thread per 8 columns.
+template <int D>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const bf16_t* __restrict__ dqp,
+                                                        const uint16_t* __restrict__ selpre,
+                                                        bf16_t* __restrict__ dq, int Hq, int G, int N,
+                                                        int topk, int MWB, float scale, size_t rows) {
+  constexpr int TPR = D / 8;
+  const size_t row = size_t(blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
+  const int c8 = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const int t = int(row % N);
+  const size_t bh = row / N;  // b * Hq + h
+  const size_t tok = (bh / Hq * (Hq / G) + (bh % Hq) / G) * N + t;
+  const int nsel = selpre[tok * (MWB + 1) + MWB];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bf16_t* src = dqp + row * size_t(topk + 1) * D + c8 * 8;
+  auto add = [&](int slot) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + size_t(slot) * D);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_lo(w[i]);
+      acc[2 * i + 1] += bf16_hi(w[i]);
+    }
+  };
+  for (int sl = 0; sl < nsel; ++sl) add(sl);
+  add(topk);
+  uint4 o;
+  o.x = pack_bf16(acc[0] * scale, acc[1] * scale);
+  o.y = pack_bf16(acc[2] * scale, acc[3] * scale);
+  o.z = pack_bf16(acc[4] * scale, acc[5] * scale);
+  o.w = pack_bf16(acc[6] * scale, acc[7] * scale);
+  *reinterpret_cast<uint4*>(dq + row * D + c8 * 8) = o;
+}
+
+// ds of a sparse-scope row from the dbeta values at its selected blocks:
+// ds[m] = (m selected ? dbeta[m] : 0) - g[m] * sum(dbeta) over the history,
+// g = exp(s - LSE_s); 0 from the own block on.  One wave per row.
+__global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict__ scores,
+                                                        const float* __restrict__ lse_s,
+                                                        const uint32_t* __restrict__ selbits,
+                                                        float* __restrict__ ds, int Hq, int G, int N,
+                                                        int C, int MWB, size_t rows) {
+  const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int t = int(row % N);
+  const size_t bh = row / N;
+  const size_t tok = (bh / Hq * (Hq / G) + (bh % Hq) / G) * N + t;
+  const int c = min(t / KT, C);
+  const uint32_t* bits = selbits + tok * MWB;
+  float* drow = ds + row * C;
+  const float* srow = scores + row * C;
+  float tot = 0.f;
+  for (int m2 = lane; m2 < c; m2 += 64)
+    if ((bits[m2 >> 5] >> (m2 & 31)) & 1u) tot += drow[m2];
+  for (int off = 32; off >= 1; off >>= 1) tot += shfl_xor(tot, off);
+  const float ls = lse_s[row];
+  for (int m2 = lane; m2 < C; m2 += 64) {
+    float out = 0.f;
+    if (m2 < c) {
+      const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
+      const bool sel = (bits[m2 >> 5] >> (m2 & 31)) & 1u;
+      out = (sel ? drow[m2] : 0.f) - gate * tot;
+    }
+    drow[m2] = out;
   }
 }
 
@@ -798,38 +1219,72 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   return true;
 }
 
-// Workspace: Delta per row | (sparse) per-token selection bitmask.
+// Workspace: Delta per row | (sparse) per-token selection bitmask, its prefix
+// counts, and the partial dQ slots.
+
+struct BwdWs {
+  size_t delta, selbits, selpre, dqp, total;
+};
+
+static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
+  BwdWs w{};
+  const size_t rows = size_t(d.B) * d.Hq * d.N;
+  const size_t tokens = size_t(d.B) * d.Hkv * d.N;
+  const int MWB = d.C > 31 ? (d.C + 31) / 32 : 1;
+  w.delta = 0;
+  size_t at = align_up(rows * sizeof(float));
+  if (sparse) {
+    w.selbits = at;
+    at += align_up(tokens * MWB * sizeof(uint32_t));
+    w.selpre = at;
+    at += align_up(tokens * (MWB + 1) * sizeof(uint16_t));
+    w.dqp = at;
+    at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
+  }
+  w.total = at;
+  return w;
+}
 
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
-  size_t bytes = align_up(size_t(d.B) * d.Hq * d.N * sizeof(float));
-  if (sparse) {
-    const int MWB = (d.C + 31) / 32;
-    bytes += align_up(size_t(d.B) * d.Hkv * d.N * (MWB > 0 ? MWB : 1) * sizeof(uint32_t));
-  }
-  (void)topk;
-  return bytes;
+  return bwd_ws_layout(d, topk, sparse).total;
+}
+
+template <int D, int G>
+static void launch_dq_sparse(BwdArgs a, size_t rows, hipStream_t s) {
+  SAS_LAUNCH("bwd_dq_kv", (bwd_dq_kv_kernel<D, G>), dim3(a.n_tiles * a.n_pairs), dim3(512), 0, s, a);
+  constexpr int RPB = 256 / (D / 8);
+  SAS_LAUNCH("dq_reduce", (dq_reduce_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a.dqp,
+             a.selpre, a.dq, a.Hq, G, a.N, a.topk, a.MWB, a.scale, rows);
+  SAS_LAUNCH("ds_sparse", ds_sparse_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.scores, a.lse_s,
+             a.selbits, a.ds, a.Hq, G, a.N, a.C, a.MWB, rows);
+}
+
+template <int D, int G>
+static void launch_dq_full(BwdArgs a, hipStream_t s) {
+  constexpr int NSUB = 2, WAVES = 8, NST = 2;
+  constexpr int TOK_WG = 16 * NSUB * WAVES / G;
+  a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
+  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, false>), dim3(a.n_tiles * a.n_pairs),
+             dim3(64 * WAVES), 0, s, a);
 }
 
 template <int D, int G, bool SPARSE>
 static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
-  constexpr int NSUB = 2;
-  constexpr int WAVES = 8;
-  constexpr int NST = 2;
-  constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   const size_t rows = size_t(B) * a.Hq * a.N;
   SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
              dim3(256), 0, s, a.o, a.dout, a.delta, rows);
   if (SPARSE) {
     const size_t tokens = size_t(B) * a.Hkv * a.N;
-    SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits, a.N,
-               a.topk, a.MWB, tokens);
+    SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits,
+               a.selpre, a.N, a.topk, a.MWB, tokens);
   }
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
   SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
-  a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
-  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, SPARSE>), dim3(a.n_tiles * a.n_pairs),
-             dim3(64 * WAVES), 0, s, a);
+  if (SPARSE)
+    launch_dq_sparse<D, G>(a, rows, s);
+  else
+    launch_dq_full<D, G>(a, s);
   return hipGetLastError();
 }
 
@@ -840,11 +1295,13 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            hipStream_t s) {
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
-  float* delta = reinterpret_cast<float*>(w);
-  uint32_t* selbits = reinterpret_cast<uint32_t*>(w + align_up(size_t(d.B) * d.Hq * d.N * sizeof(float)));
+  const BwdWs L = bwd_ws_layout(d, topk, sp);
+  float* delta = reinterpret_cast<float*>(w + L.delta);
   BwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
             scores, idx, lse, lse_s, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, ds, delta,
-            sp ? selbits : nullptr, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
+            sp ? reinterpret_cast<uint32_t*>(w + L.selbits) : nullptr,
+            sp ? reinterpret_cast<uint16_t*>(w + L.selpre) : nullptr,
+            sp ? reinterpret_cast<bf16_t*>(w + L.dqp) : nullptr, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
             (d.N + KT - 1) / KT, scale};
   if (a.MWB < 1) a.MWB = 1;
   const int G = d.G();

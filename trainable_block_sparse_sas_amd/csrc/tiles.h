@@ -153,6 +153,12 @@ __device__ void sparse_tables(const int32_t* __restrict__ idx, const float* __re
   }
 }
 
+// One lane's share of a wave's direct global -> LDS copy: 16 bytes from src
+// land at lds + 16 lane (lds is the wave-uniform base).
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds, 16, 0, 0);
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + c receives
 // element c of the 4 x 16-bit values addressed by lanes a, a + 4, a + 8 and
 // a + 12 of its group (checked on gfx950 with a standalone probe).  Pointing
