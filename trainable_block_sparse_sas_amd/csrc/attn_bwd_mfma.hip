@@ -52,6 +52,9 @@ struct BwdArgs {
   uint32_t* selbits; // workspace [B, Hkv, N, MWB] (sparse)
   uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
   bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: partial dQ per selected block (sparse)
+  const float* rowstat;  // workspace [B, Hq, N] x {Delta, -lse log2e, -(lse + LSE_s) log2e, 0} (sparse)
+  float* dbeta;          // workspace [B, Hq, N, topk]: dbeta per selected block, by slot (sparse)
+  float* dummy;          // workspace line that absorbs masked stores
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
 };
@@ -60,7 +63,10 @@ struct BwdArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __restrict__ o,
                                                              const bf16_t* __restrict__ dout,
-                                                             float* __restrict__ delta, size_t rows) {
+                                                             float* __restrict__ delta,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ lse_s,
+                                                             float4* __restrict__ rowstat, size_t rows) {
   constexpr int LPR = D / 8;  // lanes per row, 16-byte loads
   const size_t row = size_t(blockIdx.x) * (256 / LPR) + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
@@ -76,43 +82,15 @@ __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __res
     }
   }
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += shfl_xor(acc, off);
-  if (row < rows && sub == 0) delta[row] = acc;
-}
-
-// One wave per token: bitmask of the token's valid selected blocks, and (pre
-// != NULL) the number of set bits before each word, pre[tok][w] for w = 0 ..
-// MWB (the last entry is the token's number of selected blocks).
-__global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
-                                                      uint32_t* __restrict__ bits,
-                                                      uint16_t* __restrict__ pre, int N, int topk,
-                                                      int MWB, size_t tokens) {
-  const size_t tok = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (tok >= tokens) return;
-  const int t = int(tok % N);
-  const int c = t / KT;
-  const int32_t* ir = idx + tok * topk;
-  int carry = 0;
-  for (int w0 = 0; w0 < MWB; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t word = 0;
-    for (int e = 0; e < topk; ++e) {
-      const int m = ir[e];
-      if (m >= 0 && m < c && (m >> 5) == w) word |= 1u << (m & 31);
-    }
-    if (w < MWB) bits[tok * MWB + w] = word;
-    if (pre) {
-      const int cnt = __popc(word);
-      int incl = cnt;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      if (w < MWB) pre[tok * (MWB + 1) + w] = uint16_t(carry + incl - cnt);
-      carry += __shfl(incl, 63, 64);
+  if (row < rows && sub == 0) {
+    delta[row] = acc;
+    // sparse scope: the row's softmax offsets in base 2 for its own block
+    // (-lse) and for a gated block (-(lse + LSE_s); the block's score is added)
+    if (rowstat) {
+      const float l = lse[row];
+      rowstat[row] = make_float4(acc, -l * kLog2e, -(l + lse_s[row]) * kLog2e, 0.f);
     }
   }
-  if (pre && lane == 0) pre[tok * (MWB + 1) + MWB] = uint16_t(carry);
 }
 
 // --------------------------------------------------------------- dK / dV ----
@@ -416,337 +394,257 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------- dQ, sparse scope ----
-// KV-major, the dK/dV kernel's row stream: a workgroup owns block m of one KV
-// head and takes RS = 128 rows per step (waves 0-3 rows 0-63, waves 4-7 rows
-// 64-127, each wave 16 of the block's keys).  Per step it recomputes P and dS
-// for its rows, sums dS over the block's 64 keys into dbeta (gated rows; the
-// value goes to ds[row, m], finished by ds_sparse_kernel), stages dS^T over
-// the step's Q and dO area of LDS, and writes the block's share of dQ, dS K over the 64
-// keys, to the row's slot of the partial buffer: slot = rank of m among the
-// token's selected blocks, or topk for the own block (dq_reduce_kernel adds the
-// slots).  Every (row, key) pair is computed once, with no tile of unselected
-// blocks.
+// Key-major over the selection lists.  A workgroup takes one work item: a run
+// of at most L.chunk tokens of block m's sequence (its own tokens, then the
+// tokens whose Top-K holds m, ascending), i.e. chunk x G query rows.  Each wave
+// owns 16 of those rows per step and all 64 keys (lane = row, S^T = K Q^T with
+// K read from the block's LDS tile, dP^T = V dO^T with V held in registers),
+// so dS^T never leaves the
+// wave: its C fragments are the B operand of dQ^T = K^T dS^T, with the keys of
+// a 32-wide k step in the order {4 lq + i, 16 + 4 lq + i}, and K^T comes from
+// the block's K tile through transposing LDS reads in the same order.  Per
+// row the block contributes dbeta = sum of dS over its keys (gated rows) and
+// a dQ share, both written to the row's slot: the rank of m among the row's
+// selected blocks (topk for the own block's dQ share).  Waves run independent two-stage pipelines on private LDS stages:
+// no workgroup barrier after the prologue, and a fixed count of stores per
+// step so the wait for the next stage's loads does not wait for them.
 template <int D, int G>
-__global__ __launch_bounds__(512) void bwd_dq_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) {
   using namespace tiles;
   constexpr int WAVES = 8;
-  constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;
   constexpr int ND = D / 16;
   constexpr int CH = D / 8;
-  constexpr int RS = 128;           // rows per step
-  constexpr int TPS = RS / G;       // tokens per step
-  constexpr int NPIECE = RS * D * 2 / 1024;
-  constexpr int PPW = NPIECE / WAVES;
-  constexpr int NSTAT = 6;          // lse, Delta, score, LSE_s, prefix count, selection word
-  // Stage layout (16-bit units): Q [RS][D] | dO [RS][D] | fp32 [NSTAT][RS].
-  constexpr int ST_DO = RS * D, ST_F = 2 * RS * D;
-  constexpr int STAGE = 2 * RS * D + NSTAT * RS * 2;
-  constexpr int DSP = RS + 8;       // dS^T [key][row] stride (padded)
-  constexpr int QCAP = 1024;
-  static_assert(KT * DSP <= 2 * RS * D, "dS^T fits in the step's Q and dO area");
-  static_assert(NPIECE % WAVES == 0, "tile loads must split evenly over the waves");
-  static_assert(QCAP >= NT + TPS, "queue holds one scan chunk plus a step");
-  __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];  // the block's keys, row-major
-  __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];
-  __shared__ __attribute__((aligned(16))) float red[4][RS];
-  __shared__ int queue[QCAP];
-  __shared__ int q_wave[WAVES];
+  constexpr int STG = 2 * 16 * D;        // per wave stage: Q | dO of 16 rows
+  constexpr int NLD = 16 * CH / 64;      // wave DMA instructions per operand
+  constexpr int NSTORE = NLD + 1;        // stores per step: dQ share rows + dbeta
+  static_assert(KT * D <= WAVES * STG, "V tile fits in the stage area");
+  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t S0[WAVES * STG];
+  __shared__ __attribute__((aligned(16))) uint16_t S1[WAVES * STG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave >> 2, kw = wave & 3;  // row group (64 rows), key group (16 keys)
-  int tile, pair;
-  xcd_order(blockIdx.x, a.n_tiles, a.n_pairs, &tile, &pair);
-  const int m = a.n_tiles - 1 - tile;
+  const int pairs = a.n_pairs;
+  const int pair = blockIdx.x % pairs, item = blockIdx.x / pairs;
+  if (item >= int(L.nitems[pair])) return;
+  const uint32_t iv = L.items[size_t(pair) * L.maxitems + item];
+  const int m = int(iv & 0xffffu), run = int(iv >> 16);
   const int b = pair / a.Hkv, g = pair % a.Hkv;
   const int N = a.N, C = a.C;
   const int j0 = m * KT;
-  const float c1 = a.scale * kLog2e;
+  const int own_n = min(KT, N - j0);
+  const uint32_t* bo = L.blkoff + size_t(pair) * (L.NB + 1) + m;
+  const uint32_t* ents = L.ents + size_t(pair) * L.ents_per_pair + bo[0];
+  const int len = own_n + int(bo[1] - bo[0]);
+  const int p0 = run * L.chunk, p1 = min(len, p0 + L.chunk);
+  const int nrows = (p1 - p0) * G;
+  const int ngroups = (nrows + 15) >> 4;
+  const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
   const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
-  const size_t tok0 = (size_t(b) * a.Hkv + g) * N;   // token index base (selection tables)
-  const int MWB = a.MWB;
+  const float c1 = a.scale * kLog2e;
+  const int topk1 = a.topk + 1;
 
-  // The block's keys into LDS (A operand of dQ^T = K^T dS^T, read transposed),
-  // and this wave's 16 keys as B operands of S and dP.
+  // ---- prologue: K tile (kept) and V tile (over stage 0) into LDS, then the
+  // A operands of S^T and dP^T into registers.
   {
-    // 16 pieces of 1 KB (4 rows each for D = 128) over the waves; swizzled
-    // like the Q tile: row r's chunk pc holds chunk pc ^ k_swz(r).
     const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+    const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
     constexpr int KPIECE = KT * D * 2 / 1024;
     for (int j = wave; j < KPIECE; j += WAVES) {
       const int sl = 64 * j + lane;
       const int r = sl / CH, pc = sl % CH;
-      const int key = min(j0 + r, N - 1);
-      dma16_to_lds(kh + size_t(key) * D + ((pc ^ k_swz<D>(r)) * 8), Ksh + j * 512);
+      const size_t key = size_t(min(j0 + r, N - 1));
+      const int c = (pc ^ k_swz<D>(r)) * 8;
+      dma16_to_lds(kh + key * D + c, Ksh + j * 512);
+      dma16_to_lds(vh + key * D + c, S0 + j * 512);
     }
   }
-  uint4 kf[KS], vf[KS];
+  wait_vm<0>();
+  __syncthreads();
+  uint4 vf[4][KS];
   {
-    const int my_key = j0 + kw * 16 + (lane & 15);
-    const size_t kr = (size_t(b) * a.Hkv + g) * N + (my_key < N ? my_key : 0);
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.k + kr * D + ks * 32 + (lane >> 4) * 8)
-                          : make_uint4(0, 0, 0, 0);
-      vf[ks] = my_key < N ? *reinterpret_cast<const uint4*>(a.v + kr * D + ks * 32 + (lane >> 4) * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  }
-
-  // ---- token stream (the dK/dV kernel's): own block, then selecting tokens
-  const int own_n = min(KT, N - j0);
-  int own_pos = 0;
-  int qh = 0, qt = 0, scan = j0 + KT;
-  const uint32_t* bits = a.selbits + tok0 * size_t(MWB);
-  auto refill = [&]() {
-    while (qt - qh < TPS && scan < N) {
-      const int t = scan + tid;
-      const bool sel = t < N && ((bits[size_t(t) * MWB + (m >> 5)] >> (m & 31)) & 1u);
-      const unsigned long long bal = __ballot(sel);
-      if (lane == 0) q_wave[wave] = __popcll(bal);
-      __syncthreads();
-      int base = qt, total = 0;
-      for (int w = 0; w < WAVES; ++w) {
-        const int c = q_wave[w];
-        base += w < wave ? c : 0;
-        total += c;
-      }
-      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-      if (sel) queue[(base + __popcll(bal & lt)) % QCAP] = t;
-      __syncthreads();
-      qt += total;
-      scan += NT;
-    }
-  };
-  auto take = [&](int& phase, int& first, int& cnt) {
-    if (own_pos < own_n) {
-      phase = 0;
-      first = j0 + own_pos;
-      cnt = min(TPS, own_n - own_pos);
-      own_pos += cnt;
-      return;
-    }
-    phase = 1;
-    first = qh;
-    cnt = qt > qh ? min(TPS, qt - qh) : -1;
-    qh += cnt > 0 ? cnt : 0;
-  };
-  auto token_of = [&](int phase, int first, int cnt, int i) -> int {
-    if (i >= cnt) return -1;
-    if (phase == 1) return queue[(first + i) % QCAP];
-    return first + i;
-  };
-  auto rst = [&](auto tag) -> uint16_t* {
-    if constexpr (decltype(tag)::value == 0) return R0;
-    else return R1;
-  };
-  auto issue = [&](auto tag, int phase, int first, int cnt, int ln) {
-    constexpr int P = decltype(tag)::value;
-    uint16_t* st = rst(tag);
+    const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int j = wave * PPW + i;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = 16 * kt + lr;
+        vf[kt][ks] = *reinterpret_cast<const uint4*>(S0 + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
+      }
+  }
+  __syncthreads();  // the V tile is read before stage 0 is reloaded
+  if (nk == 0) return;
+
+  // entry of a row of group gk: token | slot << 23 (own block: slot topk);
+  // rows past the item read a valid address and are masked by q < nrows.
+  auto entry = [&](int gk, int r) -> uint32_t {
+    const int q = 16 * gk + r;
+    const int p = p0 + q / G;
+    const bool hist = q < nrows && p >= own_n;
+    const uint32_t e = *(hist ? ents + (p - own_n) : L.ents);
+    return hist ? e : (uint32_t(j0 + min(p, own_n - 1)) | (uint32_t(a.topk) << 23));
+  };
+  auto grow_of = [&](int gk, int r, uint32_t e) -> size_t {
+    const int q = 16 * gk + r;
+    const int t = q < nrows ? int(e & 0x7fffffu) : 0;
+    return hrow0 + size_t(q % G) * N + t;
+  };
+  auto stg = [&](auto tag) -> uint16_t* {
+    if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;
+    else return S1 + wave * STG;
+  };
+  // Q and dO rows of group gk into a stage; row r's entry comes from lane r.
+  auto issue = [&](auto tag, int gk, uint32_t e, int ln) {
+    uint16_t* st = stg(tag);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
       const int sl = 64 * j + ln;
       const int r = sl / CH, pc = sl % CH;
-      const int t = token_of(phase, first, cnt, r / G);
-      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
-      const int c = pc ^ k_swz<D>(r);
-      __builtin_amdgcn_global_load_lds(a.q + gr * D + c * 8, (lds_ptr_t)(st + j * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.dout + gr * D + c * 8, (lds_ptr_t)(st + ST_DO + j * 512), 16, 0,
-                                       0);
+      const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+      const size_t gr = grow_of(gk, r, er);
+      const int c = (pc ^ k_swz<D>(r)) * 8;
+      dma16_to_lds(a.q + gr * D + c, st + j * 512);
+      dma16_to_lds(a.dout + gr * D + c, st + 16 * D + j * 512);
     }
-    // per-row statistics: 2 x NSTAT loads of 64 rows over the waves
-    for (int k = wave; k < 2 * NSTAT; k += WAVES) {
-      const int stat = k >> 1, r = 64 * (k & 1) + ln;
-      const int t = token_of(phase, first, cnt, r / G);
-      const int tt = t >= 0 ? t : 0;
-      const size_t gr = hrow0 + size_t(r % G) * N + tt;
-      const void* src;
-      switch (stat) {
-        case 0: src = a.lse + gr; break;
-        case 1: src = a.delta + gr; break;
-        case 2: src = phase == 1 ? a.scores + gr * C + m : a.lse + gr; break;
-        case 3: src = a.lse_s + gr; break;
-        // prefix count: a 32-bit load of the aligned pair holding the 16-bit entry
-        case 4:
-          src = phase == 1 ? (const void*)(a.selpre + (((tok0 + tt) * (MWB + 1) + (m >> 5)) & ~size_t(1)))
-                           : (const void*)(a.lse + gr);
-          break;
-        default: src = phase == 1 ? (const void*)(bits + size_t(tt) * MWB + (m >> 5)) : (const void*)(a.lse + gr);
-      }
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + ST_F + (stat * RS + 64 * (k & 1)) * 2), 4, 0, 0);
-    }
-    if (tid < RS) tok_sh[P][tid] = token_of(phase, first, cnt, tid / G);
+  };
+  struct Stat {
+    float4 rs;
+    float sc;
+  };
+  auto load_stat = [&](int gk, uint32_t e, int lr) -> Stat {
+    const size_t gr = grow_of(gk, lr, e);
+    Stat s;
+    s.rs = reinterpret_cast<const float4*>(a.rowstat)[gr];
+    s.sc = a.scores[gr * C + (int(e & 0x7fffffu) >= j0 + KT ? m : 0)];
+    return s;
   };
 
-  // Reduce-scatter of 16 values over the 16 lanes of a row of lanes: afterwards
-  // lane lr holds the sum of value lr.
-  auto reduce16 = [&](float (&v)[16], int lr) -> float {
-#pragma unroll
-    for (int M = 8, n = 16; M >= 1; M >>= 1, n >>= 1) {
-      const bool hi = (lr & M) != 0;
-#pragma unroll
-      for (int j = 0; j < n / 2; ++j) {
-        const float send = hi ? v[j] : v[j + n / 2];
-        const float keep = hi ? v[j + n / 2] : v[j];
-        v[j] = keep + __shfl_xor(send, M, 64);
-      }
-    }
-    return v[0];
-  };
-
-  auto compute = [&](auto tag, auto mkt, int ln) {
-    constexpr int P = decltype(tag)::value;
-    constexpr bool MK = decltype(mkt)::value;
-    uint16_t* st = rst(tag);
-    const uint16_t* Qs = st;
-    const uint16_t* dOs = st + ST_DO;
-    const float* F = reinterpret_cast<const float*>(st + ST_F);
+  auto compute = [&](auto tag, int gk, uint32_t e, const Stat& stt, int ln) {
+    const uint16_t* Qs = stg(tag);
+    const uint16_t* dOs = Qs + 16 * D;
     const int lr = ln & 15, lq = ln >> 4;
-    const int key = j0 + kw * 16 + lr;
     const int qsw = k_swz<D>(lr);
-    // S and dP for this wave's 64 rows (64 rg + 16 rs + lr) and 16 keys.
     f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int rs = 0; rs < 4; ++rs) {
-      sacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = lr * D + (((4 * ks + lq) ^ qsw) * 8);
+      const uint4 qb = *reinterpret_cast<const uint4*>(Qs + off);
+      const uint4 ob = *reinterpret_cast<const uint4*>(dOs + off);
 #pragma unroll
-      for (int rs = 0; rs < 4; ++rs) {
-        const int off = (64 * rg + 16 * rs + lr) * D + (((4 * ks + lq) ^ qsw) * 8);
-        const uint4 qa = *reinterpret_cast<const uint4*>(Qs + off);
-        const uint4 oa = *reinterpret_cast<const uint4*>(dOs + off);
-        sacc[rs] = mfma16(qa, kf[ks], sacc[rs]);
-        pacc[rs] = mfma16(oa, vf[ks], pacc[rs]);
-      }
-    // dS (lane: key, rows 64 rg + 16 rs + 4 lq + i)
-    float dsv[16];
-    uint2 dpk[4];
-#pragma unroll
-    for (int rs = 0; rs < 4; ++rs) {
-      const int r0 = 64 * rg + 16 * rs + 4 * lq;
-      const float4 lse = *reinterpret_cast<const float4*>(F + r0);
-      const float4 del = *reinterpret_cast<const float4*>(F + RS + r0);
-      const float4 sc = *reinterpret_cast<const float4*>(F + 2 * RS + r0);
-      const float4 lss = *reinterpret_cast<const float4*>(F + 3 * RS + r0);
-      const int4 tk = *reinterpret_cast<const int4*>(&tok_sh[P][r0]);
-      const float lv[4] = {lse.x, lse.y, lse.z, lse.w}, dl[4] = {del.x, del.y, del.z, del.w};
-      const float sv[4] = {sc.x, sc.y, sc.z, sc.w}, ls[4] = {lss.x, lss.y, lss.z, lss.w};
-      const int tv[4] = {tk.x, tk.y, tk.z, tk.w};
-      float d[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float off = MK ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
-        float x = fmaf(sacc[rs][i], c1, off);
-        const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
-        x = ok ? x : kNegInf;
-        d[i] = exp2_hw(x) * (pacc[rs][i] - dl[i]);
-        dsv[4 * rs + i] = d[i];
-      }
-      dpk[rs] = make_uint2(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]));
-    }
-    // dbeta: sum of dS over this wave's 16 keys, one row per lane; the four key
-    // groups meet in LDS.
-    if (!MK) {
-      const float part = reduce16(dsv, lr);
-      red[kw][64 * rg + 16 * (lr >> 2) + 4 * lq + (lr & 3)] = part;
-    }
-    ring_barrier();  // every wave is done with Q and dO of this stage
-    // dS^T [key][row] over the Q (and dO) area
-    uint16_t* dst = st;
-#pragma unroll
-    for (int rs = 0; rs < 4; ++rs)
-      *reinterpret_cast<uint2*>(dst + (kw * 16 + lr) * DSP + 64 * rg + 16 * rs + 4 * lq) = dpk[rs];
-    if (!MK && tid < RS) {
-      const int t = tok_sh[P][tid];
-      if (t >= 0) {
-        const float db = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-        a.ds[(hrow0 + size_t(tid % G) * N + t) * C + m] = db;
+      for (int kt = 0; kt < 4; ++kt) {
+        const int r = 16 * kt + lr;
+        const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
+        sacc[kt] = mfma16(ka, qb, sacc[kt]);
+        pacc[kt] = mfma16(vf[kt][ks], ob, pacc[kt]);
       }
     }
-    ring_barrier();  // dS^T complete
-    // dQ^T (d x rows) for rows 16 wave .. 16 wave + 15: A = K^T (keys along k),
-    // B = dS^T, both read transposed: lane s of group lq points at key
-    // 32 kk + 8 lq + s / 4 (and + 4), column 4 (s % 4) of its 16-wide tile.
+    const int q = 16 * gk + lr;
+    const bool valid = q < nrows;
+    const int t = int(e & 0x7fffffu);
+    const bool own = t < j0 + KT;
+    const float off = own ? stt.rs.y : fmaf(stt.sc, kLog2e, stt.rs.z);
+    const float dl = stt.rs.x;
+    float db = 0.f;
+    uint4 dsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float d[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = 2 * kk + h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 16 * kt + 4 * lq + i;
+          const bool ok = valid && (!own || key <= t);
+          const float p = exp2_hw(ok ? fmaf(sacc[kt][i], c1, off) : kNegInf);
+          const float x = p * (pacc[kt][i] - dl);
+          db += x;
+          d[4 * h + i] = x;
+        }
+      }
+      dsb[kk] = make_uint4(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]), pack_bf16(d[4], d[5]),
+                           pack_bf16(d[6], d[7]));
+    }
+    db += shfl_xor(db, 16);
+    db += shfl_xor(db, 32);
     f32x4 dqa[ND];
 #pragma unroll
     for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int ka = 32 * kk + 8 * lq + (lr >> 2), kb = ka + 4;
-      const uint2 s0 = lds_read_tr16(dst + ka * DSP + 16 * wave + 4 * (lr & 3));
-      const uint2 s1 = lds_read_tr16(dst + kb * DSP + 16 * wave + 4 * (lr & 3));
-      const uint4 dsb = make_uint4(s0.x, s0.y, s1.x, s1.y);
+      const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
+      const int swa = k_swz<D>(ka), swb = k_swz<D>(kb);
 #pragma unroll
       for (int md = 0; md < ND; ++md) {
         const int col = 16 * md + 4 * (lr & 3);
-        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ k_swz<D>(ka)) << 3) + (col & 7)));
-        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ k_swz<D>(kb)) << 3) + (col & 7)));
-        dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb, dqa[md]);
+        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ swa) << 3) + (col & 7)));
+        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ swb) << 3) + (col & 7)));
+        dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb[kk], dqa[md]);
       }
     }
-    // partial dQ of row 16 wave + lr: lane holds d = 16 md + 4 lq + i
-    {
-      const int r = 16 * wave + lr;
-      const int t = tok_sh[P][r];
-      if (t >= 0) {
-        int slot = a.topk;
-        if (!MK) {
-          const uint32_t pw = reinterpret_cast<const uint32_t*>(F + 4 * RS)[r];
-          const size_t pidx = (tok0 + t) * (MWB + 1) + (m >> 5);
-          const int pre = int((pidx & 1) ? (pw >> 16) : (pw & 0xffffu));
-          const uint32_t word = reinterpret_cast<const uint32_t*>(F + 5 * RS)[r];
-          slot = pre + __popc(word & ((1u << (m & 31)) - 1u));
-        }
-        bf16_t* dp = a.dqp + ((hrow0 + size_t(r % G) * N + t) * (a.topk + 1) + slot) * D;
+    // dQ^T fragments to the wave's stage (Q area, already consumed) as rows,
+    // chunk c of row r at c ^ (r % CH), then whole rows out: every store
+    // writes full lines.  Rows past the item go to the dummy line, and so does
+    // dbeta of own rows, so each step issues the same count of stores.
+    uint16_t* W = const_cast<uint16_t*>(Qs);
 #pragma unroll
-        for (int md = 0; md < ND; ++md) {
-          uint2 w;
-          w.x = pack_bf16(dqa[md][0], dqa[md][1]);
-          w.y = pack_bf16(dqa[md][2], dqa[md][3]);
-          *reinterpret_cast<uint2*>(dp + 16 * md + 4 * lq) = w;
-        }
-      }
+    for (int md = 0; md < ND; ++md) {
+      uint2 w;
+      w.x = pack_bf16(dqa[md][0], dqa[md][1]);
+      w.y = pack_bf16(dqa[md][2], dqa[md][3]);
+      const int c = (2 * md + (lq >> 1)) ^ (lr % CH);
+      *reinterpret_cast<uint2*>(W + lr * D + c * 8 + 4 * (lq & 1)) = w;
     }
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int sl = 64 * j + ln;
+      const int r = sl / CH, cc = sl % CH;
+      const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+      const bool vr = 16 * gk + r < nrows;
+      const uint4 v = *reinterpret_cast<const uint4*>(W + r * D + ((cc ^ (r % CH)) * 8));
+      bf16_t* dp = vr ? a.dqp + (grow_of(gk, r, er) * topk1 + (er >> 23)) * D + cc * 8
+                      : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+      *reinterpret_cast<uint4*>(dp) = v;
+    }
+    const size_t gr = grow_of(gk, lr, e);
+    float* dbp = (valid && !own) ? a.dbeta + gr * a.topk + (e >> 23) : a.dummy + 64;
+    *dbp = db;
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using Own = std::integral_constant<bool, true>;
-  using Hist = std::integral_constant<bool, false>;
-  int cur_phase, cur_first, cur_cnt;
-  take(cur_phase, cur_first, cur_cnt);
-  if (own_pos >= own_n) refill();
-  if (cur_cnt > 0) issue(S0{}, cur_phase, cur_first, cur_cnt, lane);
-  auto step = [&](auto tag, auto mkt) {
+  using S0t = std::integral_constant<int, 0>;
+  using S1t = std::integral_constant<int, 1>;
+  // pipeline: group k = wave + WAVES k of this wave
+  uint32_t e0 = entry(wave, lane & 15);
+  uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
+  issue(S0t{}, wave, e0, lane);
+  Stat st0 = load_stat(wave, e0, lane & 15), st1;
+  wait_vm<0>();
+  auto step = [&](auto tag, int k) {
     using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    wait_vm<0>();
-    ring_barrier();
-    int nph, nfirst, ncnt;
-    take(nph, nfirst, ncnt);
-    if (ncnt > 0) issue(Pn{}, nph, nfirst, ncnt, ln);
-    compute(tag, mkt, ln);
-    if (own_pos >= own_n) refill();
-    cur_phase = nph;
-    cur_first = nfirst;
-    cur_cnt = ncnt;
+    const int gk = wave + WAVES * k;
+    uint32_t e2 = 0;
+    if (k + 1 < nk) {
+      issue(Pn{}, gk + WAVES, e1, ln);
+      st1 = load_stat(gk + WAVES, e1, ln & 15);
+      if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
+    }
+    compute(tag, gk, e0, st0, ln);
+    wait_vm<NSTORE>();
+    e0 = e1;
+    e1 = e2;
+    st0 = st1;
   };
-  int ph = 0;
-  while (cur_cnt > 0 && cur_phase == 0) {
-    step(S0{}, Own{});
-    if (cur_cnt <= 0 || cur_phase != 0) { ph = 1; break; }
-    step(S1{}, Own{});
-  }
-  while (cur_cnt > 0) {
-    if (ph == 0) step(S0{}, Hist{});
-    else step(S1{}, Hist{});
-    ph ^= 1;
+  for (int k = 0; k < nk; k += 2) {
+    step(S0t{}, k);
+    if (k + 1 < nk) step(S1t{}, k + 1);
   }
 }
 
@@ -785,14 +683,17 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const bf16_t* __restrict
   *reinterpret_cast<uint4*>(dq + row * D + c8 * 8) = o;
 }
 
-// ds of a sparse-scope row from the dbeta values at its selected blocks:
-// ds[m] = (m selected ? dbeta[m] : 0) - g[m] * sum(dbeta) over the history,
-// g = exp(s - LSE_s); 0 from the own block on.  One wave per row.
+// ds of a sparse-scope row from its dbeta slots (slot = rank of the block
+// among the row's selected blocks): ds[m] = (m selected ? dbeta[slot(m)] : 0)
+// - g[m] * sum(dbeta) over the history, g = exp(s - LSE_s); 0 from the own
+// block on.  One wave per row.
 __global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict__ scores,
                                                         const float* __restrict__ lse_s,
                                                         const uint32_t* __restrict__ selbits,
+                                                        const uint16_t* __restrict__ selpre,
+                                                        const float* __restrict__ dbeta,
                                                         float* __restrict__ ds, int Hq, int G, int N,
-                                                        int C, int MWB, size_t rows) {
+                                                        int C, int MWB, int topk, size_t rows) {
   const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -801,21 +702,27 @@ __global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict_
   const size_t tok = (bh / Hq * (Hq / G) + (bh % Hq) / G) * N + t;
   const int c = min(t / KT, C);
   const uint32_t* bits = selbits + tok * MWB;
-  float* drow = ds + row * C;
-  const float* srow = scores + row * C;
+  const int nsel = selpre[tok * (MWB + 1) + MWB];
+  const float* db = dbeta + row * topk;
   float tot = 0.f;
-  for (int m2 = lane; m2 < c; m2 += 64)
-    if ((bits[m2 >> 5] >> (m2 & 31)) & 1u) tot += drow[m2];
+  for (int s2 = lane; s2 < nsel; s2 += 64) tot += db[s2];
   for (int off = 32; off >= 1; off >>= 1) tot += shfl_xor(tot, off);
   const float ls = lse_s[row];
-  for (int m2 = lane; m2 < C; m2 += 64) {
+  const float* srow = scores + row * C;
+  float* drow = ds + row * C;
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int run = 0;
+  for (int m0 = 0; m0 < C; m0 += 64) {
+    const int m2 = m0 + lane;
+    const bool sel = m2 < c && ((bits[m2 >> 5] >> (m2 & 31)) & 1u);
+    const unsigned long long bal = __ballot(sel);
     float out = 0.f;
     if (m2 < c) {
       const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-      const bool sel = (bits[m2 >> 5] >> (m2 & 31)) & 1u;
-      out = (sel ? drow[m2] : 0.f) - gate * tot;
+      out = (sel ? db[run + __popcll(bal & lt)] : 0.f) - gate * tot;
     }
-    drow[m2] = out;
+    if (m2 < C) drow[m2] = out;
+    run += __popcll(bal);
   }
 }
 
@@ -1211,35 +1118,39 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   if (d.C < 1) return false;
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  if (sparse) {
-    // the dQ kernel's per-workgroup tables (256 rows, 256 / G tokens)
-    if (size_t(256) * topk > kDqBiasMax || size_t(256 / G) * topk > kDqListMax) return false;
-    if (((d.C + 32) >> 5) > kDqMaskWords) return false;
-  }
+  // sparse scope: list entries hold the token in 23 bits and the slot in 9,
+  // work items the block in 16 bits
+  if (sparse && (d.N > (1 << 22) || topk > 256)) return false;
   return true;
 }
 
-// Workspace: Delta per row | (sparse) per-token selection bitmask, its prefix
-// counts, and the partial dQ slots.
+// Workspace: Delta per row | (sparse) row statistics, selection lists, the
+// partial dQ slots and a dummy line for masked stores.
+
+constexpr int kDqChunk = 256;  // tokens per work item of the sparse dQ kernel
 
 struct BwdWs {
-  size_t delta, selbits, selpre, dqp, total;
+  size_t delta, rowstat, lists, dqp, dbeta, dummy, total;
 };
 
 static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
   BwdWs w{};
   const size_t rows = size_t(d.B) * d.Hq * d.N;
-  const size_t tokens = size_t(d.B) * d.Hkv * d.N;
-  const int MWB = d.C > 31 ? (d.C + 31) / 32 : 1;
   w.delta = 0;
   size_t at = align_up(rows * sizeof(float));
   if (sparse) {
-    w.selbits = at;
-    at += align_up(tokens * MWB * sizeof(uint32_t));
-    w.selpre = at;
-    at += align_up(tokens * (MWB + 1) * sizeof(uint16_t));
+    w.rowstat = at;
+    at += align_up(rows * sizeof(float4));
+    size_t lb = 0;
+    sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kDqChunk, nullptr, &lb);
+    w.lists = at;
+    at += align_up(lb);
     w.dqp = at;
     at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
+    w.dbeta = at;
+    at += align_up(rows * size_t(topk > 0 ? topk : 1) * sizeof(float));
+    w.dummy = at;
+    at += align_up(512);
   }
   w.total = at;
   return w;
@@ -1250,13 +1161,13 @@ size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 }
 
 template <int D, int G>
-static void launch_dq_sparse(BwdArgs a, size_t rows, hipStream_t s) {
-  SAS_LAUNCH("bwd_dq_kv", (bwd_dq_kv_kernel<D, G>), dim3(a.n_tiles * a.n_pairs), dim3(512), 0, s, a);
+static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStream_t s) {
+  SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(a.n_pairs * L.maxitems), dim3(512), 0, s, a, L);
   constexpr int RPB = 256 / (D / 8);
   SAS_LAUNCH("dq_reduce", (dq_reduce_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a.dqp,
              a.selpre, a.dq, a.Hq, G, a.N, a.topk, a.MWB, a.scale, rows);
   SAS_LAUNCH("ds_sparse", ds_sparse_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.scores, a.lse_s,
-             a.selbits, a.ds, a.Hq, G, a.N, a.C, a.MWB, rows);
+             a.selbits, a.selpre, a.dbeta, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, rows);
 }
 
 template <int D, int G>
@@ -1269,20 +1180,19 @@ static void launch_dq_full(BwdArgs a, hipStream_t s) {
 }
 
 template <int D, int G, bool SPARSE>
-static hipError_t bwd_mfma_t(BwdArgs a, int B, hipStream_t s) {
+static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s) {
   const size_t rows = size_t(B) * a.Hq * a.N;
   SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
-             dim3(256), 0, s, a.o, a.dout, a.delta, rows);
+             dim3(256), 0, s, a.o, a.dout, a.delta, a.lse, a.lse_s, (float4*)a.rowstat, rows);
   if (SPARSE) {
-    const size_t tokens = size_t(B) * a.Hkv * a.N;
-    SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, a.idx, a.selbits,
-               a.selpre, a.N, a.topk, a.MWB, tokens);
+    const hipError_t e = launch_sel_lists(a.idx, L, B, a.Hkv, a.N, a.C, a.topk, KT, s);
+    if (e != hipSuccess) return e;
   }
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
   SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
   if (SPARSE)
-    launch_dq_sparse<D, G>(a, rows, s);
+    launch_dq_sparse<D, G>(a, L, rows, s);
   else
     launch_dq_full<D, G>(a, s);
   return hipGetLastError();
@@ -1295,19 +1205,44 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            hipStream_t s) {
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
-  const BwdWs L = bwd_ws_layout(d, topk, sp);
-  float* delta = reinterpret_cast<float*>(w + L.delta);
-  BwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
-            scores, idx, lse, lse_s, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, ds, delta,
-            sp ? reinterpret_cast<uint32_t*>(w + L.selbits) : nullptr,
-            sp ? reinterpret_cast<uint16_t*>(w + L.selpre) : nullptr,
-            sp ? reinterpret_cast<bf16_t*>(w + L.dqp) : nullptr, d.Hq, d.Hkv, d.N, d.C, sp ? topk : 0, (d.C + 31) / 32, 0, 0,
-            (d.N + KT - 1) / KT, scale};
-  if (a.MWB < 1) a.MWB = 1;
+  const BwdWs W = bwd_ws_layout(d, topk, sp);
+  SelLists L{};
+  if (sp) L = sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kDqChunk, w + W.lists, nullptr);
+  BwdArgs a{};
+  a.q = (const bf16_t*)q;
+  a.k = (const bf16_t*)k;
+  a.v = (const bf16_t*)v;
+  a.o = (const bf16_t*)o;
+  a.dout = (const bf16_t*)dout;
+  a.scores = scores;
+  a.idx = idx;
+  a.lse = lse;
+  a.lse_s = lse_s;
+  a.dq = (bf16_t*)dq;
+  a.dk = (bf16_t*)dk;
+  a.dv = (bf16_t*)dv;
+  a.ds = ds;
+  a.delta = reinterpret_cast<float*>(w + W.delta);
+  if (sp) {
+    a.selbits = L.bits;
+    a.selpre = L.pre;
+    a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
+    a.rowstat = reinterpret_cast<const float*>(w + W.rowstat);
+    a.dbeta = reinterpret_cast<float*>(w + W.dbeta);
+    a.dummy = reinterpret_cast<float*>(w + W.dummy);
+  }
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.N = d.N;
+  a.C = d.C;
+  a.topk = sp ? topk : 0;
+  a.MWB = sp ? L.MWB : 1;
+  a.NB = (d.N + KT - 1) / KT;
+  a.scale = scale;
   const int G = d.G();
-#define SAS_BWD_CASE(DD, GG)                                                              \
-  if (d.D == DD && G == GG)                                                               \
-    return sp ? bwd_mfma_t<DD, GG, true>(a, d.B, s) : bwd_mfma_t<DD, GG, false>(a, d.B, s);
+#define SAS_BWD_CASE(DD, GG)                                                                        \
+  if (d.D == DD && G == GG)                                                                         \
+    return sp ? bwd_mfma_t<DD, GG, true>(a, L, d.B, s) : bwd_mfma_t<DD, GG, false>(a, L, d.B, s);
   SAS_BWD_CASE(128, 4)
   SAS_BWD_CASE(128, 1)
   SAS_BWD_CASE(128, 2)

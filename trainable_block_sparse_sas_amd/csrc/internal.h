@@ -50,6 +50,27 @@ hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B,
                        int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s);
 
+// ---- selection lists (key-major sparse kernels) ---------------------------------
+// Per KV head, the tokens selecting each history block, ascending; built from
+// the Top-K indices by launch_sel_lists into a workspace slice.
+struct SelLists {
+  uint32_t* bits;    // [pairs * N][MWB] selected-block bitmask per token
+  uint16_t* pre;     // [pairs * N][MWB + 1] set bits before each word; [MWB] = count
+  uint32_t* cnt;     // [pairs][NB][nseg] tokens of a segment selecting a block
+  uint32_t* segoff;  // [pairs][NB][nseg] list offset of (block, segment)
+  uint32_t* blkoff;  // [pairs][NB + 1] list offset of each block; [NB] = total
+  uint32_t* nitems;  // [pairs] work items
+  uint32_t* items;   // [pairs][maxitems] block | (run index << 16)
+  uint32_t* ents;    // [pairs][ents_per_pair] token | (slot << 23)
+  int MWB, NB, nseg, chunk, maxitems;
+  size_t ents_per_pair;
+};
+// base == NULL: sizes only (*bytes).  chunk = tokens per work item.
+SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int chunk, char* base,
+                          size_t* bytes);
+hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
+                            int topk, int block, hipStream_t s);
+
 // ---- gated attention ----------------------------------------------------------
 size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);

@@ -1,0 +1,212 @@
+// Per-block lists of the tokens that select each history block: the transpose
+// of the Top-K selection (each token's k chosen earlier blocks, the sparse
+// branch of the method: jaehun.me review "Why the Four Design Choices Matter",
+// the Top-K gate; the blog's 方法核心 section), used by the key-major kernels.
+//
+//   bits   per token, a bitmask of its valid selected blocks (m < own block;
+//          entries out of range or repeated count once), and pre, the number of
+//          set bits before each 32-block word (pre[MWB] = number selected).
+//   count  per (KV head, word w, token segment): how many tokens of the segment
+//          select each of the word's 32 blocks.
+//   scan   per KV head: exclusive offsets over (block, segment), so each
+//          block's list is its segments' tokens in ascending order, and the work
+//          items: runs of at most CHUNK tokens over a block's virtual sequence
+//          (its own tokens, then its list).
+//   fill   the lists, entry = token | (rank of the block among the token's
+//          selected blocks) << 23.
+// Every step is deterministic: the lists come out sorted by token.
+#include "common.h"
+#include "internal.h"
+
+namespace sas {
+namespace {
+
+constexpr int SEG = 2048;  // tokens per segment of the count / fill passes
+
+__global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
+                                                      uint32_t* __restrict__ bits,
+                                                      uint16_t* __restrict__ pre, int N, int topk,
+                                                      int block, int MWB, size_t tokens) {
+  const size_t tok = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= tokens) return;
+  const int t = int(tok % N);
+  const int c = t / block;
+  const int32_t* ir = idx + tok * topk;
+  int carry = 0;
+  for (int w0 = 0; w0 < MWB; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t word = 0;
+    for (int e = 0; e < topk; ++e) {
+      const int m = ir[e];
+      if (m >= 0 && m < c && (m >> 5) == w) word |= 1u << (m & 31);
+    }
+    if (w < MWB) bits[tok * MWB + w] = word;
+    const int cnt = __popc(word);
+    int incl = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (w < MWB) pre[tok * (MWB + 1) + w] = uint16_t(carry + incl - cnt);
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) pre[tok * (MWB + 1) + MWB] = uint16_t(carry);
+}
+
+// One wave per (KV head, word, segment).  FILL = false: counts; true: entries.
+template <bool FILL>
+__global__ __launch_bounds__(64) void sel_pass_kernel(SelLists L, int N, int C, int block) {
+  const int lane = threadIdx.x;
+  const int seg = blockIdx.x % L.nseg;
+  const int w = (blockIdx.x / L.nseg) % L.MWB;
+  const int pair = blockIdx.x / (L.nseg * L.MWB);
+  const int MWB = L.MWB;
+  // tokens that can select a block of word w start at block 32 w + 1
+  const int t0 = max(seg * SEG, (32 * w + 1) * block);
+  const int t1 = min(N, (seg + 1) * SEG);
+  const size_t tok0 = size_t(pair) * N;
+  const size_t cell = (size_t(pair) * L.NB + 32 * w) * L.nseg + seg;  // (pair, m = 32 w, seg)
+  // running position per block b of the word: lane b holds it
+  uint32_t run = 0;
+  if (FILL && lane < 32 && 32 * w + lane < C) run = L.segoff[cell + size_t(lane) * L.nseg];
+  uint32_t* ents = L.ents + size_t(pair) * L.ents_per_pair;
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int tb = t0; tb < t1; tb += 64) {
+    const int t = tb + lane;
+    const bool ok = t < t1;
+    const uint32_t word = ok ? L.bits[(tok0 + t) * MWB + w] : 0u;
+    const int base = (FILL && ok) ? int(L.pre[(tok0 + t) * (MWB + 1) + w]) : 0;
+#pragma unroll 4
+    for (int b = 0; b < 32; ++b) {
+      const bool sel = (word >> b) & 1u;
+      const unsigned long long bal = __ballot(sel);
+      if (bal == 0ull) continue;
+      const uint32_t rb = __shfl(run, b, 64);
+      if (FILL && sel) {
+        const uint32_t slot = uint32_t(base + __popc(word & ((1u << b) - 1u)));
+        ents[rb + __popcll(bal & lt)] = uint32_t(t) | (slot << 23);
+      }
+      if (lane == b) run = rb + uint32_t(__popcll(bal));
+    }
+  }
+  if (!FILL && lane < 32 && 32 * w + lane < C) L.cnt[cell + size_t(lane) * L.nseg] = run;
+}
+
+// Workgroup-wide exclusive scan of one value per thread (1024 threads).
+__device__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t x = lane < 16 ? sh[lane] : 0u;
+    uint32_t xi = x;
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint32_t y = __shfl_up(xi, off, 64);
+      if (lane >= off) xi += y;
+    }
+    if (lane < 16) sh[16 + lane] = xi - x;
+    if (lane == 15) sh[32] = xi;
+  }
+  __syncthreads();
+  const uint32_t r = sh[16 + wave] + incl - v;
+  *total = sh[32];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per KV head: block offsets, segment offsets and work items.
+__global__ __launch_bounds__(1024) void sel_scan_kernel(SelLists L, int N, int C, int block) {
+  __shared__ uint32_t sh[40];
+  const int pair = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int NB = L.NB, nseg = L.nseg;
+  uint32_t ecarry = 0, icarry = 0;
+  for (int m0 = 0; m0 < NB; m0 += 1024) {
+    const int m = m0 + tid;
+    uint32_t cm = 0, items = 0;
+    if (m < NB) {
+      if (m < C)
+        for (int sg = 0; sg < nseg; ++sg) cm += L.cnt[(size_t(pair) * NB + m) * nseg + sg];
+      const int own = min(block, N - m * block);
+      items = (uint32_t(own) + cm + L.chunk - 1) / L.chunk;
+    }
+    uint32_t etot, itot;
+    const uint32_t eoff = ecarry + block_scan_excl(cm, sh, &etot);
+    const uint32_t ioff = icarry + block_scan_excl(items, sh, &itot);
+    if (m < NB) {
+      L.blkoff[size_t(pair) * (NB + 1) + m] = eoff;
+      uint32_t run = eoff;
+      if (m < C)
+        for (int sg = 0; sg < nseg; ++sg) {
+          const size_t cell = (size_t(pair) * NB + m) * nseg + sg;
+          const uint32_t c = L.cnt[cell];
+          L.segoff[cell] = run;
+          run += c;
+        }
+      uint32_t* it = L.items + size_t(pair) * L.maxitems + ioff;
+      for (uint32_t i = 0; i < items; ++i) it[i] = uint32_t(m) | (i << 16);
+    }
+    ecarry += etot;
+    icarry += itot;
+  }
+  if (tid == 0) {
+    L.blkoff[size_t(pair) * (NB + 1) + NB] = ecarry;
+    L.nitems[pair] = icarry;
+  }
+}
+
+}  // namespace
+
+SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int chunk, char* base,
+                          size_t* bytes) {
+  SelLists L{};
+  const size_t pairs = size_t(B) * Hkv, tokens = pairs * N;
+  L.MWB = C > 0 ? (C + 31) / 32 : 1;
+  L.NB = (N + block - 1) / block;
+  L.nseg = (N + SEG - 1) / SEG;
+  L.chunk = chunk;
+  L.ents_per_pair = size_t(N) * topk;
+  L.maxitems = L.NB + int((size_t(N) * (topk + 1) + chunk - 1) / chunk);
+  size_t at = 0;
+  auto take = [&](size_t n) {
+    const size_t o = at;
+    at += align_up(n);
+    return base ? base + o : nullptr;
+  };
+  L.bits = reinterpret_cast<uint32_t*>(take(tokens * L.MWB * 4));
+  L.pre = reinterpret_cast<uint16_t*>(take(tokens * (L.MWB + 1) * 2));
+  L.cnt = reinterpret_cast<uint32_t*>(take(pairs * L.NB * L.nseg * 4));
+  L.segoff = reinterpret_cast<uint32_t*>(take(pairs * L.NB * L.nseg * 4));
+  L.blkoff = reinterpret_cast<uint32_t*>(take(pairs * (L.NB + 1) * 4));
+  L.nitems = reinterpret_cast<uint32_t*>(take(pairs * 4));
+  L.items = reinterpret_cast<uint32_t*>(take(pairs * L.maxitems * 4));
+  L.ents = reinterpret_cast<uint32_t*>(take(pairs * L.ents_per_pair * 4));
+  if (bytes) *bytes = at;
+  return L;
+}
+
+hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
+                            int topk, int block, hipStream_t s) {
+  const size_t tokens = size_t(B) * Hkv * N;
+  const int pairs = B * Hkv;
+  SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, idx, L.bits, L.pre, N,
+             topk, block, L.MWB, tokens);
+  if (C > 0) {
+    SAS_LAUNCH("sel_count", sel_pass_kernel<false>, dim3(pairs * L.MWB * L.nseg), dim3(64), 0, s, L, N, C,
+               block);
+  }
+  SAS_LAUNCH("sel_scan", sel_scan_kernel, dim3(pairs), dim3(1024), 0, s, L, N, C, block);
+  if (C > 0) {
+    SAS_LAUNCH("sel_fill", sel_pass_kernel<true>, dim3(pairs * L.MWB * L.nseg), dim3(64), 0, s, L, N, C,
+               block);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sas
