@@ -26,6 +26,7 @@
 #include "mfma.h"
 #include "tiles.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace sas {
@@ -394,19 +395,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------- dQ, sparse scope ----
-// Key-major over the selection lists.  A workgroup takes one work item: a run
-// of at most L.chunk tokens of block m's sequence (its own tokens, then the
-// tokens whose Top-K holds m, ascending), i.e. chunk x G query rows.  Each wave
-// owns 16 of those rows per step and all 64 keys (lane = row, S^T = K Q^T with
-// K read from the block's LDS tile, dP^T = V dO^T with V held in registers),
-// so dS^T never leaves the
-// wave: its C fragments are the B operand of dQ^T = K^T dS^T, with the keys of
-// a 32-wide k step in the order {4 lq + i, 16 + 4 lq + i}, and K^T comes from
-// the block's K tile through transposing LDS reads in the same order.  Per
-// row the block contributes dbeta = sum of dS over its keys (gated rows) and
-// a dQ share, both written to the row's slot: the rank of m among the row's
-// selected blocks (topk for the own block's dQ share).  Waves run independent two-stage pipelines on private LDS stages:
-// no workgroup barrier after the prologue, and a fixed count of stores per
+// Key-major over the selection lists.  Persistent workgroups walk the work
+// items (a block's own tokens, or a run of list entries within one token
+// span; items of a span run together, so their query rows are shared in
+// cache).  For an item of block m each wave owns 16 of its rows per step and
+// all 64 keys (lane = row, S^T = K Q^T with K read from the block's LDS tile,
+// dP^T = V dO^T with V held in registers), so dS^T never leaves the wave: its
+// C fragments are the B operand of dQ^T = K^T dS^T, with the keys of a 32-wide
+// k step in the order {4 lq + i, 16 + 4 lq + i}, and K^T comes from the K tile
+// through transposing LDS reads in the same order.  Per row the block
+// contributes dbeta = sum of dS over its keys (gated rows) and a dQ share,
+// both written to the row's slot: the rank of m among the row's selected
+// blocks (topk for the own block's dQ share).  Waves run independent
+// two-stage pipelines on private LDS stages, with a fixed count of stores per
 // step so the wait for the next stage's loads does not wait for them.
 template <int D, int G>
 __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) {
@@ -414,237 +415,242 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
   constexpr int WAVES = 8;
   constexpr int KS = D / 32;
   constexpr int ND = D / 16;
-  constexpr int CH = D / 8;
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;           // rows per wave-wide 16-byte access
   constexpr int STG = 2 * 16 * D;        // per wave stage: Q | dO of 16 rows
-  constexpr int NLD = 16 * CH / 64;      // wave DMA instructions per operand
+  constexpr int NLD = 16 / RPL;          // wave DMA instructions per operand
   constexpr int NSTORE = NLD + 1;        // stores per step: dQ share rows + dbeta
   static_assert(KT * D <= WAVES * STG, "V tile fits in the stage area");
+  static_assert(16 % G == 0, "a 16-row group holds whole tokens");
   __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t S0[WAVES * STG];
   __shared__ __attribute__((aligned(16))) uint16_t S1[WAVES * STG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pairs = a.n_pairs;
-  const int pair = blockIdx.x % pairs, item = blockIdx.x / pairs;
-  if (item >= int(L.nitems[pair])) return;
-  const uint32_t iv = L.items[size_t(pair) * L.maxitems + item];
-  const int m = int(iv & 0xffffu), run = int(iv >> 16);
-  const int b = pair / a.Hkv, g = pair % a.Hkv;
-  const int N = a.N, C = a.C;
-  const int j0 = m * KT;
-  const int own_n = min(KT, N - j0);
-  const uint32_t* bo = L.blkoff + size_t(pair) * (L.NB + 1) + m;
-  const uint32_t* ents = L.ents + size_t(pair) * L.ents_per_pair + bo[0];
-  const int len = own_n + int(bo[1] - bo[0]);
-  const int p0 = run * L.chunk, p1 = min(len, p0 + L.chunk);
-  const int nrows = (p1 - p0) * G;
-  const int ngroups = (nrows + 15) >> 4;
-  const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
-  const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
-  const float c1 = a.scale * kLog2e;
+  const int N = a.N, C = a.C, pairs = a.n_pairs;
   const int topk1 = a.topk + 1;
-
-  // ---- prologue: K tile (kept) and V tile (over stage 0) into LDS, then the
-  // A operands of S^T and dP^T into registers.
-  {
-    const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-    const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-    constexpr int KPIECE = KT * D * 2 / 1024;
-    for (int j = wave; j < KPIECE; j += WAVES) {
-      const int sl = 64 * j + lane;
-      const int r = sl / CH, pc = sl % CH;
-      const size_t key = size_t(min(j0 + r, N - 1));
-      const int c = (pc ^ k_swz<D>(r)) * 8;
-      dma16_to_lds(kh + key * D + c, Ksh + j * 512);
-      dma16_to_lds(vh + key * D + c, S0 + j * 512);
-    }
-  }
-  wait_vm<0>();
-  __syncthreads();
-  uint4 vf[4][KS];
-  {
-    const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int r = 16 * kt + lr;
-        vf[kt][ks] = *reinterpret_cast<const uint4*>(S0 + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
-      }
-  }
-  __syncthreads();  // the V tile is read before stage 0 is reloaded
-  if (nk == 0) return;
-
-  // entry of a row of group gk: token | slot << 23 (own block: slot topk);
-  // rows past the item read a valid address and are masked by q < nrows.
-  auto entry = [&](int gk, int r) -> uint32_t {
-    const int q = 16 * gk + r;
-    const int p = p0 + q / G;
-    const bool hist = q < nrows && p >= own_n;
-    const uint32_t e = *(hist ? ents + (p - own_n) : L.ents);
-    return hist ? e : (uint32_t(j0 + min(p, own_n - 1)) | (uint32_t(a.topk) << 23));
-  };
-  auto grow_of = [&](int gk, int r, uint32_t e) -> size_t {
-    const int q = 16 * gk + r;
-    const int t = q < nrows ? int(e & 0x7fffffu) : 0;
-    return hrow0 + size_t(q % G) * N + t;
-  };
-  auto stg = [&](auto tag) -> uint16_t* {
-    if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;
-    else return S1 + wave * STG;
-  };
-  // Q and dO rows of group gk into a stage; row r's entry comes from lane r.
-  auto issue = [&](auto tag, int gk, uint32_t e, int ln) {
-    uint16_t* st = stg(tag);
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int sl = 64 * j + ln;
-      const int r = sl / CH, pc = sl % CH;
-      const uint32_t er = uint32_t(__shfl(int(e), r, 64));
-      const size_t gr = grow_of(gk, r, er);
-      const int c = (pc ^ k_swz<D>(r)) * 8;
-      dma16_to_lds(a.q + gr * D + c, st + j * 512);
-      dma16_to_lds(a.dout + gr * D + c, st + 16 * D + j * 512);
-    }
-  };
-  struct Stat {
-    float4 rs;
-    float sc;
-  };
-  auto load_stat = [&](int gk, uint32_t e, int lr) -> Stat {
-    const size_t gr = grow_of(gk, lr, e);
-    Stat s;
-    s.rs = reinterpret_cast<const float4*>(a.rowstat)[gr];
-    s.sc = a.scores[gr * C + (int(e & 0x7fffffu) >= j0 + KT ? m : 0)];
-    return s;
-  };
-
-  auto compute = [&](auto tag, int gk, uint32_t e, const Stat& stt, int ln) {
-    const uint16_t* Qs = stg(tag);
-    const uint16_t* dOs = Qs + 16 * D;
-    const int lr = ln & 15, lq = ln >> 4;
-    const int qsw = k_swz<D>(lr);
-    f32x4 sacc[4], pacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = lr * D + (((4 * ks + lq) ^ qsw) * 8);
-      const uint4 qb = *reinterpret_cast<const uint4*>(Qs + off);
-      const uint4 ob = *reinterpret_cast<const uint4*>(dOs + off);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int r = 16 * kt + lr;
-        const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
-        sacc[kt] = mfma16(ka, qb, sacc[kt]);
-        pacc[kt] = mfma16(vf[kt][ks], ob, pacc[kt]);
-      }
-    }
-    const int q = 16 * gk + lr;
-    const bool valid = q < nrows;
-    const int t = int(e & 0x7fffffu);
-    const bool own = t < j0 + KT;
-    const float off = own ? stt.rs.y : fmaf(stt.sc, kLog2e, stt.rs.z);
-    const float dl = stt.rs.x;
-    float db = 0.f;
-    uint4 dsb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float d[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kt = 2 * kk + h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 16 * kt + 4 * lq + i;
-          const bool ok = valid && (!own || key <= t);
-          const float p = exp2_hw(ok ? fmaf(sacc[kt][i], c1, off) : kNegInf);
-          const float x = p * (pacc[kt][i] - dl);
-          db += x;
-          d[4 * h + i] = x;
-        }
-      }
-      dsb[kk] = make_uint4(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]), pack_bf16(d[4], d[5]),
-                           pack_bf16(d[6], d[7]));
-    }
-    db += shfl_xor(db, 16);
-    db += shfl_xor(db, 32);
-    f32x4 dqa[ND];
-#pragma unroll
-    for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
-      const int swa = k_swz<D>(ka), swb = k_swz<D>(kb);
-#pragma unroll
-      for (int md = 0; md < ND; ++md) {
-        const int col = 16 * md + 4 * (lr & 3);
-        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ swa) << 3) + (col & 7)));
-        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ swb) << 3) + (col & 7)));
-        dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb[kk], dqa[md]);
-      }
-    }
-    // dQ^T fragments to the wave's stage (Q area, already consumed) as rows,
-    // chunk c of row r at c ^ (r % CH), then whole rows out: every store
-    // writes full lines.  Rows past the item go to the dummy line, and so does
-    // dbeta of own rows, so each step issues the same count of stores.
-    uint16_t* W = const_cast<uint16_t*>(Qs);
-#pragma unroll
-    for (int md = 0; md < ND; ++md) {
-      uint2 w;
-      w.x = pack_bf16(dqa[md][0], dqa[md][1]);
-      w.y = pack_bf16(dqa[md][2], dqa[md][3]);
-      const int c = (2 * md + (lq >> 1)) ^ (lr % CH);
-      *reinterpret_cast<uint2*>(W + lr * D + c * 8 + 4 * (lq & 1)) = w;
-    }
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int sl = 64 * j + ln;
-      const int r = sl / CH, cc = sl % CH;
-      const uint32_t er = uint32_t(__shfl(int(e), r, 64));
-      const bool vr = 16 * gk + r < nrows;
-      const uint4 v = *reinterpret_cast<const uint4*>(W + r * D + ((cc ^ (r % CH)) * 8));
-      bf16_t* dp = vr ? a.dqp + (grow_of(gk, r, er) * topk1 + (er >> 23)) * D + cc * 8
-                      : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
-      *reinterpret_cast<uint4*>(dp) = v;
-    }
-    const size_t gr = grow_of(gk, lr, e);
-    float* dbp = (valid && !own) ? a.dbeta + gr * a.topk + (e >> 23) : a.dummy + 64;
-    *dbp = db;
-  };
-
+  const float c1 = a.scale * kLog2e;
+  const int total = pairs * L.maxitems;
   using S0t = std::integral_constant<int, 0>;
   using S1t = std::integral_constant<int, 1>;
-  // pipeline: group k = wave + WAVES k of this wave
-  uint32_t e0 = entry(wave, lane & 15);
-  uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
-  issue(S0t{}, wave, e0, lane);
-  Stat st0 = load_stat(wave, e0, lane & 15), st1;
-  wait_vm<0>();
-  auto step = [&](auto tag, int k) {
-    using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int gk = wave + WAVES * k;
-    uint32_t e2 = 0;
-    if (k + 1 < nk) {
-      issue(Pn{}, gk + WAVES, e1, ln);
-      st1 = load_stat(gk + WAVES, e1, ln & 15);
-      if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
+
+  for (int vi = blockIdx.x; vi < total; vi += gridDim.x) {
+    const int pair = vi % pairs, item = vi / pairs;
+    if (item >= int(L.nitems[pair])) continue;
+    const uint4 it = reinterpret_cast<const uint4*>(L.items)[size_t(pair) * L.maxitems + item];
+    const int m = int(it.x & 0xffffu);
+    const bool own_item = (it.x >> 31) != 0;
+    const int b = pair / a.Hkv, g = pair % a.Hkv;
+    const int j0 = m * KT;
+    const int ntok = own_item ? min(KT, N - j0) : int(it.z - it.y);
+    const uint32_t* ep = L.ents + size_t(pair) * L.ents_per_pair + it.y;
+    const int nrows = ntok * G;
+    const int ngroups = (nrows + 15) >> 4;
+    const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
+    const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
+
+    // ---- K tile (kept) and V tile (over stage 0) into LDS, then the V
+    // operands of dP^T into registers.
+    __syncthreads();  // the previous item is done with the K tile and stages
+    {
+      const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+      const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+      constexpr int KPIECE = KT * D * 2 / 1024;
+      for (int j = wave; j < KPIECE; j += WAVES) {
+        const int r = RPL * j + lane / CH, pc = lane % CH;
+        const size_t key = size_t(min(j0 + r, N - 1));
+        const int c = (pc ^ k_swz<D>(r)) * 8;
+        dma16_to_lds(kh + key * D + c, Ksh + j * 512);
+        dma16_to_lds(vh + key * D + c, S0 + j * 512);
+      }
     }
-    compute(tag, gk, e0, st0, ln);
-    wait_vm<NSTORE>();
-    e0 = e1;
-    e1 = e2;
-    st0 = st1;
-  };
-  for (int k = 0; k < nk; k += 2) {
-    step(S0t{}, k);
-    if (k + 1 < nk) step(S1t{}, k + 1);
+    wait_vm<0>();
+    __syncthreads();
+    uint4 vf[4][KS];
+    {
+      const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int r = 16 * kt + lr;
+          vf[kt][ks] = *reinterpret_cast<const uint4*>(S0 + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
+        }
+    }
+    __syncthreads();  // the V tile is read before stage 0 is reloaded
+    if (nk == 0) continue;
+
+    // Lane constants of the item.  Row r_j = RPL j + lane / CH of a group is
+    // loaded and stored by this lane at chunk lane % CH; the head of a row is
+    // r % G, so everything but the token is fixed per item.
+    size_t qoff[NLD], soff[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int r = RPL * j + lane / CH, pc = lane % CH;
+      const size_t hr = hrow0 + size_t(r % G) * N;
+      qoff[j] = hr * D + ((pc ^ k_swz<D>(r)) * 8);
+      soff[j] = hr * size_t(topk1) * D + pc * 8;
+    }
+    const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
+
+    // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
+    auto entry = [&](int gk, int lr) -> uint32_t {
+      const int p = min((16 * gk + lr) / G, ntok - 1);
+      if (own_item) return uint32_t(j0 + p) | (uint32_t(a.topk) << 23);
+      return ep[p];
+    };
+    auto stg = [&](auto tag) -> uint16_t* {
+      if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;
+      else return S1 + wave * STG;
+    };
+    auto issue = [&](auto tag, int gk, uint32_t e, int ln) {
+      uint16_t* st = stg(tag);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int r = RPL * j + ln / CH;
+        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+        const uint32_t t = 16 * gk + r < nrows ? (er & 0x7fffffu) : 0u;
+        const size_t off = qoff[j] + size_t(t) * D;
+        dma16_to_lds(a.q + off, st + j * 512);
+        dma16_to_lds(a.dout + off, st + 16 * D + j * 512);
+      }
+    };
+    struct Stat {
+      float4 rs;
+      float sc;
+    };
+    auto load_stat = [&](uint32_t e) -> Stat {
+      const size_t gr = rbase + (e & 0x7fffffu);
+      Stat s;
+      s.rs = reinterpret_cast<const float4*>(a.rowstat)[gr];
+      s.sc = own_item ? 0.f : a.scores[gr * C + m];
+      return s;
+    };
+
+    auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, const Stat& stt, int ln) {
+      constexpr bool MASK = decltype(maskt)::value;
+      const uint16_t* Qs = stg(tag);
+      const uint16_t* dOs = Qs + 16 * D;
+      const int lr = ln & 15, lq = ln >> 4;
+      const int qsw = k_swz<D>(lr);
+      f32x4 sacc[4], pacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = lr * D + (((4 * ks + lq) ^ qsw) * 8);
+        const uint4 qb = *reinterpret_cast<const uint4*>(Qs + off);
+        const uint4 ob = *reinterpret_cast<const uint4*>(dOs + off);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int r = 16 * kt + lr;
+          const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
+          sacc[kt] = mfma16(ka, qb, sacc[kt]);
+          pacc[kt] = mfma16(vf[kt][ks], ob, pacc[kt]);
+        }
+      }
+      const bool valid = 16 * gk + lr < nrows;
+      const int t = int(e & 0x7fffffu);
+      // keys a row may see: all (gated block), key <= t (own block), none
+      // (rows past the item)
+      const int tlim = valid ? (own_item ? t : 0x7fffffff) : -1;
+      const float off = own_item ? stt.rs.y : fmaf(stt.sc, kLog2e, stt.rs.z);
+      const float dl = stt.rs.x;
+      float db = 0.f;
+      uint4 dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float d[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kt = 2 * kk + h;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = fmaf(sacc[kt][i], c1, off);
+            if (MASK) x = j0 + 16 * kt + 4 * lq + i <= tlim ? x : kNegInf;
+            const float y = exp2_hw(x) * (pacc[kt][i] - dl);
+            db += y;
+            d[4 * h + i] = y;
+          }
+        }
+        dsb[kk] = make_uint4(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]), pack_bf16(d[4], d[5]),
+                             pack_bf16(d[6], d[7]));
+      }
+      db += shfl_xor(db, 16);
+      db += shfl_xor(db, 32);
+      f32x4 dqa[ND];
+#pragma unroll
+      for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
+        const int swa = k_swz<D>(ka), swb = k_swz<D>(kb);
+#pragma unroll
+        for (int md = 0; md < ND; ++md) {
+          const int col = 16 * md + 4 * (lr & 3);
+          const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ swa) << 3) + (col & 7)));
+          const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ swb) << 3) + (col & 7)));
+          dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb[kk], dqa[md]);
+        }
+      }
+      // dQ^T fragments to the wave's stage (Q area, already consumed) as rows,
+      // chunk c of row r at c ^ (r % CH), then whole rows out: every store
+      // writes full lines.  Rows past the item go to the dummy line, and so
+      // does dbeta of own rows, so each step issues the same count of stores.
+      uint16_t* W = stg(tag);
+#pragma unroll
+      for (int md = 0; md < ND; ++md) {
+        uint2 w;
+        w.x = pack_bf16(dqa[md][0], dqa[md][1]);
+        w.y = pack_bf16(dqa[md][2], dqa[md][3]);
+        const int c = (2 * md + (lq >> 1)) ^ (lr % CH);
+        *reinterpret_cast<uint2*>(W + lr * D + c * 8 + 4 * (lq & 1)) = w;
+      }
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int r = RPL * j + ln / CH, cc = ln % CH;
+        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+        const uint4 v = *reinterpret_cast<const uint4*>(W + r * D + ((cc ^ (r % CH)) * 8));
+        bf16_t* dp = 16 * gk + r < nrows
+                         ? a.dqp + soff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
+                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+        *reinterpret_cast<uint4*>(dp) = v;
+      }
+      float* dbp = (valid && !own_item) ? a.dbeta + (rbase + t) * a.topk + (e >> 23) : a.dummy + 64;
+      *dbp = db;
+    };
+
+    // pipeline over this wave's groups gk = wave + WAVES k
+    uint32_t e0 = entry(wave, lane & 15);
+    uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
+    issue(S0t{}, wave, e0, lane);
+    Stat st0 = load_stat(e0), st1 = st0;
+    wait_vm<0>();
+    auto step = [&](auto tag, int k) {
+      using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int gk = wave + WAVES * k;
+      uint32_t e2 = 0;
+      if (k + 1 < nk) {
+        issue(Pn{}, gk + WAVES, e1, ln);
+        st1 = load_stat(e1);
+        if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
+      }
+      compute(tag, std::true_type{}, gk, e0, st0, ln);
+      wait_vm<NSTORE>();
+      e0 = e1;
+      e1 = e2;
+      st0 = st1;
+    };
+    for (int k = 0; k < nk; k += 2) {
+      step(S0t{}, k);
+      if (k + 1 < nk) step(S1t{}, k + 1);
+    }
   }
 }
 
@@ -1162,7 +1168,9 @@ size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 template <int D, int G>
 static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStream_t s) {
-  SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(a.n_pairs * L.maxitems), dim3(512), 0, s, a, L);
+  // persistent: one workgroup per compute unit (the LDS stages fill it)
+  const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
+  SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(grid), dim3(512), 0, s, a, L);
   constexpr int RPB = 256 / (D / 8);
   SAS_LAUNCH("dq_reduce", (dq_reduce_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a.dqp,
              a.selpre, a.dq, a.Hq, G, a.N, a.topk, a.MWB, a.scale, rows);

@@ -33,6 +33,15 @@ struct Dims {
   int G() const { return Hq / Hkv; }
 };
 
+// Compute units of the current device (persistent-grid sizing).
+inline int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 // Device workspace carving: 256-byte aligned slices.
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -60,7 +69,7 @@ struct SelLists {
   uint32_t* segoff;  // [pairs][NB][nseg] list offset of (block, segment)
   uint32_t* blkoff;  // [pairs][NB + 1] list offset of each block; [NB] = total
   uint32_t* nitems;  // [pairs] work items
-  uint32_t* items;   // [pairs][maxitems] block | (run index << 16)
+  uint32_t* items;   // [pairs][maxitems][4] {block | own << 31, first entry, end entry, 0}
   uint32_t* ents;    // [pairs][ents_per_pair] token | (slot << 23)
   int MWB, NB, nseg, chunk, maxitems;
   size_t ents_per_pair;

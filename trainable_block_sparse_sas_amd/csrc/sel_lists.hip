@@ -10,18 +10,22 @@
 //          select each of the word's 32 blocks.
 //   scan   per KV head: exclusive offsets over (block, segment), so each
 //          block's list is its segments' tokens in ascending order, and the work
-//          items: runs of at most CHUNK tokens over a block's virtual sequence
-//          (its own tokens, then its list).
+//          items in (token span, block) order: a block's own tokens, or a run of
+//          at most `chunk` list entries whose tokens fall in one span of
+//          ISEG segments (items that run together then share query rows).
 //   fill   the lists, entry = token | (rank of the block among the token's
 //          selected blocks) << 23.
 // Every step is deterministic: the lists come out sorted by token.
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace sas {
 namespace {
 
-constexpr int SEG = 2048;  // tokens per segment of the count / fill passes
+constexpr int SEG = 2048;          // tokens per segment of the count / fill passes
+constexpr int kSegsPerSpan = 2;    // segments per token span of the work items
 
 __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
                                                       uint32_t* __restrict__ bits,
@@ -121,24 +125,20 @@ __device__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t* total) {
 }
 
 // One workgroup per KV head: block offsets, segment offsets and work items.
+// Item = {m | own << 31, first entry, end entry, 0} (entries pair-relative).
 __global__ __launch_bounds__(1024) void sel_scan_kernel(SelLists L, int N, int C, int block) {
   __shared__ uint32_t sh[40];
   const int pair = blockIdx.x;
   const int tid = threadIdx.x;
   const int NB = L.NB, nseg = L.nseg;
-  uint32_t ecarry = 0, icarry = 0;
+  uint32_t ecarry = 0;
   for (int m0 = 0; m0 < NB; m0 += 1024) {
     const int m = m0 + tid;
-    uint32_t cm = 0, items = 0;
-    if (m < NB) {
-      if (m < C)
-        for (int sg = 0; sg < nseg; ++sg) cm += L.cnt[(size_t(pair) * NB + m) * nseg + sg];
-      const int own = min(block, N - m * block);
-      items = (uint32_t(own) + cm + L.chunk - 1) / L.chunk;
-    }
-    uint32_t etot, itot;
+    uint32_t cm = 0;
+    if (m < C)
+      for (int sg = 0; sg < nseg; ++sg) cm += L.cnt[(size_t(pair) * NB + m) * nseg + sg];
+    uint32_t etot;
     const uint32_t eoff = ecarry + block_scan_excl(cm, sh, &etot);
-    const uint32_t ioff = icarry + block_scan_excl(items, sh, &itot);
     if (m < NB) {
       L.blkoff[size_t(pair) * (NB + 1) + m] = eoff;
       uint32_t run = eoff;
@@ -149,16 +149,52 @@ __global__ __launch_bounds__(1024) void sel_scan_kernel(SelLists L, int N, int C
           L.segoff[cell] = run;
           run += c;
         }
-      uint32_t* it = L.items + size_t(pair) * L.maxitems + ioff;
-      for (uint32_t i = 0; i < items; ++i) it[i] = uint32_t(m) | (i << 16);
     }
     ecarry += etot;
+  }
+  if (tid == 0) L.blkoff[size_t(pair) * (NB + 1) + NB] = ecarry;
+  __syncthreads();  // segment offsets visible to the whole workgroup
+  // work items over cells (span, block), span-major
+  const int spi = kSegsPerSpan;
+  const int nspan = (nseg + spi - 1) / spi;
+  const int ncell = nspan * NB;
+  uint32_t icarry = 0;
+  uint32_t* items = L.items + size_t(pair) * L.maxitems * 4;
+  for (int c0 = 0; c0 < ncell; c0 += 1024) {
+    const int cell = c0 + tid;
+    const int sp = cell / NB, m = cell % NB;
+    uint32_t first = 0, cnt = 0, own = 0;
+    if (cell < ncell) {
+      own = (m * block) / (SEG * spi) == sp ? 1u : 0u;
+      if (m < C) {
+        const int s0 = sp * spi, s1 = min(nseg, s0 + spi);
+        const size_t base = (size_t(pair) * NB + m) * nseg;
+        first = L.segoff[base + s0];
+        cnt = (s1 < nseg ? L.segoff[base + s1] : L.blkoff[size_t(pair) * (NB + 1) + m + 1]) - first;
+      }
+    }
+    const uint32_t n = own + (cnt + L.chunk - 1) / L.chunk;
+    uint32_t itot;
+    const uint32_t ioff = icarry + block_scan_excl(n, sh, &itot);
+    if (cell < ncell) {
+      uint32_t* it = items + size_t(ioff) * 4;
+      if (own) {
+        it[0] = uint32_t(m) | 0x80000000u;
+        it[1] = 0;
+        it[2] = 0;
+        it[3] = 0;
+        it += 4;
+      }
+      for (uint32_t e = 0; e < cnt; e += L.chunk, it += 4) {
+        it[0] = uint32_t(m);
+        it[1] = first + e;
+        it[2] = first + min(cnt, e + uint32_t(L.chunk));
+        it[3] = 0;
+      }
+    }
     icarry += itot;
   }
-  if (tid == 0) {
-    L.blkoff[size_t(pair) * (NB + 1) + NB] = ecarry;
-    L.nitems[pair] = icarry;
-  }
+  if (tid == 0) L.nitems[pair] = icarry;
 }
 
 }  // namespace
@@ -172,7 +208,12 @@ SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int
   L.nseg = (N + SEG - 1) / SEG;
   L.chunk = chunk;
   L.ents_per_pair = size_t(N) * topk;
-  L.maxitems = L.NB + int((size_t(N) * (topk + 1) + chunk - 1) / chunk);
+  {
+    // own items + full runs + one partial run per nonempty (span, block) cell
+    const size_t nspan = (L.nseg + kSegsPerSpan - 1) / kSegsPerSpan;
+    const size_t ents = size_t(N) * topk;
+    L.maxitems = int(L.NB + ents / chunk + std::min(ents, nspan * L.NB) + 1);
+  }
   size_t at = 0;
   auto take = [&](size_t n) {
     const size_t o = at;
@@ -185,7 +226,7 @@ SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int
   L.segoff = reinterpret_cast<uint32_t*>(take(pairs * L.NB * L.nseg * 4));
   L.blkoff = reinterpret_cast<uint32_t*>(take(pairs * (L.NB + 1) * 4));
   L.nitems = reinterpret_cast<uint32_t*>(take(pairs * 4));
-  L.items = reinterpret_cast<uint32_t*>(take(pairs * L.maxitems * 4));
+  L.items = reinterpret_cast<uint32_t*>(take(pairs * L.maxitems * 16));
   L.ents = reinterpret_cast<uint32_t*>(take(pairs * L.ents_per_pair * 4));
   if (bytes) *bytes = at;
   return L;
