@@ -654,52 +654,21 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
   }
 }
 
-// dq = scale * (sum of a row's partial slots): its selected blocks' slots
-// 0 .. nsel-1 and the own block's slot topk.  One thread per 8 columns.
+// Per sparse-scope row, one wave:
+//   dq = scale * (sum of the row's dQ share slots: its selected blocks' slots
+//        0 .. nsel-1 and the own block's slot topk), and
+//   ds[m] = (m selected ? dbeta[slot(m)] : 0) - g[m] * sum(dbeta) for the
+//        history blocks m < c, g = exp(s - LSE_s); 0 from the own block on
+//        (slot(m) = rank of m among the row's selected blocks).
+// Each lane takes 2 dq columns and 8 consecutive blocks per pass.
 template <int D>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const bf16_t* __restrict__ dqp,
-                                                        const uint16_t* __restrict__ selpre,
-                                                        bf16_t* __restrict__ dq, int Hq, int G, int N,
-                                                        int topk, int MWB, float scale, size_t rows) {
-  constexpr int TPR = D / 8;
-  const size_t row = size_t(blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
-  const int c8 = threadIdx.x % TPR;
-  if (row >= rows) return;
-  const int t = int(row % N);
-  const size_t bh = row / N;  // b * Hq + h
-  const size_t tok = (bh / Hq * (Hq / G) + (bh % Hq) / G) * N + t;
-  const int nsel = selpre[tok * (MWB + 1) + MWB];
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const bf16_t* src = dqp + row * size_t(topk + 1) * D + c8 * 8;
-  auto add = [&](int slot) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + size_t(slot) * D);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_lo(w[i]);
-      acc[2 * i + 1] += bf16_hi(w[i]);
-    }
-  };
-  for (int sl = 0; sl < nsel; ++sl) add(sl);
-  add(topk);
-  uint4 o;
-  o.x = pack_bf16(acc[0] * scale, acc[1] * scale);
-  o.y = pack_bf16(acc[2] * scale, acc[3] * scale);
-  o.z = pack_bf16(acc[4] * scale, acc[5] * scale);
-  o.w = pack_bf16(acc[6] * scale, acc[7] * scale);
-  *reinterpret_cast<uint4*>(dq + row * D + c8 * 8) = o;
-}
-
-// ds of a sparse-scope row from its dbeta slots (slot = rank of the block
-// among the row's selected blocks): ds[m] = (m selected ? dbeta[slot(m)] : 0)
-// - g[m] * sum(dbeta) over the history, g = exp(s - LSE_s); 0 from the own
-// block on.  One wave per row.
-__global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict__ scores,
-                                                        const float* __restrict__ lse_s,
-                                                        const uint32_t* __restrict__ selbits,
-                                                        const uint16_t* __restrict__ selpre,
-                                                        const float* __restrict__ dbeta,
-                                                        float* __restrict__ ds, int Hq, int G, int N,
-                                                        int C, int MWB, int topk, size_t rows) {
+__global__ __launch_bounds__(256) void rows_sparse_kernel(
+    const bf16_t* __restrict__ dqp, const float* __restrict__ dbeta, const float* __restrict__ scores,
+    const float* __restrict__ lse_s, const uint32_t* __restrict__ selbits,
+    const uint16_t* __restrict__ selpre, bf16_t* __restrict__ dq, float* __restrict__ ds, int Hq, int G,
+    int N, int C, int MWB, int topk, float scale, size_t rows) {
+  constexpr int LPS = D / 2;       // lanes per slot (2 columns each)
+  constexpr int SG = 64 / LPS;     // slots per pass
   const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -707,8 +676,42 @@ __global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict_
   const size_t bh = row / N;
   const size_t tok = (bh / Hq * (Hq / G) + (bh % Hq) / G) * N + t;
   const int c = min(t / KT, C);
-  const uint32_t* bits = selbits + tok * MWB;
   const int nsel = selpre[tok * (MWB + 1) + MWB];
+  const int topk1 = topk + 1;
+
+  // ---- dq
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(dqp) + row * size_t(topk1) * LPS + lane % LPS;
+    float a0 = 0.f, a1 = 0.f;
+    int s2 = lane / LPS;
+    for (; s2 + 3 * SG < nsel; s2 += 4 * SG) {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = src[size_t(s2 + u * SG) * LPS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 += bf16_lo(w[u]);
+        a1 += bf16_hi(w[u]);
+      }
+    }
+    for (; s2 < nsel; s2 += SG) {
+      const uint32_t w = src[size_t(s2) * LPS];
+      a0 += bf16_lo(w);
+      a1 += bf16_hi(w);
+    }
+    if (lane < LPS) {
+      const uint32_t w = src[size_t(topk) * LPS];
+      a0 += bf16_lo(w);
+      a1 += bf16_hi(w);
+    }
+    if (SG == 2) {
+      a0 += shfl_xor(a0, 32);
+      a1 += shfl_xor(a1, 32);
+    }
+    if (lane < LPS) reinterpret_cast<uint32_t*>(dq)[row * LPS + lane] = pack_bf16(a0 * scale, a1 * scale);
+  }
+
+  // ---- ds
   const float* db = dbeta + row * topk;
   float tot = 0.f;
   for (int s2 = lane; s2 < nsel; s2 += 64) tot += db[s2];
@@ -716,19 +719,53 @@ __global__ __launch_bounds__(256) void ds_sparse_kernel(const float* __restrict_
   const float ls = lse_s[row];
   const float* srow = scores + row * C;
   float* drow = ds + row * C;
-  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const uint32_t* bits = selbits + tok * MWB;
+  const bool vec = (C & 3) == 0;
   int run = 0;
-  for (int m0 = 0; m0 < C; m0 += 64) {
-    const int m2 = m0 + lane;
-    const bool sel = m2 < c && ((bits[m2 >> 5] >> (m2 & 31)) & 1u);
-    const unsigned long long bal = __ballot(sel);
-    float out = 0.f;
-    if (m2 < c) {
-      const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-      out = (sel ? db[run + __popcll(bal & lt)] : 0.f) - gate * tot;
+  for (int m0 = 0; m0 < C; m0 += 512) {
+    const int col0 = m0 + 8 * lane;
+    const uint32_t b8 = col0 < c ? (bits[col0 >> 5] >> (col0 & 31)) & 0xffu : 0u;
+    const int cnt = __popc(b8);
+    int incl = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
     }
-    if (m2 < C) drow[m2] = out;
-    run += __popcll(bal);
+    const int excl = run + incl - cnt;
+    run += __shfl(incl, 63, 64);
+    float out[8];
+    if (col0 < c && vec && col0 + 8 <= C) {
+      const float4 sa = *reinterpret_cast<const float4*>(srow + col0);
+      const float4 sb = *reinterpret_cast<const float4*>(srow + col0 + 4);
+      const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool sel = (b8 >> i) & 1u;
+        const float gate = exp2_hw((sv[i] - ls) * kLog2e);
+        const float dbv = sel ? db[excl + __popc(b8 & ((1u << i) - 1u))] : 0.f;
+        out[i] = col0 + i < c ? dbv - gate * tot : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m2 = col0 + i;
+        float v = 0.f;
+        if (m2 < c) {
+          const bool sel = (b8 >> i) & 1u;
+          const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
+          v = (sel ? db[excl + __popc(b8 & ((1u << i) - 1u))] : 0.f) - gate * tot;
+        }
+        out[i] = v;
+      }
+    }
+    if (vec && col0 + 8 <= C) {
+      *reinterpret_cast<float4*>(drow + col0) = make_float4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<float4*>(drow + col0 + 4) = make_float4(out[4], out[5], out[6], out[7]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (col0 + i < C) drow[col0 + i] = out[i];
+    }
   }
 }
 
@@ -1171,11 +1208,9 @@ static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStrea
   // persistent: one workgroup per compute unit (the LDS stages fill it)
   const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
   SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(grid), dim3(512), 0, s, a, L);
-  constexpr int RPB = 256 / (D / 8);
-  SAS_LAUNCH("dq_reduce", (dq_reduce_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a.dqp,
-             a.selpre, a.dq, a.Hq, G, a.N, a.topk, a.MWB, a.scale, rows);
-  SAS_LAUNCH("ds_sparse", ds_sparse_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.scores, a.lse_s,
-             a.selbits, a.selpre, a.dbeta, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, rows);
+  SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbeta,
+             a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, a.scale,
+             rows);
 }
 
 template <int D, int G>
