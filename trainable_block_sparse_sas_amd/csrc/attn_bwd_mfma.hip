@@ -52,9 +52,9 @@ struct BwdArgs {
   float* delta;      // workspace [B, Hq, N]
   uint32_t* selbits; // workspace [B, Hkv, N, MWB] (sparse)
   uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
-  bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: partial dQ per selected block (sparse)
+  bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: dQ share per slot (sparse)
+  float* dbl;        // workspace [pairs, list entries, G]: dbeta per list entry and head (sparse)
   const float* rowstat;  // workspace [B, Hq, N] x {Delta, -lse log2e, -(lse + LSE_s) log2e, 0} (sparse)
-  float* dbeta;          // workspace [B, Hq, N, topk]: dbeta per selected block, by slot (sparse)
   float* dummy;          // workspace line that absorbs masked stores
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
@@ -421,8 +421,11 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
   constexpr int NLD = 16 / RPL;          // wave DMA instructions per operand
   constexpr int NSTORE = NLD + 1;        // stores per step: dQ share rows + dbeta
   static_assert(KT * D <= WAVES * STG, "V tile fits in the stage area");
+  constexpr int WST = D + 8;             // row stride (16-bit units) of the dQ staging rows
+  static_assert(16 * WST <= STG, "dQ staging fits in a stage");
   static_assert(16 % G == 0, "a 16-row group holds whole tokens");
-  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];   // K, row-major, swizzled
+  __shared__ __attribute__((aligned(16))) uint4 KTa[2 * ND * 64];  // A operands of dQ^T, per lane
   __shared__ __attribute__((aligned(16))) uint16_t S0[WAVES * STG];
   __shared__ __attribute__((aligned(16))) uint16_t S1[WAVES * STG];
 
@@ -450,9 +453,11 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
     const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
     const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
 
-    // ---- K tile (kept) and V tile (over stage 0) into LDS, then the V
-    // operands of dP^T into registers.
-    __syncthreads();  // the previous item is done with the K tile and stages
+    // ---- K tile (kept) and V tile (over stage 0) into LDS; V operands of
+    // dP^T into registers; the A operands of dQ^T (K^T, keys of k step kk in
+    // the order {4 lq + i, 16 + 4 lq + i}) laid out per lane, so the step reads
+    // them with one 16-byte access each.
+    __syncthreads();  // the previous item is done with the tiles and stages
     {
       const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
       const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
@@ -477,22 +482,31 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
           const int r = 16 * kt + lr;
           vf[kt][ks] = *reinterpret_cast<const uint4*>(S0 + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
         }
+      for (int u = wave; u < 2 * ND; u += WAVES) {
+        const int kk = u / ND, md = u % ND;
+        const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
+        const int col = 16 * md + 4 * (lr & 3);
+        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ k_swz<D>(ka)) << 3) + (col & 7)));
+        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ k_swz<D>(kb)) << 3) + (col & 7)));
+        KTa[u * 64 + lane] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+      }
     }
-    __syncthreads();  // the V tile is read before stage 0 is reloaded
+    __syncthreads();  // V tile read before stage 0 is reloaded; K^T operands written
     if (nk == 0) continue;
 
     // Lane constants of the item.  Row r_j = RPL j + lane / CH of a group is
     // loaded and stored by this lane at chunk lane % CH; the head of a row is
     // r % G, so everything but the token is fixed per item.
-    size_t qoff[NLD], soff[NLD];
+    size_t qoff[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int r = RPL * j + lane / CH, pc = lane % CH;
-      const size_t hr = hrow0 + size_t(r % G) * N;
-      qoff[j] = hr * D + ((pc ^ k_swz<D>(r)) * 8);
-      soff[j] = hr * size_t(topk1) * D + pc * 8;
+      qoff[j] = (hrow0 + size_t(r % G) * N) * D + ((pc ^ k_swz<D>(r)) * 8);
     }
     const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
+    // dbeta records of the item's list entries: [entry][head], so row q of the
+    // item (entry q / G, head q % G) is float q
+    float* dbl_item = a.dbl + (size_t(pair) * L.ents_per_pair + it.y) * G;
 
     // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
     auto entry = [&](int gk, int lr) -> uint32_t {
@@ -528,12 +542,11 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
       return s;
     };
 
-    auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, const Stat& stt, int ln) {
-      constexpr bool MASK = decltype(maskt)::value;
+    auto compute = [&](auto tag, int gk, uint32_t e, const Stat& stt, int ln) {
       const uint16_t* Qs = stg(tag);
       const uint16_t* dOs = Qs + 16 * D;
       const int lr = ln & 15, lq = ln >> 4;
-      const int qsw = k_swz<D>(lr);
+      const int qsw = k_swz<D>(lr);  // = k_swz(16 kt + lr) for every kt
       f32x4 sacc[4], pacc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -547,8 +560,7 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
         const uint4 ob = *reinterpret_cast<const uint4*>(dOs + off);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const int r = 16 * kt + lr;
-          const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
+          const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + 16 * kt * D + off);
           sacc[kt] = mfma16(ka, qb, sacc[kt]);
           pacc[kt] = mfma16(vf[kt][ks], ob, pacc[kt]);
         }
@@ -570,8 +582,7 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
           const int kt = 2 * kk + h;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = fmaf(sacc[kt][i], c1, off);
-            if (MASK) x = j0 + 16 * kt + 4 * lq + i <= tlim ? x : kNegInf;
+            const float x = j0 + 16 * kt + 4 * lq + i <= tlim ? fmaf(sacc[kt][i], c1, off) : kNegInf;
             const float y = exp2_hw(x) * (pacc[kt][i] - dl);
             db += y;
             d[4 * h + i] = y;
@@ -586,41 +597,33 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
 #pragma unroll
       for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
-        const int swa = k_swz<D>(ka), swb = k_swz<D>(kb);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int md = 0; md < ND; ++md) {
-          const int col = 16 * md + 4 * (lr & 3);
-          const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ swa) << 3) + (col & 7)));
-          const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ swb) << 3) + (col & 7)));
-          dqa[md] = mfma16(make_uint4(k0.x, k0.y, k1.x, k1.y), dsb[kk], dqa[md]);
-        }
-      }
-      // dQ^T fragments to the wave's stage (Q area, already consumed) as rows,
-      // chunk c of row r at c ^ (r % CH), then whole rows out: every store
-      // writes full lines.  Rows past the item go to the dummy line, and so
-      // does dbeta of own rows, so each step issues the same count of stores.
+        for (int md = 0; md < ND; ++md) dqa[md] = mfma16(KTa[(kk * ND + md) * 64 + ln], dsb[kk], dqa[md]);
+      // dQ^T fragments to the wave's stage (Q and dO consumed) as rows of
+      // stride WST, then whole rows out, so every store writes full lines.
+      // dbeta goes to the list entry's record (16 consecutive floats per step).
+      // Rows past the item, and dbeta of own rows, go to the dummy line: each
+      // step issues the same count of stores.
       uint16_t* W = stg(tag);
 #pragma unroll
       for (int md = 0; md < ND; ++md) {
         uint2 w;
         w.x = pack_bf16(dqa[md][0], dqa[md][1]);
         w.y = pack_bf16(dqa[md][2], dqa[md][3]);
-        const int c = (2 * md + (lq >> 1)) ^ (lr % CH);
-        *reinterpret_cast<uint2*>(W + lr * D + c * 8 + 4 * (lq & 1)) = w;
+        *reinterpret_cast<uint2*>(W + lr * WST + 16 * md + 4 * lq) = w;
       }
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int r = RPL * j + ln / CH, cc = ln % CH;
         const uint32_t er = uint32_t(__shfl(int(e), r, 64));
-        const uint4 v = *reinterpret_cast<const uint4*>(W + r * D + ((cc ^ (r % CH)) * 8));
-        bf16_t* dp = 16 * gk + r < nrows
-                         ? a.dqp + soff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
-                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(W + r * WST + cc * 8);
+        const size_t grow = hrow0 + size_t(r % G) * N + (er & 0x7fffffu);
+        bf16_t* dp = 16 * gk + r < nrows ? a.dqp + (grow * topk1 + (er >> 23)) * D + cc * 8
+                                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
         *reinterpret_cast<uint4*>(dp) = v;
       }
-      float* dbp = (valid && !own_item) ? a.dbeta + (rbase + t) * a.topk + (e >> 23) : a.dummy + 64;
+      float* dbp = (valid && !own_item) ? dbl_item + 16 * gk + lr : a.dummy + 64;
       *dbp = db;
     };
 
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
         st1 = load_stat(e1);
         if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
       }
-      compute(tag, std::true_type{}, gk, e0, st0, ln);
+      compute(tag, gk, e0, st0, ln);
       wait_vm<NSTORE>();
       e0 = e1;
       e1 = e2;
@@ -659,11 +662,13 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
 //        0 .. nsel-1 and the own block's slot topk), and
 //   ds[m] = (m selected ? dbeta[slot(m)] : 0) - g[m] * sum(dbeta) for the
 //        history blocks m < c, g = exp(s - LSE_s); 0 from the own block on
-//        (slot(m) = rank of m among the row's selected blocks).
+//        (slot(m) = rank of m among the row's selected blocks; its dbeta is
+//        the record of the row's entry in m's list, pos[token][slot]).
 // Each lane takes 2 dq columns and 8 consecutive blocks per pass.
 template <int D>
 __global__ __launch_bounds__(256) void rows_sparse_kernel(
-    const bf16_t* __restrict__ dqp, const float* __restrict__ dbeta, const float* __restrict__ scores,
+    const bf16_t* __restrict__ dqp, const float* __restrict__ dbl, const uint32_t* __restrict__ pos,
+    size_t ents_per_pair, const float* __restrict__ scores,
     const float* __restrict__ lse_s, const uint32_t* __restrict__ selbits,
     const uint16_t* __restrict__ selpre, bf16_t* __restrict__ dq, float* __restrict__ ds, int Hq, int G,
     int N, int C, int MWB, int topk, float scale, size_t rows) {
@@ -712,9 +717,13 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
   }
 
   // ---- ds
-  const float* db = dbeta + row * topk;
+  // dbeta of slot s2: record pos[tok][s2] of the pair's list entries, head h
+  const int h = int(bh % Hq) % G;
+  const float* dbp = dbl + (bh / Hq * (Hq / G) + (bh % Hq) / G) * ents_per_pair * G + h;
+  const uint32_t* ps = pos + tok * topk;
+  auto dbeta = [&](int s2) -> float { return dbp[size_t(ps[s2]) * G]; };
   float tot = 0.f;
-  for (int s2 = lane; s2 < nsel; s2 += 64) tot += db[s2];
+  for (int s2 = lane; s2 < nsel; s2 += 64) tot += dbeta(s2);
   for (int off = 32; off >= 1; off >>= 1) tot += shfl_xor(tot, off);
   const float ls = lse_s[row];
   const float* srow = scores + row * C;
@@ -742,7 +751,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
       for (int i = 0; i < 8; ++i) {
         const bool sel = (b8 >> i) & 1u;
         const float gate = exp2_hw((sv[i] - ls) * kLog2e);
-        const float dbv = sel ? db[excl + __popc(b8 & ((1u << i) - 1u))] : 0.f;
+        const float dbv = sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f;
         out[i] = col0 + i < c ? dbv - gate * tot : 0.f;
       }
     } else {
@@ -753,7 +762,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
         if (m2 < c) {
           const bool sel = (b8 >> i) & 1u;
           const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-          v = (sel ? db[excl + __popc(b8 & ((1u << i) - 1u))] : 0.f) - gate * tot;
+          v = (sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f) - gate * tot;
         }
         out[i] = v;
       }
@@ -1173,7 +1182,7 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
 constexpr int kDqChunk = 256;  // tokens per work item of the sparse dQ kernel
 
 struct BwdWs {
-  size_t delta, rowstat, lists, dqp, dbeta, dummy, total;
+  size_t delta, rowstat, lists, dqp, dbl, dummy, total;
 };
 
 static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
@@ -1190,8 +1199,8 @@ static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
     at += align_up(lb);
     w.dqp = at;
     at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
-    w.dbeta = at;
-    at += align_up(rows * size_t(topk > 0 ? topk : 1) * sizeof(float));
+    w.dbl = at;
+    at += align_up(size_t(d.B) * d.Hkv * d.N * size_t(topk > 0 ? topk : 1) * d.G() * sizeof(float));
     w.dummy = at;
     at += align_up(512);
   }
@@ -1208,8 +1217,8 @@ static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStrea
   // persistent: one workgroup per compute unit (the LDS stages fill it)
   const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
   SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(grid), dim3(512), 0, s, a, L);
-  SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbeta,
-             a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, a.scale,
+  SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbl,
+             L.pos, L.ents_per_pair, a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, a.scale,
              rows);
 }
 
@@ -1271,7 +1280,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.selpre = L.pre;
     a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
     a.rowstat = reinterpret_cast<const float*>(w + W.rowstat);
-    a.dbeta = reinterpret_cast<float*>(w + W.dbeta);
+    a.dbl = reinterpret_cast<float*>(w + W.dbl);
     a.dummy = reinterpret_cast<float*>(w + W.dummy);
   }
   a.Hq = d.Hq;

@@ -71,7 +71,8 @@ struct SelLists {
   uint32_t* nitems;  // [pairs] work items
   uint32_t* items;   // [pairs][maxitems][4] {block | own << 31, first entry, end entry, 0}
   uint32_t* ents;    // [pairs][ents_per_pair] token | (slot << 23)
-  int MWB, NB, nseg, chunk, maxitems;
+  uint32_t* pos;     // [pairs * N][topk] list position of each (token, slot) entry
+  int MWB, NB, nseg, chunk, maxitems, topk;
   size_t ents_per_pair;
 };
 // base == NULL: sizes only (*bytes).  chunk = tokens per work item.

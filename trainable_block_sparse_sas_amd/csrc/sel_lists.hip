@@ -14,7 +14,7 @@
 //          at most `chunk` list entries whose tokens fall in one span of
 //          ISEG segments (items that run together then share query rows).
 //   fill   the lists, entry = token | (rank of the block among the token's
-//          selected blocks) << 23.
+//          selected blocks) << 23, and per (token, rank) the entry's position.
 // Every step is deterministic: the lists come out sorted by token.
 #include "common.h"
 #include "internal.h"
@@ -89,7 +89,9 @@ __global__ __launch_bounds__(64) void sel_pass_kernel(SelLists L, int N, int C, 
       const uint32_t rb = __shfl(run, b, 64);
       if (FILL && sel) {
         const uint32_t slot = uint32_t(base + __popc(word & ((1u << b) - 1u)));
-        ents[rb + __popcll(bal & lt)] = uint32_t(t) | (slot << 23);
+        const uint32_t at = rb + uint32_t(__popcll(bal & lt));
+        ents[at] = uint32_t(t) | (slot << 23);
+        L.pos[(tok0 + t) * L.topk + slot] = at;
       }
       if (lane == b) run = rb + uint32_t(__popcll(bal));
     }
@@ -228,6 +230,8 @@ SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int
   L.nitems = reinterpret_cast<uint32_t*>(take(pairs * 4));
   L.items = reinterpret_cast<uint32_t*>(take(pairs * L.maxitems * 16));
   L.ents = reinterpret_cast<uint32_t*>(take(pairs * L.ents_per_pair * 4));
+  L.pos = reinterpret_cast<uint32_t*>(take(tokens * size_t(topk > 0 ? topk : 1) * 4));
+  L.topk = topk;
   if (bytes) *bytes = at;
   return L;
 }
