@@ -511,8 +511,10 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
     // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
     auto entry = [&](int gk, int lr) -> uint32_t {
       const int p = min((16 * gk + lr) / G, ntok - 1);
-      if (own_item) return uint32_t(j0 + p) | (uint32_t(a.topk) << 23);
-      return ep[p];
+      // one load either way (own items read a valid dummy word), so the
+      // result is a select rather than a branch around a load
+      const uint32_t v = (own_item ? L.ents : ep)[own_item ? 0 : p];
+      return own_item ? (uint32_t(j0 + p) | (uint32_t(a.topk) << 23)) : v;
     };
     auto stg = [&](auto tag) -> uint16_t* {
       if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;

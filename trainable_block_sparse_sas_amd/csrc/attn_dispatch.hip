@@ -15,7 +15,7 @@ hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const vo
                            float* delta, hipStream_t s);
 
 bool fwd_mfma_supported(const Dims& d, int topk, bool sparse);
-size_t fwd_mfma_workspace(const Dims& d);
+size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                            int topk, float scale, void* ws, hipStream_t s);
@@ -30,7 +30,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
 
 size_t fwd_workspace(const Dims& d, int topk, bool bf16) {
   const bool sparse = topk >= 0;
-  if (bf16 && fwd_mfma_supported(d, sparse ? topk : 0, sparse)) return fwd_mfma_workspace(d);
+  if (bf16 && fwd_mfma_supported(d, sparse ? topk : 0, sparse))
+    return fwd_mfma_workspace(d, sparse ? topk : 0, sparse);
   return 0;
 }
 

@@ -495,22 +495,20 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
 }  // namespace
 
 // Shapes the matrix-core forward covers: bf16, block 64, D 64/128, G in
-// {1,2,4,8}, at least one complete block; sparse scope needs the per-workgroup
-// index lists and bias table to fit in LDS.
+// {1,2,4,8}, at least one complete block; sparse scope (key-major over the
+// selection lists) packs a token into 23 bits of a list entry and a block
+// into 16 bits of a work item.
 bool fwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   if (d.block != KT || (d.D != 64 && d.D != 128)) return false;
   if (d.C < 1) return false;
   const int G = d.G();
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  if (sparse) {
-    // sorted lists (tokens x topk) and the gate bias table (256 rows x topk)
-    if (size_t(256) * topk > kBiasMax || size_t(256 / G) * topk > kListMax) return false;
-    if (((d.C + 32) >> 5) > kMaskWords) return false;
-  }
+  if (sparse && (d.N > (1 << 22) || topk > 256)) return false;
   return true;
 }
 
-size_t fwd_mfma_workspace(const Dims& d) {
+size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
+  if (sparse) return fwd_sel_workspace(d, topk);
   const int NB = (d.N + KT - 1) / KT;
   return align_up(size_t(d.B) * d.Hkv * NB * KT * d.D * sizeof(bf16_t));
 }
@@ -522,11 +520,15 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
             (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, idx ? topk : 0, 0, 0,
             (d.N + KT - 1) / KT, scale};
   const int G = d.G();
-  const bool sp = idx != nullptr;
-#define SAS_FWD_CASE(DD, GG)                                                                  \
-  if (d.D == DD && G == GG) {                                                                 \
-    return sp ? fwd_mfma_t<DD, GG, true>(a, d.B, s) : fwd_mfma_t<DD, GG, false>(a, d.B, s); \
+  if (idx != nullptr) {
+    // sparse scope: the gate normaliser, then the key-major forward
+    const size_t rows = size_t(d.B) * d.Hq * d.N;
+    SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
+               d.N, d.C, KT, rows);
+    return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, ws, s);
   }
+#define SAS_FWD_CASE(DD, GG) \
+  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG, false>(a, d.B, s);
   SAS_FWD_CASE(128, 4)
   SAS_FWD_CASE(128, 1)
   SAS_FWD_CASE(128, 2)
