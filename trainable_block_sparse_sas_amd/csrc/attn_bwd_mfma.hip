@@ -102,13 +102,13 @@ __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __res
 // and dO rows (row-major, 16-byte chunks XOR-swizzled by row) and, per row,
 // lse, Delta, the block's selector score and LSE_s.  The own block's tokens
 // come first (causal mask, bias 0), then every later token (full scope) or the
-// later tokens whose selection holds m (sparse scope, compacted on the fly).
+// block's list of the later tokens whose selection holds m (sparse scope).
 //   S = Q K^T, dP = dO V^T      A: Q / dO row fragments
 //   dV += P^T dO, dK += dS^T Q  A: P^T / dS^T from registers (the permuted row
 //                               order of the S accumulators); B: dO / Q read
 //                               transposed from the row-major tile
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L) {
   using namespace tiles;
   constexpr int WAVES = 4;
   constexpr int NT = 64 * WAVES;
@@ -119,18 +119,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TPS = RS / G;       // tokens per step
   constexpr int NPIECE = RS * D * 2 / 1024;  // 1 KB loads per operand per step
   constexpr int PPW = NPIECE / WAVES;
-  constexpr int L = 2 * PPW + 1;    // loads per wave per step
   // Stage layout (16-bit units): Q [RS][D] | dO [RS][D] | fp32 [4][RS]
   // (lse, Delta, score of block m, LSE_s): one load target per stage.
   constexpr int ST_DO = RS * D, ST_F = 2 * RS * D;
   constexpr int STAGE = 2 * RS * D + 4 * RS * 2;
-  constexpr int QCAP = 512;
   static_assert(NPIECE % WAVES == 0 && WAVES == 4, "stat loads: one per wave");
-  static_assert(QCAP >= NT + TPS, "queue holds one scan chunk plus a step");
+  static_assert(RS == 64, "a lane holds the token of its own row");
   __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
   __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];  // token of each row, -1: none
-  __shared__ int queue[SPARSE ? QCAP : 1];
-  __shared__ int q_wave[WAVES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,75 +158,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     dv[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- token stream: own block, then history (uniform state in every thread)
+  // ---- token stream: step k < n_own covers own tokens k TPS .. (causal),
+  // later steps the history: consecutive tokens (full scope) or the block's
+  // list entries (sparse scope).
   const int own_n = min(KT, N - j0);
-  int own_pos = 0;                 // next own token offset
-  int seq = j0 + KT;               // full scope: next history token
-  int qh = 0, qt = 0, scan = j0 + KT;  // sparse: queue head / tail, next token to scan
-  const uint32_t* bits = SPARSE ? a.selbits + (size_t(b) * a.Hkv + g) * size_t(N) * a.MWB : nullptr;
-  // Sparse: top up the queue to a step's worth of tokens (or the end).
-  auto refill = [&]() {
-    while (qt - qh < TPS && scan < N) {
-      const int t = scan + tid;
-      const bool sel = t < N && ((bits[size_t(t) * a.MWB + (m >> 5)] >> (m & 31)) & 1u);
-      const unsigned long long bal = __ballot(sel);
-      if (lane == 0) q_wave[wave] = __popcll(bal);
-      __syncthreads();
-      int base = qt, total = 0;
-      for (int w = 0; w < WAVES; ++w) {
-        const int c = q_wave[w];
-        base += w < wave ? c : 0;
-        total += c;
-      }
-      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-      if (sel) queue[(base + __popcll(bal & lt)) % QCAP] = t;
-      __syncthreads();
-      qt += total;
-      scan += NT;
+  const int n_own = (own_n + TPS - 1) / TPS;
+  const uint32_t* lst = nullptr;
+  int n_hist;
+  if constexpr (SPARSE) {
+    const uint32_t* bo = L.blkoff + size_t(pair) * (L.NB + 1) + m;
+    lst = L.ents + size_t(pair) * L.ents_per_pair + bo[0];
+    n_hist = int(bo[1] - bo[0]);
+  } else {
+    n_hist = max(0, N - (j0 + KT));
+  }
+  const int n_steps = n_own + (n_hist + TPS - 1) / TPS;
+  // token of the i-th token slot of step k (-1: none); the sparse list is
+  // read unconditionally (a valid word for own steps) so that it is a select,
+  // not a branch around a load
+  auto tok_at = [&](int k, int i) -> int {
+    const bool own = k < n_own;
+    const int p = own ? k * TPS + i : (k - n_own) * TPS + i;
+    const int lim = own ? own_n : n_hist;
+    int t = own ? j0 + p : j0 + KT + p;
+    if constexpr (SPARSE) {
+      const uint32_t e = (own ? L.ents : lst)[own ? 0 : min(p, max(n_hist - 1, 0))];
+      if (!own) t = int(e & 0x7fffffu);
     }
-  };
-  // Tokens of the next step: returns the first token (own / full scope) or the
-  // queue head (sparse history), and the count; -1 count: no more rows.
-  // phase: 0 own block, 1 history.
-  auto take = [&](int& phase, int& first, int& cnt) {
-    if (own_pos < own_n) {
-      phase = 0;
-      first = j0 + own_pos;
-      cnt = min(TPS, own_n - own_pos);
-      own_pos += cnt;
-      return;
-    }
-    phase = 1;
-    if (!SPARSE) {
-      first = seq;
-      cnt = seq < N ? min(TPS, N - seq) : -1;
-      seq += TPS;
-      return;
-    }
-    first = qh;
-    cnt = qt > qh ? min(TPS, qt - qh) : -1;
-    qh += cnt > 0 ? cnt : 0;
-  };
-  auto token_of = [&](int phase, int first, int cnt, int i) -> int {  // i-th token of a step
-    if (i >= cnt) return -1;
-    if (SPARSE && phase == 1) return queue[(first + i) % QCAP];
-    return first + i;
+    return p < lim ? t : -1;
   };
 
   auto rst = [&](auto tag) -> uint16_t* {
     if constexpr (decltype(tag)::value == 0) return R0;
     else return R1;
   };
-  // Loads of one step into stage `tag` (ln: opaque lane index).
-  auto issue = [&](auto tag, int phase, int first, int cnt, int ln) {
+  // Loads of step k into stage `tag`; tk: token of the lane's row ln of the
+  // step (ln: opaque lane index).
+  auto issue = [&](auto tag, int k, int tk, int ln) {
     constexpr int P = decltype(tag)::value;
+    const int phase = k < n_own ? 0 : 1;
     uint16_t* st = rst(tag);
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int j = wave * PPW + i;          // 1 KB piece of the Q (dO) tile
       const int sl = 64 * j + ln;            // 16-byte slot: row r, stored chunk pc
       const int r = sl / CH, pc = sl % CH;
-      const int t = token_of(phase, first, cnt, r / G);
+      const int t = __shfl(tk, r, 64);
       const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
       const int c = pc ^ k_swz<D>(r);
       __builtin_amdgcn_global_load_lds(a.q + gr * D + c * 8, (lds_ptr_t)(st + j * 512), 16, 0, 0);
@@ -239,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     {
       const int r = ln;  // stat `wave` of row r
-      const int t = token_of(phase, first, cnt, r / G);
+      const int t = tk;
       const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
       // (own-block rows use no score; they read lse there, which always exists)
       const float* src = wave == 0 ? a.lse + gr
@@ -343,42 +316,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using S1 = std::integral_constant<int, 1>;
   using Own = std::integral_constant<bool, true>;
   using Hist = std::integral_constant<bool, false>;
-  int cur_phase, cur_first, cur_cnt;
-  take(cur_phase, cur_first, cur_cnt);
-  if (SPARSE && own_pos >= own_n) refill();
-  if (cur_cnt > 0) issue(S0{}, cur_phase, cur_first, cur_cnt, lane);
-  // One step on stage `tag`: wait for its rows, load the next step's rows
-  // into the other stage, compute.  MK: own-block rows (the first steps).
-  auto step = [&](auto tag, auto mkt) {
+  int tk1 = n_steps > 0 ? tok_at(0, lane / G) : -1;  // the lane's row, step 0
+  if (n_steps > 0) issue(S0{}, 0, tk1, lane);
+  tk1 = n_steps > 1 ? tok_at(1, lane / G) : -1;      // step 1
+  // One step on stage `tag`: wait for its rows, load step k + 1 into the
+  // other stage and fetch the tokens of step k + 2, compute.
+  auto step = [&](auto tag, auto mkt, int k) {
     using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
     int ln = lane;
     asm volatile("" : "+v"(ln));
     wait_vm<0>();
     ring_barrier();
-    int nph, nfirst, ncnt;
-    take(nph, nfirst, ncnt);
-    if (ncnt > 0) issue(Pn{}, nph, nfirst, ncnt, ln);
+    if (k + 1 < n_steps) issue(Pn{}, k + 1, tk1, ln);
+    const int tk2 = k + 2 < n_steps ? tok_at(k + 2, ln / G) : -1;
     compute(tag, mkt, ln);
-    // Sparse: top up the token queue once the own block's steps are issued.
-    if (SPARSE && own_pos >= own_n) refill();
-    cur_phase = nph;
-    cur_first = nfirst;
-    cur_cnt = ncnt;
+    tk1 = tk2;
   };
   // Own-block steps (one variant per loop: no accumulator merges), then the
-  // history, continuing on the stage where the first loop stopped.
-  int ph = 0;
-  while (cur_cnt > 0 && cur_phase == 0) {
-    step(S0{}, Own{});
-    if (cur_cnt <= 0 || cur_phase != 0) { ph = 1; break; }
-    step(S1{}, Own{});
+  // history on the stage where the first loop stopped.
+  int k = 0;
+  for (; k + 1 < n_own; k += 2) {
+    step(S0{}, Own{}, k);
+    step(S1{}, Own{}, k + 1);
   }
-  while (cur_cnt > 0) {
-    if (ph == 0) step(S0{}, Hist{});
-    else step(S1{}, Hist{});
-    ph ^= 1;
+  if (k < n_own) {
+    step(S0{}, Own{}, k);
+    ++k;
   }
-  (void)L;
+  if ((k & 1) && k < n_steps) {
+    step(S1{}, Hist{}, k);
+    ++k;
+  }
+  for (; k + 1 < n_steps; k += 2) {
+    step(S0{}, Hist{}, k);
+    step(S1{}, Hist{}, k + 1);
+  }
+  if (k < n_steps) step(S0{}, Hist{}, k);
+
 
   // Write dK (scaled) and dV: lane holds column 16 nd + lr of keys 4 lq + i of
   // the wave's 16.
@@ -1244,7 +1218,7 @@ static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s)
   }
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
-  SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a);
+  SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a, L);
   if (SPARSE)
     launch_dq_sparse<D, G>(a, L, rows, s);
   else
