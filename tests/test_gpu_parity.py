@@ -49,6 +49,10 @@ TRAIN_CASES = [
     ("bf16-g1-d64-sparse", "bf16", 2, 4, 4, 64, 256, 64, 1),
     ("bf16-block32-sparse", "bf16", 1, 4, 1, 128, 200, 32, 2),
     ("bf16-topk0", "bf16", 1, 4, 2, 128, 256, 64, 0),
+    # G = 2 and D = 64 at sparse scope; and G = 8 over two token spans of the
+    # key-major work items, with block lists longer than one work item
+    ("bf16-g2-d64-sparse", "bf16", 2, 4, 2, 64, 640, 64, 4),
+    ("bf16-g8-spans-sparse", "bf16", 1, 8, 1, 128, 4672, 64, 5),
 ]
 
 
