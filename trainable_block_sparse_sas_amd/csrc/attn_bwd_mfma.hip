@@ -9,18 +9,24 @@
 // The review's kernel paragraph ("A Concrete Walkthrough") describes the
 // block-wise aggregation of the log-gate gradient.
 //
-// Three kernels:
-//   prep  Delta per row, and (sparse scope) a per-token bitmask of selected blocks.
-//   dkdv  KV-major: a workgroup owns one block (64 keys, 16 per wave) of one KV
-//         head and streams the query rows that attend it, 32 rows per step: the
-//         own block's rows (causal) and every later row that gates the block
-//         (full scope: all of them; sparse scope: the tokens whose bitmask holds
-//         the block, compacted on the fly so no step carries an idle row).
-//         Lane = key layout (S = Q K^T), so dV = P^T dO and dK = dS^T Q
-//         contract over rows with P and dS straight from registers.
-//   dq    query-major like the forward (lane = row, S^T = K Q^T), recomputing P
-//         and dP^T = V dO^T per tile; dQ^T += K^T dS^T; dbeta is a lane-local
-//         row sum written per (row, block), then the dense ds epilogue.
+// Kernels:
+//   delta      Delta per row (and, sparse scope, the row's base-2 softmax
+//              offsets for its own and its gated blocks).
+//   dkdv       KV-major: a workgroup owns one block (64 keys, 16 per wave) of
+//              one KV head and streams the query rows that attend it, 64 rows
+//              per step: the own block's rows (causal) and every later row
+//              (full scope) or the block's list of selecting tokens (sparse
+//              scope, sel_lists.hip).  Lane = key layout (S = Q K^T), so dV =
+//              P^T dO and dK = dS^T Q contract over rows with P and dS straight
+//              from registers.
+//   dq_sel     sparse scope, key-major over the same lists with lane = row:
+//              per (row, selected block) the block's dQ share and dbeta.
+//   rows       sparse scope, per row: dq = sum of its dQ shares, and
+//              ds = dbeta - g sum(dbeta).
+//   dq         full scope, query-major like the forward (lane = row, S^T =
+//              K Q^T), recomputing P and dP^T = V dO^T per tile; dQ^T += K^T
+//              dS^T; dbeta is a lane-local row sum written per (row, block),
+//              then the dense ds epilogue.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -764,12 +770,9 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
 // dZ = P (dP - Delta), dbeta = sum of dZ over the tile (gated history tiles
 // only, written to ds as scratch), dZ packed to bf16 for the dQ product.  Own
 // blocks run in a second, masked loop.  The epilogue writes dq and turns the
-// row's dbeta into ds = dbeta - g sum(dbeta) (dense over the history).
-constexpr int kDqMaskWords = 1024;  // sparse scope: C + 1 <= 32768 blocks
-constexpr int kDqListMax = 4096;    // sparse scope: tokens per workgroup x topk
-constexpr int kDqBiasMax = 8192;    // sparse scope: rows per workgroup x topk
-
-template <int D, int G, int NSUB, int WAVES, int NST, bool SPARSE>
+// row's dbeta into ds = dbeta - g sum(dbeta) (dense over the history).  This
+// is the full-scope dQ; sparse scope is key-major (bwd_dq_sel_kernel).
+template <int D, int G, int NSUB, int WAVES, int NST>
 __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   using namespace tiles;
   constexpr int NT = 64 * WAVES;
@@ -781,18 +784,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   constexpr int CH = D / 8;
   constexpr int NKL = KT * D * 2 / 1024;  // 1 KB wave loads per operand tile
   constexpr int LPW = NKL / WAVES;
-  constexpr int L = 2 * LPW + (SPARSE ? 0 : 1);  // loads per wave per tile
+  constexpr int L = 2 * LPW + 1;          // loads per wave per tile
   static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
   static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
   static_assert(NST == 2 || NST == 3, "two or three ring stages");
-  static_assert(kDqBiasMax >= kDqListMax, "raw index scratch reuses the bias table");
   __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D], K2[NST > 2 ? KT * D : 8];
   __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D], V1[KT * D], V2[NST > 2 ? KT * D : 8];
-  __shared__ __attribute__((aligned(16))) float S0[SPARSE ? 1 : WAVES * 64], S1[SPARSE ? 1 : WAVES * 64],
-      S2[SPARSE || NST < 3 ? 1 : WAVES * 64];
-  __shared__ int32_t umask[SPARSE ? kDqMaskWords : 1];
-  __shared__ int32_t sorted[SPARSE ? kDqListMax : 1];
-  __shared__ float beta[SPARSE ? kDqBiasMax : 1];
+  __shared__ __attribute__((aligned(16))) float S0[WAVES * 64], S1[WAVES * 64], S2[NST < 3 ? 1 : WAVES * 64];
   __shared__ float tot_sh[ROWS_WG];
   // per row: lse (base 2), Delta, LSE_s -- read per step rather than held in
   // registers across the tile loop
@@ -819,11 +817,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     sub_live[s] = t0 < N;
   }
 
-  // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
-  const int MW = (C + 32) >> 5;
-  if (SPARSE)
-    sparse_tables<G, NSUB, WAVES>(a.idx, a.scores, a.lse_s, a.Hq, a.Hkv, N, C, a.topk, b, g, t_wg0, umask,
-                                  sorted, beta);
   if (tid == 0) wg_last = -1;
   __syncthreads();
   {
@@ -838,7 +831,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
   uint4 qf[NSUB][KS], of[NSUB][KS];
   float dbt[NSUB];
   f32x4 dqa[NSUB][MD];
-  int cursor[NSUB];
   for (int s = 0; s < NSUB; ++s) {
     const int rt = tok_of(s, lr);
     const bool ok = rt < N;
@@ -854,22 +846,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       rs[2] = ok ? a.lse_s[gr] : 0.f;
     }
     dbt[s] = 0.f;
-    cursor[s] = 0;
     for (int md = 0; md < MD; ++md) dqa[s][md] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto next_tile = [&](int mm) -> int {
-    if (!SPARSE) return (mm + 1 <= last_tile) ? mm + 1 : -1;
-    for (int w = (mm + 1) >> 5; w < MW; ++w) {
-      uint32_t bits = uint32_t(umask[w]);
-      if (w == ((mm + 1) >> 5)) bits &= ~0u << ((mm + 1) & 31);
-      if (bits) {
-        const int r = w * 32 + __builtin_ctz(bits);
-        return r <= last_tile ? r : -1;
-      }
-    }
-    return -1;
-  };
+  auto next_tile = [&](int mm) -> int { return (mm + 1 <= last_tile) ? mm + 1 : -1; };
+
 
   // ---- direct global -> LDS tile loads ------------------------------------------
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
@@ -920,7 +901,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
         __builtin_amdgcn_global_load_lds(vh + key * D + c * 8, (lds_ptr_t)(vd + j * 512), 16, 0, 0);
       }
     }
-    if (!SPARSE) {
+    {
       // score of row (ln % (16 NSUB)) of this wave, block m
       const int sr = ln % (16 * NSUB);
       const int st = min(tok_of(sr >> 4, sr & 15), N - 1);
@@ -975,18 +956,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       bool sel = false;
       float bsel = kNegInf;
       if (hist && row_t[s] < N) {
-        if (SPARSE) {
-          const int tok = row_t[s] - t_wg0;
-          const int32_t* srt = sorted + tok * a.topk;
-          int cu = cursor[s];
-          sel = (cu < a.topk && srt[cu] == m);
-          if (sel) bsel = beta[((wave * NSUB + s) * 16 + lr) * a.topk + cu];
-          while (cu < a.topk && srt[cu] == m) ++cu;
-          cursor[s] = cu;
-        } else {
-          sel = true;
-          bsel = (Ss[wave * 64 + 16 * s + lr] - lses) * kLog2e;
-        }
+        sel = true;
+        bsel = (Ss[wave * 64 + 16 * s + lr] - lses) * kLog2e;
       }
       const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
       nmask |= int(nd) << s;
@@ -1126,13 +1097,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     const float ls = a.lse_s[gr];
     const float* srow = a.scores + gr * C;
     float* drow = a.ds + gr * C;
-    const uint32_t* bits = SPARSE ? a.selbits + ((size_t(b) * a.Hkv + g) * N + t) * a.MWB : nullptr;
     for (int m2 = lane; m2 < C; m2 += 64) {
       float out = 0.f;
       if (m2 < c) {
         const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-        const bool sel = SPARSE ? ((bits[m2 >> 5] >> (m2 & 31)) & 1u) : true;
-        out = (sel ? drow[m2] : 0.f) - gate * tot;
+        out = drow[m2] - gate * tot;
       }
       drow[m2] = out;
     }
@@ -1203,7 +1172,7 @@ static void launch_dq_full(BwdArgs a, hipStream_t s) {
   constexpr int NSUB = 2, WAVES = 8, NST = 2;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
-  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, false>), dim3(a.n_tiles * a.n_pairs),
+  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST>), dim3(a.n_tiles * a.n_pairs),
              dim3(64 * WAVES), 0, s, a);
 }
 

@@ -21,13 +21,11 @@
 // an XOR-swizzled layout (conflict-free 16-byte MFMA operand reads); V comes
 // from a per-block transposed copy in the workspace, written by vt_kernel with
 // the keys permuted to the MFMA k order of P^T and the same kind of swizzle.
-// Full scope also streams the rows' selector scores of the tile.
+// Each K stage also holds the rows' selector scores of its tile.
 //
-// Sparse scope: each token's selected blocks are sorted in LDS and the gate
-// biases of every (row, selected block) are tabulated up front; the workgroup
-// visits the union of its rows' blocks in ascending order and a subtile skips
-// a tile none of its rows selected.  Full scope visits every block up to the
-// own one.
+// This kernel is the full-scope forward: a workgroup visits every block up
+// to its last own block.  Sparse scope is key-major over the selection lists
+// (attn_fwd_sel.hip).
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -40,9 +38,6 @@ namespace {
 
 using namespace tiles;
 
-constexpr int kMaskWords = 1024;  // sparse scope: C + 1 <= 32768 blocks
-constexpr int kListMax = 4096;    // sparse scope: tokens per workgroup x topk
-constexpr int kBiasMax = 8192;    // sparse scope: rows per workgroup x topk
 
 struct FwdArgs {
   const bf16_t* q;
@@ -50,11 +45,10 @@ struct FwdArgs {
   const bf16_t* v;
   const bf16_t* vt;  // workspace: transposed, permuted, swizzled V blocks
   const float* scores;
-  const int32_t* idx;
   bf16_t* o;
   float* lse;
   float* lse_s;
-  int Hq, Hkv, N, C, topk, n_tiles, n_pairs, NB;
+  int Hq, Hkv, N, C, n_tiles, n_pairs, NB;
   float scale;
 };
 
@@ -89,7 +83,7 @@ __global__ __launch_bounds__(256) void lse_rows_kernel(const float* __restrict__
   if (lane == 0) lse_s[row] = c > 0 ? mx + log_hw(sm) : kNegInf;
 }
 
-template <int D, int G, int NSUB, int WAVES, int NST, bool SPARSE>
+template <int D, int G, int NSUB, int WAVES, int NST>
 __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;    // k-steps of S = K Q^T
@@ -100,28 +94,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int CH = D / 8;               // 16-byte chunks per K row
   constexpr int NKL = KT * D * 2 / 1024;  // 1 KB wave loads per K (and per V) tile
   constexpr int LPW = NKL / WAVES;        // per wave, per operand
-  constexpr int L = 2 * LPW + (SPARSE ? 0 : 1);  // DMA instructions per wave per tile
+  constexpr int L = 2 * LPW + 1;          // DMA instructions per wave per tile
   static_assert(NKL % WAVES == 0, "tile loads must split evenly over the waves");
   static_assert(16 * NSUB <= 64, "one score load covers a wave's rows");
-  static_assert(kBiasMax >= kListMax, "raw index scratch reuses the bias table");
   static_assert(NSUB == 1 || NSUB == 2, "one or two subtiles per wave");
   // One array per ring stage: the compiler can then tell a stage being read
   // from the stages the in-flight loads write, and adds no waits of its own.
-  // Full scope: each K stage also holds the rows' selector scores of its tile
-  // (WAVES * 64 fp32 after the keys), so a stage is two load targets, not three.
-  constexpr int KX = KT * D + (SPARSE ? 0 : WAVES * 64 * 2);
+  // Each K stage also holds the rows' selector scores of its tile (WAVES * 64
+  // fp32 after the keys), so a stage is two load targets, not three.
+  constexpr int KX = KT * D + WAVES * 64 * 2;
   __shared__ __attribute__((aligned(16))) uint16_t K0[KX], K1[KX], K2[NST > 2 ? KX : 8],
       K3[NST > 3 ? KX : 8];
   __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT], V1[D * KT], V2[NST > 2 ? D * KT : 8],
       V3[NST > 3 ? D * KT : 8];
   __shared__ float lses_sh[ROWS_WG];
   __shared__ int wg_last;
-  // Sparse-scope tables, static so that reads in the loop do not alias the
-  // in-flight tile loads: union of selected blocks (bit mask), each token's
-  // selections sorted, and the gate bias of every (row, selection).
-  __shared__ int32_t umask[SPARSE ? kMaskWords : 1];
-  __shared__ int32_t sorted[SPARSE ? kListMax : 1];
-  __shared__ float beta[SPARSE ? kBiasMax : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -150,11 +137,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   }
   __syncthreads();
 
-  // ---- sparse scope: per-token sorted selections, union, gate-bias table ----
-  const int MW = (C + 32) >> 5;  // bits 0..C (the own block may be block C)
-  if (SPARSE)
-    sparse_tables<G, NSUB, WAVES>(a.idx, a.scores, a.lse_s, a.Hq, a.Hkv, N, C, a.topk, b, g, t_wg0, umask,
-                                  sorted, beta);
   if (tid == 0) wg_last = -1;
   __syncthreads();
   {
@@ -168,33 +150,20 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   // ---- Q fragments (B operand of S^T = K Q^T), one row per lane ----------------
   uint4 qf[NSUB][KS];
   float lses[NSUB];
-  int cursor[NSUB];
   for (int s = 0; s < NSUB; ++s) {
     const bool ok = row_t[s] < N;
     const bf16_t* qr = a.q + ((size_t(b) * a.Hq + row_h[s]) * N + (ok ? row_t[s] : 0)) * D;
     for (int ks = 0; ks < KS; ++ks)
       qf[s][ks] = ok ? *reinterpret_cast<const uint4*>(qr + ks * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
     lses[s] = lses_sh[wave * 16 * NSUB + s * 16 + lr];
-    cursor[s] = 0;
   }
 
-  auto next_tile = [&](int m) -> int {
-    if (!SPARSE) return (m + 1 <= last_tile) ? m + 1 : -1;
-    for (int w = (m + 1) >> 5; w < MW; ++w) {
-      uint32_t bits = uint32_t(umask[w]);
-      if (w == ((m + 1) >> 5)) bits &= ~0u << ((m + 1) & 31);
-      if (bits) {
-        const int r = w * 32 + __builtin_ctz(bits);
-        return r <= last_tile ? r : -1;
-      }
-    }
-    return -1;
-  };
+  auto next_tile = [&](int m) -> int { return (m + 1 <= last_tile) ? m + 1 : -1; };
 
   // ---- direct global -> LDS tile loads ------------------------------------------
   const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
   const bf16_t* vth = a.vt + (size_t(b) * a.Hkv + g) * size_t(a.NB) * KT * D;
-  // this lane's score row (full scope): the wave's rows 16s + lr, repeated
+  // this lane's score row: the wave's rows 16s + lr, repeated
   const int srow_i = lane % (16 * NSUB);
   const int s_s = srow_i >> 4, s_lr = srow_i & 15;
   const int s_t = min(t_wg0 + (wave * NSUB + s_s) * TOK_SUB + s_lr / G, N - 1);
@@ -250,8 +219,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
       __builtin_amdgcn_global_load_lds(vth + size_t(m) * KT * D + (64 * j + lane) * 8,
                                        (lds_ptr_t)(vd + j * 512), 16, 0, 0);
     }
-    if (!SPARSE)
-      __builtin_amdgcn_global_load_lds(s_base + min(m, C - 1), (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(s_base + min(m, C - 1), (lds_ptr_t)(sst(tag) + wave * 64), 4, 0, 0);
   };
   auto wait_tile = [&](int after) {
     // wait until at most `after` later tiles' loads are still outstanding
@@ -311,18 +279,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
       bool sel = false;
       float bsel = kNegInf;
       if (hist && row_t[s] < N) {
-        if (SPARSE) {
-          const int tok = row_t[s] - t_wg0;
-          const int32_t* srt = sorted + tok * a.topk;
-          int cu = cursor[s];
-          sel = (cu < a.topk && srt[cu] == m);
-          if (sel) bsel = beta[((wave * NSUB + s) * 16 + lr) * a.topk + cu];
-          while (cu < a.topk && srt[cu] == m) ++cu;
-          cursor[s] = cu;
-        } else {
-          sel = true;
-          bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
-        }
+        sel = true;
+        bsel = (Ss[wave * 64 + 16 * s + lr] - lses[s]) * kLog2e;
       }
       const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
       nmask |= int(nd) << s;
@@ -415,12 +373,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
         }
       }
     };
-    if (SPARSE && NSUB == 2) {
-      // each subtile only when one of its rows selected the tile (its K and V
-      // fragments are then read once per subtile)
-      if (nmask & 1) compute(std::integral_constant<int, 1>{});
-      if (nmask & 2) compute(std::integral_constant<int, 2>{});
-    } else if (nmask) {
+    if (nmask) {
       // every subtile of the wave (a subtile without the tile has bias -inf
       // on all rows and adds nothing)
       compute(std::integral_constant<int, (1 << NSUB) - 1>{});
@@ -472,9 +425,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int G, bool SPARSE>
+template <int D, int G>
 hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
-  // Sparse scope: wider workgroups (more tokens share each K/V tile load).
   constexpr int NSUB = 2;
   constexpr int WAVES = 8;
   constexpr int NST = 2;
@@ -487,7 +439,7 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
                      a.lse_s, a.N, a.C, KT, rows);
   SAS_LAUNCH("vt", (vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
                      const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
-  SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST, SPARSE>),
+  SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST>),
                      dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
@@ -516,9 +468,8 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                            int topk, float scale, void* ws, hipStream_t s) {
-  FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores, idx,
-            (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, idx ? topk : 0, 0, 0,
-            (d.N + KT - 1) / KT, scale};
+  FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
+            (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale};
   const int G = d.G();
   if (idx != nullptr) {
     // sparse scope: the gate normaliser, then the key-major forward
@@ -528,7 +479,7 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
     return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, ws, s);
   }
 #define SAS_FWD_CASE(DD, GG) \
-  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG, false>(a, d.B, s);
+  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, s);
   SAS_FWD_CASE(128, 4)
   SAS_FWD_CASE(128, 1)
   SAS_FWD_CASE(128, 2)

@@ -65,94 +65,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | 0xF00 | (((n >> 4) & 3) << 14));
 }
 
-// Sparse-scope tables of a workgroup that owns the TOK_WG = 16 NSUB WAVES / G
-// tokens t_wg0 .. of KV head g (rows r = 16 subtile + lane row; subtile sg
-// holds tokens t_wg0 + sg 16/G + (lane row)/G, query heads g G + (lane row)%G):
-//   sorted[tok][e]  the token's valid selections (0 <= m < own block) in
-//                   ascending order, then 0x7fffffff;
-//   umask           bit mask of the union of the selections and the subtiles'
-//                   own blocks (bits 0 .. C);
-//   beta[r][e]      gate bias (s - LSE_s) log2(e) of row r's e-th sorted
-//                   selection, -inf for padding.
-// beta doubles as scratch for the raw indices.  Every thread of the workgroup
-// must call it; global reads are issued in batches of 8 per thread.
-template <int G, int NSUB, int WAVES>
-__device__ void sparse_tables(const int32_t* __restrict__ idx, const float* __restrict__ scores,
-                              const float* __restrict__ lse_s, int Hq, int Hkv, int N, int C, int topk,
-                              int b, int g, int t_wg0, int32_t* umask, int32_t* sorted, float* beta) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int TOK_SUB = 16 / G;
-  constexpr int ROWS_WG = 16 * NSUB * WAVES;
-  constexpr int TOK_WG = ROWS_WG / G;
-  constexpr int BATCH = 8;
-  const int tid = threadIdx.x;
-  const int MW = (C + 32) >> 5;
-  int32_t* raw = reinterpret_cast<int32_t*>(beta);
-  for (int i = tid; i < MW; i += NT) umask[i] = 0;
-  const int n_sel = TOK_WG * topk;
-  const int32_t* ig = idx + ((size_t(b) * Hkv + g) * N + t_wg0) * size_t(topk);
-  for (int i0 = tid; i0 < n_sel; i0 += NT * BATCH) {
-    int v[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int i = i0 + u * NT;
-      v[u] = (i < n_sel && t_wg0 + i / topk < N) ? ig[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int i = i0 + u * NT;
-      if (i < n_sel) {
-        const int t = t_wg0 + i / topk;
-        raw[i] = (v[u] < 0 || v[u] >= t / KT) ? 0x7fffffff : v[u];
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < n_sel; i += NT) {
-    const int tok = i / topk, e = i % topk;
-    const int32_t* rr = raw + tok * topk;
-    const int m = rr[e];
-    int rank = 0;
-    for (int e2 = 0; e2 < topk; ++e2) {
-      const int m2 = rr[e2];
-      rank += (m2 < m) || (m2 == m && e2 < e);
-    }
-    sorted[tok * topk + rank] = m;
-    if (m != 0x7fffffff) atomicOr(&umask[m >> 5], 1 << (m & 31));
-  }
-  if (tid < WAVES * NSUB) {
-    const int t0 = t_wg0 + tid * TOK_SUB;
-    if (t0 < N) atomicOr(&umask[(t0 / KT) >> 5], 1 << ((t0 / KT) & 31));
-  }
-  __syncthreads();
-  const int n_bias = ROWS_WG * topk;
-  for (int i0 = tid; i0 < n_bias; i0 += NT * BATCH) {
-    float sv[BATCH], lv[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int i = i0 + u * NT;
-      sv[u] = kNegInf;
-      lv[u] = 0.f;
-      if (i < n_bias) {
-        const int r = i / topk, e = i % topk;
-        const int rl = r & 15;
-        const int t = t_wg0 + (r >> 4) * TOK_SUB + rl / G;
-        const int mm = sorted[(t - t_wg0) * topk + e];
-        if (t < N && mm != 0x7fffffff) {
-          const size_t gr = (size_t(b) * Hq + g * G + rl % G) * N + t;
-          sv[u] = scores[gr * C + mm];
-          lv[u] = lse_s[gr];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int i = i0 + u * NT;
-      if (i < n_bias) beta[i] = sv[u] == kNegInf ? kNegInf : (sv[u] - lv[u]) * kLog2e;
-    }
-  }
-}
-
 // One lane's share of a wave's direct global -> LDS copy: 16 bytes from src
 // land at lds + 16 lane (lds is the wave-uniform base).
 __device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
