@@ -31,15 +31,17 @@ struct DecodeArgs {
   float scale;
 };
 
+constexpr int kMaxTopk = 256;
+
 // Resolves attended entry e of (b, g) into a block index, or -1 when the
-// entry is empty (invalid / repeated idx entry, beyond the dense range).
-__device__ __forceinline__ int entry_block(const DecodeArgs& a, int b, int g, int e, int c) {
+// entry is empty (invalid / repeated idx entry, beyond the dense range).  ir:
+// the (b, g) row of idx, staged in LDS.
+__device__ __forceinline__ int entry_block(const DecodeArgs& a, const int32_t* ir, int e, int c) {
   if (a.idx == nullptr) {
     return e <= c ? e : -1;  // blocks 0..c-1, then the current block c
   }
   if (e == a.topk) return c;  // the current block
   if (e > a.topk) return -1;
-  const int32_t* ir = a.idx + (size_t(b) * a.Hkv + g) * a.topk;
   const int m = ir[e];
   if (m < 0 || m >= c) return -1;
   for (int e2 = 0; e2 < e; ++e2)
@@ -58,8 +60,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float qsh[G][D];
   __shared__ float sc[2][G][kKeys];
   __shared__ float red[4][G][D];
+  __shared__ int32_t ir_sh[kMaxTopk];
   const int part_i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.idx != nullptr)
+    for (int i = tid; i < a.topk; i += 256) ir_sh[i] = a.idx[(size_t(b) * a.Hkv + g) * a.topk + i];
   int len = a.cache_len[b];
   len = len > a.L ? a.L : len;
   const int pos = len - 1;
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   // The (block, key range) of each of this workgroup's steps; steps of one
   // block beyond 64 keys (block > 64) follow in order.
   auto step_range = [&](int e, int& j0, int& j_end) -> bool {
-    const int m = len > 0 ? entry_block(a, b, g, e, c) : -1;
+    const int m = len > 0 ? entry_block(a, ir_sh, e, c) : -1;
     if (m < 0) return false;
     j0 = m * a.block;
     j_end = (m == c) ? pos + 1 : j0 + a.block;
@@ -106,6 +111,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   int e = part_i * a.EPW, e_end = e + a.EPW;
   int j0 = 0, j_end = 0;
   bool have = false;
+  __syncthreads();  // ir_sh ready
   while (e < e_end && !(have = step_range(e, j0, j_end))) ++e;
   if (have) load(j0, j_end, kr, vr);
   __syncthreads();  // qsh ready
@@ -213,29 +219,53 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the P partials of each (b, query head) by log-sum-exp.
+// Merge the P partials of each (b, query head) by log-sum-exp: the partials'
+// (max, sum) lane-parallel into LDS weights, then per column a sum of P
+// independent loads.
+constexpr int kMergeMax = 4096;  // partials per (b, g); decode_plan keeps P near 2048 / (B Hkv)
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part,
                                                          T* __restrict__ o,
                                                          float* __restrict__ lse, int Hq, int Hkv,
                                                          int P) {
+  __shared__ float w_sh[kMergeMax];
+  __shared__ float red[D / 64];
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv, g = h / G, hh = h % G;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
   const float* base = part + (size_t(b) * Hkv + g) * P * G * (D + 2) + hh * (D + 2);
   const size_t stride = size_t(G) * (D + 2);
   float M = kNegInf;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * stride]);
-  float L = 0.f, acc = 0.f;
-  if (M != kNegInf) {
-    for (int p = 0; p < P; ++p) {
-      const float mp = base[p * stride];
-      if (mp == kNegInf) continue;
-      const float w = exp_hw(mp - M);
-      L = fmaf(base[p * stride + 1], w, L);
-      acc = fmaf(base[p * stride + 2 + d], w, acc);
-    }
+  for (int p = d; p < P; p += D) M = fmaxf(M, base[p * stride]);
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+  for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  float L = 0.f;
+  for (int p = d; p < P; p += D) {
+    const float mp = base[p * stride];
+    const float w = (M == kNegInf || mp == kNegInf) ? 0.f : exp_hw(mp - M);
+    w_sh[p] = w;
+    L = fmaf(base[p * stride + 1], w, L);
   }
+  for (int off = 32; off >= 1; off >>= 1) L += shfl_xor(L, off);
+  if (lane == 0) red[wave] = L;
+  __syncthreads();
+  L = 0.f;
+  for (int w = 0; w < D / 64; ++w) L += red[w];
+  float acc = 0.f;
+  int p = 0;
+  for (; p + 4 <= P; p += 4) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = base[(p + u) * stride + 2 + d];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = fmaf(x[u], w_sh[p + u], acc);
+  }
+  for (; p < P; ++p) acc = fmaf(base[p * stride + 2 + d], w_sh[p], acc);
   const size_t orow = size_t(b) * Hq + h;
   o[orow * D + d] = from_f32<T>(M == kNegInf ? 0.f : acc / L);
   if (lse && d == 0) lse[orow] = (M == kNegInf) ? kNegInf : M + log_hw(L);
@@ -288,6 +318,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
   if (B == 0 || Hq == 0) return hipSuccess;
   int E, w, P;
   decode_plan(B, Hkv, L_max, block, idx ? topk : -1, &E, &w, &P);
+  if (P > kMergeMax) return hipErrorInvalidValue;  // decode_plan keeps P <= 2049
   DecodeArgs a{q, kc, vc, cache_len, idx, (float*)ws, Hq, Hkv, L_max, D, block,
                idx ? topk : 0, L_max / block, w, P, scale};
   if (bf16) {

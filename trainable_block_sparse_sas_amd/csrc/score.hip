@@ -189,18 +189,24 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
       qv[h][i] = to_f32(q[(size_t(b) * Hq + g * G + h) * D + sub * VEC + i]);
   const int rows_per_wg = RPW * 4 * 4;  // 4 waves, 4 loads per wave
   const int m_base = blockIdx.x * rows_per_wg;
+  // All four row loads first (their addresses do not depend on cache_len, so
+  // they overlap its load); rows past the history are masked below.
+  uint4 raw[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int m = m_base + (it * 4 + wave) * RPW + rsub;
+    raw[it] = m < C ? *reinterpret_cast<const uint4*>(kbar + ((size_t(b) * Hkv + g) * C + m) * D + sub * VEC)
+                    : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int m = m_base + (it * 4 + wave) * RPW + rsub;
     float dots[MAXG];
     const bool in = m < C;
     T kv[VEC];
-    if (in && m < c_eff) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(
-          kbar + ((size_t(b) * Hkv + g) * C + m) * D + sub * VEC);
-      const T* p = reinterpret_cast<const T*>(&raw);
-      for (int i = 0; i < VEC; ++i) kv[i] = p[i];
-    } else {
-      for (int i = 0; i < VEC; ++i) kv[i] = T(0);
+    {
+      const T* p = reinterpret_cast<const T*>(&raw[it]);
+      for (int i = 0; i < VEC; ++i) kv[i] = m < c_eff ? p[i] : T(0);
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {

@@ -383,12 +383,27 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
   } else if (C <= 1024) {
     SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
-  } else if (topk <= 32) {
-    SAS_LAUNCH("topk_long", (topk_long_kernel<16, 8>), dim3(rows), dim3(1024), 0, s, scores, idx,
-                       cache_len, Hkv, hpr, Nq, C, block, topk);
   } else {
-    SAS_LAUNCH("topk_long", (topk_long_kernel<16, 64>), dim3(rows), dim3(1024), 0, s, scores, idx,
-                       cache_len, Hkv, hpr, Nq, C, block, topk);
+    // candidates per lane: just enough for C (16 waves x 64 lanes x PER);
+    // survivors per lane in the second stage: 16 K / 64
+#define SAS_TOPK_LONG(PER, PER2)                                                                          \
+  SAS_LAUNCH("topk_long", (topk_long_kernel<PER, PER2>), dim3(rows), dim3(1024), 0, s, scores, idx, cache_len, \
+             Hkv, hpr, Nq, C, block, topk)
+    const int per = C <= 2048 ? 2 : C <= 4096 ? 4 : C <= 8192 ? 8 : 16;
+    const int per2 = topk <= 16 ? 4 : topk <= 32 ? 8 : 64;
+    if (per == 2 && per2 == 4) SAS_TOPK_LONG(2, 4);
+    else if (per == 2 && per2 == 8) SAS_TOPK_LONG(2, 8);
+    else if (per == 2) SAS_TOPK_LONG(2, 64);
+    else if (per == 4 && per2 == 4) SAS_TOPK_LONG(4, 4);
+    else if (per == 4 && per2 == 8) SAS_TOPK_LONG(4, 8);
+    else if (per == 4) SAS_TOPK_LONG(4, 64);
+    else if (per == 8 && per2 == 4) SAS_TOPK_LONG(8, 4);
+    else if (per == 8 && per2 == 8) SAS_TOPK_LONG(8, 8);
+    else if (per == 8) SAS_TOPK_LONG(8, 64);
+    else if (per2 == 4) SAS_TOPK_LONG(16, 4);
+    else if (per2 == 8) SAS_TOPK_LONG(16, 8);
+    else SAS_TOPK_LONG(16, 64);
+#undef SAS_TOPK_LONG
   }
   return hipGetLastError();
 }
