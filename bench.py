@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="training workload only (no decode, no full scope)")
     ap.add_argument("--workload", default="train-32k-sparse")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the two decode workloads (one JSON line of decode results)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device copy first (counter calibration)")
     return ap.parse_args()
@@ -281,6 +283,24 @@ def cpu_baseline(w):
                       f"group ({ws.Hq} query heads) of the same seeded inputs, Top-K {ws.topk}"}
 
 
+def bench_decodes(torch, wmap):
+    dec = {}
+    for name in ("decode-128k-b8", "decode-512k-b1"):
+        wd = wmap[name]
+        r = bench_decode(torch, wd, 30, 5)
+        dec[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_step": round(r["ms_step"], 4),
+                     "ms_score": round(r["ms_score"], 4), "ms_topk": round(r["ms_topk"], 4),
+                     "ms_attend": round(r["ms_attend"], 4), "attend_GBps_on_kv": round(r["attend_gbs"], 1),
+                     "topk": wd.topk}
+        if name == "decode-512k-b1":
+            rd = bench_decode(torch, wd, 10, 2, dense=True)
+            dec[name]["dense_ms"] = round(rd["ms_step"], 4)
+            dec[name]["dense_GBps"] = round(rd["attend_gbs"], 1)
+            dec[name]["speedup_vs_dense"] = round(rd["ms_step"] / r["ms_step"], 2)
+            dec[name]["pages_speedup_context"] = "5.6x end-to-end Qwen3-4B decode at 512K, batch 1, unnamed GPU"
+    return dec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -294,6 +314,9 @@ def main():
     wmap = {w.name: w for w in WORKLOADS}
     w = wmap[args.workload]
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decodes(torch, wmap)}))
+        return
     if args.copy_probe:
         copy_probe(torch)
     tr = bench_train(torch, w, args.steps, args.warmup)
@@ -327,21 +350,7 @@ def main():
             "tflops": round((full["flops_fwd"] + full["flops_bwd"]) / (full["ms_step"] * 1e-3) / 1e12, 3),
             "fwd_tflops": round(full["flops_fwd"] / (full["ms_fwd"] * 1e-3) / 1e12, 3),
             "bwd_tflops": round(full["flops_bwd"] / (full["ms_bwd"] * 1e-3) / 1e12, 3)}
-        dec = {}
-        for name in ("decode-128k-b8", "decode-512k-b1"):
-            wd = wmap[name]
-            r = bench_decode(torch, wd, 30, 5)
-            dec[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_step": round(r["ms_step"], 4),
-                         "ms_score": round(r["ms_score"], 4), "ms_topk": round(r["ms_topk"], 4),
-                         "ms_attend": round(r["ms_attend"], 4), "attend_GBps_on_kv": round(r["attend_gbs"], 1),
-                         "topk": wd.topk}
-            if name == "decode-512k-b1":
-                rd = bench_decode(torch, wd, 10, 2, dense=True)
-                dec[name]["dense_ms"] = round(rd["ms_step"], 4)
-                dec[name]["dense_GBps"] = round(rd["attend_gbs"], 1)
-                dec[name]["speedup_vs_dense"] = round(rd["ms_step"] / r["ms_step"], 2)
-                dec[name]["pages_speedup_context"] = "5.6x end-to-end Qwen3-4B decode at 512K, batch 1, unnamed GPU"
-        out["decode"] = dec
+        out["decode"] = bench_decodes(torch, wmap)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))

@@ -8,6 +8,11 @@
       run, each scaled by what the same counter reads for a plain copy kernel
       that reads and writes 1 GiB (bench.py --copy-probe).
 
+  python -m trainable_block_sparse_sas_amd.profsum counters DB --cmd "..." --match fwd_sel bwd_dq_sel ...
+      per-kernel counter totals per dispatch (summed over counter instances)
+      with the kernel's duration; SQ_INSTS_MFMA gives the executed matrix
+      work (each v_mfma_f32_16x16x32_bf16 is 16384 flops).
+
 Reads only the SQLite views rocprofv3 writes (kernels, pmc_events).
 """
 from __future__ import annotations
@@ -114,6 +119,37 @@ def traffic(fetch_db, write_db, kernel, workload, cmd_fetch, cmd_write):
     return "\n".join(lines) + "\n"
 
 
+def counters(db, cmd, match):
+    con = sqlite3.connect(db)
+    per = {}  # kernel -> dispatch -> {counter: total}, durations
+    durs = {}
+    for name, disp, dur, cn, cv in con.execute(
+            "select name, dispatch_id, duration, counter_name, counter_value from pmc_events"):
+        n = short_name(name)
+        if not any(m + "_kernel<" in n or n.endswith(m + "_kernel") for m in match):
+            continue
+        d = per.setdefault(n, {}).setdefault(disp, {})
+        d[cn] = d.get(cn, 0.0) + cv
+        durs.setdefault(n, {})[disp] = dur / 1e3  # us
+    names = sorted({c for k in per.values() for d in k.values() for c in d})
+    out = ["# Counter summary", "", "Command:", "", "```", cmd, "```", "",
+           "Per dispatch, summed over counter instances, averaged over dispatches. Duration is",
+           "the profiled dispatch (counters slow kernels down; use the kernel trace for time).", "",
+           "| kernel | dispatches | duration us | " + " | ".join(names) + " | MFMA TFLOP/s executed | VALU per MFMA |",
+           "|---|---:|---:|" + "---:|" * len(names) + "---:|---:|"]
+    for k in sorted(per):
+        disp = per[k]
+        avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in names}
+        dur = sum(durs[k].values()) / len(durs[k])
+        mf = avg.get("SQ_INSTS_MFMA", 0.0)
+        va = avg.get("SQ_INSTS_VALU", 0.0)
+        tf = mf * 16384 / (dur * 1e-6) / 1e12 if dur else 0.0
+        vpm = f"{va / mf:.2f}" if mf else "-"
+        out.append(f"| `{k[:70]}` | {len(disp)} | {dur:.1f} | " + " | ".join(f"{avg[c]:.4g}" for c in names)
+                   + f" | {tf:.1f} | {vpm} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -127,7 +163,14 @@ def main():
     b.add_argument("--workload", required=True)
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
+    cn = sub.add_parser("counters")
+    cn.add_argument("db")
+    cn.add_argument("--cmd", required=True)
+    cn.add_argument("--match", nargs="+", required=True)
     args = ap.parse_args()
+    if args.what == "counters":
+        print(counters(args.db, args.cmd, args.match), end="")
+        return
     if args.what == "stats":
         print(stats(args.db, args.cmd), end="")
     else:
