@@ -477,11 +477,13 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
     // Lane constants of the item.  Row r_j = RPL j + lane / CH of a group is
     // loaded and stored by this lane at chunk lane % CH; the head of a row is
     // r % G, so everything but the token is fixed per item.
-    size_t qoff[NLD];
+    size_t qoff[NLD], soff[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int r = RPL * j + lane / CH, pc = lane % CH;
-      qoff[j] = (hrow0 + size_t(r % G) * N) * D + ((pc ^ k_swz<D>(r)) * 8);
+      const size_t hr = hrow0 + size_t(r % G) * N;
+      qoff[j] = hr * D + ((pc ^ k_swz<D>(r)) * 8);
+      soff[j] = hr * size_t(topk1) * D + pc * 8;  // slot row of token 0, this lane's chunk
     }
     const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
     // dbeta records of the item's list entries: [entry][head], so row q of the
@@ -600,9 +602,9 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
         const int r = RPL * j + ln / CH, cc = ln % CH;
         const uint32_t er = uint32_t(__shfl(int(e), r, 64));
         const uint4 v = *reinterpret_cast<const uint4*>(W + r * WST + cc * 8);
-        const size_t grow = hrow0 + size_t(r % G) * N + (er & 0x7fffffu);
-        bf16_t* dp = 16 * gk + r < nrows ? a.dqp + (grow * topk1 + (er >> 23)) * D + cc * 8
-                                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+        bf16_t* dp = 16 * gk + r < nrows
+                         ? a.dqp + soff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
+                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
         *reinterpret_cast<uint4*>(dp) = v;
       }
       float* dbp = (valid && !own_item) ? dbl_item + 16 * gk + lr : a.dummy + 64;

@@ -126,11 +126,13 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
 
     // Lane constants of the item: row r_j = RPL j + lane / CH of a group is
     // loaded by this lane at chunk lane % CH; its head is r % G.
-    size_t qoff[NLD];
+    size_t qoff[NLD], ooff[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int r = RPL * j + lane / CH, pc = lane % CH;
-      qoff[j] = (hrow0 + size_t(r % G) * N) * D + ((pc ^ k_swz<D>(r)) * 8);
+      const size_t hr = hrow0 + size_t(r % G) * N;
+      qoff[j] = hr * D + ((pc ^ k_swz<D>(r)) * 8);
+      ooff[j] = hr * size_t(topk1) * D + pc * 8;  // slot row of token 0, this lane's chunk
     }
     const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
     // (m, l) records of the item's list entries: row q of the item is record q
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       return (a.scores[gr * C + m] - a.lse_s[gr]) * kLog2e;
     };
 
-    auto compute = [&](auto tag, int gk, uint32_t e, float bias, int ln) {
+    auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, float bias, int ln) {
+      constexpr bool MASK = decltype(maskt)::value;
       uint16_t* Qs = stg(tag);
       const int lr = ln & 15, lq = ln >> 4;
       const int qsw = k_swz<D>(lr);  // = k_swz(16 kt + lr) for every kt
@@ -191,7 +194,8 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[kt][i] = j0 + 16 * kt + 4 * lq + i <= tlim ? fmaf(sacc[kt][i], c1, bias) : kNegInf;
+          x[kt][i] = fmaf(sacc[kt][i], c1, bias);
+          if (MASK) x[kt][i] = j0 + 16 * kt + 4 * lq + i <= tlim ? x[kt][i] : kNegInf;
           mx = fmaxf(mx, x[kt][i]);
         }
       mx = fmaxf(mx, shfl_xor(mx, 16));
@@ -238,9 +242,9 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         const int r = RPL * j + ln / CH, cc = ln % CH;
         const uint32_t er = uint32_t(__shfl(int(e), r, 64));
         const uint4 v = *reinterpret_cast<const uint4*>(W + r * D + ((cc ^ (r % CH)) * 8));
-        const size_t grow = hrow0 + size_t(r % G) * N + (er & 0x7fffffu);
-        bf16_t* dp = 16 * gk + r < nrows ? a.op + (grow * topk1 + (er >> 23)) * D + cc * 8
-                                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+        bf16_t* dp = 16 * gk + r < nrows
+                         ? a.op + ooff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
+                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
         *reinterpret_cast<uint4*>(dp) = v;
       }
       float2* sp = !valid ? reinterpret_cast<float2*>(a.dummy + 64)
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         b1 = load_bias(e1);
         if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
       }
-      compute(tag, gk, e0, b0, ln);
+      compute(tag, std::true_type{}, gk, e0, b0, ln);
       wait_vm<NSTORE>();
       e0 = e1;
       e1 = e2;
