@@ -49,8 +49,11 @@ __device__ __forceinline__ int entry_block(const DecodeArgs& a, const int32_t* i
   return m;
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
+// ONE: every workgroup has exactly one attended entry of at most 64 keys
+// (EPW = 1, block <= 64): no next-step prefetch registers, so more
+// workgroups fit on a compute unit and all of them are resident at once.
+template <typename T, int D, int G, bool ONE>
+__global__ __launch_bounds__(256, ONE ? 2 : 1) void decode_partial_kernel(DecodeArgs a) {
   constexpr int DQ = D / 4;                 // K columns per lane (4 lanes per key)
   constexpr int VE = 16 / int(sizeof(T));   // V columns per 16-byte load
   constexpr int LPV = D / VE;               // lanes per V row
@@ -119,13 +122,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   while (have) {
     // next step
     int ne = e, nj0 = j0 + kKeys, nj_end = j_end;
-    bool nhave = nj0 < j_end;
-    if (!nhave) {
+    bool nhave = !ONE && nj0 < j_end;
+    if (!ONE && !nhave) {
       ++ne;
       while (ne < e_end && !(nhave = step_range(ne, nj0, nj_end))) ++ne;
     }
-    uint4 kn[KLD], vn[VKEYS];
-    if (nhave) load(nj0, nj_end, kn, vn);
+    uint4 kn[ONE ? 1 : KLD], vn[ONE ? 1 : VKEYS];
+    if constexpr (!ONE)
+      if (nhave) load(nj0, nj_end, kn, vn);
     // scores of this chunk's 64 keys
     const int j = j0 + key;
     {
@@ -188,8 +192,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     e = ne;
     j0 = nj0;
     j_end = nj_end;
-    for (int i = 0; i < KLD; ++i) kr[i] = kn[i];
-    for (int r = 0; r < VKEYS; ++r) vr[r] = vn[r];
+    if constexpr (!ONE) {
+      for (int i = 0; i < KLD; ++i) kr[i] = kn[i];
+      for (int r = 0; r < VKEYS; ++r) vr[r] = vn[r];
+    }
     buf ^= 1;
   }
   // Sum the V slots of each wave, then the four waves, and write the partial.
@@ -289,9 +295,15 @@ template <typename T, int D>
 hipError_t decode_t(const DecodeArgs& a0, int B, T* o, float* lse, hipStream_t s) {
   DecodeArgs a = a0;
   dim3 grid(a.P, a.Hkv, B);
+  const bool one = a.EPW == 1 && a.block <= kKeys;
   switch (a.Hq / a.Hkv) {
-#define SAS_DEC_G(GG) \
-  case GG: SAS_LAUNCH("decode_partial", (decode_partial_kernel<T, D, GG>), grid, dim3(256), 0, s, a); break;
+#define SAS_DEC_G(GG)                                                                                 \
+  case GG:                                                                                            \
+    if (one)                                                                                          \
+      SAS_LAUNCH("decode_partial", (decode_partial_kernel<T, D, GG, true>), grid, dim3(256), 0, s, a); \
+    else                                                                                              \
+      SAS_LAUNCH("decode_partial", (decode_partial_kernel<T, D, GG, false>), grid, dim3(256), 0, s, a); \
+    break;
     SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4) SAS_DEC_G(5) SAS_DEC_G(6) SAS_DEC_G(7)
     SAS_DEC_G(8) SAS_DEC_G(9) SAS_DEC_G(10) SAS_DEC_G(11) SAS_DEC_G(12) SAS_DEC_G(13) SAS_DEC_G(14)
     SAS_DEC_G(15) SAS_DEC_G(16)
