@@ -60,6 +60,8 @@ struct BwdArgs {
   uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
   bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: dQ share per slot (sparse)
   float* dbl;        // workspace [pairs, list entries, G]: dbeta per list entry and head (sparse)
+  bf16_t* dsr;       // workspace [pairs, list entries, G, 64]: dS of the entry's block (sparse)
+  bf16_t* dso;       // workspace [B, Hq, N, 64]: dS of the row's own block (sparse)
   const float* rowstat;  // workspace [B, Hq, N] x {Delta, -lse log2e, -(lse + LSE_s) log2e, 0} (sparse)
   float* dummy;          // workspace line that absorbs masked stores
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
@@ -133,6 +135,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   static_assert(RS == 64, "a lane holds the token of its own row");
   __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
   __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];  // token of each row, -1: none
+  // sparse scope: the step's dS rows [row][key] (bf16, padded) and the four
+  // waves' per-row sums of dS over their keys, written out as records
+  constexpr int TST = KT + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t dst_sh[SPARSE ? RS * TST : 8];
+  __shared__ __attribute__((aligned(16))) float dbs_sh[SPARSE ? WAVES * RS : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,6 +186,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     n_hist = max(0, N - (j0 + KT));
   }
   const int n_steps = n_own + (n_hist + TPS - 1) / TPS;
+  // sparse scope: record of row 0 of history step k is rec0 + (k - n_own) RS
+  const size_t rec0 = SPARSE ? (size_t(pair) * L.ents_per_pair + (lst - (L.ents + size_t(pair) * L.ents_per_pair))) * G
+                             : 0;
   // token of the i-th token slot of step k (-1: none); the sparse list is
   // read unconditionally (a valid word for own steps) so that it is a select,
   // not a branch around a load
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   };
 
   // One step on stage `tag`; MK: own-block rows (causal, bias 0) else gated history rows.
-  auto compute = [&](auto tag, auto mkt, int ln) {
+  auto compute = [&](auto tag, auto mkt, int ln, int kcur) {
     constexpr int P = decltype(tag)::value;
     constexpr bool MK = decltype(mkt)::value;
     const uint16_t* Qs = rst(tag);
@@ -261,6 +271,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       }
     // P and dS: lane holds key `key`, rows 16 rs + 4 lq + i.
     uint4 pa[2], dsa[2];
+    float dsum[SPARSE ? 16 : 1];
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       const int r0 = 16 * rs + 4 * lq;
@@ -282,6 +293,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         x = ok ? x : kNegInf;
         p[i] = exp2_hw(x);
         d[i] = p[i] * (pacc[rs][i] - dl[i]);
+      }
+      if constexpr (SPARSE) {
+        // dS rows for the dQ pass, and this wave's share of the row sums
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst_sh[(r0 + i) * TST + wave * 16 + lr] = f32_to_bf16(d[i]);
+          dsum[4 * rs + i] = d[i];
+        }
       }
       const int kk = rs >> 1;
       if (rs & 1) {
@@ -315,6 +334,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         dk[nd] = mfma16(dsa[kk], make_uint4(q0.x, q0.y, q1.x, q1.y), dk[nd]);
       }
     }
+    if constexpr (SPARSE) {
+      // Sum over the wave's 16 keys (lanes lr): afterwards lane lr holds
+      // value lr, i.e. row 16 (lr / 4) + 4 lq + lr % 4.
+#pragma unroll
+      for (int M = 8, n = 16; M >= 1; M >>= 1, n >>= 1) {
+        const bool hi = (lr & M) != 0;
+#pragma unroll
+        for (int j = 0; j < n / 2; ++j) {
+          const float send = hi ? dsum[j] : dsum[j + n / 2];
+          const float keep = hi ? dsum[j + n / 2] : dsum[j];
+          dsum[j] = keep + __shfl_xor(send, M, 64);
+        }
+      }
+      dbs_sh[wave * RS + 16 * (lr >> 2) + 4 * lq + (lr & 3)] = dsum[0];
+      ring_barrier();  // the step's dS rows and row sums are complete
+      // Records: history rows r of step k are consecutive (entry, head)
+      // records; own rows go to the per-row own-block array.
+      const int* tkr = tok_sh[P];
+      const int tid = wave * 64 + ln;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = (u * 256 + tid) >> 3, c8 = tid & 7;  // row, 16-byte chunk
+        const uint4 v = *reinterpret_cast<const uint4*>(dst_sh + r * TST + c8 * 8);
+        const int t = tkr[r];
+        if (t >= 0) {
+          bf16_t* dst = MK ? a.dso + (hrow0 + size_t(r % G) * N + t) * KT
+                           : a.dsr + (rec0 + size_t(kcur - n_own) * RS + r) * KT;
+          *reinterpret_cast<uint4*>(dst + c8 * 8) = v;
+        }
+      }
+      if (!MK && tid < RS && tkr[tid] >= 0) {
+        const float db = dbs_sh[tid] + dbs_sh[RS + tid] + dbs_sh[2 * RS + tid] + dbs_sh[3 * RS + tid];
+        a.dbl[rec0 + size_t(kcur - n_own) * RS + tid] = db;
+      }
+    }
   };
 
   // ---- the ring: step k computes stage k % 2 and loads step k + 1 into the other
@@ -335,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     ring_barrier();
     if (k + 1 < n_steps) issue(Pn{}, k + 1, tk1, ln);
     const int tk2 = k + 2 < n_steps ? tok_at(k + 2, ln / G) : -1;
-    compute(tag, mkt, ln);
+    compute(tag, mkt, ln, k);
     tk1 = tk2;
   };
   // Own-block steps (one variant per loop: no accumulator merges), then the
@@ -633,6 +687,175 @@ __global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) 
       e0 = e1;
       e1 = e2;
       st0 = st1;
+    };
+    for (int k = 0; k < nk; k += 2) {
+      step(S0t{}, k);
+      if (k + 1 < nk) step(S1t{}, k + 1);
+    }
+  }
+}
+
+// --------------------------------------------------- dQ from dS, sparse scope ----
+// dQ shares from the dS rows the dK/dV kernel recorded: per (row, selected
+// block) the share is dS[row, keys of m] K_m.  Persistent workgroups walk the
+// same work items as the key-major kernels; each wave takes 16 rows per step
+// (their dS records are consecutive for a list item), dQ^T = K^T dS^T with
+// K^T laid out per lane in LDS (keys of a 32-wide k step in the order
+// {4 lq + i, 16 + 4 lq + i}) and dS^T read from the staged rows in the same
+// order.  The shares leave through LDS as whole rows into the row's slot.
+template <int D, int G>
+__global__ __launch_bounds__(1024) void bwd_dq_ds_kernel(BwdArgs a, SelLists L) {
+  using namespace tiles;
+  constexpr int WAVES = 16;
+  constexpr int ND = D / 16;
+  constexpr int CH = D / 8;              // 16-byte chunks of a dQ row
+  constexpr int RPL = 64 / CH;           // dQ rows per wave-wide 16-byte store
+  constexpr int NST = 16 / RPL;          // stores per step
+  constexpr int SCH = KT / 8;            // 16-byte chunks of a dS row (8)
+  constexpr int STG = 16 * KT;           // per wave stage: 16 dS rows
+  constexpr int WST = D + 8;             // dQ staging row stride
+  static_assert(16 % G == 0, "a 16-row group holds whole tokens");
+  static_assert(KT * D <= WAVES * 16 * WST, "K tile fits in the staging area");
+  __shared__ __attribute__((aligned(16))) uint4 KTa[2 * ND * 64];  // A operands of dQ^T, per lane
+  __shared__ __attribute__((aligned(16))) uint16_t S0[WAVES * STG];
+  __shared__ __attribute__((aligned(16))) uint16_t S1[WAVES * STG];
+  __shared__ __attribute__((aligned(16))) uint16_t Wsh[WAVES * 16 * WST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = a.N, pairs = a.n_pairs;
+  const int topk1 = a.topk + 1;
+  const int total = pairs * L.maxitems;
+  using S0t = std::integral_constant<int, 0>;
+  using S1t = std::integral_constant<int, 1>;
+
+  for (int vi = blockIdx.x; vi < total; vi += gridDim.x) {
+    const int pair = vi % pairs, item = vi / pairs;
+    if (item >= int(L.nitems[pair])) continue;
+    const uint4 it = reinterpret_cast<const uint4*>(L.items)[size_t(pair) * L.maxitems + item];
+    const int m = int(it.x & 0xffffu);
+    const bool own_item = (it.x >> 31) != 0;
+    const int b = pair / a.Hkv, g = pair % a.Hkv;
+    const int j0 = m * KT;
+    const int ntok = own_item ? min(KT, N - j0) : int(it.z - it.y);
+    const uint32_t* ep = L.ents + size_t(pair) * L.ents_per_pair + it.y;
+    const int nrows = ntok * G;
+    const int ngroups = (nrows + 15) >> 4;
+    const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
+    const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
+    const size_t rec_item = (size_t(pair) * L.ents_per_pair + it.y) * G;  // record of the item's row 0
+
+    // ---- K tile (over the staging area), then K^T per lane into KTa
+    __syncthreads();  // the previous item is done with KTa and the staging area
+    {
+      const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+      constexpr int KPIECE = KT * D * 2 / 1024;
+      for (int j = wave; j < KPIECE; j += WAVES) {
+        const int r = RPL * j + lane / CH, pc = lane % CH;
+        const size_t key = size_t(min(j0 + r, N - 1));
+        dma16_to_lds(kh + key * D + ((pc ^ k_swz<D>(r)) * 8), Wsh + j * 512);
+      }
+    }
+    wait_vm<0>();
+    __syncthreads();
+    {
+      const int lr = lane & 15, lq = lane >> 4;
+      for (int u = wave; u < 2 * ND; u += WAVES) {
+        const int kk = u / ND, md = u % ND;
+        const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
+        const int col = 16 * md + 4 * (lr & 3);
+        const uint2 k0 = lds_read_tr16(Wsh + ka * D + ((((col >> 3) ^ k_swz<D>(ka)) << 3) + (col & 7)));
+        const uint2 k1 = lds_read_tr16(Wsh + kb * D + ((((col >> 3) ^ k_swz<D>(kb)) << 3) + (col & 7)));
+        KTa[u * 64 + lane] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+      }
+    }
+    __syncthreads();  // K^T operands written; the staging area is free again
+    if (nk == 0) continue;
+
+    // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
+    auto entry = [&](int gk, int lr) -> uint32_t {
+      const int p = min((16 * gk + lr) / G, ntok - 1);
+      const uint32_t v = (own_item ? L.ents : ep)[own_item ? 0 : p];
+      return own_item ? (uint32_t(j0 + p) | (uint32_t(a.topk) << 23)) : v;
+    };
+    auto stg = [&](auto tag) -> uint16_t* {
+      if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;
+      else return S1 + wave * STG;
+    };
+    // dS rows of group gk: row r's chunk pc lands at chunk pc ^ (r % 8)
+    auto issue = [&](auto tag, int gk, uint32_t e, int ln) {
+      uint16_t* st = stg(tag);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sl = 64 * j + ln;
+        const int r = sl / SCH, pc = sl % SCH;
+        const int c = pc ^ (r & 7);
+        const bool ok = 16 * gk + r < nrows;
+        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+        const bf16_t* src = own_item ? a.dso + (hrow0 + size_t(r % G) * N + (er & 0x7fffffu)) * KT
+                                     : a.dsr + (rec_item + size_t(ok ? 16 * gk + r : 0)) * KT;
+        dma16_to_lds(src + c * 8, st + j * 512);
+      }
+    };
+
+    auto compute = [&](auto tag, int gk, uint32_t e, int ln) {
+      const uint16_t* Ds = stg(tag);
+      const int lr = ln & 15, lq = ln >> 4;
+      // B operands: row lr, keys 32 kk + 4 lq .. +3 and 32 kk + 16 + 4 lq .. +3
+      uint4 dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ca = 4 * kk + (lq >> 1), cb = ca + 2;  // 16-byte chunks of the two key runs
+        const uint2 x0 = *reinterpret_cast<const uint2*>(Ds + lr * KT + ((ca ^ (lr & 7)) * 8) + 4 * (lq & 1));
+        const uint2 x1 = *reinterpret_cast<const uint2*>(Ds + lr * KT + ((cb ^ (lr & 7)) * 8) + 4 * (lq & 1));
+        dsb[kk] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      }
+      f32x4 dqa[ND];
+#pragma unroll
+      for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int md = 0; md < ND; ++md) dqa[md] = mfma16(KTa[(kk * ND + md) * 64 + ln], dsb[kk], dqa[md]);
+      uint16_t* W = Wsh + wave * 16 * WST;
+#pragma unroll
+      for (int md = 0; md < ND; ++md) {
+        uint2 w;
+        w.x = pack_bf16(dqa[md][0], dqa[md][1]);
+        w.y = pack_bf16(dqa[md][2], dqa[md][3]);
+        *reinterpret_cast<uint2*>(W + lr * WST + 16 * md + 4 * lq) = w;
+      }
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        const int r = RPL * j + ln / CH, cc = ln % CH;
+        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
+        const uint4 v = *reinterpret_cast<const uint4*>(W + r * WST + cc * 8);
+        const size_t grow = hrow0 + size_t(r % G) * N + (er & 0x7fffffu);
+        bf16_t* dp = 16 * gk + r < nrows ? a.dqp + (grow * topk1 + (er >> 23)) * D + cc * 8
+                                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
+        *reinterpret_cast<uint4*>(dp) = v;
+      }
+    };
+
+    // pipeline over this wave's groups gk = wave + WAVES k
+    uint32_t e0 = entry(wave, lane & 15);
+    uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
+    issue(S0t{}, wave, e0, lane);
+    wait_vm<0>();
+    auto step = [&](auto tag, int k) {
+      using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int gk = wave + WAVES * k;
+      uint32_t e2 = 0;
+      if (k + 1 < nk) {
+        issue(Pn{}, gk + WAVES, e1, ln);
+        if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
+      }
+      compute(tag, gk, e0, ln);
+      wait_vm<NST>();
+      e0 = e1;
+      e1 = e2;
     };
     for (int k = 0; k < nk; k += 2) {
       step(S0t{}, k);
@@ -1129,7 +1352,7 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
 constexpr int kDqChunk = 256;  // tokens per work item of the sparse dQ kernel
 
 struct BwdWs {
-  size_t delta, rowstat, lists, dqp, dbl, dummy, total;
+  size_t delta, rowstat, lists, dqp, dbl, dsr, dso, dummy, total;
 };
 
 static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
@@ -1148,6 +1371,10 @@ static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
     at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
     w.dbl = at;
     at += align_up(size_t(d.B) * d.Hkv * d.N * size_t(topk > 0 ? topk : 1) * d.G() * sizeof(float));
+    w.dsr = at;
+    at += align_up(size_t(d.B) * d.Hkv * d.N * size_t(topk > 0 ? topk : 1) * d.G() * KT * sizeof(bf16_t));
+    w.dso = at;
+    at += align_up(rows * KT * sizeof(bf16_t));
     w.dummy = at;
     at += align_up(512);
   }
@@ -1163,7 +1390,7 @@ template <int D, int G>
 static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStream_t s) {
   // persistent: one workgroup per compute unit (the LDS stages fill it)
   const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
-  SAS_LAUNCH("bwd_dq_sel", (bwd_dq_sel_kernel<D, G>), dim3(grid), dim3(512), 0, s, a, L);
+  SAS_LAUNCH("bwd_dq_ds", (bwd_dq_ds_kernel<D, G>), dim3(grid), dim3(1024), 0, s, a, L);
   SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbl,
              L.pos, L.ents_per_pair, a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, a.scale,
              rows);
@@ -1228,6 +1455,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
     a.rowstat = reinterpret_cast<const float*>(w + W.rowstat);
     a.dbl = reinterpret_cast<float*>(w + W.dbl);
+    a.dsr = reinterpret_cast<bf16_t*>(w + W.dsr);
+    a.dso = reinterpret_cast<bf16_t*>(w + W.dso);
     a.dummy = reinterpret_cast<float*>(w + W.dummy);
   }
   a.Hq = d.Hq;
