@@ -184,12 +184,13 @@ def bench_decode(torch, w, steps, warmup, dense=False):
 
 # Algorithmic work of the matrix-core kernels per attended (query row, key)
 # pair: the forward's S = QK^T and PV (4D flops; fwd_sel at sparse scope,
-# fwd_mfma at full scope); the dQ kernel's S and dP recompute plus dS K (6D;
-# bwd_dq_sel / bwd_dq); the dK/dV kernel's S and dP recompute plus P^T dO and
-# dS^T Q (8D).
-KERNEL_FLOPS_PER_PAIR = {"fwd_sel": 4, "fwd_mfma": 4, "bwd_dq_sel": 6, "bwd_dq": 6, "bwd_dkdv": 8}
+# fwd_mfma at full scope); at sparse scope the dQ kernel's dS K over the dS the
+# dK/dV kernel recorded (2D; bwd_dq_ds), at full scope its S and dP recompute
+# plus dS K (6D; bwd_dq); the dK/dV kernel's S and dP recompute plus P^T dO
+# and dS^T Q (8D).
+KERNEL_FLOPS_PER_PAIR = {"fwd_sel": 4, "fwd_mfma": 4, "bwd_dq_ds": 2, "bwd_dq": 6, "bwd_dkdv": 8}
 KERNEL_SOURCES = {"fwd_sel": "attn_fwd_sel.hip", "fwd_mfma": "attn_fwd_mfma.hip",
-                  "bwd_dq_sel": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
+                  "bwd_dq_ds": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
                   "bwd_dkdv": "attn_bwd_mfma.hip"}
 
 

@@ -10,8 +10,7 @@
 // block-wise aggregation of the log-gate gradient.
 //
 // Kernels:
-//   delta      Delta per row (and, sparse scope, the row's base-2 softmax
-//              offsets for its own and its gated blocks).
+//   delta      Delta per row.
 //   dkdv       KV-major: a workgroup owns one block (64 keys, 16 per wave) of
 //              one KV head and streams the query rows that attend it, 64 rows
 //              per step: the own block's rows (causal) and every later row
@@ -19,8 +18,10 @@
 //              scope, sel_lists.hip).  Lane = key layout (S = Q K^T), so dV =
 //              P^T dO and dK = dS^T Q contract over rows with P and dS straight
 //              from registers.
-//   dq_sel     sparse scope, key-major over the same lists with lane = row:
-//              per (row, selected block) the block's dQ share and dbeta.
+//              Sparse scope: the step's dS rows and per-row dbeta are also
+//              recorded per list entry (and per own-block row).
+//   dq_ds      sparse scope, key-major over the same lists: per (row,
+//              selected block) the dQ share dS K from the recorded dS rows.
 //   rows       sparse scope, per row: dq = sum of its dQ shares, and
 //              ds = dbeta - g sum(dbeta).
 //   dq         full scope, query-major like the forward (lane = row, S^T =
@@ -62,7 +63,6 @@ struct BwdArgs {
   float* dbl;        // workspace [pairs, list entries, G]: dbeta per list entry and head (sparse)
   bf16_t* dsr;       // workspace [pairs, list entries, G, 64]: dS of the entry's block (sparse)
   bf16_t* dso;       // workspace [B, Hq, N, 64]: dS of the row's own block (sparse)
-  const float* rowstat;  // workspace [B, Hq, N] x {Delta, -lse log2e, -(lse + LSE_s) log2e, 0} (sparse)
   float* dummy;          // workspace line that absorbs masked stores
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
@@ -72,10 +72,7 @@ struct BwdArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __restrict__ o,
                                                              const bf16_t* __restrict__ dout,
-                                                             float* __restrict__ delta,
-                                                             const float* __restrict__ lse,
-                                                             const float* __restrict__ lse_s,
-                                                             float4* __restrict__ rowstat, size_t rows) {
+                                                             float* __restrict__ delta, size_t rows) {
   constexpr int LPR = D / 8;  // lanes per row, 16-byte loads
   const size_t row = size_t(blockIdx.x) * (256 / LPR) + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
@@ -91,15 +88,7 @@ __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __res
     }
   }
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += shfl_xor(acc, off);
-  if (row < rows && sub == 0) {
-    delta[row] = acc;
-    // sparse scope: the row's softmax offsets in base 2 for its own block
-    // (-lse) and for a gated block (-(lse + LSE_s); the block's score is added)
-    if (rowstat) {
-      const float l = lse[row];
-      rowstat[row] = make_float4(acc, -l * kLog2e, -(l + lse_s[row]) * kLog2e, 0.f);
-    }
-  }
+  if (row < rows && sub == 0) delta[row] = acc;
 }
 
 // --------------------------------------------------------------- dK / dV ----
@@ -428,273 +417,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   }
 }
 
-// ------------------------------------------------------- dQ, sparse scope ----
-// Key-major over the selection lists.  Persistent workgroups walk the work
-// items (a block's own tokens, or a run of list entries within one token
-// span; items of a span run together, so their query rows are shared in
-// cache).  For an item of block m each wave owns 16 of its rows per step and
-// all 64 keys (lane = row, S^T = K Q^T with K read from the block's LDS tile,
-// dP^T = V dO^T with V held in registers), so dS^T never leaves the wave: its
-// C fragments are the B operand of dQ^T = K^T dS^T, with the keys of a 32-wide
-// k step in the order {4 lq + i, 16 + 4 lq + i}, and K^T comes from the K tile
-// through transposing LDS reads in the same order.  Per row the block
-// contributes dbeta = sum of dS over its keys (gated rows) and a dQ share,
-// both written to the row's slot: the rank of m among the row's selected
-// blocks (topk for the own block's dQ share).  Waves run independent
-// two-stage pipelines on private LDS stages, with a fixed count of stores per
-// step so the wait for the next stage's loads does not wait for them.
-template <int D, int G>
-__global__ __launch_bounds__(512) void bwd_dq_sel_kernel(BwdArgs a, SelLists L) {
-  using namespace tiles;
-  constexpr int WAVES = 8;
-  constexpr int KS = D / 32;
-  constexpr int ND = D / 16;
-  constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int RPL = 64 / CH;           // rows per wave-wide 16-byte access
-  constexpr int STG = 2 * 16 * D;        // per wave stage: Q | dO of 16 rows
-  constexpr int NLD = 16 / RPL;          // wave DMA instructions per operand
-  constexpr int NSTORE = NLD + 1;        // stores per step: dQ share rows + dbeta
-  static_assert(KT * D <= WAVES * STG, "V tile fits in the stage area");
-  constexpr int WST = D + 8;             // row stride (16-bit units) of the dQ staging rows
-  static_assert(16 * WST <= STG, "dQ staging fits in a stage");
-  static_assert(16 % G == 0, "a 16-row group holds whole tokens");
-  __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];   // K, row-major, swizzled
-  __shared__ __attribute__((aligned(16))) uint4 KTa[2 * ND * 64];  // A operands of dQ^T, per lane
-  __shared__ __attribute__((aligned(16))) uint16_t S0[WAVES * STG];
-  __shared__ __attribute__((aligned(16))) uint16_t S1[WAVES * STG];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = a.N, C = a.C, pairs = a.n_pairs;
-  const int topk1 = a.topk + 1;
-  const float c1 = a.scale * kLog2e;
-  const int total = pairs * L.maxitems;
-  using S0t = std::integral_constant<int, 0>;
-  using S1t = std::integral_constant<int, 1>;
-
-  for (int vi = blockIdx.x; vi < total; vi += gridDim.x) {
-    const int pair = vi % pairs, item = vi / pairs;
-    if (item >= int(L.nitems[pair])) continue;
-    const uint4 it = reinterpret_cast<const uint4*>(L.items)[size_t(pair) * L.maxitems + item];
-    const int m = int(it.x & 0xffffu);
-    const bool own_item = (it.x >> 31) != 0;
-    const int b = pair / a.Hkv, g = pair % a.Hkv;
-    const int j0 = m * KT;
-    const int ntok = own_item ? min(KT, N - j0) : int(it.z - it.y);
-    const uint32_t* ep = L.ents + size_t(pair) * L.ents_per_pair + it.y;
-    const int nrows = ntok * G;
-    const int ngroups = (nrows + 15) >> 4;
-    const int nk = ngroups > wave ? (ngroups - wave + WAVES - 1) / WAVES : 0;
-    const size_t hrow0 = (size_t(b) * a.Hq + g * G) * N;
-
-    // ---- K tile (kept) and V tile (over stage 0) into LDS; V operands of
-    // dP^T into registers; the A operands of dQ^T (K^T, keys of k step kk in
-    // the order {4 lq + i, 16 + 4 lq + i}) laid out per lane, so the step reads
-    // them with one 16-byte access each.
-    __syncthreads();  // the previous item is done with the tiles and stages
-    {
-      const bf16_t* kh = a.k + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-      const bf16_t* vh = a.v + (size_t(b) * a.Hkv + g) * size_t(N) * D;
-      constexpr int KPIECE = KT * D * 2 / 1024;
-      for (int j = wave; j < KPIECE; j += WAVES) {
-        const int r = RPL * j + lane / CH, pc = lane % CH;
-        const size_t key = size_t(min(j0 + r, N - 1));
-        const int c = (pc ^ k_swz<D>(r)) * 8;
-        dma16_to_lds(kh + key * D + c, Ksh + j * 512);
-        dma16_to_lds(vh + key * D + c, S0 + j * 512);
-      }
-    }
-    wait_vm<0>();
-    __syncthreads();
-    uint4 vf[4][KS];
-    {
-      const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int r = 16 * kt + lr;
-          vf[kt][ks] = *reinterpret_cast<const uint4*>(S0 + r * D + (((4 * ks + lq) ^ k_swz<D>(r)) * 8));
-        }
-      for (int u = wave; u < 2 * ND; u += WAVES) {
-        const int kk = u / ND, md = u % ND;
-        const int ka = 32 * kk + 4 * lq + (lr >> 2), kb = ka + 16;
-        const int col = 16 * md + 4 * (lr & 3);
-        const uint2 k0 = lds_read_tr16(Ksh + ka * D + ((((col >> 3) ^ k_swz<D>(ka)) << 3) + (col & 7)));
-        const uint2 k1 = lds_read_tr16(Ksh + kb * D + ((((col >> 3) ^ k_swz<D>(kb)) << 3) + (col & 7)));
-        KTa[u * 64 + lane] = make_uint4(k0.x, k0.y, k1.x, k1.y);
-      }
-    }
-    __syncthreads();  // V tile read before stage 0 is reloaded; K^T operands written
-    if (nk == 0) continue;
-
-    // Lane constants of the item.  Row r_j = RPL j + lane / CH of a group is
-    // loaded and stored by this lane at chunk lane % CH; the head of a row is
-    // r % G, so everything but the token is fixed per item.
-    size_t qoff[NLD], soff[NLD];
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int r = RPL * j + lane / CH, pc = lane % CH;
-      const size_t hr = hrow0 + size_t(r % G) * N;
-      qoff[j] = hr * D + ((pc ^ k_swz<D>(r)) * 8);
-      soff[j] = hr * size_t(topk1) * D + pc * 8;  // slot row of token 0, this lane's chunk
-    }
-    const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
-    // dbeta records of the item's list entries: [entry][head], so row q of the
-    // item (entry q / G, head q % G) is float q
-    float* dbl_item = a.dbl + (size_t(pair) * L.ents_per_pair + it.y) * G;
-
-    // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
-    auto entry = [&](int gk, int lr) -> uint32_t {
-      const int p = min((16 * gk + lr) / G, ntok - 1);
-      // one load either way (own items read a valid dummy word), so the
-      // result is a select rather than a branch around a load
-      const uint32_t v = (own_item ? L.ents : ep)[own_item ? 0 : p];
-      return own_item ? (uint32_t(j0 + p) | (uint32_t(a.topk) << 23)) : v;
-    };
-    auto stg = [&](auto tag) -> uint16_t* {
-      if constexpr (decltype(tag)::value == 0) return S0 + wave * STG;
-      else return S1 + wave * STG;
-    };
-    auto issue = [&](auto tag, int gk, uint32_t e, int ln) {
-      uint16_t* st = stg(tag);
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int r = RPL * j + ln / CH;
-        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
-        const uint32_t t = 16 * gk + r < nrows ? (er & 0x7fffffu) : 0u;
-        const size_t off = qoff[j] + size_t(t) * D;
-        dma16_to_lds(a.q + off, st + j * 512);
-        dma16_to_lds(a.dout + off, st + 16 * D + j * 512);
-      }
-    };
-    struct Stat {
-      float4 rs;
-      float sc;
-    };
-    auto load_stat = [&](uint32_t e) -> Stat {
-      const size_t gr = rbase + (e & 0x7fffffu);
-      Stat s;
-      s.rs = reinterpret_cast<const float4*>(a.rowstat)[gr];
-      s.sc = own_item ? 0.f : a.scores[gr * C + m];
-      return s;
-    };
-
-    auto compute = [&](auto tag, int gk, uint32_t e, const Stat& stt, int ln) {
-      const uint16_t* Qs = stg(tag);
-      const uint16_t* dOs = Qs + 16 * D;
-      const int lr = ln & 15, lq = ln >> 4;
-      const int qsw = k_swz<D>(lr);  // = k_swz(16 kt + lr) for every kt
-      f32x4 sacc[4], pacc[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = lr * D + (((4 * ks + lq) ^ qsw) * 8);
-        const uint4 qb = *reinterpret_cast<const uint4*>(Qs + off);
-        const uint4 ob = *reinterpret_cast<const uint4*>(dOs + off);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(Ksh + 16 * kt * D + off);
-          sacc[kt] = mfma16(ka, qb, sacc[kt]);
-          pacc[kt] = mfma16(vf[kt][ks], ob, pacc[kt]);
-        }
-      }
-      const bool valid = 16 * gk + lr < nrows;
-      const int t = int(e & 0x7fffffu);
-      // keys a row may see: all (gated block), key <= t (own block), none
-      // (rows past the item)
-      const int tlim = valid ? (own_item ? t : 0x7fffffff) : -1;
-      const float off = own_item ? stt.rs.y : fmaf(stt.sc, kLog2e, stt.rs.z);
-      const float dl = stt.rs.x;
-      float db = 0.f;
-      uint4 dsb[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float d[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kt = 2 * kk + h;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = j0 + 16 * kt + 4 * lq + i <= tlim ? fmaf(sacc[kt][i], c1, off) : kNegInf;
-            const float y = exp2_hw(x) * (pacc[kt][i] - dl);
-            db += y;
-            d[4 * h + i] = y;
-          }
-        }
-        dsb[kk] = make_uint4(pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3]), pack_bf16(d[4], d[5]),
-                             pack_bf16(d[6], d[7]));
-      }
-      db += shfl_xor(db, 16);
-      db += shfl_xor(db, 32);
-      f32x4 dqa[ND];
-#pragma unroll
-      for (int md = 0; md < ND; ++md) dqa[md] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int md = 0; md < ND; ++md) dqa[md] = mfma16(KTa[(kk * ND + md) * 64 + ln], dsb[kk], dqa[md]);
-      // dQ^T fragments to the wave's stage (Q and dO consumed) as rows of
-      // stride WST, then whole rows out, so every store writes full lines.
-      // dbeta goes to the list entry's record (16 consecutive floats per step).
-      // Rows past the item, and dbeta of own rows, go to the dummy line: each
-      // step issues the same count of stores.
-      uint16_t* W = stg(tag);
-#pragma unroll
-      for (int md = 0; md < ND; ++md) {
-        uint2 w;
-        w.x = pack_bf16(dqa[md][0], dqa[md][1]);
-        w.y = pack_bf16(dqa[md][2], dqa[md][3]);
-        *reinterpret_cast<uint2*>(W + lr * WST + 16 * md + 4 * lq) = w;
-      }
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int r = RPL * j + ln / CH, cc = ln % CH;
-        const uint32_t er = uint32_t(__shfl(int(e), r, 64));
-        const uint4 v = *reinterpret_cast<const uint4*>(W + r * WST + cc * 8);
-        bf16_t* dp = 16 * gk + r < nrows
-                         ? a.dqp + soff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
-                         : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
-        *reinterpret_cast<uint4*>(dp) = v;
-      }
-      float* dbp = (valid && !own_item) ? dbl_item + 16 * gk + lr : a.dummy + 64;
-      *dbp = db;
-    };
-
-    // pipeline over this wave's groups gk = wave + WAVES k
-    uint32_t e0 = entry(wave, lane & 15);
-    uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
-    issue(S0t{}, wave, e0, lane);
-    Stat st0 = load_stat(e0), st1 = st0;
-    wait_vm<0>();
-    auto step = [&](auto tag, int k) {
-      using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int gk = wave + WAVES * k;
-      uint32_t e2 = 0;
-      if (k + 1 < nk) {
-        issue(Pn{}, gk + WAVES, e1, ln);
-        st1 = load_stat(e1);
-        if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
-      }
-      compute(tag, gk, e0, st0, ln);
-      wait_vm<NSTORE>();
-      e0 = e1;
-      e1 = e2;
-      st0 = st1;
-    };
-    for (int k = 0; k < nk; k += 2) {
-      step(S0t{}, k);
-      if (k + 1 < nk) step(S1t{}, k + 1);
-    }
-  }
-}
-
 // --------------------------------------------------- dQ from dS, sparse scope ----
 // dQ shares from the dS rows the dK/dV kernel recorded: per (row, selected
 // block) the share is dS[row, keys of m] K_m.  Persistent workgroups walk the
@@ -996,7 +718,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
 // only, written to ds as scratch), dZ packed to bf16 for the dQ product.  Own
 // blocks run in a second, masked loop.  The epilogue writes dq and turns the
 // row's dbeta into ds = dbeta - g sum(dbeta) (dense over the history).  This
-// is the full-scope dQ; sparse scope is key-major (bwd_dq_sel_kernel).
+// is the full-scope dQ; sparse scope is key-major (bwd_dq_ds_kernel).
 template <int D, int G, int NSUB, int WAVES, int NST>
 __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   using namespace tiles;
@@ -1352,7 +1074,7 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
 constexpr int kDqChunk = 256;  // tokens per work item of the sparse dQ kernel
 
 struct BwdWs {
-  size_t delta, rowstat, lists, dqp, dbl, dsr, dso, dummy, total;
+  size_t delta, lists, dqp, dbl, dsr, dso, dummy, total;
 };
 
 static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
@@ -1361,8 +1083,6 @@ static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
   w.delta = 0;
   size_t at = align_up(rows * sizeof(float));
   if (sparse) {
-    w.rowstat = at;
-    at += align_up(rows * sizeof(float4));
     size_t lb = 0;
     sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kDqChunk, nullptr, &lb);
     w.lists = at;
@@ -1409,7 +1129,7 @@ template <int D, int G, bool SPARSE>
 static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s) {
   const size_t rows = size_t(B) * a.Hq * a.N;
   SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
-             dim3(256), 0, s, a.o, a.dout, a.delta, a.lse, a.lse_s, (float4*)a.rowstat, rows);
+             dim3(256), 0, s, a.o, a.dout, a.delta, rows);
   if (SPARSE) {
     const hipError_t e = launch_sel_lists(a.idx, L, B, a.Hkv, a.N, a.C, a.topk, KT, s);
     if (e != hipSuccess) return e;
@@ -1453,7 +1173,6 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.selbits = L.bits;
     a.selpre = L.pre;
     a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
-    a.rowstat = reinterpret_cast<const float*>(w + W.rowstat);
     a.dbl = reinterpret_cast<float*>(w + W.dbl);
     a.dsr = reinterpret_cast<bf16_t*>(w + W.dsr);
     a.dso = reinterpret_cast<bf16_t*>(w + W.dso);

@@ -3,12 +3,12 @@
   python -m trainable_block_sparse_sas_amd.profsum stats DB --cmd "..."
       kernel-trace table: launches, average and total duration per kernel.
   python -m trainable_block_sparse_sas_amd.profsum traffic --fetch DB --write DB
-         --kernel bwd_dq_sel --workload train-32k-sparse --cmd-fetch "..." --cmd-write "..."
+         --kernel bwd_dkdv --workload train-32k-sparse --cmd-fetch "..." --cmd-write "..."
       HBM bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE
       run, each scaled by what the same counter reads for a plain copy kernel
       that reads and writes 1 GiB (bench.py --copy-probe).
 
-  python -m trainable_block_sparse_sas_amd.profsum counters DB --cmd "..." --match fwd_sel bwd_dq_sel ...
+  python -m trainable_block_sparse_sas_amd.profsum counters DB --cmd "..." --match fwd_sel bwd_dkdv ...
       per-kernel counter totals per dispatch (summed over counter instances)
       with the kernel's duration; SQ_INSTS_MFMA gives the executed matrix
       work (each v_mfma_f32_16x16x32_bf16 is 16384 flops).
@@ -26,7 +26,7 @@ import sqlite3
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 KERNEL_SOURCES = {"fwd_sel": "attn_fwd_sel.hip", "fwd_mfma": "attn_fwd_mfma.hip",
-                  "bwd_dq_sel": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
+                  "bwd_dq_ds": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
                   "bwd_dkdv": "attn_bwd_mfma.hip"}
 
 
