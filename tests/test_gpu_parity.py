@@ -120,6 +120,11 @@ TOPK_CASES = [
     (1500, 1, 1, 32),
     (2047, 1, None, 16),
     (8191, 1, None, 32),
+    (8191, 1, None, 64),
+    (16000, 1, None, 8),
+    (3000, 1, None, 17),
+    (12000, 1, None, 1),
+    (2500, 3, 1, 40),
     (5000, 1, None, 256),
 ]
 

@@ -6,10 +6,12 @@
 // head-index order.  Exactly min(K, c) blocks are kept, ordered by score
 // descending with ties to the lower block index (-0.0 == +0.0, NaN == -inf).
 //
-// Selection is sort-free: an MSB-first radix select over the order-preserving
-// uint32 key finds the K-th largest key T in four 8-bit passes (LDS histogram),
-// every key > T is kept and the keys equal to T are taken in index order.
-// Only the K survivors are then ranked, by counting.
+// Rows of up to 1024 candidates (and long rows with K > 64) use an MSB-first
+// radix select over the order-preserving uint32 key: it finds the K-th largest
+// key T in four 8-bit passes (LDS histogram), every key > T is kept and the
+// keys equal to T are taken in index order; only the K survivors are then
+// ranked, by counting.  Long rows with K <= 64 (decode) merge sorted runs in
+// registers instead, with no histogram passes and no atomics.
 #include "common.h"
 #include "internal.h"
 
@@ -371,6 +373,284 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
   }
 }
 
+// ---- long rows, K <= 64: sorted runs merged in registers --------------------
+// One row per workgroup of 16 waves.  Each lane sorts its PER composite keys
+// (score key << 32 | ~block: all distinct, larger = higher score, ties to the
+// lower block; an invalid candidate is 0) descending with a bitonic network,
+// keeps its best E = min(PER, KP) and groups of R = KP / E lanes build sorted
+// runs of KP keys (element q E + r of a run: lane q of the group, register r).
+// Two sorted runs A and B reduce to the KP largest keys of their union by
+// max(A[j], B[KP - 1 - j]), a bitonic sequence that the half-cleaners sort
+// again; both partner groups compute it (one sees the sequence reversed,
+// which sorts to the same run), so after log2(64 / R) rounds every group of
+// the wave holds the wave's best KP keys.  The 16 wave runs are merged the
+// same way through LDS.  The final run is the answer in rank order.
+
+// x of lane (lane ^ mask) without LDS permutes: within a 16-lane row the
+// xor is composed from DPP moves (row_half_mirror = xor 7, quad_perm = xor
+// 1..3, row_ror:8 = xor 8), across rows from the gfx950 row swaps (after
+// v_permlane16_swap(x, x) the first result holds row r ^ 1's x in the odd
+// rows and the second in the even rows; likewise for halves with the 32-lane
+// swap).  Every call site passes a mask that is constant after unrolling, so
+// the branches fold away.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t lanes_xor(uint32_t x, int mask, int lane) {
+  if (mask & 4) x = dpp<0x141>(x);
+  const int q = (mask & 3) ^ ((mask & 4) ? 3 : 0);
+  if (q == 1) x = dpp<0xB1>(x);       // quad_perm [1,0,3,2]
+  else if (q == 2) x = dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  else if (q == 3) x = dpp<0x1B>(x);  // quad_perm [3,2,1,0]
+  if (mask & 8) x = dpp<0x128>(x);    // row_ror:8
+  if (mask & 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = (lane & 16) ? a[0] : a[1];
+  }
+  if (mask & 32) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = (lane & 32) ? a[0] : a[1];
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int mask) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = lanes_xor(uint32_t(v), mask, lane);
+  const uint32_t hi = lanes_xor(uint32_t(v >> 32), mask, lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint32_t shfl_xor_key(uint32_t v, int mask) {
+  return lanes_xor(v, mask, threadIdx.x & 63);
+}
+
+// Sorts the bitonic run held by each group of R lanes (E keys per lane)
+// descending: half-cleaners at element distances KP/2 .. 1 (KP = R E).
+template <int E, int R, typename T>
+__device__ __forceinline__ void bitonic_clean(T (&v)[E], int lane) {
+#pragma unroll
+  for (int d = R * E / 2; d >= 1; d >>= 1) {
+    if (d >= E) {
+      const int dl = d / E;
+      const bool lower = (lane & dl) == 0;
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const T p = shfl_xor_key(v[r], dl);
+        v[r] = lower ? (v[r] > p ? v[r] : p) : (v[r] < p ? v[r] : p);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        if ((r & d) == 0) {
+          const T a = v[r], b = v[r + d];
+          v[r] = a > b ? a : b;
+          v[r + d] = a > b ? b : a;
+        }
+    }
+  }
+}
+
+// Every group of R lanes holds a sorted run of R E keys; afterwards every
+// group holds the R E largest keys of all 64 / R runs of the wave, sorted.
+template <int E, int R, typename T>
+__device__ __forceinline__ void merge_wave_runs(T (&v)[E], int lane) {
+#pragma unroll
+  for (int D = R; D < 64; D <<= 1) {
+    T p[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) p[r] = shfl_xor_key(v[E - 1 - r], D | (R - 1));
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = v[r] > p[r] ? v[r] : p[r];
+    bitonic_clean<E, R>(v, lane);
+  }
+}
+
+// Sorted runs of ML E keys over groups of ML lanes from sorted runs of half
+// that length (one bitonic merge per doubling), for ML = 2 .. R.
+template <int E, int ML, int R, typename T>
+__device__ __forceinline__ void build_runs(T (&v)[E], int lane) {
+  if constexpr (ML <= R) {
+    const bool lower = (lane & (ML - 1)) < ML / 2;
+    T p[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) p[r] = shfl_xor_key(v[E - 1 - r], ML - 1);
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = lower ? (v[r] > p[r] ? v[r] : p[r]) : (v[r] < p[r] ? v[r] : p[r]);
+    bitonic_clean<E, ML>(v, lane);
+    build_runs<E, 2 * ML, R, T>(v, lane);
+  }
+}
+
+// Merges the 16 wave runs in runs[0] (each R lanes x E keys, sorted) into
+// one, GPW = 64 / R runs per merging wave per round; returns the buffer that
+// holds the result in its row 0 (visible to every wave on return).
+template <int E, int R, int KP, typename T>
+__device__ __forceinline__ int merge_block_runs(T (*runs)[16][KP], int w, int lane) {
+  constexpr int GPW = 64 / R;
+  static_assert(GPW >= 2, "a round must reduce the run count");
+  int nruns = 16, buf = 0;
+  while (nruns > 1) {
+    const int nw = (nruns + GPW - 1) / GPW;
+    __syncthreads();
+    if (w < nw) {
+      const int src = w * GPW + lane / R;
+      T v[E];
+#pragma unroll
+      for (int r = 0; r < E; ++r) v[r] = src < nruns ? runs[buf][src][(lane % R) * E + r] : T(0);
+      merge_wave_runs<E, R, T>(v, lane);
+      if (lane < R)
+#pragma unroll
+        for (int r = 0; r < E; ++r) runs[buf ^ 1][w][lane * E + r] = v[r];
+    }
+    buf ^= 1;
+    nruns = nw;
+  }
+  __syncthreads();
+  return buf;
+}
+
+// A filter runs first.  Take each lane's largest score key (32-bit, the score
+// alone): if tau is the K-th largest of these lane maxima, K lanes hold a key
+// whose score key is >= tau, so the K-th largest key and everything above it
+// has a score key >= tau, and every key below is out.  With random scores the
+// survivors are barely more than K; when they fit one wave (at most 64) each
+// survivor's rank is counted directly.  Otherwise (many equal scores) the
+// whole row goes through the run merge above.
+template <int PER, int KP>
+__global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict__ scores,
+                                                         int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ cache_len,
+                                                         int Hkv, int hpr, int Nq, int C, int block,
+                                                         int topk) {
+  constexpr int E = PER < KP ? PER : KP;  // keys per lane in a run
+  constexpr int R = KP / E;               // lanes per run
+  constexpr int E1 = KP <= 8 ? 1 : KP / 8;  // filter: 32-bit runs of KP as E1 x R1
+  constexpr int R1 = KP / E1;
+  static_assert(R <= 32 && (KP & (KP - 1)) == 0 && (PER & (PER - 1)) == 0, "run shape");
+  __shared__ uint64_t runs[2][16][KP];
+  __shared__ uint32_t fruns[2][16][KP];
+  __shared__ uint64_t surv[64];
+  __shared__ uint32_t rank[64];
+  __shared__ int wcnt[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long row = blockIdx.x;
+  const long t = row % Nq, bg = row / Nq;
+  const int b = int(bg / Hkv), g = int(bg % Hkv);
+  // score loads first: their addresses do not depend on cache_len
+  float u[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int m = (i * 16 + w) * 64 + lane;
+    u[i] = 0.f;
+    if (m < C) {
+      const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C + m;
+      u[i] = base[0];
+      for (int h = 1; h < hpr; ++h) u[i] = u[i] + base[size_t(h) * Nq * C];
+    }
+  }
+  if (threadIdx.x < 64) rank[threadIdx.x] = 0;
+  int c;
+  if (cache_len) {
+    const int len = cache_len[b];
+    c = len > 0 ? (len - 1) / block : 0;
+  } else {
+    c = int(t / block);
+  }
+  c = c < C ? c : C;
+  const int K = topk < c ? topk : c;
+  int32_t* out = idx + size_t(row) * topk;
+  if (K == 0) {
+    for (int e = threadIdx.x; e < topk; e += 1024) out[e] = -1;
+    return;
+  }
+  uint64_t key[PER];
+  uint32_t fmax = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int m = (i * 16 + w) * 64 + lane;
+    const uint32_t hk = m < c ? score_key(u[i]) : 0u;  // valid score keys are > 0
+    key[i] = m < c ? (uint64_t(hk) << 32) | uint32_t(~uint32_t(m)) : 0ull;
+    fmax = fmax > hk ? fmax : hk;
+  }
+  // ---- filter (candidate m < 1024 sits alone on thread m, so at least K
+  // lanes hold a valid key): the wave's KP largest lane maxima, then the row's
+  uint32_t f[1] = {fmax};
+  build_runs<1, 2, KP, uint32_t>(f, lane);
+  if constexpr (KP < 64) merge_wave_runs<1, KP, uint32_t>(f, lane);
+  if (lane < KP) fruns[0][w][lane] = f[0];
+  int buf = merge_block_runs<E1, R1, KP, uint32_t>(fruns, w, lane);
+  const uint32_t tau = fruns[buf][0][K - 1];
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(uint32_t(key[i] >> 32) >= tau));
+  if (lane == 0) wcnt[w] = cnt;
+  __syncthreads();
+  int S = 0, before = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    before += v < w ? wcnt[v] : 0;
+    S += wcnt[v];
+  }
+  if (S <= 64) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool in = uint32_t(key[i] >> 32) >= tau;
+      const unsigned long long bt = __ballot(in);
+      if (in) surv[before + __popcll(bt & lt)] = key[i];
+      before += __popcll(bt);
+    }
+    __syncthreads();
+    // rank of survivor `lane`: wave w counts the larger ones among 4w .. 4w+3
+    if (lane < S) {
+      const uint64_t me = surv[lane];
+      uint32_t larger = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = 4 * w + j;
+        larger += (o < S && surv[o] > me) ? 1u : 0u;
+      }
+      if (larger) atomicAdd(&rank[lane], larger);
+    }
+    __syncthreads();
+    if (w == 0) {
+      if (lane < S && rank[lane] < uint32_t(K)) out[rank[lane]] = int(~uint32_t(surv[lane]));
+      if (lane >= K && lane < topk) out[lane] = -1;
+    }
+    return;
+  }
+
+  // ---- full run merge
+  // the lane's keys, descending
+#pragma unroll
+  for (int k = 2; k <= PER; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool desc = (i & k) == 0;
+          const uint64_t a = key[i], bb = key[l];
+          const bool sw = desc ? a < bb : a > bb;
+          key[i] = sw ? bb : a;
+          key[l] = sw ? a : bb;
+        }
+      }
+  uint64_t v[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = key[r];
+  build_runs<E, 2, R, uint64_t>(v, lane);
+  merge_wave_runs<E, R, uint64_t>(v, lane);
+  if (lane < R)
+#pragma unroll
+    for (int r = 0; r < E; ++r) runs[0][w][lane * E + r] = v[r];
+  buf = merge_block_runs<E, R, KP, uint64_t>(runs, w, lane);
+  for (int e = threadIdx.x; e < topk; e += 1024)
+    out[e] = e < K ? int(~uint32_t(runs[buf][0][e])) : -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
@@ -383,6 +663,24 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
   } else if (C <= 1024) {
     SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
+  } else if (topk <= 64 && C <= 16384) {
+    // candidates per lane: just enough for C (16 waves x 64 lanes x PER);
+    // run length: the power of two at or above K (at least 8)
+#define SAS_TOPK_RUNS(PER, KP)                                                                          \
+  SAS_LAUNCH("topk_runs", (topk_runs_kernel<PER, KP>), dim3(rows), dim3(1024), 0, s, scores, idx, cache_len, \
+             Hkv, hpr, Nq, C, block, topk)
+#define SAS_TOPK_RUNS_KP(PER)                        \
+  if (topk <= 8) SAS_TOPK_RUNS(PER, 8);               \
+  else if (topk <= 16) SAS_TOPK_RUNS(PER, 16);        \
+  else if (topk <= 32) SAS_TOPK_RUNS(PER, 32);        \
+  else SAS_TOPK_RUNS(PER, 64);
+    const int per = C <= 2048 ? 2 : C <= 4096 ? 4 : C <= 8192 ? 8 : 16;
+    if (per == 2) { SAS_TOPK_RUNS_KP(2) }
+    else if (per == 4) { SAS_TOPK_RUNS_KP(4) }
+    else if (per == 8) { SAS_TOPK_RUNS_KP(8) }
+    else { SAS_TOPK_RUNS_KP(16) }
+#undef SAS_TOPK_RUNS_KP
+#undef SAS_TOPK_RUNS
   } else {
     // candidates per lane: just enough for C (16 waves x 64 lanes x PER);
     // survivors per lane in the second stage: 16 K / 64
