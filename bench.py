@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import math
 import os
 import sys
@@ -78,8 +79,10 @@ class Timer:
 
         return _Span()
 
-    def ms(self, name):
+    def ms(self, name, median=False):
         ev = self.marks.get(name, [])
+        if median and ev:
+            return statistics.median(s.elapsed_time(e) for s, e in ev)
         return sum(s.elapsed_time(e) for s, e in ev) / max(1, len(ev))
 
 
@@ -135,51 +138,64 @@ def bench_train(torch, w, steps, warmup, scope_topk="cfg"):
 
 
 def bench_decode(torch, w, steps, warmup, dense=False):
+    """Decode step times, median over `steps` iterations, with the last-level
+    cache and L2 flushed before each timed span by a 1 GiB read (a sum over a
+    1 GiB buffer).  A 1 GiB write flush leaves the memory-side cache full of
+    dirty lines whose write-back then competes with the decode reads; its step
+    time is reported beside it."""
     from trainable_block_sparse_sas_amd.inputs import decode_inputs
     from trainable_block_sparse_sas_amd.pipeline import DecodeStep
+    from trainable_block_sparse_sas_amd import binding as sas
 
     q, kc, vc, lens = decode_inputs(w, device="cuda")
     step = DecodeStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, None if dense else w.topk, w.torch_dtype)
     step.pool(kc)  # pooled keys are kept beside the cache (prefill time)
     torch.cuda.synchronize()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > 256 MB last-level cache
-    tm = Timer(torch)
-    times = []
-    for i in range(warmup + steps):
-        flush.fill_(i & 0xFF)
-        if dense:
-            with tm.span("step"):
-                step.attend(q, kc, vc, lens)
-        else:
-            with tm.span("step"):
-                step.select(q, lens)
-                step.attend(q, kc, vc, lens)
-        if i == warmup - 1:
-            torch.cuda.synchronize()
-            tm.marks.clear()
-    torch.cuda.synchronize()
-    ms = tm.ms("step")
-    # Per stage (separate steps).
-    for i in range(max(3, steps // 2)):
-        flush.fill_(i & 0xFF)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
+    acc = torch.zeros(1, dtype=torch.float32, device="cuda")
+    tiny = torch.zeros(16, dtype=torch.float32, device="cuda")
+
+    def read_flush(i):
+        torch.sum(flush, dim=0, keepdim=True, out=acc)
+
+    def write_flush(i):
+        flush.fill_(float(i & 7))
+
+    def run_step():
         if not dense:
-            with tm.span("score"):
-                from trainable_block_sparse_sas_amd import binding as sas
-                sas.sas_score_blocks(q, None, step.kbar, step.u, lens, w.block, w.scale, group_sum=True, L=w.N)
-            with tm.span("topk"):
-                sas.sas_topk_select(step.u, step.idx, lens, 1, w.block)
-        flush.fill_((i + 7) & 0xFF)
-        with tm.span("attend"):
-            step.attend(q, kc, vc, lens)
-    torch.cuda.synchronize()
+            step.select(q, lens)
+        step.attend(q, kc, vc, lens)
+
+    def timed(fn, pre, n, name, tm):
+        for i in range(warmup + n):
+            pre(i)
+            if i < warmup:
+                fn()
+                continue
+            with tm.span(name):
+                fn()
+        torch.cuda.synchronize()
+        return tm.ms(name, median=True)
+
+    tm = Timer(torch)
+    ms = timed(run_step, read_flush, steps, "step", tm)
+    ms_wf = timed(run_step, write_flush, steps, "step_wf", tm)
+    floor = timed(lambda: tiny.fill_(1.0), read_flush, steps, "floor", tm)
+    ms_score = ms_topk = 0.0
+    if not dense:
+        ms_score = timed(lambda: sas.sas_score_blocks(q, None, step.kbar, step.u, lens, w.block, w.scale,
+                                                      group_sum=True, L=w.N), read_flush, steps, "score", tm)
+        ms_topk = timed(lambda: sas.sas_topk_select(step.u, step.idx, lens, 1, w.block), read_flush, steps,
+                        "topk", tm)
+    ms_attend = timed(lambda: step.attend(q, kc, vc, lens), read_flush, steps, "attend", tm)
     C = w.N // w.block
     kv_blocks = C if dense else (w.topk + 1)
     kv_bytes = w.B * w.Hkv * kv_blocks * w.block * w.D * 2 * 2
     kbar_bytes = 0 if dense else w.B * w.Hkv * C * w.D * 2
     return dict(ms_step=ms, tokens_per_s=w.B / (ms * 1e-3), kv_bytes=kv_bytes, kbar_bytes=kbar_bytes,
-                ms_score=tm.ms("score") if not dense else 0.0, ms_topk=tm.ms("topk") if not dense else 0.0,
-                ms_attend=tm.ms("attend"),
-                attend_gbs=kv_bytes / (tm.ms("attend") * 1e-3) / 1e9)
+                ms_step_write_flush=ms_wf, ms_event_floor=floor,
+                ms_score=ms_score, ms_topk=ms_topk, ms_attend=ms_attend,
+                attend_gbs=kv_bytes / (ms_attend * 1e-3) / 1e9)
 
 
 # Algorithmic work of the matrix-core kernels per attended (query row, key)
@@ -288,13 +304,17 @@ def bench_decodes(torch, wmap):
     dec = {}
     for name in ("decode-128k-b8", "decode-512k-b1"):
         wd = wmap[name]
-        r = bench_decode(torch, wd, 30, 5)
+        r = bench_decode(torch, wd, 50, 10)
         dec[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_step": round(r["ms_step"], 4),
+                     "ms_step_after_write_flush": round(r["ms_step_write_flush"], 4),
                      "ms_score": round(r["ms_score"], 4), "ms_topk": round(r["ms_topk"], 4),
                      "ms_attend": round(r["ms_attend"], 4), "attend_GBps_on_kv": round(r["attend_gbs"], 1),
+                     "ms_event_pair_floor": round(r["ms_event_floor"], 4),
+                     "timing": "median of 50 HIP-event spans, 1 GiB read flush before each span; "
+                               "stage spans each include the event-pair floor",
                      "topk": wd.topk}
         if name == "decode-512k-b1":
-            rd = bench_decode(torch, wd, 10, 2, dense=True)
+            rd = bench_decode(torch, wd, 20, 3, dense=True)
             dec[name]["dense_ms"] = round(rd["ms_step"], 4)
             dec[name]["dense_GBps"] = round(rd["attend_gbs"], 1)
             dec[name]["speedup_vs_dense"] = round(rd["ms_step"] / r["ms_step"], 2)

@@ -167,6 +167,7 @@ DECODE_CASES = [
     ("bf16-dense", "bf16", 8, 2, 128, 2048, 64, None),
     ("f32-d64", "f32", 4, 1, 64, 1024, 64, 2),
     ("bf16-block32", "bf16", 4, 2, 128, 1000, 32, 5),
+    ("bf16-g16-d64", "bf16", 16, 1, 64, 1280, 64, 3),
 ]
 
 

@@ -55,6 +55,35 @@ __device__ __forceinline__ float sum_xrows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// x of lane (lane ^ mask) without LDS permutes: within a 16-lane row the
+// xor is composed from DPP moves (row_half_mirror = xor 7, quad_perm = xor
+// 1..3, row_ror:8 = xor 8), across rows from the gfx950 row swaps (after
+// v_permlane16_swap(x, x) the first result holds row r ^ 1's x in the odd
+// rows and the second in the even rows; likewise for halves with the 32-lane
+// swap).  Every call site passes a mask that is constant after unrolling, so
+// the branches fold away.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t lanes_xor(uint32_t x, int mask, int lane) {
+  if (mask & 4) x = dpp<0x141>(x);
+  const int q = (mask & 3) ^ ((mask & 4) ? 3 : 0);
+  if (q == 1) x = dpp<0xB1>(x);       // quad_perm [1,0,3,2]
+  else if (q == 2) x = dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  else if (q == 3) x = dpp<0x1B>(x);  // quad_perm [3,2,1,0]
+  if (mask & 8) x = dpp<0x128>(x);    // row_ror:8
+  if (mask & 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = (lane & 16) ? a[0] : a[1];
+  }
+  if (mask & 32) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = (lane & 32) ? a[0] : a[1];
+  }
+  return x;
+}
+
 // Order-preserving map of an fp32 value to uint32 (larger float -> larger key).
 // -0.0 is folded onto +0.0 and NaN onto -inf first.
 __device__ __forceinline__ uint32_t score_key(float f) {

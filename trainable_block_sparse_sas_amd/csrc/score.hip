@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __r
   }
 }
 
-// Decode scores: one query token per sequence scans the pooled keys of its KV
+// Decode scores (fp32): one query token per sequence scans the pooled keys of its KV
 // head.  A K̄ row (D values) is read by LPR lanes with 16-byte loads, so a wave
 // covers 64/LPR rows per load; partial dots are reduced across those lanes.
 // The G query heads of the group are handled together; with group_sum the fp32
@@ -234,6 +234,83 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   }
 }
 
+// Decode scores on the matrix cores (bf16): the G query heads of a KV head
+// form the A operand (rows 0..G-1 of a 16-row tile, the rest zero) and 16
+// pooled keys the B operand, so one v_mfma_f32_16x16x32_bf16 per 32 columns
+// scores 16 blocks for all heads.  Lane (lq, lr) loads row lr of the tile at
+// the KS consecutive 16-byte chunks lq KS .. lq KS + KS - 1 (the head rows
+// use the same column order), i.e. 64 contiguous bytes per lane.  Each wave
+// scores TPW tiles with all loads issued first (they do not depend on
+// cache_len).  The heads' scores of block lr come out in lanes lr, lr + 16,
+// lr + 32, lr + 48 (4 heads each) and are added in head-index order.
+template <int D, int G, int TPW>
+__global__ __launch_bounds__(256) void score_decode_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kbar, float* __restrict__ out,
+    const int32_t* __restrict__ cache_len, int Hq, int Hkv, int L, int C, int block, float scale,
+    int group_sum) {
+  constexpr int KS = D / 32;
+  static_assert(G <= 16, "one 16-row tile of heads");
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = (blockIdx.x * 4 + wave) * TPW * 16;  // first block of the wave
+  const bf16_t* kb = kbar + (size_t(b) * Hkv + g) * size_t(C) * D;
+  uint4 kf[TPW][KS];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int m = m0 + tt * 16 + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[tt][ks] = m < C ? *reinterpret_cast<const uint4*>(kb + size_t(m) * D + (lq * KS + ks) * 8)
+                         : make_uint4(0, 0, 0, 0);
+  }
+  uint4 qa[KS];
+  {
+    const bf16_t* qr = q + (size_t(b) * Hq + g * G + (lr < G ? lr : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[ks] = lr < G ? *reinterpret_cast<const uint4*>(qr + (lq * KS + ks) * 8) : make_uint4(0, 0, 0, 0);
+  }
+  int len = cache_len[b];
+  len = len > L ? L : len;
+  const int c = len > 0 ? (len - 1) / block : 0;
+  const int c_eff = c < C ? c : C;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[ks], kf[tt][ks], acc);
+    const int m = m0 + tt * 16 + lr;
+    if (group_sum) {
+      // heads 4 lq .. 4 lq + 3 of block lr sit in lane (lq, lr)
+      float hv[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = acc[j];
+        hv[j] = x;
+        if constexpr (G > 4) hv[4 + j] = __shfl_xor(x, 16, 64);
+        if constexpr (G > 8) hv[8 + j] = __shfl_xor(x, 32, 64);
+        if constexpr (G > 12) hv[12 + j] = __shfl_xor(x, 48, 64);
+      }
+      if (lq == 0 && m < C) {
+        float u = kNegInf;
+        if (m < c_eff) {
+          u = hv[0] * scale;
+#pragma unroll
+          for (int h = 1; h < G; ++h) u = u + hv[h] * scale;
+        }
+        out[(size_t(b) * Hkv + g) * C + m] = u;
+      }
+    } else if (m < C) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * lq + j;
+        if (h < G) out[(size_t(b) * Hq + g * G + h) * C + m] = m < c_eff ? acc[j] * scale : kNegInf;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, int block, int C,
@@ -281,6 +358,28 @@ hipError_t launch_score_train(const void* q, const void* kbar, float* scores, co
   return hipGetLastError();
 }
 
+template <int D>
+static void score_decode_mfma_t(const void* q, const void* kbar, float* scores, const int32_t* cl,
+                                int B, int Hq, int Hkv, int L, int block, int C, float scale,
+                                bool group_sum, hipStream_t s) {
+  constexpr int TPW = 2;
+  const int rows_per_wg = 4 * TPW * 16;
+  dim3 grid((C + rows_per_wg - 1) / rows_per_wg, Hkv, B);
+  switch (Hq / Hkv) {
+#define SAS_SCDM_G(GG)                                                                              \
+  case GG:                                                                                         \
+    SAS_LAUNCH("score_decode", (score_decode_mfma_kernel<D, GG, TPW>), grid, dim3(256), 0, s,       \
+               (const bf16_t*)q, (const bf16_t*)kbar, scores, cl, Hq, Hkv, L, C, block, scale,      \
+               group_sum ? 1 : 0);                                                                 \
+    break;
+    SAS_SCDM_G(1) SAS_SCDM_G(2) SAS_SCDM_G(3) SAS_SCDM_G(4) SAS_SCDM_G(5) SAS_SCDM_G(6) SAS_SCDM_G(7)
+    SAS_SCDM_G(8) SAS_SCDM_G(9) SAS_SCDM_G(10) SAS_SCDM_G(11) SAS_SCDM_G(12) SAS_SCDM_G(13)
+    SAS_SCDM_G(14) SAS_SCDM_G(15) SAS_SCDM_G(16)
+#undef SAS_SCDM_G
+    default: break;
+  }
+}
+
 template <typename T, int D>
 static void score_decode_t(const void* q, const void* kbar, float* scores, const int32_t* cl,
                            int B, int Hq, int Hkv, int L, int block, int C, float scale,
@@ -309,8 +408,8 @@ hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
                                hipStream_t s) {
   if (B == 0 || C == 0) return hipSuccess;
   if (bf16) {
-    if (D == 64) score_decode_t<bf16_t, 64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
-    else score_decode_t<bf16_t, 128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+    if (D == 64) score_decode_mfma_t<64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+    else score_decode_mfma_t<128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
   } else {
     if (D == 64) score_decode_t<float, 64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
     else score_decode_t<float, 128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
