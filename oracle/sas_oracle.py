@@ -108,6 +108,42 @@ def block_scores(q, kbar, block, scale, positions):
     return s
 
 
+def selector_backward(q, k, ds, block, scale):
+    """Gradient of the mean-pool selector score for an upstream ds = dL/ds.
+
+    The selector score is s[b,h,t,m] = scale * q[b,h,t] . K̄[b,g(h),m] for
+    history blocks m < c(t), with K̄ the mean of each complete block of K
+    (block_scores and pool_block_keys above).  This is the last link of the
+    gradient path from the output through the gate to the selector ([Review]
+    "A Concrete Walkthrough", Step 5; pooling-based block summaries: [Review]
+    "Our Perspective").  Entries m >= c(t) of ds are not part of s and are
+    ignored.  By the chain rule through the bilinear score and the mean:
+      dq[b,h,t]    = scale * sum_{m < c(t)} ds[b,h,t,m] K̄[b,g(h),m]
+      dK̄[b,g,m]    = scale * sum_{h of g} sum_{t: m < c(t)} ds[b,h,t,m] q[b,h,t]
+      dk[b,g,j]    = dK̄[b,g,j // b] / b for j in a complete block, else 0.
+    q: [B, Hq, N, D]; k: [B, Hkv, N, D]; ds: [B, Hq, N, C] with C = N // block.
+    Returns float64 dq [B, Hq, N, D], dkbar [B, Hkv, C, D], dk [B, Hkv, N, D].
+    """
+    q = _as64(q)
+    ds = _as64(ds)
+    kbar = pool_block_keys(k, block)
+    B, Hq, N, D = q.shape
+    Hkv, C = kbar.shape[1], kbar.shape[2]
+    G = Hq // Hkv
+    c = history_blocks(np.arange(N), block)
+    valid = np.arange(C)[None, :] < c[:, None]  # [N, C]
+    dq = np.zeros_like(q)
+    dkbar = np.zeros((B, Hkv, C, D))
+    for b in range(B):
+        for h in range(Hq):
+            dsm = np.where(valid, ds[b, h, :, :C], 0.0)
+            dq[b, h] = scale * (dsm @ kbar[b, h // G])
+            dkbar[b, h // G] += scale * (dsm.T @ q[b, h])
+    dk = np.zeros((B, Hkv, N, D))
+    dk[:, :, : C * block] = np.repeat(dkbar / block, block, axis=2)
+    return dq, dkbar, dk
+
+
 def group_sum_scores(scores_f32, heads_per_row):
     """fp32 sum of the scores of each KV head's query heads, in head-index order.
 

@@ -229,6 +229,18 @@ def test_decode_parity(case):
     # Idle sequence: zeros and -inf.
     assert torch.all(step.o[~torch.tensor(active)] == 0)
     assert torch.all(step.lse[~torch.tensor(active)] == float("-inf"))
+    # The workspace's arrival counters are back at zero: a second call on the
+    # same workspace gives the same bits; so does a call for fewer sequences.
+    o1, lse1 = step.o.clone(), step.lse.clone()
+    step.o.zero_()
+    sas.sas_sparse_decode(q, kc, vc, lens_d, idx_in, step.o, step.lse, block, scale, step.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(step.o, o1) and torch.equal(step.lse, lse1)
+    o2, lse2 = step.o[:2].clone(), step.lse[:2].clone()
+    sas.sas_sparse_decode(q[:2].contiguous(), kc[:2].contiguous(), vc[:2].contiguous(), lens_d[:2].contiguous(),
+                          None if idx_in is None else idx_in[:2].contiguous(), o2, lse2, block, scale, step.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1[:2]) and torch.equal(lse2, lse1[:2])
 
 
 def test_empty_sizes_are_noops():

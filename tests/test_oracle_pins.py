@@ -489,3 +489,84 @@ def test_decode_idle_and_overlong_sequences():
     assert np.all(od[0] == 0)
     u = orc.decode_scores(q, orc.pool_block_keys(kc, 16), np.array([0, 64]), 16, 0.3, True)
     assert np.all(u[0] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# Selector backward (mean-pool selector)
+# ---------------------------------------------------------------------------
+
+def _selector_problem(seed, B=1, Hq=4, Hkv=2, N=40, D=6, block=8):
+    r = rng(seed)
+    q = r.standard_normal((B, Hq, N, D))
+    k = r.standard_normal((B, Hkv, N, D))
+    C = N // block
+    w = r.standard_normal((B, Hq, N, C))  # the upstream ds
+    return q, k, w, C
+
+
+def _selector_loss(q, k, w, block, scale):
+    """sum over the finite scores of w * s, through the oracle's own forward."""
+    N = q.shape[2]
+    kbar = orc.pool_block_keys(k, block)
+    s = orc.block_scores(q, kbar, block, scale, np.broadcast_to(np.arange(N), (q.shape[0], N)))
+    return float(np.sum(np.where(np.isfinite(s), w * s, 0.0)))
+
+
+@pytest.mark.parametrize("N", [40, 37])  # 37: a tail of 5 tokens outside every complete block
+def test_selector_backward_finite_differences(N):
+    q, k, w, C = _selector_problem(3, N=N)
+    block, scale = 8, 0.37
+    dq, dkbar, dk = orc.selector_backward(q, k, w[..., : N // block], block, scale)
+    eps = 1e-5
+    for arr, grad in ((q, dq), (k, dk)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            a0 = arr[i]
+            arr[i] = a0 + eps
+            lp = _selector_loss(q, k, w[..., : N // block], block, scale)
+            arr[i] = a0 - eps
+            lm = _selector_loss(q, k, w[..., : N // block], block, scale)
+            arr[i] = a0
+            assert abs((lp - lm) / (2 * eps) - grad[i]) < 1e-7, (i, (lp - lm) / (2 * eps), grad[i])
+
+
+def test_selector_backward_against_library_autograd():
+    q, k, w, C = _selector_problem(5, B=2, Hq=6, Hkv=3, N=48, D=8, block=8)
+    block, scale = 8, 0.25
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    B, Hq, N, D = q.shape
+    G = Hq // k.shape[1]
+    kbar = kt[:, :, : C * block].reshape(B, k.shape[1], C, block, D).mean(dim=3)
+    s = scale * torch.matmul(qt, kbar.repeat_interleave(G, dim=1).transpose(-1, -2).contiguous())
+    mask = torch.arange(C)[None, :] < (torch.arange(N) // block)[:, None]
+    (torch.where(mask, s, torch.zeros_like(s)) * torch.tensor(w)).sum().backward()
+    dq, dkbar, dk = orc.selector_backward(q, k, w, block, scale)
+    assert np.allclose(dq, qt.grad.numpy(), atol=1e-12, rtol=1e-10)
+    assert np.allclose(dk, kt.grad.numpy(), atol=1e-12, rtol=1e-10)
+
+
+def test_selector_backward_bilinear_identity_and_pool_structure():
+    # s is bilinear in (q, K̄), so sum ds * s = sum q . dq = sum K̄ . dK̄; every
+    # token of block m carries dK̄[m] / b and the tail carries nothing.
+    q, k, w, C = _selector_problem(7, N=45)
+    block, scale = 8, 0.5
+    C = 45 // block
+    w = w[..., :C]
+    dq, dkbar, dk = orc.selector_backward(q, k, w, block, scale)
+    kbar = orc.pool_block_keys(k, block)
+    s = orc.block_scores(q, kbar, block, scale, np.arange(45)[None, :])
+    lhs = np.sum(np.where(np.isfinite(s), w * s, 0.0))
+    assert abs(lhs - np.sum(q * dq)) < 1e-10
+    assert abs(lhs - np.sum(kbar * dkbar)) < 1e-10
+    for m in range(C):
+        for j in range(m * block, (m + 1) * block):
+            assert np.allclose(dk[:, :, j], dkbar[:, :, m] / block, atol=0, rtol=1e-15)
+    assert np.all(dk[:, :, C * block:] == 0)
+    # queries of block 0 have no history: zero gradient
+    assert np.all(dq[:, :, :block] == 0)
+    # with N a multiple of b no query has the last block in its history
+    q2, k2, w2, C2 = _selector_problem(8, N=48)
+    _, dkbar2, _ = orc.selector_backward(q2, k2, w2, block, scale)
+    assert np.all(dkbar2[:, :, C2 - 1] == 0) and np.any(dkbar2[:, :, C2 - 2] != 0)
