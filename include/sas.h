@@ -80,7 +80,8 @@ typedef enum {
   SAS_OP_TOPK = 2,
   SAS_OP_FWD = 3,
   SAS_OP_BWD = 4,
-  SAS_OP_DECODE = 5
+  SAS_OP_DECODE = 5,
+  SAS_OP_SELECTOR_BWD = 6
 } sas_op;
 
 /*
@@ -195,6 +196,36 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       float* lse, int B, int Hq, int Hkv, int L_max, int D,
                       int block, int topk, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sas_selector_bwd -- gradient of the mean-pool selector score for an upstream
+ *   ds (the last link of the gradient path output -> gate -> score ->
+ *   selector, review "A Concrete Walkthrough", Step 5; pooling-based block
+ *   summaries, review "Our Perspective").  With s[b,h,t,m] = scale q.K̄ for
+ *   history blocks m < c(t) = t / block (sas_score_blocks) and K̄ the mean of
+ *   each complete block of k:
+ *     dq[b,h,t]  = scale * sum_{m < c(t)} ds[b,h,t,m] kbar[b,g,m]
+ *     dkbar[b,g,m] = scale * sum_{h of group g} sum_{t: m < c(t)} ds[b,h,t,m] q[b,h,t]
+ *     dk[b,g,j]  = dkbar[b,g,j / block] / block  (j in a complete block; 0 in the tail)
+ *   Entries of ds with m >= c(t) are ignored.
+ * q:          [B,Hq,N,D] in dtype; kbar: [B,Hkv,C,D] in dtype, C = N / block
+ *             (the pooled keys the scores were computed from).
+ * ds:         fp32 [B,Hq,N,C] (e.g. the ds output of sas_gated_attn_bwd).
+ * dq, dk:     [B,Hq,N,D] / [B,Hkv,N,D] outputs in dtype.  accumulate = 0
+ *             overwrites them; 1 adds this gradient to what they hold (the
+ *             sum is formed in fp32 and rounded once), e.g. to the dq and dk
+ *             of sas_gated_attn_bwd.
+ * dkbar:      optional fp32 [B,Hkv,C,D] output (NULL: not written).
+ * workspace:  sas_workspace_bytes(SAS_OP_SELECTOR_BWD, ...) bytes (fp32
+ *             partial sums of dkbar over token chunks), contents ignored.
+ * bf16 contracts ds rounded to bf16 on the matrix cores (fp32 accumulation);
+ * fp32 accumulates in fp32 throughout.
+ * Errors: SAS_EINVAL, SAS_EUNSUPPORTED (D outside {64, 128}), SAS_EWORKSPACE.
+ */
+int sas_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq,
+                     void* dk, float* dkbar, int B, int Hq, int Hkv, int N, int D,
+                     int block, float scale, int accumulate, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sas_workspace_bytes -- device workspace a call with these sizes needs

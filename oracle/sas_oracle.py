@@ -108,7 +108,7 @@ def block_scores(q, kbar, block, scale, positions):
     return s
 
 
-def selector_backward(q, k, ds, block, scale):
+def selector_backward(q, k, ds, block, scale, kbar=None):
     """Gradient of the mean-pool selector score for an upstream ds = dL/ds.
 
     The selector score is s[b,h,t,m] = scale * q[b,h,t] . K̄[b,g(h),m] for
@@ -122,11 +122,13 @@ def selector_backward(q, k, ds, block, scale):
       dK̄[b,g,m]    = scale * sum_{h of g} sum_{t: m < c(t)} ds[b,h,t,m] q[b,h,t]
       dk[b,g,j]    = dK̄[b,g,j // b] / b for j in a complete block, else 0.
     q: [B, Hq, N, D]; k: [B, Hkv, N, D]; ds: [B, Hq, N, C] with C = N // block.
+    kbar: the pooled keys to use for dq when they are held rounded (e.g. in
+    bf16); None pools k.
     Returns float64 dq [B, Hq, N, D], dkbar [B, Hkv, C, D], dk [B, Hkv, N, D].
     """
     q = _as64(q)
     ds = _as64(ds)
-    kbar = pool_block_keys(k, block)
+    kbar = pool_block_keys(k, block) if kbar is None else _as64(kbar)
     B, Hq, N, D = q.shape
     Hkv, C = kbar.shape[1], kbar.shape[2]
     G = Hq // Hkv

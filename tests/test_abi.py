@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
-                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_workspace_bytes",
+                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_selector_bwd", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
     for n in names:
@@ -39,6 +39,12 @@ def test_version_and_workspace_sizes():
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 3, 2, 64, 128, 64, -1, 1) == ctypes.c_size_t(-1).value
     assert sas.sas_workspace_bytes(99, 1, 4, 2, 64, 128, 64, -1, 1) == ctypes.c_size_t(-1).value
+    # selector backward: fp32 partials of dK̄ per 1024-token chunk (bf16), one chunk (fp32)
+    assert sas.sas_workspace_bytes(sas.SAS_OP_SELECTOR_BWD, 1, 32, 8, 32768, 128, 64, -1, 1) == \
+        32 * 8 * 512 * 128 * 4
+    assert sas.sas_workspace_bytes(sas.SAS_OP_SELECTOR_BWD, 1, 4, 2, 512, 64, 64, -1, 0) == 2 * 8 * 64 * 4
+    assert sas.sas_workspace_bytes(sas.SAS_OP_SELECTOR_BWD, 1, 4, 2, 512, 96, 64, -1, 1) == \
+        ctypes.c_size_t(-1).value
 
 
 def fwd(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, topk=0, dtype=1, ptr=1, idx=None, ws=None, wsb=0,
@@ -135,3 +141,21 @@ def test_errors_are_thread_local():
     t.join()
     assert seen["msg"] == ""
     assert "multiple" in sas.sas_last_error()
+
+
+def test_selector_bwd_host_checks():
+    v = ctypes.c_void_p(8)
+    base = [v, v, v, v, v, N]
+
+    def call(B=1, Hq=4, Hkv=2, N_=128, D=128, block=64, scale=0.1, acc=0, dtype=1, ws=v, wsb=1 << 30, ptrs=None):
+        return L.sas_selector_bwd(*(ptrs or base), B, Hq, Hkv, N_, D, block, scale, acc, dtype, ws, wsb, N)
+
+    assert call(Hq=3) == sas.SAS_EINVAL
+    assert call(D=96) == sas.SAS_EUNSUPPORTED
+    assert call(block=0) == sas.SAS_EINVAL
+    assert call(scale=0.0) == sas.SAS_EINVAL
+    assert call(acc=2) == sas.SAS_EINVAL
+    assert call(ptrs=[v, N, v, v, v, N]) == sas.SAS_EINVAL
+    assert "non-NULL" in sas.sas_last_error()
+    assert call(ws=N, wsb=0) == sas.SAS_EWORKSPACE
+    assert call(B=0, ptrs=[N] * 6) == sas.SAS_OK

@@ -278,3 +278,49 @@ def test_repeated_and_invalid_idx_entries():
     normwise(to64(step.dk), dk, 2e-2, "dk")
     normwise(to64(step.dv), dv, 2e-2, "dv")
     normwise(to64(step.ds), ds, 2e-2, "ds")
+
+
+SELECTOR_CASES = [
+    # name, dtype, B, Hq, Hkv, D, N, block
+    ("f32-d64", "f32", 1, 4, 2, 64, 300, 32),
+    ("bf16-g4-d128", "bf16", 1, 8, 2, 128, 1536, 64),
+    ("bf16-g2-d64-tail", "bf16", 2, 4, 2, 64, 1130, 64),
+    ("bf16-chunks", "bf16", 1, 4, 1, 128, 2600, 32),
+]
+
+
+@pytest.mark.parametrize("case", SELECTOR_CASES, ids=[c[0] for c in SELECTOR_CASES])
+def test_selector_backward_parity(case):
+    name, dts, B, Hq, Hkv, D, N, block = case
+    dt = _dt(dts)
+    C = N // block
+    g = torch.Generator().manual_seed(N + D)
+    q = torch.randn((B, Hq, N, D), generator=g).to(dt)
+    k = torch.randn((B, Hkv, N, D), generator=g).to(dt)
+    ds = torch.randn((B, Hq, N, C), generator=g)
+    kbar = torch.tensor(orc.pool_block_keys(to64(k), block)).to(dt)  # the pooled keys as the GPU holds them
+    scale = D ** -0.5
+    # oracle on the pooled keys as the GPU holds them
+    dq_ref, dkbar_ref, dk_ref = orc.selector_backward(to64(q), to64(k), ds.numpy(), block, scale,
+                                                      kbar=to64(kbar))
+    ws = sas.workspace(sas.SAS_OP_SELECTOR_BWD, B, Hq, Hkv, N, D, block, -1,
+                       sas.SAS_BF16 if dt == torch.bfloat16 else sas.SAS_F32)
+    dq = torch.full((B, Hq, N, D), float("nan"), dtype=dt, device=DEV)
+    dk = torch.full((B, Hkv, N, D), float("nan"), dtype=dt, device=DEV)
+    dkbar = torch.empty((B, Hkv, C, D), dtype=torch.float32, device=DEV)
+    qd, kbd, dsd = q.to(DEV), kbar.to(DEV), ds.to(DEV)
+    sas.sas_selector_bwd(qd, kbd, dsd, dq, dk, block, scale, dkbar=dkbar, workspace=ws)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dt == torch.float32 else 2e-2
+    normwise(to64(dq), dq_ref, tol, "dq")
+    normwise(to64(dkbar), dkbar_ref, tol, "dkbar")
+    normwise(to64(dk), dk_ref, tol, "dk")
+    assert torch.all(dk[:, :, C * block:] == 0)
+    # accumulate: adds onto what dq and dk hold
+    dq0 = torch.randn((B, Hq, N, D), generator=g).to(dt)
+    dk0 = torch.randn((B, Hkv, N, D), generator=g).to(dt)
+    dq2, dk2 = dq0.to(DEV), dk0.to(DEV)
+    sas.sas_selector_bwd(qd, kbd, dsd, dq2, dk2, block, scale, accumulate=True, workspace=ws)
+    torch.cuda.synchronize()
+    normwise(to64(dq2), to64(dq0) + dq_ref, tol, "dq accumulate")
+    normwise(to64(dk2), to64(dk0) + dk_ref, tol, "dk accumulate")

@@ -24,10 +24,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 SAS_OK, SAS_EINVAL, SAS_EUNSUPPORTED, SAS_EHIP, SAS_EWORKSPACE = 0, -1, -2, -3, -4
 SAS_F32, SAS_BF16 = 0, 1
-SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE = 1, 2, 3, 4, 5
+SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTOR_BWD = 1, 2, 3, 4, 5, 6
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-            "sas_sparse_decode", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_sparse_decode", "sas_selector_bwd", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -36,6 +36,7 @@ _lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp,
 _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_workspace_bytes.argtypes = [_i] * 9
 _lib.sas_workspace_bytes.restype = _sz
 _lib.sas_last_error.restype = ctypes.c_char_p
@@ -46,7 +47,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-              "sas_sparse_decode"):
+              "sas_sparse_decode", "sas_selector_bwd"):
     getattr(_lib, _name).restype = _i
 
 
@@ -203,3 +204,15 @@ def sas_sparse_decode(q, k_cache, v_cache, cache_len, idx, o, lse, block, scale,
     _check(_lib.sas_sparse_decode(_p(q), _p(k_cache), _p(v_cache), _p(cache_len), _idx_ptr(idx), _p(o),
                                   _p(lse), B, Hq, Hkv, L, D, block, topk, scale, _dt(q),
                                   _p(workspace), wsb, _stream(stream)))
+
+
+def sas_selector_bwd(q, kbar, ds, dq, dk, block, scale, dkbar=None, accumulate=False, workspace=None,
+                     stream=None):
+    """q [B,Hq,N,D], kbar [B,Hkv,C,D], ds fp32 [B,Hq,N,C] -> dq [B,Hq,N,D], dk [B,Hkv,N,D]
+    (written, or added to with accumulate=True), optional dkbar fp32 [B,Hkv,C,D]."""
+    B, Hq, N, D = q.shape
+    Hkv = kbar.shape[1]
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_selector_bwd(_p(q), _p(kbar), _p(ds), _p(dq), _p(dk), _p(dkbar), B, Hq, Hkv, N, D,
+                                 block, scale, 1 if accumulate else 0, _dt(q), _p(workspace), wsb,
+                                 _stream(stream)))

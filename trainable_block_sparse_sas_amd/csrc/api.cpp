@@ -78,6 +78,9 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
       return sas::bwd_workspace(d, topk, bf16);
     case SAS_OP_DECODE:
       return sas::decode_workspace(B, Hq, Hkv, n, D, block, topk);
+    case SAS_OP_SELECTOR_BWD:
+      if (D != 64 && D != 128) return size_t(-1);
+      return sas::selector_bwd_workspace(d, bf16);
     default:
       return size_t(-1);
   }
@@ -229,6 +232,31 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                                     D, block, idx ? topk : -1, scale, dtype == SAS_BF16, workspace,
                                     static_cast<hipStream_t>(stream));
   return hip_status(e, "sas_sparse_decode");
+}
+
+int sas_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq, void* dk,
+                     float* dkbar, int B, int Hq, int Hkv, int N, int D, int block, float scale,
+                     int accumulate, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_common(B, Hq, Hkv, N, D, block, dtype, "sas_selector_bwd");
+  if (!st) st = check_scale(scale, "sas_selector_bwd");
+  if (st) return st;
+  if (accumulate != 0 && accumulate != 1)
+    return fail(SAS_EINVAL, "sas_selector_bwd: accumulate must be 0 or 1 (got %d)", accumulate);
+  if (empty(B, Hq, N)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !kbar || !ds || !dq || !dk)
+    return fail(SAS_EINVAL, "sas_selector_bwd: q, kbar, ds, dq and dk must be non-NULL");
+  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
+  const bool bf16 = dtype == SAS_BF16;
+  const size_t need = sas::selector_bwd_workspace(d, bf16);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SAS_EWORKSPACE, "sas_selector_bwd: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  hipError_t e = sas::launch_selector_bwd(q, kbar, ds, dq, dk, dkbar, d, scale, accumulate != 0, bf16, workspace,
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_selector_bwd");
 }
 
 }  // extern "C"

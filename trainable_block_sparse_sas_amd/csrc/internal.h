@@ -98,6 +98,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       hipStream_t s);
 
 // ---- decode --------------------------------------------------------------------
+size_t selector_bwd_workspace(const Dims& d, bool bf16);
+hipError_t launch_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq, void* dk,
+                               float* dkbar, const Dims& d, float scale, bool accumulate, bool bf16,
+                               void* ws, hipStream_t s);
 size_t decode_workspace(int B, int Hq, int Hkv, int L_max, int D, int block, int topk);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* cache_len,
                          const int32_t* idx, void* o, float* lse, int B, int Hq, int Hkv,
