@@ -254,6 +254,50 @@ def roofline(kernels, pairs, D, workload):
             "timing": "HIP events around each launch on its stream (library kernel timing)"}
 
 
+def bench_selector_bwd(torch, w, steps):
+    """The mean-pool selector's backward (sas_selector_bwd, accumulating into
+    dq and dk) on the ds of one sparse training step, timed on its own.
+    Work: per (query row, history block) score entry, 2D flops for dq and 2D
+    for dK̄; the ds array is fp32 [B, Hq, N, C]."""
+    from trainable_block_sparse_sas_amd.inputs import training_inputs
+    from trainable_block_sparse_sas_amd.pipeline import TrainStep
+    from trainable_block_sparse_sas_amd import binding as sas
+
+    q, k, v, do = training_inputs(w, device="cuda")
+    step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, w.torch_dtype)
+    step.run(q, k, v, do)
+    ws = sas.workspace(sas.SAS_OP_SELECTOR_BWD, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, -1,
+                       sas.SAS_BF16 if w.torch_dtype == torch.bfloat16 else sas.SAS_F32)
+
+    def one():
+        sas.sas_selector_bwd(q, step.kbar, step.ds, step.dq, step.dk, w.block, w.scale, accumulate=True,
+                             workspace=ws)
+
+    one()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        one()
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    sas.sas_profile_read()
+    sas.sas_profile_enable(True)
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    sas.sas_profile_enable(False)
+    kernels = {name: round(t / cnt, 4) for name, (t, cnt) in sas.sas_profile_read().items()}
+    C = w.N // w.block
+    entries = w.B * w.Hq * sum(min(t // w.block, C) for t in range(w.N))
+    flops = 4 * w.D * entries
+    return {"ms": round(ms, 4), "kernels_ms": kernels, "score_entries": entries,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "note": "NEXT-row kernel, timed on its own; not part of the step above"}
+
+
 def copy_probe(torch):
     """One plain streaming kernel over 1 GiB (bitwise not of 2^28 int32: 1 GiB
     read, 1 GiB written); its counter readings calibrate FETCH_SIZE and
@@ -372,6 +416,7 @@ def main():
             "fwd_tflops": round(full["flops_fwd"] / (full["ms_fwd"] * 1e-3) / 1e12, 3),
             "bwd_tflops": round(full["flops_bwd"] / (full["ms_bwd"] * 1e-3) / 1e12, 3)}
         out["decode"] = bench_decodes(torch, wmap)
+        out["selector_bwd"] = bench_selector_bwd(torch, w, 5)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
