@@ -26,6 +26,8 @@
 #include "mfma.h"
 #include "tiles.h"
 
+#include <type_traits>
+
 namespace sas {
 namespace {
 
@@ -142,93 +144,158 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelArgs a) {
 }
 
 // ----------------------------------------------------------- dK̄ (bf16) ----
+// Workgroup: MT = 128 blocks of one KV head and one token chunk; wave w owns
+// blocks m0 + 32 w .. m0 + 32 w + 31 (two 16-block tiles) x all D columns.
+// Steps of 64 tokens of one head run through two LDS stages: while a step's
+// products run, the next step's q rows (direct global -> LDS copies) and ds
+// values (registers, bf16 into LDS after the barrier) are in flight.
 template <int D>
-__global__ __launch_bounds__(256) void sel_dkbar_kernel(SelArgs a) {
+__global__ __launch_bounds__(256, 2) void sel_dkbar_kernel(SelArgs a) {
   using namespace tiles;
   constexpr int ND = D / 16;
   constexpr int CH = D / 8;
   constexpr int QPL = 64 * CH / 256;  // direct q copies per lane per step
-  constexpr int DST = 64;             // ds tile row: 64 blocks (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[64 * DST];
+  constexpr int MT = 128;             // blocks per workgroup
+  constexpr int DST = MT;             // ds tile row (bf16)
+  constexpr int SPT = 32;             // ds values per thread per step
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[64 * D], Q1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t S0[64 * DST], S1[64 * DST];
   const int ch = blockIdx.x, mtile = blockIdx.y, bg = blockIdx.z;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int N = a.N, C = a.C;
-  const int m0 = mtile * 64;
+  const int m0 = mtile * MT;
   if (!chunk_active(ch, a.tch, N, a.block, m0)) return;  // nothing of this chunk reaches the tile
   // first token whose history holds block m0, and the chunk's token range
   const int t_begin = max(ch * a.tch, (m0 + 1) * a.block);
   const int t_end = min(N, (ch + 1) * a.tch);
-  f32x4 acc[ND];
+  const int nt = (t_end - t_begin + 63) / 64;  // steps per head
+  const int nsteps = G * nt;
+  const bool vec4 = (C & 3) == 0;
+  f32x4 acc[2][ND];
 #pragma unroll
-  for (int nd = 0; nd < ND; ++nd) acc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) acc[u][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int trow = 4 * lq + (lr >> 2), tcol = 4 * (lr & 3);
-  // ds staging: thread -> (row r = tid / 4, 16 columns (tid % 4) 16 ..)
-  const int sr = tid >> 2, sc0 = (tid & 3) * 16;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
+  // ds staging: thread -> row sr (of 64), columns sc0 .. sc0 + 31
+  const int sr = tid >> 2, sc0 = (tid & 3) * SPT;
+  float v[SPT];
+  auto load_ds = [&](int s) {
+    const int h = g * G + s / nt, t0 = t_begin + (s % nt) * 64;
+    const int tt = t0 + sr;
+    const int ct = tt < t_end ? min(tt / a.block, C) : 0;  // row tt's history: m < ct
+    const float* src = a.ds + ((size_t(b) * a.Hq + h) * N + (tt < t_end ? tt : t0)) * size_t(C) + m0 + sc0;
+#pragma unroll
+    for (int j = 0; j < SPT; j += 4) {
+      const int m = m0 + sc0 + j;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (vec4 && m + 3 < ct) {
+        x = *reinterpret_cast<const float4*>(src + j);
+      } else if (m < ct) {
+        x.x = src[j];
+        x.y = m + 1 < ct ? src[j + 1] : 0.f;
+        x.z = m + 2 < ct ? src[j + 2] : 0.f;
+        x.w = m + 3 < ct ? src[j + 3] : 0.f;
+      }
+      v[j] = x.x;
+      v[j + 1] = x.y;
+      v[j + 2] = x.z;
+      v[j + 3] = x.w;
+    }
+  };
+  auto stq = [&](auto tag) -> uint16_t* {
+    if constexpr (decltype(tag)::value == 0) return Q0;
+    else return Q1;
+  };
+  auto sts = [&](auto tag) -> uint16_t* {
+    if constexpr (decltype(tag)::value == 0) return S0;
+    else return S1;
+  };
+  auto issue_q = [&](auto tag, int s) {
+    const int h = g * G + s / nt, t0 = t_begin + (s % nt) * 64;
     const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + (size_t(b) * a.Hq + h) * size_t(N) * D;
-    const float* dsh = a.ds + (size_t(b) * a.Hq + h) * size_t(N) * C;
-    for (int t0 = t_begin; t0 < t_end; t0 += 64) {
-      __syncthreads();  // every wave is done with the previous tiles
+    uint16_t* dst = stq(tag);
 #pragma unroll
-      for (int i = 0; i < QPL; ++i) {
-        const int piece = wave * QPL + i;
-        const int sl = 64 * piece + lane;
-        const int r = sl / CH, pc = sl % CH;
-        const int tq = t0 + r < t_end ? t0 + r : t0;  // rows past the range: a real row, weight 0
-        dma16_to_lds(qh + size_t(tq) * D + ((pc ^ k_swz<D>(r)) * 8), Qs + piece * 512);
+    for (int i = 0; i < QPL; ++i) {
+      const int piece = wave * QPL + i;
+      const int sl = 64 * piece + lane;
+      const int r = sl / CH, pc = sl % CH;
+      const int tq = t0 + r < t_end ? t0 + r : t0;  // rows past the range: a real row, weight 0
+      dma16_to_lds(qh + size_t(tq) * D + ((pc ^ k_swz<D>(r)) * 8), dst + piece * 512);
+    }
+  };
+  auto store_ds = [&](auto tag) {
+    uint16_t* dst = sts(tag);
+#pragma unroll
+    for (int cc = 0; cc < SPT / 8; ++cc) {
+      const int c8 = (sc0 >> 3) + cc;
+      *reinterpret_cast<uint4*>(dst + sr * DST + ((c8 ^ (sr & 15)) << 3)) =
+          make_uint4(pack_bf16(v[8 * cc + 0], v[8 * cc + 1]), pack_bf16(v[8 * cc + 2], v[8 * cc + 3]),
+                     pack_bf16(v[8 * cc + 4], v[8 * cc + 5]), pack_bf16(v[8 * cc + 6], v[8 * cc + 7]));
+    }
+  };
+  auto compute = [&](auto tag) {
+    const uint16_t* Qs = stq(tag);
+    const uint16_t* Ds = sts(tag);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ra = 32 * kk + trow, rb = ra + 16;
+      uint4 dsa[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int dcol = 32 * wave + 16 * u + tcol;
+        const uint2 d0 = lds_read_tr16(Ds + ra * DST + (((dcol >> 3) ^ (ra & 15)) << 3) + (dcol & 7));
+        const uint2 d1 = lds_read_tr16(Ds + rb * DST + (((dcol >> 3) ^ (rb & 15)) << 3) + (dcol & 7));
+        dsa[u] = make_uint4(d0.x, d0.y, d1.x, d1.y);
       }
-      {
-        const int tt = t0 + sr;
-        const int ct = tt < t_end ? min(tt / a.block, C) : 0;  // row tt's history: m < ct
-        const float* src = dsh + size_t(tt < t_end ? tt : t0) * C + m0 + sc0;
-        float v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int m = m0 + sc0 + j;
-          v[j] = m < ct ? src[j] : 0.f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int c8 = (sc0 >> 3) + cc;
-          *reinterpret_cast<uint4*>(Ds + sr * DST + ((c8 ^ k_swz<64>(sr)) << 3)) =
-              make_uint4(pack_bf16(v[8 * cc + 0], v[8 * cc + 1]), pack_bf16(v[8 * cc + 2], v[8 * cc + 3]),
-                         pack_bf16(v[8 * cc + 4], v[8 * cc + 5]), pack_bf16(v[8 * cc + 6], v[8 * cc + 7]));
-        }
-      }
-      wait_vm<0>();
-      __syncthreads();  // q and ds tiles complete
-      // wave: blocks m0 + 16 wave + (0..15); k = tokens t0 .. t0 + 63
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ra = 32 * kk + trow, rb = ra + 16;
-        const int dcol = 16 * wave + tcol;
-        const uint2 d0 = lds_read_tr16(Ds + ra * DST + (((dcol >> 3) ^ k_swz<64>(ra)) << 3) + (dcol & 7));
-        const uint2 d1 = lds_read_tr16(Ds + rb * DST + (((dcol >> 3) ^ k_swz<64>(rb)) << 3) + (dcol & 7));
-        const uint4 dsa = make_uint4(d0.x, d0.y, d1.x, d1.y);
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const int col = 16 * nd + tcol;
-          const uint2 q0 = lds_read_tr16(Qs + ra * D + (((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7));
-          const uint2 q1 = lds_read_tr16(Qs + rb * D + (((col >> 3) ^ k_swz<D>(rb)) << 3) + (col & 7));
-          acc[nd] = mfma16(dsa, make_uint4(q0.x, q0.y, q1.x, q1.y), acc[nd]);
-        }
+      for (int nd = 0; nd < ND; ++nd) {
+        const int col = 16 * nd + tcol;
+        const uint2 q0 = lds_read_tr16(Qs + ra * D + (((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7));
+        const uint2 q1 = lds_read_tr16(Qs + rb * D + (((col >> 3) ^ k_swz<D>(rb)) << 3) + (col & 7));
+        const uint4 qb = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        acc[0][nd] = mfma16(dsa[0], qb, acc[0][nd]);
+        acc[1][nd] = mfma16(dsa[1], qb, acc[1][nd]);
       }
     }
+  };
+  using T0 = std::integral_constant<int, 0>;
+  using T1 = std::integral_constant<int, 1>;
+  // one step on stage `tag`: its ds into LDS, barrier, the next step's loads
+  // into the other stage, the products
+  auto step = [&](auto tag, int s) {
+    using Tn = std::integral_constant<int, decltype(tag)::value ^ 1>;
+    store_ds(tag);
+    wait_vm<0>();
+    __syncthreads();  // this stage complete; every wave is done with the other
+    if (s + 1 < nsteps) {
+      issue_q(Tn{}, s + 1);
+      load_ds(s + 1);
+    }
+    compute(tag);
+  };
+  issue_q(T0{}, 0);
+  load_ds(0);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(T0{}, s);
+    step(T1{}, s + 1);
   }
-  // lane (lq, lr): block m0 + 16 wave + 4 lq + i, column 16 nd + lr
+  if (s < nsteps) step(T0{}, s);
+  // lane (lq, lr): block m0 + 32 wave + 16 u + 4 lq + i, column 16 nd + lr
   float* out = a.part + ((size_t(ch) * a.B * a.Hkv + bg) * C) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wave * 16 + 4 * lq + i;
-    if (m >= C) continue;
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd) out[size_t(m) * D + 16 * nd + lr] = acc[nd][i] * a.scale;
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wave * 32 + 16 * u + 4 * lq + i;
+      if (m >= C) continue;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) out[size_t(m) * D + 16 * nd + lr] = acc[u][nd][i] * a.scale;
+    }
 }
 
 // ------------------------------------------------------ fp32 (per element) --
@@ -274,7 +341,7 @@ __global__ __launch_bounds__(D) void sel_pool_bwd_kernel(SelArgs a) {
     return;
   }
   const int bg = b * a.Hkv + g;
-  const int m0 = (m / 64) * 64;
+  const int m0 = (m / 128) * 128;  // the dK̄ kernel's block tile
   float s = 0.f;
   for (int ch = 0; ch < a.nch; ++ch)
     if (chunk_active(ch, a.tch, N, a.block, m0))
@@ -292,7 +359,7 @@ hipError_t selector_bwd_t(SelArgs a, bool bf16, hipStream_t s) {
   if (bf16) {
     SAS_LAUNCH("sel_dq", (sel_dq_kernel<D>), dim3((a.N + 63) / 64, a.Hq, a.B), dim3(256), 0, s, a);
     if (a.C > 0)
-      SAS_LAUNCH("sel_dkbar", (sel_dkbar_kernel<D>), dim3(a.nch, (a.C + 63) / 64, a.B * a.Hkv), dim3(256), 0, s, a);
+      SAS_LAUNCH("sel_dkbar", (sel_dkbar_kernel<D>), dim3(a.nch, (a.C + 127) / 128, a.B * a.Hkv), dim3(256), 0, s, a);
     SAS_LAUNCH("sel_pool_bwd", (sel_pool_bwd_kernel<bf16_t, D>), dim3(a.C + 1, a.Hkv, a.B), dim3(D), 0, s, a);
   } else {
     SAS_LAUNCH("sel_dq", (sel_dq_f32_kernel<D>), dim3(a.N, a.Hq, a.B), dim3(D), 0, s, a);
