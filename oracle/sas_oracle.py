@@ -146,6 +146,32 @@ def selector_backward(q, k, ds, block, scale, kbar=None):
     return dq, dkbar, dk
 
 
+def selector_dq_rows(kbar, ds, block, scale, b, h, rows):
+    """dq of selected query rows of head h in batch b: the row-local part of
+    `selector_backward`, scale * sum_{m < c(t)} ds[t,m] K̄_m.  kbar: [B, Hkv, C, D]
+    (pooled keys as held); ds: [B, Hq, N, C]; Hq is read from ds.  Returns [R, D]."""
+    Hq, C = ds.shape[1], kbar.shape[2]
+    G = Hq // kbar.shape[1]
+    rows = np.asarray(rows)
+    c = history_blocks(rows, block)
+    dsr = np.where(np.arange(C)[None, :] < c[:, None], _as64(ds[b, h][rows][:, :C]), 0.0)
+    return scale * (dsr @ _as64(kbar[b, h // G]))
+
+
+def selector_dkbar_blocks(q, ds, block, scale, b, g, G, blocks):
+    """dK̄ of selected blocks of KV head g in batch b (G query heads per KV
+    head): the block-local part of `selector_backward`, scale * sum over the
+    group's heads and the queries t with m < c(t), i.e. t >= (m+1) b, of
+    ds[t,m] q_t.  q: [B, Hq, N, D]; ds: [B, Hq, N, C].  Returns [M, D]."""
+    D = q.shape[3]
+    out = np.zeros((len(blocks), D))
+    for i, m in enumerate(blocks):
+        t0 = (int(m) + 1) * block
+        for h in range(g * G, (g + 1) * G):
+            out[i] += scale * (_as64(ds[b, h, t0:, m]) @ _as64(q[b, h, t0:]))
+    return out
+
+
 def group_sum_scores(scores_f32, heads_per_row):
     """fp32 sum of the scores of each KV head's query heads, in head-index order.
 

@@ -110,6 +110,36 @@ def test_training_fullsize(wi):
     normwise(to64(step.dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
 
 
+def test_selector_bwd_fullsize():
+    """The selector backward at the 32K training shape, on a seeded ds of the
+    same shape as the attention backward's output."""
+    w = WORKLOADS[2]
+    dt = w.torch_dtype
+    q, k, _, _ = training_inputs(w, device="cpu")
+    C, G = w.C, w.Hq // w.Hkv
+    ds = torch.randn((w.B, w.Hq, w.N, C), generator=torch.Generator().manual_seed(4242))
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(to64(k), w.block)).to(dt))
+    qd, dsd = q.to(DEV), ds.to(DEV)
+    kbd = torch.tensor(kbar_r).to(dt).to(DEV)
+    dq = torch.empty((w.B, w.Hq, w.N, w.D), dtype=dt, device=DEV)
+    dk = torch.empty((w.B, w.Hkv, w.N, w.D), dtype=dt, device=DEV)
+    dkbar = torch.empty((w.B, w.Hkv, C, w.D), dtype=torch.float32, device=DEV)
+    ws = sas.workspace(sas.SAS_OP_SELECTOR_BWD, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, -1, sas.SAS_BF16)
+    sas.sas_selector_bwd(qd, kbd, dsd, dq, dk, w.block, w.scale, dkbar=dkbar, workspace=ws)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.N, w.block)
+    for h in (0, w.Hq // 2 + 1, w.Hq - 1):
+        ref = orc.selector_dq_rows(kbar_r, ds.numpy(), w.block, w.scale, 0, h, rows)
+        normwise(to64(dq[0, h, rows]), ref, 2e-2, f"dq h{h}")
+    blocks = np.array([0, 1, C // 2, C - 2, C - 1])
+    for g in (0, w.Hkv - 1):
+        ref = orc.selector_dkbar_blocks(to64(q), ds.numpy(), w.block,
+                                        w.scale, 0, g, G, blocks)
+        normwise(to64(dkbar[0, g, blocks]), ref, 2e-2, f"dkbar g{g}")
+        toks = np.concatenate([np.arange(m * w.block, (m + 1) * w.block) for m in blocks])
+        normwise(to64(dk[0, g, toks]), np.repeat(ref / w.block, w.block, axis=0), 2e-2, f"dk g{g}")
+
+
 @pytest.mark.parametrize("wi", [3, 4], ids=["decode-128k-b8", "decode-512k-b1"])
 def test_decode_fullsize(wi):
     w = WORKLOADS[wi]

@@ -570,3 +570,21 @@ def test_selector_backward_bilinear_identity_and_pool_structure():
     q2, k2, w2, C2 = _selector_problem(8, N=48)
     _, dkbar2, _ = orc.selector_backward(q2, k2, w2, block, scale)
     assert np.all(dkbar2[:, :, C2 - 1] == 0) and np.any(dkbar2[:, :, C2 - 2] != 0)
+
+
+def test_selector_subset_helpers_match_full_backward():
+    q, k, w, C = _selector_problem(11, B=2, Hq=6, Hkv=2, N=53, D=5, block=8)
+    block, scale = 8, 0.3
+    C = 53 // block
+    w = w[..., :C]
+    dq, dkbar, _ = orc.selector_backward(q, k, w, block, scale)
+    kbar = orc.pool_block_keys(k, block)
+    rows = [0, 7, 8, 30, 52]
+    for b in range(2):
+        for h in (0, 3, 5):
+            assert np.allclose(orc.selector_dq_rows(kbar, w, block, scale, b, h, rows), dq[b, h, rows],
+                               atol=1e-13, rtol=1e-12)
+        for g in range(2):
+            blocks = [0, 2, C - 1]
+            assert np.allclose(orc.selector_dkbar_blocks(q, w, block, scale, b, g, 3, blocks),
+                               dkbar[b, g, blocks], atol=1e-13, rtol=1e-12)
