@@ -198,6 +198,46 @@ def bench_decode(torch, w, steps, warmup, dense=False):
                 attend_gbs=kv_bytes / (ms_attend * 1e-3) / 1e9)
 
 
+def bench_paged_decode(torch, w, steps, warmup):
+    """The same decode step over a paged copy of the cache (pages of one block
+    per sequence and KV head, shuffled in a pool; sas_paged_decode runs scores,
+    Top-K and attention), median over `steps` spans after a 1 GiB read flush."""
+    from trainable_block_sparse_sas_amd.inputs import decode_inputs
+    from trainable_block_sparse_sas_amd import binding as sas
+
+    q, kc, vc, lens = decode_inputs(w, device="cuda")
+    B, Hkv, L, D = kc.shape
+    C = L // w.block
+    n_pages = B * C
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(5)).to("cuda")
+    table = perm.reshape(B, C).to(torch.int32).contiguous()
+    kp = torch.empty((n_pages, Hkv, w.block, D), dtype=kc.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = kc.reshape(B, Hkv, C, w.block, D).permute(0, 2, 1, 3, 4).reshape(n_pages, Hkv, w.block, D)
+    vp[perm] = vc.reshape(B, Hkv, C, w.block, D).permute(0, 2, 1, 3, 4).reshape(n_pages, Hkv, w.block, D)
+    del kc, vc
+    kbp = torch.empty((n_pages, Hkv, D), dtype=kp.dtype, device="cuda")
+    sas.sas_pool_pages(kp, kbp, table.reshape(-1).contiguous(), w.block)
+    o = torch.empty((B, w.Hq, D), dtype=kp.dtype, device="cuda")
+    lse = torch.empty((B, w.Hq), dtype=torch.float32, device="cuda")
+    ws = sas.workspace(sas.SAS_OP_PAGED_DECODE, B, w.Hq, Hkv, L, D, w.block, w.topk,
+                       sas.SAS_BF16 if kp.dtype == torch.bfloat16 else sas.SAS_F32)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    acc = torch.zeros(1, dtype=torch.float32, device="cuda")
+    tm = Timer(torch)
+    for i in range(warmup + steps):
+        torch.sum(flush, dim=0, keepdim=True, out=acc)
+        if i < warmup:
+            sas.sas_paged_decode(q, kp, vp, kbp, table, lens, w.topk, o, lse, w.block, w.scale, workspace=ws)
+            continue
+        with tm.span("paged"):
+            sas.sas_paged_decode(q, kp, vp, kbp, table, lens, w.topk, o, lse, w.block, w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ms = tm.ms("paged", median=True)
+    return {"ms_step": round(ms, 4), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "layout": "pages of one block x all KV heads, shuffled pool; block table per sequence"}
+
+
 # Algorithmic work of the matrix-core kernels per attended (query row, key)
 # pair: the forward's S = QK^T and PV (4D flops; fwd_sel at sparse scope,
 # fwd_mfma at full scope); at sparse scope the dQ kernel's dS K over the dS the
@@ -357,6 +397,8 @@ def bench_decodes(torch, wmap):
                      "timing": "median of 50 HIP-event spans, 1 GiB read flush before each span; "
                                "stage spans each include the event-pair floor",
                      "topk": wd.topk}
+        dec[name]["paged"] = bench_paged_decode(torch, wd, 50, 10)
+        torch.cuda.empty_cache()
         if name == "decode-512k-b1":
             rd = bench_decode(torch, wd, 20, 3, dense=True)
             dec[name]["dense_ms"] = round(rd["ms_step"], 4)

@@ -81,7 +81,8 @@ typedef enum {
   SAS_OP_FWD = 3,
   SAS_OP_BWD = 4,
   SAS_OP_DECODE = 5,
-  SAS_OP_SELECTOR_BWD = 6
+  SAS_OP_SELECTOR_BWD = 6,
+  SAS_OP_PAGED_DECODE = 7
 } sas_op;
 
 /*
@@ -196,6 +197,48 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       float* lse, int B, int Hq, int Hkv, int L_max, int D,
                       int block, int topk, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged KV cache.  A page holds one block (`block` tokens) of one sequence for
+ * every KV head: k_pages, v_pages [num_pages, Hkv, block, D], so each block
+ * of each head stays one contiguous run.  block_table int32 [B, max_blocks]
+ * on the device maps logical block m of sequence b to its page; the entries
+ * for m <= (cache_len[b] - 1) / block must be valid page indices (they are
+ * not checked).  kbar_pages [num_pages, Hkv, D] holds each full page's pooled
+ * keys.
+ *
+ * sas_pool_pages -- kbar_pages[p, g] = mean of the block keys of page p, head g
+ *   (pooling-based block summaries, review "Our Perspective"), for the n_pages
+ *   page indices in `pages` (int32, device).  Errors: SAS_EINVAL,
+ *   SAS_EUNSUPPORTED (D outside {64, 128}).
+ */
+int sas_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages,
+                   int n_pages, int Hkv, int D, int block, int dtype, void* stream);
+
+/*
+ * sas_paged_decode -- one decode step over a paged cache, the whole chain:
+ *   group-summed selector scores of the history blocks from their pages'
+ *   pooled keys (as sas_score_blocks), Top-K (as sas_topk_select), then
+ *   attention over the selected blocks and the current block with no gate
+ *   (as sas_sparse_decode; review "A Concrete Walkthrough", Step 6, paper
+ *   Alg. 2).
+ * q:          [B,Hq,D]; cache_len int32 [B] (a length above max_blocks *
+ *             block counts as that; <= 0 is an idle sequence).
+ * topk:       0 .. 256 blocks (0: the current block only).
+ * o:          [B,Hq,D] output; lse optional fp32 [B,Hq] output.
+ * idx_out:    optional int32 [B,Hkv,topk] output, the selected blocks.
+ * workspace:  sas_workspace_bytes(SAS_OP_PAGED_DECODE, B, Hq, Hkv,
+ *             max_blocks * block, D, block, topk, dtype) bytes.
+ * bf16 only.  Errors: SAS_EINVAL, SAS_EUNSUPPORTED (fp32, D outside {64,
+ *         128}, more than 16 query heads per KV head, topk > 256,
+ *         max_blocks > 16384), SAS_EWORKSPACE.
+ */
+int sas_paged_decode(const void* q, const void* k_pages, const void* v_pages,
+                     const void* kbar_pages, const int32_t* block_table,
+                     int max_blocks, const int32_t* cache_len, int topk, void* o,
+                     float* lse, int32_t* idx_out, int B, int Hq, int Hkv, int D,
+                     int block, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * sas_selector_bwd -- gradient of the mean-pool selector score for an upstream

@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
-                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_selector_bwd", "sas_workspace_bytes",
+                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
+                          "sas_paged_decode", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
     for n in names:
@@ -159,3 +160,28 @@ def test_selector_bwd_host_checks():
     assert "non-NULL" in sas.sas_last_error()
     assert call(ws=N, wsb=0) == sas.SAS_EWORKSPACE
     assert call(B=0, ptrs=[N] * 6) == sas.SAS_OK
+
+
+def test_paged_decode_host_checks():
+    v = ctypes.c_void_p(8)
+
+    def call(maxb=16, topk=4, B=2, Hq=8, Hkv=2, D=128, block=64, scale=0.1, dtype=1, ptrs=None, ws=v, wsb=1 << 30):
+        p = ptrs or [v, v, v, v, v]
+        return L.sas_paged_decode(*p, maxb, v, topk, v, N, N, B, Hq, Hkv, D, block, scale, dtype, ws, wsb, N)
+
+    assert call(dtype=0) == sas.SAS_EUNSUPPORTED
+    assert call(topk=-1) == sas.SAS_EINVAL
+    assert call(topk=300) == sas.SAS_EUNSUPPORTED
+    assert call(Hq=40) == sas.SAS_EUNSUPPORTED
+    assert call(maxb=20000) == sas.SAS_EUNSUPPORTED
+    assert call(maxb=-1) == sas.SAS_EINVAL
+    assert call(D=96) == sas.SAS_EUNSUPPORTED
+    assert call(ptrs=[v, v, v, v, N]) == sas.SAS_EINVAL
+    assert call(ws=N, wsb=0) == sas.SAS_EWORKSPACE
+    assert call(B=0, ptrs=[N] * 5) == sas.SAS_OK
+    need = sas.sas_workspace_bytes(sas.SAS_OP_PAGED_DECODE, 2, 8, 2, 16 * 64, 128, 64, 4, 1)
+    assert need >= 2 * 2 * 16 * 4 + sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 2, 8, 2, 16 * 64, 128, 64, 4, 1)
+    assert call(wsb=need - 1) == sas.SAS_EWORKSPACE
+    assert L.sas_pool_pages(v, v, v, -1, 2, 128, 64, 1, N) == sas.SAS_EINVAL
+    assert L.sas_pool_pages(v, v, N, 3, 2, 128, 64, 1, N) == sas.SAS_EINVAL
+    assert L.sas_pool_pages(N, N, N, 0, 2, 128, 64, 1, N) == sas.SAS_OK

@@ -324,3 +324,72 @@ def test_selector_backward_parity(case):
     torch.cuda.synchronize()
     normwise(to64(dq2), to64(dq0) + dq_ref, tol, "dq accumulate")
     normwise(to64(dk2), to64(dk0) + dk_ref, tol, "dk accumulate")
+
+
+PAGED_CASES = [
+    # name, Hq, Hkv, D, max_blocks, block, topk
+    ("g4-k4", 8, 2, 128, 24, 64, 4),
+    ("g5-d64-k3", 10, 2, 64, 20, 64, 3),
+    ("block128-k2", 8, 2, 128, 10, 128, 2),
+    ("k0-current-only", 4, 1, 128, 8, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
+def test_paged_decode_parity(case):
+    name, Hq, Hkv, D, maxb, block, topk = case
+    dt = torch.bfloat16
+    B = 4
+    L = maxb * block
+    w = Workload(name, "decode", "bf16", B, Hq, Hkv, D, L, block, topk, index=11)
+    q, kc, vc, _ = decode_inputs(w, device="cpu")
+    lens = torch.tensor([L, L - 37, block + 3, 0], dtype=torch.int32)
+    G = Hq // Hkv
+    # pages in a shuffled pool with spare pages: block m of sequence b -> page table[b, m]
+    n_pages = B * maxb + 5
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
+    table = perm[: B * maxb].reshape(B, maxb).to(torch.int32)
+    kp = torch.zeros((n_pages, Hkv, block, D), dtype=dt)
+    vp = torch.zeros((n_pages, Hkv, block, D), dtype=dt)
+    for b in range(B):
+        for m in range(maxb):
+            kp[table[b, m]] = kc[b, :, m * block:(m + 1) * block]
+            vp[table[b, m]] = vc[b, :, m * block:(m + 1) * block]
+    kpd, vpd, tbd = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    kbp = torch.zeros((n_pages, Hkv, D), dtype=dt, device=DEV)
+    sas.sas_pool_pages(kpd, kbp, table.reshape(-1).contiguous().to(DEV), block)
+    torch.cuda.synchronize()
+    kbar = orc.pool_block_keys(to64(kc), block)  # [B, Hkv, C, D]
+    kbar_r = to64(torch.tensor(kbar).to(dt))
+    kbar_close(to64(kbp[table.long()].permute(0, 2, 1, 3)), kbar_r)
+    # the oracle's pooled keys feed the GPU scores, so both rank the same numbers
+    kbp_r = torch.zeros((n_pages, Hkv, D), dtype=dt)
+    for b in range(B):
+        for m in range(maxb):
+            kbp_r[table[b, m]] = torch.tensor(kbar_r[b, :, m]).to(dt)
+    o = torch.empty((B, Hq, D), dtype=dt, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, Hkv, max(topk, 1)), dtype=torch.int32, device=DEV)
+    ws = sas.workspace(sas.SAS_OP_PAGED_DECODE, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
+    scale = w.scale
+    sas.sas_paged_decode(q.to(DEV), kpd, vpd, kbp_r.to(DEV), tbd, lens.to(DEV), topk, o, lse, block, scale,
+                         idx_out=idx if topk > 0 else None, workspace=ws)
+    torch.cuda.synchronize()
+    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, True)
+    c = np.maximum(lens.numpy() - 1, 0) // block
+    idx_ref = np.zeros((B, Hkv, 0), dtype=np.int64)  # topk 0: the current block only
+    active = lens.numpy() > 0
+    if topk > 0:
+        idx_ref = orc.topk_select(u_ref[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+        # rows whose K-th and (K+1)-th scores are a near-tie may legitimately differ
+        srt = -np.sort(-np.where(np.isfinite(u_ref), u_ref, -np.inf), axis=-1)
+        gap = np.abs(srt[..., topk - 1] - srt[..., topk]) if u_ref.shape[-1] > topk else np.full(srt.shape[:2], np.inf)
+        firm = np.all((gap > 1e-4 * np.abs(srt[..., topk - 1]) + 1e-6) | (c[:, None] <= topk), axis=1)
+        got = idx.cpu().numpy()
+        assert np.array_equal(got[firm], idx_ref[firm]), "paged Top-K"
+        active = active & firm
+    o_ref, lse_ref = orc.sparse_decode(to64(q), to64(kc), to64(vc), lens.numpy(), idx_ref, block, scale)
+    max_abs(to64(o)[active], o_ref[active], 2e-2, "o")
+    normwise(to64(lse)[active], lse_ref[active], 1e-4, "lse")
+    idle = lens.numpy() <= 0
+    assert torch.all(o[torch.tensor(idle)] == 0)

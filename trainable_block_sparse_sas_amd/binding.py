@@ -25,9 +25,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 SAS_OK, SAS_EINVAL, SAS_EUNSUPPORTED, SAS_EHIP, SAS_EWORKSPACE = 0, -1, -2, -3, -4
 SAS_F32, SAS_BF16 = 0, 1
 SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTOR_BWD = 1, 2, 3, 4, 5, 6
+SAS_OP_PAGED_DECODE = 7
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-            "sas_sparse_decode", "sas_selector_bwd", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
+            "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -37,6 +39,8 @@ _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
+_lib.sas_pool_pages.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+_lib.sas_paged_decode.argtypes = [_vp] * 5 + [_i, _vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_workspace_bytes.argtypes = [_i] * 9
 _lib.sas_workspace_bytes.restype = _sz
 _lib.sas_last_error.restype = ctypes.c_char_p
@@ -47,7 +51,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-              "sas_sparse_decode", "sas_selector_bwd"):
+              "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode"):
     getattr(_lib, _name).restype = _i
 
 
@@ -216,3 +220,21 @@ def sas_selector_bwd(q, kbar, ds, dq, dk, block, scale, dkbar=None, accumulate=F
     _check(_lib.sas_selector_bwd(_p(q), _p(kbar), _p(ds), _p(dq), _p(dk), _p(dkbar), B, Hq, Hkv, N, D,
                                  block, scale, 1 if accumulate else 0, _dt(q), _p(workspace), wsb,
                                  _stream(stream)))
+
+
+def sas_pool_pages(k_pages, kbar_pages, pages, block, stream=None):
+    """k_pages [P,Hkv,block,D] -> kbar_pages [P,Hkv,D] rows of the int32 page list `pages`."""
+    Hkv, D = k_pages.shape[1], k_pages.shape[3]
+    _check(_lib.sas_pool_pages(_p(k_pages), _p(kbar_pages), _p(pages), pages.numel(), Hkv, D, block, _dt(k_pages),
+                               _stream(stream)))
+
+
+def sas_paged_decode(q, k_pages, v_pages, kbar_pages, block_table, cache_len, topk, o, lse, block, scale,
+                     idx_out=None, workspace=None, stream=None):
+    """q [B,Hq,D]; pages [P,Hkv,block,D]; kbar_pages [P,Hkv,D]; block_table int32 [B,max_blocks]."""
+    B, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_paged_decode(_p(q), _p(k_pages), _p(v_pages), _p(kbar_pages), _p(block_table),
+                                 block_table.shape[1], _p(cache_len), topk, _p(o), _p(lse), _p(idx_out), B, Hq,
+                                 Hkv, D, block, scale, _dt(q), _p(workspace), wsb, _stream(stream)))

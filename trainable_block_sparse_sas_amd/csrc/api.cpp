@@ -46,6 +46,21 @@ int check_common(int B, int Hq, int Hkv, int n, int D, int block, int dtype, con
 
 bool empty(int B, int Hq, int n) { return B == 0 || Hq == 0 || n == 0; }
 
+// Paged decode workspace: group-summed scores, the selected blocks, the
+// attention partials.
+struct PagedWs {
+  size_t scores, idx, part, total;
+};
+PagedWs paged_ws(int B, int Hq, int Hkv, int L_max, int D, int block, int topk) {
+  PagedWs w{};
+  const size_t C = size_t(L_max / block);
+  w.scores = 0;
+  w.idx = sas::align_up(size_t(B) * Hkv * C * sizeof(float));
+  w.part = w.idx + sas::align_up(size_t(B) * Hkv * size_t(topk > 0 ? topk : 1) * sizeof(int32_t));
+  w.total = w.part + sas::decode_workspace(B, Hq, Hkv, L_max, D, block, topk);
+  return w;
+}
+
 // The logit scale must be a positive finite number (the kernels take the row
 // maximum of the raw scores, which is the maximum of the scaled ones only for
 // a positive scale).
@@ -81,6 +96,9 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
     case SAS_OP_SELECTOR_BWD:
       if (D != 64 && D != 128) return size_t(-1);
       return sas::selector_bwd_workspace(d, bf16);
+    case SAS_OP_PAGED_DECODE:
+      if (topk < 0) return size_t(-1);
+      return paged_ws(B, Hq, Hkv, n, D, block, topk).total;
     default:
       return size_t(-1);
   }
@@ -232,6 +250,61 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                                     D, block, idx ? topk : -1, scale, dtype == SAS_BF16, workspace,
                                     static_cast<hipStream_t>(stream));
   return hip_status(e, "sas_sparse_decode");
+}
+
+int sas_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages, int n_pages, int Hkv,
+                   int D, int block, int dtype, void* stream) {
+  int st = check_common(1, Hkv, Hkv, 0, D, block, dtype, "sas_pool_pages");
+  if (st) return st;
+  if (n_pages < 0) return fail(SAS_EINVAL, "sas_pool_pages: n_pages must be >= 0");
+  if (n_pages == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!k_pages || !kbar_pages || !pages)
+    return fail(SAS_EINVAL, "sas_pool_pages: k_pages, kbar_pages and pages must be non-NULL");
+  hipError_t e = sas::launch_pool_pages(k_pages, kbar_pages, pages, n_pages, Hkv, D, block, dtype == SAS_BF16,
+                                        static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_pool_pages");
+}
+
+int sas_paged_decode(const void* q, const void* k_pages, const void* v_pages, const void* kbar_pages,
+                     const int32_t* block_table, int max_blocks, const int32_t* cache_len, int topk,
+                     void* o, float* lse, int32_t* idx_out, int B, int Hq, int Hkv, int D, int block,
+                     float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (max_blocks < 0 || block < 1) return fail(SAS_EINVAL, "sas_paged_decode: max_blocks >= 0 and block >= 1 required");
+  if (max_blocks > kMaxBlocks) return fail(SAS_EUNSUPPORTED, "sas_paged_decode: max_blocks %d > %d", max_blocks, kMaxBlocks);
+  if (size_t(max_blocks) * size_t(block) > size_t(0x7fffffff))
+    return fail(SAS_EINVAL, "sas_paged_decode: max_blocks * block too large");
+  const int L_max = max_blocks * block;
+  int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, "sas_paged_decode");
+  if (!st) st = check_scale(scale, "sas_paged_decode");
+  if (st) return st;
+  if (dtype != SAS_BF16) return fail(SAS_EUNSUPPORTED, "sas_paged_decode: bf16 only");
+  if (Hq / Hkv > kMaxGroupDecode)
+    return fail(SAS_EUNSUPPORTED, "sas_paged_decode: at most %d query heads per KV head", kMaxGroupDecode);
+  if (topk < 0) return fail(SAS_EINVAL, "sas_paged_decode: topk must be >= 0");
+  if (topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "sas_paged_decode: topk %d > %d", topk, kMaxTopk);
+  if (B == 0 || Hq == 0 || max_blocks == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k_pages || !v_pages || !kbar_pages || !block_table || !cache_len || !o)
+    return fail(SAS_EINVAL, "sas_paged_decode: q, pages, pooled keys, block_table, cache_len and o must be non-NULL");
+  const PagedWs W = paged_ws(B, Hq, Hkv, L_max, D, block, topk);
+  if (!workspace || workspace_bytes < W.total)
+    return fail(SAS_EWORKSPACE, "sas_paged_decode: workspace of %zu bytes required (got %zu)", W.total, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(w + W.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + W.idx);
+  hipError_t e = sas::launch_score_decode(q, kbar_pages, scores, cache_len, B, Hq, Hkv, L_max, D, block,
+                                          max_blocks, scale, true, true, s, block_table);
+  if (e == hipSuccess && topk > 0) e = sas::launch_topk(scores, idx, cache_len, B, Hkv, 1, 1, max_blocks, block, topk, s);
+  if (e == hipSuccess)
+    e = sas::launch_decode(q, k_pages, v_pages, cache_len, idx, o, lse, B, Hq, Hkv, L_max, D, block, topk, scale,
+                           true, w + W.part, s, block_table);
+  return hip_status(e, "sas_paged_decode");
 }
 
 int sas_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq, void* dk,

@@ -31,6 +31,7 @@ struct DecodeArgs {
   float* part;  // [B, Hkv, P, G, D + 2]
   int Hq, Hkv, L, D, block, topk, C, EPW, P;
   float scale;
+  const int32_t* table;  // null: kc, vc [B, Hkv, L, D]; else pages [num_pages, Hkv, block, D]
 };
 
 constexpr int kMaxTopk = 256;
@@ -269,8 +270,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   len = len > a.L ? a.L : len;
   const int pos = len - 1;
   const int c = len > 0 ? pos / a.block : 0;
-  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(a.kc) + (size_t(b) * a.Hkv + g) * size_t(a.L) * D;
-  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(a.vc) + (size_t(b) * a.Hkv + g) * size_t(a.L) * D;
+  // row 0 of block m of this (b, g): contiguous cache or the block's page
+  auto block_base = [&](const void* base, int m) -> const bf16_t* {
+    const bf16_t* p = reinterpret_cast<const bf16_t*>(base);
+    if (a.table) return p + (size_t(a.table[size_t(b) * a.C + m]) * a.Hkv + g) * size_t(a.block) * D;
+    return p + ((size_t(b) * a.Hkv + g) * size_t(a.L) + size_t(m) * a.block) * D;
+  };
 
   auto step_range = [&](int e, int& j0, int& j_end) -> bool {
     const int m = len > 0 ? entry_block(a, ir_sh, e, c) : -1;
@@ -281,11 +286,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   };
   // K of the wave's 16 keys into registers, V of the step's 64 keys into LDS
   // stage `st` (rows beyond j_end repeat row j0: finite, and their P is 0).
+  // A step never leaves its block: positions j map to row j - m b of block m.
   auto issue = [&](int j0, int j_end, uint4* kd, int st) {
+    const int m = j0 / a.block, jb = m * a.block;
+    const bf16_t* kb = block_base(a.kc, m) - size_t(jb) * D;
+    const bf16_t* vb = block_base(a.vc, m) - size_t(jb) * D;
     const int j = j0 + wave * 16 + lr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kd[ks] = j < j_end ? *reinterpret_cast<const uint4*>(kbase + size_t(j) * D + (lq * KS + ks) * 8)
+      kd[ks] = j < j_end ? *reinterpret_cast<const uint4*>(kb + size_t(j) * D + (lq * KS + ks) * 8)
                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       const int sl = 64 * piece + lane;  // 16-byte slot: row r, stored chunk pc
       const int r = sl / CH, pc = sl % CH;
       const int jr = j0 + r < j_end ? j0 + r : j0;
-      dma16_to_lds(vbase + size_t(jr) * D + ((pc ^ k_swz<D>(r)) * 8), Vs[st] + piece * 512);
+      dma16_to_lds(vb + size_t(jr) * D + ((pc ^ k_swz<D>(r)) * 8), Vs[st] + piece * 512);
     }
   };
 
@@ -541,13 +550,13 @@ size_t decode_workspace(int B, int Hq, int Hkv, int L_max, int D, int block, int
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* cache_len,
                          const int32_t* idx, void* o, float* lse, int B, int Hq, int Hkv,
                          int L_max, int D, int block, int topk, float scale, bool bf16, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const int32_t* table) {
   if (B == 0 || Hq == 0) return hipSuccess;
   int E, w, P;
   decode_plan(B, Hkv, L_max, block, idx ? topk : -1, &E, &w, &P);
   if (P > kMergeMax) return hipErrorInvalidValue;  // decode_plan keeps P <= 2049
   DecodeArgs a{q, kc, vc, cache_len, idx, (float*)ws, Hq, Hkv, L_max, D, block,
-               idx ? topk : 0, L_max / block, w, P, scale};
+               idx ? topk : 0, L_max / block, w, P, scale, table};
   if (bf16) {
     if (D == 64) return decode_mfma_t<64>(a, B, (bf16_t*)o, lse, s);
     return decode_mfma_t<128>(a, B, (bf16_t*)o, lse, s);

@@ -50,10 +50,14 @@ hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, 
                        int C, bool bf16, hipStream_t s);
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
                               float scale, bool group_sum, bool bf16, hipStream_t s);
+// table (bf16 only): pooled key m of sequence b is row table[b * C + m] of
+// kbar [num_pages, Hkv, D].
 hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
                                const int32_t* cache_len, int B, int Hq, int Hkv, int L, int D,
                                int block, int C, float scale, bool group_sum, bool bf16,
-                               hipStream_t s);
+                               hipStream_t s, const int32_t* table = nullptr);
+hipError_t launch_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages, int n_pages,
+                             int Hkv, int D, int block, bool bf16, hipStream_t s);
 
 // ---- Top-K ------------------------------------------------------------------------
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B,
@@ -103,9 +107,11 @@ hipError_t launch_selector_bwd(const void* q, const void* kbar, const float* ds,
                                float* dkbar, const Dims& d, float scale, bool accumulate, bool bf16,
                                void* ws, hipStream_t s);
 size_t decode_workspace(int B, int Hq, int Hkv, int L_max, int D, int block, int topk);
+// table (bf16 only): block m of sequence b is page table[b * (L_max / block) + m]
+// of kc, vc [num_pages, Hkv, block, D].
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* cache_len,
                          const int32_t* idx, void* o, float* lse, int B, int Hq, int Hkv,
                          int L_max, int D, int block, int topk, float scale, bool bf16, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const int32_t* table = nullptr);
 
 }  // namespace sas

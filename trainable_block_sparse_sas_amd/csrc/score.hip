@@ -25,6 +25,21 @@ __global__ void pool_kernel(const T* __restrict__ k, T* __restrict__ kbar, int H
   }
 }
 
+// Pooled keys of cache pages: kbar_pages[p, g] = mean of the `block` keys of
+// page p, head g ([num_pages, Hkv, block, D] -> [num_pages, Hkv, D]); one
+// workgroup per (listed page, KV head).
+template <typename T>
+__global__ void pool_pages_kernel(const T* __restrict__ kp, T* __restrict__ kbar,
+                                  const int32_t* __restrict__ pages, int Hkv, int D, int block) {
+  const int p = pages[blockIdx.x], g = blockIdx.y;
+  const T* src = kp + (size_t(p) * Hkv + g) * size_t(block) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < block; ++j) acc += to_f32(src[size_t(j) * D + d]);
+    kbar[(size_t(p) * Hkv + g) * D + d] = from_f32<T>(acc / float(block));
+  }
+}
+
 // Training scores: a workgroup owns 64 query rows of one KV head and loops over
 // that head's G query heads and over 64-wide tiles of blocks.  Tiles are staged
 // in LDS as fp32; each thread produces 4 rows x 4 blocks per tile.
@@ -242,12 +257,14 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 // use the same column order), i.e. 64 contiguous bytes per lane.  Each wave
 // scores TPW tiles with all loads issued first (they do not depend on
 // cache_len).  The heads' scores of block lr come out in lanes lr, lr + 16,
-// lr + 32, lr + 48 (4 heads each) and are added in head-index order.
+// lr + 32, lr + 48 (4 heads each) and are added in head-index order.  With a
+// page table, pooled key m of sequence b is row table[b, m] of kbar
+// [num_pages, Hkv, D] (pages past the sequence's history are not read).
 template <int D, int G, int TPW>
 __global__ __launch_bounds__(256) void score_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kbar, float* __restrict__ out,
     const int32_t* __restrict__ cache_len, int Hq, int Hkv, int L, int C, int block, float scale,
-    int group_sum) {
+    int group_sum, const int32_t* __restrict__ table) {
   constexpr int KS = D / 32;
   static_assert(G <= 16, "one 16-row tile of heads");
   const int g = blockIdx.y, b = blockIdx.z;
@@ -255,14 +272,22 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(
   const int lr = lane & 15, lq = lane >> 4;
   const int m0 = (blockIdx.x * 4 + wave) * TPW * 16;  // first block of the wave
   const bf16_t* kb = kbar + (size_t(b) * Hkv + g) * size_t(C) * D;
+  int hist = C;  // blocks that may be read: all of them, or the history when paged
+  if (table) {
+    int len0 = cache_len[b];
+    len0 = len0 > L ? L : len0;
+    hist = len0 > 0 ? min((len0 - 1) / block, C) : 0;
+  }
   uint4 kf[TPW][KS];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int m = m0 + tt * 16 + lr;
+    const bf16_t* row = nullptr;
+    if (m < hist)
+      row = table ? kbar + (size_t(table[size_t(b) * C + m]) * Hkv + g) * D : kb + size_t(m) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[tt][ks] = m < C ? *reinterpret_cast<const uint4*>(kb + size_t(m) * D + (lq * KS + ks) * 8)
-                         : make_uint4(0, 0, 0, 0);
+      kf[tt][ks] = row ? *reinterpret_cast<const uint4*>(row + (lq * KS + ks) * 8) : make_uint4(0, 0, 0, 0);
   }
   uint4 qa[KS];
   {
@@ -361,7 +386,7 @@ hipError_t launch_score_train(const void* q, const void* kbar, float* scores, co
 template <int D>
 static void score_decode_mfma_t(const void* q, const void* kbar, float* scores, const int32_t* cl,
                                 int B, int Hq, int Hkv, int L, int block, int C, float scale,
-                                bool group_sum, hipStream_t s) {
+                                bool group_sum, const int32_t* table, hipStream_t s) {
   constexpr int TPW = 2;
   const int rows_per_wg = 4 * TPW * 16;
   dim3 grid((C + rows_per_wg - 1) / rows_per_wg, Hkv, B);
@@ -370,7 +395,7 @@ static void score_decode_mfma_t(const void* q, const void* kbar, float* scores, 
   case GG:                                                                                         \
     SAS_LAUNCH("score_decode", (score_decode_mfma_kernel<D, GG, TPW>), grid, dim3(256), 0, s,       \
                (const bf16_t*)q, (const bf16_t*)kbar, scores, cl, Hq, Hkv, L, C, block, scale,      \
-               group_sum ? 1 : 0);                                                                 \
+               group_sum ? 1 : 0, table);                                                          \
     break;
     SAS_SCDM_G(1) SAS_SCDM_G(2) SAS_SCDM_G(3) SAS_SCDM_G(4) SAS_SCDM_G(5) SAS_SCDM_G(6) SAS_SCDM_G(7)
     SAS_SCDM_G(8) SAS_SCDM_G(9) SAS_SCDM_G(10) SAS_SCDM_G(11) SAS_SCDM_G(12) SAS_SCDM_G(13)
@@ -402,14 +427,27 @@ static void score_decode_t(const void* q, const void* kbar, float* scores, const
   }
 }
 
+hipError_t launch_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages, int n_pages,
+                             int Hkv, int D, int block, bool bf16, hipStream_t s) {
+  if (n_pages == 0 || Hkv == 0) return hipSuccess;
+  dim3 grid(n_pages, Hkv);
+  if (bf16)
+    SAS_LAUNCH("pool_pages", pool_pages_kernel<bf16_t>, grid, dim3(D), 0, s, (const bf16_t*)k_pages,
+               (bf16_t*)kbar_pages, pages, Hkv, D, block);
+  else
+    SAS_LAUNCH("pool_pages", pool_pages_kernel<float>, grid, dim3(D), 0, s, (const float*)k_pages,
+               (float*)kbar_pages, pages, Hkv, D, block);
+  return hipGetLastError();
+}
+
 hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
                                const int32_t* cache_len, int B, int Hq, int Hkv, int L, int D,
                                int block, int C, float scale, bool group_sum, bool bf16,
-                               hipStream_t s) {
+                               hipStream_t s, const int32_t* table) {
   if (B == 0 || C == 0) return hipSuccess;
   if (bf16) {
-    if (D == 64) score_decode_mfma_t<64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
-    else score_decode_mfma_t<128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
+    if (D == 64) score_decode_mfma_t<64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, table, s);
+    else score_decode_mfma_t<128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, table, s);
   } else {
     if (D == 64) score_decode_t<float, 64>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
     else score_decode_t<float, 128>(q, kbar, scores, cache_len, B, Hq, Hkv, L, block, C, scale, group_sum, s);
