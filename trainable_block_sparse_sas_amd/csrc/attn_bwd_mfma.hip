@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         for (int j = 0; j < n / 2; ++j) {
           const float send = hi ? dsum[j] : dsum[j + n / 2];
           const float keep = hi ? dsum[j + n / 2] : dsum[j];
-          dsum[j] = keep + __shfl_xor(send, M, 64);
+          dsum[j] = keep + __uint_as_float(lanes_xor(__float_as_uint(send), M, ln));
         }
       }
       dbs_sh[wave * RS + 16 * (lr >> 2) + 4 * lq + (lr & 3)] = dsum[0];

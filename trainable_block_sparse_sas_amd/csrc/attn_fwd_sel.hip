@@ -198,8 +198,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
           if (MASK) x[kt][i] = j0 + 16 * kt + 4 * lq + i <= tlim ? x[kt][i] : kNegInf;
           mx = fmaxf(mx, x[kt][i]);
         }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_xrows(mx);
       const float ms = mx == kNegInf ? 0.f : mx;
       float l = 0.f;
       uint4 pb[2];
@@ -216,8 +215,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         pb[kk] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                             pack_bf16(p[6], p[7]));
       }
-      l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
+      l = sum_xrows(l);
       f32x4 oacc[ND];
 #pragma unroll
       for (int md = 0; md < ND; ++md) oacc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
