@@ -283,25 +283,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         p[i] = exp2_hw(x);
         d[i] = p[i] * (pacc[rs][i] - dl[i]);
       }
-      if constexpr (SPARSE) {
-        // dS rows for the dQ pass, and this wave's share of the row sums
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst_sh[(r0 + i) * TST + wave * 16 + lr] = f32_to_bf16(d[i]);
-          dsum[4 * rs + i] = d[i];
-        }
-      }
       const int kk = rs >> 1;
+      const uint32_t d01 = pack_bf16(d[0], d[1]), d23 = pack_bf16(d[2], d[3]);
       if (rs & 1) {
         pa[kk].z = pack_bf16(p[0], p[1]);
         pa[kk].w = pack_bf16(p[2], p[3]);
-        dsa[kk].z = pack_bf16(d[0], d[1]);
-        dsa[kk].w = pack_bf16(d[2], d[3]);
+        dsa[kk].z = d01;
+        dsa[kk].w = d23;
       } else {
         pa[kk].x = pack_bf16(p[0], p[1]);
         pa[kk].y = pack_bf16(p[2], p[3]);
-        dsa[kk].x = pack_bf16(d[0], d[1]);
-        dsa[kk].y = pack_bf16(d[2], d[3]);
+        dsa[kk].x = d01;
+        dsa[kk].y = d23;
+      }
+      if constexpr (SPARSE) {
+        // dS rows for the dQ pass (the bf16 values of the MFMA operand), and
+        // this wave's share of the row sums
+        uint16_t* col = dst_sh + r0 * TST + wave * 16 + lr;
+        col[0] = uint16_t(d01);
+        col[TST] = uint16_t(d01 >> 16);
+        col[2 * TST] = uint16_t(d23);
+        col[3 * TST] = uint16_t(d23 >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsum[4 * rs + i] = d[i];
       }
     }
     // dV += P^T dO, dK += dS^T Q.  B operand (32 rows x 16 columns) read

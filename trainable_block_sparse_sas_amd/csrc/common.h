@@ -18,11 +18,10 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
 }
 
 // float -> bfloat16 with round-to-nearest-even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950; NaN
+// stays NaN).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T>
