@@ -197,6 +197,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     if constexpr (decltype(tag)::value == 0) return R0;
     else return R1;
   };
+  // Per-lane offsets that stay fixed from step to step, kept in registers: the
+  // Q / dO source of each 1 KB piece relative to token 0 and the row whose
+  // token it gathers, the stat row base of the lane's row, and the LDS
+  // offsets of the transposed reads of the Q / dO tile.
+  int prow[PPW];
+  size_t poff[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int sl = 64 * (wave * PPW + i) + lane;  // 16-byte slot: row r, stored chunk pc
+    const int r = sl / CH, pc = sl % CH;
+    prow[i] = r;
+    poff[i] = (hrow0 + size_t(r % G) * N) * D + ((pc ^ k_swz<D>(r)) * 8);
+  }
+  const size_t srow = hrow0 + size_t(lane % G) * N;
+  int troff[ND][2][2];
+  {
+    const int lr = lane & 15, lq = lane >> 4;
+    const int trow = 4 * lq + (lr >> 2), tcol = 4 * (lr & 3);
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ra = 32 * kk + 16 * h + trow;
+          const int col = 16 * nd + tcol;
+          troff[nd][kk][h] = ra * D + (((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7);
+        }
+  }
   // Loads of step k into stage `tag`; tk: token of the lane's row ln of the
   // step (ln: opaque lane index).
   auto issue = [&](auto tag, int k, int tk, int ln) {
@@ -205,20 +234,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     uint16_t* st = rst(tag);
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-      const int j = wave * PPW + i;          // 1 KB piece of the Q (dO) tile
-      const int sl = 64 * j + ln;            // 16-byte slot: row r, stored chunk pc
-      const int r = sl / CH, pc = sl % CH;
-      const int t = __shfl(tk, r, 64);
-      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
-      const int c = pc ^ k_swz<D>(r);
-      __builtin_amdgcn_global_load_lds(a.q + gr * D + c * 8, (lds_ptr_t)(st + j * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.dout + gr * D + c * 8, (lds_ptr_t)(st + ST_DO + j * 512), 16, 0,
-                                       0);
+      const int j = wave * PPW + i;  // 1 KB piece of the Q (dO) tile
+      const int t = __shfl(tk, prow[i], 64);
+      const size_t off = poff[i] + size_t(t >= 0 ? t : 0) * D;
+      __builtin_amdgcn_global_load_lds(a.q + off, (lds_ptr_t)(st + j * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.dout + off, (lds_ptr_t)(st + ST_DO + j * 512), 16, 0, 0);
     }
     {
       const int r = ln;  // stat `wave` of row r
       const int t = tk;
-      const size_t gr = hrow0 + size_t(r % G) * N + (t >= 0 ? t : 0);
+      const size_t gr = srow + (t >= 0 ? t : 0);
       // (own-block rows use no score; they read lse there, which always exists)
       const float* src = wave == 0 ? a.lse + gr
                        : wave == 1 ? a.delta + gr
@@ -311,16 +336,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     // dV += P^T dO, dK += dS^T Q.  B operand (32 rows x 16 columns) read
     // transposed: lane s of group lq points at row 32 kk + 4 lq + s / 4 (and
     // + 16), column 16 nd + 4 (s % 4).
-    const int trow = 4 * lq + (lr >> 2);
-    const int tcol = 4 * (lr & 3);
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int ra = 32 * kk + trow, rb = ra + 16;
-        const int col = 16 * nd + tcol;
-        const int oa = ra * D + (((col >> 3) ^ k_swz<D>(ra)) << 3) + (col & 7);
-        const int ob = rb * D + (((col >> 3) ^ k_swz<D>(rb)) << 3) + (col & 7);
+        const int oa = troff[nd][kk][0], ob = troff[nd][kk][1];
         const uint2 o0 = lds_read_tr16(dOs + oa), o1 = lds_read_tr16(dOs + ob);
         const uint2 q0 = lds_read_tr16(Qs + oa), q1 = lds_read_tr16(Qs + ob);
         dv[nd] = mfma16(pa[kk], make_uint4(o0.x, o0.y, o1.x, o1.y), dv[nd]);
