@@ -27,24 +27,37 @@ namespace {
 constexpr int SEG = 2048;          // tokens per segment of the count / fill passes
 constexpr int kSegsPerSpan = 2;    // segments per token span of the work items
 
+// One wave per token: lane e ORs its entry's bit into the wave's words in LDS
+// (a repeated entry sets the same bit), then lane w takes word w.
+constexpr int kMaxWords = 512;  // 16384 blocks, the most a sparse-scope call accepts
+
 __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
                                                       uint32_t* __restrict__ bits,
                                                       uint16_t* __restrict__ pre, int N, int topk,
                                                       int block, int MWB, size_t tokens) {
+  __shared__ uint32_t wsh[4][kMaxWords];
   const size_t tok = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (tok >= tokens) return;
   const int t = int(tok % N);
   const int c = t / block;
   const int32_t* ir = idx + tok * topk;
+  uint32_t* ws = wsh[wave];
+  for (int w = lane; w < MWB; w += 64) ws[w] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int e = lane; e < topk; e += 64) {
+    const int m = ir[e];
+    if (m >= 0 && m < c) atomicOr(ws + (m >> 5), 1u << (m & 31));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int carry = 0;
   for (int w0 = 0; w0 < MWB; w0 += 64) {
     const int w = w0 + lane;
-    uint32_t word = 0;
-    for (int e = 0; e < topk; ++e) {
-      const int m = ir[e];
-      if (m >= 0 && m < c && (m >> 5) == w) word |= 1u << (m & 31);
-    }
+    const uint32_t word = w < MWB ? ws[w] : 0u;
     if (w < MWB) bits[tok * MWB + w] = word;
     const int cnt = __popc(word);
     int incl = cnt;
@@ -86,7 +99,7 @@ __global__ __launch_bounds__(64) void sel_pass_kernel(SelLists L, int N, int C, 
       const bool sel = (word >> b) & 1u;
       const unsigned long long bal = __ballot(sel);
       if (bal == 0ull) continue;
-      const uint32_t rb = __shfl(run, b, 64);
+      const uint32_t rb = uint32_t(__builtin_amdgcn_readlane(int(run), b));
       if (FILL && sel) {
         const uint32_t slot = uint32_t(base + __popc(word & ((1u << b) - 1u)));
         const uint32_t at = rb + uint32_t(__popcll(bal & lt));
@@ -240,6 +253,7 @@ hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hk
                             int topk, int block, hipStream_t s) {
   const size_t tokens = size_t(B) * Hkv * N;
   const int pairs = B * Hkv;
+  if (L.MWB > kMaxWords) return hipErrorInvalidValue;  // more blocks than the entry points accept
   SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, idx, L.bits, L.pre, N,
              topk, block, L.MWB, tokens);
   if (C > 0) {
