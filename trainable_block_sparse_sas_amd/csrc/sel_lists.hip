@@ -149,21 +149,44 @@ __global__ __launch_bounds__(1024) void sel_scan_kernel(SelLists L, int N, int C
   uint32_t ecarry = 0;
   for (int m0 = 0; m0 < NB; m0 += 1024) {
     const int m = m0 + tid;
+    // a block's segment counts are one contiguous row (16-byte pieces when
+    // nseg is a multiple of 4)
+    const bool vec = (nseg & 3) == 0;
+    const size_t rowc = (size_t(pair) * NB + m) * nseg;
     uint32_t cm = 0;
-    if (m < C)
-      for (int sg = 0; sg < nseg; ++sg) cm += L.cnt[(size_t(pair) * NB + m) * nseg + sg];
+    if (m < C) {
+      if (vec)
+        for (int sg = 0; sg < nseg; sg += 4) {
+          const uint4 c4 = *reinterpret_cast<const uint4*>(L.cnt + rowc + sg);
+          cm += c4.x + c4.y + c4.z + c4.w;
+        }
+      else
+        for (int sg = 0; sg < nseg; ++sg) cm += L.cnt[rowc + sg];
+    }
     uint32_t etot;
     const uint32_t eoff = ecarry + block_scan_excl(cm, sh, &etot);
     if (m < NB) {
       L.blkoff[size_t(pair) * (NB + 1) + m] = eoff;
       uint32_t run = eoff;
-      if (m < C)
-        for (int sg = 0; sg < nseg; ++sg) {
-          const size_t cell = (size_t(pair) * NB + m) * nseg + sg;
-          const uint32_t c = L.cnt[cell];
-          L.segoff[cell] = run;
-          run += c;
-        }
+      if (m < C) {
+        if (vec)
+          for (int sg = 0; sg < nseg; sg += 4) {
+            const uint4 c4 = *reinterpret_cast<const uint4*>(L.cnt + rowc + sg);
+            uint4 o;
+            o.x = run;
+            o.y = o.x + c4.x;
+            o.z = o.y + c4.y;
+            o.w = o.z + c4.z;
+            run = o.w + c4.w;
+            *reinterpret_cast<uint4*>(L.segoff + rowc + sg) = o;
+          }
+        else
+          for (int sg = 0; sg < nseg; ++sg) {
+            const uint32_t c = L.cnt[rowc + sg];
+            L.segoff[rowc + sg] = run;
+            run += c;
+          }
+      }
     }
     ecarry += etot;
   }
