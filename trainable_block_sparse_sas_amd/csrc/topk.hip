@@ -622,13 +622,106 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
     out[e] = e < K ? int(~uint32_t(runs[buf][0][e])) : -1;
 }
 
+// Rows of up to 1024 candidates with K <= 64 (training): one wave per row and
+// no workgroup barrier.  The K-th largest of the lanes' maximum score keys
+// bounds the K-th key from below (candidate m < 64 sits alone on lane m, and
+// c >= K), so only keys at or above it survive; with many equal scores (more
+// than 64 survivors) the wave radix select picks exactly K instead.  The
+// survivors are sorted in one 64-lane bitonic network, lane e holding the
+// e-th largest.
+template <int PER>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores,
+                                                        int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ cache_len, int Hkv,
+                                                        int hpr, int Nq, int C, int block, int topk,
+                                                        long total_rows) {
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint64_t surv[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long row = long(blockIdx.x) * 4 + w;
+  if (row >= total_rows) return;  // waves are independent: no workgroup barrier below
+  const long t = row % Nq, bg = row / Nq;
+  const int b = int(bg / Hkv), g = int(bg % Hkv);
+  int c;
+  if (cache_len) {
+    const int len = cache_len[b];
+    c = len > 0 ? (len - 1) / block : 0;
+  } else {
+    c = int(t / block);
+  }
+  c = c < C ? c : C;
+  const int K = topk < c ? topk : c;
+  int32_t* out = idx + size_t(row) * topk;
+  if (K == 0) {
+    if (lane < topk) out[lane] = -1;
+    return;
+  }
+  uint32_t hk[PER];
+  uint32_t fmax = 0;
+  const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int m = i * 64 + lane;
+    hk[i] = 0;
+    if (m < c) {
+      float u = base[m];
+      for (int h = 1; h < hpr; ++h) u = u + base[size_t(h) * Nq * C + m];
+      hk[i] = score_key(u);  // valid score keys are > 0
+    }
+    fmax = fmax > hk[i] ? fmax : hk[i];
+  }
+  uint32_t f[1] = {fmax};
+  build_runs<1, 2, 64, uint32_t>(f, lane);  // lane e: the e-th largest lane maximum
+  const uint32_t tau = uint32_t(__builtin_amdgcn_readlane(int(f[0]), K - 1));
+  int S = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) S += __popcll(__ballot(hk[i] >= tau));
+  bool take[PER];
+  if (S <= 64) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) take[i] = hk[i] >= tau;
+  } else {
+    uint32_t lo[PER];
+    bool valid[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      lo[i] = ~uint32_t(i * 64 + lane);
+      valid[i] = i * 64 + lane < c;
+    }
+    wave_select<PER>(hk, lo, valid, K, hist[w], take);
+  }
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const unsigned long long bt = __ballot(take[i]);
+    if (take[i]) surv[w][n + __popcll(bt & lt)] = (uint64_t(hk[i]) << 32) | uint32_t(~uint32_t(i * 64 + lane));
+    n += __popcll(bt);
+  }
+  wave_sync();
+  uint64_t x[1] = {lane < n ? surv[w][lane] : 0ull};
+  build_runs<1, 2, 64, uint64_t>(x, lane);
+  if (lane < topk) out[lane] = lane < K ? int(~uint32_t(x[0])) : -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
                        int hpr, int Nq, int C, int block, int topk, hipStream_t s) {
   const long rows = long(B) * Hkv * Nq;
   if (rows == 0 || topk == 0) return hipSuccess;
-  if (C <= 256) {
+  if (C <= 1024 && topk <= 64) {
+    const dim3 grid((rows + 3) / 4);
+    if (C <= 256)
+      SAS_LAUNCH("topk", (topk_wave_kernel<4>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
+                 block, topk, rows);
+    else if (C <= 512)
+      SAS_LAUNCH("topk", (topk_wave_kernel<8>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
+                 block, topk, rows);
+    else
+      SAS_LAUNCH("topk", (topk_wave_kernel<16>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
+                 block, topk, rows);
+  } else if (C <= 256) {
     SAS_LAUNCH("topk", (topk_kernel<1, 4>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
   } else if (C <= 1024) {
