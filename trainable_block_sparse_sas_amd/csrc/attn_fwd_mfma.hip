@@ -64,14 +64,39 @@ __global__ __launch_bounds__(256) void lse_rows_kernel(const float* __restrict__
   const int t = int(row % size_t(N));
   const int c = min(t / block, C);
   const float* srow = scores + row * size_t(C);
+  // chunks of 512 history scores: lane holds 4 + 4 consecutive ones, all
+  // loaded before the chunk's max and exp sum
+  const bool vec = (C & 3) == 0;
   float mx = kNegInf, sm = 0.f;
-  for (int m = lane; m < c; m += 64) {
-    const float x = srow[m];
-    if (x > mx) {
-      sm = sm * exp2_hw((mx - x) * kLog2e) + 1.f;
-      mx = x;
-    } else if (mx != kNegInf) {
-      sm += exp2_hw((x - mx) * kLog2e);
+  for (int m0 = 0; m0 < c; m0 += 512) {
+    float x[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mb = m0 + 256 * h + 4 * lane;
+      float4 v = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      if (vec && mb + 3 < c) {
+        v = *reinterpret_cast<const float4*>(srow + mb);
+      } else if (mb < c) {
+        v.x = srow[mb];
+        v.y = mb + 1 < c ? srow[mb + 1] : kNegInf;
+        v.z = mb + 2 < c ? srow[mb + 2] : kNegInf;
+        v.w = mb + 3 < c ? srow[mb + 3] : kNegInf;
+      }
+      x[4 * h + 0] = v.x;
+      x[4 * h + 1] = v.y;
+      x[4 * h + 2] = v.z;
+      x[4 * h + 3] = v.w;
+    }
+    float cm = x[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) cm = fmaxf(cm, x[u]);
+    const float nm = fmaxf(mx, cm);
+    if (nm != kNegInf) {
+      float add = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add += exp2_hw((x[u] - nm) * kLog2e);
+      sm = (mx == kNegInf ? 0.f : sm * exp2_hw((mx - nm) * kLog2e)) + add;
+      mx = nm;
     }
   }
   for (int off = 32; off >= 1; off >>= 1) {
