@@ -20,6 +20,32 @@ namespace {
 
 constexpr int kMaxTopk = 256;
 
+// Group score of each of the lane's PER candidates m[i] (where ok[i]): the sum
+// of the row's hpr head scores, hstride floats apart, added in head order.
+// Every load of a chunk of HC heads is issued before the first add, so a row
+// costs one memory round trip per chunk rather than one per head (HC shrinks
+// as PER grows, to bound the registers the loads hold).
+template <int PER>
+__device__ __forceinline__ void group_sum(const float* __restrict__ row0, size_t hstride, int hpr,
+                                          const int (&m)[PER], const bool (&ok)[PER], float (&u)[PER]) {
+  constexpr int HC = PER <= 8 ? 4 : 1;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) u[i] = 0.f;
+  for (int h0 = 0; h0 < hpr; h0 += HC) {
+    float v[HC][PER];
+#pragma unroll
+    for (int j = 0; j < HC; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        v[j][i] = (h0 + j < hpr && ok[i]) ? row0[size_t(h0 + j) * hstride + m[i]] : 0.f;
+#pragma unroll
+    for (int j = 0; j < HC; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (h0 + j < hpr) u[i] = h0 + j == 0 ? v[j][i] : u[i] + v[j][i];
+  }
+}
+
 // WPR waves cooperate on one row; PER lanes-slots per lane (c <= 64*WPR*PER).
 template <int WPR, int PER>
 __global__ __launch_bounds__(256 * (WPR > 4 ? 4 : 1)) void topk_kernel(
@@ -62,17 +88,17 @@ __global__ __launch_bounds__(256 * (WPR > 4 ? 4 : 1)) void topk_kernel(
   {
     const int g = int(bg % Hkv);
     const int b = int(bg / Hkv);
+    int m[PER];
+    float u[PER];
+#pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int m = (i * WPR + wr) * 64 + lane;
-      valid[i] = active && m < c;
-      key[i] = 0;
-      if (valid[i]) {
-        const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C + m;
-        float u = base[0];
-        for (int h = 1; h < hpr; ++h) u = u + base[size_t(h) * Nq * C];
-        key[i] = score_key(u);
-      }
+      m[i] = (i * WPR + wr) * 64 + lane;
+      valid[i] = active && m[i] < c;
     }
+    group_sum<PER>(scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C, size_t(Nq) * C, hpr, m,
+                   valid, u);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = valid[i] ? score_key(u[i]) : 0u;
   }
   // Radix select of the K-th largest key.
   uint32_t prefix = 0;
@@ -299,17 +325,19 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
 
   uint32_t hi[PER], lo[PER];
   bool valid[PER], take[PER];
-  for (int i = 0; i < PER; ++i) {
-    const int m = (i * 16 + w) * 64 + lane;
-    valid[i] = m < c;
-    hi[i] = 0;
-    lo[i] = ~uint32_t(m);
-    if (valid[i]) {
-      const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C + m;
-      float u = base[0];
-      for (int h = 1; h < hpr; ++h) u = u + base[size_t(h) * Nq * C];
-      hi[i] = score_key(u);
+  {
+    int m[PER];
+    float u[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      m[i] = (i * 16 + w) * 64 + lane;
+      valid[i] = m[i] < c;
+      lo[i] = ~uint32_t(m[i]);
     }
+    group_sum<PER>(scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C, size_t(Nq) * C, hpr, m,
+                   valid, u);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) hi[i] = valid[i] ? score_key(u[i]) : 0u;
   }
   if (K > 0) wave_select<PER>(hi, lo, valid, K, hist[w], take);
   else
@@ -374,7 +402,7 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
 }
 
 // ---- long rows, K <= 64: sorted runs merged in registers --------------------
-// One row per workgroup of 16 waves.  Each lane sorts its PER composite keys
+// One row per workgroup of W waves.  Each lane sorts its PER composite keys
 // (score key << 32 | ~block: all distinct, larger = higher score, ties to the
 // lower block; an invalid candidate is 0) descending with a bitonic network,
 // keeps its best E = min(PER, KP) and groups of R = KP / E lanes build sorted
@@ -383,7 +411,7 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
 // max(A[j], B[KP - 1 - j]), a bitonic sequence that the half-cleaners sort
 // again; both partner groups compute it (one sees the sequence reversed,
 // which sorts to the same run), so after log2(64 / R) rounds every group of
-// the wave holds the wave's best KP keys.  The 16 wave runs are merged the
+// the wave holds the wave's best KP keys.  The W wave runs are merged the
 // same way through LDS.  The final run is the answer in rank order.
 
 __device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int mask) {
@@ -453,14 +481,14 @@ __device__ __forceinline__ void build_runs(T (&v)[E], int lane) {
   }
 }
 
-// Merges the 16 wave runs in runs[0] (each R lanes x E keys, sorted) into
+// Merges the W wave runs in runs[0] (each R lanes x E keys, sorted) into
 // one, GPW = 64 / R runs per merging wave per round; returns the buffer that
 // holds the result in its row 0 (visible to every wave on return).
-template <int E, int R, int KP, typename T>
-__device__ __forceinline__ int merge_block_runs(T (*runs)[16][KP], int w, int lane) {
+template <int E, int R, int KP, int W, typename T>
+__device__ __forceinline__ int merge_block_runs(T (*runs)[W][KP], int w, int lane) {
   constexpr int GPW = 64 / R;
   static_assert(GPW >= 2, "a round must reduce the run count");
-  int nruns = 16, buf = 0;
+  int nruns = W, buf = 0;
   while (nruns > 1) {
     const int nw = (nruns + GPW - 1) / GPW;
     __syncthreads();
@@ -488,8 +516,8 @@ __device__ __forceinline__ int merge_block_runs(T (*runs)[16][KP], int w, int la
 // survivors are barely more than K; when they fit one wave (at most 64) each
 // survivor's rank is counted directly.  Otherwise (many equal scores) the
 // whole row goes through the run merge above.
-template <int PER, int KP>
-__global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict__ scores,
+template <int PER, int KP, int W>
+__global__ __launch_bounds__(64 * W) void topk_runs_kernel(const float* __restrict__ scores,
                                                          int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ cache_len,
                                                          int Hkv, int hpr, int Nq, int C, int block,
@@ -499,26 +527,27 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
   constexpr int E1 = KP <= 8 ? 1 : KP / 8;  // filter: 32-bit runs of KP as E1 x R1
   constexpr int R1 = KP / E1;
   static_assert(R <= 32 && (KP & (KP - 1)) == 0 && (PER & (PER - 1)) == 0, "run shape");
-  __shared__ uint64_t runs[2][16][KP];
-  __shared__ uint32_t fruns[2][16][KP];
+  __shared__ uint64_t runs[2][W][KP];
+  __shared__ uint32_t fruns[2][W][KP];
   __shared__ uint64_t surv[64];
   __shared__ uint32_t rank[64];
-  __shared__ int wcnt[16];
+  __shared__ int wcnt[W];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long row = blockIdx.x;
   const long t = row % Nq, bg = row / Nq;
   const int b = int(bg / Hkv), g = int(bg % Hkv);
   // score loads first: their addresses do not depend on cache_len
   float u[PER];
+  {
+    int m[PER];
+    bool in[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int m = (i * 16 + w) * 64 + lane;
-    u[i] = 0.f;
-    if (m < C) {
-      const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C + m;
-      u[i] = base[0];
-      for (int h = 1; h < hpr; ++h) u[i] = u[i] + base[size_t(h) * Nq * C];
+    for (int i = 0; i < PER; ++i) {
+      m[i] = (i * W + w) * 64 + lane;
+      in[i] = m[i] < C;
     }
+    group_sum<PER>(scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C, size_t(Nq) * C, hpr, m, in,
+                   u);
   }
   if (threadIdx.x < 64) rank[threadIdx.x] = 0;
   int c;
@@ -532,25 +561,25 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
   const int K = topk < c ? topk : c;
   int32_t* out = idx + size_t(row) * topk;
   if (K == 0) {
-    for (int e = threadIdx.x; e < topk; e += 1024) out[e] = -1;
+    for (int e = threadIdx.x; e < topk; e += 64 * W) out[e] = -1;
     return;
   }
   uint64_t key[PER];
   uint32_t fmax = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int m = (i * 16 + w) * 64 + lane;
+    const int m = (i * W + w) * 64 + lane;
     const uint32_t hk = m < c ? score_key(u[i]) : 0u;  // valid score keys are > 0
     key[i] = m < c ? (uint64_t(hk) << 32) | uint32_t(~uint32_t(m)) : 0ull;
     fmax = fmax > hk ? fmax : hk;
   }
-  // ---- filter (candidate m < 1024 sits alone on thread m, so at least K
+  // ---- filter (candidate m < 64 W sits alone on thread m, so at least K
   // lanes hold a valid key): the wave's KP largest lane maxima, then the row's
   uint32_t f[1] = {fmax};
   build_runs<1, 2, KP, uint32_t>(f, lane);
   if constexpr (KP < 64) merge_wave_runs<1, KP, uint32_t>(f, lane);
   if (lane < KP) fruns[0][w][lane] = f[0];
-  int buf = merge_block_runs<E1, R1, KP, uint32_t>(fruns, w, lane);
+  int buf = merge_block_runs<E1, R1, KP, W, uint32_t>(fruns, w, lane);
   const uint32_t tau = fruns[buf][0][K - 1];
   const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   int cnt = 0;
@@ -560,7 +589,7 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
   __syncthreads();
   int S = 0, before = 0;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
+  for (int v = 0; v < W; ++v) {
     before += v < w ? wcnt[v] : 0;
     S += wcnt[v];
   }
@@ -573,13 +602,14 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
       before += __popcll(bt);
     }
     __syncthreads();
-    // rank of survivor `lane`: wave w counts the larger ones among 4w .. 4w+3
+    // rank of survivor `lane`: wave w counts the larger ones among its
+    // 64 / W survivors (64 w / W ...)
     if (lane < S) {
       const uint64_t me = surv[lane];
       uint32_t larger = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = 4 * w + j;
+      for (int j = 0; j < 64 / W; ++j) {
+        const int o = (64 / W) * w + j;
         larger += (o < S && surv[o] > me) ? 1u : 0u;
       }
       if (larger) atomicAdd(&rank[lane], larger);
@@ -617,8 +647,8 @@ __global__ __launch_bounds__(1024) void topk_runs_kernel(const float* __restrict
   if (lane < R)
 #pragma unroll
     for (int r = 0; r < E; ++r) runs[0][w][lane * E + r] = v[r];
-  buf = merge_block_runs<E, R, KP, uint64_t>(runs, w, lane);
-  for (int e = threadIdx.x; e < topk; e += 1024)
+  buf = merge_block_runs<E, R, KP, W, uint64_t>(runs, w, lane);
+  for (int e = threadIdx.x; e < topk; e += 64 * W)
     out[e] = e < K ? int(~uint32_t(runs[buf][0][e])) : -1;
 }
 
@@ -658,17 +688,22 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   }
   uint32_t hk[PER];
   uint32_t fmax = 0;
-  const float* base = scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C;
+  {
+    int m[PER];
+    bool in[PER];
+    float u[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int m = i * 64 + lane;
-    hk[i] = 0;
-    if (m < c) {
-      float u = base[m];
-      for (int h = 1; h < hpr; ++h) u = u + base[size_t(h) * Nq * C + m];
-      hk[i] = score_key(u);  // valid score keys are > 0
+    for (int i = 0; i < PER; ++i) {
+      m[i] = i * 64 + lane;
+      in[i] = m[i] < c;
     }
-    fmax = fmax > hk[i] ? fmax : hk[i];
+    group_sum<PER>(scores + ((size_t(b) * Hkv + g) * hpr * size_t(Nq) + t) * C, size_t(Nq) * C, hpr, m, in,
+                   u);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      hk[i] = in[i] ? score_key(u[i]) : 0u;  // valid score keys are > 0
+      fmax = fmax > hk[i] ? fmax : hk[i];
+    }
   }
   uint32_t f[1] = {fmax};
   build_runs<1, 2, 64, uint32_t>(f, lane);  // lane e: the e-th largest lane maximum
@@ -728,21 +763,20 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
     SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, rows);
   } else if (topk <= 64 && C <= 16384) {
-    // candidates per lane: just enough for C (16 waves x 64 lanes x PER);
-    // run length: the power of two at or above K (at least 8)
-#define SAS_TOPK_RUNS(PER, KP)                                                                          \
-  SAS_LAUNCH("topk_runs", (topk_runs_kernel<PER, KP>), dim3(rows), dim3(1024), 0, s, scores, idx, cache_len, \
-             Hkv, hpr, Nq, C, block, topk)
-#define SAS_TOPK_RUNS_KP(PER)                        \
-  if (topk <= 8) SAS_TOPK_RUNS(PER, 8);               \
-  else if (topk <= 16) SAS_TOPK_RUNS(PER, 16);        \
-  else if (topk <= 32) SAS_TOPK_RUNS(PER, 32);        \
-  else SAS_TOPK_RUNS(PER, 64);
-    const int per = C <= 2048 ? 2 : C <= 4096 ? 4 : C <= 8192 ? 8 : 16;
-    if (per == 2) { SAS_TOPK_RUNS_KP(2) }
-    else if (per == 4) { SAS_TOPK_RUNS_KP(4) }
-    else if (per == 8) { SAS_TOPK_RUNS_KP(8) }
-    else { SAS_TOPK_RUNS_KP(16) }
+    // 8 waves up to 8192 candidates (16 above), PER candidates per lane: just
+    // enough for C; run length: the power of two at or above K (at least 8)
+#define SAS_TOPK_RUNS(PER, KP, W)                                                                     \
+  SAS_LAUNCH("topk_runs", (topk_runs_kernel<PER, KP, W>), dim3(rows), dim3(64 * W), 0, s, scores, idx, \
+             cache_len, Hkv, hpr, Nq, C, block, topk)
+#define SAS_TOPK_RUNS_KP(PER, W)                        \
+  if (topk <= 8) SAS_TOPK_RUNS(PER, 8, W);               \
+  else if (topk <= 16) SAS_TOPK_RUNS(PER, 16, W);        \
+  else if (topk <= 32) SAS_TOPK_RUNS(PER, 32, W);        \
+  else SAS_TOPK_RUNS(PER, 64, W);
+    if (C <= 2048) { SAS_TOPK_RUNS_KP(4, 8) }
+    else if (C <= 4096) { SAS_TOPK_RUNS_KP(8, 8) }
+    else if (C <= 8192) { SAS_TOPK_RUNS_KP(16, 8) }
+    else { SAS_TOPK_RUNS_KP(16, 16) }
 #undef SAS_TOPK_RUNS_KP
 #undef SAS_TOPK_RUNS
   } else {
