@@ -33,7 +33,11 @@ Readings where the pages are silent (each also listed in the design notes):
     scope); unselected history blocks receive -inf logits;
   * decode: the new token is already in the cache at position len-1; it
     attends to its own block plus the selected history blocks with no gate;
-  * idx entries outside [0, c) are ignored and a repeated entry counts once.
+  * idx entries outside [0, c) are ignored and a repeated entry counts once;
+  * gate activations other than the softmax (sigmoid, raw logit: the pages'
+    ablation of the gate activation) keep everything else as it is: the own
+    block's gate is 1, unselected history blocks get -inf, and with no
+    normaliser an unselected block's ds is 0 and LSE_s is reported as 0.
 
 Parity status: every function below is pinned by tests that do not re-type
 its formula (library attention routines, autograd, finite differences,
@@ -235,25 +239,44 @@ def _selection_mask(idx_row_sets, c, C):
     return sel
 
 
-def _row_terms(s_rows, idx_rows, rows, block, N, C):
+GATES = ("softmax", "sigmoid", "raw")
+
+
+def _log_sigmoid(x):
+    """log(1 / (1 + e^-x)) = -log(1 + e^-x), without overflow."""
+    return -np.logaddexp(0.0, -x)
+
+
+def _row_terms(s_rows, idx_rows, rows, block, N, C, gate="softmax"):
     """Per-row gate terms shared by forward and backward.
 
     For each query t in `rows`: c(t), LSE_s(t) over its history blocks,
-    beta[t,m] = s[t,m] - LSE_s(t) = log g_m  ([Review] "Why the Four Design
-    Choices Matter": log g_m = s_m - LSE(s); gate g = softmax(s) over history
-    blocks: [Blog] 方法核心, [Review] "New Approach", paper Eq. 4), the
-    selection mask, and the additive bias over all N keys:
+    beta[t,m] = log g_m, the selection mask, and the additive bias over all N
+    keys:
         0          own block, key j <= t   (current block gate is 1, log 1 = 0)
         beta[t,m]  key j in a selected history block m
         -inf       any other key (unselected history, the future)
+    The gate activation ([Review] "Why the Four Design Choices Matter", gate
+    activation; [Blog] 方法核心, the ablation table's gate-activation row):
+        softmax  g = softmax(s) over the history, beta = s - LSE_s (the SAS
+                 gate: [Blog] 方法核心, [Review] "New Approach", paper Eq. 4)
+        sigmoid  g = sigmoid(s) per block, beta = log sigmoid(s)
+        raw      the logit injected as it is, beta = s (g = e^s)
+    Only the softmax gate has a normaliser; the others report LSE_s = 0.
     """
+    if gate not in GATES:
+        raise ValueError(f"unknown gate {gate!r}")
     rows = np.asarray(rows)
     c = rows // block
     hist = np.arange(C)[None, :] < c[:, None]  # [R, C]
     s_hist = np.where(hist, _as64(s_rows), NEG_INF)
-    lse_s = _logsumexp(s_hist, axis=-1)  # -inf when c == 0
-    with np.errstate(invalid="ignore"):
-        beta = np.where(hist, s_hist - lse_s[:, None], NEG_INF)
+    if gate == "softmax":
+        lse_s = _logsumexp(s_hist, axis=-1)  # -inf when c == 0
+        with np.errstate(invalid="ignore"):
+            beta = np.where(hist, s_hist - lse_s[:, None], NEG_INF)
+    else:
+        lse_s = np.zeros(len(rows))
+        beta = np.where(hist, _log_sigmoid(s_hist) if gate == "sigmoid" else s_hist, NEG_INF)
     if idx_rows is None:  # full scope: every history block is gated
         sel = hist.copy()
     else:
@@ -269,21 +292,40 @@ def _row_terms(s_rows, idx_rows, rows, block, N, C):
     return c, lse_s, beta, sel, bias
 
 
-def _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows):
+def _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate="softmax"):
     N = k.shape[2]
     C = s.shape[3]
     g = h // G
     idx_rows = None if idx is None else [idx[b, g, t] for t in rows]
-    c, lse_s, beta, sel, bias = _row_terms(s[b, h, rows], idx_rows, rows, block, N, C)
+    c, lse_s, beta, sel, bias = _row_terms(s[b, h, rows], idx_rows, rows, block, N, C, gate)
     z = scale * (_as64(q[b, h, rows]) @ _as64(k[b, g]).T) + bias
     lse = _logsumexp(z, axis=-1)
     p = np.exp(z - lse[:, None])
     return c, lse_s, beta, sel, p, lse
 
 
-def gated_attention_forward(q, k, v, s, idx, block, scale, rows=None):
+def _gate_ds(gate, dbeta, beta, s_rows, c):
+    """ds from dbeta (the dz sum of each selected history block, 0 otherwise)
+    by the chain rule through beta = log g(s), zero outside the history:
+        softmax  ds = dbeta - g * sum_m' dbeta      (log g = s - LSE(s))
+        sigmoid  ds = dbeta * (1 - sigmoid(s))      (d log sigmoid(s) / ds)
+        raw      ds = dbeta                         (beta = s)
+    """
+    C = dbeta.shape[1]
+    hist = np.arange(C)[None, :] < c[:, None]
+    if gate == "softmax":
+        g = np.where(hist, np.exp(np.where(hist, beta, 0.0)), 0.0)
+        return np.where(hist, dbeta - g * dbeta.sum(axis=1, keepdims=True), 0.0)
+    if gate == "sigmoid":
+        one_minus = np.exp(_log_sigmoid(-np.where(hist, _as64(s_rows), 0.0)))
+        return np.where(hist, dbeta * one_minus, 0.0)
+    return np.where(hist, dbeta, 0.0)
+
+
+def gated_attention_forward(q, k, v, s, idx, block, scale, rows=None, gate="softmax"):
     """SAS forward o = softmax(q K_S^T * scale + log g_S) V_S
-    ([Blog] 方法核心 and [Review] "New Approach", paper Eq. 9).
+    ([Blog] 方法核心 and [Review] "New Approach", paper Eq. 9); `gate` picks the
+    gate activation (see `_row_terms`).
 
     q: [B,Hq,N,D]; k, v: [B,Hkv,N,D]; s: [B,Hq,N,C] selector scores;
     idx: None (full scope: all history blocks gated) or int [B,Hkv,N,K]
@@ -302,14 +344,14 @@ def gated_attention_forward(q, k, v, s, idx, block, scale, rows=None):
     lse_s = np.zeros((B, Hq, R))
     for b in range(B):
         for h in range(Hq):
-            _, ls, _, _, p, l = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            _, ls, _, _, p, l = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
             o[b, h] = p @ _as64(v[b, h // G])
             lse[b, h] = l
             lse_s[b, h] = ls
     return o, lse, lse_s
 
 
-def gated_attention_backward(q, k, v, do, s, idx, block, scale):
+def gated_attention_backward(q, k, v, do, s, idx, block, scale, gate="softmax"):
     """Gradients of L = sum(dO * o) for the SAS forward, with s held as an input.
 
     Returns (dq, dk, dv, ds) in float64.  dq, dk, dv are the partial
@@ -321,6 +363,7 @@ def gated_attention_backward(q, k, v, do, s, idx, block, scale):
     zero outside the history.  dbeta is g_m times the inner-gate gradient of
     [Blog] 方法核心 / [Review] "Why the Four Design Choices Matter" (paper
     Eq. 5); the second term is the chain rule through log g = s - LSE(s).
+    The sigmoid and raw gates take their own chain rule (`_gate_ds`).
     The recomputed forward is this oracle's own (exact o and softmax).
     """
     B, Hq, N, D = q.shape
@@ -335,7 +378,7 @@ def gated_attention_backward(q, k, v, do, s, idx, block, scale):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
             qh, kh, vh, doh = _as64(q[b, h]), _as64(k[b, g]), _as64(v[b, g]), _as64(do[b, h])
             o = p @ vh
             delta = np.sum(doh * o, axis=-1)
@@ -349,14 +392,11 @@ def gated_attention_backward(q, k, v, do, s, idx, block, scale):
             for m in range(C):
                 dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
             dbeta = np.where(sel, dbeta, 0.0)
-            hist = np.arange(C)[None, :] < c[:, None]
-            gate = np.where(hist, np.exp(np.where(hist, beta, 0.0)), 0.0)
-            total = dbeta.sum(axis=1, keepdims=True)
-            ds[b, h] = np.where(hist, dbeta - gate * total, 0.0)
+            ds[b, h] = _gate_ds(gate, dbeta, beta, s[b, h], c)
     return dq, dk, dv, ds
 
 
-def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows):
+def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows, gate="softmax"):
     """dq and ds of selected query rows (row-local parts of the backward).
 
     Same definitions as `gated_attention_backward`, evaluated only for the
@@ -367,7 +407,7 @@ def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows):
     C = s.shape[3]
     g = h // G
     rows = np.asarray(rows)
-    c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+    c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
     vh, kh, doh = _as64(v[b, g]), _as64(k[b, g]), _as64(do[b, h, rows])
     o = p @ vh
     delta = np.sum(doh * o, axis=-1)
@@ -377,13 +417,12 @@ def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows):
     for m in range(C):
         dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
     dbeta = np.where(sel, dbeta, 0.0)
-    hist = np.arange(C)[None, :] < c[:, None]
-    gate = np.where(hist, np.exp(np.where(hist, beta, 0.0)), 0.0)
-    ds = np.where(hist, dbeta - gate * dbeta.sum(axis=1, keepdims=True), 0.0)
+    ds = _gate_ds(gate, dbeta, beta, s[b, h, rows], c)
     return dq, ds
 
 
-def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024, rows=None):
+def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024, rows=None,
+                  gate="softmax"):
     """dk and dv of selected keys of KV head g in batch b.
 
     dk[j] = scale * sum_{h in group(g)} sum_t dz[h,t,j] q[h,t];
@@ -403,7 +442,7 @@ def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024,
     for h in range(g * G, (g + 1) * G):
         for r0 in range(0, len(all_rows), row_chunk):
             rows = all_rows[r0:r0 + row_chunk]
-            _, _, _, _, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows)
+            _, _, _, _, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
             vh = _as64(v[b, g])
             doh = _as64(do[b, h, rows])
             o = p @ vh

@@ -588,3 +588,133 @@ def test_selector_subset_helpers_match_full_backward():
             blocks = [0, 2, C - 1]
             assert np.allclose(orc.selector_dkbar_blocks(q, w, block, scale, b, g, 3, blocks),
                                dkbar[b, g, blocks], atol=1e-13, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Gate activations other than the softmax (the pages' ablation: sigmoid gate,
+# raw logit injected into the attention logits)
+# ---------------------------------------------------------------------------
+
+def _gate_value(gate, s):
+    return 1.0 / (1.0 + np.exp(-s)) if gate == "sigmoid" else np.exp(s)
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_gate_variant_forward_as_multiplicative_gate(gate, sparse):
+    """With gate value g_m (sigmoid(s_m), or e^{s_m} for the raw logit) the
+    forward is the gate multiplying exp(z) inside the softmax: o = sum_j g e^z v /
+    sum_j g e^z, own block g = 1 (blog 方法核心 / review "New Approach" with the
+    gate of the ablation), written out key by key."""
+    block, D, N = 4, 5, 28
+    q, k, v, do, s = rand_problem(61, Hq=2, Hkv=1, N=N, D=D, block=block)
+    scale = 0.6
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, 2) if sparse else None
+    o, lse, lse_s = orc.gated_attention_forward(q, k, v, s, idx, block, scale, gate=gate)
+    np.testing.assert_array_equal(lse_s, 0.0)
+    for h in range(2):
+        for t in range(N):
+            c = t // block
+            sel = set(range(c)) if idx is None else {int(m) for m in idx[0, 0, t] if 0 <= m < c}
+            num = np.zeros(D)
+            den = 0.0
+            for j in range(t + 1):
+                m = j // block
+                if m == c:
+                    w = 1.0
+                elif m in sel:
+                    w = _gate_value(gate, s[0, h, t, m])
+                else:
+                    continue
+                e = w * math.exp(scale * float(q[0, h, t] @ k[0, 0, j]))
+                num += e * v[0, 0, j]
+                den += e
+            np.testing.assert_allclose(o[0, h, t], num / den, rtol=1e-12, atol=1e-13)
+            assert abs(lse[0, h, t] - math.log(den)) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_gate_variant_finite_differences(gate, sparse):
+    """Central differences of L = sum(dO * o) in fp64 match dq, dk, dv and ds
+    for the sigmoid and raw-logit gates."""
+    block, D, N, Hq, Hkv = 4, 4, 20, 2, 1
+    q, k, v, do, s = rand_problem(71, Hq=Hq, Hkv=Hkv, N=N, D=D, block=block)
+    scale = 0.7
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, 2) if sparse else None
+    dq, dk, dv, ds = orc.gated_attention_backward(q, k, v, do, s, idx, block, scale, gate=gate)
+    eps = 1e-6
+    r = rng(9)
+
+    def loss():
+        o, _, _ = orc.gated_attention_forward(q, k, v, s, idx, block, scale, gate=gate)
+        return float(np.sum(o * do))
+
+    def fd(arr, pos):
+        a0 = arr[pos]
+        arr[pos] = a0 + eps
+        lp = loss()
+        arr[pos] = a0 - eps
+        lm = loss()
+        arr[pos] = a0
+        return (lp - lm) / (2 * eps)
+
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for _ in range(8):
+            pos = tuple(int(r.integers(0, n)) for n in arr.shape)
+            assert abs(fd(arr, pos) - grad[pos]) < 1e-7 * max(1.0, abs(grad[pos]))
+    for t in (6, 13, 19):
+        for h in range(Hq):
+            for m in range(s.shape[3]):
+                pos = (0, h, t, m)
+                assert abs(fd(s, pos) - ds[pos]) < 1e-7, (gate, pos, fd(s, pos), ds[pos])
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+def test_gate_variant_inner_gradient_closed_form(gate):
+    """ds_m = dg_m^inner * dg/ds with the pages' inner-gate gradient
+    dg_m = sum_{i in B_m} (p_i / g_m) dO.(v_i - o) (review "Why the Four Design
+    Choices Matter", paper Eq. 5) and dg/ds = g (1 - g) for the sigmoid gate,
+    e^s for the raw logit; p from the library softmax."""
+    block, D, N = 8, 8, 40
+    q, k, v, do, s = rand_problem(43, Hq=1, Hkv=1, N=N, D=D, block=block)
+    scale = 0.5
+    _, _, _, ds = orc.gated_attention_backward(q, k, v, do, s, None, block, scale, gate=gate)
+    qt, kt, vt, st = (torch.tensor(x[0]) for x in (q, k, v, s))
+    for t in (17, 30, 39):
+        c = t // block
+        g = torch.sigmoid(st[0, t, :c]) if gate == "sigmoid" else torch.exp(st[0, t, :c])
+        z = torch.full((N,), float("-inf"), dtype=torch.float64)
+        for j in range(t + 1):
+            m = j // block
+            z[j] = scale * qt[0, t] @ kt[0, j] + (torch.log(g[m]) if m < c else 0.0)
+        p = torch.softmax(z, dim=0)
+        o = p @ vt[0]
+        dO = torch.tensor(do[0, 0, t])
+        dg = torch.stack([(p[m * block:(m + 1) * block] / g[m] * ((vt[0, m * block:(m + 1) * block] - o) @ dO)).sum()
+                          for m in range(c)])
+        dgds = g * (1 - g) if gate == "sigmoid" else g
+        np.testing.assert_allclose(ds[0, 0, t, :c], (dg * dgds).numpy(), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(ds[0, 0, t, c:], 0.0)
+
+
+def test_gate_variants_reduce_to_plain_sparse_attention():
+    """Raw logit s = 0 (gate 1) and a saturated sigmoid (s = 40) both give plain
+    causal attention over the own block and the selected blocks: library
+    attention with that mask."""
+    block, D, N = 4, 6, 32
+    q, k, v, do, s = rand_problem(81, Hq=2, Hkv=1, N=N, D=D, block=block)
+    scale = 0.45
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, 3)
+    mask = torch.zeros((N, N), dtype=torch.bool)
+    for t in range(N):
+        c = t // block
+        for j in range(t + 1):
+            m = j // block
+            mask[t, j] = m == c or m in {int(x) for x in idx[0, 0, t] if 0 <= x < c}
+    expect = causal_sdpa(torch.tensor(q[0]), torch.tensor(k[0]), torch.tensor(v[0]), scale,
+                         mask=mask).numpy()
+    o_raw = orc.gated_attention_forward(q, k, v, np.zeros_like(s), idx, block, scale, gate="raw")[0]
+    o_sig = orc.gated_attention_forward(q, k, v, np.full_like(s, 40.0), idx, block, scale, gate="sigmoid")[0]
+    np.testing.assert_allclose(o_raw[0], expect, atol=1e-12)
+    np.testing.assert_allclose(o_sig[0], expect, atol=1e-12)
