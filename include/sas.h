@@ -82,8 +82,20 @@ typedef enum {
   SAS_OP_BWD = 4,
   SAS_OP_DECODE = 5,
   SAS_OP_SELECTOR_BWD = 6,
-  SAS_OP_PAGED_DECODE = 7
+  SAS_OP_PAGED_DECODE = 7,
+  SAS_OP_FWD_GATE = 8,   /* sas_gated_attn_fwd_gate, any gate */
+  SAS_OP_BWD_GATE = 9    /* sas_gated_attn_bwd_gate, any gate */
 } sas_op;
+
+/* Gate activation of the gated attention (blog 方法核心, the ablation table's
+   gate-activation row; review "Why the Four Design Choices Matter", gate
+   activation): the SAS softmax gate and the two non-competitive gates the
+   pages compare it with. */
+typedef enum {
+  SAS_GATE_SOFTMAX = 0,  /* log g = s - LSE_s over the history (SAS) */
+  SAS_GATE_SIGMOID = 1,  /* log g = log sigmoid(s), per block */
+  SAS_GATE_RAW = 2       /* log g = s: the raw logit injected as a bias */
+} sas_gate;
 
 /*
  * sas_score_blocks -- block mean-pooling and selector scores.
@@ -177,6 +189,38 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v,
                        int Hkv, int N, int D, int block, int topk, float scale,
                        int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * sas_gated_attn_fwd_gate / sas_gated_attn_bwd_gate -- the forward and the
+ *   backward above with another gate activation (sas_gate).  Only the gated
+ *   history blocks' bias and ds change; the own block keeps bias 0 and, at
+ *   sparse scope, unselected blocks keep -inf:
+ *     SAS_GATE_SOFTMAX  exactly sas_gated_attn_fwd / _bwd.
+ *     SAS_GATE_SIGMOID  bias log sigmoid(s[t,m]); ds = dbeta (1 - sigmoid(s)).
+ *     SAS_GATE_RAW      bias s[t,m];               ds = dbeta.
+ *   Neither non-softmax gate has a normaliser: the forward writes lse_s = 0
+ *   and the backward ignores lse_s (it may be NULL), and ds of an unselected
+ *   history block is 0.
+ * gate:       a sas_gate value; anything else is SAS_EINVAL.
+ * workspace:  sas_workspace_bytes(SAS_OP_FWD_GATE or SAS_OP_BWD_GATE, ...)
+ *             bytes (the sigmoid gate keeps log sigmoid(s), fp32 [B,Hq,N,C],
+ *             in it); SAS_GATE_SOFTMAX needs only SAS_OP_FWD / SAS_OP_BWD.
+ * Other arguments, layouts, ownership and errors: as for the calls above.
+ */
+int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v,
+                            const float* scores, const int32_t* idx, void* o,
+                            float* lse, float* lse_s, int B, int Hq, int Hkv,
+                            int N, int D, int block, int topk, float scale,
+                            int dtype, int gate, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int sas_gated_attn_bwd_gate(const void* q, const void* k, const void* v,
+                            const void* o, const void* dout,
+                            const float* scores, const int32_t* idx,
+                            const float* lse, const float* lse_s, void* dq,
+                            void* dk, void* dv, float* ds, int B, int Hq,
+                            int Hkv, int N, int D, int block, int topk,
+                            float scale, int dtype, int gate, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * sas_sparse_decode -- one decode step: each sequence's new token attends to

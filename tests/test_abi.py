@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
-                          "sas_gated_attn_bwd", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
+                          "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
+                          "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
                           "sas_paged_decode", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
@@ -185,3 +186,34 @@ def test_paged_decode_host_checks():
     assert L.sas_pool_pages(v, v, v, -1, 2, 128, 64, 1, N) == sas.SAS_EINVAL
     assert L.sas_pool_pages(v, v, N, 3, 2, 128, 64, 1, N) == sas.SAS_EINVAL
     assert L.sas_pool_pages(N, N, N, 0, 2, 128, 64, 1, N) == sas.SAS_OK
+
+
+def test_gate_variant_host_checks():
+    """Gate variants: an unknown gate is rejected before any GPU work, empty
+    calls succeed, the workspace grows by the rewritten scores (fp32
+    [B,Hq,N,C]) and, for the backward, a zero LSE_s per row; the softmax gate
+    needs exactly the plain call's workspace."""
+    p = ctypes.c_void_p(1)
+    args = (p, p, p, p, None, p, p, p, 1, 4, 2, 128, 128, 64, 0, 0.1, 1)
+    assert L.sas_gated_attn_fwd_gate(*args, 7, None, 0, None) == sas.SAS_EINVAL
+    assert "gate" in sas._lib.sas_last_error().decode()
+    assert L.sas_gated_attn_fwd_gate(*args[:8], 0, *args[9:], 1, None, 0, None) == sas.SAS_OK
+    bargs = (p,) * 13 + (1, 4, 2, 128, 128, 64, 0, 0.1, 1)
+    assert L.sas_gated_attn_bwd_gate(*bargs, -1, None, 0, None) == sas.SAS_EINVAL
+    # the backward of a non-softmax gate does not read lse_s: NULL is fine for the host checks
+    nb = list(bargs)
+    nb[8] = None
+    nb[13] = 0  # B = 0: an empty call
+    assert L.sas_gated_attn_bwd_gate(*nb, 2, None, 0, None) == sas.SAS_OK
+    B, Hq, Hkv, N, D, blk = 1, 32, 8, 8192, 128, 64
+    rows, C = B * Hq * N, N // blk
+    f0 = sas.sas_workspace_bytes(sas.SAS_OP_FWD, B, Hq, Hkv, N, D, blk, -1, 1)
+    fg = sas.sas_workspace_bytes(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, blk, -1, 1)
+    assert fg >= f0 + rows * C * 4
+    b0 = sas.sas_workspace_bytes(sas.SAS_OP_BWD, B, Hq, Hkv, N, D, blk, 32, 1)
+    bg = sas.sas_workspace_bytes(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, blk, 32, 1)
+    assert bg >= b0 + rows * C * 4 + rows * 4
+    # a workspace big enough for the softmax gate only is refused on the host
+    small = sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 4, 2, 128, 128, 64, -1, 1)
+    assert small < sas.sas_workspace_bytes(sas.SAS_OP_FWD_GATE, 1, 4, 2, 128, 128, 64, -1, 1)
+    assert L.sas_gated_attn_fwd_gate(*args, 1, p, small, None) == sas.SAS_EWORKSPACE

@@ -393,3 +393,72 @@ def test_paged_decode_parity(case):
     normwise(to64(lse)[active], lse_ref[active], 1e-4, "lse")
     idle = lens.numpy() <= 0
     assert torch.all(o[torch.tensor(idle)] == 0)
+
+
+GATE_CASES = [
+    # name, dtype, B, Hq, Hkv, D, N, block, topk
+    ("f32-full", "f32", 1, 2, 1, 64, 320, 64, None),
+    ("f32-ragged-sparse", "f32", 2, 4, 2, 64, 300, 64, 2),
+    ("bf16-full", "bf16", 1, 8, 2, 128, 384, 64, None),
+    ("bf16-ragged-sparse", "bf16", 1, 8, 2, 128, 450, 64, 3),
+]
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_gate_variant_parity(case, gate):
+    """Sigmoid and raw-logit gates (the pages' gate-activation ablation) through
+    sas_gated_attn_fwd_gate / _bwd_gate against the oracle at the same
+    tolerances as the softmax gate; lse_s is written as 0 and the backward
+    takes no lse_s."""
+    name, dts, B, Hq, Hkv, D, N, block, topk = case
+    dt = _dt(dts)
+    w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=11)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    scale = w.scale
+    G = Hq // Hkv
+    C = N // block
+    tol = tolerances(dt)
+    _, _, s32, idx = _oracle_selector(q, k, block, scale, topk, G)
+    scores = torch.tensor(s32).to(DEV)
+    idx_t = None if idx is None else torch.tensor(idx).to(DEV)
+    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW}[gate]
+    tk = -1 if topk is None else topk
+    sdt = sas.SAS_F32 if dt == torch.float32 else sas.SAS_BF16
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    lse_s = torch.full((B, Hq, N), 7.0, dtype=torch.float32, device=DEV)
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, block, scale, g, wsf)
+    torch.cuda.synchronize()
+    s64 = s32.astype(np.float64)
+    o_ref, lse_ref, _ = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale,
+                                                    gate=gate)
+    if tol["o_abs"] is not None:
+        max_abs(to64(o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(o), o_ref, tol["o_rel"], "o")
+    normwise(to64(lse), lse_ref, tol["lse"], "lse")
+    assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
+
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, None, dq, dk, dv, ds, block, scale, g,
+                                wsb)
+    torch.cuda.synchronize()
+    r_dq, r_dk, r_dv, r_ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx,
+                                                          block, scale, gate=gate)
+    normwise(to64(dq), r_dq, tol["grad"], "dq")
+    normwise(to64(dk), r_dk, tol["grad"], "dk")
+    normwise(to64(dv), r_dv, tol["grad"], "dv")
+    normwise(to64(ds), r_ds, tol["ds"], "ds")
+    if idx is not None:  # no normaliser: unselected history blocks get exactly 0
+        sel = np.zeros((B, Hq, N, C), dtype=bool)
+        for b in range(B):
+            for h in range(Hq):
+                for t in range(N):
+                    for m in idx[b, h // G, t]:
+                        if 0 <= m < t // block:
+                            sel[b, h, t, m] = True
+        assert torch.count_nonzero(ds.cpu()[torch.tensor(~sel)]).item() == 0, "ds outside the selection"

@@ -26,9 +26,11 @@ SAS_OK, SAS_EINVAL, SAS_EUNSUPPORTED, SAS_EHIP, SAS_EWORKSPACE = 0, -1, -2, -3, 
 SAS_F32, SAS_BF16 = 0, 1
 SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTOR_BWD = 1, 2, 3, 4, 5, 6
 SAS_OP_PAGED_DECODE = 7
+SAS_OP_FWD_GATE, SAS_OP_BWD_GATE = 8, 9
+SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW = 0, 1, 2
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-            "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
+            "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
             "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
@@ -37,6 +39,8 @@ _lib.sas_score_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _
 _lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_pool_pages.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
@@ -51,7 +55,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-              "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode"):
+              "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode"):
     getattr(_lib, _name).restype = _i
 
 
@@ -197,6 +201,29 @@ def sas_gated_attn_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds
                                    _p(lse), _p(lse_s), _p(dq), _p(dk), _p(dv), _p(ds), B, Hq, Hkv,
                                    N, D, block, topk, scale, _dt(q), _p(workspace), wsb,
                                    _stream(stream)))
+
+
+def sas_gated_attn_fwd_gate(q, k, v, scores, idx, o, lse, lse_s, block, scale, gate, workspace=None,
+                            stream=None):
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_gated_attn_fwd_gate(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(o), _p(lse),
+                                        _p(lse_s), B, Hq, Hkv, N, D, block, topk, scale, _dt(q), gate,
+                                        _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_bwd_gate(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, block, scale,
+                            gate, workspace=None, stream=None):
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_gated_attn_bwd_gate(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(scores), _idx_ptr(idx),
+                                        _p(lse), _p(lse_s), _p(dq), _p(dk), _p(dv), _p(ds), B, Hq, Hkv,
+                                        N, D, block, topk, scale, _dt(q), gate, _p(workspace), wsb,
+                                        _stream(stream)))
 
 
 def sas_sparse_decode(q, k_cache, v_cache, cache_len, idx, o, lse, block, scale, workspace=None,

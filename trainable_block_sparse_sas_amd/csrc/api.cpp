@@ -99,6 +99,10 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
     case SAS_OP_PAGED_DECODE:
       if (topk < 0) return size_t(-1);
       return paged_ws(B, Hq, Hkv, n, D, block, topk).total;
+    case SAS_OP_FWD_GATE:
+      return sas::fwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID);
+    case SAS_OP_BWD_GATE:
+      return sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID);
     default:
       return size_t(-1);
   }
@@ -177,27 +181,74 @@ static int check_attn(const char* what, int B, int Hq, int Hkv, int N, int D, in
   return SAS_OK;
 }
 
-int sas_gated_attn_fwd(const void* q, const void* k, const void* v, const float* scores,
-                       const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq,
-                       int Hkv, int N, int D, int block, int topk, float scale, int dtype,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_attn("sas_gated_attn_fwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
-  if (!st) st = check_scale(scale, "sas_gated_attn_fwd");
+static int attn_fwd(const char* what, const void* q, const void* k, const void* v, const float* scores,
+                    const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
+                    int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (!st) st = check_scale(scale, what);
   if (st) return st;
+  if (gate != SAS_GATE_SOFTMAX && gate != SAS_GATE_SIGMOID && gate != SAS_GATE_RAW)
+    return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
   if (empty(B, Hq, N)) {
     g_error.clear();
     return SAS_OK;
   }
   if (!q || !k || !v || !scores || !o || !lse || !lse_s)
-    return fail(SAS_EINVAL, "sas_gated_attn_fwd: q, k, v, scores, o, lse, lse_s must be non-NULL");
+    return fail(SAS_EINVAL, "%s: q, k, v, scores, o, lse, lse_s must be non-NULL", what);
   sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
   const bool bf16 = dtype == SAS_BF16;
-  const size_t need = sas::fwd_workspace(d, idx ? topk : -1, bf16);
+  const size_t need = sas::fwd_gate_workspace(d, idx ? topk : -1, bf16, gate);
   if (need && (!workspace || workspace_bytes < need))
-    return fail(SAS_EWORKSPACE, "sas_gated_attn_fwd: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    return fail(SAS_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", what, need, workspace_bytes);
   hipError_t e = sas::launch_fwd(q, k, v, scores, idx, o, lse, lse_s, d, idx ? topk : 0, scale,
-                                 bf16, workspace, static_cast<hipStream_t>(stream));
-  return hip_status(e, "sas_gated_attn_fwd");
+                                 bf16, gate, workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+static int attn_bwd(const char* what, const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* scores, const int32_t* idx, const float* lse,
+                    const float* lse_s, void* dq, void* dk, void* dv, float* ds, int B, int Hq, int Hkv,
+                    int N, int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
+  if (!st) st = check_scale(scale, what);
+  if (st) return st;
+  if (gate != SAS_GATE_SOFTMAX && gate != SAS_GATE_SIGMOID && gate != SAS_GATE_RAW)
+    return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
+  if (empty(B, Hq, N)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k || !v || !o || !dout || !scores || !lse || (!lse_s && gate == SAS_GATE_SOFTMAX) || !dq ||
+      !dk || !dv || !ds)
+    return fail(SAS_EINVAL, "%s: every tensor pointer except idx (and lse_s for a non-softmax gate) must be non-NULL",
+                what);
+  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
+  const bool bf16 = dtype == SAS_BF16;
+  const size_t need = sas::bwd_gate_workspace(d, idx ? topk : -1, bf16, gate);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SAS_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", what, need, workspace_bytes);
+  hipError_t e = sas::launch_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d,
+                                 idx ? topk : 0, scale, bf16, gate, workspace,
+                                 static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+int sas_gated_attn_fwd(const void* q, const void* k, const void* v, const float* scores,
+                       const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq,
+                       int Hkv, int N, int D, int block, int topk, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd("sas_gated_attn_fwd", q, k, v, scores, idx, o, lse, lse_s, B, Hq, Hkv, N, D, block, topk,
+                  scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream);
+}
+
+int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v, const float* scores,
+                            const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq,
+                            int Hkv, int N, int D, int block, int topk, float scale, int dtype, int gate,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd("sas_gated_attn_fwd_gate", q, k, v, scores, idx, o, lse, lse_s, B, Hq, Hkv, N, D, block,
+                  topk, scale, dtype, gate, workspace, workspace_bytes, stream);
 }
 
 int sas_gated_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -206,24 +257,18 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        float* ds, int B, int Hq, int Hkv, int N, int D, int block, int topk,
                        float scale, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  int st = check_attn("sas_gated_attn_bwd", B, Hq, Hkv, N, D, block, idx, topk, dtype);
-  if (!st) st = check_scale(scale, "sas_gated_attn_bwd");
-  if (st) return st;
-  if (empty(B, Hq, N)) {
-    g_error.clear();
-    return SAS_OK;
-  }
-  if (!q || !k || !v || !o || !dout || !scores || !lse || !lse_s || !dq || !dk || !dv || !ds)
-    return fail(SAS_EINVAL, "sas_gated_attn_bwd: every tensor pointer except idx must be non-NULL");
-  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
-  const bool bf16 = dtype == SAS_BF16;
-  const size_t need = sas::bwd_workspace(d, idx ? topk : -1, bf16);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(SAS_EWORKSPACE, "sas_gated_attn_bwd: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
-  hipError_t e = sas::launch_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d,
-                                 idx ? topk : 0, scale, bf16, workspace,
-                                 static_cast<hipStream_t>(stream));
-  return hip_status(e, "sas_gated_attn_bwd");
+  return attn_bwd("sas_gated_attn_bwd", q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, B, Hq,
+                  Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream);
+}
+
+int sas_gated_attn_bwd_gate(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* scores, const int32_t* idx,
+                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
+                            float* ds, int B, int Hq, int Hkv, int N, int D, int block, int topk,
+                            float scale, int dtype, int gate, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return attn_bwd("sas_gated_attn_bwd_gate", q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, B,
+                  Hq, Hkv, N, D, block, topk, scale, dtype, gate, workspace, workspace_bytes, stream);
 }
 
 int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,

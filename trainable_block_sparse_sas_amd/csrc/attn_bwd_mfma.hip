@@ -66,6 +66,7 @@ struct BwdArgs {
   float* dummy;          // workspace line that absorbs masked stores
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
+  int gate;          // gate activation (kGateSoftmax, kGateSigmoid, kGateRaw)
 };
 
 // ---------------------------------------------------------------- prep ------
@@ -616,9 +617,11 @@ __global__ __launch_bounds__(1024) void bwd_dq_ds_kernel(BwdArgs a, SelLists L) 
 //   ds[m] = (m selected ? dbeta[slot(m)] : 0) - g[m] * sum(dbeta) for the
 //        history blocks m < c, g = exp(s - LSE_s); 0 from the own block on
 //        (slot(m) = rank of m among the row's selected blocks; its dbeta is
-//        the record of the row's entry in m's list, pos[token][slot]).
+//        the record of the row's entry in m's list, pos[token][slot]);
+//        GATE: the gate activation, whose chain rule gate_ds applies (the
+//        softmax gate's is the formula above).
 // Each lane takes 2 dq columns and 8 consecutive blocks per pass.
-template <int D>
+template <int D, int GATE>
 __global__ __launch_bounds__(256) void rows_sparse_kernel(
     const bf16_t* __restrict__ dqp, const float* __restrict__ dbl, const uint32_t* __restrict__ pos,
     size_t ents_per_pair, const float* __restrict__ scores,
@@ -703,9 +706,8 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bool sel = (b8 >> i) & 1u;
-        const float gate = exp2_hw((sv[i] - ls) * kLog2e);
         const float dbv = sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f;
-        out[i] = col0 + i < c ? dbv - gate * tot : 0.f;
+        out[i] = col0 + i < c ? gate_ds(GATE, dbv, sv[i] - ls, tot) : 0.f;
       }
     } else {
 #pragma unroll
@@ -714,8 +716,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
         float v = 0.f;
         if (m2 < c) {
           const bool sel = (b8 >> i) & 1u;
-          const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-          v = (sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f) - gate * tot;
+          v = gate_ds(GATE, sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f, srow[m2] - ls, tot);
         }
         out[i] = v;
       }
@@ -1068,13 +1069,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     const float ls = a.lse_s[gr];
     const float* srow = a.scores + gr * C;
     float* drow = a.ds + gr * C;
-    for (int m2 = lane; m2 < C; m2 += 64) {
-      float out = 0.f;
-      if (m2 < c) {
-        const float gate = exp2_hw((srow[m2] - ls) * kLog2e);
-        out = drow[m2] - gate * tot;
+    if (a.gate == kGateSoftmax) {
+      for (int m2 = lane; m2 < C; m2 += 64) {
+        float out = 0.f;
+        if (m2 < c) out = gate_ds(kGateSoftmax, drow[m2], srow[m2] - ls, tot);
+        drow[m2] = out;
       }
-      drow[m2] = out;
+    } else {
+      for (int m2 = lane; m2 < C; m2 += 64) {
+        float out = 0.f;
+        if (m2 < c) out = gate_ds(a.gate, drow[m2], srow[m2] - ls, tot);
+        drow[m2] = out;
+      }
     }
   }
 }
@@ -1135,9 +1141,14 @@ static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStrea
   // persistent: one workgroup per compute unit (the LDS stages fill it)
   const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
   SAS_LAUNCH("bwd_dq_ds", (bwd_dq_ds_kernel<D, G>), dim3(grid), dim3(1024), 0, s, a, L);
-  SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbl,
-             L.pos, L.ents_per_pair, a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C, a.MWB, a.topk, a.scale,
-             rows);
+#define SAS_ROWS_SPARSE(GT)                                                                                 \
+  SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D, GT>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbl, \
+             L.pos, L.ents_per_pair, a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C,   \
+             a.MWB, a.topk, a.scale, rows)
+  if (a.gate == kGateSigmoid) SAS_ROWS_SPARSE(kGateSigmoid);
+  else if (a.gate == kGateRaw) SAS_ROWS_SPARSE(kGateRaw);
+  else SAS_ROWS_SPARSE(kGateSoftmax);
+#undef SAS_ROWS_SPARSE
 }
 
 template <int D, int G>
@@ -1171,7 +1182,7 @@ static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s)
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
-                           float* ds, const Dims& d, int topk, float scale, void* ws,
+                           float* ds, const Dims& d, int topk, float scale, int gate, void* ws,
                            hipStream_t s) {
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
@@ -1210,6 +1221,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   a.MWB = sp ? L.MWB : 1;
   a.NB = (d.N + KT - 1) / KT;
   a.scale = scale;
+  a.gate = gate;
   const int G = d.G();
 #define SAS_BWD_CASE(DD, GG)                                                                        \
   if (d.D == DD && G == GG)                                                                         \

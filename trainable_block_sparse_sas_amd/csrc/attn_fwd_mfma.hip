@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
 }
 
 template <int D, int G>
-hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
+hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, hipStream_t stream) {
   constexpr int NSUB = 2;
   constexpr int WAVES = 8;
   constexpr int NST = 2;
@@ -460,8 +460,9 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, hipStream_t stream) {
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
   const size_t rows = size_t(B) * a.Hq * a.N;
-  SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
-                     a.lse_s, a.N, a.C, KT, rows);
+  if (norm)
+    SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
+               a.lse_s, a.N, a.C, KT, rows);
   SAS_LAUNCH("vt", (vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
                      const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
   SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST>),
@@ -492,19 +493,21 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, void* ws, hipStream_t s) {
+                           int topk, float scale, bool norm, void* ws, hipStream_t s) {
   FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
             (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale};
   const int G = d.G();
   if (idx != nullptr) {
-    // sparse scope: the gate normaliser, then the key-major forward
+    // sparse scope: the gate normaliser (norm: the softmax gate; otherwise
+    // lse_s already holds 0), then the key-major forward
     const size_t rows = size_t(d.B) * d.Hq * d.N;
-    SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
-               d.N, d.C, KT, rows);
+    if (norm)
+      SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
+                 d.N, d.C, KT, rows);
     return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, ws, s);
   }
 #define SAS_FWD_CASE(DD, GG) \
-  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, s);
+  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, norm, s);
   SAS_FWD_CASE(128, 4)
   SAS_FWD_CASE(128, 1)
   SAS_FWD_CASE(128, 2)

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ scores, const int32_t* __restrict__ idx, T* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ lse_s, int Hq, int Hkv, int N, int C, int block,
-    int topk, float scale) {
+    int topk, float scale, int norm) {
   constexpr int DS = D / 4;
   extern __shared__ uint32_t dyn_mask[];
   __shared__ float ks[KT][D + 1];
@@ -85,9 +85,10 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
   const float* srow = scores + row * C;
   const bool full = (idx == nullptr);
 
-  // LSE of the row's history scores (the gate normaliser).
+  // LSE of the row's history scores (the softmax gate's normaliser; the other
+  // gates have none: 0, already in lse_s).
   float mx = kNegInf, sm = 0.f;
-  for (int m = p; m < c; m += 4) {
+  for (int m = p; norm && m < c; m += 4) {
     const float x = srow[m];
     const float nm = fmaxf(mx, x);
     sm = sm * exp_hw(mx - nm) + exp_hw(x - nm);
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
       mx = nm;
     }
   }
-  const float lses = c > 0 ? mx + log_hw(sm) : kNegInf;
-  if (rv && p == 0) lse_s[row] = lses;
+  const float lses = !norm ? 0.f : c > 0 ? mx + log_hw(sm) : kNegInf;
+  if (norm && rv && p == 0) lse_s[row] = lses;
 
   const int MW = (C + 31) / 32;
   uint32_t* mask = dyn_mask + r * MW;
@@ -175,14 +176,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
 
 // dq and ds, query-major.  dbeta of a gated history block is the sum of dz over
 // its keys (inner-gate gradient of blog 方法核心 / review paper Eq. 5, times g);
-// ds = dbeta - g * sum(dbeta) is the chain rule through log g = s - LSE(s).
+// ds = dbeta - g * sum(dbeta) is the chain rule through log g = s - LSE(s)
+// (gate_ds: the other gate activations' rules).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ scores, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, const float* __restrict__ lse_s,
     const float* __restrict__ delta, T* __restrict__ dq, float* __restrict__ ds, int Hq, int Hkv,
-    int N, int C, int block, int topk, float scale) {
+    int N, int C, int block, int topk, float scale, int gate) {
   constexpr int DS = D / 4;
   extern __shared__ uint32_t dyn_mask[];
   __shared__ float ks[KT][D + 1];
@@ -264,9 +266,8 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(
     for (int m = p; m < C; m += 4) {
       float out = 0.f;
       if (m < c) {
-        const float gate = exp_hw(srow[m] - lses);
         const float db = (full || mask_bit(mask, m)) ? dsrow[m] : 0.f;
-        out = db - gate * db_total;
+        out = gate_ds(gate, db, srow[m] - lses, db_total);
       }
       dsrow[m] = out;
     }
@@ -376,12 +377,12 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
 template <typename T, int D>
 hipError_t fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                     const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d, int topk,
-                    float scale, hipStream_t s) {
+                    float scale, bool norm, hipStream_t s) {
   const size_t mask_bytes = idx ? size_t(64) * ((d.C + 31) / 32) * 4 : 0;
   dim3 grid((d.N + 63) / 64, d.Hq, d.B);
   SAS_LAUNCH("fwd_simt", (fwd_simt_kernel<T, D>), grid, dim3(256), mask_bytes, s, (const T*)q,
                      (const T*)k, (const T*)v, scores, idx, (T*)o, lse, lse_s, d.Hq, d.Hkv, d.N,
-                     d.C, d.block, topk, scale);
+                     d.C, d.block, topk, scale, int(norm));
   return hipGetLastError();
 }
 
@@ -389,7 +390,7 @@ template <typename T, int D>
 hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* scores, const int32_t* idx, const float* lse, const float* lse_s,
                     void* dq, void* dk, void* dv, float* ds, const Dims& d, int topk, float scale,
-                    float* delta, hipStream_t s) {
+                    int gate, float* delta, hipStream_t s) {
   const size_t rows = size_t(d.B) * d.Hq * d.N;
   SAS_LAUNCH("bwd_delta", (bwd_delta_kernel<T, D>), dim3((rows + 63) / 64), dim3(256), 0, s,
                      (const T*)o, (const T*)dout, delta, rows);
@@ -397,7 +398,7 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
   SAS_LAUNCH("bwd_dq_simt", (bwd_dq_simt_kernel<T, D>), dim3((d.N + 63) / 64, d.Hq, d.B), dim3(256),
                      mask_bytes, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, scores,
                      idx, lse, lse_s, delta, (T*)dq, ds, d.Hq, d.Hkv, d.N, d.C, d.block, topk,
-                     scale);
+                     scale, gate);
   SAS_LAUNCH("bwd_dkdv_simt", (bwd_dkdv_simt_kernel<T, D>), dim3((d.N + KT - 1) / KT, d.Hkv, d.B),
                      dim3(128), 0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout,
                      scores, idx, lse, lse_s, delta, (T*)dk, (T*)dv, d.Hq, d.Hkv, d.N, d.C,
@@ -409,28 +410,28 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
 
 hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool bf16, hipStream_t s) {
+                           int topk, float scale, bool bf16, bool norm, hipStream_t s) {
   if (bf16) {
-    if (d.D == 64) return fwd_simt<bf16_t, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, s);
-    return fwd_simt<bf16_t, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, s);
+    if (d.D == 64) return fwd_simt<bf16_t, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
+    return fwd_simt<bf16_t, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
   }
-  if (d.D == 64) return fwd_simt<float, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, s);
-  return fwd_simt<float, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, s);
+  if (d.D == 64) return fwd_simt<float, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
+  return fwd_simt<float, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
 }
 
 hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
-                           float* ds, const Dims& d, int topk, float scale, bool bf16,
+                           float* ds, const Dims& d, int topk, float scale, bool bf16, int gate,
                            float* delta, hipStream_t s) {
   if (bf16) {
     if (d.D == 64)
-      return bwd_simt<bf16_t, 64>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, delta, s);
-    return bwd_simt<bf16_t, 128>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, delta, s);
+      return bwd_simt<bf16_t, 64>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, gate, delta, s);
+    return bwd_simt<bf16_t, 128>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, gate, delta, s);
   }
   if (d.D == 64)
-    return bwd_simt<float, 64>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, delta, s);
-  return bwd_simt<float, 128>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, delta, s);
+    return bwd_simt<float, 64>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, gate, delta, s);
+  return bwd_simt<float, 128>(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale, gate, delta, s);
 }
 
 }  // namespace sas

@@ -36,6 +36,22 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
+// Gate activations (the values of sas_gate).
+constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2;
+
+// ds of a history block from db (its dz sum when gated, else 0), x = s - LSE_s
+// (for the sigmoid gate s is the rewritten score log sigmoid(s) and LSE_s = 0,
+// so e^x = sigmoid(s)) and the row's dbeta total: the chain rule through log g
+// of each gate activation.
+//   softmax  db - e^x total   (log g = s - LSE(s))
+//   sigmoid  db (1 - e^x)     (d log sigmoid(s) / ds = 1 - sigmoid(s))
+//   raw      db               (log g = s)
+__device__ __forceinline__ float gate_ds(int gate, float db, float x, float tot) {
+  if (gate == kGateSigmoid) return -db * expm1f(x);
+  if (gate == kGateRaw) return db;
+  return db - exp_hw(x) * tot;
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask, 64); }
 

@@ -92,13 +92,15 @@ hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const flo
                           int topk, float scale, void* ws, hipStream_t s);
 size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);
+size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
+size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                      int topk, float scale, bool bf16, void* ws, hipStream_t s);
+                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* scores, const int32_t* idx,
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
-                      float* ds, const Dims& d, int topk, float scale, bool bf16, void* ws,
+                      float* ds, const Dims& d, int topk, float scale, bool bf16, int gate, void* ws,
                       hipStream_t s);
 
 // ---- decode --------------------------------------------------------------------
