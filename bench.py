@@ -338,6 +338,48 @@ def bench_selector_bwd(torch, w, steps):
             "note": "NEXT-row kernel, timed on its own; not part of the step above"}
 
 
+def bench_gate_variants(torch, w, steps):
+    """The pages' gate-activation ablation (sigmoid gate, raw logit) through
+    sas_gated_attn_fwd_gate / _bwd_gate on one step's scores and selection,
+    timed on their own: forward + backward per gate (the rewrite of the scores
+    included), priced with the step's algorithmic work, 14 D flops per
+    attended pair."""
+    from trainable_block_sparse_sas_amd.inputs import training_inputs
+    from trainable_block_sparse_sas_amd.pipeline import TrainStep
+    from trainable_block_sparse_sas_amd import binding as sas
+
+    q, k, v, do = training_inputs(w, device="cuda")
+    step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, w.torch_dtype)
+    step.run(q, k, v, do)
+    sdt = sas.SAS_BF16 if w.torch_dtype == torch.bfloat16 else sas.SAS_F32
+    tk = -1 if w.topk is None else w.topk
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, tk, sdt)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, tk, sdt)
+    flops = 14 * w.D * attended_pairs(w.N, w.block, w.topk, w.Hq, w.B)
+    out = {}
+    for name, g in (("sigmoid", sas.SAS_GATE_SIGMOID), ("raw", sas.SAS_GATE_RAW)):
+        def one():
+            sas.sas_gated_attn_fwd_gate(q, k, v, step.scores, step.idx, step.o, step.lse, step.lse_s, w.block,
+                                        w.scale, g, wsf)
+            sas.sas_gated_attn_bwd_gate(q, k, v, step.o, do, step.scores, step.idx, step.lse, None, step.dq,
+                                        step.dk, step.dv, step.ds, w.block, w.scale, g, wsb)
+
+        one()
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            one()
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / steps
+        out[name] = {"ms_fwd_bwd": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    del wsf, wsb
+    out["note"] = "NEXT-row entry points, timed on their own; not part of the step above"
+    return out
+
+
 def copy_probe(torch):
     """One plain streaming kernel over 1 GiB (bitwise not of 2^28 int32: 1 GiB
     read, 1 GiB written); its counter readings calibrate FETCH_SIZE and
@@ -459,6 +501,7 @@ def main():
             "bwd_tflops": round(full["flops_bwd"] / (full["ms_bwd"] * 1e-3) / 1e12, 3)}
         out["decode"] = bench_decodes(torch, wmap)
         out["selector_bwd"] = bench_selector_bwd(torch, w, 5)
+        out["gate_variants"] = bench_gate_variants(torch, w, 3)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
