@@ -110,6 +110,63 @@ def test_training_fullsize(wi):
     normwise(to64(step.dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
 
 
+@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+def test_gate_variant_fullsize(gate):
+    """The sigmoid and raw-logit gates at the 32K sparse training shape, through
+    sas_gated_attn_fwd_gate / _bwd_gate on the oracle's scores and selection:
+    sampled rows of o, lse, dq and ds, and sampled keys of dk and dv."""
+    w = WORKLOADS[2]
+    dt = w.torch_dtype
+    q, k, v, do = training_inputs(w, device=DEV)
+    q64, k64, v64, do64 = to64(q), to64(k), to64(v), to64(do)
+    G = w.Hq // w.Hkv
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(k64, w.block)).to(dt))
+    s32 = _oracle_scores_f32(q64, kbar_r, w.block, w.scale)
+    pos = np.arange(w.N)[None, :] // w.block
+    rows = _sample_rows(w.N, w.block, seed=3)
+    scores = torch.tensor(s32).to(DEV)
+    # the selection: the GPU Top-K on the oracle's scores, bit-exact on the sampled rows
+    idx_t = torch.empty((w.B, w.Hkv, w.N, w.topk), dtype=torch.int32, device=DEV)
+    sas.sas_topk_select(scores, idx_t, None, G, w.block)
+    torch.cuda.synchronize()
+    idx = idx_t.cpu().numpy()
+    assert np.array_equal(idx[:, :, rows], orc.topk_select(s32[:, :, rows], G, pos[:, rows], w.topk)), "topk"
+    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW}[gate]
+    B, Hq, Hkv, N, D, C = w.B, w.Hq, w.Hkv, w.N, w.D, w.C
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    lse_s = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, w.block, w.topk, sas.SAS_BF16, DEV)
+    sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, w.block, w.scale, g, wsf)
+    torch.cuda.synchronize()
+    del wsf
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, w.block, w.topk, sas.SAS_BF16, DEV)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, None, dq, dk, dv, ds, w.block, w.scale, g,
+                                wsb)
+    torch.cuda.synchronize()
+    del wsb
+    s64 = s32.astype(np.float64)
+    o_ref, lse_ref, _ = orc.gated_attention_forward(q64, k64, v64, s64, idx, w.block, w.scale, rows=rows,
+                                                    gate=gate)
+    max_abs(to64(o[:, :, rows]), o_ref, 2e-2, "o")
+    normwise(to64(lse[:, :, rows]), lse_ref, 1e-4, "lse")
+    assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
+    for h in (1, Hq - 2):
+        dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, h, rows, gate=gate)
+        normwise(to64(dq[0, h, rows]), dq_r, 2e-2, f"dq h{h}")
+        normwise(to64(ds[0, h, rows]), ds_r, 2e-2, f"ds h{h}")
+    g_chk = 1
+    keys = np.array([(C - 60) * w.block + 5, (C - 3) * w.block + 40, N - 1])
+    kb = np.unique(keys // w.block)
+    attend = np.nonzero(np.any(np.isin(idx[0, g_chk], kb), axis=-1) | np.isin(np.arange(N) // w.block, kb))[0]
+    dk_r, dv_r = orc.key_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, g_chk, keys, rows=attend,
+                                   gate=gate)
+    normwise(to64(dk[0, g_chk, keys]), dk_r, 2e-2, "dk")
+    normwise(to64(dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
+
+
 def test_selector_bwd_fullsize():
     """The selector backward at the 32K training shape, on a seeded ds of the
     same shape as the attention backward's output."""
