@@ -37,7 +37,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * gate activations other than the softmax (sigmoid, raw logit: the pages'
     ablation of the gate activation) keep everything else as it is: the own
     block's gate is 1, unselected history blocks get -inf, and with no
-    normaliser an unselected block's ds is 0 and LSE_s is reported as 0.
+    normaliser an unselected block's ds is 0 and LSE_s is reported as 0;
+  * the outer gate (the pages' gate-placement ablation) is g = softmax(s)
+    multiplying each attended key's value contribution after a softmax of
+    the ungated logits; `lse` is then the log-sum-exp of those logits.
 
 Parity status: every function below is pinned by tests that do not re-type
 its formula (library attention routines, autograd, finite differences,
@@ -239,7 +242,7 @@ def _selection_mask(idx_row_sets, c, C):
     return sel
 
 
-GATES = ("softmax", "sigmoid", "raw")
+GATES = ("softmax", "sigmoid", "raw", "outer")
 
 
 def _log_sigmoid(x):
@@ -262,7 +265,15 @@ def _row_terms(s_rows, idx_rows, rows, block, N, C, gate="softmax"):
                  gate: [Blog] 方法核心, [Review] "New Approach", paper Eq. 4)
         sigmoid  g = sigmoid(s) per block, beta = log sigmoid(s)
         raw      the logit injected as it is, beta = s (g = e^s)
-    Only the softmax gate has a normaliser; the others report LSE_s = 0.
+        outer    g = softmax(s) as for the SAS gate, placed outside the
+                 softmax ([Review] "Why the Four Design Choices Matter", gate
+                 placement): the logits take no bias (0 on the own block and
+                 the gated history, -inf elsewhere) and the gate scales each
+                 key's value contribution instead (gk below).
+    Only the softmax-normalised gates (softmax, outer) have LSE_s; the others
+    report LSE_s = 0.  gk[t,j] is the factor on key j's value contribution:
+    the outer gate's g of the key's block (1 on the own block, 0 on keys the
+    row does not attend); 1 for the gates inside the softmax.
     """
     if gate not in GATES:
         raise ValueError(f"unknown gate {gate!r}")
@@ -270,7 +281,7 @@ def _row_terms(s_rows, idx_rows, rows, block, N, C, gate="softmax"):
     c = rows // block
     hist = np.arange(C)[None, :] < c[:, None]  # [R, C]
     s_hist = np.where(hist, _as64(s_rows), NEG_INF)
-    if gate == "softmax":
+    if gate in ("softmax", "outer"):
         lse_s = _logsumexp(s_hist, axis=-1)  # -inf when c == 0
         with np.errstate(invalid="ignore"):
             beta = np.where(hist, s_hist - lse_s[:, None], NEG_INF)
@@ -288,8 +299,13 @@ def _row_terms(s_rows, idx_rows, rows, block, N, C, gate="softmax"):
     hist_key = (key_block[None, :] < c[:, None]) & np.take_along_axis(
         sel, np.broadcast_to(kb, (len(rows), N)), axis=1)
     beta_key = np.take_along_axis(beta, np.broadcast_to(kb, (len(rows), N)), axis=1)
-    bias = np.where(own, 0.0, np.where(hist_key, beta_key, NEG_INF))
-    return c, lse_s, beta, sel, bias
+    if gate == "outer":
+        bias = np.where(own | hist_key, 0.0, NEG_INF)
+        gk = np.where(own, 1.0, np.where(hist_key, np.exp(np.where(hist_key, beta_key, 0.0)), 0.0))
+    else:
+        bias = np.where(own, 0.0, np.where(hist_key, beta_key, NEG_INF))
+        gk = np.ones((len(rows), N))
+    return c, lse_s, beta, sel, bias, gk
 
 
 def _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate="softmax"):
@@ -297,11 +313,39 @@ def _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate="softmax"):
     C = s.shape[3]
     g = h // G
     idx_rows = None if idx is None else [idx[b, g, t] for t in rows]
-    c, lse_s, beta, sel, bias = _row_terms(s[b, h, rows], idx_rows, rows, block, N, C, gate)
+    c, lse_s, beta, sel, bias, gk = _row_terms(s[b, h, rows], idx_rows, rows, block, N, C, gate)
     z = scale * (_as64(q[b, h, rows]) @ _as64(k[b, g]).T) + bias
     lse = _logsumexp(z, axis=-1)
     p = np.exp(z - lse[:, None])
-    return c, lse_s, beta, sel, p, lse
+    return c, lse_s, beta, sel, p, lse, gk
+
+
+def _block_sums(x, block, C):
+    """[R, N] -> [R, C]: sums over the keys of each block."""
+    out = np.zeros((x.shape[0], C))
+    for m in range(C):
+        out[:, m] = x[:, m * block:(m + 1) * block].sum(axis=1)
+    return out
+
+
+def _row_backward(p, gk, doh, vh, sel, beta, s_rows, c, block, gate):
+    """dz [R,N] and ds [R,C] of a head's rows: with w = gk p the weights on v,
+    o = w v, dP = dO v^T, Delta = dO . o and dz = p (gk dP - Delta).  Gates
+    inside the softmax: dbeta = the dz sum of each selected block, ds by
+    `_gate_ds`.  The outer gate: dg_m = sum_{i in B_m} p_i dP_i (the pages'
+    outer-gate gradient, [Review] "Why the Four Design Choices Matter", paper
+    Eq. 5), ds = g (dg - sum_m' g dg), i.e. the softmax gate's rule applied to
+    g dg."""
+    C = sel.shape[1]
+    o = (gk * p) @ vh
+    delta = np.sum(doh * o, axis=-1)
+    dp = doh @ vh.T
+    dz = p * (gk * dp - delta[:, None])
+    if gate == "outer":
+        dbeta = np.where(sel, _block_sums(gk * p * dp, block, C), 0.0)
+        return dz, _gate_ds("softmax", dbeta, beta, s_rows, c)
+    dbeta = np.where(sel, _block_sums(dz, block, C), 0.0)
+    return dz, _gate_ds(gate, dbeta, beta, s_rows, c)
 
 
 def _gate_ds(gate, dbeta, beta, s_rows, c):
@@ -344,8 +388,8 @@ def gated_attention_forward(q, k, v, s, idx, block, scale, rows=None, gate="soft
     lse_s = np.zeros((B, Hq, R))
     for b in range(B):
         for h in range(Hq):
-            _, ls, _, _, p, l = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
-            o[b, h] = p @ _as64(v[b, h // G])
+            _, ls, _, _, p, l, gk = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
+            o[b, h] = (gk * p) @ _as64(v[b, h // G])
             lse[b, h] = l
             lse_s[b, h] = ls
     return o, lse, lse_s
@@ -378,21 +422,12 @@ def gated_attention_backward(q, k, v, do, s, idx, block, scale, gate="softmax"):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
+            c, _, beta, sel, p, _, gk = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
             qh, kh, vh, doh = _as64(q[b, h]), _as64(k[b, g]), _as64(v[b, g]), _as64(do[b, h])
-            o = p @ vh
-            delta = np.sum(doh * o, axis=-1)
-            dp = doh @ vh.T
-            dz = p * (dp - delta[:, None])
+            dz, ds[b, h] = _row_backward(p, gk, doh, vh, sel, beta, s[b, h], c, block, gate)
             dq[b, h] = scale * (dz @ kh)
             dk[b, g] += scale * (dz.T @ qh)
-            dv[b, g] += p.T @ doh
-            # dbeta: sum of dz over the keys of each selected history block.
-            dbeta = np.zeros((N, C))
-            for m in range(C):
-                dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
-            dbeta = np.where(sel, dbeta, 0.0)
-            ds[b, h] = _gate_ds(gate, dbeta, beta, s[b, h], c)
+            dv[b, g] += (gk * p).T @ doh
     return dq, dk, dv, ds
 
 
@@ -407,17 +442,10 @@ def row_gradients(q, k, v, do, s, idx, block, scale, b, h, rows, gate="softmax")
     C = s.shape[3]
     g = h // G
     rows = np.asarray(rows)
-    c, _, beta, sel, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
+    c, _, beta, sel, p, _, gk = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
     vh, kh, doh = _as64(v[b, g]), _as64(k[b, g]), _as64(do[b, h, rows])
-    o = p @ vh
-    delta = np.sum(doh * o, axis=-1)
-    dz = p * (doh @ vh.T - delta[:, None])
+    dz, ds = _row_backward(p, gk, doh, vh, sel, beta, s[b, h, rows], c, block, gate)
     dq = scale * (dz @ kh)
-    dbeta = np.zeros((len(rows), C))
-    for m in range(C):
-        dbeta[:, m] = dz[:, m * block:(m + 1) * block].sum(axis=1)
-    dbeta = np.where(sel, dbeta, 0.0)
-    ds = _gate_ds(gate, dbeta, beta, s[b, h, rows], c)
     return dq, ds
 
 
@@ -426,7 +454,7 @@ def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024,
     """dk and dv of selected keys of KV head g in batch b.
 
     dk[j] = scale * sum_{h in group(g)} sum_t dz[h,t,j] q[h,t];
-    dv[j] = sum_{h in group(g)} sum_t p[h,t,j] dO[h,t]; the sums run over every
+    dv[j] = sum_{h in group(g)} sum_t gk p[h,t,j] dO[h,t]; the sums run over every
     query row (rows that do not attend key j contribute p = dz = 0), or over
     `rows` when given, which must then hold every row that attends the keys.
     Rows are visited in chunks only to bound memory; each row is computed
@@ -442,15 +470,15 @@ def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024,
     for h in range(g * G, (g + 1) * G):
         for r0 in range(0, len(all_rows), row_chunk):
             rows = all_rows[r0:r0 + row_chunk]
-            _, _, _, _, p, _ = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
+            _, _, _, _, p, _, gk = _head_rows(q, k, v, s, idx, b, h, G, block, scale, rows, gate)
             vh = _as64(v[b, g])
             doh = _as64(do[b, h, rows])
-            o = p @ vh
+            o = (gk * p) @ vh
             delta = np.sum(doh * o, axis=-1)
-            pk = p[:, keys]
-            dz = pk * (doh @ vh[keys].T - delta[:, None])
+            pk, gkk = p[:, keys], gk[:, keys]
+            dz = pk * (gkk * (doh @ vh[keys].T) - delta[:, None])
             dk += scale * (dz.T @ _as64(q[b, h, rows]))
-            dv += pk.T @ doh
+            dv += (gkk * pk).T @ doh
     return dk, dv
 
 

@@ -718,3 +718,104 @@ def test_gate_variants_reduce_to_plain_sparse_attention():
     o_sig = orc.gated_attention_forward(q, k, v, np.full_like(s, 40.0), idx, block, scale, gate="sigmoid")[0]
     np.testing.assert_allclose(o_raw[0], expect, atol=1e-12)
     np.testing.assert_allclose(o_sig[0], expect, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The outer gate (the pages' gate-placement ablation): g = softmax(s) scales
+# each block's value contribution after an ungated softmax
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_outer_gate_forward_written_out(sparse):
+    """o_t = sum_j g_{m(j)} e^{z_j} v_j / sum_j e^{z_j} over the attended keys, z
+    with no bias, g = softmax of the row's history scores, own block g = 1."""
+    block, D, N = 4, 5, 28
+    q, k, v, do, s = rand_problem(91, Hq=2, Hkv=1, N=N, D=D, block=block)
+    scale = 0.6
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, 2) if sparse else None
+    o, lse, lse_s = orc.gated_attention_forward(q, k, v, s, idx, block, scale, gate="outer")
+    for h in range(2):
+        for t in range(N):
+            c = t // block
+            sel = set(range(c)) if idx is None else {int(m) for m in idx[0, 0, t] if 0 <= m < c}
+            gate = np.exp(s[0, h, t, :c] - np.log(np.sum(np.exp(s[0, h, t, :c])))) if c else np.zeros(0)
+            num = np.zeros(D)
+            den = 0.0
+            for j in range(t + 1):
+                m = j // block
+                if m != c and m not in sel:
+                    continue
+                e = math.exp(scale * float(q[0, h, t] @ k[0, 0, j]))
+                num += (1.0 if m == c else gate[m]) * e * v[0, 0, j]
+                den += e
+            np.testing.assert_allclose(o[0, h, t], num / den, rtol=1e-12, atol=1e-13)
+            assert abs(lse[0, h, t] - math.log(den)) < 1e-12
+            if c:
+                assert abs(lse_s[0, h, t] - math.log(np.sum(np.exp(s[0, h, t, :c])))) < 1e-12
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_outer_gate_finite_differences(sparse):
+    block, D, N, Hq, Hkv = 4, 4, 20, 2, 1
+    q, k, v, do, s = rand_problem(73, Hq=Hq, Hkv=Hkv, N=N, D=D, block=block)
+    scale = 0.7
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, 2) if sparse else None
+    dq, dk, dv, ds = orc.gated_attention_backward(q, k, v, do, s, idx, block, scale, gate="outer")
+    eps = 1e-6
+    r = rng(19)
+
+    def loss():
+        o, _, _ = orc.gated_attention_forward(q, k, v, s, idx, block, scale, gate="outer")
+        return float(np.sum(o * do))
+
+    def fd(arr, pos):
+        a0 = arr[pos]
+        arr[pos] = a0 + eps
+        lp = loss()
+        arr[pos] = a0 - eps
+        lm = loss()
+        arr[pos] = a0
+        return (lp - lm) / (2 * eps)
+
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for _ in range(8):
+            pos = tuple(int(r.integers(0, n)) for n in arr.shape)
+            assert abs(fd(arr, pos) - grad[pos]) < 1e-7 * max(1.0, abs(grad[pos]))
+    for t in (6, 13, 19):
+        for h in range(Hq):
+            for m in range(s.shape[3]):
+                pos = (0, h, t, m)
+                assert abs(fd(s, pos) - ds[pos]) < 1e-7, (pos, fd(s, pos), ds[pos])
+
+
+def test_outer_gate_gradient_closed_form():
+    """ds through the pages' outer-gate gradient dg_m = sum_{i in B_m} p_i dO.v_i
+    (review "Why the Four Design Choices Matter", paper Eq. 5), p the library
+    softmax of the ungated logits, pushed through the library softmax's
+    backward to the scores."""
+    block, D, N = 8, 8, 40
+    q, k, v, do, s = rand_problem(47, Hq=1, Hkv=1, N=N, D=D, block=block)
+    scale = 0.5
+    _, _, _, ds = orc.gated_attention_backward(q, k, v, do, s, None, block, scale, gate="outer")
+    qt, kt, vt = (torch.tensor(x[0, 0]) for x in (q, k, v))
+    for t in (17, 30, 39):
+        c = t // block
+        z = scale * (kt[:t + 1] @ qt[t])
+        p = torch.softmax(z, dim=0)
+        dO = torch.tensor(do[0, 0, t])
+        dg = torch.stack([(p[m * block:(m + 1) * block] * (vt[m * block:(m + 1) * block] @ dO)).sum()
+                          for m in range(c)])
+        sv = torch.tensor(s[0, 0, t, :c], requires_grad=True)
+        torch.softmax(sv, dim=0).backward(dg)
+        np.testing.assert_allclose(ds[0, 0, t, :c], sv.grad.numpy(), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(ds[0, 0, t, c:], 0.0)
+
+
+def test_outer_gate_with_one_history_block_is_the_inner_gate():
+    """With one history block g = 1, so placing it inside or outside the softmax
+    gives the same output (rows of block 1)."""
+    block, D, N = 8, 6, 16
+    q, k, v, do, s = rand_problem(53, Hq=2, Hkv=1, N=N, D=D, block=block)
+    o_out = orc.gated_attention_forward(q, k, v, s, None, block, 0.4, gate="outer")[0]
+    o_in = orc.gated_attention_forward(q, k, v, s, None, block, 0.4)[0]
+    np.testing.assert_allclose(o_out, o_in, atol=1e-13)
