@@ -94,7 +94,10 @@ typedef enum {
 typedef enum {
   SAS_GATE_SOFTMAX = 0,  /* log g = s - LSE_s over the history (SAS) */
   SAS_GATE_SIGMOID = 1,  /* log g = log sigmoid(s), per block */
-  SAS_GATE_RAW = 2       /* log g = s: the raw logit injected as a bias */
+  SAS_GATE_RAW = 2,      /* log g = s: the raw logit injected as a bias */
+  SAS_GATE_OUTER = 3     /* g = softmax(s) outside the softmax: it scales
+                            each block's value contribution (review "Why
+                            the Four Design Choices Matter", gate placement) */
 } sas_gate;
 
 /*
@@ -198,9 +201,15 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v,
  *     SAS_GATE_SOFTMAX  exactly sas_gated_attn_fwd / _bwd.
  *     SAS_GATE_SIGMOID  bias log sigmoid(s[t,m]); ds = dbeta (1 - sigmoid(s)).
  *     SAS_GATE_RAW      bias s[t,m];               ds = dbeta.
- *   Neither non-softmax gate has a normaliser: the forward writes lse_s = 0
- *   and the backward ignores lse_s (it may be NULL), and ds of an unselected
- *   history block is 0.
+ *     SAS_GATE_OUTER    no bias on gated blocks; with p = softmax(z) and
+ *                       g = softmax(s) over the history (1 on the own block),
+ *                       o = sum_j g p_j v_j, and lse is the log-sum-exp of the
+ *                       ungated z.  dg_m = sum over block m of p dO.v (paper
+ *                       Eq. 5, outer), ds = g (dg - sum_m' g dg).
+ *   The sigmoid and raw gates have no normaliser: their forward writes
+ *   lse_s = 0, their backward ignores lse_s (it may be NULL), and ds of an
+ *   unselected history block is 0.  The outer gate writes and reads lse_s as
+ *   the softmax gate does.
  * gate:       a sas_gate value; anything else is SAS_EINVAL.
  * workspace:  sas_workspace_bytes(SAS_OP_FWD_GATE or SAS_OP_BWD_GATE, ...)
  *             bytes (the sigmoid gate keeps log sigmoid(s), fp32 [B,Hq,N,C],

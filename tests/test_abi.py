@@ -205,6 +205,11 @@ def test_gate_variant_host_checks():
     nb[8] = None
     nb[13] = 0  # B = 0: an empty call
     assert L.sas_gated_attn_bwd_gate(*nb, 2, None, 0, None) == sas.SAS_OK
+    # the outer gate reads lse_s: NULL is refused
+    nb[13] = 1
+    assert L.sas_gated_attn_bwd_gate(*nb, 3, None, 0, None) == sas.SAS_EINVAL
+    # and needs no workspace beyond the softmax gate's
+    assert sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 4, 2, 128, 128, 64, -1, 1) > 0
     B, Hq, Hkv, N, D, blk = 1, 32, 8, 8192, 128, 64
     rows, C = B * Hq * N, N // blk
     f0 = sas.sas_workspace_bytes(sas.SAS_OP_FWD, B, Hq, Hkv, N, D, blk, -1, 1)

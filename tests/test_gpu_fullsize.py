@@ -110,9 +110,9 @@ def test_training_fullsize(wi):
     normwise(to64(step.dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
 
 
-@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+@pytest.mark.parametrize("gate", ["sigmoid", "raw", "outer"])
 def test_gate_variant_fullsize(gate):
-    """The sigmoid and raw-logit gates at the 32K sparse training shape, through
+    """The sigmoid, raw-logit and outer gates at the 32K sparse training shape, through
     sas_gated_attn_fwd_gate / _bwd_gate on the oracle's scores and selection:
     sampled rows of o, lse, dq and ds, and sampled keys of dk and dv."""
     w = WORKLOADS[2]
@@ -131,7 +131,7 @@ def test_gate_variant_fullsize(gate):
     torch.cuda.synchronize()
     idx = idx_t.cpu().numpy()
     assert np.array_equal(idx[:, :, rows], orc.topk_select(s32[:, :, rows], G, pos[:, rows], w.topk)), "topk"
-    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW}[gate]
+    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW, "outer": sas.SAS_GATE_OUTER}[gate]
     B, Hq, Hkv, N, D, C = w.B, w.Hq, w.Hkv, w.N, w.D, w.C
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
@@ -143,16 +143,19 @@ def test_gate_variant_fullsize(gate):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
     wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, w.block, w.topk, sas.SAS_BF16, DEV)
-    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, None, dq, dk, dv, ds, w.block, w.scale, g,
-                                wsb)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, lse_s if gate == "outer" else None, dq, dk,
+                                dv, ds, w.block, w.scale, g, wsb)
     torch.cuda.synchronize()
     del wsb
     s64 = s32.astype(np.float64)
-    o_ref, lse_ref, _ = orc.gated_attention_forward(q64, k64, v64, s64, idx, w.block, w.scale, rows=rows,
-                                                    gate=gate)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(q64, k64, v64, s64, idx, w.block, w.scale, rows=rows,
+                                                           gate=gate)
     max_abs(to64(o[:, :, rows]), o_ref, 2e-2, "o")
     normwise(to64(lse[:, :, rows]), lse_ref, 1e-4, "lse")
-    assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
+    if gate == "outer":
+        normwise(to64(lse_s[:, :, rows]), lses_ref, 1e-4, "lse_s")
+    else:
+        assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
     for h in (1, Hq - 2):
         dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, h, rows, gate=gate)
         normwise(to64(dq[0, h, rows]), dq_r, 2e-2, f"dq h{h}")

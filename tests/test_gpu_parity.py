@@ -404,13 +404,14 @@ GATE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("gate", ["sigmoid", "raw"])
+@pytest.mark.parametrize("gate", ["sigmoid", "raw", "outer"])
 @pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
 def test_gate_variant_parity(case, gate):
-    """Sigmoid and raw-logit gates (the pages' gate-activation ablation) through
-    sas_gated_attn_fwd_gate / _bwd_gate against the oracle at the same
-    tolerances as the softmax gate; lse_s is written as 0 and the backward
-    takes no lse_s."""
+    """Sigmoid and raw-logit gates (the pages' gate-activation ablation) and the
+    outer gate (gate placement) through sas_gated_attn_fwd_gate / _bwd_gate
+    against the oracle at the same tolerances as the softmax gate.  The
+    sigmoid and raw gates write lse_s = 0 and their backward takes no lse_s;
+    the outer gate's lse_s is the softmax gate's."""
     name, dts, B, Hq, Hkv, D, N, block, topk = case
     dt = _dt(dts)
     w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=11)
@@ -422,7 +423,7 @@ def test_gate_variant_parity(case, gate):
     _, _, s32, idx = _oracle_selector(q, k, block, scale, topk, G)
     scores = torch.tensor(s32).to(DEV)
     idx_t = None if idx is None else torch.tensor(idx).to(DEV)
-    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW}[gate]
+    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW, "outer": sas.SAS_GATE_OUTER}[gate]
     tk = -1 if topk is None else topk
     sdt = sas.SAS_F32 if dt == torch.float32 else sas.SAS_BF16
     o = torch.empty_like(q)
@@ -432,20 +433,23 @@ def test_gate_variant_parity(case, gate):
     sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, block, scale, g, wsf)
     torch.cuda.synchronize()
     s64 = s32.astype(np.float64)
-    o_ref, lse_ref, _ = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale,
-                                                    gate=gate)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale,
+                                                           gate=gate)
     if tol["o_abs"] is not None:
         max_abs(to64(o), o_ref, tol["o_abs"], "o")
     else:
         normwise(to64(o), o_ref, tol["o_rel"], "o")
     normwise(to64(lse), lse_ref, tol["lse"], "lse")
-    assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
+    if gate == "outer":
+        normwise(to64(lse_s), lses_ref, tol["lse"], "lse_s")
+    else:
+        assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
     wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
-    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, None, dq, dk, dv, ds, block, scale, g,
-                                wsb)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, lse_s if gate == "outer" else None, dq, dk,
+                                dv, ds, block, scale, g, wsb)
     torch.cuda.synchronize()
     r_dq, r_dk, r_dv, r_ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx,
                                                           block, scale, gate=gate)
@@ -453,7 +457,7 @@ def test_gate_variant_parity(case, gate):
     normwise(to64(dk), r_dk, tol["grad"], "dk")
     normwise(to64(dv), r_dv, tol["grad"], "dv")
     normwise(to64(ds), r_ds, tol["ds"], "ds")
-    if idx is not None:  # no normaliser: unselected history blocks get exactly 0
+    if idx is not None and gate != "outer":  # no normaliser: unselected history blocks get exactly 0
         sel = np.zeros((B, Hq, N, C), dtype=bool)
         for b in range(B):
             for h in range(Hq):

@@ -188,8 +188,7 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
-  if (gate != SAS_GATE_SOFTMAX && gate != SAS_GATE_SIGMOID && gate != SAS_GATE_RAW)
-    return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
+  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_OUTER) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
   if (empty(B, Hq, N)) {
     g_error.clear();
     return SAS_OK;
@@ -214,15 +213,15 @@ static int attn_bwd(const char* what, const void* q, const void* k, const void* 
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
-  if (gate != SAS_GATE_SOFTMAX && gate != SAS_GATE_SIGMOID && gate != SAS_GATE_RAW)
-    return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
+  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_OUTER) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
   if (empty(B, Hq, N)) {
     g_error.clear();
     return SAS_OK;
   }
-  if (!q || !k || !v || !o || !dout || !scores || !lse || (!lse_s && gate == SAS_GATE_SOFTMAX) || !dq ||
+  const bool needs_lse_s = gate == SAS_GATE_SOFTMAX || gate == SAS_GATE_OUTER;
+  if (!q || !k || !v || !o || !dout || !scores || !lse || (!lse_s && needs_lse_s) || !dq ||
       !dk || !dv || !ds)
-    return fail(SAS_EINVAL, "%s: every tensor pointer except idx (and lse_s for a non-softmax gate) must be non-NULL",
+    return fail(SAS_EINVAL, "%s: every tensor pointer except idx (and lse_s for the sigmoid and raw gates) must be non-NULL",
                 what);
   sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
   const bool bf16 = dtype == SAS_BF16;

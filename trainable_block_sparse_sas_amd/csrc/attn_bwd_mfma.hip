@@ -105,7 +105,9 @@ __global__ __launch_bounds__(256) void bwd_delta_mfma_kernel(const bf16_t* __res
 //   dV += P^T dO, dK += dS^T Q  A: P^T / dS^T from registers (the permuted row
 //                               order of the S accumulators); B: dO / Q read
 //                               transposed from the row-major tile
-template <int D, int G, bool SPARSE>
+// OUTER: the outer gate: history rows take no bias, g = exp(s - LSE_s)
+// scales P in dV and dP in dZ, and the recorded dbeta is sum P g dP (= g dg).
+template <int D, int G, bool SPARSE, bool OUTER>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L) {
   using namespace tiles;
   constexpr int WAVES = 4;
@@ -302,12 +304,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // base-2 logit offset: bias - lse
-        const float off = MK ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
+        const float off = (MK || OUTER) ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
         float x = fmaf(sacc[rs][i], c1, off);
         const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
         x = ok ? x : kNegInf;
         p[i] = exp2_hw(x);
-        d[i] = p[i] * (pacc[rs][i] - dl[i]);
+        if constexpr (OUTER && !MK) {
+          const float gf = ok ? exp2_hw((sv[i] - ls[i]) * kLog2e) : 0.f;
+          const float gdp = gf * pacc[rs][i];
+          d[i] = p[i] * (gdp - dl[i]);
+          if constexpr (SPARSE) dsum[4 * rs + i] = p[i] * gdp;  // g dg, in dbeta's place
+          p[i] *= gf;                                         // g P for dV
+        } else {
+          d[i] = p[i] * (pacc[rs][i] - dl[i]);
+        }
       }
       const int kk = rs >> 1;
       const uint32_t d01 = pack_bf16(d[0], d[1]), d23 = pack_bf16(d[2], d[3]);
@@ -330,8 +340,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         col[TST] = uint16_t(d01 >> 16);
         col[2 * TST] = uint16_t(d23);
         col[3 * TST] = uint16_t(d23 >> 16);
+        if constexpr (!(OUTER && !MK)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dsum[4 * rs + i] = d[i];
+          for (int i = 0; i < 4; ++i) dsum[4 * rs + i] = d[i];
+        }
       }
     }
     // dV += P^T dO, dK += dS^T Q.  B operand (32 rows x 16 columns) read
@@ -744,7 +756,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
 // blocks run in a second, masked loop.  The epilogue writes dq and turns the
 // row's dbeta into ds = dbeta - g sum(dbeta) (dense over the history).  This
 // is the full-scope dQ; sparse scope is key-major (bwd_dq_ds_kernel).
-template <int D, int G, int NSUB, int WAVES, int NST>
+template <int D, int G, int NSUB, int WAVES, int NST, bool OUTER>
 __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   using namespace tiles;
   constexpr int NT = 64 * WAVES;
@@ -913,7 +925,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
     const uint16_t* Vs = vst(tag);
     const float* Ss = sst(tag);
     int nmask = 0;
-    float bias2[NSUB];
+    float bias2[NSUB], gsc[NSUB];
     bool gated[NSUB];
     int row_t[NSUB];
     float lse2[NSUB], del[NSUB];
@@ -934,9 +946,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
       const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
       nmask |= int(nd) << s;
       gated[s] = sel;
-      // bias minus the row's lse (base 2); -inf where the row skips the tile
+      // bias minus the row's lse (base 2); -inf where the row skips the tile.
+      // OUTER: no bias, the gate g scales dP in dZ and in g dg (dbeta's place).
       const bool valid = row_t[s] < N && (own || sel);
-      bias2[s] = valid ? (own ? 0.f : bsel) - lse2[s] : kNegInf;
+      bias2[s] = valid ? (own || OUTER ? 0.f : bsel) - lse2[s] : kNegInf;
+      gsc[s] = OUTER && sel && !own ? exp2_hw(bsel) : 1.f;
     }
     nmask = __builtin_amdgcn_readfirstlane(nmask);
     if (nmask) {
@@ -978,8 +992,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 2 : 1) void bwd_dq_kernel(
           for (int i = 0; i < 4; ++i) {
             float x = fmaf(sa[s][i], c1, bias2[s]);
             if (MK && m * KT + 16 * mt + 4 * lq + i > row_t[s]) x = kNegInf;
-            dz[i] = exp2_hw(x) * (pa[s][i] - del[s]);
-            dsum[s] += dz[i];
+            if constexpr (OUTER) {
+              const float pv = exp2_hw(x), gdp = gsc[s] * pa[s][i];
+              dz[i] = pv * (gdp - del[s]);
+              dsum[s] += pv * gdp;
+            } else {
+              dz[i] = exp2_hw(x) * (pa[s][i] - del[s]);
+              dsum[s] += dz[i];
+            }
           }
           if (mt & 1) {
             dsf[s][mt >> 1].z = pack_bf16(dz[0], dz[1]);
@@ -1156,8 +1176,12 @@ static void launch_dq_full(BwdArgs a, hipStream_t s) {
   constexpr int NSUB = 2, WAVES = 8, NST = 2;
   constexpr int TOK_WG = 16 * NSUB * WAVES / G;
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
-  SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST>), dim3(a.n_tiles * a.n_pairs),
-             dim3(64 * WAVES), 0, s, a);
+  if (a.gate == kGateOuter)
+    SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, true>), dim3(a.n_tiles * a.n_pairs),
+               dim3(64 * WAVES), 0, s, a);
+  else
+    SAS_LAUNCH("bwd_dq", (bwd_dq_kernel<D, G, NSUB, WAVES, NST, false>), dim3(a.n_tiles * a.n_pairs),
+               dim3(64 * WAVES), 0, s, a);
 }
 
 template <int D, int G, bool SPARSE>
@@ -1171,7 +1195,10 @@ static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s)
   }
   a.n_pairs = B * a.Hkv;
   a.n_tiles = (a.N + KT - 1) / KT;
-  SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a, L);
+  if (a.gate == kGateOuter)
+    SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE, true>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a, L);
+  else
+    SAS_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<D, G, SPARSE, false>), dim3(a.n_tiles * a.n_pairs), dim3(256), 0, s, a, L);
   if (SPARSE)
     launch_dq_sparse<D, G>(a, L, rows, s);
   else

@@ -8,7 +8,11 @@
 // LSE_s = 0, the raw logit's bias s for the scores s and LSE_s = 0, so these
 // gates run the same kernels on rewritten scores; only the ds epilogues take
 // the gate (ds = dbeta (1 - g) with g = e^{s'} = sigmoid(s), or ds = dbeta,
-// instead of dbeta - g sum(dbeta)).
+// instead of dbeta - g sum(dbeta)).  The outer gate (gate placement of the
+// same pages) keeps LSE_s and the scores; its kernels take it as a template
+// argument: no bias on gated blocks, g scales P in P V, in dV and in dZ, and
+// the dK/dV kernels record g dg in dbeta's place, so the softmax gate's ds
+// epilogue applies.
 #include <algorithm>
 
 #include "common.h"
@@ -18,7 +22,7 @@ namespace sas {
 
 hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool bf16, bool norm, hipStream_t s);
+                           int topk, float scale, bool bf16, bool norm, bool outer, hipStream_t s);
 hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
@@ -29,7 +33,7 @@ bool fwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool norm, void* ws, hipStream_t s);
+                           int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s);
 
 bool bwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse);
@@ -102,13 +106,13 @@ size_t bwd_workspace(const Dims& d, int topk, bool bf16) {
 // backward) a zero LSE_s per row.
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
   const size_t base = fwd_workspace(d, topk, bf16);
-  if (gate == kGateSoftmax) return base;
+  if (gate == kGateSoftmax || gate == kGateOuter) return base;
   return align_up(base) + (gate == kGateSigmoid ? align_up(rows_of(d) * d.C * sizeof(float)) : 0);
 }
 
 size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
   const size_t base = bwd_workspace(d, topk, bf16);
-  if (gate == kGateSoftmax) return base;
+  if (gate == kGateSoftmax || gate == kGateOuter) return base;
   return align_up(base) + (gate == kGateSigmoid ? align_up(rows_of(d) * d.C * sizeof(float)) : 0) +
          align_up(rows_of(d) * sizeof(float));
 }
@@ -116,7 +120,8 @@ size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s) {
-  const bool norm = gate == kGateSoftmax;
+  const bool norm = gate == kGateSoftmax || gate == kGateOuter;
+  const bool outer = gate == kGateOuter;
   if (!norm) {
     // lse_s <- 0, and the sigmoid gate's scores log sigmoid(s)
     char* extra = static_cast<char*>(ws) + align_up(fwd_workspace(d, idx ? topk : -1, bf16));
@@ -126,8 +131,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
     if (sp) scores = sp;
   }
   if (bf16 && fwd_mfma_supported(d, topk, idx != nullptr))
-    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, ws, s);
-  return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, norm, s);
+    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, ws, s);
+  return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, norm, outer, s);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -135,7 +140,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                       float* ds, const Dims& d, int topk, float scale, bool bf16, int gate, void* ws,
                       hipStream_t s) {
-  if (gate != kGateSoftmax) {
+  if (gate == kGateSigmoid || gate == kGateRaw) {
     char* extra = static_cast<char*>(ws) + align_up(bwd_workspace(d, idx ? topk : -1, bf16));
     float* sp = nullptr;
     if (gate == kGateSigmoid) {

@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256) void lse_rows_kernel(const float* __restrict__
   if (lane == 0) lse_s[row] = c > 0 ? mx + log_hw(sm) : kNegInf;
 }
 
-template <int D, int G, int NSUB, int WAVES, int NST>
+// OUTER: the outer gate (no bias on gated tiles; P scaled by g = exp(s -
+// LSE_s) in P V only, the row sum l from the unscaled P).
+template <int D, int G, int NSUB, int WAVES, int NST, bool OUTER>
 __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int NT = 64 * WAVES;
   constexpr int KS = D / 32;    // k-steps of S = K Q^T
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
     // Which subtiles take part (a wave-uniform bit mask), and each lane's bias
     // for its row (base 2; -inf where the row does not attend the tile).
     int nmask = 0;
-    float bias2[NSUB];
+    float bias2[NSUB], gsc[NSUB];
     for (int s = 0; s < NSUB; ++s) {
       const bool own = (m == c_sub[s]);
       const bool hist = (m < c_sub[s]);
@@ -309,7 +311,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
       }
       const bool nd = sub_live[s] && (own || (hist && __ballot(sel) != 0ull));
       nmask |= int(nd) << s;
-      bias2[s] = own ? 0.f : (sel ? bsel : kNegInf);
+      bias2[s] = own ? 0.f : (sel ? (OUTER ? 0.f : bsel) : kNegInf);
+      gsc[s] = OUTER && !own && sel ? exp2_hw(bsel) : 1.f;
     }
     nmask = __builtin_amdgcn_readfirstlane(nmask);
 
@@ -376,6 +379,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
             ps += z[mt][i];
           }
         lpart[s] += ps;
+        if constexpr (OUTER) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[mt][i] *= gsc[s];  // the gate scales P V only
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           pf[s][kk].x = pack_bf16(z[2 * kk][0], z[2 * kk][1]);
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
 }
 
 template <int D, int G>
-hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, hipStream_t stream) {
+hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, bool outer, hipStream_t stream) {
   constexpr int NSUB = 2;
   constexpr int WAVES = 8;
   constexpr int NST = 2;
@@ -465,8 +474,12 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, hipStream_t stream) {
                a.lse_s, a.N, a.C, KT, rows);
   SAS_LAUNCH("vt", (vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
                      const_cast<bf16_t*>(a.vt), a.Hkv, a.N, a.NB);
-  SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST>),
-                     dim3(a.n_tiles * a.n_pairs), dim3(64 * WAVES), 0, stream, a);
+  if (outer)
+    SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST, true>), dim3(a.n_tiles * a.n_pairs),
+               dim3(64 * WAVES), 0, stream, a);
+  else
+    SAS_LAUNCH("fwd_mfma", (fwd_mfma_kernel<D, G, NSUB, WAVES, NST, false>), dim3(a.n_tiles * a.n_pairs),
+               dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -493,7 +506,7 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool norm, void* ws, hipStream_t s) {
+                           int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s) {
   FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
             (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale};
   const int G = d.G();
@@ -504,10 +517,10 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
     if (norm)
       SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
                  d.N, d.C, KT, rows);
-    return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, ws, s);
+    return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, outer, ws, s);
   }
 #define SAS_FWD_CASE(DD, GG) \
-  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, norm, s);
+  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, norm, outer, s);
   SAS_FWD_CASE(128, 4)
   SAS_FWD_CASE(128, 1)
   SAS_FWD_CASE(128, 2)

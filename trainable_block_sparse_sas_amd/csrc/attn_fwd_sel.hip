@@ -51,7 +51,9 @@ struct FwdSelArgs {
   float scale;
 };
 
-template <int D, int G>
+// OUTER: the outer gate (no bias; P scaled by g = exp(s - LSE_s) in P V only,
+// l from the unscaled P), so the combine's merge stays as it is.
+template <int D, int G, bool OUTER>
 __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L) {
   using namespace tiles;
   constexpr int WAVES = 16;
@@ -160,11 +162,13 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         dma16_to_lds(a.q + qoff[j] + size_t(t) * D, st + j * 512);
       }
     };
-    // the row's gate bias in base 2 (own block: 0)
+    // the row's gate bias in base 2 (own block: 0); OUTER: the gate g itself
+    // (own block: 1)
     auto load_bias = [&](uint32_t e) -> float {
-      if (own_item) return 0.f;
+      if (own_item) return OUTER ? 1.f : 0.f;
       const size_t gr = rbase + (e & 0x7fffffu);
-      return (a.scores[gr * C + m] - a.lse_s[gr]) * kLog2e;
+      const float lg = (a.scores[gr * C + m] - a.lse_s[gr]) * kLog2e;
+      return OUTER ? exp2_hw(lg) : lg;
     };
 
     auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, float bias, int ln) {
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[kt][i] = fmaf(sacc[kt][i], c1, bias);
+          x[kt][i] = fmaf(sacc[kt][i], c1, OUTER ? 0.f : bias);
           if (MASK) x[kt][i] = j0 + 16 * kt + 4 * lq + i <= tlim ? x[kt][i] : kNegInf;
           mx = fmaxf(mx, x[kt][i]);
         }
@@ -212,6 +216,10 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
             p[4 * h + i] = exp2_hw(x[2 * kk + h][i] - ms);
             l += p[4 * h + i];
           }
+        if constexpr (OUTER) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[j] *= bias;  // the gate scales P V only
+        }
         pb[kk] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                             pack_bf16(p[6], p[7]));
       }
@@ -390,11 +398,14 @@ FwdSelWs fwd_sel_layout(const Dims& d, int topk) {
 }
 
 template <int D, int G>
-hipError_t fwd_sel_t(const FwdSelArgs& a, const SelLists& L, int B, hipStream_t s) {
+hipError_t fwd_sel_t(const FwdSelArgs& a, const SelLists& L, int B, bool outer, hipStream_t s) {
   const size_t rows = size_t(B) * a.Hq * a.N;
   // persistent: one workgroup per compute unit (the LDS stages fill it)
   const int grid = std::min(a.n_pairs * L.maxitems, num_cus());
-  SAS_LAUNCH("fwd_sel", (fwd_sel_kernel<D, G>), dim3(grid), dim3(1024), 0, s, a, L);
+  if (outer)
+    SAS_LAUNCH("fwd_sel", (fwd_sel_kernel<D, G, true>), dim3(grid), dim3(1024), 0, s, a, L);
+  else
+    SAS_LAUNCH("fwd_sel", (fwd_sel_kernel<D, G, false>), dim3(grid), dim3(1024), 0, s, a, L);
   SAS_LAUNCH("fwd_combine", (fwd_combine_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, a, L, G, rows);
   return hipGetLastError();
 }
@@ -406,7 +417,7 @@ size_t fwd_sel_workspace(const Dims& d, int topk) { return fwd_sel_layout(d, top
 // Sparse-scope forward over the selection lists (LSE_s already in lse_s).
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, void* ws, hipStream_t s) {
+                          int topk, float scale, bool outer, void* ws, hipStream_t s) {
   char* w = static_cast<char*>(ws);
   const FwdSelWs W = fwd_sel_layout(d, topk);
   const SelLists L = sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kFwdChunk, w + W.lists, nullptr);
@@ -433,7 +444,7 @@ hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const flo
   a.scale = scale;
   const int G = d.G();
 #define SAS_FWDSEL_CASE(DD, GG) \
-  if (d.D == DD && G == GG) return fwd_sel_t<DD, GG>(a, L, d.B, s);
+  if (d.D == DD && G == GG) return fwd_sel_t<DD, GG>(a, L, d.B, outer, s);
   SAS_FWDSEL_CASE(128, 4)
   SAS_FWDSEL_CASE(128, 1)
   SAS_FWDSEL_CASE(128, 2)

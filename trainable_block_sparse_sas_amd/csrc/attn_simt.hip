@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ scores, const int32_t* __restrict__ idx, T* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ lse_s, int Hq, int Hkv, int N, int C, int block,
-    int topk, float scale, int norm) {
+    int topk, float scale, int norm, int outer) {
   constexpr int DS = D / 4;
   extern __shared__ uint32_t dyn_mask[];
   __shared__ float ks[KT][D + 1];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
   }
   float mi = kNegInf, li = 0.f;
   int cur_m = -1;
-  float cur_bias = kNegInf;
+  float cur_bias = kNegInf, cur_g = 1.f;  // outer gate: no bias, g scales the value
   const T* kh = k + (size_t(b) * Hkv + g) * N * D;
   const T* vh = v + (size_t(b) * Hkv + g) * N * D;
   const int t_last = min(N, tile * 64 + 64) - 1;
@@ -135,6 +135,11 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
         if (m != cur_m) {
           cur_m = m;
           cur_bias = (m == c) ? 0.f : ((full || mask_bit(mask, m)) ? srow[m] - lses : kNegInf);
+          cur_g = 1.f;
+          if (outer && m != c && cur_bias != kNegInf) {
+            cur_g = exp_hw(cur_bias);
+            cur_bias = 0.f;
+          }
         }
         if (cur_bias == kNegInf) continue;
         float dot = 0.f;
@@ -144,7 +149,8 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
         const float alpha = exp_hw(mi - nm);
         const float pe = exp_hw(z - nm);
         li = li * alpha + pe;
-        for (int i = 0; i < DS; ++i) acc[i] = acc[i] * alpha + pe * vs[jj][p * DS + i];
+        const float pv = pe * cur_g;
+        for (int i = 0; i < DS; ++i) acc[i] = acc[i] * alpha + pv * vs[jj][p * DS + i];
         mi = nm;
       }
     }
@@ -215,7 +221,8 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(
     dqa[i] = 0.f;
   }
   int cur_m = -1;
-  float cur_bias = kNegInf, db_cur = 0.f, db_total = 0.f;
+  float cur_bias = kNegInf, cur_g = 1.f, db_cur = 0.f, db_total = 0.f;
+  const bool outer = gate == kGateOuter;
   const T* kh = k + (size_t(b) * Hkv + g) * N * D;
   const T* vh = v + (size_t(b) * Hkv + g) * N * D;
   const int t_last = min(N, tile * 64 + 64) - 1;
@@ -238,6 +245,11 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(
           db_cur = 0.f;
           cur_m = m;
           cur_bias = (m == c) ? 0.f : ((full || mask_bit(mask, m)) ? srow[m] - lses : kNegInf);
+          cur_g = 1.f;
+          if (outer && m != c && cur_bias != kNegInf) {
+            cur_g = exp_hw(cur_bias);
+            cur_bias = 0.f;
+          }
         }
         if (cur_bias == kNegInf) continue;
         float dot = 0.f, dpp = 0.f;
@@ -247,9 +259,10 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(
         }
         const float z = quad_sum(dot) * scale + cur_bias;
         const float pr = exp_hw(z - lrow);
-        const float dz = pr * (quad_sum(dpp) - drow);
+        const float gdp = cur_g * quad_sum(dpp);
+        const float dz = pr * (gdp - drow);
         for (int i = 0; i < DS; ++i) dqa[i] = fmaf(scale * dz, ks[jj][p * DS + i], dqa[i]);
-        db_cur += dz;
+        db_cur += outer ? pr * gdp : dz;  // outer gate: g dg in dbeta's place
       }
     }
     __syncthreads();
@@ -282,13 +295,14 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
     const T* __restrict__ dout, const float* __restrict__ scores, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, const float* __restrict__ lse_s,
     const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int Hq, int Hkv,
-    int N, int C, int block, int topk, float scale) {
+    int N, int C, int block, int topk, float scale, int outer) {
   constexpr int DS = D / 4;
   constexpr int RT = 32;  // query rows per LDS tile
   __shared__ float qs[RT][D + 1];
   __shared__ float dos[RT][D + 1];
   __shared__ float rlse[RT], rdelta[RT];
   __shared__ float rbias[RT][KT];
+  __shared__ float rgate[RT][KT];  // outer gate: g of (row, block), else 1
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int kk = threadIdx.x >> 2, p = threadIdx.x & 3;
@@ -325,7 +339,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
       for (int i = threadIdx.x; i < RT * nb; i += blockDim.x) {
         const int rr = i / nb, mb = i % nb;
         const int t = r0 + rr, m = m_first + mb;
-        float bias = kNegInf;
+        float bias = kNegInf, gt = 1.f;
         if (t < N) {
           const int c = t / block;
           const size_t row = (size_t(b) * Hq + h) * N + t;
@@ -338,9 +352,14 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
               for (int e = 0; e < topk && !sel; ++e) sel = (ir[e] == m);
             }
             if (sel) bias = scores[row * C + m] - lse_s[row];
+            if (sel && outer) {
+              gt = exp_hw(bias);
+              bias = 0.f;
+            }
           }
         }
         rbias[rr][mb] = bias;
+        rgate[rr][mb] = gt;
       }
       __syncthreads();
       if (kv) {
@@ -349,6 +368,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
           if (t >= N) break;
           if (t < j) continue;
           const float bias = rbias[rr][j / block - m_first];
+          const float gt = rgate[rr][j / block - m_first];
           if (bias == kNegInf) continue;
           float dot = 0.f, dpp = 0.f;
           for (int i = 0; i < DS; ++i) {
@@ -357,9 +377,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
           }
           const float z = quad_sum(dot) * scale + bias;
           const float pr = exp_hw(z - rlse[rr]);
-          const float dz = pr * (quad_sum(dpp) - rdelta[rr]);
+          const float dz = pr * (gt * quad_sum(dpp) - rdelta[rr]);
+          const float pg = pr * gt;
           for (int i = 0; i < DS; ++i) {
-            dva[i] = fmaf(pr, dos[rr][p * DS + i], dva[i]);
+            dva[i] = fmaf(pg, dos[rr][p * DS + i], dva[i]);
             dka[i] = fmaf(scale * dz, qs[rr][p * DS + i], dka[i]);
           }
         }
@@ -377,12 +398,12 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
 template <typename T, int D>
 hipError_t fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                     const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d, int topk,
-                    float scale, bool norm, hipStream_t s) {
+                    float scale, bool norm, bool outer, hipStream_t s) {
   const size_t mask_bytes = idx ? size_t(64) * ((d.C + 31) / 32) * 4 : 0;
   dim3 grid((d.N + 63) / 64, d.Hq, d.B);
   SAS_LAUNCH("fwd_simt", (fwd_simt_kernel<T, D>), grid, dim3(256), mask_bytes, s, (const T*)q,
                      (const T*)k, (const T*)v, scores, idx, (T*)o, lse, lse_s, d.Hq, d.Hkv, d.N,
-                     d.C, d.block, topk, scale, int(norm));
+                     d.C, d.block, topk, scale, int(norm), int(outer));
   return hipGetLastError();
 }
 
@@ -402,7 +423,7 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
   SAS_LAUNCH("bwd_dkdv_simt", (bwd_dkdv_simt_kernel<T, D>), dim3((d.N + KT - 1) / KT, d.Hkv, d.B),
                      dim3(128), 0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout,
                      scores, idx, lse, lse_s, delta, (T*)dk, (T*)dv, d.Hq, d.Hkv, d.N, d.C,
-                     d.block, topk, scale);
+                     d.block, topk, scale, int(gate == kGateOuter));
   return hipGetLastError();
 }
 
@@ -410,13 +431,13 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
 
 hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool bf16, bool norm, hipStream_t s) {
+                           int topk, float scale, bool bf16, bool norm, bool outer, hipStream_t s) {
   if (bf16) {
-    if (d.D == 64) return fwd_simt<bf16_t, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
-    return fwd_simt<bf16_t, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
+    if (d.D == 64) return fwd_simt<bf16_t, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);
+    return fwd_simt<bf16_t, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);
   }
-  if (d.D == 64) return fwd_simt<float, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
-  return fwd_simt<float, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, s);
+  if (d.D == 64) return fwd_simt<float, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);
+  return fwd_simt<float, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);
 }
 
 hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const void* o,

@@ -37,7 +37,7 @@ __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f
 __device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
 // Gate activations (the values of sas_gate).
-constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2;
+constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2, kGateOuter = 3;
 
 // ds of a history block from db (its dz sum when gated, else 0), x = s - LSE_s
 // (for the sigmoid gate s is the rewritten score log sigmoid(s) and LSE_s = 0,
@@ -46,6 +46,7 @@ constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2;
 //   softmax  db - e^x total   (log g = s - LSE(s))
 //   sigmoid  db (1 - e^x)     (d log sigmoid(s) / ds = 1 - sigmoid(s))
 //   raw      db               (log g = s)
+// (the outer gate records g dg as db and takes the softmax rule)
 __device__ __forceinline__ float gate_ds(int gate, float db, float x, float tot) {
   if (gate == kGateSigmoid) return -db * expm1f(x);
   if (gate == kGateRaw) return db;

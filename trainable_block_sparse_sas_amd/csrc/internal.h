@@ -89,7 +89,7 @@ hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hk
 size_t fwd_sel_workspace(const Dims& d, int topk);
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, void* ws, hipStream_t s);
+                          int topk, float scale, bool outer, void* ws, hipStream_t s);
 size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
