@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 101
+    assert sas.sas_abi_version() == 102
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0

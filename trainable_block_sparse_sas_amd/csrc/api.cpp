@@ -76,7 +76,7 @@ extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 101; }
+int sas_abi_version(void) { return 102; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
