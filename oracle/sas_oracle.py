@@ -482,6 +482,49 @@ def key_gradients(q, k, v, do, s, idx, block, scale, b, g, keys, row_chunk=1024,
     return dk, dv
 
 
+def ste_gate_attention(q, k, v, do, s, idx, block, scale):
+    """The hard gate with a straight-through estimator ([Review] "Why the Four
+    Design Choices Matter", ranking preservation; [Blog] 方法核心, the ablation
+    table's hard-gate row), read as: the forward is plain block-sparse
+    attention over the own block and the selected blocks (hard gate 1 there,
+    0 on dropped blocks, normalised over that set S only); dq, dk, dv are its
+    gradients; and the gate gradient of every history block m, selected or
+    dropped, is that of a multiplicative gate at its hard value,
+        dh_m = sum_{i in B_m} p_i dO.(v_i - o),  p_i = exp(z_i - LSE_S),
+    (for a dropped block p_i is the weight the pages describe as unbounded),
+    passed straight through to the soft gate g = softmax(s):
+        ds_m = g_m (dh_m - sum_m' g_m' dh_m').
+    Returns (o, lse, lse_s, dq, dk, dv, ds), lse = LSE_S and lse_s = LSE(s)
+    over the history."""
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    C = s.shape[3]
+    zero = np.zeros_like(_as64(s))
+    o, lse, _ = gated_attention_forward(q, k, v, zero, idx, block, scale, gate="raw")
+    dq, dk, dv, _ = gated_attention_backward(q, k, v, do, zero, idx, block, scale, gate="raw")
+    rows = np.arange(N)
+    c = rows // block
+    hist = np.arange(C)[None, :] < c[:, None]
+    lse_s = np.zeros((B, Hq, N))
+    ds = np.zeros((B, Hq, N, C))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            z = scale * (_as64(q[b, h]) @ _as64(k[b, g]).T)
+            p = np.exp(z - lse[b, h][:, None])          # exp(z_i - LSE_S), every key
+            p = np.where(np.arange(N)[None, :] <= rows[:, None], p, 0.0)
+            dpd = _as64(do[b, h]) @ _as64(v[b, g]).T - np.sum(_as64(do[b, h]) * o[b, h], axis=-1)[:, None]
+            dh = np.where(hist, _block_sums(p * dpd, block, C), 0.0)
+            s_hist = np.where(hist, _as64(s[b, h]), NEG_INF)
+            ls = _logsumexp(s_hist, axis=-1)
+            lse_s[b, h] = ls
+            with np.errstate(invalid="ignore"):
+                gs = np.where(hist, np.exp(s_hist - ls[:, None]), 0.0)
+            ds[b, h] = np.where(hist, gs * (dh - np.sum(gs * dh, axis=1, keepdims=True)), 0.0)
+    return o, lse, lse_s, dq, dk, dv, ds
+
+
 # ----------------------------------------------------------------------------
 # a8: sparse decode attention (inference, no gate)
 # ----------------------------------------------------------------------------

@@ -819,3 +819,51 @@ def test_outer_gate_with_one_history_block_is_the_inner_gate():
     o_out = orc.gated_attention_forward(q, k, v, s, None, block, 0.4, gate="outer")[0]
     o_in = orc.gated_attention_forward(q, k, v, s, None, block, 0.4)[0]
     np.testing.assert_allclose(o_out, o_in, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The hard gate with a straight-through estimator (the pages' ranking ablation)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("topk", [0, 2])
+def test_ste_gate_against_autograd(topk):
+    """Library autograd with the straight-through trick: a multiplicative gate
+    h = hard + g - g.detach() (hard: 1 on selected blocks and the own block, 0
+    on dropped ones; g = softmax(s) over the history, 1 on the own block)
+    inside o = sum h e^z v / sum h e^z.  Its forward is the hard gate's, its
+    gradients are the oracle's, dropped blocks' ds included."""
+    block, D, N = 4, 5, 28
+    q, k, v, do, s = rand_problem(97, Hq=2, Hkv=1, N=N, D=D, block=block)
+    scale = 0.6
+    C = N // block
+    idx = orc.topk_select(s.astype(np.float32), 2, np.arange(N)[None, :] // block, topk)
+    o, lse, lse_s, dq, dk, dv, ds = orc.ste_gate_attention(q, k, v, do, s, idx, block, scale)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    st = torch.tensor(s, requires_grad=True)
+    dot = torch.tensor(do)
+    loss = 0.0
+    for h in range(2):
+        for t in range(N):
+            c = t // block
+            sel = {int(m) for m in idx[0, 0, t] if 0 <= m < c}
+            gsoft = torch.softmax(st[0, h, t, :c], dim=0) if c else None
+            z = scale * (kt[0, 0, :t + 1] @ qt[0, h, t])
+            hk = []
+            for j in range(t + 1):
+                m = j // block
+                if m == c:
+                    hk.append(torch.tensor(1.0, dtype=torch.float64))
+                else:
+                    hard = 1.0 if m in sel else 0.0
+                    hk.append(hard + gsoft[m] - gsoft[m].detach())
+            hk = torch.stack(hk)
+            w = hk * torch.exp(z - z.max())
+            out = (w[:, None] * vt[0, 0, :t + 1]).sum(0) / w.sum()
+            np.testing.assert_allclose(out.detach().numpy(), o[0, h, t], atol=1e-12)
+            loss = loss + (out * dot[0, h, t]).sum()
+    loss.backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(ds, st.grad.numpy(), atol=1e-11)
+    assert np.any(ds[0, :, :, :][np.broadcast_to(np.arange(C)[None, None, :], ds.shape[1:]) < 3] != 0)
