@@ -339,7 +339,8 @@ def bench_selector_bwd(torch, w, steps):
 
 
 def bench_gate_variants(torch, w, steps):
-    """The pages' gate ablations (sigmoid gate, raw logit, outer gate) through
+    """The pages' gate ablations (sigmoid gate, raw logit, outer gate, STE hard
+    gate; the STE backward visits every history block) through
     sas_gated_attn_fwd_gate / _bwd_gate on one step's scores and selection,
     timed on their own: forward + backward per gate (the rewrite of the scores
     included), priced with the step's algorithmic work, 14 D flops per
@@ -357,7 +358,8 @@ def bench_gate_variants(torch, w, steps):
     wsb = sas.workspace(sas.SAS_OP_BWD_GATE, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, tk, sdt)
     flops = 14 * w.D * attended_pairs(w.N, w.block, w.topk, w.Hq, w.B)
     out = {}
-    for name, g in (("sigmoid", sas.SAS_GATE_SIGMOID), ("raw", sas.SAS_GATE_RAW), ("outer", sas.SAS_GATE_OUTER)):
+    for name, g in (("sigmoid", sas.SAS_GATE_SIGMOID), ("raw", sas.SAS_GATE_RAW), ("outer", sas.SAS_GATE_OUTER),
+                    ("ste", sas.SAS_GATE_STE)):
         def one():
             sas.sas_gated_attn_fwd_gate(q, k, v, step.scores, step.idx, step.o, step.lse, step.lse_s, w.block,
                                         w.scale, g, wsf)

@@ -95,9 +95,11 @@ typedef enum {
   SAS_GATE_SOFTMAX = 0,  /* log g = s - LSE_s over the history (SAS) */
   SAS_GATE_SIGMOID = 1,  /* log g = log sigmoid(s), per block */
   SAS_GATE_RAW = 2,      /* log g = s: the raw logit injected as a bias */
-  SAS_GATE_OUTER = 3     /* g = softmax(s) outside the softmax: it scales
+  SAS_GATE_OUTER = 3,    /* g = softmax(s) outside the softmax: it scales
                             each block's value contribution (review "Why
                             the Four Design Choices Matter", gate placement) */
+  SAS_GATE_STE = 4       /* hard gate, straight-through estimator (same
+                            section, ranking preservation) */
 } sas_gate;
 
 /*
@@ -206,14 +208,22 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v,
  *                       o = sum_j g p_j v_j, and lse is the log-sum-exp of the
  *                       ungated z.  dg_m = sum over block m of p dO.v (paper
  *                       Eq. 5, outer), ds = g (dg - sum_m' g dg).
+ *     SAS_GATE_STE      the forward is plain block-sparse attention over the
+ *                       own and the selected blocks (lse = their LSE_S);
+ *                       dq, dk, dv are its gradients; for every history
+ *                       block, selected or dropped, dh_m = sum over block m
+ *                       of exp(z - LSE_S) dO.(v - o), and ds = g (dh -
+ *                       sum_m' g dh) with g = softmax(s).  The backward
+ *                       visits every history block (full-scope work).
  *   The sigmoid and raw gates have no normaliser: their forward writes
  *   lse_s = 0, their backward ignores lse_s (it may be NULL), and ds of an
- *   unselected history block is 0.  The outer gate writes and reads lse_s as
- *   the softmax gate does.
+ *   unselected history block is 0.  The outer and STE gates write and read
+ *   lse_s = LSE(s) as the softmax gate does.
  * gate:       a sas_gate value; anything else is SAS_EINVAL.
  * workspace:  sas_workspace_bytes(SAS_OP_FWD_GATE or SAS_OP_BWD_GATE, ...)
  *             bytes (the sigmoid gate keeps log sigmoid(s), fp32 [B,Hq,N,C],
- *             in it); SAS_GATE_SOFTMAX needs only SAS_OP_FWD / SAS_OP_BWD.
+ *             in it, the STE gate zero scores of that size and scratch
+ *             gradients); SAS_GATE_SOFTMAX needs only SAS_OP_FWD / SAS_OP_BWD.
  * Other arguments, layouts, ownership and errors: as for the calls above.
  */
 int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v,

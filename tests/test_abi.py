@@ -196,6 +196,7 @@ def test_gate_variant_host_checks():
     p = ctypes.c_void_p(1)
     args = (p, p, p, p, None, p, p, p, 1, 4, 2, 128, 128, 64, 0, 0.1, 1)
     assert L.sas_gated_attn_fwd_gate(*args, 7, None, 0, None) == sas.SAS_EINVAL
+    assert L.sas_gated_attn_fwd_gate(*args, 5, None, 0, None) == sas.SAS_EINVAL
     assert "gate" in sas._lib.sas_last_error().decode()
     assert L.sas_gated_attn_fwd_gate(*args[:8], 0, *args[9:], 1, None, 0, None) == sas.SAS_OK
     bargs = (p,) * 13 + (1, 4, 2, 128, 128, 64, 0, 0.1, 1)

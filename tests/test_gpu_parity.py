@@ -466,3 +466,46 @@ def test_gate_variant_parity(case, gate):
                         if 0 <= m < t // block:
                             sel[b, h, t, m] = True
         assert torch.count_nonzero(ds.cpu()[torch.tensor(~sel)]).item() == 0, "ds outside the selection"
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_ste_gate_parity(case):
+    """The hard gate with a straight-through estimator (SAS_GATE_STE) against
+    the oracle's reading: o and lse of plain block-sparse attention, lse_s =
+    LSE(s), the sparse dq, dk, dv, and ds over every history block."""
+    name, dts, B, Hq, Hkv, D, N, block, topk = case
+    dt = _dt(dts)
+    w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=13)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    scale = w.scale
+    G = Hq // Hkv
+    C = N // block
+    tol = tolerances(dt)
+    _, _, s32, idx = _oracle_selector(q, k, block, scale, topk, G)
+    scores = torch.tensor(s32).to(DEV)
+    idx_t = None if idx is None else torch.tensor(idx).to(DEV)
+    tk = -1 if topk is None else topk
+    sdt = sas.SAS_F32 if dt == torch.float32 else sas.SAS_BF16
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    lse_s = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, block, scale, sas.SAS_GATE_STE, wsf)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, lse_s, dq, dk, dv, ds, block, scale,
+                                sas.SAS_GATE_STE, wsb)
+    torch.cuda.synchronize()
+    r = orc.ste_gate_attention(to64(q), to64(k), to64(v), to64(do), s32.astype(np.float64), idx, block, scale)
+    o_ref, lse_ref, lses_ref, dq_r, dk_r, dv_r, ds_r = r
+    if tol["o_abs"] is not None:
+        max_abs(to64(o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(o), o_ref, tol["o_rel"], "o")
+    normwise(to64(lse), lse_ref, tol["lse"], "lse")
+    normwise(to64(lse_s), lses_ref, tol["lse"], "lse_s")
+    normwise(to64(dq), dq_r, tol["grad"], "dq")
+    normwise(to64(dk), dk_r, tol["grad"], "dk")
+    normwise(to64(dv), dv_r, tol["grad"], "dv")
+    normwise(to64(ds), ds_r, tol["ds"], "ds")

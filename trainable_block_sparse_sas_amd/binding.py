@@ -27,7 +27,7 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTOR_BWD = 1, 2, 3, 4, 5, 6
 SAS_OP_PAGED_DECODE = 7
 SAS_OP_FWD_GATE, SAS_OP_BWD_GATE = 8, 9
-SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER = 0, 1, 2, 3
+SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",

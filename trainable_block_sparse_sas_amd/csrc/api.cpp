@@ -2,6 +2,7 @@
 // kernel launchers.  Nothing here touches the GPU before every check passed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -100,9 +101,11 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
       if (topk < 0) return size_t(-1);
       return paged_ws(B, Hq, Hkv, n, D, block, topk).total;
     case SAS_OP_FWD_GATE:
-      return sas::fwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID);
+      return std::max(sas::fwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID),
+                      sas::fwd_gate_workspace(d, topk, bf16, SAS_GATE_STE));
     case SAS_OP_BWD_GATE:
-      return sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID);
+      return std::max(sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID),
+                      sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_STE));
     default:
       return size_t(-1);
   }
@@ -188,7 +191,7 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
-  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_OUTER) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
+  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_STE) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
   if (empty(B, Hq, N)) {
     g_error.clear();
     return SAS_OK;
@@ -213,12 +216,12 @@ static int attn_bwd(const char* what, const void* q, const void* k, const void* 
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
-  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_OUTER) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
+  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_STE) return fail(SAS_EINVAL, "%s: unknown gate %d", what, gate);
   if (empty(B, Hq, N)) {
     g_error.clear();
     return SAS_OK;
   }
-  const bool needs_lse_s = gate == SAS_GATE_SOFTMAX || gate == SAS_GATE_OUTER;
+  const bool needs_lse_s = gate == SAS_GATE_SOFTMAX || gate == SAS_GATE_OUTER || gate == SAS_GATE_STE;
   if (!q || !k || !v || !o || !dout || !scores || !lse || (!lse_s && needs_lse_s) || !dq ||
       !dk || !dv || !ds)
     return fail(SAS_EINVAL, "%s: every tensor pointer except idx (and lse_s for the sigmoid and raw gates) must be non-NULL",

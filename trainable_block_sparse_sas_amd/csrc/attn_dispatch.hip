@@ -35,6 +35,8 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                            int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s);
 
+hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s);
+
 bool bwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
@@ -86,6 +88,45 @@ hipError_t launch_gate_prep(const float* scores, float* sp, float* zero, const D
 
 size_t rows_of(const Dims& d) { return size_t(d.B) * d.Hq * d.N; }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t want = (n + 255) / 256;
+  SAS_LAUNCH("fill_zero", fill_zero_kernel, dim3(unsigned(want < 8192 ? want : 8192)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+// STE gate, last step: ds holds dh_m (every history block m < c) and becomes
+// g (dh - sum_m' g dh) with g = exp(s - LSE_s): the soft gate's Jacobian.
+// One wave per row.
+__global__ __launch_bounds__(256) void ste_ds_kernel(const float* __restrict__ scores,
+                                                     const float* __restrict__ lse_s, float* __restrict__ ds,
+                                                     int N, int C, int block, size_t rows) {
+  const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int t = int(row % N);
+  const int c = min(t / block, C);
+  const float ls = lse_s[row];
+  const float* srow = scores + row * C;
+  float* drow = ds + row * C;
+  float tot = 0.f;
+  for (int m = lane; m < c; m += 64) tot += exp_hw(srow[m] - ls) * drow[m];
+  for (int off = 32; off >= 1; off >>= 1) tot += shfl_xor(tot, off);
+  for (int m = lane; m < C; m += 64) drow[m] = m < c ? exp_hw(srow[m] - ls) * (drow[m] - tot) : 0.f;
+}
+
+// STE scratch: zero scores, then (backward) dq, dk, dv of the full-scope pass.
+size_t ste_zero_bytes(const Dims& d) { return align_up(rows_of(d) * d.C * sizeof(float)); }
+size_t ste_grad_bytes(const Dims& d, bool bf16) {
+  const size_t esz = bf16 ? 2 : 4;
+  return align_up(rows_of(d) * d.D * esz) + 2 * align_up(size_t(d.B) * d.Hkv * d.N * d.D * esz);
+}
+
 }  // namespace
 
 size_t fwd_workspace(const Dims& d, int topk, bool bf16) {
@@ -107,12 +148,16 @@ size_t bwd_workspace(const Dims& d, int topk, bool bf16) {
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
   const size_t base = fwd_workspace(d, topk, bf16);
   if (gate == kGateSoftmax || gate == kGateOuter) return base;
+  if (gate == kGateSte) return ste_zero_bytes(d) + fwd_gate_workspace(d, topk, bf16, kGateRaw);
   return align_up(base) + (gate == kGateSigmoid ? align_up(rows_of(d) * d.C * sizeof(float)) : 0);
 }
 
 size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
   const size_t base = bwd_workspace(d, topk, bf16);
   if (gate == kGateSoftmax || gate == kGateOuter) return base;
+  if (gate == kGateSte)
+    return ste_zero_bytes(d) + ste_grad_bytes(d, bf16) +
+           std::max(bwd_gate_workspace(d, topk, bf16, kGateRaw), bwd_gate_workspace(d, -1, bf16, kGateRaw));
   return align_up(base) + (gate == kGateSigmoid ? align_up(rows_of(d) * d.C * sizeof(float)) : 0) +
          align_up(rows_of(d) * sizeof(float));
 }
@@ -120,6 +165,17 @@ size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s) {
+  if (gate == kGateSte) {
+    // the hard gate: plain block-sparse attention (the raw gate on zero
+    // scores), then the real LSE_s for the backward's soft gate
+    float* zs = static_cast<float*>(ws);
+    hipError_t e = launch_fill_zero(zs, rows_of(d) * d.C, s);
+    if (e != hipSuccess) return e;
+    e = launch_fwd(q, k, v, zs, idx, o, lse, lse_s, d, topk, scale, bf16, kGateRaw,
+                   static_cast<char*>(ws) + ste_zero_bytes(d), s);
+    if (e != hipSuccess) return e;
+    return launch_lse_rows(scores, lse_s, d, s);
+  }
   const bool norm = gate == kGateSoftmax || gate == kGateOuter;
   const bool outer = gate == kGateOuter;
   if (!norm) {
@@ -140,6 +196,31 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                       float* ds, const Dims& d, int topk, float scale, bool bf16, int gate, void* ws,
                       hipStream_t s) {
+  if (gate == kGateSte) {
+    // dq, dk, dv of the hard gate's attention; then one full-scope pass on
+    // zero scores with the hard LSE_S, whose raw-gate ds is dh of every
+    // history block; then the soft gate's Jacobian
+    char* w = static_cast<char*>(ws);
+    float* zs = reinterpret_cast<float*>(w);
+    w += ste_zero_bytes(d);
+    const size_t esz = bf16 ? 2 : 4;
+    void* dq2 = w;
+    void* dk2 = w + align_up(rows_of(d) * d.D * esz);
+    void* dv2 = static_cast<char*>(dk2) + align_up(size_t(d.B) * d.Hkv * d.N * d.D * esz);
+    w += ste_grad_bytes(d, bf16);
+    hipError_t e = launch_fill_zero(zs, rows_of(d) * d.C, s);
+    if (e == hipSuccess)
+      e = launch_bwd(q, k, v, o, dout, zs, idx, lse, nullptr, dq, dk, dv, ds, d, topk, scale, bf16, kGateRaw, w,
+                     s);
+    if (e == hipSuccess)
+      e = launch_bwd(q, k, v, o, dout, zs, nullptr, lse, nullptr, dq2, dk2, dv2, ds, d, 0, scale, bf16, kGateRaw,
+                     w, s);
+    if (e != hipSuccess) return e;
+    const size_t rows = rows_of(d);
+    SAS_LAUNCH("ste_ds", ste_ds_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s, ds, d.N,
+               d.C, d.block, rows);
+    return hipGetLastError();
+  }
   if (gate == kGateSigmoid || gate == kGateRaw) {
     char* extra = static_cast<char*>(ws) + align_up(bwd_workspace(d, idx ? topk : -1, bf16));
     float* sp = nullptr;

@@ -489,6 +489,15 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, bool outer, hipStream
 // {1,2,4,8}, at least one complete block; sparse scope (key-major over the
 // selection lists) packs a token into 23 bits of a list entry and a block
 // into 16 bits of a work item.
+// LSE_s of every row on its own (any dtype: it reads only the fp32 scores).
+hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s) {
+  const size_t rows = size_t(d.B) * d.Hq * d.N;
+  if (rows == 0) return hipSuccess;
+  SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s, d.N,
+             d.C, d.block, rows);
+  return hipGetLastError();
+}
+
 bool fwd_mfma_supported(const Dims& d, int topk, bool sparse) {
   if (d.block != KT || (d.D != 64 && d.D != 128)) return false;
   if (d.C < 1) return false;

@@ -37,7 +37,7 @@ __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f
 __device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
 // Gate activations (the values of sas_gate).
-constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2, kGateOuter = 3;
+constexpr int kGateSoftmax = 0, kGateSigmoid = 1, kGateRaw = 2, kGateOuter = 3, kGateSte = 4;
 
 // ds of a history block from db (its dz sum when gated, else 0), x = s - LSE_s
 // (for the sigmoid gate s is the rewritten score log sigmoid(s) and LSE_s = 0,
