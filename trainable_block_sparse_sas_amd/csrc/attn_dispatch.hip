@@ -12,7 +12,12 @@
 // same pages) keeps LSE_s and the scores; its kernels take it as a template
 // argument: no bias on gated blocks, g scales P in P V, in dV and in dZ, and
 // the dK/dV kernels record g dg in dbeta's place, so the softmax gate's ds
-// epilogue applies.
+// epilogue applies.  The hard gate with a straight-through estimator (ranking
+// preservation, same section) is composed from the raw gate on zero scores:
+// its forward is plain block-sparse attention; its backward takes dq, dk, dv
+// from the sparse pass and, from a full-scope pass with the hard LSE_S, the
+// gate gradient dh of every history block, which ste_ds_kernel turns into
+// ds = g (dh - sum g dh) with g = softmax(s).
 #include <algorithm>
 
 #include "common.h"
