@@ -509,3 +509,34 @@ def test_ste_gate_parity(case):
     normwise(to64(dk), dk_r, tol["grad"], "dk")
     normwise(to64(dv), dv_r, tol["grad"], "dv")
     normwise(to64(ds), ds_r, tol["ds"], "ds")
+
+
+def test_full_star_by_composition():
+    """full* (the pages' full-scope simulation: noise added before Top-K) from
+    the existing calls: the caller adds its own noise to the scores given to
+    sas_topk_select and passes the clean scores to the attention.  The pages
+    give no noise distribution; seeded N(0, 1) noise stands in."""
+    B, Hq, Hkv, D, N, block, topk = 1, 8, 2, 128, 450, 64, 3
+    w = Workload("full-star", "train", "bf16", B, Hq, Hkv, D, N, block, topk, index=17)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    G = Hq // Hkv
+    tol = tolerances(torch.bfloat16)
+    _, _, s32, _ = _oracle_selector(q, k, block, w.scale, None, G)
+    noise = torch.randn(s32.shape, generator=torch.Generator().manual_seed(5)).numpy().astype(np.float32)
+    noisy = (s32 + noise).astype(np.float32)
+    pos = np.broadcast_to(np.arange(N), (B, N)) // block
+    idx = orc.topk_select(noisy, G, pos, topk)
+    step = TrainStep(B, Hq, Hkv, N, D, block, topk, torch.bfloat16)
+    sas.sas_topk_select(torch.tensor(noisy).to(DEV), step.idx, None, G, block)
+    torch.cuda.synchronize()
+    assert np.array_equal(step.idx.cpu().numpy(), idx), "topk of the noisy scores"
+    scores = torch.tensor(s32).to(DEV)
+    step.forward(q, k, v, scores, step.idx)
+    step.backward(q, k, v, do, scores, step.idx)
+    torch.cuda.synchronize()
+    s64 = s32.astype(np.float64)
+    o_ref, _, _ = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, w.scale)
+    max_abs(to64(step.o), o_ref, tol["o_abs"], "o")
+    dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, w.scale)
+    normwise(to64(step.ds), ds, tol["ds"], "ds")
+    normwise(to64(step.dq), dq, tol["grad"], "dq")
