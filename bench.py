@@ -287,11 +287,19 @@ def roofline(kernels, pairs, D, workload):
     ms = kernels[name][0]
     flops = KERNEL_FLOPS_PER_PAIR[name] * D * pairs
     ach = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": name, "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
-            "traffic": measured_traffic(name, workload),
-            "flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
-            "timing": "HIP events around each launch on its stream (library kernel timing)"}
+    traffic = measured_traffic(name, workload)
+    out = {"bound": "mfma", "kernel": name, "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
+           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+           "traffic": traffic,
+           "flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
+           "timing": "HIP events around each launch on its stream (library kernel timing)"}
+    if traffic:
+        # the measured HBM bytes over the same launch time, against 8 TB/s: the
+        # sparse-scope kernels are held by HBM rather than by the matrix cores
+        hbm = traffic / (ms * 1e-3) / 1e12
+        out["traffic_TBps"] = round(hbm, 3)
+        out["traffic_frac_of_hbm_peak"] = round(hbm * 1000.0 / PEAK_HBM_GBS, 4)
+    return out
 
 
 def bench_selector_bwd(torch, w, steps):
