@@ -15,7 +15,11 @@
  *     "New Approach", paper Eq. 4 and Eq. 9; log g = s - LSE(s) in review
  *     section "Why the Four Design Choices Matter");
  *   - inference: hard Top-K on the scores, no gate (review section "How It
- *     Works: A Concrete Walkthrough", Step 6, paper Alg. 2).
+ *     Works: A Concrete Walkthrough", Step 6, paper Alg. 2);
+ *   - the gate designs the pages compare SAS with (sigmoid gate, raw logit,
+ *     gate outside the softmax, hard gate with a straight-through estimator:
+ *     review section "Why the Four Design Choices Matter"; blog 方法核心,
+ *     ablation table): sas_gated_attn_fwd_gate / sas_gated_attn_bwd_gate.
  *
  * Conventions shared by every call
  * --------------------------------
