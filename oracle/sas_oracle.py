@@ -576,19 +576,32 @@ def sparse_decode(q, k_cache, v_cache, cache_len, idx, block, scale):
     return o, lse
 
 
-def decode_scores(q, kbar, cache_len, block, scale, group_sum):
-    """Decode-mode selector scores for one new token per sequence.
+def decode_scores(q, kbar, cache_len, L_max, block, scale, group_sum):
+    """Decode-mode selector scores for one new token per sequence
+    ([Review] "A Concrete Walkthrough", Step 6 / paper Alg. 2: score the
+    history blocks of the new token; [Review] "Background", paper Eq. 3).
 
-    q: [B, Hq, D]; kbar: [B, Hkv, C, D]; the query sits at len-1, so blocks
-    m < (len-1)//b compete (none for an idle sequence, len <= 0).  group_sum=False: float64 [B, Hq, C];
-    group_sum=True: float32 [B, Hkv, C], the fp32 sum (head-index order) of
-    each head's score rounded to fp32.  Non-candidates hold -inf.
+    q: [B, Hq, D]; kbar: [B, Hkv, C, D] with C = L_max // block; L_max is the
+    cache capacity.  Lengths are read exactly as in `sparse_decode`: a length
+    above L_max counts as L_max, and the query sits at position len-1, so the
+    blocks m < (len-1)//b compete; an idle sequence (len <= 0) has none.
+    group_sum=False: float64 [B, Hq, C]; group_sum=True: float32 [B, Hkv, C],
+    the fp32 sum (head-index order) of each head's score rounded to fp32.
+    Non-candidates hold -inf (the current block included).
     """
     B, Hq, D = q.shape
-    lens = np.minimum(np.asarray(cache_len), kbar.shape[2] * block + block - 1)
-    pos = np.maximum(lens - 1, 0).reshape(B, 1)
-    s = block_scores(np.asarray(q)[:, :, None, :], kbar, block, scale, pos)[:, :, 0, :]
+    lens = np.minimum(np.asarray(cache_len), int(L_max))  # as sparse_decode
+    pos = (lens - 1).reshape(B, 1)
+    s = block_scores(np.asarray(q)[:, :, None, :], kbar, block, scale, np.maximum(pos, 0))[:, :, 0, :]
+    s[(lens <= 0)] = NEG_INF  # idle: no candidates
     if not group_sum:
         return s
     G = Hq // kbar.shape[1]
     return group_sum_scores(s.astype(np.float32)[:, :, None, :], G)[:, :, 0, :]
+
+
+def decode_candidates(cache_len, L_max, block):
+    """Number of history blocks each decode query ranks: (min(len, L_max)-1)//b,
+    0 for an idle sequence (the readings of `sparse_decode`)."""
+    lens = np.minimum(np.asarray(cache_len), int(L_max))
+    return np.where(lens > 0, (np.maximum(lens, 1) - 1) // block, 0)

@@ -411,7 +411,7 @@ def test_decode_topk_at_least_history_is_dense():
     q, kc, vc = _decode_problem(2)
     lens = np.array([96, 61])
     block = 8
-    u = orc.decode_scores(q, orc.pool_block_keys(kc, block), lens, block, 0.3, True)
+    u = orc.decode_scores(q, orc.pool_block_keys(kc, block), lens, kc.shape[2], block, 0.3, True)
     c = (lens - 1) // block
     idx = orc.topk_select(u[:, :, None, :], 1, c[:, None], 12)[:, :, 0, :]
     a = orc.sparse_decode(q, kc, vc, lens, idx, block, 0.3)
@@ -442,8 +442,8 @@ def test_decode_scores_group_sum():
     block = 8
     kbar = orc.pool_block_keys(kc, block)
     lens = np.array([64, 30])
-    s = orc.decode_scores(q, kbar, lens, block, 0.5, False)
-    u = orc.decode_scores(q, kbar, lens, block, 0.5, True)
+    s = orc.decode_scores(q, kbar, lens, 64, block, 0.5, False)
+    u = orc.decode_scores(q, kbar, lens, 64, block, 0.5, True)
     for b in range(2):
         c = (lens[b] - 1) // block
         for g in range(2):
@@ -487,8 +487,42 @@ def test_decode_idle_and_overlong_sequences():
     np.testing.assert_array_equal(o[1], o2[1])
     od, _ = orc.sparse_decode(q, kc, vc, np.array([-3, 64]), None, 16, 0.3)
     assert np.all(od[0] == 0)
-    u = orc.decode_scores(q, orc.pool_block_keys(kc, 16), np.array([0, 64]), 16, 0.3, True)
+    u = orc.decode_scores(q, orc.pool_block_keys(kc, 16), np.array([0, 64]), 64, 16, 0.3, True)
     assert np.all(u[0] == -np.inf)
+
+
+@pytest.mark.parametrize("L_max,block", [(64, 16), (70, 16), (48, 16), (100, 32)])
+def test_decode_scores_over_long_lengths(L_max, block):
+    """Lengths at, just above and far above the capacity: the candidates are the
+    complete blocks before the block holding position min(len, L_max) - 1, found
+    here by searching for the block whose token range holds that position (not
+    by division), so the current block is -inf however long the length is; the
+    same reading as sparse_decode, whose output for an over-long length equals
+    the one for L_max."""
+    r = rng(17)
+    B, Hq, Hkv, D = 1, 2, 1, 8
+    C = L_max // block
+    q = r.standard_normal((B, Hq, D))
+    kc = r.standard_normal((B, Hkv, L_max, D))
+    vc = r.standard_normal((B, Hkv, L_max, D))
+    kbar = orc.pool_block_keys(kc, block)
+    ref_s = orc.decode_scores(q, kbar, np.array([L_max]), L_max, block, 0.3, False)
+    for n in (L_max, L_max + 1, L_max + block, 10 * L_max):
+        s = orc.decode_scores(q, kbar, np.array([n]), L_max, block, 0.3, False)
+        p = min(n, L_max) - 1
+        cur = next(m for m in range(C + 1) if m * block <= p < (m + 1) * block)
+        for m in range(C):
+            assert np.all(np.isfinite(s[0, :, m]) == (m < cur)), (n, m, cur)
+        np.testing.assert_array_equal(s, ref_s)
+        u = orc.decode_scores(q, kbar, np.array([n]), L_max, block, 0.3, True)
+        assert np.all(np.isfinite(u[0, 0]) == (np.arange(C) < cur))
+        assert orc.decode_candidates(np.array([n]), L_max, block)[0] == cur
+        # full selection over the candidates = dense decode, also over-long
+        idx = np.arange(cur, dtype=np.int32).reshape(1, 1, cur)
+        o, lse = orc.sparse_decode(q, kc, vc, np.array([n]), idx, block, 0.3)
+        od, lsed = orc.sparse_decode(q, kc, vc, np.array([L_max]), None, block, 0.3)
+        np.testing.assert_allclose(o, od, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, lsed, rtol=1e-12)
 
 
 # ---------------------------------------------------------------------------
