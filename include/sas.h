@@ -142,11 +142,18 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
  *                index (-0.0 equals +0.0, NaN ranks as -inf), remaining slots
  *                -1.  Bit-exact and deterministic.
  * cache_len:     NULL: row t has c = t / block candidates (training, Nq rows);
- *                device int32 [B]: decode, Nq must be 1, c = (len-1)/block.
- *                Candidates never exceed C.
- * workspace:     needed only for decode rows (see sas_workspace_bytes).
+ *                device int32 [B]: decode, Nq must be 1, c = min((len-1)/block, C)
+ *                (0 for len <= 0).  Top-K does not know the cache capacity
+ *                L_max: for every length up to L_max this is the history of
+ *                sas_score_blocks and sas_sparse_decode, but a length above
+ *                L_max with L_max a multiple of block makes block C-1 (the
+ *                current block there, scored -inf) a candidate.  Callers that
+ *                may pass such lengths clamp them to L_max first;
+ *                sas_paged_decode does so itself.
+ * workspace:     unused (no scratch is needed); may be NULL with size 0.
+ *                sas_workspace_bytes(SAS_OP_TOPK, ...) returns 0.
  * Errors: SAS_EINVAL (pointers, sizes, topk < 0, heads_per_row < 1);
- *         SAS_EUNSUPPORTED for topk > 256 or C > 16384; SAS_EWORKSPACE.
+ *         SAS_EUNSUPPORTED for topk > 256 or C > 16384.
  */
 int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len,
                     int B, int Hkv, int heads_per_row, int Nq, int C, int block,
@@ -293,9 +300,13 @@ int sas_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages,
  *             block counts as that; <= 0 is an idle sequence).
  * topk:       0 .. 256 blocks (0: the current block only).
  * o:          [B,Hq,D] output; lse optional fp32 [B,Hq] output.
- * idx_out:    optional int32 [B,Hkv,topk] output, the selected blocks.
+ * idx_out:    optional int32 [B,Hkv,topk] output, the selected blocks
+ *             (history blocks only: lengths are clamped to max_blocks * block).
  * workspace:  sas_workspace_bytes(SAS_OP_PAGED_DECODE, B, Hq, Hkv,
- *             max_blocks * block, D, block, topk, dtype) bytes.
+ *             max_blocks * block, D, block, topk, dtype) bytes.  After the
+ *             call its first B*Hkv*max_blocks floats hold the group-summed
+ *             scores [B,Hkv,max_blocks] the selection was made on (-inf for
+ *             non-candidates), so a caller can check or reuse them.
  * bf16 only.  Errors: SAS_EINVAL, SAS_EUNSUPPORTED (fp32, D outside {64,
  *         128}, more than 16 query heads per KV head, topk > 256,
  *         max_blocks > 16384), SAS_EWORKSPACE.

@@ -43,6 +43,50 @@ def _sample_rows(N, block, n=24, seed=0):
     return np.unique(np.concatenate([fixed, r.integers(0, N, size=n)]))
 
 
+def _rowwise(got, ref, tol, what):
+    """Each row on its own: max|got - ref| <= tol * max|ref| over that row, so a
+    small-norm row (a long softmax average) is held to its own scale."""
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    err = np.max(np.abs(got - ref), axis=1)
+    scale = np.maximum(np.max(np.abs(ref), axis=1), 1e-30)
+    bad = err > tol * scale
+    assert not bad.any(), f"{what}: {bad.sum()} rows off, worst {np.max(err / scale):.3e}"
+
+
+def _ds_invariants(step, scores, idx, G, w):
+    """Invariants of the gate gradient on the GPU's own outputs, over every row
+    of every head ([Blog] 方法核心, Fig. 4 and the inner-gate gradient; [Review]
+    "Why the Four Design Choices Matter", Eq. 5): ds = dbeta - g sum(dbeta)
+    with sum(g) = 1 gives sum_m ds = 0 over the history; at sparse scope an
+    unselected block has dbeta = 0, so ds/g is one value per row there."""
+    ds = step.ds[0]  # [Hq, N, C] fp32 on the GPU
+    C, N = w.C, w.N
+    hist = (torch.arange(C, device=DEV)[None, :] < (torch.arange(N, device=DEV) // w.block)[:, None])
+    for h in range(w.Hq):
+        d = ds[h]
+        assert torch.all(d[~hist] == 0), f"ds outside the history, head {h}"
+        tot = d.sum(dim=1, dtype=torch.float64)
+        mag = d.abs().sum(dim=1, dtype=torch.float64)
+        bad = tot.abs() > 1e-4 * mag + 1e-30
+        assert not bool(bad.any()), f"sum_m ds != 0 on {int(bad.sum())} rows of head {h}"
+    if idx is None:
+        return
+    rows = _sample_rows(N, w.block, n=400, seed=11)
+    rows = rows[rows // w.block >= w.topk + 2]  # rows with unselected history
+    s = scores[0][:, rows].double().cpu().numpy()
+    lse_s = step.lse_s[0][:, rows].double().cpu().numpy()
+    dsr = ds[:, rows].double().cpu().numpy()
+    for h in range(w.Hq):
+        for i, t in enumerate(rows):
+            c = t // w.block
+            uns = np.setdiff1d(np.arange(c), idx[0, h // G, t])
+            g = np.exp(s[h, i, uns] - lse_s[h, i])
+            keep = g > 1e-30
+            r = dsr[h, i, uns][keep] / g[keep]
+            assert np.max(np.abs(r - r.mean())) <= 1e-4 * max(abs(r.mean()), 1e-30) + 1e-12, (h, t)
+
+
 @pytest.mark.parametrize("wi", [1, 2], ids=["train-8k-full", "train-32k-sparse"])
 def test_training_fullsize(wi):
     w = WORKLOADS[wi]
@@ -87,8 +131,10 @@ def test_training_fullsize(wi):
     v64, do64, s64 = to64(v), to64(do), s32.astype(np.float64)
     o_ref, lse_ref, lses_ref = orc.gated_attention_forward(q64, k64, v64, s64, idx, w.block, w.scale, rows=rows)
     max_abs(to64(step.o[:, :, rows]), o_ref, 2e-2, "o")
+    _rowwise(to64(step.o[:, :, rows]), o_ref, 2e-2, "o per row")
     normwise(to64(step.lse[:, :, rows]), lse_ref, 1e-4, "lse")
     normwise(to64(step.lse_s[:, :, rows]), lses_ref, 1e-4, "lse_s")
+    _ds_invariants(step, scores, idx, G, w)
     for h in (0, w.Hq // 2 + 1, w.Hq - 1):
         dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, h, rows)
         normwise(to64(step.dq[0, h, rows]), dq_r, 2e-2, f"dq h{h}")
@@ -222,7 +268,7 @@ def test_decode_fullsize(wi):
             kbar[b, g] = orc.pool_block_keys(to64(kc[b:b + 1, g:g + 1]), w.block)[0, 0]
     kbar_r = to64(torch.tensor(kbar).to(dt))
     kbar_close(to64(step.kbar), kbar_r)
-    u_ref = orc.decode_scores(q64, kbar_r, lens_np, w.block, w.scale, True)
+    u_ref = orc.decode_scores(q64, kbar_r, lens_np, w.N, w.block, w.scale, True)
     sas.sas_score_blocks(q, None, torch.tensor(kbar_r).to(dt).to(DEV), step.u, lens, w.block, w.scale,
                          group_sum=True, L=w.N)
     torch.cuda.synchronize()

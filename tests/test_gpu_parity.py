@@ -175,10 +175,11 @@ DECODE_CASES = [
 def test_decode_parity(case):
     name, dts, Hq, Hkv, D, L, block, topk = case
     dt = _dt(dts)
-    B = 4
+    B = 5
     w = Workload(name, "decode", dts, B, Hq, Hkv, D, L, block, topk, index=9)
     q, kc, vc, _ = decode_inputs(w, device="cpu")
-    lens = torch.tensor([L, L - 37, 40, 0], dtype=torch.int32)
+    # full, ragged, short, idle, and a length above the capacity (counts as L)
+    lens = torch.tensor([L, L - 37, 40, 0, 10 * L + 3], dtype=torch.int32)
     q, kc, vc, lens_d = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
     scale = w.scale
     G = Hq // Hkv
@@ -197,20 +198,24 @@ def test_decode_parity(case):
     kb = torch.tensor(kbar_r).to(dt).to(DEV)
     sas.sas_score_blocks(q, None, kb, step.u, lens_d, block, scale, group_sum=True, L=L)
     torch.cuda.synchronize()
-    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, True)
+    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), L, block, scale, True)
     normwise(to64(step.u), u_ref.astype(np.float64), 1e-5, "u")
+    # -inf in exactly the same places: the current block and beyond, idle rows
+    assert np.array_equal(np.isneginf(step.u.cpu().numpy()), np.isneginf(u_ref))
     # Per-head decode scores.
     s_h = torch.empty((B, Hq, L // block), dtype=torch.float32, device=DEV)
     sas.sas_score_blocks(q, None, kb, s_h, lens_d, block, scale, group_sum=False, L=L)
     torch.cuda.synchronize()
-    s_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, False)
+    s_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), L, block, scale, False)
     normwise(to64(s_h), s_ref, 1e-5, "s")
-    # Top-K on the oracle's group sums: bit-exact.
-    c = np.maximum(lens.numpy() - 1, 0) // block
+    assert np.array_equal(np.isneginf(s_h.cpu().numpy()), np.isneginf(s_ref))
+    # Top-K on the oracle's group sums: bit-exact.  Top-K does not know the
+    # capacity, so (as its header asks) the lengths it gets are clamped to L.
+    c = orc.decode_candidates(lens.numpy(), L, block)
     idx_ref = None
     if topk is not None:
         idx_ref = orc.topk_select(u_ref[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
-        sas.sas_topk_select(torch.tensor(u_ref).to(DEV), step.idx, lens_d, 1, block)
+        sas.sas_topk_select(torch.tensor(u_ref).to(DEV), step.idx, torch.clamp(lens, max=L).to(DEV), 1, block)
         torch.cuda.synchronize()
         assert np.array_equal(step.idx.cpu().numpy(), idx_ref)
     # Attention over the selected blocks (or all blocks).
@@ -339,11 +344,12 @@ PAGED_CASES = [
 def test_paged_decode_parity(case):
     name, Hq, Hkv, D, maxb, block, topk = case
     dt = torch.bfloat16
-    B = 4
+    B = 5
     L = maxb * block
     w = Workload(name, "decode", "bf16", B, Hq, Hkv, D, L, block, topk, index=11)
     q, kc, vc, _ = decode_inputs(w, device="cpu")
-    lens = torch.tensor([L, L - 37, block + 3, 0], dtype=torch.int32)
+    # full, ragged, short, idle, over-long (counts as L: block maxb-1 is current)
+    lens = torch.tensor([L, L - 37, block + 3, 0, L + 3 * block + 5], dtype=torch.int32)
     G = Hq // Hkv
     # pages in a shuffled pool with spare pages: block m of sequence b -> page table[b, m]
     n_pages = B * maxb + 5
@@ -375,19 +381,21 @@ def test_paged_decode_parity(case):
     sas.sas_paged_decode(q.to(DEV), kpd, vpd, kbp_r.to(DEV), tbd, lens.to(DEV), topk, o, lse, block, scale,
                          idx_out=idx if topk > 0 else None, workspace=ws)
     torch.cuda.synchronize()
-    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), block, scale, True)
-    c = np.maximum(lens.numpy() - 1, 0) // block
+    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), L, block, scale, True)
+    c = orc.decode_candidates(lens.numpy(), L, block)
+    # The workspace starts with the group-summed scores the selection was made
+    # on: they match the oracle's, and Top-K on them is bit-exact.
+    u_gpu = ws[: B * Hkv * maxb * 4].view(torch.float32).reshape(B, Hkv, maxb).cpu().numpy()
+    normwise(u_gpu.astype(np.float64), u_ref.astype(np.float64), 1e-5, "u")
+    assert np.array_equal(np.isneginf(u_gpu), np.isneginf(u_ref))
     idx_ref = np.zeros((B, Hkv, 0), dtype=np.int64)  # topk 0: the current block only
     active = lens.numpy() > 0
     if topk > 0:
-        idx_ref = orc.topk_select(u_ref[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
-        # rows whose K-th and (K+1)-th scores are a near-tie may legitimately differ
-        srt = -np.sort(-np.where(np.isfinite(u_ref), u_ref, -np.inf), axis=-1)
-        gap = np.abs(srt[..., topk - 1] - srt[..., topk]) if u_ref.shape[-1] > topk else np.full(srt.shape[:2], np.inf)
-        firm = np.all((gap > 1e-4 * np.abs(srt[..., topk - 1]) + 1e-6) | (c[:, None] <= topk), axis=1)
+        idx_ref = orc.topk_select(u_gpu[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
         got = idx.cpu().numpy()
-        assert np.array_equal(got[firm], idx_ref[firm]), "paged Top-K"
-        active = active & firm
+        assert np.array_equal(got, idx_ref), "paged Top-K"
+        # history blocks only, also for the over-long sequence
+        assert np.all((got == -1) | ((got >= 0) & (got < c[:, None, None])))
     o_ref, lse_ref = orc.sparse_decode(to64(q), to64(kc), to64(vc), lens.numpy(), idx_ref, block, scale)
     max_abs(to64(o)[active], o_ref[active], 2e-2, "o")
     normwise(to64(lse)[active], lse_ref[active], 1e-4, "lse")

@@ -151,7 +151,9 @@ def workspace(op, B, Hq, Hkv, n_or_lmax, D, block, topk, dtype, device="cuda"):
 def sas_score_blocks(q, k, kbar, scores, cache_len, block, scale, group_sum=False, L=None,
                      stream=None):
     """Training: q [B,Hq,N,D], k [B,Hkv,N,D] or None, kbar [B,Hkv,C,D], scores fp32.
-    Decode (cache_len given): q [B,Hq,D], k the cache or None, L = cache capacity."""
+    Decode (cache_len given): q [B,Hq,D], k the cache or None, L = cache capacity
+    (taken from k when given; required otherwise, since the pooled keys alone
+    do not fix a capacity that is not a multiple of the block)."""
     B, Hq, D = q.shape[0], q.shape[1], q.shape[-1]
     Hkv = kbar.shape[1]
     if cache_len is None:
@@ -160,7 +162,9 @@ def sas_score_blocks(q, k, kbar, scores, cache_len, block, scale, group_sum=Fals
     else:
         Nq = 1
         if L is None:
-            L = k.shape[2] if k is not None else kbar.shape[2] * block
+            if k is None:
+                raise ValueError("sas_score_blocks: decode mode without k needs the cache capacity L")
+            L = k.shape[2]
     _check(_lib.sas_score_blocks(_p(q), _p(k), _p(kbar), _p(scores), _p(cache_len), B, Hq, Hkv,
                                  Nq, L, D, block, scale, int(bool(group_sum)), _dt(q),
                                  _stream(stream)))

@@ -152,7 +152,7 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
 int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
                     int heads_per_row, int Nq, int C, int block, int topk, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  (void)workspace;
+  (void)workspace;  // Top-K needs no scratch; the arguments are kept for ABI stability
   (void)workspace_bytes;
   if (B < 0 || Hkv < 1 || Nq < 0 || C < 0)
     return fail(SAS_EINVAL, "sas_topk_select: invalid sizes (B=%d Hkv=%d Nq=%d C=%d)", B, Hkv, Nq, C);
@@ -347,7 +347,7 @@ int sas_paged_decode(const void* q, const void* k_pages, const void* v_pages, co
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + W.idx);
   hipError_t e = sas::launch_score_decode(q, kbar_pages, scores, cache_len, B, Hq, Hkv, L_max, D, block,
                                           max_blocks, scale, true, true, s, block_table);
-  if (e == hipSuccess && topk > 0) e = sas::launch_topk(scores, idx, cache_len, B, Hkv, 1, 1, max_blocks, block, topk, s);
+  if (e == hipSuccess && topk > 0) e = sas::launch_topk(scores, idx, cache_len, B, Hkv, 1, 1, max_blocks, block, topk, s, L_max);
   if (e == hipSuccess)
     e = sas::launch_decode(q, k_pages, v_pages, cache_len, idx, o, lse, B, Hq, Hkv, L_max, D, block, topk, scale,
                            true, w + W.part, s, block_table);

@@ -60,8 +60,10 @@ hipError_t launch_pool_pages(const void* k_pages, void* kbar_pages, const int32_
                              int Hkv, int D, int block, bool bf16, hipStream_t s);
 
 // ---- Top-K ------------------------------------------------------------------------
+// Decode rows clamp cache_len to len_cap (the cache capacity, when known).
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B,
-                       int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s);
+                       int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s,
+                       int len_cap = 0x7fffffff);
 
 // ---- selection lists (key-major sparse kernels) ---------------------------------
 // Per KV head, the tokens selecting each history block, ascending; built from

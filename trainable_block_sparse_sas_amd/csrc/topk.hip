@@ -20,6 +20,23 @@ namespace {
 
 constexpr int kMaxTopk = 256;
 
+// Candidates of a row: the history blocks m < c.  Training rows: c = t / block.
+// Decode rows: the query sits at len - 1 with len clamped to len_cap (the
+// cache capacity when the caller knows it), c = (len - 1) / block, none for an
+// idle sequence.  Never more than C.
+__device__ __forceinline__ int row_candidates(const int32_t* __restrict__ cache_len, int b, long t,
+                                              int block, int C, int len_cap) {
+  int c;
+  if (cache_len) {
+    int len = cache_len[b];
+    len = len < len_cap ? len : len_cap;
+    c = len > 0 ? (len - 1) / block : 0;
+  } else {
+    c = int(t / block);
+  }
+  return c < C ? c : C;
+}
+
 // Group score of each of the lane's PER candidates m[i] (where ok[i]): the sum
 // of the row's hpr head scores, hstride floats apart, added in head order.
 // Every load of a chunk of HC heads is issued before the first add, so a row
@@ -51,7 +68,7 @@ template <int WPR, int PER>
 __global__ __launch_bounds__(256 * (WPR > 4 ? 4 : 1)) void topk_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ idx,
     const int32_t* __restrict__ cache_len, int Hkv, int hpr, int Nq, int C, int block, int topk,
-    long total_rows) {
+    int len_cap, long total_rows) {
   constexpr int WAVES = (WPR > 4 ? 16 : 4);
   constexpr int ROWS = WAVES / WPR;  // rows per workgroup
   __shared__ uint32_t hist[ROWS][256];
@@ -73,13 +90,7 @@ __global__ __launch_bounds__(256 * (WPR > 4 ? 4 : 1)) void topk_kernel(
     t = row % Nq;
     bg = row / Nq;
     const int b = int(bg / Hkv);
-    if (cache_len) {
-      int len = cache_len[b];
-      c = len > 0 ? (len - 1) / block : 0;
-    } else {
-      c = int(t / block);
-    }
-    c = c < C ? c : C;
+    c = row_candidates(cache_len, b, t, block, C, len_cap);
     K = topk < c ? topk : c;
   }
   // Load the group-summed scores as order-preserving keys.
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
                                                          int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ cache_len,
                                                          int Hkv, int hpr, int Nq, int C, int block,
-                                                         int topk) {
+                                                         int topk, int len_cap) {
   __shared__ uint32_t hist[16][256];
   __shared__ uint32_t cand_hi[16][kMaxTopk];
   __shared__ uint32_t cand_lo[16][kMaxTopk];
@@ -312,14 +323,7 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
   const long row = blockIdx.x;
   const long t = row % Nq, bg = row / Nq;
   const int b = int(bg / Hkv), g = int(bg % Hkv);
-  int c;
-  if (cache_len) {
-    const int len = cache_len[b];
-    c = len > 0 ? (len - 1) / block : 0;
-  } else {
-    c = int(t / block);
-  }
-  c = c < C ? c : C;
+  const int c = row_candidates(cache_len, b, t, block, C, len_cap);
   const int K = topk < c ? topk : c;
   const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
 
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(64 * W) void topk_runs_kernel(const float* __restri
                                                          int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ cache_len,
                                                          int Hkv, int hpr, int Nq, int C, int block,
-                                                         int topk) {
+                                                         int topk, int len_cap) {
   constexpr int E = PER < KP ? PER : KP;  // keys per lane in a run
   constexpr int R = KP / E;               // lanes per run
   constexpr int E1 = KP <= 8 ? 1 : KP / 8;  // filter: 32-bit runs of KP as E1 x R1
@@ -550,14 +554,7 @@ __global__ __launch_bounds__(64 * W) void topk_runs_kernel(const float* __restri
                    u);
   }
   if (threadIdx.x < 64) rank[threadIdx.x] = 0;
-  int c;
-  if (cache_len) {
-    const int len = cache_len[b];
-    c = len > 0 ? (len - 1) / block : 0;
-  } else {
-    c = int(t / block);
-  }
-  c = c < C ? c : C;
+  const int c = row_candidates(cache_len, b, t, block, C, len_cap);
   const int K = topk < c ? topk : c;
   int32_t* out = idx + size_t(row) * topk;
   if (K == 0) {
@@ -664,7 +661,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
                                                         int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ cache_len, int Hkv,
                                                         int hpr, int Nq, int C, int block, int topk,
-                                                        long total_rows) {
+                                                        int len_cap, long total_rows) {
   __shared__ uint32_t hist[4][256];
   __shared__ uint64_t surv[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -672,14 +669,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   if (row >= total_rows) return;  // waves are independent: no workgroup barrier below
   const long t = row % Nq, bg = row / Nq;
   const int b = int(bg / Hkv), g = int(bg % Hkv);
-  int c;
-  if (cache_len) {
-    const int len = cache_len[b];
-    c = len > 0 ? (len - 1) / block : 0;
-  } else {
-    c = int(t / block);
-  }
-  c = c < C ? c : C;
+  const int c = row_candidates(cache_len, b, t, block, C, len_cap);
   const int K = topk < c ? topk : c;
   int32_t* out = idx + size_t(row) * topk;
   if (K == 0) {
@@ -742,32 +732,32 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
-                       int hpr, int Nq, int C, int block, int topk, hipStream_t s) {
+                       int hpr, int Nq, int C, int block, int topk, hipStream_t s, int len_cap) {
   const long rows = long(B) * Hkv * Nq;
   if (rows == 0 || topk == 0) return hipSuccess;
   if (C <= 1024 && topk <= 64) {
     const dim3 grid((rows + 3) / 4);
     if (C <= 256)
       SAS_LAUNCH("topk", (topk_wave_kernel<4>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, rows);
+                 block, topk, len_cap, rows);
     else if (C <= 512)
       SAS_LAUNCH("topk", (topk_wave_kernel<8>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, rows);
+                 block, topk, len_cap, rows);
     else
       SAS_LAUNCH("topk", (topk_wave_kernel<16>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, rows);
+                 block, topk, len_cap, rows);
   } else if (C <= 256) {
     SAS_LAUNCH("topk", (topk_kernel<1, 4>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
-                       cache_len, Hkv, hpr, Nq, C, block, topk, rows);
+                       cache_len, Hkv, hpr, Nq, C, block, topk, len_cap, rows);
   } else if (C <= 1024) {
     SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
-                       cache_len, Hkv, hpr, Nq, C, block, topk, rows);
+                       cache_len, Hkv, hpr, Nq, C, block, topk, len_cap, rows);
   } else if (topk <= 64 && C <= 16384) {
     // 8 waves up to 8192 candidates (16 above), PER candidates per lane: just
     // enough for C; run length: the power of two at or above K (at least 8)
 #define SAS_TOPK_RUNS(PER, KP, W)                                                                     \
   SAS_LAUNCH("topk_runs", (topk_runs_kernel<PER, KP, W>), dim3(rows), dim3(64 * W), 0, s, scores, idx, \
-             cache_len, Hkv, hpr, Nq, C, block, topk)
+             cache_len, Hkv, hpr, Nq, C, block, topk, len_cap)
 #define SAS_TOPK_RUNS_KP(PER, W)                        \
   if (topk <= 8) SAS_TOPK_RUNS(PER, 8, W);               \
   else if (topk <= 16) SAS_TOPK_RUNS(PER, 16, W);        \
@@ -784,7 +774,7 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
     // survivors per lane in the second stage: 16 K / 64
 #define SAS_TOPK_LONG(PER, PER2)                                                                          \
   SAS_LAUNCH("topk_long", (topk_long_kernel<PER, PER2>), dim3(rows), dim3(1024), 0, s, scores, idx, cache_len, \
-             Hkv, hpr, Nq, C, block, topk)
+             Hkv, hpr, Nq, C, block, topk, len_cap)
     const int per = C <= 2048 ? 2 : C <= 4096 ? 4 : C <= 8192 ? 8 : 16;
     const int per2 = topk <= 16 ? 4 : topk <= 32 ? 8 : 64;
     if (per == 2 && per2 == 4) SAS_TOPK_LONG(2, 4);
