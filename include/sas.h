@@ -273,6 +273,33 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sas_sparse_decode_noalloc -- sas_sparse_decode without a workspace argument,
+ *   for callers that cannot allocate device memory (code under HIP graph
+ *   capture, tight serving loops, harnesses that forbid allocation).  Same
+ *   arguments, layouts, results and errors as sas_sparse_decode, minus the
+ *   workspace; the same kernels run.
+ * Scratch:    the attention partials go to a fixed scratch array of 8 MiB in
+ *             the library, one per GPU, reserved when the library's code is
+ *             loaded on that GPU and held until the process ends.  The call
+ *             allocates nothing (no hipMalloc, hipFree or allocating library
+ *             routine); its first call on a device looks up that device's
+ *             array address once.  Every call on one GPU shares that GPU's
+ *             array, so calls that overlap in time on one GPU (concurrent
+ *             streams, or threads) race and must be serialised by the caller.
+ *             No part of the array needs clearing between calls.
+ * Errors:     as sas_sparse_decode; SAS_EUNSUPPORTED (with the byte count in
+ *             sas_last_error) when the sizes need more scratch than the
+ *             8 MiB array (sas_workspace_bytes(SAS_OP_DECODE, ...) > 8 MiB;
+ *             e.g. dense decode far beyond 512K tokens per sequence),
+ *             SAS_EHIP if the array's address cannot be obtained.
+ */
+int sas_sparse_decode_noalloc(const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_len,
+                              const int32_t* idx, void* o, float* lse, int B,
+                              int Hq, int Hkv, int L_max, int D, int block,
+                              int topk, float scale, int dtype, void* stream);
+
+/*
  * Paged KV cache.  A page holds one block (`block` tokens) of one sequence for
  * every KV head: k_pages, v_pages [num_pages, Hkv, block, D], so each block
  * of each head stays one contiguous run.  block_table int32 [B, max_blocks]

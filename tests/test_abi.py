@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
                           "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
-                          "sas_paged_decode", "sas_workspace_bytes",
+                          "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
     for n in names:
@@ -223,3 +223,26 @@ def test_gate_variant_host_checks():
     small = sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 4, 2, 128, 128, 64, -1, 1)
     assert small < sas.sas_workspace_bytes(sas.SAS_OP_FWD_GATE, 1, 4, 2, 128, 128, 64, -1, 1)
     assert L.sas_gated_attn_fwd_gate(*args, 1, p, small, None) == sas.SAS_EWORKSPACE
+
+
+def test_noalloc_decode_validation_on_the_host():
+    """The allocation-free decode validates like sas_sparse_decode and refuses
+    sizes whose partials exceed its fixed 8 MiB scratch, all before any HIP
+    call (dummy pointers are never dereferenced)."""
+    vp = ctypes.c_void_p
+    d = vp(256)
+    f = ctypes.c_float
+    # dense decode, 16 query heads on one KV head, 1M tokens: more than 8 MiB of partials
+    need = sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 1, 16, 1, 1 << 20, 128, 64, -1, sas.SAS_BF16)
+    assert need > (8 << 20)
+    assert L.sas_sparse_decode_noalloc(d, d, d, d, N, d, N, 1, 16, 1, 1 << 20, 128, 64, 0, f(0.1),
+                                       sas.SAS_BF16, N) == sas.SAS_EUNSUPPORTED
+    assert "scratch" in sas.sas_last_error()
+    assert L.sas_sparse_decode_noalloc(N, d, d, d, N, d, N, 1, 4, 2, 1024, 128, 64, 0, f(0.1),
+                                       sas.SAS_BF16, N) == sas.SAS_EINVAL
+    assert L.sas_sparse_decode_noalloc(d, d, d, d, d, d, N, 1, 4, 2, 1024, 128, 64, -1, f(0.1),
+                                       sas.SAS_BF16, N) == sas.SAS_EINVAL
+    assert L.sas_sparse_decode_noalloc(d, d, d, d, N, d, N, 1, 4, 2, 1024, 96, 64, 0, f(0.1),
+                                       sas.SAS_BF16, N) == sas.SAS_EUNSUPPORTED
+    assert L.sas_sparse_decode_noalloc(d, d, d, d, N, d, N, 0, 4, 2, 1024, 128, 64, 0, f(0.1),
+                                       sas.SAS_BF16, N) == sas.SAS_OK

@@ -31,7 +31,7 @@ SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE =
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
-            "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_sparse_decode_noalloc", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -42,6 +42,7 @@ _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _v
 _lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_sparse_decode_noalloc.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
 _lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_pool_pages.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
 _lib.sas_paged_decode.argtypes = [_vp] * 5 + [_i, _vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
@@ -55,7 +56,8 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
-              "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode"):
+              "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
+              "sas_sparse_decode_noalloc"):
     getattr(_lib, _name).restype = _i
 
 
@@ -239,6 +241,16 @@ def sas_sparse_decode(q, k_cache, v_cache, cache_len, idx, o, lse, block, scale,
     _check(_lib.sas_sparse_decode(_p(q), _p(k_cache), _p(v_cache), _p(cache_len), _idx_ptr(idx), _p(o),
                                   _p(lse), B, Hq, Hkv, L, D, block, topk, scale, _dt(q),
                                   _p(workspace), wsb, _stream(stream)))
+
+
+def sas_sparse_decode_noalloc(q, k_cache, v_cache, cache_len, idx, o, lse, block, scale, stream=None):
+    """sas_sparse_decode with the library's fixed per-GPU scratch instead of a workspace."""
+    B, Hq, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    topk = idx.shape[-1] if idx is not None else 0
+    _check(_lib.sas_sparse_decode_noalloc(_p(q), _p(k_cache), _p(v_cache), _p(cache_len), _idx_ptr(idx), _p(o),
+                                          _p(lse), B, Hq, Hkv, L, D, block, topk, scale, _dt(q),
+                                          _stream(stream)))
 
 
 def sas_selector_bwd(q, kbar, ds, dq, dk, block, scale, dkbar=None, accumulate=False, workspace=None,

@@ -273,23 +273,37 @@ int sas_gated_attn_bwd_gate(const void* q, const void* k, const void* v, const v
                   Hq, Hkv, N, D, block, topk, scale, dtype, gate, workspace, workspace_bytes, stream);
 }
 
+// Checks shared by the two sparse-decode calls.  Returns SAS_OK with *noop set
+// when there is nothing to do.
+static int check_decode(const char* what, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_len, const int32_t* idx, const void* o, int B, int Hq,
+                        int Hkv, int L_max, int D, int block, int topk, float scale, int dtype, bool* noop) {
+  *noop = false;
+  int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, what);
+  if (!st) st = check_scale(scale, what);
+  if (st) return st;
+  if (Hkv > 0 && Hq / Hkv > kMaxGroupDecode)
+    return fail(SAS_EUNSUPPORTED, "%s: at most %d query heads per KV head", what, kMaxGroupDecode);
+  if (idx && topk < 0) return fail(SAS_EINVAL, "%s: topk must be >= 0 with idx", what);
+  if (idx && topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "%s: topk %d > %d", what, topk, kMaxTopk);
+  if (B == 0 || Hq == 0) {
+    g_error.clear();
+    *noop = true;
+    return SAS_OK;
+  }
+  if (!q || !k_cache || !v_cache || !cache_len || !o)
+    return fail(SAS_EINVAL, "%s: q, caches, cache_len and o must be non-NULL", what);
+  return SAS_OK;
+}
+
 int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* cache_len, const int32_t* idx, void* o, float* lse, int B,
                       int Hq, int Hkv, int L_max, int D, int block, int topk, float scale,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, "sas_sparse_decode");
-  if (!st) st = check_scale(scale, "sas_sparse_decode");
-  if (st) return st;
-  if (Hkv > 0 && Hq / Hkv > kMaxGroupDecode)
-    return fail(SAS_EUNSUPPORTED, "sas_sparse_decode: at most %d query heads per KV head", kMaxGroupDecode);
-  if (idx && topk < 0) return fail(SAS_EINVAL, "sas_sparse_decode: topk must be >= 0 with idx");
-  if (idx && topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "sas_sparse_decode: topk %d > %d", topk, kMaxTopk);
-  if (B == 0 || Hq == 0) {
-    g_error.clear();
-    return SAS_OK;
-  }
-  if (!q || !k_cache || !v_cache || !cache_len || !o)
-    return fail(SAS_EINVAL, "sas_sparse_decode: q, caches, cache_len and o must be non-NULL");
+  bool noop = false;
+  int st = check_decode("sas_sparse_decode", q, k_cache, v_cache, cache_len, idx, o, B, Hq, Hkv, L_max, D,
+                        block, topk, scale, dtype, &noop);
+  if (st || noop) return st;
   const size_t need = sas::decode_workspace(B, Hq, Hkv, L_max, D, block, idx ? topk : -1);
   if (!workspace || workspace_bytes < need)
     return fail(SAS_EWORKSPACE, "sas_sparse_decode: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
@@ -297,6 +311,28 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                                     D, block, idx ? topk : -1, scale, dtype == SAS_BF16, workspace,
                                     static_cast<hipStream_t>(stream));
   return hip_status(e, "sas_sparse_decode");
+}
+
+int sas_sparse_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cache_len, const int32_t* idx, void* o, float* lse,
+                              int B, int Hq, int Hkv, int L_max, int D, int block, int topk,
+                              float scale, int dtype, void* stream) {
+  bool noop = false;
+  int st = check_decode("sas_sparse_decode_noalloc", q, k_cache, v_cache, cache_len, idx, o, B, Hq, Hkv,
+                        L_max, D, block, topk, scale, dtype, &noop);
+  if (st || noop) return st;
+  const size_t need = sas::decode_workspace(B, Hq, Hkv, L_max, D, block, idx ? topk : -1);
+  if (need > sas::kNoAllocScratchBytes)
+    return fail(SAS_EUNSUPPORTED,
+                "sas_sparse_decode_noalloc: these sizes need %zu bytes of scratch, more than the %zu bytes "
+                "the allocation-free call holds per GPU (use sas_sparse_decode with a workspace)",
+                need, sas::kNoAllocScratchBytes);
+  void* scratch_ptr = nullptr;
+  hipError_t e = sas::noalloc_scratch(&scratch_ptr);
+  if (e != hipSuccess) return hip_status(e, "sas_sparse_decode_noalloc (scratch address)");
+  e = sas::launch_decode(q, k_cache, v_cache, cache_len, idx, o, lse, B, Hq, Hkv, L_max, D, block,
+                         idx ? topk : -1, scale, dtype == SAS_BF16, scratch_ptr, static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_sparse_decode_noalloc");
 }
 
 int sas_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages, int n_pages, int Hkv,

@@ -118,4 +118,11 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
                          int L_max, int D, int block, int topk, float scale, bool bf16, void* ws,
                          hipStream_t s, const int32_t* table = nullptr);
 
+// ---- allocation-free decode ----------------------------------------------------
+// Size of the per-GPU scratch array behind sas_sparse_decode_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace sas
