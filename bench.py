@@ -8,10 +8,13 @@ by the step time, where attended pairs count each query row's own-block keys
 (causal) plus the keys of its selected history blocks, exactly.
 
 Also reported: per-kernel times (HIP events on the launch stream), the same
-shape at full scope, and sparse decode tokens/s at 128K (batch 8) and 512K
-(batch 1, plus the dense-decode ratio), each decode step being score + Top-K +
-sparse attention over one attention layer, with the 256 MB last-level cache
-flushed between timed steps.
+shape at full scope, the 8K-token full-scope step (Qwen3-4B-like layer), and
+sparse decode tokens/s at 128K (batch 8; Top-K 16 as configured and 32, the
+2048-token budget) and 512K (batch 1, Top-K 32, plus the dense-decode ratio),
+each decode step being score + Top-K + sparse attention over one attention
+layer (sas_decode_step, with the separate calls timed beside it), with the
+256 MB last-level cache flushed between timed steps.  The CPU oracle is timed
+on a sample of the training step and on the whole 512K decode step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--quick]
 """
@@ -142,7 +145,10 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     cache and L2 flushed before each timed span by a 1 GiB read (a sum over a
     1 GiB buffer).  A 1 GiB write flush leaves the memory-side cache full of
     dirty lines whose write-back then competes with the decode reads; its step
-    time is reported beside it."""
+    time is reported beside it.  The step is sas_decode_step (scores, Top-K and
+    attention in two launches); the same step through the separate calls
+    (sas_score_blocks, sas_topk_select, sas_sparse_decode) is timed beside it.
+    Dense decode is sas_sparse_decode over every cached position."""
     from trainable_block_sparse_sas_amd.inputs import decode_inputs
     from trainable_block_sparse_sas_amd.pipeline import DecodeStep
     from trainable_block_sparse_sas_amd import binding as sas
@@ -154,6 +160,10 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
     acc = torch.zeros(1, dtype=torch.float32, device="cuda")
     tiny = torch.zeros(16, dtype=torch.float32, device="cuda")
+    ws = None
+    if not dense:
+        ws = sas.workspace(sas.SAS_OP_DECODE_STEP, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk,
+                           sas.SAS_BF16 if w.torch_dtype == torch.bfloat16 else sas.SAS_F32)
 
     def read_flush(i):
         torch.sum(flush, dim=0, keepdim=True, out=acc)
@@ -161,7 +171,11 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     def write_flush(i):
         flush.fill_(float(i & 7))
 
-    def run_step():
+    def fused_step():
+        sas.sas_decode_step(q, step.kbar, kc, vc, lens, w.topk, step.o, step.lse, w.block, w.scale,
+                            idx_out=step.idx, workspace=ws)
+
+    def separate_step():
         if not dense:
             step.select(q, lens)
         step.attend(q, kc, vc, lens)
@@ -178,24 +192,23 @@ def bench_decode(torch, w, steps, warmup, dense=False):
         return tm.ms(name, median=True)
 
     tm = Timer(torch)
+    run_step = separate_step if dense else fused_step
     ms = timed(run_step, read_flush, steps, "step", tm)
     ms_wf = timed(run_step, write_flush, steps, "step_wf", tm)
     floor = timed(lambda: tiny.fill_(1.0), read_flush, steps, "floor", tm)
-    ms_score = ms_topk = 0.0
-    if not dense:
-        ms_score = timed(lambda: sas.sas_score_blocks(q, None, step.kbar, step.u, lens, w.block, w.scale,
-                                                      group_sum=True, L=w.N), read_flush, steps, "score", tm)
-        ms_topk = timed(lambda: sas.sas_topk_select(step.u, step.idx, lens, 1, w.block), read_flush, steps,
-                        "topk", tm)
-    ms_attend = timed(lambda: step.attend(q, kc, vc, lens), read_flush, steps, "attend", tm)
+    ms_sep = ms if dense else timed(separate_step, read_flush, steps, "separate", tm)
     C = w.N // w.block
     kv_blocks = C if dense else (w.topk + 1)
     kv_bytes = w.B * w.Hkv * kv_blocks * w.block * w.D * 2 * 2
     kbar_bytes = 0 if dense else w.B * w.Hkv * C * w.D * 2
+    # algorithmic bytes of one step: pooled keys and attended K, V read; q read,
+    # o written; the group scores (fp32) written once
+    qo_bytes = 2 * w.B * w.Hq * w.D * 2
+    u_bytes = 0 if dense else w.B * w.Hkv * C * 4
+    step_bytes = kv_bytes + kbar_bytes + qo_bytes + u_bytes
     return dict(ms_step=ms, tokens_per_s=w.B / (ms * 1e-3), kv_bytes=kv_bytes, kbar_bytes=kbar_bytes,
-                ms_step_write_flush=ms_wf, ms_event_floor=floor,
-                ms_score=ms_score, ms_topk=ms_topk, ms_attend=ms_attend,
-                attend_gbs=kv_bytes / (ms_attend * 1e-3) / 1e9)
+                step_bytes=step_bytes, ms_step_write_flush=ms_wf, ms_event_floor=floor, ms_separate=ms_sep,
+                attend_gbs=kv_bytes / (ms * 1e-3) / 1e9)
 
 
 def bench_paged_decode(torch, w, steps, warmup):
@@ -436,28 +449,81 @@ def cpu_baseline(w):
                       f"group ({ws.Hq} query heads) of the same seeded inputs, Top-K {ws.topk}"}
 
 
+def decode_entry(r, topk):
+    gbs = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    return {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_step": round(r["ms_step"], 4),
+            "ms_step_separate_calls": round(r["ms_separate"], 4),
+            "ms_step_after_write_flush": round(r["ms_step_write_flush"], 4),
+            "step_bytes": r["step_bytes"], "kv_bytes": r["kv_bytes"], "kbar_bytes": r["kbar_bytes"],
+            "step_GBps": round(gbs, 1), "step_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_event_pair_floor": round(r["ms_event_floor"], 4),
+            "timing": "median of 50 HIP-event spans of sas_decode_step, 1 GiB read flush before each span "
+                      "(each span includes the event-pair floor)",
+            "topk": topk}
+
+
 def bench_decodes(torch, wmap):
     dec = {}
-    for name in ("decode-128k-b8", "decode-512k-b1"):
-        wd = wmap[name]
-        r = bench_decode(torch, wd, 50, 10)
-        dec[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_step": round(r["ms_step"], 4),
-                     "ms_step_after_write_flush": round(r["ms_step_write_flush"], 4),
-                     "ms_score": round(r["ms_score"], 4), "ms_topk": round(r["ms_topk"], 4),
-                     "ms_attend": round(r["ms_attend"], 4), "attend_GBps_on_kv": round(r["attend_gbs"], 1),
-                     "ms_event_pair_floor": round(r["ms_event_floor"], 4),
-                     "timing": "median of 50 HIP-event spans, 1 GiB read flush before each span; "
-                               "stage spans each include the event-pair floor",
-                     "topk": wd.topk}
-        dec[name]["paged"] = bench_paged_decode(torch, wd, 50, 10)
-        torch.cuda.empty_cache()
-        if name == "decode-512k-b1":
-            rd = bench_decode(torch, wd, 20, 3, dense=True)
-            dec[name]["dense_ms"] = round(rd["ms_step"], 4)
-            dec[name]["dense_GBps"] = round(rd["attend_gbs"], 1)
-            dec[name]["speedup_vs_dense"] = round(rd["ms_step"] / r["ms_step"], 2)
-            dec[name]["pages_speedup_context"] = "5.6x end-to-end Qwen3-4B decode at 512K, batch 1, unnamed GPU"
+    for name, topks in (("decode-128k-b8", (16, 32)), ("decode-512k-b1", (32,))):
+        dec[name] = {}
+        for topk in topks:
+            wd = wmap[name].with_(topk=topk)
+            r = bench_decode(torch, wd, 50, 10)
+            ent = decode_entry(r, topk)
+            ent["paged"] = bench_paged_decode(torch, wd, 50, 10)
+            dec[name][f"k{topk}"] = ent
+            torch.cuda.empty_cache()
+            if name == "decode-512k-b1":
+                rd = bench_decode(torch, wd, 20, 3, dense=True)
+                dec[name]["dense_ms"] = round(rd["ms_step"], 4)
+                dec[name]["dense_GBps"] = round(rd["attend_gbs"], 1)
+                dec[name]["speedup_vs_dense"] = round(rd["ms_step"] / r["ms_step"], 2)
+                dec[name]["pages_speedup_context"] = ("5.6x end-to-end Qwen3-4B decode at 512K, batch 1, "
+                                                      "unnamed GPU")
     return dec
+
+
+def cpu_baseline_decode(w):
+    """The oracle's decode step (group scores from the pooled keys, Top-K,
+    sparse attention; pooled keys precomputed, as on the GPU) on the same seeded
+    512K-token cache, all threads and one thread."""
+    import numpy as np
+    import torch
+
+    from oracle import sas_oracle as orc
+    from trainable_block_sparse_sas_amd.inputs import decode_inputs
+
+    q, kc, vc, lens = decode_inputs(w, device="cpu")
+    f = lambda t: t.to(torch.float64).numpy()
+    q64, kc64, vc64, lens_np = f(q), f(kc), f(vc), lens.numpy()
+    kbar = orc.pool_block_keys(kc64, w.block)
+
+    def one():
+        u = orc.decode_scores(q64, kbar, lens_np, w.N, w.block, w.scale, True)
+        c = orc.decode_candidates(lens_np, w.N, w.block)
+        idx = orc.topk_select(u[:, :, None, :], 1, c[:, None], w.topk)[:, :, 0, :]
+        orc.sparse_decode(q64, kc64, vc64, lens_np, idx, w.block, w.scale)
+
+    def timed():
+        one()
+        t0 = time.perf_counter()
+        n = 3
+        for _ in range(n):
+            one()
+        return (time.perf_counter() - t0) / n
+
+    try:
+        import threadpoolctl
+        cores = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
+        dt = timed()
+        with threadpoolctl.threadpool_limits(1):
+            dt1 = timed()
+    except Exception:
+        cores, dt, dt1 = os.cpu_count(), timed(), None
+    return {"value": w.B / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "seconds_per_step": dt,
+            "seconds_per_step_1_thread": dt1,
+            "sample": f"fp64 oracle decode step ({w.name}, Top-K {w.topk}: scores from precomputed pooled "
+                      f"keys, Top-K, sparse attention), whole workload"}
 
 
 def main():
@@ -509,11 +575,23 @@ def main():
             "tflops": round((full["flops_fwd"] + full["flops_bwd"]) / (full["ms_step"] * 1e-3) / 1e12, 3),
             "fwd_tflops": round(full["flops_fwd"] / (full["ms_fwd"] * 1e-3) / 1e12, 3),
             "bwd_tflops": round(full["flops_bwd"] / (full["ms_bwd"] * 1e-3) / 1e12, 3)}
+        w8 = wmap["train-8k-full"]
+        t8 = bench_train(torch, w8, max(3, args.steps), 2)
+        out["train_8k_full"] = {
+            "ms_step": round(t8["ms_step"], 4),
+            "tflops": round((t8["flops_fwd"] + t8["flops_bwd"]) / (t8["ms_step"] * 1e-3) / 1e12, 3),
+            "fwd_tflops": round(t8["flops_fwd"] / (t8["ms_fwd"] * 1e-3) / 1e12, 3),
+            "bwd_tflops": round(t8["flops_bwd"] / (t8["ms_bwd"] * 1e-3) / 1e12, 3),
+            "step": "pool+score -> gated fwd -> gated bwd, full scope (8192 tokens, 32/8 heads, D 128)"}
+        del t8
+        torch.cuda.empty_cache()
         out["decode"] = bench_decodes(torch, wmap)
         out["selector_bwd"] = bench_selector_bwd(torch, w, 5)
         out["gate_variants"] = bench_gate_variants(torch, w, 3)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
+        if not args.quick:
+            out["cpu_baseline_decode"] = cpu_baseline_decode(wmap["decode-512k-b1"])
     print(json.dumps(out))
 
 

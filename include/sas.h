@@ -88,7 +88,8 @@ typedef enum {
   SAS_OP_SELECTOR_BWD = 6,
   SAS_OP_PAGED_DECODE = 7,
   SAS_OP_FWD_GATE = 8,   /* sas_gated_attn_fwd_gate, any gate */
-  SAS_OP_BWD_GATE = 9    /* sas_gated_attn_bwd_gate, any gate */
+  SAS_OP_BWD_GATE = 9,   /* sas_gated_attn_bwd_gate, any gate */
+  SAS_OP_DECODE_STEP = 10 /* sas_decode_step */
 } sas_op;
 
 /* Gate activation of the gated attention (blog 方法核心, the ablation table's
@@ -273,6 +274,40 @@ int sas_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sas_decode_step -- one whole decode step for the new token of each sequence:
+ *   group-summed selector scores of its history blocks from the pooled keys
+ *   (as sas_score_blocks with group_sum), hard Top-K of them (as
+ *   sas_topk_select, lengths clamped to L_max), then attention over the
+ *   selected blocks and the current block with no gate (as sas_sparse_decode):
+ *   the inference path of review "A Concrete Walkthrough", Step 6, paper
+ *   Alg. 2, where at long contexts the selection stage is the bottleneck
+ *   (review "Decoding Efficiency", Fig. 7c; "Our Perspective", Limitations).
+ *   One call enqueues the separate calls' kernels in sequence (scores, Top-K,
+ *   per-block attention partials, their merge) on one workspace; the results
+ *   are those of the separate calls.
+ * q:          [B,Hq,D]; kbar [B,Hkv,C,D] pooled keys (C = L_max / block, e.g.
+ *             from sas_score_blocks with k = the cache); k_cache, v_cache
+ *             [B,Hkv,L_max,D]; cache_len int32 [B] (above L_max counts as
+ *             L_max; <= 0 is an idle sequence: o = 0, lse = -inf).
+ * topk:       0 .. 256 blocks (0: the current block only).
+ * o:          [B,Hq,D] output in dtype; lse optional fp32 [B,Hq] output.
+ * idx_out:    optional int32 [B,Hkv,topk] output: the selected history blocks,
+ *             score descending, ties to the lower index, -1 padding.
+ * workspace:  sas_workspace_bytes(SAS_OP_DECODE_STEP, B, Hq, Hkv, L_max, D,
+ *             block, topk, dtype) bytes, contents ignored.  After the call its
+ *             first B*Hkv*C floats hold the group-summed scores [B,Hkv,C] the
+ *             selection was made on (-inf for non-candidates).
+ * Errors: SAS_EINVAL, SAS_EUNSUPPORTED (D outside {64, 128}, more than 16
+ *         query heads per KV head, topk > 256, more than 16384 blocks),
+ *         SAS_EWORKSPACE.
+ */
+int sas_decode_step(const void* q, const void* kbar, const void* k_cache,
+                    const void* v_cache, const int32_t* cache_len, int topk,
+                    void* o, float* lse, int32_t* idx_out, int B, int Hq, int Hkv,
+                    int L_max, int D, int block, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sas_sparse_decode_noalloc -- sas_sparse_decode without a workspace argument,
  *   for callers that cannot allocate device memory (code under HIP graph
  *   capture, tight serving loops, harnesses that forbid allocation).  Same
@@ -322,7 +357,8 @@ int sas_pool_pages(const void* k_pages, void* kbar_pages, const int32_t* pages,
  *   pooled keys (as sas_score_blocks), Top-K (as sas_topk_select), then
  *   attention over the selected blocks and the current block with no gate
  *   (as sas_sparse_decode; review "A Concrete Walkthrough", Step 6, paper
- *   Alg. 2).
+ *   Alg. 2).  It runs as sas_decode_step does, reading blocks and pooled
+ *   keys through the block table.
  * q:          [B,Hq,D]; cache_len int32 [B] (a length above max_blocks *
  *             block counts as that; <= 0 is an idle sequence).
  * topk:       0 .. 256 blocks (0: the current block only).

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
                           "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
-                          "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_workspace_bytes",
+                          "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_decode_step", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
     for n in names:
@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 102
+    assert sas.sas_abi_version() == 103
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
@@ -246,3 +246,30 @@ def test_noalloc_decode_validation_on_the_host():
                                        sas.SAS_BF16, N) == sas.SAS_EUNSUPPORTED
     assert L.sas_sparse_decode_noalloc(d, d, d, d, N, d, N, 0, 4, 2, 1024, 128, 64, 0, f(0.1),
                                        sas.SAS_BF16, N) == sas.SAS_OK
+
+
+def test_decode_step_validation_on_the_host():
+    """sas_decode_step validates on the host, before any HIP call, through the
+    Python binding's argument list (so the binding's signature is exercised)."""
+    vp = ctypes.c_void_p
+    d = vp(256)
+    f = ctypes.c_float
+    ws_need = sas.sas_workspace_bytes(sas.SAS_OP_DECODE_STEP, 2, 8, 2, 4096, 128, 64, 16, sas.SAS_BF16)
+    assert 0 < ws_need < (1 << 30)
+    call = L.sas_decode_step
+    # workspace missing / too small
+    assert call(d, d, d, d, d, 16, d, N, N, 2, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, N, 0, N) == sas.SAS_EWORKSPACE
+    assert call(d, d, d, d, d, 16, d, N, N, 2, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, d, ws_need - 1,
+                N) == sas.SAS_EWORKSPACE
+    # bad arguments
+    assert call(N, d, d, d, d, 16, d, N, N, 2, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, d, ws_need,
+                N) == sas.SAS_EINVAL
+    assert call(d, d, d, d, d, -1, d, N, N, 2, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, d, ws_need,
+                N) == sas.SAS_EINVAL
+    assert call(d, d, d, d, d, 300, d, N, N, 2, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, d, 1 << 40,
+                N) == sas.SAS_EUNSUPPORTED
+    assert call(d, d, d, d, d, 16, d, N, N, 2, 40, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, d, 1 << 40,
+                N) == sas.SAS_EUNSUPPORTED
+    assert call(d, d, d, d, d, 16, d, N, N, 2, 8, 2, 4096, 128, 64, f(-1.0), sas.SAS_BF16, d, 1 << 40,
+                N) == sas.SAS_EINVAL
+    assert call(d, d, d, d, d, 16, d, N, N, 0, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, N, 0, N) == sas.SAS_OK

@@ -2,10 +2,10 @@
 
 Each call runs twice on identical inputs, with every output overwritten by NaN
 in between, and the two results must agree bit for bit.  The kernels use no
-global-memory atomics and no floating-point atomics at all; the only atomics
-are integer LDS counters and bit sets (Top-K histograms, selection bitmasks,
-running maxima of non-negative integers), whose results do not depend on the
-order in which the lanes arrive, so every sum is formed in a fixed order.
+global-memory and no floating-point atomics; the only atomics are integer LDS
+counters and bit sets (Top-K histograms, selection bitmasks, running maxima of
+non-negative integers), whose results do not depend on the order in which the
+lanes arrive, so every sum is formed in a fixed order.
 Small shapes cover every entry point; the benchmark shapes cover the training
 step and the decode step as bench.py times them.
 """
@@ -99,6 +99,10 @@ def test_decode_entry_points_deterministic():
     ws = sas.workspace(sas.SAS_OP_PAGED_DECODE, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
     _twice(lambda: sas.sas_paged_decode(q, kp, vp, kbp, table, lens, topk, o, lse, block, w.scale, idx_out=idx,
                                         workspace=ws), [o, lse, idx])
+    # the fused step on the contiguous cache
+    wsd = sas.workspace(sas.SAS_OP_DECODE_STEP, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
+    _twice(lambda: sas.sas_decode_step(q, step.kbar, kc, vc, lens, topk, o, lse, block, w.scale, idx_out=idx,
+                                       workspace=wsd), [o, lse, idx])
 
 
 @pytest.mark.slow
@@ -117,3 +121,6 @@ def test_benchmark_shapes_deterministic():
     d.pool(kc)
     torch.cuda.synchronize()
     _twice(lambda: d.run(q, kc, vc, lens), [d.u, d.idx, d.o, d.lse])
+    ws = sas.workspace(sas.SAS_OP_DECODE_STEP, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, sas.SAS_BF16)
+    _twice(lambda: sas.sas_decode_step(q, d.kbar, kc, vc, lens, w.topk, d.o, d.lse, w.block, w.scale, idx_out=d.idx,
+                                       workspace=ws), [d.o, d.lse, d.idx])

@@ -310,3 +310,49 @@ def test_decode_fullsize(wi):
             ob, _ = orc.sparse_decode(q64[:, sl], to64(kc[:, g:g + 1]), to64(vc[:, g:g + 1]), lens_np, None,
                                       w.block, w.scale)
             max_abs(to64(dstep.o[:, sl]), ob, 2e-2, "dense o")
+
+
+@pytest.mark.parametrize("wi,topk", [(3, 16), (3, 32), (4, 32)],
+                         ids=["decode-128k-b8-k16", "decode-128k-b8-k32", "decode-512k-b1-k32"])
+def test_decode_step_fullsize(wi, topk):
+    """sas_decode_step at the benchmark sizes (128K tokens x 8 sequences at the
+    configured K = 16 and at the metric's 2048-token budget, K = 32; 512K x 1),
+    in the configuration bench.py times: its scores against the oracle's, its
+    selection bit-exact against the oracle's Top-K on those scores, o and lse
+    against the oracle's sparse decode over that selection."""
+    w = WORKLOADS[wi].with_(topk=topk)
+    dt = w.torch_dtype
+    q, kc, vc, lens = decode_inputs(w, device=DEV)
+    G = w.Hq // w.Hkv
+    lens_np = lens.cpu().numpy()
+    kbar = np.empty((w.B, w.Hkv, w.C, w.D))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            kbar[b, g] = orc.pool_block_keys(to64(kc[b:b + 1, g:g + 1]), w.block)[0, 0]
+    kbar_r = to64(torch.tensor(kbar).to(dt))
+    o = torch.empty((w.B, w.Hq, w.D), dtype=dt, device=DEV)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.B, w.Hkv, topk), dtype=torch.int32, device=DEV)
+    ws = sas.workspace(sas.SAS_OP_DECODE_STEP, w.B, w.Hq, w.Hkv, w.N, w.D, w.block, topk, sas.SAS_BF16)
+    sas.sas_decode_step(q, torch.tensor(kbar_r).to(dt).to(DEV), kc, vc, lens, topk, o, lse, w.block, w.scale,
+                        idx_out=idx, workspace=ws)
+    torch.cuda.synchronize()
+    q64 = to64(q)
+    u_ref = orc.decode_scores(q64, kbar_r, lens_np, w.N, w.block, w.scale, True)
+    u_gpu = ws[: w.B * w.Hkv * w.C * 4].view(torch.float32).reshape(w.B, w.Hkv, w.C).cpu().numpy()
+    normwise(u_gpu.astype(np.float64), u_ref.astype(np.float64), 1e-5, "u")
+    c = orc.decode_candidates(lens_np, w.N, w.block)
+    idx_ref = orc.topk_select(u_gpu[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), "Top-K on the step's own scores"
+    assert len(np.unique(idx_ref)) > topk  # selection is non-trivial
+    o_ref = np.empty((w.B, w.Hq, w.D))
+    lse_ref = np.empty((w.B, w.Hq))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            sl = slice(g * G, (g + 1) * G)
+            ob, lb = orc.sparse_decode(q64[b:b + 1, sl], to64(kc[b:b + 1, g:g + 1]), to64(vc[b:b + 1, g:g + 1]),
+                                       lens_np[b:b + 1], idx_ref[b:b + 1, g:g + 1], w.block, w.scale)
+            o_ref[b, sl], lse_ref[b, sl] = ob[0], lb[0]
+    max_abs(to64(o), o_ref, 2e-2, "o")
+    _rowwise(to64(o), o_ref, 2e-2, "o per row")
+    normwise(to64(lse), lse_ref, 1e-4, "lse")

@@ -548,3 +548,70 @@ def test_full_star_by_composition():
     dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, w.scale)
     normwise(to64(step.ds), ds, tol["ds"], "ds")
     normwise(to64(step.dq), dq, tol["grad"], "dq")
+
+
+DECODE_STEP_CASES = [
+    # name, dtype, Hq, Hkv, D, L, block, topk
+    ("bf16-g4-k4", "bf16", 8, 2, 128, 2048, 64, 4),
+    ("bf16-g5-k3-ragged-cap", "bf16", 10, 2, 128, 1500, 64, 3),
+    ("bf16-block32-k5", "bf16", 4, 2, 128, 1000, 32, 5),
+    ("bf16-g16-d64-k9", "bf16", 16, 1, 64, 1280, 64, 9),
+    ("bf16-k0", "bf16", 8, 2, 128, 1024, 64, 0),
+    ("bf16-k64", "bf16", 8, 2, 128, 64 * 700, 64, 64),
+    ("bf16-k40-ties", "bf16", 4, 1, 128, 64 * 300, 64, 40),
+    ("bf16-k100", "bf16", 8, 2, 128, 64 * 300, 64, 100),
+    ("f32-k3", "f32", 4, 1, 64, 1024, 64, 3),
+    ("bf16-block128", "bf16", 8, 2, 128, 2048, 128, 3),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_STEP_CASES, ids=[c[0] for c in DECODE_STEP_CASES])
+def test_decode_step_parity(case):
+    """sas_decode_step: the scores it leaves in the workspace match the oracle's;
+    its selection is the oracle's Top-K on those very scores (bit-exact); o and
+    lse match the oracle's sparse decode over that selection."""
+    name, dts, Hq, Hkv, D, L, block, topk = case
+    dt = _dt(dts)
+    B = 5
+    w = Workload(name, "decode", dts, B, Hq, Hkv, D, L, block, topk, index=12)
+    q, kc, vc, _ = decode_inputs(w, device="cpu")
+    if "ties" in name:  # many equal pooled keys: equal scores, ties to the lower block
+        kc[:, :, : 64 * 200] = kc[:, :, :64].repeat(1, 1, 200, 1)
+    lens = torch.tensor([L, L - 37, 40, 0, 10 * L + 3], dtype=torch.int32)
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(to64(kc), block)).to(dt))
+    C = L // block
+    o = torch.full((B, Hq, D), float("nan"), dtype=dt, device=DEV)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    idx = torch.full((B, Hkv, max(topk, 1)), -7, dtype=torch.int32, device=DEV)
+    ws = sas.workspace(sas.SAS_OP_DECODE_STEP, B, Hq, Hkv, L, D, block, topk,
+                       sas.SAS_BF16 if dt == torch.bfloat16 else sas.SAS_F32)
+    qd, kcd, vcd, lensd = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    kbd = torch.tensor(kbar_r).to(dt).to(DEV)
+    sas.sas_decode_step(qd, kbd, kcd, vcd, lensd, topk, o, lse, block, w.scale,
+                        idx_out=idx[..., :topk] if topk > 0 else None, workspace=ws)
+    torch.cuda.synchronize()
+    u_ref = orc.decode_scores(to64(q), kbar_r, lens.numpy(), L, block, w.scale, True)
+    u_gpu = ws[: B * Hkv * C * 4].view(torch.float32).reshape(B, Hkv, C).cpu().numpy()
+    normwise(u_gpu.astype(np.float64), u_ref.astype(np.float64), 1e-5, "u")
+    assert np.array_equal(np.isneginf(u_gpu), np.isneginf(u_ref))
+    c = orc.decode_candidates(lens.numpy(), L, block)
+    idx_ref = np.zeros((B, Hkv, 0), dtype=np.int64)
+    if topk > 0:
+        idx_ref = orc.topk_select(u_gpu[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+        assert np.array_equal(idx.cpu().numpy()[..., :topk], idx_ref), "Top-K on the step's own scores"
+    o_ref, lse_ref = orc.sparse_decode(to64(q), to64(kc), to64(vc), lens.numpy(), idx_ref, block, w.scale)
+    active = lens.numpy() > 0
+    tol = tolerances(dt)
+    if tol["o_abs"] is not None:
+        max_abs(to64(o)[active], o_ref[active], tol["o_abs"], "o")
+    else:
+        normwise(to64(o)[active], o_ref[active], tol["o_rel"], "o")
+    normwise(to64(lse)[active], lse_ref[active], 1e-4, "lse")
+    assert torch.all(o[~torch.tensor(active)] == 0)
+    assert torch.all(lse[~torch.tensor(active)] == float("-inf"))
+    # again, without idx_out and on the dirty workspace: the same bits
+    o2 = torch.full_like(o, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    sas.sas_decode_step(qd, kbd, kcd, vcd, lensd, topk, o2, lse2, block, w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)

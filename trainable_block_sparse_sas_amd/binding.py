@@ -27,11 +27,12 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTOR_BWD = 1, 2, 3, 4, 5, 6
 SAS_OP_PAGED_DECODE = 7
 SAS_OP_FWD_GATE, SAS_OP_BWD_GATE = 8, 9
+SAS_OP_DECODE_STEP = 10
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
-            "sas_sparse_decode_noalloc", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_sparse_decode_noalloc", "sas_decode_step", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -43,6 +44,7 @@ _lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp,
 _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode_noalloc.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
+_lib.sas_decode_step.argtypes = [_vp] * 5 + [_i, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_pool_pages.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
 _lib.sas_paged_decode.argtypes = [_vp] * 5 + [_i, _vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
@@ -57,7 +59,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
               "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
-              "sas_sparse_decode_noalloc"):
+              "sas_sparse_decode_noalloc", "sas_decode_step"):
     getattr(_lib, _name).restype = _i
 
 
@@ -281,3 +283,15 @@ def sas_paged_decode(q, k_pages, v_pages, kbar_pages, block_table, cache_len, to
     _check(_lib.sas_paged_decode(_p(q), _p(k_pages), _p(v_pages), _p(kbar_pages), _p(block_table),
                                  block_table.shape[1], _p(cache_len), topk, _p(o), _p(lse), _p(idx_out), B, Hq,
                                  Hkv, D, block, scale, _dt(q), _p(workspace), wsb, _stream(stream)))
+
+
+def sas_decode_step(q, kbar, k_cache, v_cache, cache_len, topk, o, lse, block, scale, idx_out=None, workspace=None,
+                    stream=None):
+    """q [B,Hq,D]; kbar [B,Hkv,C,D]; caches [B,Hkv,L_max,D]; cache_len int32 [B]: scores, Top-K and sparse
+    attention in one call."""
+    B, Hq, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_decode_step(_p(q), _p(kbar), _p(k_cache), _p(v_cache), _p(cache_len), topk, _p(o), _p(lse),
+                                _p(idx_out), B, Hq, Hkv, L, D, block, scale, _dt(q), _p(workspace), wsb,
+                                _stream(stream)))

@@ -71,13 +71,34 @@ int check_scale(float scale, const char* what) {
   return SAS_OK;
 }
 
+// One decode step (scores, Top-K, attention, merge) over contiguous caches
+// (table == NULL) or pages: the group-summed scores land at the start of the
+// workspace, lengths are clamped to L_max before Top-K.
+hipError_t decode_chain(const void* q, const void* kbar, const void* kc, const void* vc, const int32_t* cache_len,
+                        const int32_t* table, int topk, void* o, float* lse, int32_t* idx_out, int B, int Hq,
+                        int Hkv, int L_max, int D, int block, float scale, bool bf16, void* workspace,
+                        hipStream_t s) {
+  const PagedWs W = paged_ws(B, Hq, Hkv, L_max, D, block, topk);
+  const int C = L_max / block;
+  char* w = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(w + W.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + W.idx);
+  hipError_t e = sas::launch_score_decode(q, kbar, scores, cache_len, B, Hq, Hkv, L_max, D, block, C, scale, true,
+                                          bf16, s, table);
+  if (e == hipSuccess && topk > 0) e = sas::launch_topk(scores, idx, cache_len, B, Hkv, 1, 1, C, block, topk, s, L_max);
+  if (e == hipSuccess)
+    e = sas::launch_decode(q, kc, vc, cache_len, idx, o, lse, B, Hq, Hkv, L_max, D, block, topk, scale, bf16,
+                           w + W.part, s, table);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 102; }
+int sas_abi_version(void) { return 103; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
@@ -98,6 +119,7 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
       if (D != 64 && D != 128) return size_t(-1);
       return sas::selector_bwd_workspace(d, bf16);
     case SAS_OP_PAGED_DECODE:
+    case SAS_OP_DECODE_STEP:
       if (topk < 0) return size_t(-1);
       return paged_ws(B, Hq, Hkv, n, D, block, topk).total;
     case SAS_OP_FWD_GATE:
@@ -377,17 +399,36 @@ int sas_paged_decode(const void* q, const void* k_pages, const void* v_pages, co
   const PagedWs W = paged_ws(B, Hq, Hkv, L_max, D, block, topk);
   if (!workspace || workspace_bytes < W.total)
     return fail(SAS_EWORKSPACE, "sas_paged_decode: workspace of %zu bytes required (got %zu)", W.total, workspace_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(w + W.scores);
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w + W.idx);
-  hipError_t e = sas::launch_score_decode(q, kbar_pages, scores, cache_len, B, Hq, Hkv, L_max, D, block,
-                                          max_blocks, scale, true, true, s, block_table);
-  if (e == hipSuccess && topk > 0) e = sas::launch_topk(scores, idx, cache_len, B, Hkv, 1, 1, max_blocks, block, topk, s, L_max);
-  if (e == hipSuccess)
-    e = sas::launch_decode(q, k_pages, v_pages, cache_len, idx, o, lse, B, Hq, Hkv, L_max, D, block, topk, scale,
-                           true, w + W.part, s, block_table);
+  hipError_t e = decode_chain(q, kbar_pages, k_pages, v_pages, cache_len, block_table, topk, o, lse, idx_out, B, Hq,
+                              Hkv, L_max, D, block, scale, true, workspace, static_cast<hipStream_t>(stream));
   return hip_status(e, "sas_paged_decode");
+}
+
+int sas_decode_step(const void* q, const void* kbar, const void* k_cache, const void* v_cache,
+                    const int32_t* cache_len, int topk, void* o, float* lse, int32_t* idx_out, int B, int Hq,
+                    int Hkv, int L_max, int D, int block, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_common(B, Hq, Hkv, L_max, D, block, dtype, "sas_decode_step");
+  if (!st) st = check_scale(scale, "sas_decode_step");
+  if (st) return st;
+  if (Hq / Hkv > kMaxGroupDecode)
+    return fail(SAS_EUNSUPPORTED, "sas_decode_step: at most %d query heads per KV head", kMaxGroupDecode);
+  if (topk < 0) return fail(SAS_EINVAL, "sas_decode_step: topk must be >= 0");
+  if (topk > kMaxTopk) return fail(SAS_EUNSUPPORTED, "sas_decode_step: topk %d > %d", topk, kMaxTopk);
+  if (L_max / block > kMaxBlocks)
+    return fail(SAS_EUNSUPPORTED, "sas_decode_step: %d blocks > %d", L_max / block, kMaxBlocks);
+  if (B == 0 || Hq == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !kbar || !k_cache || !v_cache || !cache_len || !o)
+    return fail(SAS_EINVAL, "sas_decode_step: q, kbar, caches, cache_len and o must be non-NULL");
+  const PagedWs W = paged_ws(B, Hq, Hkv, L_max, D, block, topk);
+  if (!workspace || workspace_bytes < W.total)
+    return fail(SAS_EWORKSPACE, "sas_decode_step: workspace of %zu bytes required (got %zu)", W.total, workspace_bytes);
+  hipError_t e = decode_chain(q, kbar, k_cache, v_cache, cache_len, nullptr, topk, o, lse, idx_out, B, Hq, Hkv,
+                              L_max, D, block, scale, dtype == SAS_BF16, workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_decode_step");
 }
 
 int sas_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq, void* dk,

@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 // column d: the first kMergeRegs partials' column values are loaded together
 // with the (max, sum) pairs (lane-parallel), so the merge costs one memory
 // round trip when P <= kMergeRegs; the weights go through LDS.
-constexpr int kMergeMax = 4096;  // partials per (b, g); decode_plan keeps P near 2048 / (B Hkv)
+constexpr int kMergeMax = 8192;  // partials per (b, g); decode_plan keeps P <= max(8192 / (B Hkv), 2049)
 constexpr int kMergeRegs = 48;
 
 template <typename T, int D>
@@ -481,11 +481,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 void decode_plan(int B, int Hkv, int L_max, int block, int topk, int* entries, int* epw, int* P) {
   const int C = L_max / block;
   const int E = topk >= 0 ? topk + 1 : C + 1;  // attended entries per (b, g)
-  // Aim for a few thousand workgroups in total; one block per workgroup when
-  // that already gives enough parallelism.
+  // One block per workgroup up to 8192 workgroups (the single-step kernel
+  // keeps no next-step registers and is about twice as fast per block as the
+  // streaming one); beyond that, blocks per workgroup for about 2048.
   const long target = 2048;
-  long groups = long(B) * Hkv;
-  int w = int((long(E) * groups + target - 1) / target);
+  const long groups = long(B) * Hkv;
+  int w = long(E) * groups <= 4 * target ? 1 : int((long(E) * groups + target - 1) / target);
   if (w < 1) w = 1;
   *entries = E;
   *epw = w;
@@ -554,7 +555,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
   if (B == 0 || Hq == 0) return hipSuccess;
   int E, w, P;
   decode_plan(B, Hkv, L_max, block, idx ? topk : -1, &E, &w, &P);
-  if (P > kMergeMax) return hipErrorInvalidValue;  // decode_plan keeps P <= 2049
+  if (P > kMergeMax) return hipErrorInvalidValue;  // decode_plan keeps P <= 8192
   DecodeArgs a{q, kc, vc, cache_len, idx, (float*)ws, Hq, Hkv, L_max, D, block,
                idx ? topk : 0, L_max / block, w, P, scale, table};
   if (bf16) {

@@ -14,6 +14,7 @@
 // registers instead, with no histogram passes and no atomics.
 #include "common.h"
 #include "internal.h"
+#include "runs.h"
 
 namespace sas {
 namespace {
@@ -417,101 +418,6 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(const float* __restrict
 // which sorts to the same run), so after log2(64 / R) rounds every group of
 // the wave holds the wave's best KP keys.  The W wave runs are merged the
 // same way through LDS.  The final run is the answer in rank order.
-
-__device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int mask) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t lo = lanes_xor(uint32_t(v), mask, lane);
-  const uint32_t hi = lanes_xor(uint32_t(v >> 32), mask, lane);
-  return (uint64_t(hi) << 32) | lo;
-}
-__device__ __forceinline__ uint32_t shfl_xor_key(uint32_t v, int mask) {
-  return lanes_xor(v, mask, threadIdx.x & 63);
-}
-
-// Sorts the bitonic run held by each group of R lanes (E keys per lane)
-// descending: half-cleaners at element distances KP/2 .. 1 (KP = R E).
-template <int E, int R, typename T>
-__device__ __forceinline__ void bitonic_clean(T (&v)[E], int lane) {
-#pragma unroll
-  for (int d = R * E / 2; d >= 1; d >>= 1) {
-    if (d >= E) {
-      const int dl = d / E;
-      const bool lower = (lane & dl) == 0;
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const T p = shfl_xor_key(v[r], dl);
-        v[r] = lower ? (v[r] > p ? v[r] : p) : (v[r] < p ? v[r] : p);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < E; ++r)
-        if ((r & d) == 0) {
-          const T a = v[r], b = v[r + d];
-          v[r] = a > b ? a : b;
-          v[r + d] = a > b ? b : a;
-        }
-    }
-  }
-}
-
-// Every group of R lanes holds a sorted run of R E keys; afterwards every
-// group holds the R E largest keys of all 64 / R runs of the wave, sorted.
-template <int E, int R, typename T>
-__device__ __forceinline__ void merge_wave_runs(T (&v)[E], int lane) {
-#pragma unroll
-  for (int D = R; D < 64; D <<= 1) {
-    T p[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) p[r] = shfl_xor_key(v[E - 1 - r], D | (R - 1));
-#pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = v[r] > p[r] ? v[r] : p[r];
-    bitonic_clean<E, R>(v, lane);
-  }
-}
-
-// Sorted runs of ML E keys over groups of ML lanes from sorted runs of half
-// that length (one bitonic merge per doubling), for ML = 2 .. R.
-template <int E, int ML, int R, typename T>
-__device__ __forceinline__ void build_runs(T (&v)[E], int lane) {
-  if constexpr (ML <= R) {
-    const bool lower = (lane & (ML - 1)) < ML / 2;
-    T p[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) p[r] = shfl_xor_key(v[E - 1 - r], ML - 1);
-#pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = lower ? (v[r] > p[r] ? v[r] : p[r]) : (v[r] < p[r] ? v[r] : p[r]);
-    bitonic_clean<E, ML>(v, lane);
-    build_runs<E, 2 * ML, R, T>(v, lane);
-  }
-}
-
-// Merges the W wave runs in runs[0] (each R lanes x E keys, sorted) into
-// one, GPW = 64 / R runs per merging wave per round; returns the buffer that
-// holds the result in its row 0 (visible to every wave on return).
-template <int E, int R, int KP, int W, typename T>
-__device__ __forceinline__ int merge_block_runs(T (*runs)[W][KP], int w, int lane) {
-  constexpr int GPW = 64 / R;
-  static_assert(GPW >= 2, "a round must reduce the run count");
-  int nruns = W, buf = 0;
-  while (nruns > 1) {
-    const int nw = (nruns + GPW - 1) / GPW;
-    __syncthreads();
-    if (w < nw) {
-      const int src = w * GPW + lane / R;
-      T v[E];
-#pragma unroll
-      for (int r = 0; r < E; ++r) v[r] = src < nruns ? runs[buf][src][(lane % R) * E + r] : T(0);
-      merge_wave_runs<E, R, T>(v, lane);
-      if (lane < R)
-#pragma unroll
-        for (int r = 0; r < E; ++r) runs[buf ^ 1][w][lane * E + r] = v[r];
-    }
-    buf ^= 1;
-    nruns = nw;
-  }
-  __syncthreads();
-  return buf;
-}
 
 // A filter runs first.  Take each lane's largest score key (32-bit, the score
 // alone): if tau is the K-th largest of these lane maxima, K lanes hold a key
