@@ -177,8 +177,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   } else {
     n_hist = max(0, N - (j0 + KT));
   }
-  const int n_steps = n_own + (n_hist + TPS - 1) / TPS;
-  // sparse scope: record of row 0 of history step k is rec0 + (k - n_own) RS
+  const int n_hsteps = (n_hist + TPS - 1) / TPS;
+  const int n_steps = n_own + n_hsteps;
+  // History steps walk the token stream from its end: step k >= n_own covers
+  // stream positions hstep(k) TPS .. (descending token order).  Every
+  // workgroup of a KV head then starts at the last tokens and, since a token
+  // selects each of its history blocks with the same probability, the
+  // resident workgroups move down the tokens together and gather the same Q
+  // and dO rows at about the same time (L2 hits instead of refetches).
+  auto hstep = [&](int k) { return n_hsteps - 1 - (k - n_own); };
+  // sparse scope: record of row 0 of history step k is rec0 + hstep(k) RS
   const size_t rec0 = SPARSE ? (size_t(pair) * L.ents_per_pair + (lst - (L.ents + size_t(pair) * L.ents_per_pair))) * G
                              : 0;
   // token of the i-th token slot of step k (-1: none); the sparse list is
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   // not a branch around a load
   auto tok_at = [&](int k, int i) -> int {
     const bool own = k < n_own;
-    const int p = own ? k * TPS + i : (k - n_own) * TPS + i;
+    const int p = own ? k * TPS + i : hstep(k) * TPS + i;
     const int lim = own ? own_n : n_hist;
     int t = own ? j0 + p : j0 + KT + p;
     if constexpr (SPARSE) {
@@ -386,13 +394,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         const int t = tkr[r];
         if (t >= 0) {
           bf16_t* dst = MK ? a.dso + (hrow0 + size_t(r % G) * N + t) * KT
-                           : a.dsr + (rec0 + size_t(kcur - n_own) * RS + r) * KT;
+                           : a.dsr + (rec0 + size_t(hstep(kcur)) * RS + r) * KT;
           *reinterpret_cast<uint4*>(dst + c8 * 8) = v;
         }
       }
       if (!MK && tid < RS && tkr[tid] >= 0) {
         const float db = dbs_sh[tid] + dbs_sh[RS + tid] + dbs_sh[2 * RS + tid] + dbs_sh[3 * RS + tid];
-        a.dbl[rec0 + size_t(kcur - n_own) * RS + tid] = db;
+        a.dbl[rec0 + size_t(hstep(kcur)) * RS + tid] = db;
       }
     }
   };
