@@ -526,6 +526,35 @@ def ste_gate_attention(q, k, v, do, s, idx, block, scale):
 
 
 # ----------------------------------------------------------------------------
+# Dense prefill (inference, no gate)
+# ----------------------------------------------------------------------------
+
+def causal_attention(q, k, v, scale):
+    """Plain causal attention of a prompt, no gate: o_t = softmax over j <= t of
+    scale * q_t . k_j, times v ([Blog] 问题动机, attention over the full
+    context; [Blog] 方法核心, kernel paragraph: the serving path prefills
+    densely and decodes sparsely).
+
+    q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; query head h reads KV head h // G.
+    Returns (o [B,Hq,N,D], lse [B,Hq,N]) in float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, N, D = q.shape
+    G = Hq // k.shape[1]
+    o = np.zeros((B, Hq, N, D))
+    lse = np.zeros((B, Hq, N))
+    future = np.triu(np.ones((N, N), dtype=bool), k=1)
+    for b in range(B):
+        for h in range(Hq):
+            z = scale * (q[b, h] @ k[b, h // G].T)
+            z[future] = NEG_INF
+            l = _logsumexp(z, axis=-1)
+            o[b, h] = np.exp(z - l[:, None]) @ v[b, h // G]
+            lse[b, h] = l
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
 # a8: sparse decode attention (inference, no gate)
 # ----------------------------------------------------------------------------
 

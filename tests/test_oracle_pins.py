@@ -901,3 +901,35 @@ def test_ste_gate_against_autograd(topk):
     np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(ds, st.grad.numpy(), atol=1e-11)
     assert np.any(ds[0, :, :, :][np.broadcast_to(np.arange(C)[None, None, :], ds.shape[1:]) < 3] != 0)
+
+
+# ---------------------------------------------------------------------------
+# Dense prefill
+# ---------------------------------------------------------------------------
+
+def test_causal_attention_is_library_causal_sdpa():
+    """The prefill oracle against the library's causal attention (fp64), and
+    against the gated forward at one history block (which is dense causal)."""
+    r = rng(21)
+    B, Hq, Hkv, N, D = 2, 4, 2, 37, 8
+    q = r.standard_normal((B, Hq, N, D))
+    k = r.standard_normal((B, Hkv, N, D))
+    v = r.standard_normal((B, Hkv, N, D))
+    o, lse = orc.causal_attention(q, k, v, 0.4)
+    for b in range(B):
+        ref = causal_sdpa(torch.tensor(q[b]), torch.tensor(k[b]), torch.tensor(v[b]), 0.4, is_causal=True)
+        np.testing.assert_allclose(o[b], ref.numpy(), atol=1e-12)
+        # lse by its definition through the library's logsumexp
+        G = Hq // Hkv
+        for h in range(Hq):
+            z = 0.4 * torch.tensor(q[b, h]) @ torch.tensor(k[b, h // G]).T
+            z = z.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+            np.testing.assert_allclose(lse[b, h], torch.logsumexp(z, dim=-1).numpy(), rtol=1e-12)
+    # N = 2 b: every query has at most one history block, whose gate is 1
+    block = 16
+    q2, k2, v2 = q[:, :, : 2 * block], k[:, :, : 2 * block], v[:, :, : 2 * block]
+    s = orc.block_scores(q2, orc.pool_block_keys(k2, block), block, 0.4, np.broadcast_to(np.arange(2 * block), (B, 2 * block)))
+    og, lg, _ = orc.gated_attention_forward(q2, k2, v2, s, None, block, 0.4)
+    o2, l2 = orc.causal_attention(q2, k2, v2, 0.4)
+    np.testing.assert_allclose(og, o2, atol=1e-12)
+    np.testing.assert_allclose(lg, l2, rtol=1e-12)
