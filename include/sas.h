@@ -89,7 +89,8 @@ typedef enum {
   SAS_OP_PAGED_DECODE = 7,
   SAS_OP_FWD_GATE = 8,   /* sas_gated_attn_fwd_gate, any gate */
   SAS_OP_BWD_GATE = 9,   /* sas_gated_attn_bwd_gate, any gate */
-  SAS_OP_DECODE_STEP = 10 /* sas_decode_step */
+  SAS_OP_DECODE_STEP = 10, /* sas_decode_step */
+  SAS_OP_PREFILL = 11      /* sas_prefill_paged (n_or_lmax = N, topk ignored) */
 } sas_op;
 
 /* Gate activation of the gated attention (blog 方法核心, the ablation table's
@@ -380,6 +381,39 @@ int sas_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                      float* lse, int32_t* idx_out, int B, int Hq, int Hkv, int D,
                      int block, float scale, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * sas_prefill_paged -- the dense prefill of a serving engine that then decodes
+ *   sparsely (blog 方法核心, kernel paragraph: dense prefill, sparse decode;
+ *   review "Our Perspective", Strengths: paged KV cache): plain causal
+ *   attention over each prompt (no gate: every key at or before the row), and
+ *   the prompt's keys and values written into the pages of its blocks with the
+ *   pooled key (mean of the block's keys, taken in fp32) of every complete
+ *   block, ready for sas_paged_decode.
+ * q:          [B,Hq,N,D]; k, v [B,Hkv,N,D]: the prompts, padded to N tokens.
+ * seq_len:    int32 [B] on the device: prompt lengths (above N counts as N;
+ *             <= 0: nothing is written to the pages of that sequence).
+ * o:          [B,Hq,N,D] output; rows t < seq_len[b] hold the attention
+ *             output (rows of padding tokens hold finite values of no meaning).
+ * lse:        optional fp32 [B,Hq,N] output (log-sum-exp of each row's logits).
+ * k_pages, v_pages [num_pages,Hkv,block,D], kbar_pages [num_pages,Hkv,D] and
+ *             block_table int32 [B,max_blocks] as for sas_paged_decode; the
+ *             entries for blocks m <= (seq_len[b] - 1) / block must be valid
+ *             page indices (not checked).  Rows t < seq_len[b] are written to
+ *             row t % block of page block_table[b, t / block]; kbar_pages is
+ *             written for the complete blocks only (a partial last block is
+ *             pooled with sas_pool_pages once it fills during decode).
+ * workspace:  sas_workspace_bytes(SAS_OP_PREFILL, B, Hq, Hkv, N, D, block, 0,
+ *             dtype) bytes, contents ignored.
+ * Errors: SAS_EINVAL (pointers, sizes, N > max_blocks * block), SAS_EUNSUPPORTED
+ *         (D outside {64, 128}), SAS_EWORKSPACE.
+ */
+int sas_prefill_paged(const void* q, const void* k, const void* v,
+                      const int32_t* seq_len, void* o, float* lse,
+                      void* k_pages, void* v_pages, void* kbar_pages,
+                      const int32_t* block_table, int max_blocks, int B, int Hq,
+                      int Hkv, int N, int D, int block, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sas_selector_bwd -- gradient of the mean-pool selector score for an upstream

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
                           "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
-                          "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_decode_step", "sas_workspace_bytes",
+                          "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes",
                           "sas_last_error", "sas_abi_version", "sas_profile_enable",
                           "sas_profile_read"}
     for n in names:
@@ -273,3 +273,19 @@ def test_decode_step_validation_on_the_host():
     assert call(d, d, d, d, d, 16, d, N, N, 2, 8, 2, 4096, 128, 64, f(-1.0), sas.SAS_BF16, d, 1 << 40,
                 N) == sas.SAS_EINVAL
     assert call(d, d, d, d, d, 16, d, N, N, 0, 8, 2, 4096, 128, 64, f(0.1), sas.SAS_BF16, N, 0, N) == sas.SAS_OK
+
+
+def test_prefill_validation_on_the_host():
+    vp = ctypes.c_void_p
+    d = vp(256)
+    f = ctypes.c_float
+    need = sas.sas_workspace_bytes(sas.SAS_OP_PREFILL, 2, 8, 2, 640, 128, 64, 0, sas.SAS_BF16)
+    assert 0 < need < (1 << 30)
+    call = L.sas_prefill_paged
+    args = (d, d, d, d, d, N, d, d, d, d)
+    assert call(*args, 10, 2, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, d, need - 1, N) == sas.SAS_EWORKSPACE
+    assert call(*args, 9, 2, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, d, need + (1 << 20), N) == sas.SAS_EINVAL
+    assert call(*args, 10, 2, 8, 2, 640, 96, 64, f(0.1), sas.SAS_BF16, d, need, N) == sas.SAS_EUNSUPPORTED
+    assert call(N, d, d, d, d, N, d, d, d, d, 10, 2, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, d, 1 << 40,
+                N) == sas.SAS_EINVAL
+    assert call(*args, 10, 0, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, N, 0, N) == sas.SAS_OK

@@ -99,7 +99,20 @@ def test_decode_entry_points_deterministic():
     ws = sas.workspace(sas.SAS_OP_PAGED_DECODE, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
     _twice(lambda: sas.sas_paged_decode(q, kp, vp, kbp, table, lens, topk, o, lse, block, w.scale, idx_out=idx,
                                         workspace=ws), [o, lse, idx])
-    # the fused step on the contiguous cache
+    # the dense prefill into pages
+    N = 640
+    qp, kq, vq = (torch.randn((B, h, N, D), generator=torch.Generator(device=DEV).manual_seed(5 + h), device=DEV)
+                  .to(torch.bfloat16) for h in (Hq, Hkv, Hkv))
+    seq = torch.tensor([N, 600, 130, 1], dtype=torch.int32, device=DEV)
+    tab2 = torch.arange(B * 10, dtype=torch.int32, device=DEV).reshape(B, 10)
+    kp2 = torch.zeros((B * 10, Hkv, block, D), dtype=torch.bfloat16, device=DEV)
+    vp2, kb2 = torch.zeros_like(kp2), torch.zeros((B * 10, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    op = torch.empty_like(qp)
+    lp = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    wsp = sas.workspace(sas.SAS_OP_PREFILL, B, Hq, Hkv, N, D, block, 0, sas.SAS_BF16)
+    _twice(lambda: sas.sas_prefill_paged(qp, kq, vq, seq, op, lp, kp2, vp2, kb2, tab2, block, w.scale, wsp),
+           [op, lp, kp2, vp2, kb2])
+    # the one-call step on the contiguous cache
     wsd = sas.workspace(sas.SAS_OP_DECODE_STEP, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
     _twice(lambda: sas.sas_decode_step(q, step.kbar, kc, vc, lens, topk, o, lse, block, w.scale, idx_out=idx,
                                        workspace=wsd), [o, lse, idx])

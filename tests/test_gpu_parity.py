@@ -615,3 +615,106 @@ def test_decode_step_parity(case):
     sas.sas_decode_step(qd, kbd, kcd, vcd, lensd, topk, o2, lse2, block, w.scale, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o2, o) and torch.equal(lse2, lse)
+
+
+PREFILL_CASES = [
+    # name, dtype, Hq, Hkv, D, N, block, max_blocks, seq_len, topk
+    ("bf16-g4", "bf16", 8, 2, 128, 640, 64, 14, [640, 600, 130], 3),
+    ("bf16-g5-d64", "bf16", 10, 2, 64, 320, 64, 6, [320, 64, 63], 2),
+    ("f32-block32", "f32", 4, 1, 64, 200, 32, 8, [200, 33, 1], 2),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_then_paged_decode(case):
+    """Dense prefill of ragged prompts into a shuffled page pool, then decode
+    from those pages: the prefill's o and lse against the oracle's causal
+    attention (valid rows), the pages and their pooled keys against the prompt
+    and the oracle's pooling, then one decode step of a new token (its K and V
+    appended to its page the way a caller does, its page pooled when that
+    completes a block) through sas_paged_decode, checked as in the paged test."""
+    name, dts, Hq, Hkv, D, N, block, maxb, lens_l, topk = case
+    dt = _dt(dts)
+    B = len(lens_l)
+    w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, None, index=13)
+    q, k, v, _ = training_inputs(w, device="cpu")
+    seq = torch.tensor(lens_l, dtype=torch.int32)
+    n_pages = B * maxb + 3
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(9))
+    table = perm[: B * maxb].reshape(B, maxb).to(torch.int32)
+    kp = torch.zeros((n_pages, Hkv, block, D), dtype=dt, device=DEV)
+    vp = torch.zeros_like(kp)
+    kbp = torch.zeros((n_pages, Hkv, D), dtype=dt, device=DEV)
+    o = torch.full((B, Hq, N, D), float("nan"), dtype=dt, device=DEV)
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=DEV)
+    sdt = sas.SAS_BF16 if dt == torch.bfloat16 else sas.SAS_F32
+    ws = sas.workspace(sas.SAS_OP_PREFILL, B, Hq, Hkv, N, D, block, 0, sdt)
+    tbd = table.to(DEV)
+    sas.sas_prefill_paged(q.to(DEV), k.to(DEV), v.to(DEV), seq.to(DEV), o, lse, kp, vp, kbp, tbd, block, w.scale, ws)
+    torch.cuda.synchronize()
+    tol = tolerances(dt)
+    for b in range(B):
+        n = lens_l[b]
+        o_ref, lse_ref = orc.causal_attention(to64(q[b:b + 1, :, :n]), to64(k[b:b + 1, :, :n]),
+                                              to64(v[b:b + 1, :, :n]), w.scale)
+        if tol["o_abs"] is not None:
+            max_abs(to64(o[b:b + 1, :, :n]), o_ref, tol["o_abs"], "prefill o")
+        else:
+            normwise(to64(o[b:b + 1, :, :n]), o_ref, tol["o_rel"], "prefill o")
+        normwise(to64(lse[b:b + 1, :, :n]), lse_ref, 1e-4, "prefill lse")
+        assert torch.isfinite(o[b]).all()
+        # pages hold the prompt's rows exactly; complete blocks hold their pooled keys
+        kpc, vpc = kp.cpu(), vp.cpu()
+        for m in range((n + block - 1) // block):
+            rows = min(block, n - m * block)
+            pg = int(table[b, m])
+            assert torch.equal(kpc[pg, :, :rows], k[b, :, m * block:m * block + rows])
+            assert torch.equal(vpc[pg, :, :rows], v[b, :, m * block:m * block + rows])
+        nfull = n // block
+        if nfull:
+            kbar_ref = to64(torch.tensor(orc.pool_block_keys(to64(k[b:b + 1, :, : nfull * block]), block)).to(dt))
+            got = to64(kbp[table[b, :nfull].long()].permute(1, 0, 2))[None]
+            kbar_close(got, kbar_ref)
+    if dt != torch.bfloat16:
+        return  # the paged decode is bf16 only
+    # One decode step: a new token per sequence at position seq_len[b].
+    gen = torch.Generator().manual_seed(77)
+    qn = torch.randn((B, Hq, D), generator=gen).to(dt)
+    kn = torch.randn((B, Hkv, D), generator=gen).to(dt)
+    vn = torch.randn((B, Hkv, D), generator=gen).to(dt)
+    kc = torch.zeros((B, Hkv, maxb * block, D), dtype=dt)
+    vc = torch.zeros_like(kc)
+    for b in range(B):
+        n = lens_l[b]
+        kc[b, :, :n], vc[b, :, :n] = k[b, :, :n], v[b, :, :n]
+        kc[b, :, n], vc[b, :, n] = kn[b], vn[b]
+        pg = int(table[b, n // block])
+        kp[pg, :, n % block] = kn[b].to(DEV)  # the caller appends the new token to its page
+        vp[pg, :, n % block] = vn[b].to(DEV)
+        if (n + 1) % block == 0:  # the append completes a block: pool that page
+            sas.sas_pool_pages(kp, kbp, torch.tensor([pg], dtype=torch.int32, device=DEV), block)
+    lens = seq + 1
+    L = maxb * block
+    od = torch.empty((B, Hq, D), dtype=dt, device=DEV)
+    lsed = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=DEV)
+    wsd = sas.workspace(sas.SAS_OP_PAGED_DECODE, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
+    sas.sas_paged_decode(qn.to(DEV), kp, vp, kbp, tbd, lens.to(DEV), topk, od, lsed, block, w.scale, idx_out=idx,
+                         workspace=wsd)
+    torch.cuda.synchronize()
+    C = maxb
+    kbar_r = np.zeros((B, Hkv, C, D))
+    for b in range(B):
+        nfull = (lens_l[b] + 1) // block
+        if nfull:
+            kbar_r[b, :, :nfull] = to64(torch.tensor(orc.pool_block_keys(to64(kc[b:b + 1, :, : nfull * block]),
+                                                                         block)).to(dt))[0]
+    u_ref = orc.decode_scores(to64(qn), kbar_r, lens.numpy(), L, block, w.scale, True)
+    u_gpu = wsd[: B * Hkv * C * 4].view(torch.float32).reshape(B, Hkv, C).cpu().numpy()
+    normwise(u_gpu.astype(np.float64), u_ref.astype(np.float64), 1e-5, "u")
+    c = orc.decode_candidates(lens.numpy(), L, block)
+    idx_ref = orc.topk_select(u_gpu[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), "Top-K on the decode's own scores"
+    o_ref, lse_ref = orc.sparse_decode(to64(qn), to64(kc), to64(vc), lens.numpy(), idx_ref, block, w.scale)
+    max_abs(to64(od), o_ref, 2e-2, "decode o")
+    normwise(to64(lsed), lse_ref, 1e-4, "decode lse")

@@ -28,11 +28,12 @@ SAS_OP_SCORE, SAS_OP_TOPK, SAS_OP_FWD, SAS_OP_BWD, SAS_OP_DECODE, SAS_OP_SELECTO
 SAS_OP_PAGED_DECODE = 7
 SAS_OP_FWD_GATE, SAS_OP_BWD_GATE = 8, 9
 SAS_OP_DECODE_STEP = 10
+SAS_OP_PREFILL = 11
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
 EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
-            "sas_sparse_decode_noalloc", "sas_decode_step", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
+            "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -45,6 +46,7 @@ _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode_noalloc.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
 _lib.sas_decode_step.argtypes = [_vp] * 5 + [_i, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_prefill_paged.argtypes = [_vp] * 10 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_selector_bwd.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_pool_pages.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
 _lib.sas_paged_decode.argtypes = [_vp] * 5 + [_i, _vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
@@ -59,7 +61,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
               "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
-              "sas_sparse_decode_noalloc", "sas_decode_step"):
+              "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged"):
     getattr(_lib, _name).restype = _i
 
 
@@ -295,3 +297,15 @@ def sas_decode_step(q, kbar, k_cache, v_cache, cache_len, topk, o, lse, block, s
     _check(_lib.sas_decode_step(_p(q), _p(kbar), _p(k_cache), _p(v_cache), _p(cache_len), topk, _p(o), _p(lse),
                                 _p(idx_out), B, Hq, Hkv, L, D, block, scale, _dt(q), _p(workspace), wsb,
                                 _stream(stream)))
+
+
+def sas_prefill_paged(q, k, v, seq_len, o, lse, k_pages, v_pages, kbar_pages, block_table, block, scale,
+                      workspace=None, stream=None):
+    """q [B,Hq,N,D]; k, v [B,Hkv,N,D]; seq_len int32 [B]; pages [P,Hkv,block,D]; kbar_pages [P,Hkv,D];
+    block_table int32 [B,max_blocks]: dense causal attention of the prompts, and their pages filled."""
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_prefill_paged(_p(q), _p(k), _p(v), _p(seq_len), _p(o), _p(lse), _p(k_pages), _p(v_pages),
+                                  _p(kbar_pages), _p(block_table), block_table.shape[1], B, Hq, Hkv, N, D, block,
+                                  scale, _dt(q), _p(workspace), wsb, _stream(stream)))

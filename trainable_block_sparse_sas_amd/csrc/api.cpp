@@ -118,6 +118,9 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
     case SAS_OP_SELECTOR_BWD:
       if (D != 64 && D != 128) return size_t(-1);
       return sas::selector_bwd_workspace(d, bf16);
+    case SAS_OP_PREFILL:
+      if (D != 64 && D != 128) return size_t(-1);
+      return sas::fwd_dense_workspace(d, bf16) + sas::align_up(size_t(B) * Hq * n * sizeof(float));
     case SAS_OP_PAGED_DECODE:
     case SAS_OP_DECODE_STEP:
       if (topk < 0) return size_t(-1);
@@ -429,6 +432,37 @@ int sas_decode_step(const void* q, const void* kbar, const void* k_cache, const 
   hipError_t e = decode_chain(q, kbar, k_cache, v_cache, cache_len, nullptr, topk, o, lse, idx_out, B, Hq, Hkv,
                               L_max, D, block, scale, dtype == SAS_BF16, workspace, static_cast<hipStream_t>(stream));
   return hip_status(e, "sas_decode_step");
+}
+
+int sas_prefill_paged(const void* q, const void* k, const void* v, const int32_t* seq_len, void* o, float* lse,
+                      void* k_pages, void* v_pages, void* kbar_pages, const int32_t* block_table, int max_blocks,
+                      int B, int Hq, int Hkv, int N, int D, int block, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_common(B, Hq, Hkv, N, D, block, dtype, "sas_prefill_paged");
+  if (!st) st = check_scale(scale, "sas_prefill_paged");
+  if (st) return st;
+  if (max_blocks < 0) return fail(SAS_EINVAL, "sas_prefill_paged: max_blocks must be >= 0");
+  if (size_t(N) > size_t(max_blocks) * size_t(block))
+    return fail(SAS_EINVAL, "sas_prefill_paged: N (%d) exceeds the table's capacity max_blocks * block (%d * %d)", N,
+                max_blocks, block);
+  if (empty(B, Hq, N)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !k || !v || !seq_len || !o || !k_pages || !v_pages || !kbar_pages || !block_table)
+    return fail(SAS_EINVAL, "sas_prefill_paged: every pointer except lse must be non-NULL");
+  sas::Dims d{B, Hq, Hkv, N, D, block, N / block};
+  const bool bf16 = dtype == SAS_BF16;
+  const size_t fws = sas::fwd_dense_workspace(d, bf16);
+  const size_t need = fws + (lse ? 0 : sas::align_up(size_t(B) * Hq * N * sizeof(float)));
+  if (!workspace || workspace_bytes < need)
+    return fail(SAS_EWORKSPACE, "sas_prefill_paged: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* lse_out = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + fws);
+  hipError_t e = sas::launch_prefill_pages(k, v, seq_len, block_table, k_pages, v_pages, kbar_pages, B, Hkv, N, D,
+                                           block, max_blocks, bf16, s);
+  if (e == hipSuccess) e = sas::launch_fwd_dense(q, k, v, o, lse_out, d, scale, bf16, workspace, s);
+  return hip_status(e, "sas_prefill_paged");
 }
 
 int sas_selector_bwd(const void* q, const void* kbar, const float* ds, void* dq, void* dk,

@@ -41,6 +41,9 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
                            int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s);
 
 hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s);
+hipError_t launch_fwd_mfma_shared_row(const void* q, const void* k, const void* v, const float* score_row,
+                                      const float* lse_s, void* o, float* lse, const Dims& d, float scale,
+                                      void* ws, hipStream_t s);
 
 bool bwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t bwd_mfma_workspace(const Dims& d, int topk, bool sparse);
@@ -245,6 +248,35 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   float* delta = static_cast<float*>(ws);
   return launch_bwd_simt(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk,
                          scale, bf16, gate, delta, s);
+}
+
+// Plain causal attention over N tokens (prefill: no gate; every key at or
+// before the row with bias 0): the full-scope raw-gate forward with zero
+// scores and a zero LSE_s.  On the matrix cores (bf16, block 64, G in {1, 2,
+// 4, 8}, at least one block) every row reads one shared row of C zero scores;
+// otherwise the SIMT forward reads a zero [B, Hq, N, C] score tensor.
+// Workspace: the forward's own workspace, the zero scores, the zero LSE_s.
+size_t fwd_dense_workspace(const Dims& d, bool bf16) {
+  const bool mfma = bf16 && fwd_mfma_supported(d, 0, false);
+  const size_t own = mfma ? align_up(fwd_mfma_workspace(d, 0, false)) : 0;
+  const size_t zs = mfma ? size_t(d.C > 0 ? d.C : 1) : rows_of(d) * size_t(d.C > 0 ? d.C : 1);
+  return own + align_up(zs * sizeof(float)) + align_up(rows_of(d) * sizeof(float));
+}
+
+hipError_t launch_fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, const Dims& d,
+                            float scale, bool bf16, void* ws, hipStream_t s) {
+  if (d.B == 0 || d.Hq == 0 || d.N == 0) return hipSuccess;
+  const bool mfma = bf16 && fwd_mfma_supported(d, 0, false);
+  char* w = static_cast<char*>(ws);
+  const size_t own = mfma ? align_up(fwd_mfma_workspace(d, 0, false)) : 0;
+  const size_t nzs = mfma ? size_t(d.C > 0 ? d.C : 1) : rows_of(d) * size_t(d.C > 0 ? d.C : 1);
+  float* zs = reinterpret_cast<float*>(w + own);
+  float* zl = reinterpret_cast<float*>(w + own + align_up(nzs * sizeof(float)));
+  hipError_t e = launch_fill_zero(zs, nzs, s);
+  if (e == hipSuccess) e = launch_fill_zero(zl, rows_of(d), s);
+  if (e != hipSuccess) return e;
+  if (mfma) return launch_fwd_mfma_shared_row(q, k, v, zs, zl, o, lse, d, scale, ws, s);
+  return launch_fwd_simt(q, k, v, zs, nullptr, o, lse, zl, d, 0, scale, bf16, false, false, s);
 }
 
 }  // namespace sas

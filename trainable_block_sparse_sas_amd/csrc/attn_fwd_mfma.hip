@@ -50,6 +50,7 @@ struct FwdArgs {
   float* lse_s;
   int Hq, Hkv, N, C, n_tiles, n_pairs, NB;
   float scale;
+  int s_stride;  // floats between score rows: C, or 0 (every row reads one shared row)
 };
 
 // LSE_s of every query row over its history scores (the gate normaliser):
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int srow_i = lane % (16 * NSUB);
   const int s_s = srow_i >> 4, s_lr = srow_i & 15;
   const int s_t = min(t_wg0 + (wave * NSUB + s_s) * TOK_SUB + s_lr / G, N - 1);
-  const float* s_base = a.scores + ((size_t(b) * a.Hq + g * G + s_lr % G) * N + s_t) * C;
+  const float* s_base = a.scores + ((size_t(b) * a.Hq + g * G + s_lr % G) * N + s_t) * size_t(a.s_stride);
   auto kst = [&](auto tag) -> uint16_t* {
     constexpr int P = decltype(tag)::value;
     if constexpr (P == 0) return K0;
@@ -517,7 +518,7 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                            int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s) {
   FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
-            (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale};
+            (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale, d.C};
   const int G = d.G();
   if (idx != nullptr) {
     // sparse scope: the gate normaliser (norm: the softmax gate; otherwise
@@ -530,6 +531,30 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
   }
 #define SAS_FWD_CASE(DD, GG) \
   if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, norm, outer, s);
+  SAS_FWD_CASE(128, 4)
+  SAS_FWD_CASE(128, 1)
+  SAS_FWD_CASE(128, 2)
+  SAS_FWD_CASE(128, 8)
+  SAS_FWD_CASE(64, 4)
+  SAS_FWD_CASE(64, 1)
+  SAS_FWD_CASE(64, 2)
+  SAS_FWD_CASE(64, 8)
+#undef SAS_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+// Full-scope forward whose history rows all read one shared row of scores
+// (score row stride 0): with that row and lse_s zero, the raw gate's bias is
+// 0 on every history block, i.e. plain causal attention (prefill).  ws: the
+// V^T blocks (fwd_mfma_workspace).
+hipError_t launch_fwd_mfma_shared_row(const void* q, const void* k, const void* v, const float* score_row,
+                                      const float* lse_s, void* o, float* lse, const Dims& d, float scale,
+                                      void* ws, hipStream_t s) {
+  FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, score_row,
+            (bf16_t*)o, lse, const_cast<float*>(lse_s), d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale, 0};
+  const int G = d.G();
+#define SAS_FWD_CASE(DD, GG) \
+  if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, false, false, s);
   SAS_FWD_CASE(128, 4)
   SAS_FWD_CASE(128, 1)
   SAS_FWD_CASE(128, 2)

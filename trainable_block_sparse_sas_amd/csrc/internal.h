@@ -118,6 +118,18 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
                          int L_max, int D, int block, int topk, float scale, bool bf16, void* ws,
                          hipStream_t s, const int32_t* table = nullptr);
 
+// ---- prefill into a paged cache ----------------------------------------------------
+// Plain causal attention (no gate) over N tokens: the full-scope forward on
+// zero scores (see attn_dispatch.hip).
+size_t fwd_dense_workspace(const Dims& d, bool bf16);
+hipError_t launch_fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, const Dims& d,
+                            float scale, bool bf16, void* ws, hipStream_t s);
+// Rows t < seq_len[b] of k, v [B, Hkv, N, D] into the pages of their blocks
+// (table [B, max_blocks]); complete blocks' pooled keys into kbar_pages.
+hipError_t launch_prefill_pages(const void* k, const void* v, const int32_t* seq_len, const int32_t* table,
+                                void* k_pages, void* v_pages, void* kbar_pages, int B, int Hkv, int N, int D,
+                                int block, int max_blocks, bool bf16, hipStream_t s);
+
 // ---- allocation-free decode ----------------------------------------------------
 // Size of the per-GPU scratch array behind sas_sparse_decode_noalloc.
 constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
