@@ -659,8 +659,8 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
     SAS_LAUNCH("topk", (topk_kernel<1, 16>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, len_cap, rows);
   } else if (topk <= 64 && C <= 16384) {
-    // 8 waves up to 8192 candidates (16 above), PER candidates per lane: just
-    // enough for C; run length: the power of two at or above K (at least 8)
+    // 8 waves, PER candidates per lane: just enough for C; run length: the
+    // power of two at or above K (at least 8)
 #define SAS_TOPK_RUNS(PER, KP, W)                                                                     \
   SAS_LAUNCH("topk_runs", (topk_runs_kernel<PER, KP, W>), dim3(rows), dim3(64 * W), 0, s, scores, idx, \
              cache_len, Hkv, hpr, Nq, C, block, topk, len_cap)
@@ -672,7 +672,7 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
     if (C <= 2048) { SAS_TOPK_RUNS_KP(4, 8) }
     else if (C <= 4096) { SAS_TOPK_RUNS_KP(8, 8) }
     else if (C <= 8192) { SAS_TOPK_RUNS_KP(16, 8) }
-    else { SAS_TOPK_RUNS_KP(16, 16) }
+    else { SAS_TOPK_RUNS_KP(32, 8) }  // 8 waves: 16 would cap a lane at 128 registers and spill
 #undef SAS_TOPK_RUNS_KP
 #undef SAS_TOPK_RUNS
   } else {
