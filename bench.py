@@ -16,7 +16,7 @@ layer (sas_decode_step, with the separate calls timed beside it), with the
 256 MB last-level cache flushed between timed steps.  The CPU oracle is timed
 on a sample of the training step and on the whole 512K decode step.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--quick]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--quick | --decode-only | --full-only]
 """
 from __future__ import annotations
 
@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="train-32k-sparse")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the two decode workloads (one JSON line of decode results)")
+    ap.add_argument("--full-only", action="store_true",
+                    help="only the full-scope step on the training shape (one JSON line; for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device copy first (counter calibration)")
     return ap.parse_args()
@@ -539,11 +541,18 @@ def main():
     wmap = {w.name: w for w in WORKLOADS}
     w = wmap[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
     if args.decode_only:
         print(json.dumps({"decode": bench_decodes(torch, wmap)}))
         return
-    if args.copy_probe:
-        copy_probe(torch)
+    if args.full_only:
+        full = bench_train(torch, w, args.steps, args.warmup, scope_topk=None)
+        print(json.dumps({"full_scope_same_shape": {
+            "ms_step": round(full["ms_step"], 3),
+            "tflops": round((full["flops_fwd"] + full["flops_bwd"]) / (full["ms_step"] * 1e-3) / 1e12, 3),
+            "kernels_ms": {k: round(v[0], 4) for k, v in sorted(full["kernels"].items(), key=lambda kv: -kv[1][0])}}}))
+        return
     tr = bench_train(torch, w, args.steps, args.warmup)
     tflops = (tr["flops_fwd"] + tr["flops_bwd"]) / (tr["ms_step"] * 1e-3) / 1e12
     out = {

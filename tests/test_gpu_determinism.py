@@ -24,11 +24,13 @@ if torch.cuda.is_available():
 DEV = "cuda"
 
 
-def _twice(run, outs):
-    """run() writes `outs`; returns True when two runs agree bit for bit."""
+def _twice(run, outs, partial=()):
+    """run() writes `outs` (and `partial`, outputs it writes only in part, such
+    as the rows of a page pool that a prompt reaches); the two runs must agree
+    bit for bit.  `outs` are overwritten with NaN (or -7) between the runs."""
     run()
     torch.cuda.synchronize()
-    first = [o.clone() for o in outs]
+    first = [o.clone() for o in list(outs) + list(partial)]
     for o in outs:
         if o.is_floating_point():
             o.fill_(float("nan"))
@@ -36,7 +38,7 @@ def _twice(run, outs):
             o.fill_(-7)
     run()
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(zip(first, outs)):
+    for i, (a, b) in enumerate(zip(first, list(outs) + list(partial))):
         assert a.dtype == b.dtype and a.shape == b.shape
         # compare the bit patterns (NaN-safe; -0.0 and +0.0 differ)
         if a.is_floating_point():
@@ -111,7 +113,7 @@ def test_decode_entry_points_deterministic():
     lp = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
     wsp = sas.workspace(sas.SAS_OP_PREFILL, B, Hq, Hkv, N, D, block, 0, sas.SAS_BF16)
     _twice(lambda: sas.sas_prefill_paged(qp, kq, vq, seq, op, lp, kp2, vp2, kb2, tab2, block, w.scale, wsp),
-           [op, lp, kp2, vp2, kb2])
+           [op, lp], partial=[kp2, vp2, kb2])
     # the one-call step on the contiguous cache
     wsd = sas.workspace(sas.SAS_OP_DECODE_STEP, B, Hq, Hkv, L, D, block, topk, sas.SAS_BF16)
     _twice(lambda: sas.sas_decode_step(q, step.kbar, kc, vc, lens, topk, o, lse, block, w.scale, idx_out=idx,

@@ -26,6 +26,9 @@ __device__ __forceinline__ int vt_key_of_pos(int p) {
   return 32 * hh + (j < 4 ? 4 * q + j : 16 + 4 * q + j - 4);
 }
 // 16-byte chunk swizzles (conflict-free reads of 16 rows at one chunk column).
+// (A swizzle that also separates the 32-byte chunk pairs of ds_read_b64_tr_b16
+// was measured: it raised the bank-conflict count of the forward and the dQ
+// kernel and left the dK/dV kernel's unchanged, so this one stays.)
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
   return D == 128 ? (key & 15) : ((key >> 1) & 7);

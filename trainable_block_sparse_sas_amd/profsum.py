@@ -1,7 +1,11 @@
 """Summaries of rocprofv3 result databases for the text files under profiles/.
 
-  python -m trainable_block_sparse_sas_amd.profsum stats DB --cmd "..."
-      kernel-trace table: launches, average and total duration per kernel.
+  python -m trainable_block_sparse_sas_amd.profsum stats DB --cmd "..." [--by-grid]
+      kernel-trace table: launches, average and total duration per kernel
+      (per kernel and launch shape with --by-grid).
+  python -m trainable_block_sparse_sas_amd.profsum traffic-by-grid --fetch DB --write DB
+         --match decode_mfma topk_runs ... --cmd-fetch "..." --cmd-write "..."
+      HBM bytes per dispatch for every matching kernel and launch shape.
   python -m trainable_block_sparse_sas_amd.profsum traffic --fetch DB --write DB
          --kernel bwd_dkdv --workload train-32k-sparse --cmd-fetch "..." --cmd-write "..."
       HBM bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE
@@ -35,18 +39,30 @@ def short_name(name: str) -> str:
     return re.sub(r"\(.*", "", n).strip()
 
 
-def kernel_rows(db):
+def _grid(cols, r):
+    """Workgroups of a dispatch as 'x,y,z' (grid sizes are in work-items)."""
+    if "grid_x" not in cols:
+        return ""
+    gx, gy, gz = (r[cols.index(c)] for c in ("grid_x", "grid_y", "grid_z"))
+    wx = r[cols.index("workgroup_x")] if "workgroup_x" in cols else 1
+    return f"{gx // max(wx, 1)},{gy},{gz}"
+
+
+def kernel_rows(db, by_grid=False):
     con = sqlite3.connect(db)
     cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
     ni = cols.index("name") if "name" in cols else cols.index("kernel_name")
     si, ei = cols.index("start"), cols.index("end")
     for r in con.execute("select * from kernels"):
-        yield short_name(r[ni]), (r[ei] - r[si]) / 1e3  # us
+        n = short_name(r[ni])
+        if by_grid:
+            n = f"{n} [{_grid(cols, r)}]"
+        yield n, (r[ei] - r[si]) / 1e3  # us
 
 
-def stats(db, cmd):
+def stats(db, cmd, by_grid=False):
     agg = {}
-    for n, us in kernel_rows(db):
+    for n, us in kernel_rows(db, by_grid):
         a = agg.setdefault(n, [0, 0.0])
         a[0] += 1
         a[1] += us
@@ -56,7 +72,7 @@ def stats(db, cmd):
     for n, (c, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
         if t / tot < 1e-4:
             continue
-        out.append(f"| `{n[:100]}` | {c} | {t / c:.1f} | {t / 1e3:.3f} | {100 * t / tot:.1f}% |")
+        out.append(f"| `{n[:120]}` | {c} | {t / c:.1f} | {t / 1e3:.3f} | {100 * t / tot:.1f}% |")
     return "\n".join(out) + "\n"
 
 
@@ -150,12 +166,60 @@ def counters(db, cmd, match):
     return "\n".join(out) + "\n"
 
 
+def counter_by_grid(db, counter):
+    """{(kernel short name, workgroups): mean counter value per dispatch}."""
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(pmc_events)")]
+    per = {}
+    for r in con.execute("select * from pmc_events"):
+        if r[cols.index("counter_name")] != counter:
+            continue
+        key = (short_name(r[cols.index("name")]), _grid(cols, r))
+        d = per.setdefault(key, {})
+        disp = r[cols.index("dispatch_id")]
+        d[disp] = d.get(disp, 0.0) + r[cols.index("counter_value")]
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def traffic_by_grid(fetch_db, write_db, match, cmd_fetch, cmd_write):
+    """HBM bytes per dispatch of every kernel matching one of `match`, per
+    launch shape (workgroups), scaled by the copy kernel's readings."""
+    f = counter_by_grid(fetch_db, "FETCH_SIZE")
+    w = counter_by_grid(write_db, "WRITE_SIZE")
+    cf = [v for (n, _), v in f.items() if "bitwise_not" in n]
+    cw = [v for (n, _), v in w.items() if "bitwise_not" in n]
+    if len(cf) != 1 or len(cw) != 1:
+        raise SystemExit("expected one copy-probe dispatch in each database")
+    sf = COPY_BYTES / (cf[0] * 1024.0)
+    sw = COPY_BYTES / (cw[0] * 1024.0)
+    lines = ["# HBM traffic per dispatch, by kernel and launch shape", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one counter per run), each scaled by",
+             "the same counter's reading for a plain copy kernel that reads and writes 1 GiB",
+             "(bench.py --copy-probe).", "", "Commands:", "", "```", cmd_fetch, cmd_write, "```", "",
+             f"fetch scale {sf:.4f}, write scale {sw:.4f}", "",
+             "| kernel | workgroups | read bytes | written bytes | total bytes |", "|---|---|---:|---:|---:|"]
+    for (n, g) in sorted(f):
+        if not any(m in n for m in match) or (n, g) not in w:
+            continue
+        rb = f[(n, g)] * 1024.0 * sf
+        wb = w[(n, g)] * 1024.0 * sw
+        lines.append(f"| `{n[:70]}` | {g} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
     a = sub.add_parser("stats")
     a.add_argument("db")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--by-grid", action="store_true", help="one row per kernel and launch shape")
+    t = sub.add_parser("traffic-by-grid")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--match", nargs="+", required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -171,8 +235,11 @@ def main():
     if args.what == "counters":
         print(counters(args.db, args.cmd, args.match), end="")
         return
+    if args.what == "traffic-by-grid":
+        print(traffic_by_grid(args.fetch, args.write, args.match, args.cmd_fetch, args.cmd_write), end="")
+        return
     if args.what == "stats":
-        print(stats(args.db, args.cmd), end="")
+        print(stats(args.db, args.cmd, args.by_grid), end="")
     else:
         print(traffic(args.fetch, args.write, args.kernel, args.workload, args.cmd_fetch,
                       args.cmd_write), end="")
