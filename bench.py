@@ -199,6 +199,16 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     ms_wf = timed(run_step, write_flush, steps, "step_wf", tm)
     floor = timed(lambda: tiny.fill_(1.0), read_flush, steps, "floor", tm)
     ms_sep = ms if dense else timed(separate_step, read_flush, steps, "separate", tm)
+    # per-kernel durations: the library brackets each launch with HIP events on
+    # its stream (read flush before every step, as above)
+    sas.sas_profile_read()
+    sas.sas_profile_enable(True)
+    for i in range(steps):
+        read_flush(i)
+        run_step()
+    torch.cuda.synchronize()
+    sas.sas_profile_enable(False)
+    kernels = {name: t / max(cnt, 1) for name, (t, cnt) in sas.sas_profile_read().items()}
     C = w.N // w.block
     kv_blocks = C if dense else (w.topk + 1)
     kv_bytes = w.B * w.Hkv * kv_blocks * w.block * w.D * 2 * 2
@@ -210,7 +220,44 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     step_bytes = kv_bytes + kbar_bytes + qo_bytes + u_bytes
     return dict(ms_step=ms, tokens_per_s=w.B / (ms * 1e-3), kv_bytes=kv_bytes, kbar_bytes=kbar_bytes,
                 step_bytes=step_bytes, ms_step_write_flush=ms_wf, ms_event_floor=floor, ms_separate=ms_sep,
-                attend_gbs=kv_bytes / (ms * 1e-3) / 1e9)
+                attend_gbs=kv_bytes / (ms * 1e-3) / 1e9, kernels=kernels)
+
+
+def decode_traffic(kernel_substr):
+    """HBM bytes per dispatch of a decode kernel from the committed counter
+    summary (profiles/decode_hbm_traffic.md), or None."""
+    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    hits = []
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("| `") and kernel_substr in line:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                try:
+                    hits.append(float(cells[-1]))
+                except ValueError:
+                    pass
+    return int(hits[0]) if len(hits) == 1 else None
+
+
+def decode_roofline(r, w):
+    """Roofline of the decode attention kernel (the step's KV reads): the K and
+    V bytes of the attended blocks over the kernel's average HIP-event time,
+    against the 8 TB/s HBM peak; traffic from the committed FETCH/WRITE summary
+    of the same kernel instantiation (the average over the workloads that share
+    it)."""
+    ms = r["kernels"].get("decode_partial")
+    if not ms:
+        return None
+    ach = r["kv_bytes"] / (ms * 1e-3) / 1e9
+    G = w.Hq // w.Hkv
+    inst = f"decode_mfma_kernel<{w.D}, {G}, true>"
+    return {"bound": "hbm", "kernel": "decode_partial", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": decode_traffic(inst),
+            "bytes_per_launch": r["kv_bytes"], "avg_launch_ms": round(ms, 5),
+            "timing": "HIP events around each launch on its stream (includes the event-pair overhead "
+                      "of a few microseconds; the rocprofv3 kernel trace gives the bare duration)"}
 
 
 def bench_paged_decode(torch, w, steps, warmup):
@@ -309,11 +356,16 @@ def roofline(kernels, pairs, D, workload):
            "flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
            "timing": "HIP events around each launch on its stream (library kernel timing)"}
     if traffic:
-        # the measured HBM bytes over the same launch time, against 8 TB/s: the
-        # sparse-scope kernels are held by HBM rather than by the matrix cores
+        # The algorithmic work puts the kernel on the matrix-core side of the
+        # roofline (its flops per unique byte are far above the ridge point),
+        # so `bound` is "mfma".  The measured HBM bytes over the same launch
+        # time say which peak the implementation is nearer: the sparse-scope
+        # kernels re-read gathered rows and round-trip partials, and are held
+        # by HBM traffic rather than by the matrix cores.
         hbm = traffic / (ms * 1e-3) / 1e12
         out["traffic_TBps"] = round(hbm, 3)
         out["traffic_frac_of_hbm_peak"] = round(hbm * 1000.0 / PEAK_HBM_GBS, 4)
+        out["measured_limit"] = "hbm" if hbm * 1000.0 / PEAK_HBM_GBS > ach / PEAK_BF16_TFLOPS else "mfma"
     return out
 
 
@@ -461,6 +513,7 @@ def decode_entry(r, topk):
             "ms_event_pair_floor": round(r["ms_event_floor"], 4),
             "timing": "median of 50 HIP-event spans of sas_decode_step, 1 GiB read flush before each span "
                       "(each span includes the event-pair floor)",
+            "kernels_ms": {k: round(v, 5) for k, v in sorted(r["kernels"].items(), key=lambda kv: -kv[1])},
             "topk": topk}
 
 
@@ -472,6 +525,7 @@ def bench_decodes(torch, wmap):
             wd = wmap[name].with_(topk=topk)
             r = bench_decode(torch, wd, 50, 10)
             ent = decode_entry(r, topk)
+            ent["roofline"] = decode_roofline(r, wd)
             ent["paged"] = bench_paged_decode(torch, wd, 50, 10)
             dec[name][f"k{topk}"] = ent
             torch.cuda.empty_cache()
