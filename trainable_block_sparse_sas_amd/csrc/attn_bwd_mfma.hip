@@ -660,31 +660,34 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
   const int nsel = selpre[tok * (MWB + 1) + MWB];
   const int topk1 = topk + 1;
 
-  // ---- dq
+  // dbeta of slot s2: record pos[tok][s2] of the pair's list entries, head h.
+  // Lane s2 (< 64) fetches slot s2's value once; the ds loop takes it by
+  // shuffle.  The address loads go out before the dQ slot loads, so both
+  // gathers overlap.
+  const int h = int(bh % Hq) % G;
+  const float* dbp = dbl + (bh / Hq * (Hq / G) + (bh % Hq) / G) * ents_per_pair * G + h;
+  const uint32_t* ps = pos + tok * topk;
+  const uint32_t pl = lane < nsel ? ps[lane] : 0u;
+
+  // ---- dq: the slot loads of up to 16 slots per round trip
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(dqp) + row * size_t(topk1) * LPS + lane % LPS;
     float a0 = 0.f, a1 = 0.f;
-    int s2 = lane / LPS;
-    for (; s2 + 3 * SG < nsel; s2 += 4 * SG) {
-      uint32_t w[4];
+    constexpr int U = 16;
+    // the own block's slot first, then the selected slots s2 = lane / LPS + SG j
+    uint32_t wo = lane < LPS ? src[size_t(topk) * LPS] : 0u;
+    for (int s0 = lane / LPS; s0 < nsel; s0 += U * SG) {
+      uint32_t w[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = src[size_t(s2 + u * SG) * LPS];
+      for (int u = 0; u < U; ++u) w[u] = s0 + u * SG < nsel ? src[size_t(s0 + u * SG) * LPS] : 0u;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         a0 += bf16_lo(w[u]);
         a1 += bf16_hi(w[u]);
       }
     }
-    for (; s2 < nsel; s2 += SG) {
-      const uint32_t w = src[size_t(s2) * LPS];
-      a0 += bf16_lo(w);
-      a1 += bf16_hi(w);
-    }
-    if (lane < LPS) {
-      const uint32_t w = src[size_t(topk) * LPS];
-      a0 += bf16_lo(w);
-      a1 += bf16_hi(w);
-    }
+    a0 += bf16_lo(wo);
+    a1 += bf16_hi(wo);
     if (SG == 2) {
       a0 += shfl_xor(a0, 32);
       a1 += shfl_xor(a1, 32);
@@ -693,13 +696,9 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
   }
 
   // ---- ds
-  // dbeta of slot s2: record pos[tok][s2] of the pair's list entries, head h
-  const int h = int(bh % Hq) % G;
-  const float* dbp = dbl + (bh / Hq * (Hq / G) + (bh % Hq) / G) * ents_per_pair * G + h;
-  const uint32_t* ps = pos + tok * topk;
-  auto dbeta = [&](int s2) -> float { return dbp[size_t(ps[s2]) * G]; };
-  float tot = 0.f;
-  for (int s2 = lane; s2 < nsel; s2 += 64) tot += dbeta(s2);
+  const float dbl_lane = lane < nsel ? dbp[size_t(pl) * G] : 0.f;
+  float tot = dbl_lane;
+  for (int s2 = lane + 64; s2 < nsel; s2 += 64) tot += dbp[size_t(ps[s2]) * G];
   for (int off = 32; off >= 1; off >>= 1) tot += shfl_xor(tot, off);
   const float ls = lse_s[row];
   const float* srow = scores + row * C;
@@ -718,27 +717,27 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
     }
     const int excl = run + incl - cnt;
     run += __shfl(incl, 63, 64);
+    // dbeta of this lane's 8 blocks; the shuffles run with every lane active
+    // (a lane reading an inactive lane's register would get 0)
+    float dbv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s2 = excl + __popc(b8 & ((1u << i) - 1u));
+      const float sh = __shfl(dbl_lane, s2 & 63, 64);
+      dbv[i] = ((b8 >> i) & 1u) ? (s2 < 64 ? sh : dbp[size_t(ps[s2]) * G]) : 0.f;
+    }
     float out[8];
     if (col0 < c && vec && col0 + 8 <= C) {
       const float4 sa = *reinterpret_cast<const float4*>(srow + col0);
       const float4 sb = *reinterpret_cast<const float4*>(srow + col0 + 4);
       const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool sel = (b8 >> i) & 1u;
-        const float dbv = sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f;
-        out[i] = col0 + i < c ? gate_ds(GATE, dbv, sv[i] - ls, tot) : 0.f;
-      }
+      for (int i = 0; i < 8; ++i) out[i] = col0 + i < c ? gate_ds(GATE, dbv[i], sv[i] - ls, tot) : 0.f;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m2 = col0 + i;
-        float v = 0.f;
-        if (m2 < c) {
-          const bool sel = (b8 >> i) & 1u;
-          v = gate_ds(GATE, sel ? dbeta(excl + __popc(b8 & ((1u << i) - 1u))) : 0.f, srow[m2] - ls, tot);
-        }
-        out[i] = v;
+        out[i] = m2 < c ? gate_ds(GATE, dbv[i], srow[m2] - ls, tot) : 0.f;
       }
     }
     if (vec && col0 + 8 <= C) {
