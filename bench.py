@@ -302,14 +302,13 @@ def bench_paged_decode(torch, w, steps, warmup):
 
 # Algorithmic work of the matrix-core kernels per attended (query row, key)
 # pair: the forward's S = QK^T and PV (4D flops; fwd_sel at sparse scope,
-# fwd_mfma at full scope); at sparse scope the dQ kernel's dS K over the dS the
-# dK/dV kernel recorded (2D; bwd_dq_ds), at full scope its S and dP recompute
-# plus dS K (6D; bwd_dq); the dK/dV kernel's S and dP recompute plus P^T dO
-# and dS^T Q (8D).
-KERNEL_FLOPS_PER_PAIR = {"fwd_sel": 4, "fwd_mfma": 4, "bwd_dq_ds": 2, "bwd_dq": 6, "bwd_dkdv": 8}
+# fwd_mfma at full scope); the dK/dV kernel's S and dP recompute plus P^T dO
+# and dS^T Q (8D), and at sparse scope also the rows' dQ shares dS K (2D); at
+# full scope the dQ kernel's S and dP recompute plus dS K (6D; bwd_dq).
+KERNEL_FLOPS_PER_PAIR = {"fwd_sel": 4, "fwd_mfma": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+SPARSE_KERNEL_FLOPS_PER_PAIR = dict(KERNEL_FLOPS_PER_PAIR, bwd_dkdv=10)
 KERNEL_SOURCES = {"fwd_sel": "attn_fwd_sel.hip", "fwd_mfma": "attn_fwd_mfma.hip",
-                  "bwd_dq_ds": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
-                  "bwd_dkdv": "attn_bwd_mfma.hip"}
+                  "bwd_dq": "attn_bwd_mfma.hip", "bwd_dkdv": "attn_bwd_mfma.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -342,12 +341,13 @@ def measured_traffic(kernel, workload):
         return None
 
 
-def roofline(kernels, pairs, D, workload):
+def roofline(kernels, pairs, D, workload, sparse=True):
     """Roofline entry for the kernel with the largest share of the step."""
-    name = max((k for k in kernels if k in KERNEL_FLOPS_PER_PAIR),
+    per_pair = SPARSE_KERNEL_FLOPS_PER_PAIR if sparse else KERNEL_FLOPS_PER_PAIR
+    name = max((k for k in kernels if k in per_pair),
                key=lambda k: kernels[k][0] * kernels[k][1])
     ms = kernels[name][0]
-    flops = KERNEL_FLOPS_PER_PAIR[name] * D * pairs
+    flops = per_pair[name] * D * pairs
     ach = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(name, workload)
     out = {"bound": "mfma", "kernel": name, "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,

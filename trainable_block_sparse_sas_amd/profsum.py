@@ -30,8 +30,7 @@ import sqlite3
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 KERNEL_SOURCES = {"fwd_sel": "attn_fwd_sel.hip", "fwd_mfma": "attn_fwd_mfma.hip",
-                  "bwd_dq_ds": "attn_bwd_mfma.hip", "bwd_dq": "attn_bwd_mfma.hip",
-                  "bwd_dkdv": "attn_bwd_mfma.hip"}
+                  "bwd_dq": "attn_bwd_mfma.hip", "bwd_dkdv": "attn_bwd_mfma.hip"}
 
 
 def short_name(name: str) -> str:
