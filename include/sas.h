@@ -55,7 +55,10 @@
  *   on `stream` (a hipStream_t; NULL is the null stream): inputs must stay
  *   valid and outputs untouched until the stream reaches that point.  The
  *   library allocates no memory; calls that need scratch take a caller
- *   workspace of at least sas_workspace_bytes() bytes.  No call keeps a
+ *   workspace of at least sas_workspace_bytes() bytes.  A workspace carries
+ *   nothing from one call to the next, so calls enqueued in order on one
+ *   stream may share one buffer of the largest size they need (the sparse
+ *   forward and backward of a training step, for instance).  No call keeps a
  *   pointer after it returns.  Calls are thread-safe (the error string is
  *   thread-local).  Sizes of zero (B, Hq, N or L_max) are valid and do nothing.
  */

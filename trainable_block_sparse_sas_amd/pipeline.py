@@ -35,8 +35,12 @@ class TrainStep:
         self.dv = torch.empty((B, Hkv, N, D), dtype=dtype, device=dev)
         self.ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=dev)
         tk = -1 if topk is None else topk
-        self.ws_fwd = sas.workspace(sas.SAS_OP_FWD, B, Hq, Hkv, N, D, block, tk, sdt, dev)
-        self.ws_bwd = sas.workspace(sas.SAS_OP_BWD, B, Hq, Hkv, N, D, block, tk, sdt, dev)
+        # one scratch buffer for both calls: they run in stream order and a
+        # workspace carries nothing from one call to the next
+        n_ws = max(sas.sas_workspace_bytes(op, B, Hq, Hkv, N, D, block, tk, sdt)
+                   for op in (sas.SAS_OP_FWD, sas.SAS_OP_BWD))
+        self.ws = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws else None
+        self.ws_fwd = self.ws_bwd = self.ws
 
     def select(self, q, k):
         sas.sas_score_blocks(q, k, self.kbar, self.scores, None, self.block, self.scale)
