@@ -136,6 +136,23 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
                      int dtype, void* stream);
 
 /*
+ * sas_score_blocks_lse -- the training-mode sas_score_blocks (cache_len NULL,
+ *   group_sum 0, Nq = L = N) that also writes the softmax gate's normaliser
+ *   LSE_s(t) = log sum_{m < c(t)} exp(s[t,m]) per query row (review "Why the
+ *   Four Design Choices Matter": log g = s - LSE(s); -inf for rows without
+ *   history), so that the forward need not read the scores a second time for
+ *   it (sas_gated_attn_fwd_lse).
+ * lse_s:   fp32 [B,Hq,N] output.  With bf16 and block % 16 == 0 the score
+ *          kernel computes it from the scores it writes (fp32 running max and
+ *          sum per row); otherwise a pass over the written scores does.  It
+ *          matches the lse_s of sas_gated_attn_fwd up to fp32 summation order.
+ * Other arguments and errors: as sas_score_blocks.
+ */
+int sas_score_blocks_lse(const void* q, const void* k, void* kbar, float* scores,
+                         float* lse_s, int B, int Hq, int Hkv, int N, int D,
+                         int block, float scale, int dtype, void* stream);
+
+/*
  * sas_topk_select -- hard Top-K over each row's history blocks (review
  *   "Background", paper Eq. 3; training selection per query token and KV
  *   head; review "A Concrete Walkthrough" Step 3 and Step 6).
@@ -187,6 +204,21 @@ int sas_gated_attn_fwd(const void* q, const void* k, const void* v,
                        float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
                        int D, int block, int topk, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sas_gated_attn_fwd_lse -- sas_gated_attn_fwd with LSE_s given: lse_s
+ *   (fp32 [B,Hq,N], e.g. from sas_score_blocks_lse on the same scores) is an
+ *   input and is only read; the forward skips its own pass over the scores
+ *   for it.  o and lse as sas_gated_attn_fwd; same workspace
+ *   (SAS_OP_FWD) and errors.  Passing an LSE_s that does not belong to
+ *   `scores` gives the attention of a different gate (no check is made).
+ */
+int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v,
+                           const float* scores, const int32_t* idx,
+                           const float* lse_s, void* o, float* lse, int B,
+                           int Hq, int Hkv, int N, int D, int block, int topk,
+                           float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * sas_gated_attn_bwd -- gradients of the forward for an upstream dO

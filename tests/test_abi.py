@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert set(names) == {"sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd",
+    assert set(names) == {"sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select",
+                          "sas_gated_attn_fwd", "sas_gated_attn_fwd_lse",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
                           "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
                           "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes",
@@ -35,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 103
+    assert sas.sas_abi_version() == 104
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
@@ -289,3 +290,28 @@ def test_prefill_validation_on_the_host():
     assert call(N, d, d, d, d, N, d, d, d, d, 10, 2, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, d, 1 << 40,
                 N) == sas.SAS_EINVAL
     assert call(*args, 10, 0, 8, 2, 640, 128, 64, f(0.1), sas.SAS_BF16, N, 0, N) == sas.SAS_OK
+
+
+def test_fused_gate_normaliser_validation_on_the_host():
+    """sas_score_blocks_lse and sas_gated_attn_fwd_lse: argument checks run
+    before any launch (no call here reaches the GPU)."""
+    d = ctypes.c_void_p(256)
+    f = ctypes.c_float
+    call = L.sas_score_blocks_lse
+    # lse_s missing, scale invalid, head dims unsupported, Hq % Hkv != 0
+    assert call(d, N, d, d, N, 1, 4, 2, 256, 128, 64, f(0.1), sas.SAS_BF16, N) == sas.SAS_EINVAL
+    assert "lse_s" in sas.sas_last_error()
+    assert call(d, N, d, d, d, 1, 4, 2, 256, 128, 64, f(-1.0), sas.SAS_BF16, N) == sas.SAS_EINVAL
+    assert call(d, N, d, d, d, 1, 4, 2, 256, 96, 64, f(0.1), sas.SAS_BF16, N) == sas.SAS_EUNSUPPORTED
+    assert call(d, N, d, d, d, 1, 5, 2, 256, 128, 64, f(0.1), sas.SAS_BF16, N) == sas.SAS_EINVAL
+    # empty sizes are no-ops even with NULL tensors
+    assert call(N, N, N, N, N, 0, 4, 2, 256, 128, 64, f(0.1), sas.SAS_BF16, N) == sas.SAS_OK
+    fwd = L.sas_gated_attn_fwd_lse
+    need = sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 8, 2, 512, 128, 64, 4, sas.SAS_BF16)
+    assert need > 0
+    assert fwd(d, d, d, d, d, d, d, d, 1, 8, 2, 512, 128, 64, 4, f(0.1), sas.SAS_BF16, d, need - 1,
+               N) == sas.SAS_EWORKSPACE
+    assert fwd(d, d, d, d, d, N, d, d, 1, 8, 2, 512, 128, 64, 4, f(0.1), sas.SAS_BF16, d, need,
+               N) == sas.SAS_EINVAL
+    assert fwd(d, d, d, d, d, d, d, d, 1, 8, 2, 512, 128, 64, 300, f(0.1), sas.SAS_BF16, d, 1 << 40,
+               N) == sas.SAS_EUNSUPPORTED

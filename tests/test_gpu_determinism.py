@@ -52,9 +52,10 @@ def test_training_entry_points_deterministic(topk):
     w = Workload("det", "train", "bf16", 1, 8, 2, 128, 4672, 64, topk, index=21)
     q, k, v, do = training_inputs(w, device=DEV)
     step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, topk, torch.bfloat16)
-    sel_outs = [step.kbar, step.scores] + ([] if topk is None else [step.idx])
-    _twice(lambda: step.select(q, k), sel_outs)
-    _twice(lambda: step.forward(q, k, v), [step.o, step.lse, step.lse_s])
+    sel_outs = [step.kbar, step.scores, step.lse_s] + ([] if topk is None else [step.idx])
+    _twice(lambda: step.select(q, k), sel_outs)  # scores and the gate normaliser LSE_s
+    _twice(lambda: step.forward(q, k, v), [step.o, step.lse])  # LSE_s given (an input)
+    _twice(lambda: step.forward(q, k, v, step.scores), [step.o, step.lse, step.lse_s])  # LSE_s computed
     _twice(lambda: step.backward(q, k, v, do), [step.dq, step.dk, step.dv, step.ds])
     # the gate variants
     B, Hq, Hkv, N, D, C = w.B, w.Hq, w.Hkv, w.N, w.D, w.C

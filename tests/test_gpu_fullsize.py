@@ -105,8 +105,15 @@ def test_training_fullsize(wi):
     s32 = _oracle_scores_f32(q64, kbar_r, w.block, w.scale)
     rows = _sample_rows(w.N, w.block)
     # GPU scores from the oracle's pooled keys, sampled rows.
-    sas.sas_score_blocks(q, None, torch.tensor(kbar_r).to(dt).to(DEV), step.scores, None, w.block, w.scale)
+    kbar_dev = torch.tensor(kbar_r).to(dt).to(DEV)
+    sas.sas_score_blocks(q, None, kbar_dev, step.scores, None, w.block, w.scale)
+    # the same scores through the score kernel that also writes LSE_s
+    s_lse = torch.empty_like(step.scores)
+    lse_s_sc = torch.empty_like(step.lse_s)
+    sas.sas_score_blocks_lse(q, None, kbar_dev, s_lse, lse_s_sc, w.block, w.scale)
     torch.cuda.synchronize()
+    assert torch.equal(s_lse[:, :, rows], step.scores[:, :, rows]), "scores (score kernel with LSE_s)"
+    del s_lse
     normwise(to64(step.scores[:, :, rows]), s32[:, :, rows].astype(np.float64), 1e-5, "scores")
     scores = torch.tensor(s32).to(DEV)
     idx = None
@@ -134,6 +141,7 @@ def test_training_fullsize(wi):
     _rowwise(to64(step.o[:, :, rows]), o_ref, 2e-2, "o per row")
     normwise(to64(step.lse[:, :, rows]), lse_ref, 1e-4, "lse")
     normwise(to64(step.lse_s[:, :, rows]), lses_ref, 1e-4, "lse_s")
+    normwise(to64(lse_s_sc[:, :, rows]), lses_ref, 1e-4, "lse_s (score kernel)")
     _ds_invariants(step, scores, idx, G, w)
     for h in (0, w.Hq // 2 + 1, w.Hq - 1):
         dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, w.block, w.scale, 0, h, rows)

@@ -112,6 +112,42 @@ def test_training_parity(case):
     normwise(to64(step.ds), ds, tol["ds"], "ds")
 
 
+@pytest.mark.parametrize("case", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
+def test_fused_gate_normaliser(case):
+    """The training step's own path: sas_score_blocks_lse writes the scores of
+    sas_score_blocks bit for bit plus the gate normaliser LSE_s (jaehun.me
+    review, "Why the Four Design Choices Matter": log g = s - LSE(s)), and
+    sas_gated_attn_fwd_lse on them matches the oracle forward on the same
+    scores and indices.  LSE_s: fp32 running max and exp sum with the hardware
+    exp2 and log, a few ulps: 1e-5 normwise."""
+    name, dts, B, Hq, Hkv, D, N, block, topk = case
+    dt = _dt(dts)
+    w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=11)
+    q, k, v, _ = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    scale = w.scale
+    tol = tolerances(dt)
+    step = TrainStep(B, Hq, Hkv, N, D, block, topk, dt)
+    step.lse_s.fill_(float("nan"))
+    step.select(q, k)
+    s2 = torch.full_like(step.scores, float("nan"))
+    sas.sas_score_blocks(q, None, step.kbar, s2, None, block, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, step.scores), "scores differ from sas_score_blocks"
+    s64 = to64(step.scores)
+    idx = None if topk is None else step.idx.cpu().numpy()
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale)
+    normwise(to64(step.lse_s), lses_ref, 1e-5, "lse_s")
+    lse_s_in = step.lse_s.clone()
+    step.forward(q, k, v)  # the step's own scores: the forward with LSE_s given
+    torch.cuda.synchronize()
+    assert torch.equal(step.lse_s, lse_s_in), "lse_s is an input of the forward"
+    if tol["o_abs"] is not None:
+        max_abs(to64(step.o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(step.o), o_ref, tol["o_rel"], "o")
+    normwise(to64(step.lse), lse_ref, tol["lse"], "lse")
+
+
 TOPK_CASES = [
     # C, hpr, training(1)-or-None(decode), topk
     (40, 4, 1, 5),

@@ -31,15 +31,18 @@ SAS_OP_DECODE_STEP = 10
 SAS_OP_PREFILL = 11
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
-EXPORTED = ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
+EXPORTED = ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
+            "sas_gated_attn_fwd_lse", "sas_gated_attn_bwd",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
             "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.sas_score_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+_lib.sas_score_blocks_lse.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _vp]
 _lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_fwd_lse.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
@@ -59,7 +62,8 @@ _lib.sas_profile_enable.restype = _i
 _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
-for _name in ("sas_score_blocks", "sas_topk_select", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
+for _name in ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
+              "sas_gated_attn_fwd_lse", "sas_gated_attn_bwd",
               "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
               "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged"):
     getattr(_lib, _name).restype = _i
@@ -176,6 +180,15 @@ def sas_score_blocks(q, k, kbar, scores, cache_len, block, scale, group_sum=Fals
                                  _stream(stream)))
 
 
+def sas_score_blocks_lse(q, k, kbar, scores, lse_s, block, scale, stream=None):
+    """Training scores (q [B,Hq,N,D], k [B,Hkv,N,D] or None, kbar [B,Hkv,C,D],
+    scores fp32 [B,Hq,N,C]) and the gate normaliser lse_s fp32 [B,Hq,N]."""
+    B, Hq, N, D = q.shape
+    Hkv = kbar.shape[1]
+    _check(_lib.sas_score_blocks_lse(_p(q), _p(k), _p(kbar), _p(scores), _p(lse_s), B, Hq, Hkv, N, D,
+                                     block, scale, _dt(q), _stream(stream)))
+
+
 def sas_topk_select(scores, idx, cache_len, heads_per_row, block, workspace=None, stream=None):
     """scores fp32 [B, Hkv*hpr, Nq, C] (decode: [B, Hkv*hpr, C]); idx int32 [B,Hkv,Nq,K] / [B,Hkv,K]."""
     if cache_len is None:
@@ -199,6 +212,18 @@ def sas_gated_attn_fwd(q, k, v, scores, idx, o, lse, lse_s, block, scale, worksp
     _check(_lib.sas_gated_attn_fwd(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(o), _p(lse),
                                    _p(lse_s), B, Hq, Hkv, N, D, block, topk, scale, _dt(q),
                                    _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_fwd_lse(q, k, v, scores, idx, lse_s, o, lse, block, scale, workspace=None,
+                           stream=None):
+    """The forward with LSE_s given (lse_s is an input, e.g. from sas_score_blocks_lse)."""
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    _check(_lib.sas_gated_attn_fwd_lse(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(lse_s), _p(o),
+                                       _p(lse), B, Hq, Hkv, N, D, block, topk, scale, _dt(q),
+                                       _p(workspace), wsb, _stream(stream)))
 
 
 def sas_gated_attn_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, block, scale,

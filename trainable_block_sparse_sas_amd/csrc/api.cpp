@@ -98,7 +98,7 @@ extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 103; }
+int sas_abi_version(void) { return 104; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
@@ -174,6 +174,29 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
   return hip_status(e, "sas_score_blocks");
 }
 
+int sas_score_blocks_lse(const void* q, const void* k, void* kbar, float* scores, float* lse_s, int B,
+                         int Hq, int Hkv, int N, int D, int block, float scale, int dtype, void* stream) {
+  const char* what = "sas_score_blocks_lse";
+  int st = check_common(B, Hq, Hkv, N, D, block, dtype, what);
+  if (!st) st = check_scale(scale, what);
+  if (st) return st;
+  const int C = N / block;
+  if (empty(B, Hq, N) && !(k && B > 0 && C > 0)) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!q || !kbar || !scores || !lse_s) return fail(SAS_EINVAL, "%s: q, kbar, scores and lse_s must be non-NULL", what);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SAS_BF16;
+  if (k) {
+    hipError_t e = sas::launch_pool(k, kbar, B, Hkv, N, D, block, C, bf16, s);
+    if (e != hipSuccess) return hip_status(e, "sas_score_blocks_lse (pool)");
+  }
+  if (empty(B, Hq, N)) return hip_status(hipSuccess, "");
+  sas::Dims d{B, Hq, Hkv, N, D, block, C};
+  return hip_status(sas::launch_score_train(q, kbar, scores, d, scale, false, bf16, s, lse_s), what);
+}
+
 int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,
                     int heads_per_row, int Nq, int C, int block, int topk, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -212,7 +235,7 @@ static int check_attn(const char* what, int B, int Hq, int Hkv, int N, int D, in
 static int attn_fwd(const char* what, const void* q, const void* k, const void* v, const float* scores,
                     const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
                     int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool lse_given = false) {
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
@@ -229,7 +252,7 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
   if (need && (!workspace || workspace_bytes < need))
     return fail(SAS_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", what, need, workspace_bytes);
   hipError_t e = sas::launch_fwd(q, k, v, scores, idx, o, lse, lse_s, d, idx ? topk : 0, scale,
-                                 bf16, gate, workspace, static_cast<hipStream_t>(stream));
+                                 bf16, gate, workspace, static_cast<hipStream_t>(stream), lse_given);
   return hip_status(e, what);
 }
 
@@ -268,6 +291,17 @@ int sas_gated_attn_fwd(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* stream) {
   return attn_fwd("sas_gated_attn_fwd", q, k, v, scores, idx, o, lse, lse_s, B, Hq, Hkv, N, D, block, topk,
                   scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream);
+}
+
+int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v, const float* scores,
+                           const int32_t* idx, const float* lse_s, void* o, float* lse, int B, int Hq,
+                           int Hkv, int N, int D, int block, int topk, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  // lse_s is only read (the kernels take it through the same pointer they
+  // would otherwise write it through)
+  return attn_fwd("sas_gated_attn_fwd_lse", q, k, v, scores, idx, o, lse, const_cast<float*>(lse_s), B, Hq,
+                  Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream,
+                  true);
 }
 
 int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v, const float* scores,

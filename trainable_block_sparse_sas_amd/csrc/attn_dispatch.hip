@@ -27,7 +27,7 @@ namespace sas {
 
 hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool bf16, bool norm, bool outer, hipStream_t s);
+                           int topk, float scale, bool bf16, int norm, bool outer, hipStream_t s);
 hipError_t launch_bwd_simt(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
@@ -38,9 +38,8 @@ bool fwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s);
+                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s);
 
-hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s);
 hipError_t launch_fwd_mfma_shared_row(const void* q, const void* k, const void* v, const float* score_row,
                                       const float* lse_s, void* o, float* lse, const Dims& d, float scale,
                                       void* ws, hipStream_t s);
@@ -172,7 +171,7 @@ size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s) {
+                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s, bool lse_given) {
   if (gate == kGateSte) {
     // the hard gate: plain block-sparse attention (the raw gate on zero
     // scores), then the real LSE_s for the backward's soft gate
@@ -194,9 +193,11 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
     if (e != hipSuccess) return e;
     if (sp) scores = sp;
   }
+  // gate normaliser: 0 none (lse_s holds 0), 1 computed here, 2 given in lse_s
+  const int nm = !norm ? 0 : lse_given ? 2 : 1;
   if (bf16 && fwd_mfma_supported(d, topk, idx != nullptr))
-    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, ws, s);
-  return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, norm, outer, s);
+    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, nm, outer, ws, s);
+  return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, nm, outer, s);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -276,7 +277,7 @@ hipError_t launch_fwd_dense(const void* q, const void* k, const void* v, void* o
   if (e == hipSuccess) e = launch_fill_zero(zl, rows_of(d), s);
   if (e != hipSuccess) return e;
   if (mfma) return launch_fwd_mfma_shared_row(q, k, v, zs, zl, o, lse, d, scale, ws, s);
-  return launch_fwd_simt(q, k, v, zs, nullptr, o, lse, zl, d, 0, scale, bf16, false, false, s);
+  return launch_fwd_simt(q, k, v, zs, nullptr, o, lse, zl, d, 0, scale, bf16, 0, false, s);
 }
 
 }  // namespace sas

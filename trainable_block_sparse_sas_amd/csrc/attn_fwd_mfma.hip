@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_mfma_kernel(FwdArgs a) {
 }
 
 template <int D, int G>
-hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, bool outer, hipStream_t stream) {
+hipError_t fwd_mfma_t(const FwdArgs& a0, int B, int norm, bool outer, hipStream_t stream) {
   constexpr int NSUB = 2;
   constexpr int WAVES = 8;
   constexpr int NST = 2;
@@ -470,7 +470,7 @@ hipError_t fwd_mfma_t(const FwdArgs& a0, int B, bool norm, bool outer, hipStream
   a.n_tiles = (a.N + TOK_WG - 1) / TOK_WG;
   a.n_pairs = B * a.Hkv;
   const size_t rows = size_t(B) * a.Hq * a.N;
-  if (norm)
+  if (norm == 1)
     SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, a.scores,
                a.lse_s, a.N, a.C, KT, rows);
   SAS_LAUNCH("vt", (vt_kernel<D>), dim3(a.NB, a.Hkv, B), dim3(256), 0, stream, a.v,
@@ -516,15 +516,15 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool norm, bool outer, void* ws, hipStream_t s) {
+                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s) {
   FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
             (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale, d.C};
   const int G = d.G();
   if (idx != nullptr) {
-    // sparse scope: the gate normaliser (norm: the softmax gate; otherwise
-    // lse_s already holds 0), then the key-major forward
+    // sparse scope: the gate normaliser (norm 1: the softmax gate's, computed
+    // here; 2: given; 0: lse_s already holds 0), then the key-major forward
     const size_t rows = size_t(d.B) * d.Hq * d.N;
-    if (norm)
+    if (norm == 1)
       SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
                  d.N, d.C, KT, rows);
     return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, outer, ws, s);

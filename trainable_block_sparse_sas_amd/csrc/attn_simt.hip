@@ -85,10 +85,10 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
   const float* srow = scores + row * C;
   const bool full = (idx == nullptr);
 
-  // LSE of the row's history scores (the softmax gate's normaliser; the other
-  // gates have none: 0, already in lse_s).
+  // LSE of the row's history scores (the softmax gate's normaliser; norm 2:
+  // given in lse_s; the other gates have none: 0, already in lse_s).
   float mx = kNegInf, sm = 0.f;
-  for (int m = p; norm && m < c; m += 4) {
+  for (int m = p; norm == 1 && m < c; m += 4) {
     const float x = srow[m];
     const float nm = fmaxf(mx, x);
     sm = sm * exp_hw(mx - nm) + exp_hw(x - nm);
@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(
       mx = nm;
     }
   }
-  const float lses = !norm ? 0.f : c > 0 ? mx + log_hw(sm) : kNegInf;
-  if (norm && rv && p == 0) lse_s[row] = lses;
+  const float lses = norm == 2 ? (rv ? lse_s[row] : 0.f) : !norm ? 0.f : c > 0 ? mx + log_hw(sm) : kNegInf;
+  if (norm == 1 && rv && p == 0) lse_s[row] = lses;
 
   const int MW = (C + 31) / 32;
   uint32_t* mask = dyn_mask + r * MW;
@@ -398,12 +398,12 @@ __global__ __launch_bounds__(128) void bwd_dkdv_simt_kernel(
 template <typename T, int D>
 hipError_t fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                     const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d, int topk,
-                    float scale, bool norm, bool outer, hipStream_t s) {
+                    float scale, int norm, bool outer, hipStream_t s) {
   const size_t mask_bytes = idx ? size_t(64) * ((d.C + 31) / 32) * 4 : 0;
   dim3 grid((d.N + 63) / 64, d.Hq, d.B);
   SAS_LAUNCH("fwd_simt", (fwd_simt_kernel<T, D>), grid, dim3(256), mask_bytes, s, (const T*)q,
                      (const T*)k, (const T*)v, scores, idx, (T*)o, lse, lse_s, d.Hq, d.Hkv, d.N,
-                     d.C, d.block, topk, scale, int(norm), int(outer));
+                     d.C, d.block, topk, scale, norm, int(outer));
   return hipGetLastError();
 }
 
@@ -431,7 +431,7 @@ hipError_t bwd_simt(const void* q, const void* k, const void* v, const void* o, 
 
 hipError_t launch_fwd_simt(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, bool bf16, bool norm, bool outer, hipStream_t s) {
+                           int topk, float scale, bool bf16, int norm, bool outer, hipStream_t s) {
   if (bf16) {
     if (d.D == 64) return fwd_simt<bf16_t, 64>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);
     return fwd_simt<bf16_t, 128>(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, norm, outer, s);

@@ -48,8 +48,12 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // ---- selector: pooling and scores -------------------------------------------
 hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, int block,
                        int C, bool bf16, hipStream_t s);
+// lse_s (optional, not with group_sum): also the softmax gate's LSE_s per row.
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
-                              float scale, bool group_sum, bool bf16, hipStream_t s);
+                              float scale, bool group_sum, bool bf16, hipStream_t s,
+                              float* lse_s = nullptr);
+// LSE_s of every row over its history scores (any dtype: reads the fp32 scores).
+hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s);
 // table (bf16 only): pooled key m of sequence b is row table[b * C + m] of
 // kbar [num_pages, Hkv, D].
 hipError_t launch_score_decode(const void* q, const void* kbar, float* scores,
@@ -96,9 +100,12 @@ size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
+// lse_given (softmax gate only): lse_s already holds LSE_s; it is read, not
+// computed.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s);
+                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s,
+                      bool lse_given = false);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* scores, const int32_t* idx,
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,

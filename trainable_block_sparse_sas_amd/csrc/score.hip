@@ -117,10 +117,16 @@ __global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ 
 // one head (16 per wave; the rows of a wave share one block when block % 16 == 0)
 // and walks the blocks in chunks of 64 staged in LDS.  Chunks at or beyond a
 // wave's own block are not computed, only filled with -inf.
+// lse_s (optional): the softmax gate's normaliser LSE_s(t) = log sum over the
+// history blocks m < c(t) of exp(s[t,m]) (jaehun.me review, "Why the Four
+// Design Choices Matter": log g = s - LSE(s)), -inf without history.  Each
+// lane keeps a running (max, sum of exp) of its columns for its four rows;
+// the 16 lanes of a row group merge theirs at the end.
 template <int D>
 __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __restrict__ q,
                                                                const bf16_t* __restrict__ kbar,
-                                                               float* __restrict__ out, int Hq,
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ lse_s, int Hq,
                                                                int Hkv, int N, int C, int block,
                                                                float scale) {
   constexpr int KS = D / 32, CH = D / 8;
@@ -145,6 +151,11 @@ __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __r
     const int t = t0 + 4 * lq + i;
     orow[i] = t < N ? out + ((size_t(b) * Hq + h) * N + t) * C : nullptr;
   }
+  float lmx[4], lsm[4];
+  for (int i = 0; i < 4; ++i) {
+    lmx[i] = kNegInf;
+    lsm[i] = 0.f;
+  }
   for (int m0 = 0; m0 < C; m0 += 64) {
     const bool load = m0 < c_max;  // uniform: some wave of the group computes here
     if (load) {
@@ -167,10 +178,29 @@ __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __r
           const uint4 bf = *reinterpret_cast<const uint4*>(&ks[16 * nt + lr][k2 * 32 + lq * 8]);
           acc = mfma16(qa[k2], bf, acc);
         }
+        if (lse_s != nullptr && m < c)
+          for (int i = 0; i < 4; ++i) {
+            const float x = acc[i] * scale;
+            const float nm = fmaxf(lmx[i], x);
+            lsm[i] = lsm[i] * exp2_hw((lmx[i] - nm) * kLog2e) + exp2_hw((x - nm) * kLog2e);
+            lmx[i] = nm;
+          }
       }
       if (m < C)
         for (int i = 0; i < 4; ++i)
           if (orow[i]) orow[i][m] = m < c ? acc[i] * scale : kNegInf;
+    }
+  }
+  if (lse_s != nullptr) {
+    for (int i = 0; i < 4; ++i) {
+      for (int off = 1; off < 16; off <<= 1) {
+        const float om = shfl_xor(lmx[i], off), os = shfl_xor(lsm[i], off);
+        const float nm = fmaxf(lmx[i], om);
+        if (nm != kNegInf) lsm[i] = lsm[i] * exp2_hw((lmx[i] - nm) * kLog2e) + os * exp2_hw((om - nm) * kLog2e);
+        lmx[i] = nm;
+      }
+      const int t = t0 + 4 * lq + i;
+      if (lr == 0 && t < N) lse_s[(size_t(b) * Hq + h) * N + t] = c > 0 ? lmx[i] + log_hw(lsm[i]) : kNegInf;
     }
   }
 }
@@ -361,16 +391,17 @@ static void score_train_t(const void* q, const void* kbar, float* scores, const 
 }
 
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
-                              float scale, bool group_sum, bool bf16, hipStream_t s) {
-  if (d.N == 0 || d.B == 0 || d.C == 0) return hipSuccess;
+                              float scale, bool group_sum, bool bf16, hipStream_t s, float* lse_s) {
+  if (d.N == 0 || d.B == 0) return hipSuccess;
+  if (d.C == 0) return lse_s ? launch_lse_rows(scores, lse_s, d, s) : hipSuccess;  // rows without history
   if (bf16 && !group_sum && d.block % 16 == 0) {
     dim3 grid((d.N + 63) / 64, d.Hq, d.B);
     if (d.D == 64)
       SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
     else
       SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
     return hipGetLastError();
   }
   if (bf16) {
@@ -380,7 +411,9 @@ hipError_t launch_score_train(const void* q, const void* kbar, float* scores, co
     if (d.D == 64) score_train_t<float, 64>(q, kbar, scores, d, scale, group_sum, s);
     else score_train_t<float, 128>(q, kbar, scores, d, scale, group_sum, s);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !lse_s) return e;
+  return launch_lse_rows(scores, lse_s, d, s);  // a pass over the scores just written
 }
 
 template <int D>

@@ -1,7 +1,8 @@
 """Buffers and call sequences of the two SAS hot paths on one GPU.
 
-Training (full or sparse scope):  sas_score_blocks (pool + score)
-  -> sas_topk_select (sparse scope only) -> sas_gated_attn_fwd -> sas_gated_attn_bwd.
+Training (full or sparse scope):  sas_score_blocks_lse (pool + score + the gate
+  normaliser) -> sas_topk_select (sparse scope only) -> sas_gated_attn_fwd_lse
+  -> sas_gated_attn_bwd.
 Decode:  sas_score_blocks (group-summed scores from pooled keys kept beside the
   cache) -> sas_topk_select -> sas_sparse_decode.
 
@@ -43,15 +44,19 @@ class TrainStep:
         self.ws_fwd = self.ws_bwd = self.ws
 
     def select(self, q, k):
-        sas.sas_score_blocks(q, k, self.kbar, self.scores, None, self.block, self.scale)
+        # scores and, in the same kernel, the gate normaliser LSE_s
+        sas.sas_score_blocks_lse(q, k, self.kbar, self.scores, self.lse_s, self.block, self.scale)
         if self.idx is not None:
             sas.sas_topk_select(self.scores, self.idx, None, self.Hq // self.Hkv, self.block)
 
     def forward(self, q, k, v, scores=None, idx=None):
-        scores = self.scores if scores is None else scores
         idx = self.idx if idx is None else idx
-        sas.sas_gated_attn_fwd(q, k, v, scores, idx, self.o, self.lse, self.lse_s, self.block,
-                               self.scale, self.ws_fwd)
+        if scores is None:  # the step's own scores, whose LSE_s select() wrote
+            sas.sas_gated_attn_fwd_lse(q, k, v, self.scores, idx, self.lse_s, self.o, self.lse, self.block,
+                                       self.scale, self.ws_fwd)
+        else:
+            sas.sas_gated_attn_fwd(q, k, v, scores, idx, self.o, self.lse, self.lse_s, self.block,
+                                   self.scale, self.ws_fwd)
 
     def backward(self, q, k, v, do, scores=None, idx=None):
         scores = self.scores if scores is None else scores
