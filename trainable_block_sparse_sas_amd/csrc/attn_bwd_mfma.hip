@@ -167,20 +167,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   uint4 kq[NDW][2];
   if constexpr (SPARSE) {
     const uint16_t* kh = reinterpret_cast<const uint16_t*>(a.k) + (size_t(b) * a.Hkv + g) * size_t(N) * D;
+    // all loads first (keys clamped to N - 1), then the selects, so that the
+    // 16 NDW loads go out together
+    uint32_t h[NDW][2][8];
+#pragma unroll
+    for (int nd = 0; nd < NDW; ++nd)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          h[nd][kk][j] = kh[size_t(min(j0 + 32 * kk + 8 * (lane >> 4) + j, N - 1)) * D +
+                            16 * (NDW * wave + nd) + (lane & 15)];
 #pragma unroll
     for (int nd = 0; nd < NDW; ++nd)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int col = 16 * (NDW * wave + nd) + (lane & 15);
-        uint32_t w[4];
+        uint32_t* x = h[nd][kk];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int k0 = j0 + 32 * kk + 8 * (lane >> 4) + 2 * j;
-          const uint32_t lo = k0 < N ? kh[size_t(k0) * D + col] : 0u;
-          const uint32_t hi = k0 + 1 < N ? kh[size_t(k0 + 1) * D + col] : 0u;
-          w[j] = lo | (hi << 16);
-        }
-        kq[nd][kk] = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int j = 0; j < 8; ++j) x[j] = j0 + 32 * kk + 8 * (lane >> 4) + j < N ? x[j] : 0u;
+        kq[nd][kk] = make_uint4(x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16));
       }
   }
   f32x4 dk[ND], dv[ND];
@@ -215,16 +220,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   // sparse scope: record of row 0 of history step k is rec0 + hstep(k) RS
   const size_t rec0 = SPARSE ? (size_t(pair) * L.ents_per_pair + (lst - (L.ents + size_t(pair) * L.ents_per_pair))) * G
                              : 0;
-  // token of the i-th token slot of step k (-1: none); the sparse list is
-  // read unconditionally (a valid word for own steps) so that it is a select,
-  // not a branch around a load
-  auto tok_at = [&](int k, int i) -> int {
+  // Token of the i-th token slot of step k, in two parts.  tok_raw issues
+  // the slot's list-entry load (sparse history steps; own steps read a valid
+  // word of the workspace) and returns the word unexamined; tok_fin makes it
+  // the slot's token (-1: none).  tok_fin runs a step later, after that
+  // step's wait for its ring stage: a use of the loaded word right away would
+  // make the wave wait for the tile loads issued before it as well (vector
+  // memory operations complete in order), i.e. for the next step's tiles.
+  auto tok_raw = [&](int k, int i) -> uint32_t {
+    if constexpr (SPARSE) {
+      const bool own = k < n_own;
+      const int p = hstep(k) * TPS + i;
+      return (own ? L.ents : lst)[own ? 0 : min(max(p, 0), max(n_hist - 1, 0))];
+    } else {
+      return 0u;
+    }
+  };
+  auto tok_fin = [&](int k, int i, uint32_t e) -> int {
     const bool own = k < n_own;
     const int p = own ? k * TPS + i : hstep(k) * TPS + i;
     const int lim = own ? own_n : n_hist;
     int t = own ? j0 + p : j0 + KT + p;
     if constexpr (SPARSE) {
-      const uint32_t e = (own ? L.ents : lst)[own ? 0 : min(p, max(n_hist - 1, 0))];
       if (!own) t = int(e);  // token | rank << 23 (rank < 256: stays positive)
     }
     return p < lim ? t : -1;
@@ -449,21 +466,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   using S1 = std::integral_constant<int, 1>;
   using Own = std::integral_constant<bool, true>;
   using Hist = std::integral_constant<bool, false>;
-  int tk1 = n_steps > 0 ? tok_at(0, lane / G) : -1;  // the lane's row, step 0
-  if (n_steps > 0) issue(S0{}, 0, tk1, lane);
-  tk1 = n_steps > 1 ? tok_at(1, lane / G) : -1;      // step 1
+  // the lane's row: step 0's token, and step 1's raw list word
+  if (n_steps > 0) issue(S0{}, 0, tok_fin(0, lane / G, tok_raw(0, lane / G)), lane);
+  uint32_t raw1 = n_steps > 0 ? tok_raw(min(1, n_steps - 1), lane / G) : 0u;
   // One step on stage `tag`: wait for its rows, load step k + 1 into the
-  // other stage and fetch the tokens of step k + 2, compute.
+  // other stage and the raw list words of step k + 2 (the last step's again
+  // past the end: an unconditional load, never examined), compute.
   auto step = [&](auto tag, auto mkt, int k) {
     using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
     int ln = lane;
     asm volatile("" : "+v"(ln));
     wait_vm<0>();
     ring_barrier();
-    if (k + 1 < n_steps) issue(Pn{}, k + 1, tk1, ln);
-    const int tk2 = k + 2 < n_steps ? tok_at(k + 2, ln / G) : -1;
+    if (k + 1 < n_steps) issue(Pn{}, k + 1, tok_fin(k + 1, ln / G, raw1), ln);
+    const uint32_t raw2 = tok_raw(min(k + 2, n_steps - 1), ln / G);
     compute(tag, mkt, ln, k);
-    tk1 = tk2;
+    raw1 = raw2;
   };
   // Own-block steps (one variant per loop: no accumulator merges), then the
   // history on the stage where the first loop stopped.

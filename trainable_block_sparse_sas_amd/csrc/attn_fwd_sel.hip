@@ -140,12 +140,18 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
     // (m, l) records of the item's list entries: row q of the item is record q
     float2* stl_item = a.stl + (size_t(pair) * L.ents_per_pair + it.y) * G;
 
-    // entry of row lr of group gk: token | slot << 23 (own block: slot topk)
-    auto entry = [&](int gk, int lr) -> uint32_t {
+    // Entry of row lr of group gk: token | slot << 23 (own block: slot
+    // topk), in two parts.  entry_raw issues the list load (own items read a
+    // valid word) and returns the word unexamined; entry_fin makes the entry.
+    // The loaded word is first examined a step later, after that step's wait:
+    // examining it at once would make the wave wait for the Q tile loads
+    // issued before it as well (vector memory operations complete in order).
+    auto entry_raw = [&](int gk, int lr) -> uint32_t {
       const int p = min((16 * gk + lr) / G, ntok - 1);
-      // one load either way (own items read a valid dummy word), so the
-      // result is a select rather than a branch around a load
-      const uint32_t v = (own_item ? L.ents : ep)[own_item ? 0 : p];
+      return (own_item ? L.ents : ep)[own_item ? 0 : p];
+    };
+    auto entry_fin = [&](int gk, int lr, uint32_t v) -> uint32_t {
+      const int p = min((16 * gk + lr) / G, ntok - 1);
       return own_item ? (uint32_t(j0 + p) | (uint32_t(a.topk) << 23)) : v;
     };
     auto stg = [&](auto tag) -> uint16_t* {
@@ -162,12 +168,17 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         dma16_to_lds(a.q + qoff[j] + size_t(t) * D, st + j * 512);
       }
     };
-    // the row's gate bias in base 2 (own block: 0); OUTER: the gate g itself
-    // (own block: 1)
-    auto load_bias = [&](uint32_t e) -> float {
-      if (own_item) return OUTER ? 1.f : 0.f;
+    // The row's gate bias in base 2 (own block: 0); OUTER: the gate g itself
+    // (own block: 1).  Split like the entries: bias_raw loads (s, LSE_s),
+    // bias_fin forms the bias a step later.
+    auto bias_raw = [&](uint32_t e) -> float2 {
+      if (own_item) return make_float2(0.f, 0.f);
       const size_t gr = rbase + (e & 0x7fffffu);
-      const float lg = (a.scores[gr * C + m] - a.lse_s[gr]) * kLog2e;
+      return make_float2(a.scores[gr * C + m], a.lse_s[gr]);
+    };
+    auto bias_fin = [&](float2 r) -> float {
+      if (own_item) return OUTER ? 1.f : 0.f;
+      const float lg = (r.x - r.y) * kLog2e;
       return OUTER ? exp2_hw(lg) : lg;
     };
 
@@ -258,28 +269,33 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       *sp = make_float2(mx, l);
     };
 
-    // pipeline over this wave's groups gk = wave + WAVES k
-    uint32_t e0 = entry(wave, lane & 15);
-    uint32_t e1 = nk > 1 ? entry(wave + WAVES, lane & 15) : 0u;
+    // pipeline over this wave's groups gk = wave + WAVES k.  The raw words
+    // of group k + 1 (entry, and the bias inputs) are loaded during step k - 1
+    // and step k (unconditional loads: past the last group they repeat it,
+    // never examined) and examined at the start of step k + 1.
+    const int glast = wave + WAVES * (nk - 1);
+    uint32_t e0 = entry_fin(wave, lane & 15, entry_raw(wave, lane & 15));
+    uint32_t r1 = entry_raw(min(wave + WAVES, glast), lane & 15);
     issue(S0t{}, wave, e0, lane);
-    float b0 = load_bias(e0), b1 = b0;
+    float b0 = bias_fin(bias_raw(e0));
+    float2 br1 = make_float2(0.f, 0.f);
     wait_vm<0>();
     auto step = [&](auto tag, int k) {
       using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int gk = wave + WAVES * k;
-      uint32_t e2 = 0;
+      const uint32_t e1 = entry_fin(gk + WAVES, ln & 15, r1);
       if (k + 1 < nk) {
         issue(Pn{}, gk + WAVES, e1, ln);
-        b1 = load_bias(e1);
-        if (k + 2 < nk) e2 = entry(gk + 2 * WAVES, ln & 15);
+        br1 = bias_raw(e1);
       }
+      const uint32_t r2 = entry_raw(min(gk + 2 * WAVES, glast), ln & 15);
       compute(tag, std::true_type{}, gk, e0, b0, ln);
       wait_vm<NSTORE>();
       e0 = e1;
-      e1 = e2;
-      b0 = b1;
+      r1 = r2;
+      b0 = bias_fin(br1);
     };
     for (int k = 0; k < nk; k += 2) {
       step(S0t{}, k);
