@@ -25,7 +25,7 @@ namespace sas {
 namespace {
 
 constexpr int SEG = 512;           // tokens per segment of the count / fill passes
-constexpr int kSegsPerSpan = 8;    // segments per token span of the work items (4096 tokens)
+constexpr int kSegsPerSpan = 4;    // segments per token span of the work items (2048 tokens)
 
 // One wave per token: lane e ORs its entry's bit into the wave's words in LDS
 // (a repeated entry sets the same bit), then lane w takes word w.
