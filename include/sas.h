@@ -93,7 +93,9 @@ typedef enum {
   SAS_OP_FWD_GATE = 8,   /* sas_gated_attn_fwd_gate, any gate */
   SAS_OP_BWD_GATE = 9,   /* sas_gated_attn_bwd_gate, any gate */
   SAS_OP_DECODE_STEP = 10, /* sas_decode_step */
-  SAS_OP_PREFILL = 11      /* sas_prefill_paged (n_or_lmax = N, topk ignored) */
+  SAS_OP_PREFILL = 11,     /* sas_prefill_paged (n_or_lmax = N, topk ignored) */
+  SAS_OP_CTX = 12          /* the saved context of sas_gated_attn_fwd_ctx /
+                              sas_gated_attn_bwd_ctx (0: none is used) */
 } sas_op;
 
 /* Gate activation of the gated attention (blog 方法核心, the ablation table's
@@ -219,6 +221,46 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v,
                            int Hq, int Hkv, int N, int D, int block, int topk,
                            float scale, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * sas_gated_attn_fwd_ctx / sas_gated_attn_bwd_ctx -- a training step's forward
+ *   and backward with a saved context, as a framework keeps tensors from the
+ *   forward for the backward.  The forward is sas_gated_attn_fwd_lse (LSE_s
+ *   given); it also writes into `ctx` what the backward would otherwise
+ *   rebuild or gather again: the selection lists of idx (the per-block lists
+ *   of selecting tokens the key-major kernels walk) and, per (KV head, list
+ *   entry, query head of the group), the base-2 log gate (s - LSE_s) log2 e
+ *   of that history entry (review "Why the Four Design Choices Matter":
+ *   log g = s - LSE(s)).  The backward is sas_gated_attn_bwd for the same
+ *   inputs, reading the lists and log gates from `ctx` instead.
+ * ctx:       caller-owned device buffer of at least
+ *            sas_workspace_bytes(SAS_OP_CTX, B, Hq, Hkv, N, D, block, topk,
+ *            dtype) bytes.  That is 0 where the context is not used (full
+ *            scope, fp32, or shapes outside the matrix-core path); then ctx
+ *            may be NULL and the calls equal sas_gated_attn_fwd_lse and
+ *            sas_gated_attn_bwd.  Between the two calls the caller keeps it
+ *            unchanged and passes the same scores, idx and LSE_s (no check is
+ *            made: a context of other inputs gives wrong gradients).
+ *            Unlike a workspace, it carries data from one call to the next.
+ * Other arguments, and errors: as sas_gated_attn_fwd_lse and
+ *   sas_gated_attn_bwd; a missing or short ctx is SAS_EWORKSPACE.
+ */
+int sas_gated_attn_fwd_ctx(const void* q, const void* k, const void* v,
+                           const float* scores, const int32_t* idx,
+                           const float* lse_s, void* o, float* lse, int B,
+                           int Hq, int Hkv, int N, int D, int block, int topk,
+                           float scale, int dtype, void* ctx, size_t ctx_bytes,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+int sas_gated_attn_bwd_ctx(const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* scores,
+                           const int32_t* idx, const float* lse,
+                           const float* lse_s, const void* ctx,
+                           size_t ctx_bytes, void* dq, void* dk, void* dv,
+                           float* ds, int B, int Hq, int Hkv, int N, int D,
+                           int block, int topk, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * sas_gated_attn_bwd -- gradients of the forward for an upstream dO

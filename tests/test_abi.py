@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select",
-                          "sas_gated_attn_fwd", "sas_gated_attn_fwd_lse",
+                          "sas_gated_attn_fwd", "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx",
+                          "sas_gated_attn_bwd_ctx",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
                           "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages",
                           "sas_paged_decode", "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes",
@@ -36,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 104
+    assert sas.sas_abi_version() == 105
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
@@ -315,3 +316,28 @@ def test_fused_gate_normaliser_validation_on_the_host():
                N) == sas.SAS_EINVAL
     assert fwd(d, d, d, d, d, d, d, d, 1, 8, 2, 512, 128, 64, 300, f(0.1), sas.SAS_BF16, d, 1 << 40,
                N) == sas.SAS_EUNSUPPORTED
+
+
+def test_saved_context_sizes_and_validation_on_the_host():
+    """sas_gated_attn_fwd_ctx / _bwd_ctx: the context size, and a missing or
+    short context refused before any launch."""
+    d = ctypes.c_void_p(256)
+    f = ctypes.c_float
+    bf, f32 = sas.SAS_BF16, sas.SAS_F32
+    n = sas.sas_workspace_bytes(sas.SAS_OP_CTX, 1, 8, 2, 512, 128, 64, 4, bf)
+    assert n > 0
+    # used only at sparse scope on the matrix cores
+    assert sas.sas_workspace_bytes(sas.SAS_OP_CTX, 1, 8, 2, 512, 128, 64, -1, bf) == 0
+    assert sas.sas_workspace_bytes(sas.SAS_OP_CTX, 1, 8, 2, 512, 128, 64, 4, f32) == 0
+    assert sas.sas_workspace_bytes(sas.SAS_OP_CTX, 1, 8, 2, 512, 128, 32, 4, bf) == 0
+    wf = sas.sas_workspace_bytes(sas.SAS_OP_FWD, 1, 8, 2, 512, 128, 64, 4, bf)
+    wb = sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 8, 2, 512, 128, 64, 4, bf)
+    fwd, bwd = L.sas_gated_attn_fwd_ctx, L.sas_gated_attn_bwd_ctx
+    sizes = (1, 8, 2, 512, 128, 64, 4, f(0.1), bf)
+    assert fwd(d, d, d, d, d, d, d, d, *sizes, N, 0, d, wf, N) == sas.SAS_EWORKSPACE
+    assert "context" in sas.sas_last_error()
+    assert fwd(d, d, d, d, d, d, d, d, *sizes, d, n - 1, d, wf, N) == sas.SAS_EWORKSPACE
+    assert fwd(d, d, d, d, d, d, d, d, *sizes, d, n, d, wf - 1, N) == sas.SAS_EWORKSPACE
+    assert bwd(d, d, d, d, d, d, d, d, d, N, 0, d, d, d, d, *sizes, d, wb, N) == sas.SAS_EWORKSPACE
+    assert bwd(d, d, d, d, d, d, d, d, d, d, n - 1, d, d, d, d, *sizes, d, wb, N) == sas.SAS_EWORKSPACE
+    assert bwd(d, d, d, d, d, d, d, d, d, d, n, d, d, N, d, *sizes, d, wb, N) == sas.SAS_EINVAL

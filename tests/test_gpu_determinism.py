@@ -54,9 +54,14 @@ def test_training_entry_points_deterministic(topk):
     step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, topk, torch.bfloat16)
     sel_outs = [step.kbar, step.scores, step.lse_s] + ([] if topk is None else [step.idx])
     _twice(lambda: step.select(q, k), sel_outs)  # scores and the gate normaliser LSE_s
-    _twice(lambda: step.forward(q, k, v), [step.o, step.lse])  # LSE_s given (an input)
-    _twice(lambda: step.forward(q, k, v, step.scores), [step.o, step.lse, step.lse_s])  # LSE_s computed
-    _twice(lambda: step.backward(q, k, v, do), [step.dq, step.dk, step.dv, step.ds])
+    grads = [step.dq, step.dk, step.dv, step.ds]
+    # LSE_s computed, lists built by each call
+    _twice(lambda: step.forward(q, k, v, step.scores), [step.o, step.lse, step.lse_s])
+    _twice(lambda: step.backward(q, k, v, do, step.scores), grads)
+    # LSE_s given and the saved context (written in part: the list capacity)
+    ctx = [] if step.ctx is None else [step.ctx]
+    _twice(lambda: step.forward(q, k, v), [step.o, step.lse], partial=ctx)
+    _twice(lambda: step.backward(q, k, v, do), grads)
     # the gate variants
     B, Hq, Hkv, N, D, C = w.B, w.Hq, w.Hkv, w.N, w.D, w.C
     tk = -1 if topk is None else topk

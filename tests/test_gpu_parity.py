@@ -113,17 +113,19 @@ def test_training_parity(case):
 
 
 @pytest.mark.parametrize("case", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
-def test_fused_gate_normaliser(case):
+def test_training_step_own_path(case):
     """The training step's own path: sas_score_blocks_lse writes the scores of
     sas_score_blocks bit for bit plus the gate normaliser LSE_s (jaehun.me
-    review, "Why the Four Design Choices Matter": log g = s - LSE(s)), and
-    sas_gated_attn_fwd_lse on them matches the oracle forward on the same
-    scores and indices.  LSE_s: fp32 running max and exp sum with the hardware
-    exp2 and log, a few ulps: 1e-5 normwise."""
+    review, "Why the Four Design Choices Matter": log g = s - LSE(s));
+    sas_gated_attn_fwd_ctx on them (LSE_s given, saved context written) and
+    sas_gated_attn_bwd_ctx (lists and log gates from the context) match the
+    oracle forward and backward on the same scores and indices.  LSE_s: fp32
+    running max and exp sum with the hardware exp2 and log, a few ulps: 1e-5
+    normwise."""
     name, dts, B, Hq, Hkv, D, N, block, topk = case
     dt = _dt(dts)
     w = Workload(name, "train", dts, B, Hq, Hkv, D, N, block, topk, index=11)
-    q, k, v, _ = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
     scale = w.scale
     tol = tolerances(dt)
     step = TrainStep(B, Hq, Hkv, N, D, block, topk, dt)
@@ -138,7 +140,7 @@ def test_fused_gate_normaliser(case):
     o_ref, lse_ref, lses_ref = orc.gated_attention_forward(to64(q), to64(k), to64(v), s64, idx, block, scale)
     normwise(to64(step.lse_s), lses_ref, 1e-5, "lse_s")
     lse_s_in = step.lse_s.clone()
-    step.forward(q, k, v)  # the step's own scores: the forward with LSE_s given
+    step.forward(q, k, v)  # the step's own scores: LSE_s given, the context saved
     torch.cuda.synchronize()
     assert torch.equal(step.lse_s, lse_s_in), "lse_s is an input of the forward"
     if tol["o_abs"] is not None:
@@ -146,6 +148,13 @@ def test_fused_gate_normaliser(case):
     else:
         normwise(to64(step.o), o_ref, tol["o_rel"], "o")
     normwise(to64(step.lse), lse_ref, tol["lse"], "lse")
+    step.backward(q, k, v, do)  # from the saved context
+    torch.cuda.synchronize()
+    dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, scale)
+    normwise(to64(step.dq), dq, tol["grad"], "dq")
+    normwise(to64(step.dk), dk, tol["grad"], "dk")
+    normwise(to64(step.dv), dv, tol["grad"], "dv")
+    normwise(to64(step.ds), ds, tol["ds"], "ds")
 
 
 TOPK_CASES = [

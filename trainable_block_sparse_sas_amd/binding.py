@@ -29,10 +29,11 @@ SAS_OP_PAGED_DECODE = 7
 SAS_OP_FWD_GATE, SAS_OP_BWD_GATE = 8, 9
 SAS_OP_DECODE_STEP = 10
 SAS_OP_PREFILL = 11
+SAS_OP_CTX = 12
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
 EXPORTED = ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
-            "sas_gated_attn_fwd_lse", "sas_gated_attn_bwd",
+            "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx", "sas_gated_attn_bwd", "sas_gated_attn_bwd_ctx",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
             "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
             "sas_profile_enable", "sas_profile_read")
@@ -44,6 +45,8 @@ _lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp,
 _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd_lse.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
+_lib.sas_gated_attn_fwd_ctx.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp, _sz, _vp]
+_lib.sas_gated_attn_bwd_ctx.argtypes = [_vp] * 10 + [_sz] + [_vp] * 4 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_sparse_decode.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
@@ -63,7 +66,7 @@ _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
 for _name in ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
-              "sas_gated_attn_fwd_lse", "sas_gated_attn_bwd",
+              "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx", "sas_gated_attn_bwd", "sas_gated_attn_bwd_ctx",
               "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
               "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged"):
     getattr(_lib, _name).restype = _i
@@ -224,6 +227,34 @@ def sas_gated_attn_fwd_lse(q, k, v, scores, idx, lse_s, o, lse, block, scale, wo
     _check(_lib.sas_gated_attn_fwd_lse(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(lse_s), _p(o),
                                        _p(lse), B, Hq, Hkv, N, D, block, topk, scale, _dt(q),
                                        _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_fwd_ctx(q, k, v, scores, idx, lse_s, o, lse, block, scale, ctx, workspace=None,
+                           stream=None):
+    """The training forward with LSE_s given that also fills the saved context `ctx`
+    (a byte tensor of sas_workspace_bytes(SAS_OP_CTX, ...) bytes, or None if that is 0)."""
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    cb = 0 if ctx is None else ctx.numel()
+    _check(_lib.sas_gated_attn_fwd_ctx(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(lse_s), _p(o),
+                                       _p(lse), B, Hq, Hkv, N, D, block, topk, scale, _dt(q), _p(ctx), cb,
+                                       _p(workspace), wsb, _stream(stream)))
+
+
+def sas_gated_attn_bwd_ctx(q, k, v, o, dout, scores, idx, lse, lse_s, ctx, dq, dk, dv, ds, block, scale,
+                           workspace=None, stream=None):
+    """The backward reading the saved context the forward filled."""
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    topk = idx.shape[-1] if idx is not None else 0
+    wsb = 0 if workspace is None else workspace.numel()
+    cb = 0 if ctx is None else ctx.numel()
+    _check(_lib.sas_gated_attn_bwd_ctx(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(scores), _idx_ptr(idx),
+                                       _p(lse), _p(lse_s), _p(ctx), cb, _p(dq), _p(dk), _p(dv), _p(ds), B, Hq,
+                                       Hkv, N, D, block, topk, scale, _dt(q), _p(workspace), wsb,
+                                       _stream(stream)))
 
 
 def sas_gated_attn_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, block, scale,

@@ -98,7 +98,7 @@ extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 104; }
+int sas_abi_version(void) { return 105; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
@@ -131,6 +131,8 @@ size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int blo
     case SAS_OP_BWD_GATE:
       return std::max(sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_SIGMOID),
                       sas::bwd_gate_workspace(d, topk, bf16, SAS_GATE_STE));
+    case SAS_OP_CTX:
+      return sas::train_ctx_bytes(d, topk, bf16);
     default:
       return size_t(-1);
   }
@@ -232,10 +234,13 @@ static int check_attn(const char* what, int B, int Hq, int Hkv, int N, int D, in
   return SAS_OK;
 }
 
+constexpr size_t kNoCtx = size_t(-1);  // ctx_bytes of the calls without a saved context
+
 static int attn_fwd(const char* what, const void* q, const void* k, const void* v, const float* scores,
                     const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
                     int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
-                    size_t workspace_bytes, void* stream, bool lse_given = false) {
+                    size_t workspace_bytes, void* stream, bool lse_given = false, void* ctx = nullptr,
+                    size_t ctx_bytes = kNoCtx) {
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
@@ -251,8 +256,14 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
   const size_t need = sas::fwd_gate_workspace(d, idx ? topk : -1, bf16, gate);
   if (need && (!workspace || workspace_bytes < need))
     return fail(SAS_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", what, need, workspace_bytes);
+  if (ctx_bytes != kNoCtx) {  // a call with a saved context
+    const size_t cneed = sas::train_ctx_bytes(d, idx ? topk : -1, bf16);
+    if (cneed && (!ctx || ctx_bytes < cneed))
+      return fail(SAS_EWORKSPACE, "%s: saved context of %zu bytes required (got %zu)", what, cneed, ctx_bytes);
+    if (!cneed) ctx = nullptr;
+  }
   hipError_t e = sas::launch_fwd(q, k, v, scores, idx, o, lse, lse_s, d, idx ? topk : 0, scale,
-                                 bf16, gate, workspace, static_cast<hipStream_t>(stream), lse_given);
+                                 bf16, gate, workspace, static_cast<hipStream_t>(stream), lse_given, ctx);
   return hip_status(e, what);
 }
 
@@ -260,7 +271,8 @@ static int attn_bwd(const char* what, const void* q, const void* k, const void* 
                     const void* dout, const float* scores, const int32_t* idx, const float* lse,
                     const float* lse_s, void* dq, void* dk, void* dv, float* ds, int B, int Hq, int Hkv,
                     int N, int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, const void* ctx = nullptr,
+                    size_t ctx_bytes = kNoCtx) {
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
@@ -279,9 +291,15 @@ static int attn_bwd(const char* what, const void* q, const void* k, const void* 
   const size_t need = sas::bwd_gate_workspace(d, idx ? topk : -1, bf16, gate);
   if (need && (!workspace || workspace_bytes < need))
     return fail(SAS_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", what, need, workspace_bytes);
+  if (ctx_bytes != kNoCtx) {  // a call with a saved context
+    const size_t cneed = sas::train_ctx_bytes(d, idx ? topk : -1, bf16);
+    if (cneed && (!ctx || ctx_bytes < cneed))
+      return fail(SAS_EWORKSPACE, "%s: saved context of %zu bytes required (got %zu)", what, cneed, ctx_bytes);
+    if (!cneed) ctx = nullptr;
+  }
   hipError_t e = sas::launch_bwd(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d,
                                  idx ? topk : 0, scale, bf16, gate, workspace,
-                                 static_cast<hipStream_t>(stream));
+                                 static_cast<hipStream_t>(stream), ctx);
   return hip_status(e, what);
 }
 
@@ -304,6 +322,15 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v, const fl
                   true);
 }
 
+int sas_gated_attn_fwd_ctx(const void* q, const void* k, const void* v, const float* scores,
+                           const int32_t* idx, const float* lse_s, void* o, float* lse, int B, int Hq,
+                           int Hkv, int N, int D, int block, int topk, float scale, int dtype, void* ctx,
+                           size_t ctx_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd("sas_gated_attn_fwd_ctx", q, k, v, scores, idx, o, lse, const_cast<float*>(lse_s), B, Hq,
+                  Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream,
+                  true, ctx, ctx_bytes);
+}
+
 int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v, const float* scores,
                             const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq,
                             int Hkv, int N, int D, int block, int topk, float scale, int dtype, int gate,
@@ -320,6 +347,17 @@ int sas_gated_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        void* stream) {
   return attn_bwd("sas_gated_attn_bwd", q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, B, Hq,
                   Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream);
+}
+
+int sas_gated_attn_bwd_ctx(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* scores, const int32_t* idx,
+                           const float* lse, const float* lse_s, const void* ctx, size_t ctx_bytes,
+                           void* dq, void* dk, void* dv, float* ds, int B, int Hq, int Hkv, int N, int D,
+                           int block, int topk, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_bwd("sas_gated_attn_bwd_ctx", q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, B, Hq,
+                  Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream,
+                  ctx, ctx_bytes);
 }
 
 int sas_gated_attn_bwd_gate(const void* q, const void* k, const void* v, const void* o,

@@ -62,6 +62,8 @@ struct BwdArgs {
   uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
   bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: dQ share per slot (sparse)
   float* dbl;        // workspace [pairs, list entries, G]: dbeta per list entry and head (sparse)
+  const float* lg2;  // optional [pairs, list entries, G]: base-2 log gate per list entry and head,
+                     // saved by the forward (sparse; else the scores and LSE_s give it)
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
   int gate;          // gate activation (kGateSoftmax, kGateSigmoid, kGateRaw)
@@ -300,10 +302,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       const int r = ln;  // stat `wave` of row r
       const int t = tk;
       const size_t gr = srow + (t >= 0 ? tok_of(t) : 0);
-      // (own-block rows use no score; they read lse there, which always exists)
+      // slot 2 of a history row: its saved base-2 log gate (the record of
+      // row r of the step, as for dbeta), else its score (slot 3: LSE_s).
+      // Own-block rows use neither; they read lse there, which always exists.
+      const float* s2 = a.lg2 != nullptr ? a.lg2 + rec0 + (t >= 0 ? size_t(hstep(k)) * RS + r : 0)
+                                         : a.scores + gr * C + m;
       const float* src = wave == 0 ? a.lse + gr
                        : wave == 1 ? a.delta + gr
-                       : wave == 2 ? (phase == 1 ? a.scores + gr * C + m : a.lse + gr)
+                       : wave == 2 ? (phase == 1 ? s2 : a.lse + gr)
                                    : a.lse_s + gr;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + ST_F + wave * RS * 2), 4, 0, 0);
       if (wave == 0) tok_sh[P][r] = t;
@@ -356,14 +362,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       float p[4], d[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // base-2 logit offset: bias - lse
-        const float off = (MK || OUTER) ? -lv[i] * kLog2e : (sv[i] - ls[i] - lv[i]) * kLog2e;
+        // base-2 log gate of a history row, then the base-2 logit offset:
+        // bias - lse
+        const float lg = a.lg2 != nullptr ? sv[i] : (sv[i] - ls[i]) * kLog2e;
+        const float off = (MK || OUTER) ? -lv[i] * kLog2e : lg - lv[i] * kLog2e;
         float x = fmaf(sacc[rs][i], c1, off);
         const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
         x = ok ? x : kNegInf;
         p[i] = exp2_hw(x);
         if constexpr (OUTER && !MK) {
-          const float gf = ok ? exp2_hw((sv[i] - ls[i]) * kLog2e) : 0.f;
+          const float gf = ok ? exp2_hw(lg) : 0.f;
           const float gdp = gf * pacc[rs][i];
           d[i] = p[i] * (gdp - dl[i]);
           if constexpr (SPARSE) dsum[4 * rs + i] = p[i] * gdp;  // g dg, in dbeta's place
@@ -1017,8 +1025,6 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
 // Workspace: Delta per row | (sparse) selection lists, the dQ share slots
 // and the dbeta records.
 
-constexpr int kItemChunk = 256;  // list entries per work item (the key-major kernels take blkoff)
-
 struct BwdWs {
   size_t delta, lists, dqp, dbl, total;
 };
@@ -1030,7 +1036,7 @@ static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
   size_t at = align_up(rows * sizeof(float));
   if (sparse) {
     size_t lb = 0;
-    sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kItemChunk, nullptr, &lb);
+    sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, nullptr, &lb);
     w.lists = at;
     at += align_up(lb);
     w.dqp = at;
@@ -1076,7 +1082,7 @@ static hipError_t bwd_mfma_t(BwdArgs a, const SelLists& L, int B, hipStream_t s)
   const size_t rows = size_t(B) * a.Hq * a.N;
   SAS_LAUNCH("bwd_delta_mfma", (bwd_delta_mfma_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))),
              dim3(256), 0, s, a.o, a.dout, a.delta, rows);
-  if (SPARSE) {
+  if (SPARSE && a.lg2 == nullptr) {  // (with a saved context the lists are there already)
     const hipError_t e = launch_sel_lists(a.idx, L, B, a.Hkv, a.N, a.C, a.topk, KT, s);
     if (e != hipSuccess) return e;
   }
@@ -1097,12 +1103,15 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                            float* ds, const Dims& d, int topk, float scale, int gate, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const void* ctx) {
   const bool sp = idx != nullptr;
   char* w = static_cast<char*>(ws);
   const BwdWs W = bwd_ws_layout(d, topk, sp);
   SelLists L{};
-  if (sp) L = sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kItemChunk, w + W.lists, nullptr);
+  // the lists: from the forward's saved context, or built into the workspace
+  SparseCtx C{};
+  if (sp && ctx) C = sparse_ctx_layout(d, topk, static_cast<char*>(const_cast<void*>(ctx)), nullptr);
+  if (sp) L = ctx ? C.L : sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, w + W.lists, nullptr);
   BwdArgs a{};
   a.q = (const bf16_t*)q;
   a.k = (const bf16_t*)k;
@@ -1122,6 +1131,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.selbits = L.bits;
     a.selpre = L.pre;
     a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
+    a.lg2 = C.lg2;
     a.dbl = reinterpret_cast<float*>(w + W.dbl);
   }
   a.Hq = d.Hq;

@@ -38,7 +38,8 @@ bool fwd_mfma_supported(const Dims& d, int topk, bool sparse);
 size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s);
+                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s,
+                           void* ctx = nullptr);
 
 hipError_t launch_fwd_mfma_shared_row(const void* q, const void* k, const void* v, const float* score_row,
                                       const float* lse_s, void* o, float* lse, const Dims& d, float scale,
@@ -50,7 +51,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const void* dout, const float* scores, const int32_t* idx,
                            const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                            float* ds, const Dims& d, int topk, float scale, int gate, void* ws,
-                           hipStream_t s);
+                           hipStream_t s, const void* ctx = nullptr);
 
 namespace {
 
@@ -169,9 +170,17 @@ size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate) {
          align_up(rows_of(d) * sizeof(float));
 }
 
+size_t train_ctx_bytes(const Dims& d, int topk, bool bf16) {
+  if (topk < 0 || !bf16 || !fwd_mfma_supported(d, topk, true) || !bwd_mfma_supported(d, topk, true)) return 0;
+  size_t n = 0;
+  sparse_ctx_layout(d, topk, nullptr, &n);
+  return n;
+}
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s, bool lse_given) {
+                      int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s, bool lse_given,
+                      void* ctx) {
   if (gate == kGateSte) {
     // the hard gate: plain block-sparse attention (the raw gate on zero
     // scores), then the real LSE_s for the backward's soft gate
@@ -196,7 +205,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
   // gate normaliser: 0 none (lse_s holds 0), 1 computed here, 2 given in lse_s
   const int nm = !norm ? 0 : lse_given ? 2 : 1;
   if (bf16 && fwd_mfma_supported(d, topk, idx != nullptr))
-    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, nm, outer, ws, s);
+    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, nm, outer, ws, s, ctx);
   return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, nm, outer, s);
 }
 
@@ -204,7 +213,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const void* dout, const float* scores, const int32_t* idx,
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                       float* ds, const Dims& d, int topk, float scale, bool bf16, int gate, void* ws,
-                      hipStream_t s) {
+                      hipStream_t s, const void* ctx) {
   if (gate == kGateSte) {
     // dq, dk, dv of the hard gate's attention; then one full-scope pass on
     // zero scores with the hard LSE_S, whose raw-gate ds is dh of every
@@ -245,7 +254,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   }
   if (bf16 && bwd_mfma_supported(d, topk, idx != nullptr))
     return launch_bwd_mfma(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk, scale,
-                           gate, ws, s);
+                           gate, ws, s, gate == kGateSoftmax ? ctx : nullptr);
   float* delta = static_cast<float*>(ws);
   return launch_bwd_simt(q, k, v, o, dout, scores, idx, lse, lse_s, dq, dk, dv, ds, d, topk,
                          scale, bf16, gate, delta, s);

@@ -47,6 +47,8 @@ struct FwdSelArgs {
   bf16_t* o;
   float* lse;
   float* dummy;   // line that absorbs masked stores
+  float* lg2;     // optional [pairs, list entries, G]: the base-2 log gate of each
+                  // history (entry, head), kept for the backward
   int Hq, Hkv, N, C, topk, n_pairs;
   float scale;
 };
@@ -64,6 +66,13 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
   constexpr int STG = 16 * D;            // per wave stage: Q of 16 rows
   constexpr int NLD = 16 / RPL;          // wave DMA instructions per step
   constexpr int NSTORE = NLD + 1;        // stores per step: P V rows + (m, l)
+  // Vector memory operations a step leaves in flight at its end: at least
+  // this many are issued after the next step's tile loads (own items: the
+  // entry load and the NSTORE stores; history items also the two bias loads
+  // and, with a saved context, the log-gate store), and they complete in
+  // order, so waiting until at most this many are outstanding means the
+  // tiles have landed.
+  constexpr int NAFTER = NSTORE + 1;
   static_assert(KT * D <= WAVES * STG, "V tile fits in the stage area");
   static_assert(16 % G == 0, "a 16-row group holds whole tokens");
   __shared__ __attribute__((aligned(16))) uint16_t Ksh[KT * D];   // K, row-major, swizzled
@@ -139,6 +148,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
     const size_t rbase = hrow0 + size_t((lane & 15) % G) * N;  // the lane's row lr
     // (m, l) records of the item's list entries: row q of the item is record q
     float2* stl_item = a.stl + (size_t(pair) * L.ents_per_pair + it.y) * G;
+    float* lg2_item = a.lg2 == nullptr ? nullptr : a.lg2 + (size_t(pair) * L.ents_per_pair + it.y) * G;
 
     // Entry of row lr of group gk: token | slot << 23 (own block: slot
     // topk), in two parts.  entry_raw issues the list load (own items read a
@@ -168,19 +178,15 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         dma16_to_lds(a.q + qoff[j] + size_t(t) * D, st + j * 512);
       }
     };
-    // The row's gate bias in base 2 (own block: 0); OUTER: the gate g itself
-    // (own block: 1).  Split like the entries: bias_raw loads (s, LSE_s),
-    // bias_fin forms the bias a step later.
+    // The row's log gate in base 2, (s - LSE_s) log2 e (own block: 0).
+    // Split like the entries: bias_raw loads (s, LSE_s), bias_fin forms the
+    // value a step later.
     auto bias_raw = [&](uint32_t e) -> float2 {
       if (own_item) return make_float2(0.f, 0.f);
       const size_t gr = rbase + (e & 0x7fffffu);
       return make_float2(a.scores[gr * C + m], a.lse_s[gr]);
     };
-    auto bias_fin = [&](float2 r) -> float {
-      if (own_item) return OUTER ? 1.f : 0.f;
-      const float lg = (r.x - r.y) * kLog2e;
-      return OUTER ? exp2_hw(lg) : lg;
-    };
+    auto bias_fin = [&](float2 r) -> float { return own_item ? 0.f : (r.x - r.y) * kLog2e; };
 
     auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, float bias, int ln) {
       constexpr bool MASK = decltype(maskt)::value;
@@ -228,8 +234,9 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
             l += p[4 * h + i];
           }
         if constexpr (OUTER) {
+          const float gate = exp2_hw(bias);  // g (own block: 1)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) p[j] *= bias;  // the gate scales P V only
+          for (int j = 0; j < 8; ++j) p[j] *= gate;  // the gate scales P V only
         }
         pb[kk] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                             pack_bf16(p[6], p[7]));
@@ -267,6 +274,8 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       float2* sp = !valid ? reinterpret_cast<float2*>(a.dummy + 64)
                           : (own_item ? a.sto + rbase + t : stl_item + 16 * gk + lr);
       *sp = make_float2(mx, l);
+      // the row's log gate for the backward (history rows)
+      if (lg2_item != nullptr && !own_item && valid && lq == 0) lg2_item[16 * gk + lr] = bias;
     };
 
     // pipeline over this wave's groups gk = wave + WAVES k.  The raw words
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
       }
       const uint32_t r2 = entry_raw(min(gk + 2 * WAVES, glast), ln & 15);
       compute(tag, std::true_type{}, gk, e0, b0, ln);
-      wait_vm<NSTORE>();
+      wait_vm<NAFTER>();
       e0 = e1;
       r1 = r2;
       b0 = bias_fin(br1);
@@ -387,8 +396,6 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists
   }
 }
 
-constexpr int kFwdChunk = 256;  // tokens per work item
-
 struct FwdSelWs {
   size_t lists, op, stl, sto, dummy, total;
 };
@@ -397,7 +404,7 @@ FwdSelWs fwd_sel_layout(const Dims& d, int topk) {
   FwdSelWs w{};
   const size_t rows = size_t(d.B) * d.Hq * d.N;
   size_t lb = 0;
-  sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kFwdChunk, nullptr, &lb);
+  sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, nullptr, &lb);
   size_t at = 0;
   w.lists = at;
   at += align_up(lb);
@@ -431,12 +438,17 @@ hipError_t fwd_sel_t(const FwdSelArgs& a, const SelLists& L, int B, bool outer, 
 size_t fwd_sel_workspace(const Dims& d, int topk) { return fwd_sel_layout(d, topk).total; }
 
 // Sparse-scope forward over the selection lists (LSE_s already in lse_s).
+// ctx (optional): the lists are built there instead of in the workspace, and
+// the history entries' log gates are recorded beside them for the backward.
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, bool outer, void* ws, hipStream_t s) {
+                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx) {
   char* w = static_cast<char*>(ws);
   const FwdSelWs W = fwd_sel_layout(d, topk);
-  const SelLists L = sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kFwdChunk, w + W.lists, nullptr);
+  SparseCtx C{};
+  if (ctx) C = sparse_ctx_layout(d, topk, static_cast<char*>(ctx), nullptr);
+  const SelLists L =
+      ctx ? C.L : sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, w + W.lists, nullptr);
   const hipError_t e = launch_sel_lists(idx, L, d.B, d.Hkv, d.N, d.C, topk, KT, s);
   if (e != hipSuccess) return e;
   FwdSelArgs a{};
@@ -451,6 +463,7 @@ hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const flo
   a.o = (bf16_t*)o;
   a.lse = lse;
   a.dummy = reinterpret_cast<float*>(w + W.dummy);
+  a.lg2 = C.lg2;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
   a.N = d.N;

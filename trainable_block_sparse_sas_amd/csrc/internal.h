@@ -90,27 +90,45 @@ SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int
                           size_t* bytes);
 hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
                             int topk, int block, hipStream_t s);
+constexpr int kListChunk = 256;  // list entries per work item of the key-major kernels
+
+// Saved context of a sparse-scope training forward, read by its backward:
+// the selection lists of idx, then per (KV head, list entry, query head of the
+// group) the base-2 log gate (s - LSE_s) log2 e of that history entry.
+struct SparseCtx {
+  SelLists L;
+  float* lg2;  // [pairs][ents_per_pair][G]
+};
+// base == NULL: sizes only (*bytes).
+SparseCtx sparse_ctx_layout(const Dims& d, int topk, char* base, size_t* bytes);
+// Bytes of the saved context a training forward writes for these sizes: the
+// layout above where the sparse scope runs on the matrix cores, else 0 (the
+// context is not used).
+size_t train_ctx_bytes(const Dims& d, int topk, bool bf16);
 
 // ---- gated attention ----------------------------------------------------------
 size_t fwd_sel_workspace(const Dims& d, int topk);
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, bool outer, void* ws, hipStream_t s);
+                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx = nullptr);
 size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 // lse_given (softmax gate only): lse_s already holds LSE_s; it is read, not
-// computed.
+// computed.  ctx (sparse scope on the matrix cores; else unused): the saved
+// context for the backward (sparse_ctx_layout) is written.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s,
-                      bool lse_given = false);
+                      bool lse_given = false, void* ctx = nullptr);
+// ctx (softmax gate, sparse scope on the matrix cores; else unused): the
+// saved context the forward wrote; the selection lists are not rebuilt.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* scores, const int32_t* idx,
                       const float* lse, const float* lse_s, void* dq, void* dk, void* dv,
                       float* ds, const Dims& d, int topk, float scale, bool bf16, int gate, void* ws,
-                      hipStream_t s);
+                      hipStream_t s, const void* ctx = nullptr);
 
 // ---- decode --------------------------------------------------------------------
 size_t selector_bwd_workspace(const Dims& d, bool bf16);

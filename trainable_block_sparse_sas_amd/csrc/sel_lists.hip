@@ -272,6 +272,16 @@ SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int
   return L;
 }
 
+SparseCtx sparse_ctx_layout(const Dims& d, int topk, char* base, size_t* bytes) {
+  SparseCtx c{};
+  size_t lb = 0;
+  c.L = sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, d.block, kListChunk, base, &lb);
+  const size_t gb = size_t(d.B) * d.Hkv * c.L.ents_per_pair * d.G() * sizeof(float);
+  c.lg2 = base ? reinterpret_cast<float*>(base + align_up(lb)) : nullptr;
+  if (bytes) *bytes = align_up(lb) + align_up(gb);
+  return c;
+}
+
 hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
                             int topk, int block, hipStream_t s) {
   const size_t tokens = size_t(B) * Hkv * N;

@@ -1,8 +1,8 @@
 """Buffers and call sequences of the two SAS hot paths on one GPU.
 
 Training (full or sparse scope):  sas_score_blocks_lse (pool + score + the gate
-  normaliser) -> sas_topk_select (sparse scope only) -> sas_gated_attn_fwd_lse
-  -> sas_gated_attn_bwd.
+  normaliser) -> sas_topk_select (sparse scope only) -> sas_gated_attn_fwd_ctx
+  (LSE_s given; saves the selection lists and log gates) -> sas_gated_attn_bwd_ctx.
 Decode:  sas_score_blocks (group-summed scores from pooled keys kept beside the
   cache) -> sas_topk_select -> sas_sparse_decode.
 
@@ -42,6 +42,11 @@ class TrainStep:
                    for op in (sas.SAS_OP_FWD, sas.SAS_OP_BWD))
         self.ws = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws else None
         self.ws_fwd = self.ws_bwd = self.ws
+        # the forward's saved context for the backward (selection lists and
+        # log gates); valid after a forward on the step's own scores
+        n_ctx = sas.sas_workspace_bytes(sas.SAS_OP_CTX, B, Hq, Hkv, N, D, block, tk, sdt)
+        self.ctx = torch.empty(n_ctx, dtype=torch.uint8, device=dev) if n_ctx else None
+        self._ctx_valid = False
 
     def select(self, q, k):
         # scores and, in the same kernel, the gate normaliser LSE_s
@@ -50,15 +55,22 @@ class TrainStep:
             sas.sas_topk_select(self.scores, self.idx, None, self.Hq // self.Hkv, self.block)
 
     def forward(self, q, k, v, scores=None, idx=None):
+        own = scores is None and idx is None  # the step's own scores and selection
         idx = self.idx if idx is None else idx
-        if scores is None:  # the step's own scores, whose LSE_s select() wrote
-            sas.sas_gated_attn_fwd_lse(q, k, v, self.scores, idx, self.lse_s, self.o, self.lse, self.block,
-                                       self.scale, self.ws_fwd)
+        if own:  # LSE_s from select(); the saved context filled for the backward
+            sas.sas_gated_attn_fwd_ctx(q, k, v, self.scores, idx, self.lse_s, self.o, self.lse, self.block,
+                                       self.scale, self.ctx, self.ws_fwd)
         else:
-            sas.sas_gated_attn_fwd(q, k, v, scores, idx, self.o, self.lse, self.lse_s, self.block,
-                                   self.scale, self.ws_fwd)
+            sas.sas_gated_attn_fwd(q, k, v, self.scores if scores is None else scores, idx, self.o, self.lse,
+                                   self.lse_s, self.block, self.scale, self.ws_fwd)
+        self._ctx_valid = own
 
     def backward(self, q, k, v, do, scores=None, idx=None):
+        if scores is None and idx is None and self._ctx_valid:
+            sas.sas_gated_attn_bwd_ctx(q, k, v, self.o, do, self.scores, self.idx, self.lse, self.lse_s,
+                                       self.ctx, self.dq, self.dk, self.dv, self.ds, self.block, self.scale,
+                                       self.ws_bwd)
+            return
         scores = self.scores if scores is None else scores
         idx = self.idx if idx is None else idx
         sas.sas_gated_attn_bwd(q, k, v, self.o, do, scores, idx, self.lse, self.lse_s, self.dq,
