@@ -148,6 +148,10 @@ int sas_score_blocks(const void* q, const void* k, void* kbar, float* scores,
  *          kernel computes it from the scores it writes (fp32 running max and
  *          sum per row); otherwise a pass over the written scores does.  It
  *          matches the lse_s of sas_gated_attn_fwd up to fp32 summation order.
+ * scores:  only the history columns m < c(t) of each row are written; the
+ *          others (-inf in sas_score_blocks) are left as they are, since no
+ *          call reads them: a caller that wants the dense form fills the
+ *          tensor with -inf once.
  * Other arguments and errors: as sas_score_blocks.
  */
 int sas_score_blocks_lse(const void* q, const void* k, void* kbar, float* scores,
@@ -242,6 +246,9 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v,
  *            unchanged and passes the same scores, idx and LSE_s (no check is
  *            made: a context of other inputs gives wrong gradients).
  *            Unlike a workspace, it carries data from one call to the next.
+ * ds (backward): the history columns m < c(t) as in sas_gated_attn_bwd; the
+ *            other columns (0 there) may be left unwritten: a caller that
+ *            wants the dense form fills ds with zeros once.
  * Other arguments, and errors: as sas_gated_attn_fwd_lse and
  *   sas_gated_attn_bwd; a missing or short ctx is SAS_EWORKSPACE.
  */

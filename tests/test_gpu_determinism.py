@@ -24,16 +24,18 @@ if torch.cuda.is_available():
 DEV = "cuda"
 
 
-def _twice(run, outs, partial=()):
+def _twice(run, outs, partial=(), fill=float("nan")):
     """run() writes `outs` (and `partial`, outputs it writes only in part, such
     as the rows of a page pool that a prompt reaches); the two runs must agree
-    bit for bit.  `outs` are overwritten with NaN (or -7) between the runs."""
+    bit for bit.  `outs` are overwritten with `fill` (NaN; integer outputs -7)
+    between the runs; a call that leaves part of an output to the caller's fill
+    (scores beyond the history: -inf; ds there: 0) is given that fill."""
     run()
     torch.cuda.synchronize()
     first = [o.clone() for o in list(outs) + list(partial)]
     for o in outs:
         if o.is_floating_point():
-            o.fill_(float("nan"))
+            o.fill_(fill)
         else:
             o.fill_(-7)
     run()
@@ -52,8 +54,9 @@ def test_training_entry_points_deterministic(topk):
     w = Workload("det", "train", "bf16", 1, 8, 2, 128, 4672, 64, topk, index=21)
     q, k, v, do = training_inputs(w, device=DEV)
     step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, topk, torch.bfloat16)
-    sel_outs = [step.kbar, step.scores, step.lse_s] + ([] if topk is None else [step.idx])
-    _twice(lambda: step.select(q, k), sel_outs)  # scores and the gate normaliser LSE_s
+    sel_outs = [step.kbar, step.lse_s] + ([] if topk is None else [step.idx])
+    _twice(lambda: step.select(q, k), sel_outs)  # the gate normaliser LSE_s
+    _twice(lambda: step.select(q, k), [step.scores], fill=float("-inf"))  # history columns
     grads = [step.dq, step.dk, step.dv, step.ds]
     # LSE_s computed, lists built by each call
     _twice(lambda: step.forward(q, k, v, step.scores), [step.o, step.lse, step.lse_s])
@@ -61,7 +64,8 @@ def test_training_entry_points_deterministic(topk):
     # LSE_s given and the saved context (written in part: the list capacity)
     ctx = [] if step.ctx is None else [step.ctx]
     _twice(lambda: step.forward(q, k, v), [step.o, step.lse], partial=ctx)
-    _twice(lambda: step.backward(q, k, v, do), grads)
+    _twice(lambda: step.backward(q, k, v, do), grads[:3])
+    _twice(lambda: step.backward(q, k, v, do), [step.ds], fill=0.0)  # history columns
     # the gate variants
     B, Hq, Hkv, N, D, C = w.B, w.Hq, w.Hkv, w.N, w.D, w.C
     tk = -1 if topk is None else topk
@@ -132,8 +136,11 @@ def test_benchmark_shapes_deterministic():
     w = WORKLOADS[2]
     q, k, v, do = training_inputs(w, device=DEV)
     step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, w.topk, w.torch_dtype)
+    # scores and ds: the step writes their history columns only (the rest
+    # keeps the step's -inf and zero fills), so they are not refilled
     _twice(lambda: step.run(q, k, v, do),
-           [step.kbar, step.scores, step.idx, step.o, step.lse, step.lse_s, step.dq, step.dk, step.dv, step.ds])
+           [step.kbar, step.idx, step.o, step.lse, step.lse_s, step.dq, step.dk, step.dv],
+           partial=[step.scores, step.ds])
     del step, q, k, v, do
     torch.cuda.empty_cache()
     w = WORKLOADS[4]

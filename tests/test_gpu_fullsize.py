@@ -108,7 +108,7 @@ def test_training_fullsize(wi):
     kbar_dev = torch.tensor(kbar_r).to(dt).to(DEV)
     sas.sas_score_blocks(q, None, kbar_dev, step.scores, None, w.block, w.scale)
     # the same scores through the score kernel that also writes LSE_s
-    s_lse = torch.empty_like(step.scores)
+    s_lse = torch.full_like(step.scores, float("-inf"))  # it writes the history columns only
     lse_s_sc = torch.empty_like(step.lse_s)
     sas.sas_score_blocks_lse(q, None, kbar_dev, s_lse, lse_s_sc, w.block, w.scale)
     torch.cuda.synchronize()

@@ -196,7 +196,7 @@ int sas_score_blocks_lse(const void* q, const void* k, void* kbar, float* scores
   }
   if (empty(B, Hq, N)) return hip_status(hipSuccess, "");
   sas::Dims d{B, Hq, Hkv, N, D, block, C};
-  return hip_status(sas::launch_score_train(q, kbar, scores, d, scale, false, bf16, s, lse_s), what);
+  return hip_status(sas::launch_score_train(q, kbar, scores, d, scale, false, bf16, s, lse_s, true), what);
 }
 
 int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len, int B, int Hkv,

@@ -67,6 +67,7 @@ struct BwdArgs {
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
   float scale;
   int gate;          // gate activation (kGateSoftmax, kGateSigmoid, kGateRaw)
+  int ds_hist_only;  // sparse: ds columns m >= c(t) (no history block) are not written
 };
 
 constexpr int kTokMask = 0x7fffff;  // token field of a selection-list entry
@@ -535,7 +536,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
 //        (slot(m) = rank of m among the row's selected blocks; its dbeta is
 //        the record of the row's entry in m's list, pos[token][slot]);
 //        GATE: the gate activation, whose chain rule gate_ds applies (the
-//        softmax gate's is the formula above).
+//        softmax gate's is the formula above); hist_only: the columns from
+//        the own block on are not written.
 // Each lane takes 2 dq columns and 8 consecutive blocks per pass.
 template <int D, int GATE>
 __global__ __launch_bounds__(256) void rows_sparse_kernel(
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
     size_t ents_per_pair, const float* __restrict__ scores,
     const float* __restrict__ lse_s, const uint32_t* __restrict__ selbits,
     const uint16_t* __restrict__ selpre, bf16_t* __restrict__ dq, float* __restrict__ ds, int Hq, int G,
-    int N, int C, int MWB, int topk, float scale, size_t rows) {
+    int N, int C, int MWB, int topk, float scale, size_t rows, int hist_only) {
   constexpr int LPS = D / 2;       // lanes per slot (2 columns each)
   constexpr int SG = 64 / LPS;     // slots per pass
   const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -601,8 +603,9 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
   float* drow = ds + row * C;
   const uint32_t* bits = selbits + tok * MWB;
   const bool vec = (C & 3) == 0;
+  const int ncol = hist_only ? c : C;  // columns written (hist_only: the history)
   int run = 0;
-  for (int m0 = 0; m0 < C; m0 += 512) {
+  for (int m0 = 0; m0 < ncol; m0 += 512) {
     const int col0 = m0 + 8 * lane;
     const uint32_t b8 = col0 < c ? (bits[col0 >> 5] >> (col0 & 31)) & 0xffu : 0u;
     const int cnt = __popc(b8);
@@ -636,13 +639,13 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
         out[i] = m2 < c ? gate_ds(GATE, dbv[i], srow[m2] - ls, tot) : 0.f;
       }
     }
-    if (vec && col0 + 8 <= C) {
+    if (vec && col0 + 8 <= ncol) {
       *reinterpret_cast<float4*>(drow + col0) = make_float4(out[0], out[1], out[2], out[3]);
       *reinterpret_cast<float4*>(drow + col0 + 4) = make_float4(out[4], out[5], out[6], out[7]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (col0 + i < C) drow[col0 + i] = out[i];
+        if (col0 + i < ncol) drow[col0 + i] = out[i];
     }
   }
 }
@@ -1057,7 +1060,7 @@ static void launch_dq_sparse(BwdArgs a, const SelLists& L, size_t rows, hipStrea
 #define SAS_ROWS_SPARSE(GT)                                                                                 \
   SAS_LAUNCH("rows_sparse", (rows_sparse_kernel<D, GT>), dim3((rows + 3) / 4), dim3(256), 0, s, a.dqp, a.dbl, \
              L.pos, L.ents_per_pair, a.scores, a.lse_s, a.selbits, a.selpre, a.dq, a.ds, a.Hq, G, a.N, a.C,   \
-             a.MWB, a.topk, a.scale, rows)
+             a.MWB, a.topk, a.scale, rows, a.ds_hist_only)
   if (a.gate == kGateSigmoid) SAS_ROWS_SPARSE(kGateSigmoid);
   else if (a.gate == kGateRaw) SAS_ROWS_SPARSE(kGateRaw);
   else SAS_ROWS_SPARSE(kGateSoftmax);
@@ -1132,6 +1135,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.selpre = L.pre;
     a.dqp = reinterpret_cast<bf16_t*>(w + W.dqp);
     a.lg2 = C.lg2;
+    a.ds_hist_only = ctx != nullptr;  // the saved-context backward leaves them to the caller
     a.dbl = reinterpret_cast<float*>(w + W.dbl);
   }
   a.Hq = d.Hq;

@@ -49,9 +49,11 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, int block,
                        int C, bool bf16, hipStream_t s);
 // lse_s (optional, not with group_sum): also the softmax gate's LSE_s per row.
+// hist_only: the columns m >= c(t) of each row (no history block) are not
+// written.
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
                               float scale, bool group_sum, bool bf16, hipStream_t s,
-                              float* lse_s = nullptr);
+                              float* lse_s = nullptr, bool hist_only = false);
 // LSE_s of every row over its history scores (any dtype: reads the fp32 scores).
 hipError_t launch_lse_rows(const float* scores, float* lse_s, const Dims& d, hipStream_t s);
 // table (bf16 only): pooled key m of sequence b is row table[b * C + m] of

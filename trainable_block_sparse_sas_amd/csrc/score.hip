@@ -43,12 +43,13 @@ __global__ void pool_pages_kernel(const T* __restrict__ kp, T* __restrict__ kbar
 // Training scores: a workgroup owns 64 query rows of one KV head and loops over
 // that head's G query heads and over 64-wide tiles of blocks.  Tiles are staged
 // in LDS as fp32; each thread produces 4 rows x 4 blocks per tile.
+// hist_only: the columns m >= c(t) (no history block) are not written.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ q,
                                                           const T* __restrict__ kbar,
                                                           float* __restrict__ out, int Hq, int Hkv,
                                                           int N, int C, int block, float scale,
-                                                          int group_sum) {
+                                                          int group_sum, int hist_only) {
   constexpr int TR = 64, TM = 64, PAD = 1;
   __shared__ float qs[TR][D + PAD];
   __shared__ float ks[TM][D + PAD];
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ 
         int c = t / block;
         for (int j = 0; j < 4; ++j) {
           int m = mt + c0 + j;
-          if (m >= C) continue;
+          if (m >= C || (hist_only && m >= c)) continue;
           float sv = m < c ? acc[i][j] * scale : kNegInf;
           if (group_sum) {
             usum[i][j] = (h == g * G) ? sv : usum[i][j] + sv;
@@ -122,13 +123,14 @@ __global__ __launch_bounds__(256) void score_train_kernel(const T* __restrict__ 
 // Design Choices Matter": log g = s - LSE(s)), -inf without history.  Each
 // lane keeps a running (max, sum of exp) of its columns for its four rows;
 // the 16 lanes of a row group merge theirs at the end.
+// hist_only: the columns m >= c(t) (no history block) are not written.
 template <int D>
 __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __restrict__ q,
                                                                const bf16_t* __restrict__ kbar,
                                                                float* __restrict__ out,
                                                                float* __restrict__ lse_s, int Hq,
                                                                int Hkv, int N, int C, int block,
-                                                               float scale) {
+                                                               float scale, int hist_only) {
   constexpr int KS = D / 32, CH = D / 8;
   __shared__ __attribute__((aligned(16))) uint16_t ks[64][D + 8];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void score_train_mfma_kernel(const bf16_t* __r
             lmx[i] = nm;
           }
       }
-      if (m < C)
+      if (m < (hist_only ? c : C))
         for (int i = 0; i < 4; ++i)
           if (orow[i]) orow[i][m] = m < c ? acc[i] * scale : kNegInf;
     }
@@ -383,33 +385,36 @@ hipError_t launch_pool(const void* k, void* kbar, int B, int Hkv, int L, int D, 
 
 template <typename T, int D>
 static void score_train_t(const void* q, const void* kbar, float* scores, const Dims& d,
-                          float scale, bool group_sum, hipStream_t s) {
+                          float scale, bool group_sum, bool hist_only, hipStream_t s) {
   dim3 grid((d.N + 63) / 64, d.Hkv, d.B);
   SAS_LAUNCH("score_train", (score_train_kernel<T, D>), grid, dim3(256), 0, s, (const T*)q,
                      (const T*)kbar, scores, d.Hq, d.Hkv, d.N, d.C, d.block, scale,
-                     group_sum ? 1 : 0);
+                     group_sum ? 1 : 0, hist_only ? 1 : 0);
 }
 
 hipError_t launch_score_train(const void* q, const void* kbar, float* scores, const Dims& d,
-                              float scale, bool group_sum, bool bf16, hipStream_t s, float* lse_s) {
+                              float scale, bool group_sum, bool bf16, hipStream_t s, float* lse_s,
+                              bool hist_only) {
   if (d.N == 0 || d.B == 0) return hipSuccess;
   if (d.C == 0) return lse_s ? launch_lse_rows(scores, lse_s, d, s) : hipSuccess;  // rows without history
   if (bf16 && !group_sum && d.block % 16 == 0) {
     dim3 grid((d.N + 63) / 64, d.Hq, d.B);
     if (d.D == 64)
       SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale,
+                         int(hist_only));
     else
       SAS_LAUNCH("score_train_mfma", score_train_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale);
+                         (const bf16_t*)kbar, scores, lse_s, d.Hq, d.Hkv, d.N, d.C, d.block, scale,
+                         int(hist_only));
     return hipGetLastError();
   }
   if (bf16) {
-    if (d.D == 64) score_train_t<bf16_t, 64>(q, kbar, scores, d, scale, group_sum, s);
-    else score_train_t<bf16_t, 128>(q, kbar, scores, d, scale, group_sum, s);
+    if (d.D == 64) score_train_t<bf16_t, 64>(q, kbar, scores, d, scale, group_sum, hist_only, s);
+    else score_train_t<bf16_t, 128>(q, kbar, scores, d, scale, group_sum, hist_only, s);
   } else {
-    if (d.D == 64) score_train_t<float, 64>(q, kbar, scores, d, scale, group_sum, s);
-    else score_train_t<float, 128>(q, kbar, scores, d, scale, group_sum, s);
+    if (d.D == 64) score_train_t<float, 64>(q, kbar, scores, d, scale, group_sum, hist_only, s);
+    else score_train_t<float, 128>(q, kbar, scores, d, scale, group_sum, hist_only, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !lse_s) return e;

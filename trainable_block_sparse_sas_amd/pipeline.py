@@ -26,7 +26,9 @@ class TrainStep:
         self.dtype = dtype
         sdt = sas.SAS_BF16 if dtype == torch.bfloat16 else sas.SAS_F32
         self.kbar = torch.empty((B, Hkv, C, D), dtype=dtype, device=dev)
-        self.scores = torch.empty((B, Hq, N, C), dtype=torch.float32, device=dev)
+        # the calls write only each row's history columns: the others keep
+        # these fills (-inf scores, zero ds), as in the dense form
+        self.scores = torch.full((B, Hq, N, C), float("-inf"), dtype=torch.float32, device=dev)
         self.idx = None if topk is None else torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=dev)
         self.o = torch.empty((B, Hq, N, D), dtype=dtype, device=dev)
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
@@ -34,7 +36,7 @@ class TrainStep:
         self.dq = torch.empty((B, Hq, N, D), dtype=dtype, device=dev)
         self.dk = torch.empty((B, Hkv, N, D), dtype=dtype, device=dev)
         self.dv = torch.empty((B, Hkv, N, D), dtype=dtype, device=dev)
-        self.ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=dev)
+        self.ds = torch.zeros((B, Hq, N, C), dtype=torch.float32, device=dev)
         tk = -1 if topk is None else topk
         # one scratch buffer for both calls: they run in stream order and a
         # workspace carries nothing from one call to the next
