@@ -289,7 +289,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
     float b0 = bias_fin(bias_raw(e0));
     float2 br1 = make_float2(0.f, 0.f);
     wait_vm<0>();
-    auto step = [&](auto tag, int k) {
+    auto step = [&](auto tag, auto maskt, int k) {
       using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -300,16 +300,23 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         br1 = bias_raw(e1);
       }
       const uint32_t r2 = entry_raw(min(gk + 2 * WAVES, glast), ln & 15);
-      compute(tag, std::true_type{}, gk, e0, b0, ln);
+      compute(tag, maskt, gk, e0, b0, ln);
       wait_vm<NAFTER>();
       e0 = e1;
       r1 = r2;
       b0 = bias_fin(br1);
     };
-    for (int k = 0; k < nk; k += 2) {
-      step(S0t{}, k);
-      if (k + 1 < nk) step(S1t{}, k + 1);
-    }
+    // own items mask the keys after the row's token; history items need no
+    // mask (a row past the item computes finite values from token 0's Q, and
+    // its outputs go to the dummy line).  One loop per variant.
+    auto steps = [&](auto maskt) {
+      for (int k = 0; k < nk; k += 2) {
+        step(S0t{}, maskt, k);
+        if (k + 1 < nk) step(S1t{}, maskt, k + 1);
+      }
+    };
+    if (own_item) steps(std::true_type{});
+    else steps(std::false_type{});
   }
 }
 
