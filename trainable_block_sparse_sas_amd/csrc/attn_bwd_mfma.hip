@@ -220,6 +220,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   // resident workgroups move down the tokens together and gather the same Q
   // and dO rows at about the same time (L2 hits instead of refetches).
   auto hstep = [&](int k) { return n_hsteps - 1 - (k - n_own); };
+  // sparse scope with a saved context: history rows read their log gates
+  const bool use_lg2 = SPARSE && a.lg2 != nullptr;
   // sparse scope: record of row 0 of history step k is rec0 + hstep(k) RS
   const size_t rec0 = SPARSE ? (size_t(pair) * L.ents_per_pair + (lst - (L.ents + size_t(pair) * L.ents_per_pair))) * G
                              : 0;
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       // slot 2 of a history row: its saved base-2 log gate (the record of
       // row r of the step, as for dbeta), else its score (slot 3: LSE_s).
       // Own-block rows use neither; they read lse there, which always exists.
-      const float* s2 = a.lg2 != nullptr ? a.lg2 + rec0 + (t >= 0 ? size_t(hstep(k)) * RS + r : 0)
-                                         : a.scores + gr * C + m;
+      const float* s2 = use_lg2 ? a.lg2 + rec0 + (t >= 0 ? size_t(hstep(k)) * RS + r : 0)
+                                : a.scores + gr * C + m;
       const float* src = wave == 0 ? a.lse + gr
                        : wave == 1 ? a.delta + gr
                        : wave == 2 ? (phase == 1 ? s2 : a.lse + gr)
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       for (int i = 0; i < 4; ++i) {
         // base-2 log gate of a history row, then the base-2 logit offset:
         // bias - lse
-        const float lg = a.lg2 != nullptr ? sv[i] : (sv[i] - ls[i]) * kLog2e;
+        const float lg = use_lg2 ? sv[i] : (sv[i] - ls[i]) * kLog2e;
         const float off = (MK || OUTER) ? -lv[i] * kLog2e : lg - lv[i] * kLog2e;
         float x = fmaf(sacc[rs][i], c1, off);
         const bool ok = tv[i] >= 0 && key < N && (!MK || key <= tv[i]);
