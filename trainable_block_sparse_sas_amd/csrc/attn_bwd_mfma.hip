@@ -71,6 +71,7 @@ struct BwdArgs {
 };
 
 constexpr int kTokMask = 0x7fffff;  // token field of a selection-list entry
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- prep ------
 template <int D>
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   constexpr int ST_DO = RS * D, ST_F = 2 * RS * D;
   constexpr int STAGE = 2 * RS * D + 4 * RS * 2;
   static_assert(NPIECE % WAVES == 0 && WAVES == 4, "stat loads: one per wave");
+  static_assert(RS * (D + 8) <= ST_F, "staged dQ rows fit over the Q and dO tiles");
   static_assert(RS == 64, "a lane holds the token of its own row");
   __shared__ __attribute__((aligned(16))) uint16_t R0[STAGE], R1[STAGE];
   __shared__ __attribute__((aligned(16))) int tok_sh[2][RS];  // token of each row, -1: none
@@ -448,25 +450,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         a.dbl[rec0 + size_t(hstep(kcur)) * RS + tid] = db;
       }
       // The rows' dQ shares over this block: dQ^T = K^T dS^T (B operand: row
-      // 16 rs + lr, keys 32 kk + 8 lq .. of the dS rows), unscaled, to the
-      // row's slot (own rows: slot topk; history rows: the entry's rank).
-      // Lane holds columns 16 (NDW wave + nd) + 4 lq .. + 3 of its row.
+      // 16 rs + lr, keys 32 kk + 8 lq .. of the dS rows), unscaled.  Lane
+      // holds columns 16 (NDW wave + nd) + 4 lq .. + 3 of its row; they are
+      // staged as bf16 rows over the step's consumed Q and dO tiles, then
+      // leave as whole rows, 16 bytes a lane, to the row's slot (own rows:
+      // slot topk; history rows: the entry's rank).  The stores are
+      // non-temporal: the shares are read once, by the rows kernel, and kept
+      // out of the way of the gathered Q and dO rows in L2 (the kernel ran
+      // 7% faster than with 8-byte pieces stored straight from registers).
+      constexpr int WST = D + 8;
+      uint16_t* wst = rst(tag);
 #pragma unroll
       for (int rs = 0; rs < 4; ++rs) {
         const int r = 16 * rs + lr;
         const uint4 b0 = *reinterpret_cast<const uint4*>(dst_sh + r * TST + 8 * lq);
         const uint4 b1 = *reinterpret_cast<const uint4*>(dst_sh + r * TST + 32 + 8 * lq);
-        const int e = tkr[r];
-        const int t = e >= 0 ? e & kTokMask : 0;
-        const int slot = MK ? a.topk : (e >= 0 ? e >> 23 : 0);
-        bf16_t* dst = a.dqp + ((hrow0 + size_t(r % G) * N + t) * (a.topk + 1) + slot) * D;
 #pragma unroll
         for (int nd = 0; nd < NDW; ++nd) {
           f32x4 acc = mfma16(kq[nd][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
           acc = mfma16(kq[nd][1], b1, acc);
-          if (e >= 0)
-            *reinterpret_cast<uint2*>(dst + 16 * (NDW * wave + nd) + 4 * lq) =
-                make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+          *reinterpret_cast<uint2*>(wst + r * WST + 16 * (NDW * wave + nd) + 4 * lq) =
+              make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+        }
+      }
+      ring_barrier();  // the staged dQ rows are complete
+#pragma unroll
+      for (int u = 0; u < RS * CH / NT; ++u) {
+        const int r = (u * NT + tid) / CH, cc = (u * NT + tid) % CH;
+        const int e = tkr[r];
+        if (e >= 0) {
+          const int slot = MK ? a.topk : e >> 23;
+          bf16_t* dst = a.dqp + ((hrow0 + size_t(r % G) * N + (e & kTokMask)) * (a.topk + 1) + slot) * D;
+          const uint4 v = *reinterpret_cast<const uint4*>(wst + r * WST + cc * 8);
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst + cc * 8));
         }
       }
     }

@@ -34,6 +34,7 @@ namespace sas {
 namespace {
 
 constexpr int KT = 64;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct FwdSelArgs {
   const bf16_t* q;
@@ -269,7 +270,10 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         bf16_t* dp = 16 * gk + r < nrows
                          ? a.op + ooff[j] + (size_t(er & 0x7fffffu) * topk1 + (er >> 23)) * D
                          : reinterpret_cast<bf16_t*>(a.dummy) + cc * 8;
-        *reinterpret_cast<uint4*>(dp) = v;
+        // non-temporal: the slots are read once, by the combine kernel; kept
+        // out of the way of the gathered query rows in L2 (measured 17%
+        // faster kernel)
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dp));
       }
       float2* sp = !valid ? reinterpret_cast<float2*>(a.dummy + 64)
                           : (own_item ? a.sto + rbase + t : stl_item + 16 * gk + lr);
