@@ -595,7 +595,8 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
     for (int s0 = lane / LPS; s0 < nsel; s0 += U * SG) {
       uint32_t w[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[u] = s0 + u * SG < nsel ? src[size_t(s0 + u * SG) * LPS] : 0u;
+      for (int u = 0; u < U; ++u)  // (non-temporal: each share is read once)
+        w[u] = s0 + u * SG < nsel ? __builtin_nontemporal_load(src + size_t(s0 + u * SG) * LPS) : 0u;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         a0 += bf16_lo(w[u]);
@@ -657,9 +658,11 @@ __global__ __launch_bounds__(256) void rows_sparse_kernel(
         out[i] = m2 < c ? gate_ds(GATE, dbv[i], srow[m2] - ls, tot) : 0.f;
       }
     }
-    if (vec && col0 + 8 <= ncol) {
-      *reinterpret_cast<float4*>(drow + col0) = make_float4(out[0], out[1], out[2], out[3]);
-      *reinterpret_cast<float4*>(drow + col0 + 4) = make_float4(out[4], out[5], out[6], out[7]);
+    if (vec && col0 + 8 <= ncol) {  // non-temporal: nothing here reads ds again
+      typedef float f32x4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(f32x4v{out[0], out[1], out[2], out[3]}, reinterpret_cast<f32x4v*>(drow + col0));
+      __builtin_nontemporal_store(f32x4v{out[4], out[5], out[6], out[7]},
+                                  reinterpret_cast<f32x4v*>(drow + col0 + 4));
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists
       float w[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        x[u] = src[size_t(c0 + j + u * SG) * LPS];
+        x[u] = __builtin_nontemporal_load(src + size_t(c0 + j + u * SG) * LPS);  // read once
         w[u] = __shfl(wl, j + u * SG, 64);
       }
 #pragma unroll
