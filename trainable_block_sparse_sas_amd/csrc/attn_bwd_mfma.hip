@@ -312,10 +312,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       // Own-block rows use neither; they read lse there, which always exists.
       const float* s2 = use_lg2 ? a.lg2 + rec0 + (t >= 0 ? size_t(hstep(k)) * RS + r : 0)
                                 : a.scores + gr * C + m;
+      // (slot 3, LSE_s, is not needed with saved log gates: that wave reads
+      // the lse word again, one the workgroup has just fetched)
       const float* src = wave == 0 ? a.lse + gr
                        : wave == 1 ? a.delta + gr
                        : wave == 2 ? (phase == 1 ? s2 : a.lse + gr)
-                                   : a.lse_s + gr;
+                                   : (use_lg2 ? a.lse : a.lse_s) + gr;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + ST_F + wave * RS * 2), 4, 0, 0);
       if (wave == 0) tok_sh[P][r] = t;
     }
