@@ -151,6 +151,21 @@ def test_training_step_own_path(case):
     step.backward(q, k, v, do)  # from the saved context
     torch.cuda.synchronize()
     dq, dk, dv, ds = orc.gated_attention_backward(to64(q), to64(k), to64(v), to64(do), s64, idx, block, scale)
+    # history columns only: the columns m >= c(t) keep what the buffers held
+    C = step.scores.shape[-1]
+    future = torch.arange(C, device=DEV)[None, :] >= (torch.arange(N, device=DEV) // block)[:, None]
+    s_mark = torch.full_like(step.scores, 7.0)
+    sas.sas_score_blocks_lse(q, None, step.kbar, s_mark, torch.empty_like(step.lse_s), block, scale)
+    ds_mark = torch.full_like(step.ds, 7.0)
+    sas.sas_gated_attn_bwd_ctx(q, k, v, step.o, do, step.scores, step.idx, step.lse, step.lse_s, step.ctx,
+                               step.dq, step.dk, step.dv, ds_mark, block, scale, step.ws_bwd)
+    torch.cuda.synchronize()
+    fut = future[None, None].expand_as(s_mark)
+    assert bool((s_mark[fut] == 7.0).all()), "scores written beyond the history"
+    assert torch.equal(s_mark[~fut], step.scores[~fut]), "history scores"
+    if step.ctx is not None:  # the saved-context path (matrix cores): ds beyond the history untouched
+        assert bool((ds_mark[fut] == 7.0).all()), "ds written beyond the history"
+    assert torch.equal(ds_mark[~fut], step.ds[~fut]), "history ds"
     normwise(to64(step.dq), dq, tol["grad"], "dq")
     normwise(to64(step.dk), dk, tol["grad"], "dk")
     normwise(to64(step.dv), dv, tol["grad"], "dv")
