@@ -40,8 +40,7 @@ struct FwdSelArgs {
   const bf16_t* q;
   const bf16_t* k;
   const bf16_t* v;
-  const float* scores;
-  const float* lse_s;
+  const float* gates;  // [pairs * N][topk][G]: base-2 log gate of each (token, slot) and head
   bf16_t* op;     // [B, Hq, N, topk + 1, D]: unnormalised P V of each slot
   float2* stl;    // [pairs, list entries, G]: (m_b, l_b) per list entry and head
   float2* sto;    // [B, Hq, N]: (m_b, l_b) of the own block
@@ -69,7 +68,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
   constexpr int NSTORE = NLD + 1;        // stores per step: P V rows + (m, l)
   // Vector memory operations a step leaves in flight at its end: at least
   // this many are issued after the next step's tile loads (own items: the
-  // entry load and the NSTORE stores; history items also the two bias loads
+  // entry load and the NSTORE stores; history items also the bias load
   // and, with a saved context, the log-gate store), and they complete in
   // order, so waiting until at most this many are outstanding means the
   // tiles have landed.
@@ -179,15 +178,15 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
         dma16_to_lds(a.q + qoff[j] + size_t(t) * D, st + j * 512);
       }
     };
-    // The row's log gate in base 2, (s - LSE_s) log2 e (own block: 0).
-    // Split like the entries: bias_raw loads (s, LSE_s), bias_fin forms the
-    // value a step later.
-    auto bias_raw = [&](uint32_t e) -> float2 {
-      if (own_item) return make_float2(0.f, 0.f);
-      const size_t gr = rbase + (e & 0x7fffffu);
-      return make_float2(a.scores[gr * C + m], a.lse_s[gr]);
+    // The row's log gate in base 2, (s - LSE_s) log2 e (own block: 0), from
+    // the list build's record of the entry's (token, slot).  Split like the
+    // entries: bias_raw loads it, bias_fin takes it a step later.
+    const float* gate_row = a.gates + size_t(pair) * N * a.topk * G + (lane & 15) % G;
+    auto bias_raw = [&](uint32_t e) -> float {
+      if (own_item) return 0.f;
+      return gate_row[(size_t(e & 0x7fffffu) * a.topk + (e >> 23)) * G];
     };
-    auto bias_fin = [&](float2 r) -> float { return own_item ? 0.f : (r.x - r.y) * kLog2e; };
+    auto bias_fin = [&](float r) -> float { return own_item ? 0.f : r; };
 
     auto compute = [&](auto tag, auto maskt, int gk, uint32_t e, float bias, int ln) {
       constexpr bool MASK = decltype(maskt)::value;
@@ -291,7 +290,7 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
     uint32_t r1 = entry_raw(min(wave + WAVES, glast), lane & 15);
     issue(S0t{}, wave, e0, lane);
     float b0 = bias_fin(bias_raw(e0));
-    float2 br1 = make_float2(0.f, 0.f);
+    float br1 = 0.f;
     wait_vm<0>();
     auto step = [&](auto tag, auto maskt, int k) {
       using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists
 }
 
 struct FwdSelWs {
-  size_t lists, op, stl, sto, dummy, total;
+  size_t lists, gates, op, stl, sto, dummy, total;
 };
 
 FwdSelWs fwd_sel_layout(const Dims& d, int topk) {
@@ -419,6 +418,8 @@ FwdSelWs fwd_sel_layout(const Dims& d, int topk) {
   size_t at = 0;
   w.lists = at;
   at += align_up(lb);
+  w.gates = at;
+  at += align_up(size_t(d.B) * d.Hkv * d.N * size_t(topk > 0 ? topk : 1) * d.G() * sizeof(float));
   w.op = at;
   at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
   w.stl = at;
@@ -460,14 +461,14 @@ hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const flo
   if (ctx) C = sparse_ctx_layout(d, topk, static_cast<char*>(ctx), nullptr);
   const SelLists L =
       ctx ? C.L : sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, w + W.lists, nullptr);
-  const hipError_t e = launch_sel_lists(idx, L, d.B, d.Hkv, d.N, d.C, topk, KT, s);
+  const SelGates sg{scores, lse_s, reinterpret_cast<float*>(w + W.gates), d.Hkv, d.G(), d.C};
+  const hipError_t e = launch_sel_lists(idx, L, d.B, d.Hkv, d.N, d.C, topk, KT, s, &sg);
   if (e != hipSuccess) return e;
   FwdSelArgs a{};
   a.q = (const bf16_t*)q;
   a.k = (const bf16_t*)k;
   a.v = (const bf16_t*)v;
-  a.scores = scores;
-  a.lse_s = lse_s;
+  a.gates = sg.out;
   a.op = reinterpret_cast<bf16_t*>(w + W.op);
   a.stl = reinterpret_cast<float2*>(w + W.stl);
   a.sto = reinterpret_cast<float2*>(w + W.sto);

@@ -90,8 +90,17 @@ struct SelLists {
 // base == NULL: sizes only (*bytes).  chunk = tokens per work item.
 SelLists sel_lists_layout(int B, int Hkv, int N, int C, int topk, int block, int chunk, char* base,
                           size_t* bytes);
+// Optional output of the list build: per (token, slot) and query head of the
+// group the base-2 log gate (s - LSE_s) log2 e of the slot's block, read from
+// scores [B, Hkv G, N, C] and lse_s [B, Hkv G, N] row by row.
+struct SelGates {
+  const float* scores;
+  const float* lse_s;
+  float* out;  // [pairs * N][topk][G]
+  int Hkv, G, C;
+};
 hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
-                            int topk, int block, hipStream_t s);
+                            int topk, int block, hipStream_t s, const SelGates* gates = nullptr);
 constexpr int kListChunk = 256;  // list entries per work item of the key-major kernels
 
 // Saved context of a sparse-scope training forward, read by its backward:

@@ -6,6 +6,9 @@
 //   bits   per token, a bitmask of its valid selected blocks (m < own block;
 //          entries out of range or repeated count once), and pre, the number of
 //          set bits before each 32-block word (pre[MWB] = number selected).
+//          Optionally also the log gates of the token's slots, so that the
+//          forward reads one contiguous record per (token, slot) instead of
+//          gathering a score and an LSE_s per query row.
 //   count  per (KV head, word w, token segment): how many tokens of the segment
 //          select each of the word's 32 blocks.
 //   scan   per KV head: exclusive offsets over (block, segment), so each
@@ -28,14 +31,18 @@ constexpr int SEG = 512;           // tokens per segment of the count / fill pas
 constexpr int kSegsPerSpan = 4;    // segments per token span of the work items (2048 tokens)
 
 // One wave per token: lane e ORs its entry's bit into the wave's words in LDS
-// (a repeated entry sets the same bit), then lane w takes word w.
+// (a repeated entry sets the same bit), then lane w takes word w.  With gates,
+// lane e then writes the log gates of its entry's slot (the slot's rank from
+// the words and their prefix counts; a repeated entry writes the same values
+// to the same slot).
 constexpr int kMaxWords = 512;  // 16384 blocks, the most a sparse-scope call accepts
 
 __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict__ idx,
                                                       uint32_t* __restrict__ bits,
                                                       uint16_t* __restrict__ pre, int N, int topk,
-                                                      int block, int MWB, size_t tokens) {
+                                                      int block, int MWB, size_t tokens, SelGates sg) {
   __shared__ uint32_t wsh[4][kMaxWords];
+  __shared__ uint16_t psh[4][kMaxWords];
   const size_t tok = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (tok >= tokens) return;
@@ -65,10 +72,41 @@ __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict_
       const int y = __shfl_up(incl, off, 64);
       if (lane >= off) incl += y;
     }
-    if (w < MWB) pre[tok * (MWB + 1) + w] = uint16_t(carry + incl - cnt);
+    if (w < MWB) {
+      pre[tok * (MWB + 1) + w] = uint16_t(carry + incl - cnt);
+      psh[wave][w] = uint16_t(carry + incl - cnt);
+    }
     carry += __shfl(incl, 63, 64);
   }
   if (lane == 0) pre[tok * (MWB + 1) + MWB] = uint16_t(carry);
+  if (sg.out == nullptr) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // query row of head h of the group: (pair G + h) N + t
+  const int G = sg.G;
+  const size_t r0 = (tok / N) * size_t(G) * N + t;
+  for (int e = lane; e < topk; e += 64) {
+    const int m = ir[e];
+    if (m < 0 || m >= c) continue;
+    const int wd = m >> 5;
+    const uint32_t slot = psh[wave][wd] + uint32_t(__popc(ws[wd] & ((1u << (m & 31)) - 1u)));
+    float x[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      if (h < G) {
+        const size_t r = r0 + size_t(h) * N;
+        x[h] = (sg.scores[r * sg.C + m] - sg.lse_s[r]) * kLog2e;
+      }
+    float* op = sg.out + (tok * topk + slot) * G;
+    if (G == 4) {
+      *reinterpret_cast<float4*>(op) = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (h < G) op[h] = x[h];
+    }
+  }
 }
 
 // One wave per (KV head, word, segment).  FILL = false: counts; true: entries.
@@ -283,12 +321,17 @@ SparseCtx sparse_ctx_layout(const Dims& d, int topk, char* base, size_t* bytes) 
 }
 
 hipError_t launch_sel_lists(const int32_t* idx, const SelLists& L, int B, int Hkv, int N, int C,
-                            int topk, int block, hipStream_t s) {
+                            int topk, int block, hipStream_t s, const SelGates* gates) {
   const size_t tokens = size_t(B) * Hkv * N;
   const int pairs = B * Hkv;
   if (L.MWB > kMaxWords) return hipErrorInvalidValue;  // more blocks than the entry points accept
+  SelGates sg{};
+  if (gates) {
+    if (gates->G < 1 || gates->G > 8) return hipErrorInvalidValue;
+    sg = *gates;
+  }
   SAS_LAUNCH("selbits", selbits_kernel, dim3((tokens + 3) / 4), dim3(256), 0, s, idx, L.bits, L.pre, N,
-             topk, block, L.MWB, tokens);
+             topk, block, L.MWB, tokens, sg);
   if (C > 0) {
     SAS_LAUNCH("sel_count", sel_pass_kernel<false>, dim3(pairs * L.MWB * L.nseg), dim3(64), 0, s, L, N, C,
                block);
