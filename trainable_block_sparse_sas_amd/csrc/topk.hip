@@ -41,12 +41,14 @@ __device__ __forceinline__ int row_candidates(const int32_t* __restrict__ cache_
 // Group score of each of the lane's PER candidates m[i] (where ok[i]): the sum
 // of the row's hpr head scores, hstride floats apart, added in head order.
 // Every load of a chunk of HC heads is issued before the first add, so a row
-// costs one memory round trip per chunk rather than one per head (HC shrinks
-// as PER grows, to bound the registers the loads hold).
+// costs one memory round trip per chunk rather than one per head.  From 8
+// candidates a lane on, a chunk is one head: the registers the loads would
+// hold cost more occupancy than the round trips (rows of 512 candidates and
+// 4 heads: 0.38 ms at one head per chunk, 0.41 ms at four).
 template <int PER>
 __device__ __forceinline__ void group_sum(const float* __restrict__ row0, size_t hstride, int hpr,
                                           const int (&m)[PER], const bool (&ok)[PER], float (&u)[PER]) {
-  constexpr int HC = PER <= 8 ? 4 : 1;
+  constexpr int HC = PER <= 4 ? 4 : 1;
 #pragma unroll
   for (int i = 0; i < PER; ++i) u[i] = 0.f;
   for (int h0 = 0; h0 < hpr; h0 += HC) {
