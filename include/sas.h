@@ -189,6 +189,27 @@ int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len,
                     void* stream);
 
 /*
+ * sas_topk_select_gated -- sas_topk_select on training rows (cache_len NULL,
+ *   c = t / block candidates) that also writes, for the selection, the
+ *   softmax gate's base-2 log gates (review "Why the Four Design Choices
+ *   Matter": log g = s - LSE(s)), which sas_gated_attn_fwd_ctx can take
+ *   instead of gathering them from the scores again.
+ * scores, idx:  as sas_topk_select; idx is the same, bit for bit.
+ * lse_s:        fp32 [B, Hkv*heads_per_row, Nq] LSE_s of each query row (as
+ *               sas_score_blocks_lse writes it).
+ * gates:        fp32 [B, Hkv, Nq, topk, heads_per_row] output: slot j of row
+ *               t holds, for the j-th smallest selected block m (ascending
+ *               block order, j < min(topk, c)), (s[t,m] - LSE_s(t)) log2 e of
+ *               each query head of the group, computed in fp32 in that
+ *               order; slots from min(topk, c) on are not written.
+ * Errors: as sas_topk_select; SAS_EUNSUPPORTED for C > 1024, topk > 64 or
+ *         heads_per_row other than 1, 2, 4 and 8.
+ */
+int sas_topk_select_gated(const float* scores, const float* lse_s, int32_t* idx,
+                          float* gates, int B, int Hkv, int heads_per_row,
+                          int Nq, int C, int block, int topk, void* stream);
+
+/*
  * sas_gated_attn_fwd -- SAS gated attention forward (blog 方法核心; review
  *   "New Approach", paper Eq. 9; tiled FlashAttention-style evaluation with
  *   an online softmax: review "A Concrete Walkthrough", kernel paragraph).
@@ -246,6 +267,11 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v,
  *            unchanged and passes the same scores, idx and LSE_s (no check is
  *            made: a context of other inputs gives wrong gradients).
  *            Unlike a workspace, it carries data from one call to the next.
+ * gates (forward): NULL, or the log gates that sas_topk_select_gated wrote
+ *            for these scores, LSE_s and idx (fp32 [B, Hkv, N, topk, Hq/Hkv]);
+ *            the forward then reads them instead of gathering each selected
+ *            entry's score (same values, so the same results).  Read only;
+ *            SAS_EINVAL without idx.
  * ds (backward): the history columns m < c(t) as in sas_gated_attn_bwd; the
  *            other columns (0 there) may be left unwritten: a caller that
  *            wants the dense form fills ds with zeros once.
@@ -254,11 +280,11 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v,
  */
 int sas_gated_attn_fwd_ctx(const void* q, const void* k, const void* v,
                            const float* scores, const int32_t* idx,
-                           const float* lse_s, void* o, float* lse, int B,
-                           int Hq, int Hkv, int N, int D, int block, int topk,
-                           float scale, int dtype, void* ctx, size_t ctx_bytes,
-                           void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           const float* lse_s, const float* gates, void* o,
+                           float* lse, int B, int Hq, int Hkv, int N, int D,
+                           int block, int topk, float scale, int dtype,
+                           void* ctx, size_t ctx_bytes, void* workspace,
+                           size_t workspace_bytes, void* stream);
 int sas_gated_attn_bwd_ctx(const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* scores,
                            const int32_t* idx, const float* lse,

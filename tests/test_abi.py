@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert set(names) == {"sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select",
+    assert set(names) == {"sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_topk_select_gated",
                           "sas_gated_attn_fwd", "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx",
                           "sas_gated_attn_bwd_ctx",
                           "sas_gated_attn_bwd", "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate",
@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_workspace_sizes():
-    assert sas.sas_abi_version() == 105
+    assert sas.sas_abi_version() == 106
     assert sas.sas_workspace_bytes(sas.SAS_OP_SCORE, 1, 32, 8, 8192, 128, 64, -1, 1) == 0
     assert sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 32, 8, 8192, 128, 64, -1, 1) >= 32 * 8192 * 4
     assert sas.sas_workspace_bytes(sas.SAS_OP_DECODE, 8, 32, 8, 131072, 128, 64, 16, 1) > 0
@@ -334,10 +334,35 @@ def test_saved_context_sizes_and_validation_on_the_host():
     wb = sas.sas_workspace_bytes(sas.SAS_OP_BWD, 1, 8, 2, 512, 128, 64, 4, bf)
     fwd, bwd = L.sas_gated_attn_fwd_ctx, L.sas_gated_attn_bwd_ctx
     sizes = (1, 8, 2, 512, 128, 64, 4, f(0.1), bf)
-    assert fwd(d, d, d, d, d, d, d, d, *sizes, N, 0, d, wf, N) == sas.SAS_EWORKSPACE
+    assert fwd(d, d, d, d, d, d, N, d, d, *sizes, N, 0, d, wf, N) == sas.SAS_EWORKSPACE
     assert "context" in sas.sas_last_error()
-    assert fwd(d, d, d, d, d, d, d, d, *sizes, d, n - 1, d, wf, N) == sas.SAS_EWORKSPACE
-    assert fwd(d, d, d, d, d, d, d, d, *sizes, d, n, d, wf - 1, N) == sas.SAS_EWORKSPACE
+    assert fwd(d, d, d, d, d, d, N, d, d, *sizes, d, n - 1, d, wf, N) == sas.SAS_EWORKSPACE
+    assert fwd(d, d, d, d, d, d, d, d, d, *sizes, d, n, d, wf - 1, N) == sas.SAS_EWORKSPACE
+    # given log gates belong to a selection: not at full scope
+    full = (1, 8, 2, 512, 128, 64, 0, f(0.1), bf)
+    assert fwd(d, d, d, d, N, d, d, d, d, *full, N, 0, d, 1 << 40, N) == sas.SAS_EINVAL
+    assert "idx" in sas.sas_last_error()
     assert bwd(d, d, d, d, d, d, d, d, d, N, 0, d, d, d, d, *sizes, d, wb, N) == sas.SAS_EWORKSPACE
     assert bwd(d, d, d, d, d, d, d, d, d, d, n - 1, d, d, d, d, *sizes, d, wb, N) == sas.SAS_EWORKSPACE
     assert bwd(d, d, d, d, d, d, d, d, d, d, n, d, d, N, d, *sizes, d, wb, N) == sas.SAS_EINVAL
+
+
+def test_gated_topk_validation_on_the_host():
+    """sas_topk_select_gated: argument checks before any launch; its range is the
+    one-wave-per-row Top-K (C <= 1024, topk <= 64, heads_per_row 1, 2, 4, 8)."""
+    N = None
+    v = ctypes.c_void_p(256)
+    call = L.sas_topk_select_gated
+    # empty sizes and topk 0 are no-ops even with NULL tensors
+    assert call(N, N, N, N, 0, 2, 4, 16, 8, 64, 4, N) == sas.SAS_OK
+    assert call(N, N, N, N, 1, 2, 4, 16, 8, 64, 0, N) == sas.SAS_OK
+    assert call(v, v, v, N, 1, 2, 4, 16, 8, 64, 4, N) == sas.SAS_EINVAL
+    assert "gates" in sas.sas_last_error()
+    assert call(v, N, v, v, 1, 2, 4, 16, 8, 64, 4, N) == sas.SAS_EINVAL
+    assert call(v, v, v, v, 1, 2, 0, 16, 8, 64, 4, N) == sas.SAS_EINVAL
+    assert call(v, v, v, v, 1, 2, 4, 16, 8, 0, 4, N) == sas.SAS_EINVAL
+    assert call(v, v, v, v, 1, 2, 4, 16, 8, 64, -1, N) == sas.SAS_EINVAL
+    assert call(v, v, v, v, 1, 2, 4, 16, 1025, 64, 4, N) == sas.SAS_EUNSUPPORTED
+    assert call(v, v, v, v, 1, 2, 4, 16, 8, 64, 65, N) == sas.SAS_EUNSUPPORTED
+    assert call(v, v, v, v, 1, 2, 16, 16, 8, 64, 4, N) == sas.SAS_EUNSUPPORTED
+    assert call(v, v, v, v, 1, 2, 3, 16, 8, 64, 4, N) == sas.SAS_EUNSUPPORTED

@@ -55,7 +55,9 @@ def test_training_entry_points_deterministic(topk):
     q, k, v, do = training_inputs(w, device=DEV)
     step = TrainStep(w.B, w.Hq, w.Hkv, w.N, w.D, w.block, topk, torch.bfloat16)
     sel_outs = [step.kbar, step.lse_s] + ([] if topk is None else [step.idx])
-    _twice(lambda: step.select(q, k), sel_outs)  # the gate normaliser LSE_s
+    # the gate normaliser LSE_s; the gated Top-K's log gates (slots from the
+    # row's candidate count on are not written)
+    _twice(lambda: step.select(q, k), sel_outs, partial=[] if step.gates is None else [step.gates])
     _twice(lambda: step.select(q, k), [step.scores], fill=float("-inf"))  # history columns
     grads = [step.dq, step.dk, step.dv, step.ds]
     # LSE_s computed, lists built by each call
@@ -140,7 +142,7 @@ def test_benchmark_shapes_deterministic():
     # keeps the step's -inf and zero fills), so they are not refilled
     _twice(lambda: step.run(q, k, v, do),
            [step.kbar, step.idx, step.o, step.lse, step.lse_s, step.dq, step.dk, step.dv],
-           partial=[step.scores, step.ds])
+           partial=[step.scores, step.ds] + ([] if step.gates is None else [step.gates]))
     del step, q, k, v, do
     torch.cuda.empty_cache()
     w = WORKLOADS[4]

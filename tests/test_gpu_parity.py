@@ -220,6 +220,57 @@ def test_topk_bit_exact(case):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+GATED_TOPK_CASES = [
+    # C, hpr, block, topk: the one-wave-per-row range (C <= 1024, topk <= 64)
+    (40, 4, 1, 5),
+    (300, 1, 1, 32),
+    (500, 8, 1, 17),
+    (900, 2, 1, 64),
+    (160, 4, 64, 32),
+]
+
+
+@pytest.mark.parametrize("case", GATED_TOPK_CASES, ids=[f"C{c[0]}-g{c[1]}-b{c[2]}-k{c[3]}" for c in GATED_TOPK_CASES])
+def test_topk_gated_bit_exact(case):
+    """sas_topk_select_gated: idx bit for bit as the oracle's Top-K (and as
+    sas_topk_select), and slot j of row t holds (s[t, m_j] - LSE_s(t)) log2 e
+    for the j-th smallest selected block m_j of every head of the group (the
+    softmax gate's log g = s - LSE(s) of jaehun.me review, "Why the Four
+    Design Choices Matter", in base 2), as fp32 evaluates that expression;
+    slots from min(topk, c) on are left as they were."""
+    C, hpr, block, topk = case
+    Hkv, B = 2, 1
+    N = C + 8 if block == 1 else C * block
+    s = score_matrix((B, Hkv * hpr, N, C), seed=C + 7)
+    s = torch.round(s * 8) / 8  # many exact ties
+    s[0, 0, :, :3] = torch.tensor([float("nan"), -0.0, 0.0])
+    s[0, 0, :, 3:5] = torch.tensor([float("inf"), float("-inf")])
+    lse_s = torch.randn((B, Hkv * hpr, N), generator=torch.Generator().manual_seed(C)) * 3.0
+    c = np.minimum(np.arange(N) // block, C)
+    ref = orc.topk_select(s.numpy(), hpr, c[None, :], topk)
+    idx = torch.empty((B, Hkv, N, topk), dtype=torch.int32, device=DEV)
+    gates = torch.full((B, Hkv, N, topk, hpr), 7.0, dtype=torch.float32, device=DEV)
+    sd, ld = s.to(DEV), lse_s.to(DEV)
+    sas.sas_topk_select_gated(sd, ld, idx, gates, block)
+    idx2 = torch.empty_like(idx)
+    sas.sas_topk_select(sd, idx2, None, hpr, block)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(idx2.cpu().numpy(), got)
+    # expected log gates, in fp32, by slot in ascending block order
+    srt = np.sort(np.where(ref >= 0, ref, np.iinfo(np.int32).max), axis=-1)
+    valid = srt != np.iinfo(np.int32).max
+    m = torch.from_numpy(np.where(valid, srt, 0).astype(np.int64))  # [B, Hkv, N, topk]
+    sg = s.reshape(B, Hkv, hpr, N, C)
+    lg = lse_s.reshape(B, Hkv, hpr, N)
+    sel = torch.gather(sg, 4, m[:, :, None, :, :].expand(B, Hkv, hpr, N, topk))  # [B, Hkv, hpr, N, topk]
+    log2e = torch.tensor(1.4426950408889634, dtype=torch.float32)
+    exp = ((sel - lg[..., None]) * log2e).permute(0, 1, 3, 4, 2)  # [B, Hkv, N, topk, hpr]
+    exp = torch.where(torch.from_numpy(valid)[..., None], exp, torch.tensor(7.0))
+    torch.testing.assert_close(gates.cpu(), exp, rtol=0, atol=0, equal_nan=True)
+
+
 DECODE_CASES = [
     # name, dtype, Hq, Hkv, D, L, block, topk
     ("bf16-g4", "bf16", 8, 2, 128, 2048, 64, 4),

@@ -32,7 +32,7 @@ SAS_OP_PREFILL = 11
 SAS_OP_CTX = 12
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW, SAS_GATE_OUTER, SAS_GATE_STE = 0, 1, 2, 3, 4
 
-EXPORTED = ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
+EXPORTED = ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_topk_select_gated", "sas_gated_attn_fwd",
             "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx", "sas_gated_attn_bwd", "sas_gated_attn_bwd_ctx",
             "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
             "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged", "sas_workspace_bytes", "sas_last_error", "sas_abi_version",
@@ -42,10 +42,11 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 _lib.sas_score_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
 _lib.sas_score_blocks_lse.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _vp]
 _lib.sas_topk_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.sas_topk_select_gated.argtypes = [_vp] * 4 + [_i] * 7 + [_vp]
 _lib.sas_gated_attn_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd_lse.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
-_lib.sas_gated_attn_fwd_ctx.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp, _sz, _vp]
+_lib.sas_gated_attn_fwd_ctx.argtypes = [_vp] * 9 + [_i] * 7 + [_f, _i, _vp, _sz, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd_ctx.argtypes = [_vp] * 10 + [_sz] + [_vp] * 4 + [_i] * 7 + [_f, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_fwd_gate.argtypes = [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
 _lib.sas_gated_attn_bwd_gate.argtypes = [_vp] * 13 + [_i] * 7 + [_f, _i, _i, _vp, _sz, _vp]
@@ -65,7 +66,7 @@ _lib.sas_profile_enable.restype = _i
 _lib.sas_profile_read.argtypes = [_i, ctypes.c_char_p, _i, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(_i)]
 _lib.sas_profile_read.restype = _i
-for _name in ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_gated_attn_fwd",
+for _name in ("sas_score_blocks", "sas_score_blocks_lse", "sas_topk_select", "sas_topk_select_gated", "sas_gated_attn_fwd",
               "sas_gated_attn_fwd_lse", "sas_gated_attn_fwd_ctx", "sas_gated_attn_bwd", "sas_gated_attn_bwd_ctx",
               "sas_gated_attn_fwd_gate", "sas_gated_attn_bwd_gate", "sas_sparse_decode", "sas_selector_bwd", "sas_pool_pages", "sas_paged_decode",
               "sas_sparse_decode_noalloc", "sas_decode_step", "sas_prefill_paged"):
@@ -206,6 +207,15 @@ def sas_topk_select(scores, idx, cache_len, heads_per_row, block, workspace=None
                                 block, topk, _p(workspace), wsb, _stream(stream)))
 
 
+def sas_topk_select_gated(scores, lse_s, idx, gates, block, stream=None):
+    """Training Top-K (scores fp32 [B, Hkv*hpr, N, C], idx int32 [B, Hkv, N, K]) that also writes
+    gates fp32 [B, Hkv, N, K, hpr]: the selection's base-2 log gates by slot (ascending block)."""
+    B, H, Nq, C = scores.shape
+    Hkv, topk, hpr = idx.shape[1], idx.shape[-1], gates.shape[-1]
+    _check(_lib.sas_topk_select_gated(_p(scores), _p(lse_s), _p(idx), _p(gates), B, Hkv, hpr, Nq, C, block,
+                                      topk, _stream(stream)))
+
+
 def sas_gated_attn_fwd(q, k, v, scores, idx, o, lse, lse_s, block, scale, workspace=None,
                        stream=None):
     B, Hq, N, D = q.shape
@@ -230,16 +240,17 @@ def sas_gated_attn_fwd_lse(q, k, v, scores, idx, lse_s, o, lse, block, scale, wo
 
 
 def sas_gated_attn_fwd_ctx(q, k, v, scores, idx, lse_s, o, lse, block, scale, ctx, workspace=None,
-                           stream=None):
+                           stream=None, gates=None):
     """The training forward with LSE_s given that also fills the saved context `ctx`
-    (a byte tensor of sas_workspace_bytes(SAS_OP_CTX, ...) bytes, or None if that is 0)."""
+    (a byte tensor of sas_workspace_bytes(SAS_OP_CTX, ...) bytes, or None if that is 0);
+    gates: None, or sas_topk_select_gated's log gates for these scores, LSE_s and idx."""
     B, Hq, N, D = q.shape
     Hkv = k.shape[1]
     topk = idx.shape[-1] if idx is not None else 0
     wsb = 0 if workspace is None else workspace.numel()
     cb = 0 if ctx is None else ctx.numel()
-    _check(_lib.sas_gated_attn_fwd_ctx(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(lse_s), _p(o),
-                                       _p(lse), B, Hq, Hkv, N, D, block, topk, scale, _dt(q), _p(ctx), cb,
+    _check(_lib.sas_gated_attn_fwd_ctx(_p(q), _p(k), _p(v), _p(scores), _idx_ptr(idx), _p(lse_s), _p(gates),
+                                       _p(o), _p(lse), B, Hq, Hkv, N, D, block, topk, scale, _dt(q), _p(ctx), cb,
                                        _p(workspace), wsb, _stream(stream)))
 
 

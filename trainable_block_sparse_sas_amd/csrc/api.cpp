@@ -98,7 +98,7 @@ extern "C" {
 
 const char* sas_last_error(void) { return g_error.c_str(); }
 
-int sas_abi_version(void) { return 105; }
+int sas_abi_version(void) { return 106; }
 
 size_t sas_workspace_bytes(int op, int B, int Hq, int Hkv, int n, int D, int block, int topk,
                            int dtype) {
@@ -222,6 +222,28 @@ int sas_topk_select(const float* scores, int32_t* idx, const int32_t* cache_len,
   return hip_status(e, "sas_topk_select");
 }
 
+int sas_topk_select_gated(const float* scores, const float* lse_s, int32_t* idx, float* gates, int B,
+                          int Hkv, int heads_per_row, int Nq, int C, int block, int topk, void* stream) {
+  if (B < 0 || Hkv < 1 || Nq < 0 || C < 0)
+    return fail(SAS_EINVAL, "sas_topk_select_gated: invalid sizes (B=%d Hkv=%d Nq=%d C=%d)", B, Hkv, Nq, C);
+  if (heads_per_row < 1) return fail(SAS_EINVAL, "sas_topk_select_gated: heads_per_row must be >= 1");
+  if (block < 1) return fail(SAS_EINVAL, "sas_topk_select_gated: block must be >= 1");
+  if (topk < 0) return fail(SAS_EINVAL, "sas_topk_select_gated: topk must be >= 0");
+  const int h = heads_per_row;
+  if (C > 1024 || topk > 64 || (h != 1 && h != 2 && h != 4 && h != 8))
+    return fail(SAS_EUNSUPPORTED, "sas_topk_select_gated: needs C <= 1024, topk <= 64, heads_per_row 1, 2, 4 or 8 "
+                "(C=%d topk=%d heads_per_row=%d)", C, topk, heads_per_row);
+  if (B == 0 || Nq == 0 || topk == 0) {
+    g_error.clear();
+    return SAS_OK;
+  }
+  if (!scores || !lse_s || !idx || !gates)
+    return fail(SAS_EINVAL, "sas_topk_select_gated: scores, lse_s, idx and gates must be non-NULL");
+  hipError_t e = sas::launch_topk_gated(scores, lse_s, idx, gates, B, Hkv, heads_per_row, Nq, C, block, topk,
+                                        static_cast<hipStream_t>(stream));
+  return hip_status(e, "sas_topk_select_gated");
+}
+
 static int check_attn(const char* what, int B, int Hq, int Hkv, int N, int D, int block,
                       const int32_t* idx, int topk, int dtype) {
   int st = check_common(B, Hq, Hkv, N, D, block, dtype, what);
@@ -240,7 +262,7 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
                     const int32_t* idx, void* o, float* lse, float* lse_s, int B, int Hq, int Hkv, int N,
                     int D, int block, int topk, float scale, int dtype, int gate, void* workspace,
                     size_t workspace_bytes, void* stream, bool lse_given = false, void* ctx = nullptr,
-                    size_t ctx_bytes = kNoCtx) {
+                    size_t ctx_bytes = kNoCtx, const float* gates = nullptr) {
   int st = check_attn(what, B, Hq, Hkv, N, D, block, idx, topk, dtype);
   if (!st) st = check_scale(scale, what);
   if (st) return st;
@@ -262,8 +284,9 @@ static int attn_fwd(const char* what, const void* q, const void* k, const void* 
       return fail(SAS_EWORKSPACE, "%s: saved context of %zu bytes required (got %zu)", what, cneed, ctx_bytes);
     if (!cneed) ctx = nullptr;
   }
+  if (gates && !idx) return fail(SAS_EINVAL, "%s: gates are the log gates of a selection (idx required)", what);
   hipError_t e = sas::launch_fwd(q, k, v, scores, idx, o, lse, lse_s, d, idx ? topk : 0, scale,
-                                 bf16, gate, workspace, static_cast<hipStream_t>(stream), lse_given, ctx);
+                                 bf16, gate, workspace, static_cast<hipStream_t>(stream), lse_given, ctx, gates);
   return hip_status(e, what);
 }
 
@@ -323,12 +346,12 @@ int sas_gated_attn_fwd_lse(const void* q, const void* k, const void* v, const fl
 }
 
 int sas_gated_attn_fwd_ctx(const void* q, const void* k, const void* v, const float* scores,
-                           const int32_t* idx, const float* lse_s, void* o, float* lse, int B, int Hq,
-                           int Hkv, int N, int D, int block, int topk, float scale, int dtype, void* ctx,
-                           size_t ctx_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+                           const int32_t* idx, const float* lse_s, const float* gates, void* o, float* lse,
+                           int B, int Hq, int Hkv, int N, int D, int block, int topk, float scale, int dtype,
+                           void* ctx, size_t ctx_bytes, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_fwd("sas_gated_attn_fwd_ctx", q, k, v, scores, idx, o, lse, const_cast<float*>(lse_s), B, Hq,
                   Hkv, N, D, block, topk, scale, dtype, SAS_GATE_SOFTMAX, workspace, workspace_bytes, stream,
-                  true, ctx, ctx_bytes);
+                  true, ctx, ctx_bytes, gates);
 }
 
 int sas_gated_attn_fwd_gate(const void* q, const void* k, const void* v, const float* scores,

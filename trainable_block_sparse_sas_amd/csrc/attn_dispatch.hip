@@ -39,7 +39,7 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                            int topk, float scale, int norm, bool outer, void* ws, hipStream_t s,
-                           void* ctx = nullptr);
+                           void* ctx = nullptr, const float* gates = nullptr);
 
 hipError_t launch_fwd_mfma_shared_row(const void* q, const void* k, const void* v, const float* score_row,
                                       const float* lse_s, void* o, float* lse, const Dims& d, float scale,
@@ -180,7 +180,7 @@ size_t train_ctx_bytes(const Dims& d, int topk, bool bf16) {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s, bool lse_given,
-                      void* ctx) {
+                      void* ctx, const float* gates) {
   if (gate == kGateSte) {
     // the hard gate: plain block-sparse attention (the raw gate on zero
     // scores), then the real LSE_s for the backward's soft gate
@@ -205,7 +205,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
   // gate normaliser: 0 none (lse_s holds 0), 1 computed here, 2 given in lse_s
   const int nm = !norm ? 0 : lse_given ? 2 : 1;
   if (bf16 && fwd_mfma_supported(d, topk, idx != nullptr))
-    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, nm, outer, ws, s, ctx);
+    return launch_fwd_mfma(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, nm, outer, ws, s, ctx, gates);
   return launch_fwd_simt(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, bf16, nm, outer, s);
 }
 

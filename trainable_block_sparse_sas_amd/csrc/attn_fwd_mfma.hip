@@ -516,7 +516,8 @@ size_t fwd_mfma_workspace(const Dims& d, int topk, bool sparse) {
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const float* scores,
                            const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
-                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s, void* ctx) {
+                           int topk, float scale, int norm, bool outer, void* ws, hipStream_t s, void* ctx,
+                           const float* gates) {
   FwdArgs a{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)ws, scores,
             (bf16_t*)o, lse, lse_s, d.Hq, d.Hkv, d.N, d.C, 0, 0, (d.N + KT - 1) / KT, scale, d.C};
   const int G = d.G();
@@ -527,7 +528,7 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const fl
     if (norm == 1)
       SAS_LAUNCH("lse_rows", lse_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, lse_s,
                  d.N, d.C, KT, rows);
-    return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, outer, ws, s, ctx);
+    return launch_fwd_sel(q, k, v, scores, idx, o, lse, lse_s, d, topk, scale, outer, ws, s, ctx, gates);
   }
 #define SAS_FWD_CASE(DD, GG) \
   if (d.D == DD && G == GG) return fwd_mfma_t<DD, GG>(a, d.B, norm, outer, s);

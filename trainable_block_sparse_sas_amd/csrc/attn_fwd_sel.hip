@@ -461,9 +461,12 @@ size_t fwd_sel_workspace(const Dims& d, int topk) { return fwd_sel_layout(d, top
 // Sparse-scope forward over the selection lists (LSE_s already in lse_s).
 // ctx (optional): the lists are built there instead of in the workspace, and
 // the history entries' log gates are recorded beside them for the backward.
+// gates (optional): the (token, slot) log gates, already written by the
+// gated Top-K; else the list build writes them from the scores.
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx) {
+                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx,
+                          const float* gates) {
   char* w = static_cast<char*>(ws);
   const FwdSelWs W = fwd_sel_layout(d, topk);
   SparseCtx C{};
@@ -471,13 +474,13 @@ hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const flo
   const SelLists L =
       ctx ? C.L : sel_lists_layout(d.B, d.Hkv, d.N, d.C, topk, KT, kListChunk, w + W.lists, nullptr);
   const SelGates sg{scores, lse_s, reinterpret_cast<float*>(w + W.gates), d.Hkv, d.G(), d.C};
-  const hipError_t e = launch_sel_lists(idx, L, d.B, d.Hkv, d.N, d.C, topk, KT, s, &sg);
+  const hipError_t e = launch_sel_lists(idx, L, d.B, d.Hkv, d.N, d.C, topk, KT, s, gates ? nullptr : &sg);
   if (e != hipSuccess) return e;
   FwdSelArgs a{};
   a.q = (const bf16_t*)q;
   a.k = (const bf16_t*)k;
   a.v = (const bf16_t*)v;
-  a.gates = sg.out;
+  a.gates = gates ? gates : sg.out;
   a.op = reinterpret_cast<bf16_t*>(w + W.op);
   a.stl = reinterpret_cast<float2*>(w + W.stl);
   a.sto = reinterpret_cast<float2*>(w + W.sto);

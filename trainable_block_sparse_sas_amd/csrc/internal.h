@@ -67,6 +67,11 @@ hipError_t launch_pool_pages(const void* k_pages, void* kbar_pages, const int32_
 
 // ---- Top-K ------------------------------------------------------------------------
 // Decode rows clamp cache_len to len_cap (the cache capacity, when known).
+// Training Top-K that also writes the selection's base-2 log gates
+// (s - LSE_s) log2 e, [rows][topk][hpr] by slot (ascending block order);
+// hipErrorNotSupported outside C <= 1024, topk <= 64, hpr in {1, 2, 4, 8}.
+hipError_t launch_topk_gated(const float* scores, const float* lse_s, int32_t* idx, float* gates, int B,
+                             int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_len, int B,
                        int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s,
                        int len_cap = 0x7fffffff);
@@ -121,18 +126,21 @@ size_t train_ctx_bytes(const Dims& d, int topk, bool bf16);
 size_t fwd_sel_workspace(const Dims& d, int topk);
 hipError_t launch_fwd_sel(const void* q, const void* k, const void* v, const float* scores,
                           const int32_t* idx, void* o, float* lse, const float* lse_s, const Dims& d,
-                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx = nullptr);
+                          int topk, float scale, bool outer, void* ws, hipStream_t s, void* ctx = nullptr,
+                          const float* gates = nullptr);
 size_t fwd_workspace(const Dims& d, int topk, bool bf16);
 size_t bwd_workspace(const Dims& d, int topk, bool bf16);
 size_t fwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 size_t bwd_gate_workspace(const Dims& d, int topk, bool bf16, int gate);
 // lse_given (softmax gate only): lse_s already holds LSE_s; it is read, not
 // computed.  ctx (sparse scope on the matrix cores; else unused): the saved
-// context for the backward (sparse_ctx_layout) is written.
+// context for the backward (sparse_ctx_layout) is written.  gates (same
+// scope): the selection's log gates from launch_topk_gated, read instead of
+// the scores' selected entries.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* scores,
                       const int32_t* idx, void* o, float* lse, float* lse_s, const Dims& d,
                       int topk, float scale, bool bf16, int gate, void* ws, hipStream_t s,
-                      bool lse_given = false, void* ctx = nullptr);
+                      bool lse_given = false, void* ctx = nullptr, const float* gates = nullptr);
 // ctx (softmax gate, sparse scope on the matrix cores; else unused): the
 // saved context the forward wrote; the selection lists are not rebuilt.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,

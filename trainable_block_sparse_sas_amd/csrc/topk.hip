@@ -563,13 +563,22 @@ __global__ __launch_bounds__(64 * W) void topk_runs_kernel(const float* __restri
 // c >= K), so only keys at or above it survive; with many equal scores (more
 // than 64 survivors) the wave radix select picks exactly K instead.  The
 // survivors are sorted in one 64-lane bitonic network, lane e holding the
-// e-th largest.
-template <int PER>
+// e-th largest.  GH > 0 (training rows, GH = hpr): lane e also writes the softmax gate's
+// base-2 log gates (s - LSE_s) log2 e of its block for every head of the row,
+// at the block's slot, its rank in ascending block order among the selected
+// (the slot the key-major attention kernels give it), so the forward need not
+// gather them from the scores it has just left.
+struct TopkGates {
+  const float* lse_s;  // [B, Hkv hpr, Nq] gate normaliser of each query row
+  float* out;          // [rows][topk][hpr]
+};
+
+template <int PER, int GH>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores,
                                                         int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ cache_len, int Hkv,
                                                         int hpr, int Nq, int C, int block, int topk,
-                                                        int len_cap, long total_rows) {
+                                                        int len_cap, long total_rows, TopkGates tg) {
   __shared__ uint32_t hist[4][256];
   __shared__ uint64_t surv[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -634,7 +643,35 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   wave_sync();
   uint64_t x[1] = {lane < n ? surv[w][lane] : 0ull};
   build_runs<1, 2, 64, uint64_t>(x, lane);
-  if (lane < topk) out[lane] = lane < K ? int(~uint32_t(x[0])) : -1;
+  const int me = int(~uint32_t(x[0]));  // lane e < K: the e-th best block
+  if (lane < topk) out[lane] = lane < K ? me : -1;
+  if constexpr (GH > 0) {
+    // the block's scores were read above (cache hits); all loads go out
+    // first (lanes past K read column 0), then the slot, the block's rank in
+    // ascending block order among the K selected, is counted while they are
+    // in flight
+    const size_t r0 = (size_t(b) * Hkv + g) * GH * size_t(Nq) + t;  // query row of head 0
+    const int mc = lane < K ? me : 0;
+    float sv[GH], lv[GH];
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      const size_t r = r0 + size_t(h) * Nq;
+      sv[h] = scores[r * C + mc];
+      lv[h] = tg.lse_s[r];
+    }
+    int slot = 0;
+    for (int j = 0; j < K; ++j) slot += __builtin_amdgcn_readlane(me, j) < me ? 1 : 0;
+    if (lane < K) {
+      float* op = tg.out + (size_t(row) * topk + slot) * GH;
+      if constexpr (GH == 4) {
+        *reinterpret_cast<float4*>(op) = make_float4((sv[0] - lv[0]) * kLog2e, (sv[1] - lv[1]) * kLog2e,
+                                                     (sv[2] - lv[2]) * kLog2e, (sv[3] - lv[3]) * kLog2e);
+      } else {
+#pragma unroll
+        for (int h = 0; h < GH; ++h) op[h] = (sv[h] - lv[h]) * kLog2e;
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -645,15 +682,16 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
   if (rows == 0 || topk == 0) return hipSuccess;
   if (C <= 1024 && topk <= 64) {
     const dim3 grid((rows + 3) / 4);
+    const TopkGates tg{};
     if (C <= 256)
-      SAS_LAUNCH("topk", (topk_wave_kernel<4>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, len_cap, rows);
+      SAS_LAUNCH("topk", (topk_wave_kernel<4, 0>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr,
+                 Nq, C, block, topk, len_cap, rows, tg);
     else if (C <= 512)
-      SAS_LAUNCH("topk", (topk_wave_kernel<8>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, len_cap, rows);
+      SAS_LAUNCH("topk", (topk_wave_kernel<8, 0>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr,
+                 Nq, C, block, topk, len_cap, rows, tg);
     else
-      SAS_LAUNCH("topk", (topk_wave_kernel<16>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr, Nq, C,
-                 block, topk, len_cap, rows);
+      SAS_LAUNCH("topk", (topk_wave_kernel<16, 0>), grid, dim3(256), 0, s, scores, idx, cache_len, Hkv, hpr,
+                 Nq, C, block, topk, len_cap, rows, tg);
   } else if (C <= 256) {
     SAS_LAUNCH("topk", (topk_kernel<1, 4>), dim3((rows + 3) / 4), dim3(256), 0, s, scores, idx,
                        cache_len, Hkv, hpr, Nq, C, block, topk, len_cap, rows);
@@ -699,6 +737,33 @@ hipError_t launch_topk(const float* scores, int32_t* idx, const int32_t* cache_l
     else SAS_TOPK_LONG(16, 64);
 #undef SAS_TOPK_LONG
   }
+  return hipGetLastError();
+}
+
+// Training rows (c = t / block), with the selection's log gates; the wave
+// kernel's range only (C <= 1024, topk <= 64, hpr one of 1, 2, 4, 8).
+hipError_t launch_topk_gated(const float* scores, const float* lse_s, int32_t* idx, float* gates, int B,
+                             int Hkv, int hpr, int Nq, int C, int block, int topk, hipStream_t s) {
+  const long rows = long(B) * Hkv * Nq;
+  if (rows == 0 || topk == 0) return hipSuccess;
+  if (C > 1024 || topk > 64) return hipErrorNotSupported;
+  const dim3 grid((rows + 3) / 4);
+  const TopkGates tg{lse_s, gates};
+  const int cap = 0x7fffffff;
+#define SAS_TOPK_GATED(PER, GH)                                                                              \
+  SAS_LAUNCH("topk", (topk_wave_kernel<PER, GH>), grid, dim3(256), 0, s, scores, idx, nullptr, Hkv, hpr, Nq, C, \
+             block, topk, cap, rows, tg)
+#define SAS_TOPK_GATED_PER(GH)                \
+  if (C <= 256) SAS_TOPK_GATED(4, GH);         \
+  else if (C <= 512) SAS_TOPK_GATED(8, GH);    \
+  else SAS_TOPK_GATED(16, GH);
+  if (hpr == 1) { SAS_TOPK_GATED_PER(1) }
+  else if (hpr == 2) { SAS_TOPK_GATED_PER(2) }
+  else if (hpr == 4) { SAS_TOPK_GATED_PER(4) }
+  else if (hpr == 8) { SAS_TOPK_GATED_PER(8) }
+  else return hipErrorNotSupported;
+#undef SAS_TOPK_GATED_PER
+#undef SAS_TOPK_GATED
   return hipGetLastError();
 }
 

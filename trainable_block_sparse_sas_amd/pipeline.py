@@ -1,8 +1,10 @@
 """Buffers and call sequences of the two SAS hot paths on one GPU.
 
 Training (full or sparse scope):  sas_score_blocks_lse (pool + score + the gate
-  normaliser) -> sas_topk_select (sparse scope only) -> sas_gated_attn_fwd_ctx
-  (LSE_s given; saves the selection lists and log gates) -> sas_gated_attn_bwd_ctx.
+  normaliser) -> sas_topk_select_gated (sparse scope only; also the selection's
+  log gates; sas_topk_select where C > 1024 or K > 64) -> sas_gated_attn_fwd_ctx
+  (LSE_s and the log gates given; saves the selection lists and log gates) ->
+  sas_gated_attn_bwd_ctx.
 Decode:  sas_score_blocks (group-summed scores from pooled keys kept beside the
   cache) -> sas_topk_select -> sas_sparse_decode.
 
@@ -49,11 +51,17 @@ class TrainStep:
         n_ctx = sas.sas_workspace_bytes(sas.SAS_OP_CTX, B, Hq, Hkv, N, D, block, tk, sdt)
         self.ctx = torch.empty(n_ctx, dtype=torch.uint8, device=dev) if n_ctx else None
         self._ctx_valid = False
+        # the selection's log gates from the gated Top-K (its range only)
+        G = Hq // Hkv
+        gated = topk is not None and 0 < topk <= 64 and C <= 1024 and G in (1, 2, 4, 8)
+        self.gates = torch.empty((B, Hkv, N, topk, G), dtype=torch.float32, device=dev) if gated else None
 
     def select(self, q, k):
         # scores and, in the same kernel, the gate normaliser LSE_s
         sas.sas_score_blocks_lse(q, k, self.kbar, self.scores, self.lse_s, self.block, self.scale)
-        if self.idx is not None:
+        if self.gates is not None:
+            sas.sas_topk_select_gated(self.scores, self.lse_s, self.idx, self.gates, self.block)
+        elif self.idx is not None:
             sas.sas_topk_select(self.scores, self.idx, None, self.Hq // self.Hkv, self.block)
 
     def forward(self, q, k, v, scores=None, idx=None):
@@ -61,7 +69,7 @@ class TrainStep:
         idx = self.idx if idx is None else idx
         if own:  # LSE_s from select(); the saved context filled for the backward
             sas.sas_gated_attn_fwd_ctx(q, k, v, self.scores, idx, self.lse_s, self.o, self.lse, self.block,
-                                       self.scale, self.ctx, self.ws_fwd)
+                                       self.scale, self.ctx, self.ws_fwd, gates=self.gates)
         else:
             sas.sas_gated_attn_fwd(q, k, v, self.scores if scores is None else scores, idx, self.o, self.lse,
                                    self.lse_s, self.block, self.scale, self.ws_fwd)
