@@ -104,6 +104,8 @@ def test_training_fullsize(wi):
     gpu_chain_idx = None if w.topk is None else step.idx.cpu().numpy()
     s32 = _oracle_scores_f32(q64, kbar_r, w.block, w.scale)
     rows = _sample_rows(w.N, w.block)
+    if step.gates is not None:  # the gated Top-K of the step's selection
+        _check_gates(step, rows, G)
     # GPU scores from the oracle's pooled keys, sampled rows.
     kbar_dev = torch.tensor(kbar_r).to(dt).to(DEV)
     sas.sas_score_blocks(q, None, kbar_dev, step.scores, None, w.block, w.scale)
@@ -162,6 +164,27 @@ def test_training_fullsize(wi):
                                    rows=attend)
     normwise(to64(step.dk[0, g_chk, keys]), dk_r, 2e-2, "dk")
     normwise(to64(step.dv[0, g_chk, keys]), dv_r, 2e-2, "dv")
+
+
+def _check_gates(step, rows, G):
+    """The log gates sas_topk_select_gated wrote beside the step's selection, on
+    sampled rows: slot j holds (s - LSE_s) log2 e of the j-th smallest selected
+    block for every head of the group, bit for bit as fp32 evaluates it from
+    the step's own scores and LSE_s."""
+    idx = step.idx[:, :, rows].cpu()
+    big = torch.iinfo(torch.int32).max
+    srt, _ = torch.sort(torch.where(idx >= 0, idx, torch.full_like(idx, big)), dim=-1)
+    valid = srt != big
+    m = torch.where(valid, srt, torch.zeros_like(srt)).long()
+    B, Hkv, R, K = idx.shape
+    C = step.scores.shape[-1]
+    s = step.scores[:, :, rows].cpu().reshape(B, Hkv, G, R, C)
+    lse_s = step.lse_s[:, :, rows].cpu().reshape(B, Hkv, G, R)
+    sel = torch.gather(s, 4, m[:, :, None].expand(B, Hkv, G, R, K))
+    log2e = torch.tensor(1.4426950408889634, dtype=torch.float32)
+    want = ((sel - lse_s[..., None]) * log2e).permute(0, 1, 3, 4, 2)
+    got = step.gates[:, :, rows].cpu()
+    assert torch.equal(got[valid], want[valid]), "log gates of the gated Top-K"
 
 
 @pytest.mark.parametrize("gate", ["sigmoid", "raw", "outer"])
