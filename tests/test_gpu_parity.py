@@ -143,6 +143,14 @@ def test_training_step_own_path(case):
     step.forward(q, k, v)  # the step's own scores: LSE_s given, the context saved
     torch.cuda.synchronize()
     assert torch.equal(step.lse_s, lse_s_in), "lse_s is an input of the forward"
+    if step.gates is not None:
+        # the gated Top-K's log gates stand in for the forward's own: same bits
+        o2, lse2 = torch.empty_like(step.o), torch.empty_like(step.lse)
+        ctx2 = None if step.ctx is None else torch.empty_like(step.ctx)
+        sas.sas_gated_attn_fwd_ctx(q, k, v, step.scores, step.idx, step.lse_s, o2, lse2, block, scale, ctx2,
+                                   step.ws_fwd)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, step.o) and torch.equal(lse2, step.lse), "forward with and without given gates"
     if tol["o_abs"] is not None:
         max_abs(to64(step.o), o_ref, tol["o_abs"], "o")
     else:
