@@ -91,13 +91,17 @@ __global__ __launch_bounds__(256) void selbits_kernel(const int32_t* __restrict_
     if (m < 0 || m >= c) continue;
     const int wd = m >> 5;
     const uint32_t slot = psh[wave][wd] + uint32_t(__popc(ws[wd] & ((1u << (m & 31)) - 1u)));
-    float x[8];
+    // every load first (heads past G repeat head G - 1), so they go out
+    // together rather than one head per round trip
+    float sv[8], lv[8], x[8];
 #pragma unroll
-    for (int h = 0; h < 8; ++h)
-      if (h < G) {
-        const size_t r = r0 + size_t(h) * N;
-        x[h] = (sg.scores[r * sg.C + m] - sg.lse_s[r]) * kLog2e;
-      }
+    for (int h = 0; h < 8; ++h) {
+      const size_t r = r0 + size_t(h < G ? h : G - 1) * N;
+      sv[h] = sg.scores[r * sg.C + m];
+      lv[h] = sg.lse_s[r];
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) x[h] = (sv[h] - lv[h]) * kLog2e;
     float* op = sg.out + (tok * topk + slot) * G;
     if (G == 4) {
       *reinterpret_cast<float4*>(op) = make_float4(x[0], x[1], x[2], x[3]);

@@ -563,11 +563,11 @@ __global__ __launch_bounds__(64 * W) void topk_runs_kernel(const float* __restri
 // c >= K), so only keys at or above it survive; with many equal scores (more
 // than 64 survivors) the wave radix select picks exactly K instead.  The
 // survivors are sorted in one 64-lane bitonic network, lane e holding the
-// e-th largest.  GH > 0 (training rows, GH = hpr): lane e also writes the softmax gate's
-// base-2 log gates (s - LSE_s) log2 e of its block for every head of the row,
-// at the block's slot, its rank in ascending block order among the selected
-// (the slot the key-major attention kernels give it), so the forward need not
-// gather them from the scores it has just left.
+// e-th largest.  GH > 0 (training rows, GH = hpr): lane e also writes the
+// softmax gate's base-2 log gates (s - LSE_s) log2 e of its block for every
+// head of the row, at the block's slot, its rank in ascending block order
+// among the selected (the slot the key-major attention kernels give it), so
+// that the forward need not gather them from the score tensor again.
 struct TopkGates {
   const float* lse_s;  // [B, Hkv hpr, Nq] gate normaliser of each query row
   float* out;          // [rows][topk][hpr]
