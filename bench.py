@@ -147,8 +147,8 @@ def bench_decode(torch, w, steps, warmup, dense=False):
     cache and L2 flushed before each timed span by a 1 GiB read (a sum over a
     1 GiB buffer).  A 1 GiB write flush leaves the memory-side cache full of
     dirty lines whose write-back then competes with the decode reads; its step
-    time is reported beside it.  The step is sas_decode_step (scores, Top-K and
-    attention in two launches); the same step through the separate calls
+    time is reported beside it.  The step is sas_decode_step (scores, Top-K,
+    per-block attention and merge, launched by one call); the same step through the separate calls
     (sas_score_blocks, sas_topk_select, sas_sparse_decode) is timed beside it.
     Dense decode is sas_sparse_decode over every cached position."""
     from trainable_block_sparse_sas_amd.inputs import decode_inputs
