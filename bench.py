@@ -469,38 +469,74 @@ def copy_probe(torch):
     del src, dst
 
 
-def cpu_baseline(w):
-    """The oracle, as it stands, on a bounded prefix sample of the workload."""
+def _threads():
+    try:
+        import threadpoolctl
+        return max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        return os.cpu_count()
+
+
+def oracle_train_ops(ws, seed):
+    """Wall-clock seconds of the oracle's training ops on workload ws (one run
+    each): pool + score, Top-K (sparse scope), forward, backward."""
     import numpy as np
     import torch
 
     from oracle import sas_oracle as orc
     from trainable_block_sparse_sas_amd.inputs import training_inputs
 
-    n_s = 16384
-    ws = w.with_(N=n_s, Hq=w.Hq // w.Hkv, Hkv=1, B=1)
-    q, k, v, do = training_inputs(ws, device="cpu", seed=1000 + w.index)
+    q, k, v, do = training_inputs(ws, device="cpu", seed=seed)
     f = lambda t: t.to(torch.float64).numpy()
     q, k, v, do = f(q), f(k), f(v), f(do)
+    ops = {}
     t0 = time.perf_counter()
     kbar = orc.pool_block_keys(k, ws.block)
-    pos = np.arange(n_s)[None, :]
+    pos = np.broadcast_to(np.arange(ws.N), (ws.B, ws.N))
     s = orc.block_scores(q, kbar, ws.block, ws.scale, pos)
-    idx = None if ws.topk is None else orc.topk_select(s.astype(np.float32), ws.Hq, pos // ws.block, ws.topk)
+    t1 = time.perf_counter()
+    idx = None
+    if ws.topk is not None:
+        idx = orc.topk_select(s.astype(np.float32), ws.Hq // ws.Hkv, pos // ws.block, ws.topk)
+    t2 = time.perf_counter()
     orc.gated_attention_forward(q, k, v, s, idx, ws.block, ws.scale)
+    t3 = time.perf_counter()
     orc.gated_attention_backward(q, k, v, do, s, idx, ws.block, ws.scale)
-    dt = time.perf_counter() - t0
+    t4 = time.perf_counter()
+    ops = {"pool_score": t1 - t0, "topk": t2 - t1, "fwd": t3 - t2, "bwd": t4 - t3}
+    return ops, t4 - t0
+
+
+def cpu_baseline(w):
+    """The oracle, as it stands, on a bounded prefix sample of the workload."""
+    n_s = 16384
+    ws = w.with_(N=n_s, Hq=w.Hq // w.Hkv, Hkv=1, B=1)
+    ops, dt = oracle_train_ops(ws, 1000 + w.index)
     pairs = attended_pairs(n_s, ws.block, ws.topk, ws.Hq, 1)
     flops = 14 * ws.D * pairs
-    try:
-        import threadpoolctl
-        cores = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
-    except Exception:
-        cores = os.cpu_count()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": dt,
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "seconds": dt, "seconds_per_op": {k: round(v, 3) for k, v in ops.items()},
             "sample": f"fp64 oracle pool+score+Top-K+fwd+bwd on the first {n_s} tokens of one KV-head "
                       f"group ({ws.Hq} query heads) of the same seeded inputs, Top-K {ws.topk}"}
+
+
+def cpu_baseline_tiny(w):
+    """The oracle on the whole small fp32 workload (full scope), all threads and
+    one thread (after one untimed run)."""
+    oracle_train_ops(w, 1000 + w.index)
+    ops, dt = oracle_train_ops(w, 1000 + w.index)
+    try:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            ops1, dt1 = oracle_train_ops(w, 1000 + w.index)
+    except Exception:
+        ops1, dt1 = None, None
+    pairs = attended_pairs(w.N, w.block, w.topk, w.Hq, w.B)
+    return {"value": 14 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "seconds": dt, "seconds_per_op": {k: round(v, 4) for k, v in ops.items()},
+            "seconds_1_thread": dt1,
+            "seconds_per_op_1_thread": None if ops1 is None else {k: round(v, 4) for k, v in ops1.items()},
+            "sample": f"fp64 oracle pool+score+fwd+bwd, whole {w.name} workload"}
 
 
 def decode_entry(r, topk):
@@ -542,7 +578,7 @@ def bench_decodes(torch, wmap):
 def cpu_baseline_decode(w):
     """The oracle's decode step (group scores from the pooled keys, Top-K,
     sparse attention; pooled keys precomputed, as on the GPU) on the same seeded
-    512K-token cache, all threads and one thread."""
+    cache as the GPU run, all threads and one thread."""
     import numpy as np
     import torch
 
@@ -552,6 +588,7 @@ def cpu_baseline_decode(w):
     q, kc, vc, lens = decode_inputs(w, device="cpu")
     f = lambda t: t.to(torch.float64).numpy()
     q64, kc64, vc64, lens_np = f(q), f(kc), f(vc), lens.numpy()
+    del kc, vc
     kbar = orc.pool_block_keys(kc64, w.block)
 
     def one():
@@ -570,7 +607,7 @@ def cpu_baseline_decode(w):
 
     try:
         import threadpoolctl
-        cores = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
+        cores = _threads()
         dt = timed()
         with threadpoolctl.threadpool_limits(1):
             dt1 = timed()
@@ -647,6 +684,12 @@ def main():
             "bwd_tflops": round(t8["flops_bwd"] / (t8["ms_bwd"] * 1e-3) / 1e12, 3),
             "step": "pool+score -> gated fwd -> gated bwd, full scope (8192 tokens, 32/8 heads, D 128)"}
         del t8
+        w0 = wmap["tiny-f32-full"]
+        t0w = bench_train(torch, w0, 20, 3)
+        out["train_tiny_f32"] = {
+            "ms_step": round(t0w["ms_step"], 4),
+            "step": "pool+score -> gated fwd -> gated bwd, full scope, fp32 (512 tokens, 2/1 heads, D 64; "
+                    "the oracle-sized parity case, timed for the record)"}
         torch.cuda.empty_cache()
         out["decode"] = bench_decodes(torch, wmap)
         out["selector_bwd"] = bench_selector_bwd(torch, w, 5)
@@ -655,6 +698,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
         if not args.quick:
             out["cpu_baseline_decode"] = cpu_baseline_decode(wmap["decode-512k-b1"])
+            out["cpu_baseline_decode_128k"] = cpu_baseline_decode(wmap["decode-128k-b8"])
+            out["cpu_baseline_tiny"] = cpu_baseline_tiny(wmap["tiny-f32-full"])
     print(json.dumps(out))
 
 
