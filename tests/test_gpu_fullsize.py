@@ -387,3 +387,52 @@ def test_decode_step_fullsize(wi, topk):
     max_abs(to64(o), o_ref, 2e-2, "o")
     _rowwise(to64(o), o_ref, 2e-2, "o per row")
     normwise(to64(lse), lse_ref, 1e-4, "lse")
+
+
+@pytest.mark.parametrize("wi,topk", [(3, 16), (4, 32)], ids=["decode-128k-b8-k16", "decode-512k-b1-k32"])
+def test_paged_decode_fullsize_matches_contiguous(wi, topk):
+    """The paged decode chain at the benchmark sizes, in bench.py's page layout
+    (pages of one block x all KV heads in a shuffled pool with spare pages, a
+    block table per sequence): the pooled pages against the oracle's pooling
+    (a sample), and the selection, o and lse bit for bit equal to
+    sas_decode_step on the same caches laid out contiguously with the same
+    pooled keys (the same kernels; only the addressing differs).
+    sas_decode_step itself is held to the oracle in test_decode_step_fullsize."""
+    w = WORKLOADS[wi].with_(topk=topk)
+    dt = w.torch_dtype
+    q, kc, vc, lens = decode_inputs(w, device=DEV)
+    C, blk = w.C, w.block
+    n_pages = w.B * C + 7
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(3))
+    table = perm[: w.B * C].reshape(w.B, C).to(torch.int32).to(DEV)
+    rows = table.reshape(-1).long()
+    kp = torch.zeros((n_pages, w.Hkv, blk, w.D), dtype=dt, device=DEV)
+    vp = torch.zeros_like(kp)
+    kp[rows] = kc.view(w.B, w.Hkv, C, blk, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * C, w.Hkv, blk, w.D)
+    vp[rows] = vc.view(w.B, w.Hkv, C, blk, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * C, w.Hkv, blk, w.D)
+    kbp = torch.zeros((n_pages, w.Hkv, w.D), dtype=dt, device=DEV)
+    sas.sas_pool_pages(kp, kbp, table.reshape(-1).contiguous(), blk)
+    torch.cuda.synchronize()
+    kbar = kbp[rows].reshape(w.B, C, w.Hkv, w.D).permute(0, 2, 1, 3).contiguous()  # [B, Hkv, C, D]
+    ref = orc.pool_block_keys(to64(kc[:1, :2]), blk)  # sequence 0, KV heads 0 and 1
+    kbar_close(to64(kbar[:1, :2]), to64(torch.tensor(ref).to(dt)), "pooled pages")
+    outs = []
+    for paged in (False, True):
+        o = torch.empty((w.B, w.Hq, w.D), dtype=dt, device=DEV)
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=DEV)
+        idx = torch.empty((w.B, w.Hkv, topk), dtype=torch.int32, device=DEV)
+        if paged:
+            ws = sas.workspace(sas.SAS_OP_PAGED_DECODE, w.B, w.Hq, w.Hkv, w.N, w.D, blk, topk, sas.SAS_BF16)
+            sas.sas_paged_decode(q, kp, vp, kbp, table, lens, topk, o, lse, blk, w.scale, idx_out=idx,
+                                 workspace=ws)
+        else:
+            ws = sas.workspace(sas.SAS_OP_DECODE_STEP, w.B, w.Hq, w.Hkv, w.N, w.D, blk, topk, sas.SAS_BF16)
+            sas.sas_decode_step(q, kbar, kc, vc, lens, topk, o, lse, blk, w.scale, idx_out=idx, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((idx, o, lse))
+        del ws
+    (i1, o1, l1), (i2, o2, l2) = outs
+    assert torch.equal(i1, i2), "paged selection"
+    assert torch.equal(o1, o2), "paged o"
+    assert torch.equal(l1, l2), "paged lse"
+    assert len(torch.unique(i1)) > topk  # selection is non-trivial
