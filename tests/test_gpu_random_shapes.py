@@ -5,7 +5,9 @@ counts, every group size the kernels specialise, D 64 and 128, blocks 16 to
 128, Top-K from 0 to past the history, bf16 and fp32; decode lengths that are
 idle, ragged, full or over the capacity.  The oracle's scores and indices feed
 the attention calls, as in the fixed training cases; decode runs the whole
-step (sas_decode_step) and is held to the oracle on the scores it selected on.
+step (sas_decode_step) and is held to the oracle on the scores it selected on;
+the gate variants (sigmoid, raw logit, outer) and the selector backward run
+on random shapes too.
 Tolerances are those of the fixed cases (tests/gpu_util.py).
 """
 import numpy as np
@@ -148,3 +150,90 @@ def test_decode_step_random_shape(i):
         normwise(to64(o)[active], o_ref[active], tol["o_rel"], "o")
     normwise(to64(lse)[active], lse_ref[active], 1e-4, "lse")
     assert torch.all(o[~torch.tensor(active)] == 0)
+
+
+GATES = ["sigmoid", "raw", "outer"]
+GATE_IDS = list(range(12))
+
+
+@pytest.mark.parametrize("i", GATE_IDS, ids=[f"gate{i}" for i in GATE_IDS])
+def test_gate_variant_random_shape(i):
+    """sas_gated_attn_fwd_gate / _bwd_gate with the sigmoid, raw-logit and outer
+    gates on random shapes, against the oracle's gate variants."""
+    dts, B, Hq, Hkv, D, N, block, topk = _train_shape(100 + i)
+    gate = GATES[i % 3]
+    print(f"case gate{i}: {gate} {dts} B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} block{block} topk{topk}", flush=True)
+    dt = torch.float32 if dts == "f32" else torch.bfloat16
+    w = Workload(f"grand{i}", "train", dts, B, Hq, Hkv, D, N, block, topk, index=60 + i)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    G, scale, tol, C = Hq // Hkv, w.scale, tolerances(dt), N // block
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(k64, block)).to(dt))
+    pos = np.broadcast_to(np.arange(N), (B, N))
+    s32 = orc.block_scores(q64, kbar_r, block, scale, pos).astype(np.float32)
+    idx = None if topk is None else orc.topk_select(s32, G, pos // block, topk)
+    scores = torch.tensor(s32).to(DEV)
+    idx_t = None if idx is None else torch.tensor(idx).to(DEV)
+    g = {"sigmoid": sas.SAS_GATE_SIGMOID, "raw": sas.SAS_GATE_RAW, "outer": sas.SAS_GATE_OUTER}[gate]
+    tk = -1 if topk is None else topk
+    sdt = sas.SAS_F32 if dt == torch.float32 else sas.SAS_BF16
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    lse_s = torch.full((B, Hq, N), 7.0, dtype=torch.float32, device=DEV)
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, block, scale, g, wsf)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, lse_s if gate == "outer" else None, dq, dk,
+                                dv, ds, block, scale, g, wsb)
+    torch.cuda.synchronize()
+    s64 = s32.astype(np.float64)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(q64, k64, v64, s64, idx, block, scale, gate=gate)
+    if tol["o_abs"] is not None:
+        max_abs(to64(o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(o), o_ref, tol["o_rel"], "o")
+    normwise(to64(lse), lse_ref, tol["lse"], "lse")
+    if gate == "outer":
+        normwise(to64(lse_s), lses_ref, tol["lse"], "lse_s")
+    else:
+        assert torch.count_nonzero(lse_s).item() == 0, "lse_s"
+    r_dq, r_dk, r_dv, r_ds = orc.gated_attention_backward(q64, k64, v64, to64(do), s64, idx, block, scale,
+                                                          gate=gate)
+    normwise(to64(dq), r_dq, tol["grad"], "dq")
+    normwise(to64(dk), r_dk, tol["grad"], "dk")
+    normwise(to64(dv), r_dv, tol["grad"], "dv")
+    normwise(to64(ds), r_ds, tol["ds"], "ds")
+
+
+SEL_IDS = list(range(6))
+
+
+@pytest.mark.parametrize("i", SEL_IDS, ids=[f"selector{i}" for i in SEL_IDS])
+def test_selector_backward_random_shape(i):
+    """sas_selector_bwd on random shapes (ragged tails, every group size, both
+    dtypes) against the oracle on the pooled keys as the GPU holds them."""
+    dts, B, Hq, Hkv, D, N, block, _ = _train_shape(200 + i)
+    print(f"case selector{i}: {dts} B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} block{block}", flush=True)
+    dt = torch.float32 if dts == "f32" else torch.bfloat16
+    C = N // block
+    g = torch.Generator().manual_seed(9000 + i)
+    q = torch.randn((B, Hq, N, D), generator=g).to(dt)
+    k = torch.randn((B, Hkv, N, D), generator=g).to(dt)
+    ds = torch.randn((B, Hq, N, C), generator=g)
+    kbar = torch.tensor(orc.pool_block_keys(to64(k), block)).to(dt)
+    scale = D ** -0.5
+    dq_ref, dkbar_ref, dk_ref = orc.selector_backward(to64(q), to64(k), ds.numpy(), block, scale, kbar=to64(kbar))
+    ws = sas.workspace(sas.SAS_OP_SELECTOR_BWD, B, Hq, Hkv, N, D, block, -1,
+                       sas.SAS_BF16 if dt == torch.bfloat16 else sas.SAS_F32)
+    dq = torch.full((B, Hq, N, D), float("nan"), dtype=dt, device=DEV)
+    dk = torch.full((B, Hkv, N, D), float("nan"), dtype=dt, device=DEV)
+    dkbar = torch.empty((B, Hkv, C, D), dtype=torch.float32, device=DEV)
+    sas.sas_selector_bwd(q.to(DEV), kbar.to(DEV), ds.to(DEV), dq, dk, block, scale, dkbar=dkbar, workspace=ws)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dt == torch.float32 else 2e-2
+    normwise(to64(dq), dq_ref, tol, "dq")
+    normwise(to64(dkbar), dkbar_ref, tol, "dkbar")
+    normwise(to64(dk), dk_ref, tol, "dk")
+    assert torch.all(dk[:, :, C * block:] == 0)
