@@ -52,7 +52,7 @@ def kernel_rows(db, by_grid=False):
     cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
     ni = cols.index("name") if "name" in cols else cols.index("kernel_name")
     si, ei = cols.index("start"), cols.index("end")
-    for r in con.execute("select * from kernels"):
+    for r in con.execute("select * from kernels order by start"):
         n = short_name(r[ni])
         if by_grid:
             n = f"{n} [{_grid(cols, r)}]"
@@ -60,18 +60,24 @@ def kernel_rows(db, by_grid=False):
 
 
 def stats(db, cmd, by_grid=False):
+    """Per kernel: launches, average, average without the kernel's first
+    launch (which runs cold: the command's warm-up), total and share."""
     agg = {}
     for n, us in kernel_rows(db, by_grid):
-        a = agg.setdefault(n, [0, 0.0])
+        a = agg.setdefault(n, [0, 0.0, None])
         a[0] += 1
         a[1] += us
+        if a[2] is None:
+            a[2] = us
     tot = sum(v[1] for v in agg.values())
     out = ["# Kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
-           "| kernel | launches | avg us | total ms | share |", "|---|---:|---:|---:|---:|"]
-    for n, (c, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+           "| kernel | launches | avg us | avg us after the first launch | total ms | share |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for n, (c, t, first) in sorted(agg.items(), key=lambda x: -x[1][1]):
         if t / tot < 1e-4:
             continue
-        out.append(f"| `{n[:120]}` | {c} | {t / c:.1f} | {t / 1e3:.3f} | {100 * t / tot:.1f}% |")
+        warm = f"{(t - first) / (c - 1):.1f}" if c > 1 else "-"
+        out.append(f"| `{n[:120]}` | {c} | {t / c:.1f} | {warm} | {t / 1e3:.3f} | {100 * t / tot:.1f}% |")
     return "\n".join(out) + "\n"
 
 
