@@ -12,7 +12,7 @@ import torch
 
 from oracle import sas_oracle as orc
 from tests.gpu_util import kbar_close, max_abs, normwise, to64
-from trainable_block_sparse_sas_amd.inputs import WORKLOADS, decode_inputs, training_inputs
+from trainable_block_sparse_sas_amd.inputs import WORKLOADS, Workload, decode_inputs, training_inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -436,3 +436,80 @@ def test_paged_decode_fullsize_matches_contiguous(wi, topk):
     assert torch.equal(o1, o2), "paged o"
     assert torch.equal(l1, l2), "paged lse"
     assert len(torch.unique(i1)) > topk  # selection is non-trivial
+
+
+def test_training_at_the_largest_topk():
+    """Sparse scope at Top-K 256, the largest the calls take (and the largest
+    rank the selection lists encode): 257 history blocks and a ragged tail.
+    Top-K bit-exact on every row; o, lse, lse_s on sampled rows; dq and ds
+    through the oracle's row gradients; dk and dv on keys of late blocks."""
+    B, Hq, Hkv, D, block, topk = 1, 2, 1, 64, 64, 256
+    N = 258 * block + 37
+    w = Workload("train-topk256", "train", "bf16", B, Hq, Hkv, D, N, block, topk, index=90)
+    dt = w.torch_dtype
+    q, k, v, do = training_inputs(w, device=DEV)
+    q64, k64, v64, do64 = to64(q), to64(k), to64(v), to64(do)
+    G, C = Hq // Hkv, N // block
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(k64, block)).to(dt))
+    s32 = _oracle_scores_f32(q64, kbar_r, block, w.scale)
+    pos = np.arange(N)[None, :] // block
+    idx = orc.topk_select(s32, G, pos, topk)
+    step = TrainStep(B, Hq, Hkv, N, D, block, topk, dt)
+    scores = torch.tensor(s32).to(DEV)
+    sas.sas_topk_select(scores, step.idx, None, G, block)
+    torch.cuda.synchronize()
+    assert np.array_equal(step.idx.cpu().numpy(), idx), "topk 256, every row"
+    idx_t = torch.tensor(idx).to(DEV)
+    step.forward(q, k, v, scores, idx_t)
+    step.backward(q, k, v, do, scores, idx_t)
+    torch.cuda.synchronize()
+    rows = _sample_rows(N, block)
+    s64 = s32.astype(np.float64)
+    o_ref, lse_ref, lses_ref = orc.gated_attention_forward(q64, k64, v64, s64, idx, block, w.scale, rows=rows)
+    max_abs(to64(step.o[:, :, rows]), o_ref, 2e-2, "o")
+    _rowwise(to64(step.o[:, :, rows]), o_ref, 2e-2, "o per row")
+    normwise(to64(step.lse[:, :, rows]), lse_ref, 1e-4, "lse")
+    normwise(to64(step.lse_s[:, :, rows]), lses_ref, 1e-4, "lse_s")
+    for h in range(Hq):
+        dq_r, ds_r = orc.row_gradients(q64, k64, v64, do64, s64, idx, block, w.scale, 0, h, rows)
+        normwise(to64(step.dq[0, h, rows]), dq_r, 2e-2, f"dq h{h}")
+        normwise(to64(step.ds[0, h, rows]), ds_r, 2e-2, f"ds h{h}")
+    keys = np.array([(C - 6) * block + 5, (C - 1) * block + 63, N - 1])
+    kb = np.unique(keys // block)
+    attend = np.nonzero(np.any(np.isin(idx[0, 0], kb), axis=-1) | np.isin(np.arange(N) // block, kb))[0]
+    dk_r, dv_r = orc.key_gradients(q64, k64, v64, do64, s64, idx, block, w.scale, 0, 0, keys, rows=attend)
+    normwise(to64(step.dk[0, 0, keys]), dk_r, 2e-2, "dk")
+    normwise(to64(step.dv[0, 0, keys]), dv_r, 2e-2, "dv")
+
+
+def test_decode_step_at_the_largest_sizes():
+    """sas_decode_step at the largest history the calls take (16384 blocks of
+    64 tokens: a 1M-token cache) and the largest Top-K (256): scores against the
+    oracle's, the selection bit-exact on those scores, o and lse against the
+    oracle's sparse decode."""
+    block, topk = 64, 256
+    L = 16384 * block
+    w = Workload("decode-1m-k256", "decode", "bf16", 1, 4, 1, 128, L, block, topk, index=91)
+    dt = w.torch_dtype
+    q, kc, vc, lens = decode_inputs(w, device=DEV)
+    C = L // block
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(to64(kc), block)).to(dt))
+    o = torch.empty((w.B, w.Hq, w.D), dtype=dt, device=DEV)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.B, w.Hkv, topk), dtype=torch.int32, device=DEV)
+    ws = sas.workspace(sas.SAS_OP_DECODE_STEP, w.B, w.Hq, w.Hkv, L, w.D, block, topk, sas.SAS_BF16)
+    sas.sas_decode_step(q, torch.tensor(kbar_r).to(dt).to(DEV), kc, vc, lens, topk, o, lse, block, w.scale,
+                        idx_out=idx, workspace=ws)
+    torch.cuda.synchronize()
+    lens_np = lens.cpu().numpy()
+    q64 = to64(q)
+    u_ref = orc.decode_scores(q64, kbar_r, lens_np, L, block, w.scale, True)
+    u_gpu = ws[: w.B * w.Hkv * C * 4].view(torch.float32).reshape(w.B, w.Hkv, C).cpu().numpy()
+    normwise(u_gpu.astype(np.float64), u_ref.astype(np.float64), 1e-5, "u")
+    c = orc.decode_candidates(lens_np, L, block)
+    idx_ref = orc.topk_select(u_gpu[:, :, None, :], 1, c[:, None], topk)[:, :, 0, :]
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), "Top-K 256 over 16383 candidates"
+    o_ref, lse_ref = orc.sparse_decode(q64, to64(kc), to64(vc), lens_np, idx_ref, block, w.scale)
+    max_abs(to64(o), o_ref, 2e-2, "o")
+    _rowwise(to64(o), o_ref, 2e-2, "o per row")
+    normwise(to64(lse), lse_ref, 1e-4, "lse")

@@ -53,6 +53,9 @@ TRAIN_CASES = [
     # key-major work items, with block lists longer than one work item
     ("bf16-g2-d64-sparse", "bf16", 2, 4, 2, 64, 640, 64, 4),
     ("bf16-g8-spans-sparse", "bf16", 1, 8, 1, 128, 4672, 64, 5),
+    # D = 64 (two P V slots per pass in the combine) with rows selecting 15,
+    # 31 and 33 .. 40 blocks: counts where the two lane halves' loops end apart
+    ("bf16-d64-many-sel", "bf16", 1, 4, 2, 64, 2600, 64, 40),
 ]
 
 

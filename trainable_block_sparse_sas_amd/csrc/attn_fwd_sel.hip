@@ -375,14 +375,20 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists
     const float wl = exp2_hw(ml.x - M);  // 0 past nsel
     lsum += wl * ml.y;
     const int n = min(64, nsel - c0);
-    int j = lane / LPS;
-    for (; j + 7 * SG < n; j += 8 * SG) {
+    // Every lane runs the same iterations: the shuffles read other lanes'
+    // weights, and a lane reading an inactive lane's register gets 0.  Lane
+    // half hf (SG = 2: two slots per pass) takes slot j0 + hf; past n it
+    // reads a valid slot with weight 0.
+    const int hf = lane / LPS;
+    int j0 = 0;
+    for (; j0 + 8 * SG <= n; j0 += 8 * SG) {
       uint32_t x[8];
       float w[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        x[u] = __builtin_nontemporal_load(src + size_t(c0 + j + u * SG) * LPS);  // read once
-        w[u] = __shfl(wl, j + u * SG, 64);
+        const int sl = j0 + u * SG + hf;  // < n
+        x[u] = __builtin_nontemporal_load(src + size_t(c0 + sl) * LPS);  // read once
+        w[u] = __shfl(wl, sl, 64);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -390,11 +396,13 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdSelArgs a, SelLists
         a1 = fmaf(w[u], bf16_hi(x[u]), a1);
       }
     }
-    for (; j < n; j += SG) {
-      const uint32_t x = src[size_t(c0 + j) * LPS];
-      const float w = __shfl(wl, j, 64);
-      a0 = fmaf(w, bf16_lo(x), a0);
-      a1 = fmaf(w, bf16_hi(x), a1);
+    for (; j0 < n; j0 += SG) {
+      const int sl = j0 + hf < n ? j0 + hf : j0;
+      const uint32_t x = src[size_t(c0 + sl) * LPS];
+      const float w = __shfl(wl, sl, 64);
+      const float ww = j0 + hf < n ? w : 0.f;
+      a0 = fmaf(ww, bf16_lo(x), a0);
+      a1 = fmaf(ww, bf16_hi(x), a1);
     }
   }
   for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor(lsum, off);
