@@ -41,12 +41,25 @@ def _train_shape(i):
     return dts, B, Hkv * G, Hkv, D, N, block, topk
 
 
-TRAIN_IDS = list(range(20))
+def _train_shape_many(i):
+    """Longer rows selecting most of their history (long selection lists,
+    many P V slots per row)."""
+    r = np.random.default_rng(7500 + i)
+    Hkv = int(r.choice([1, 2]))
+    G = int(r.choice([1, 2, 4, 8]))
+    D = int(r.choice([64, 128]))
+    N = int(r.integers(1000, 3000))
+    C = N // 64
+    topk = int(r.integers(C // 2, C + 3))
+    return "bf16", 1, Hkv * G, Hkv, D, N, 64, topk
+
+
+TRAIN_IDS = list(range(20)) + list(range(100, 108))
 
 
 @pytest.mark.parametrize("i", TRAIN_IDS, ids=[f"train{i}" for i in TRAIN_IDS])
 def test_training_random_shape(i):
-    dts, B, Hq, Hkv, D, N, block, topk = _train_shape(i)
+    dts, B, Hq, Hkv, D, N, block, topk = _train_shape(i) if i < 100 else _train_shape_many(i)
     print(f"case train{i}: {dts} B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} block{block} topk{topk}", flush=True)
     dt = torch.float32 if dts == "f32" else torch.bfloat16
     w = Workload(f"rand{i}", "train", dts, B, Hq, Hkv, D, N, block, topk, index=20 + i)
