@@ -744,6 +744,8 @@ PREFILL_CASES = [
     ("bf16-g4", "bf16", 8, 2, 128, 640, 64, 14, [640, 600, 130], 3),
     ("bf16-g5-d64", "bf16", 10, 2, 64, 320, 64, 6, [320, 64, 63], 2),
     ("f32-block32", "f32", 4, 1, 64, 200, 32, 8, [200, 33, 1], 2),
+    # longer prompts: 47 tiles of the full-scope kernel on the shared zero score row
+    ("bf16-g4-long", "bf16", 8, 2, 128, 3000, 64, 48, [3000, 2417, 64], 8),
 ]
 
 
