@@ -6,7 +6,8 @@ counts, every group size the kernels specialise, D 64 and 128, blocks 16 to
 idle, ragged, full or over the capacity.  The oracle's scores and indices feed
 the attention calls, as in the fixed training cases; decode runs the whole
 step (sas_decode_step) and is held to the oracle on the scores it selected on;
-the gate variants (sigmoid, raw logit, outer) and the selector backward run
+the gate variants (sigmoid, raw logit, outer, straight-through) and the
+selector backward run
 on random shapes too.
 Tolerances are those of the fixed cases (tests/gpu_util.py).
 """
@@ -250,3 +251,53 @@ def test_selector_backward_random_shape(i):
     normwise(to64(dkbar), dkbar_ref, tol, "dkbar")
     normwise(to64(dk), dk_ref, tol, "dk")
     assert torch.all(dk[:, :, C * block:] == 0)
+
+
+STE_IDS = list(range(6))
+
+
+@pytest.mark.parametrize("i", STE_IDS, ids=[f"ste{i}" for i in STE_IDS])
+def test_ste_gate_random_shape(i):
+    """The hard gate with a straight-through estimator on random shapes (both
+    scopes), against the oracle's reading of it."""
+    dts, B, Hq, Hkv, D, N, block, topk = _train_shape(300 + i)
+    N = min(N, 600)  # the oracle's STE visits every history block of every row
+    print(f"case ste{i}: {dts} B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} block{block} topk{topk}", flush=True)
+    dt = torch.float32 if dts == "f32" else torch.bfloat16
+    if topk is not None:
+        topk = min(topk, N // block + 2)
+    w = Workload(f"srand{i}", "train", dts, B, Hq, Hkv, D, N, block, topk, index=80 + i)
+    q, k, v, do = (x.to(DEV) for x in training_inputs(w, device="cpu"))
+    G, scale, tol, C = Hq // Hkv, w.scale, tolerances(dt), N // block
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    kbar_r = to64(torch.tensor(orc.pool_block_keys(k64, block)).to(dt))
+    pos = np.broadcast_to(np.arange(N), (B, N))
+    s32 = orc.block_scores(q64, kbar_r, block, scale, pos).astype(np.float32)
+    idx = None if topk is None else orc.topk_select(s32, G, pos // block, topk)
+    scores = torch.tensor(s32).to(DEV)
+    idx_t = None if idx is None else torch.tensor(idx).to(DEV)
+    tk = -1 if topk is None else topk
+    sdt = sas.SAS_F32 if dt == torch.float32 else sas.SAS_BF16
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    lse_s = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    wsf = sas.workspace(sas.SAS_OP_FWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_fwd_gate(q, k, v, scores, idx_t, o, lse, lse_s, block, scale, sas.SAS_GATE_STE, wsf)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, Hq, N, C), dtype=torch.float32, device=DEV)
+    wsb = sas.workspace(sas.SAS_OP_BWD_GATE, B, Hq, Hkv, N, D, block, tk, sdt, DEV)
+    sas.sas_gated_attn_bwd_gate(q, k, v, o, do, scores, idx_t, lse, lse_s, dq, dk, dv, ds, block, scale,
+                                sas.SAS_GATE_STE, wsb)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, lses_ref, dq_r, dk_r, dv_r, ds_r = orc.ste_gate_attention(
+        q64, k64, v64, to64(do), s32.astype(np.float64), idx, block, scale)
+    if tol["o_abs"] is not None:
+        max_abs(to64(o), o_ref, tol["o_abs"], "o")
+    else:
+        normwise(to64(o), o_ref, tol["o_rel"], "o")
+    normwise(to64(lse), lse_ref, tol["lse"], "lse")
+    normwise(to64(lse_s), lses_ref, tol["lse"], "lse_s")
+    normwise(to64(dq), dq_r, tol["grad"], "dq")
+    normwise(to64(dk), dk_r, tol["grad"], "dk")
+    normwise(to64(dv), dv_r, tol["grad"], "dv")
+    normwise(to64(ds), ds_r, tol["ds"], "ds")
