@@ -7,8 +7,7 @@ idle, ragged, full or over the capacity.  The oracle's scores and indices feed
 the attention calls, as in the fixed training cases; decode runs the whole
 step (sas_decode_step) and is held to the oracle on the scores it selected on;
 the gate variants (sigmoid, raw logit, outer, straight-through) and the
-selector backward run
-on random shapes too.
+selector backward run on random shapes too.
 Tolerances are those of the fixed cases (tests/gpu_util.py).
 """
 import numpy as np
