@@ -197,6 +197,9 @@ TOPK_CASES = [
     (12000, 1, None, 1),
     (2500, 3, 1, 40),
     (5000, 1, None, 256),
+    (12000, 1, None, 40),   # 8-wave runs with 32 candidates a lane, K in 33..64 and 17..32
+    (16384, 2, None, 64),
+    (9000, 1, None, 24),
 ]
 
 
