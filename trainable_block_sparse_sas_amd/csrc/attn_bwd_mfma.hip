@@ -62,6 +62,7 @@ struct BwdArgs {
   uint16_t* selpre;  // workspace [B, Hkv, N, MWB + 1]: set bits before each word (sparse)
   bf16_t* dqp;       // workspace [B, Hq, N, topk + 1, D]: dQ share per slot (sparse)
   float* dbl;        // workspace [pairs, list entries, G]: dbeta per list entry and head (sparse)
+  bf16_t* dummy;     // workspace, one row of D: target of the stores of rows a step does not hold (sparse)
   const float* lg2;  // optional [pairs, list entries, G]: base-2 log gate per list entry and head,
                      // saved by the forward (sparse; else the scores and LSE_s give it)
   int Hq, Hkv, N, C, topk, MWB, n_tiles, n_pairs, NB;
@@ -467,11 +468,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
         const int r = 16 * rs + lr;
         const uint4 b0 = *reinterpret_cast<const uint4*>(dst_sh + r * TST + 8 * lq);
         const uint4 b1 = *reinterpret_cast<const uint4*>(dst_sh + r * TST + 32 + 8 * lq);
+        // The row's address is formed once and kept opaque: built from the
+        // stage array in few steps, every store keeps the array's alias
+        // scope, so the compiler sees it cannot touch the other stage and
+        // does not wait here for that stage's loads (a longer address chain
+        // lost the scope on the second tile's store and drained them).
+        int wo = r * WST + 16 * NDW * wave + 4 * lq;
+        asm volatile("" : "+v"(wo));
+        uint16_t* wrow = wst + wo;
 #pragma unroll
         for (int nd = 0; nd < NDW; ++nd) {
           f32x4 acc = mfma16(kq[nd][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
           acc = mfma16(kq[nd][1], b1, acc);
-          *reinterpret_cast<uint2*>(wst + r * WST + 16 * (NDW * wave + nd) + 4 * lq) =
+          *reinterpret_cast<uint2*>(wrow + 16 * nd) =
               make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
         }
       }
@@ -480,12 +489,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
       for (int u = 0; u < RS * CH / NT; ++u) {
         const int r = (u * NT + tid) / CH, cc = (u * NT + tid) % CH;
         const int e = tkr[r];
-        if (e >= 0) {
-          const int slot = MK ? a.topk : e >> 23;
-          bf16_t* dst = a.dqp + ((hrow0 + size_t(r % G) * N + (e & kTokMask)) * (a.topk + 1) + slot) * D;
-          const uint4 v = *reinterpret_cast<const uint4*>(wst + r * WST + cc * 8);
-          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst + cc * 8));
-        }
+        // rows the step does not hold store to the dummy row, so that every
+        // step issues the same stores (the next step's wait leaves them in
+        // flight)
+        const int slot = MK ? a.topk : e >> 23;
+        bf16_t* dst = e >= 0 ? a.dqp + ((hrow0 + size_t(r % G) * N + (e & kTokMask)) * (a.topk + 1) + slot) * D
+                             : a.dummy;
+        const uint4 v = *reinterpret_cast<const uint4*>(wst + r * WST + cc * 8);
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst + cc * 8));
       }
     }
   };
@@ -498,6 +509,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
   // the lane's row: step 0's token, and step 1's raw list word
   if (n_steps > 0) issue(S0{}, 0, tok_fin(0, lane / G, tok_raw(0, lane / G)), lane);
   uint32_t raw1 = n_steps > 0 ? tok_raw(min(1, n_steps - 1), lane / G) : 0u;
+  wait_vm<0>();
   // One step on stage `tag`: wait for its rows, load step k + 1 into the
   // other stage and the raw list words of step k + 2 (the last step's again
   // past the end: an unconditional load, never examined), compute.
@@ -505,7 +517,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, SelLists L)
     using Pn = std::integral_constant<int, decltype(tag)::value ^ 1>;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    wait_vm<0>();
+    // this stage's rows and the list words; at sparse scope every step ends
+    // with the same RS * CH / NT share stores, which stay in flight (before
+    // the first step nothing is in flight)
+    wait_vm<SPARSE ? RS * CH / NT : 0>();
     ring_barrier();
     if (k + 1 < n_steps) issue(Pn{}, k + 1, tok_fin(k + 1, ln / G, raw1), ln);
     const uint32_t raw2 = tok_raw(min(k + 2, n_steps - 1), ln / G);
@@ -1052,7 +1067,7 @@ bool bwd_mfma_supported(const Dims& d, int topk, bool sparse) {
 // and the dbeta records.
 
 struct BwdWs {
-  size_t delta, lists, dqp, dbl, total;
+  size_t delta, lists, dqp, dbl, dummy, total;
 };
 
 static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
@@ -1069,6 +1084,8 @@ static BwdWs bwd_ws_layout(const Dims& d, int topk, bool sparse) {
     at += align_up(rows * size_t(topk + 1) * d.D * sizeof(bf16_t));
     w.dbl = at;
     at += align_up(size_t(d.B) * d.Hkv * d.N * size_t(topk > 0 ? topk : 1) * d.G() * sizeof(float));
+    w.dummy = at;
+    at += align_up(size_t(d.D) * sizeof(bf16_t));
   }
   w.total = at;
   return w;
@@ -1160,6 +1177,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     a.lg2 = C.lg2;
     a.ds_hist_only = ctx != nullptr;  // the saved-context backward leaves them to the caller
     a.dbl = reinterpret_cast<float*>(w + W.dbl);
+    a.dummy = reinterpret_cast<bf16_t*>(w + W.dummy);
   }
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
